@@ -1,0 +1,145 @@
+"""Paged KV storage: block mapping, pool layout, token write, block copy (oracle; test infrastructure only).
+
+[LC] = page "长上下文优化：注意力稀疏化与 KV Cache 管理" (plumephp.com/llm-long-context-optimization),
+       the block-table sketch (logical tokens 0-15 / 16-31 / 32.. in physical blocks 7 / 2 / 19).
+[PA] = page "KV Cache 与 PagedAttention：显存复用与长上下文推理" (plumephp.com/ai-kv-cache-paged-attention),
+       blocks "PagedAttention 的设计", "物理布局示意", "三大运行时组件", and the copy_on_write snippet.
+
+What the pages fix: a sequence's tokens are cut into fixed 16-token blocks;
+logical block j of a sequence lives in the physical block its block table
+names at index j; physical blocks come from one shared pool.  What they leave
+open and is taken here as the storage convention (the same one the HIP
+library documents):
+
+  K pool  [num_blocks][num_kv_heads][16][head_dim]   token-major tile
+  V pool  [num_blocks][num_kv_heads][head_dim][16]   dim-major tile
+  scales  [num_blocks][num_kv_heads][16] float32     FP8 only, K and V separately
+
+Storage dtypes are held here as raw numpy arrays: "f32" float32, "bf16" uint16
+bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes.
+"""
+
+import numpy as np
+
+from . import fp8
+
+BLOCK_SIZE = 16
+DTYPES = ("f32", "bf16", "f16", "fp8")
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "fp8": np.uint8}
+
+
+def storage_dtype(kv_dtype: str):
+    return _STORAGE[kv_dtype]
+
+
+def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored elements (fp8 codes decode without their scale)."""
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        bits = a.astype(np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return fp8.decode(a)
+    raise ValueError(dtype)
+
+
+def physical_block(table_row, pos: int, num_blocks: int, block_size: int = BLOCK_SIZE) -> int:
+    """Physical block of logical position pos ([PA] 物理布局示意): the table entry of block pos // 16.
+
+    Raises if the entry is not a valid pool index (e.g. -1 for an unmapped block).
+    """
+    b = int(table_row[pos // block_size])
+    if not 0 <= b < num_blocks:
+        raise IndexError(f"position {pos}: table entry {b} is not a block of a {num_blocks}-block pool")
+    return b
+
+
+def slot(table_row, pos: int, num_blocks: int, block_size: int = BLOCK_SIZE) -> int:
+    """Flat token slot in the pool: physical block * 16 + offset inside the block."""
+    return physical_block(table_row, pos, num_blocks, block_size) * block_size + pos % block_size
+
+
+def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, fill=0):
+    """Allocate (k_pool, v_pool, k_scale, v_scale) in the documented layout; scales None unless fp8."""
+    st = storage_dtype(kv_dtype)
+    k = np.full((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), fill, dtype=st)
+    v = np.full((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), fill, dtype=st)
+    if kv_dtype == "fp8":
+        ks = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
+        vs = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
+    else:
+        ks = vs = None
+    return k, v, ks, vs
+
+
+def write_tokens(pools, kv_dtype: str, k_src, v_src, src_dtype: str, table_rows, seq_ids, positions):
+    """Store new tokens' K and V (all KV heads) at the slots their block tables give.
+
+    k_src, v_src: [T][Hkv][D] raw source arrays in src_dtype.  Token t belongs
+    to sequence seq_ids[t] at logical position positions[t].  For f32/bf16/f16
+    pools the source dtype must equal the pool dtype and the bytes are stored
+    unchanged; for fp8 pools each (token, KV head) row is quantised with its own
+    scale (fp8.quantize_per_token).  Mutates pools in place.
+    """
+    k_pool, v_pool, k_scale, v_scale = pools
+    nb = k_pool.shape[0]
+    if kv_dtype == "fp8":
+        if src_dtype == "fp8":
+            raise ValueError("fp8 pools take f32/bf16/f16 sources")
+        kq, ks = fp8.quantize_per_token(to_f64(k_src, src_dtype).astype(np.float32))
+        vq, vs = fp8.quantize_per_token(to_f64(v_src, src_dtype).astype(np.float32))
+    elif src_dtype != kv_dtype:
+        raise ValueError("a non-fp8 pool stores source bytes of its own dtype")
+    for t, (s, p) in enumerate(zip(seq_ids, positions)):
+        b = physical_block(table_rows[s], p, nb)
+        o = p % BLOCK_SIZE
+        if kv_dtype == "fp8":
+            k_pool[b, :, o, :] = kq[t]
+            v_pool[b, :, :, o] = vq[t]
+            k_scale[b, :, o] = ks[t]
+            v_scale[b, :, o] = vs[t]
+        else:
+            k_pool[b, :, o, :] = k_src[t]
+            v_pool[b, :, :, o] = v_src[t]
+
+
+def gather_logical(pools, kv_dtype: str, table_row, positions, num_blocks=None):
+    """Logical K, V [len(positions)][Hkv][D] as float64, dequantised for fp8.
+
+    Each position is looked up through the block table ([LC] block-table sketch);
+    reading an unmapped (-1) or out-of-pool entry raises.
+    """
+    k_pool, v_pool, k_scale, v_scale = pools
+    nb = k_pool.shape[0] if num_blocks is None else num_blocks
+    hkv, d = k_pool.shape[1], k_pool.shape[3]
+    K = np.empty((len(positions), hkv, d))
+    V = np.empty((len(positions), hkv, d))
+    for i, p in enumerate(positions):
+        b = physical_block(table_row, int(p), nb)
+        o = int(p) % BLOCK_SIZE
+        k = to_f64(k_pool[b, :, o, :], kv_dtype)
+        v = to_f64(v_pool[b, :, :, o], kv_dtype)
+        if kv_dtype == "fp8":
+            k = k * k_scale[b, :, o].astype(np.float64)[:, None]
+            v = v * v_scale[b, :, o].astype(np.float64)[:, None]
+        K[i], V[i] = k, v
+    return K, V
+
+
+def copy_blocks(pools, pairs):
+    """Copy whole physical blocks src -> dst (K, V and, for fp8, both scales).
+
+    This is the data half of copy-on-write ([PA] 三大运行时组件 and the
+    copy_on_write snippet): before a write into a block that other sequences
+    still reference, its contents go to a fresh private block.  Pairs apply in
+    order.
+    """
+    for arr in pools:
+        if arr is None:
+            continue
+        for src, dst in pairs:
+            arr[dst] = arr[src]
