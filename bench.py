@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+A step is one decode step of one layer over the whole batch, every kernel of
+the path on the GPU with all inputs resident in HBM:
+  paged_decode_slots -> paged_kv_write (the new token of every sequence)
+  -> paged_decode_attn (partition kernel + log-sum-exp merge).
+Default workload: the Llama-3-8B-shaped layer (64 sequences, lengths U{512..8192},
+32 q / 8 KV heads, head_dim 128, bf16 KV, shuffled 16-token blocks).
+
+Printed: one JSON line.  `value` is KV bytes read per step / step time (GB/s);
+`roofline` describes the partition kernel (its algorithmic KV bytes per launch
+over its own average duration, timed with HIP events on its stream);
+`cpu_baseline` is the fp64 CPU oracle timed on the host's cores over a bounded
+sample of the same workload.
+
+    python bench.py [--steps 50] [--warmup 5] [--workload llama3] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV GB/s read (% of HBM peak) and decode tokens/s, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("paged_kv_cache_283_amd/csrc/decode_attn.hip", "paged_kv_cache_283_amd/csrc/device_common.hpp",
+                  "paged_kv_cache_283_amd/csrc/geometry.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_partition_llama3_traffic.txt")
+WORKLOAD_NAMES = {"llama3": "llama3-8b-layer-decode", "fp8long": "fp8-kv-32k-shared-prefix",
+                  "streaming": "streamingllm-131k-sinks4-window4096", "h2o": "h2o-8k-mass",
+                  "llama2": "llama2-70b-80-layer-decode", "tiny": "tiny-paged-decode"}
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_per_launch):
+    """HBM traffic of the partition kernel from the committed counter summary, if it is current."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_hash") != kernel_hash():
+        return None, "kernel changed since the counters were taken"
+    try:
+        return float(kv["traffic_bytes_per_launch"]), kv.get("note")
+    except (KeyError, ValueError):
+        return None, None
+
+
+def kv_bytes_per_token(w):
+    eb = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}[w.kv_dtype]
+    per = w.num_kv_heads * 2 * w.head_dim * eb
+    if w.kv_dtype == "fp8":
+        per += w.num_kv_heads * 2 * 4
+    return per
+
+
+def attended_tokens(w, lay):
+    """Positions decode attention reads per layer: the whole context, or sinks + window."""
+    n = 0
+    for L in lay.lens:
+        L = int(L)
+        n += w.num_sinks + w.window if (w.window > 0 and L > w.num_sinks + w.window) else L
+    return int(n)
+
+
+def cpu_baseline(w, lay, ksrc, vsrc, q, seconds):
+    """Time the fp64 oracle on host cores over the workload's sequences (cycled), bounded in time."""
+    import math
+
+    import numpy as np
+    import torch
+
+    from oracle import attention, policies
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    per_tok = kv_bytes_per_token(w)
+    # host copies of the sample's source rows (not timed): the oracle decodes and attends
+    sample, budget_rows = [], 600_000
+    for s in range(w.num_seqs):
+        L = int(lay.lens[s])
+        keep = policies.streaming_keep(L, w.num_sinks, w.window)
+        pos = np.nonzero(keep)[0]
+        i = np.searchsorted(lay.data_pos[s], pos)
+        rows = torch.from_numpy(lay.data_row[s][i]).to(ksrc.device)
+        sample.append((s, keep, ksrc.index_select(0, rows).cpu(), vsrc.index_select(0, rows).cpu()))
+        budget_rows -= pos.size
+        if budget_rows <= 0:
+            break
+    qh = q.cpu()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    done_bytes, n_seq = 0, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for s, keep, k, v in sample:
+            K = k.to(torch.float64).numpy()
+            V = v.to(torch.float64).numpy()
+            attention.decode_attention(qh[s].to(torch.float64).numpy(), K, V, scale)
+            done_bytes += K.shape[0] * per_tok
+            n_seq += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} sequence-decodes of the {w.name} workload ({len(sample)} distinct sequences, "
+                      f"{done_bytes / 1e9:.2f} GB of KV) in {dt:.1f} s, numpy float64, bf16->f64 decode included",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama3", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--rotate", type=int, default=2, help="disjoint pool replicas cycled so that the 256 MB "
+                    "Infinity Cache cannot serve repeated steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--probe-only", action="store_true", help="run only the HBM read/copy probes")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from paged_kv_cache_283_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---- HBM probes: practical read and copy ceilings on this machine
+    probe_n = 4 << 30
+    buf = torch.empty(probe_n, dtype=torch.uint8, device=dev)
+    buf2 = torch.empty(probe_n // 4, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1024, dtype=torch.float32, device=dev)
+    ops.probe_read(buf, sink)
+    ops.probe_copy(buf2, buf[: probe_n // 4])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        ops.probe_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * probe_n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    e0.record()
+    for _ in range(5):
+        ops.probe_copy(buf2, buf[: probe_n // 4])
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * (probe_n // 4) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, buf2
+    if args.probe_only:
+        print(json.dumps({"probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1),
+                          "copy_bytes_per_launch": 2 * (probe_n // 4)}))
+        return
+
+    # ---- workload: pools filled through the library's own write path (untimed prefill)
+    w = W.WORKLOADS[args.workload]
+    lay = W.make_layout(w)
+    tables = torch.from_numpy(lay.tables).to(dev)
+    lens = torch.from_numpy(lay.lens).to(dev)
+    layers = w.num_layers
+    replicas = 1 if layers > 1 else max(1, args.rotate)
+    from tests import _harness as H   # pool construction + fill helpers shared with the GPU tests
+    pools = []
+    for layer in range(max(layers, replicas)):
+        p = H.make_pools(w, lay.num_blocks)
+        ksrc, vsrc = W.kv_source(w, lay, layer=layer if layers > 1 else 0, device=dev)
+        H.fill(w, lay, p, ksrc, vsrc, tables, hold_last=True)
+        pools.append(p)
+        if layer + 1 < max(layers, replicas):
+            del ksrc, vsrc
+    # the new token of every sequence (this step's K/V rows) and the queries
+    r = torch.from_numpy(H.newest_rows(lay)).to(dev)
+    k_new, v_new = ksrc.index_select(0, r).contiguous(), vsrc.index_select(0, r).contiguous()
+    q = W.queries(w, device=dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32, device=dev)
+    slots = torch.empty(w.num_seqs, dtype=torch.int64, device=dev)
+    ws = ops.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, lay.max_len, w.num_sinks, w.window,
+                             False, dev)
+    torch.cuda.synchronize()
+
+    launches = []
+    for p in pools:
+        k, v, ks, vs = p
+        launches.append((
+            ops.paged_decode_slots(tables, lens, lay.num_blocks, slot_mapping=slots, stream=stream, prepare=True),
+            ops.paged_kv_write(k_new, v_new, k, v, slots, ks, vs, stream=stream, prepare=True),
+            ops.paged_decode_attn(out, q, k, v, tables, lens, lay.max_len, k_scale=ks, v_scale=vs,
+                                  num_sinks=w.num_sinks, window=w.window, workspace=ws, stream=stream,
+                                  prepare=True)))
+
+    def step(i):
+        if layers > 1:
+            for la in launches:
+                for f in la:
+                    f()
+        else:
+            for f in launches[i % replicas]:
+                f()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    n_attn = args.steps * (layers if layers > 1 else 1)
+    ops.timing_begin(n_attn)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    kernel_ms = ops.timing_end(n_attn)
+    step_ms = t_start.elapsed_time(t_end) / args.steps
+
+    n_tok = attended_tokens(w, lay)
+    per_tok = kv_bytes_per_token(w)
+    kv_bytes_layer = n_tok * per_tok
+    kv_bytes_step = kv_bytes_layer * layers
+    value = kv_bytes_step / (step_ms * 1e-3) / 1e9
+    k_avg_ms = float(np.mean(kernel_ms))
+    achieved = kv_bytes_layer / (k_avg_ms * 1e-3) / 1e9
+    traffic, traffic_note = read_traffic(kv_bytes_layer)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "batch": w.num_seqs, "layers": layers,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "kv_dtype": w.kv_dtype, "block_size": 16, "max_context_len": lay.max_len,
+                   "attended_tokens_per_layer": n_tok, "num_sinks": w.num_sinks, "window": w.window,
+                   "pool_replicas_rotated": replicas},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "tokens_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kv_bytes_per_step": kv_bytes_step,
+        "partition_kernel_avg_us": round(1e3 * k_avg_ms, 2),
+        "partition_kernel_min_us": round(1e3 * float(np.min(kernel_ms)), 2),
+        "probe_read_gbs": round(read_gbs, 1),
+        "probe_copy_gbs": round(copy_gbs, 1),
+        "frac_of_probe_read": round(achieved / read_gbs, 4),
+        "wall_s": round(wall, 3),
+        "kernel_hash": kernel_hash(),
+    }
+    if traffic_note:
+        result["traffic_note"] = traffic_note
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, lay, ksrc, vsrc, q, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

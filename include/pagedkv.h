@@ -1,0 +1,235 @@
+/*
+ * pagedkv.h -- C ABI of the gfx950 (MI355X) paged KV-cache decode library.
+ *
+ * Pages this interface follows (cited by title and section throughout):
+ *   [LC] "长上下文优化：注意力稀疏化与 KV Cache 管理"
+ *        https://www.plumephp.com/llm-long-context-optimization/
+ *   [PA] "KV Cache 与 PagedAttention：显存复用与长上下文推理"
+ *        https://www.plumephp.com/ai-kv-cache-paged-attention/
+ *   [SO] "系统优化"
+ *        https://www.threethreeliu.top/projects/knowledge-inference-optimization-memory-9b32e2e927
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer (HBM of the current HIP device)
+ *    unless its comment says "host".  Arrays are dense and row-major.
+ *  - The caller owns all memory.  The library never allocates or frees device
+ *    memory; scratch space is a caller-provided workspace sized by a query call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work and returns; nothing synchronises implicitly.
+ *  - Return value: a pkv_status.  Scalar arguments and pointer presence are
+ *    validated on the host BEFORE any HIP call, so a bad argument never reaches
+ *    the GPU.  pkv_last_error() gives a thread-local message for the last
+ *    non-OK status.  The library never throws and never aborts.
+ *  - Device-resident indices (block tables, slot mappings, context lengths,
+ *    block pairs) cannot be checked on the host.  Kernels bound-check each one
+ *    they use and never touch memory outside the arrays described here; what an
+ *    out-of-range value does to the result is stated per call.
+ *
+ * KV pool layout (one pool per layer; block_size is 16, [PA] "PagedAttention 的设计")
+ * ---------------------------------------------------------------------------------
+ *   k_pool  [num_blocks][num_kv_heads][16][head_dim]   token-major tile
+ *   v_pool  [num_blocks][num_kv_heads][head_dim][16]   dim-major tile
+ *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 only)
+ * A token at logical position p of a sequence lives in physical block
+ * table[p / 16] at offset p % 16 ([PA] "物理布局示意", [LC] block-table sketch);
+ * its flat slot is block * 16 + offset.  With FP8 the stored value is
+ * decode(code) * scale, one scale per (token, KV head) for K and one for V
+ * ([PA] "量化原理": per-token scaling).
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,        /* an argument is out of its documented range or a pointer is NULL */
+  PKV_EUNSUPPORTED = 2,  /* valid in principle, not built: head_dim, group size, dtype combination */
+  PKV_EWORKSPACE = 3,    /* workspace_bytes smaller than the query call asks for */
+  PKV_EDEVICE = 4        /* a HIP launch or runtime call failed; see pkv_last_error() */
+} pkv_status;
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_F16 = 2,
+  PKV_FP8_E4M3 = 3       /* OCP E4M3FN: bias 7, max 448, no infinities, 0x7F/0xFF = NaN */
+} pkv_dtype;
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version, e.g. "pagedkv 0.1.0 gfx950". Host string, never NULL. */
+const char* pkv_version(void);
+
+/*
+ * paged_decode_slots -- slot of each sequence's newest token (decode step).
+ *
+ * The token being decoded sits at position context_lens[s] - 1; its slot is
+ * block_tables[s][(len-1)/16] * 16 + (len-1) % 16 ([PA] "PagedAttention 的设计":
+ * the block table maps logical block to physical block).
+ *   block_tables  int32 [num_seqs][block_table_stride]
+ *   context_lens  int32 [num_seqs], length INCLUDING the new token
+ *   slot_mapping  int64 [num_seqs] out; -1 where the length is < 1, exceeds
+ *                 block_table_stride*16, or the table entry is not in [0, num_blocks)
+ */
+int paged_decode_slots(const int32_t* block_tables, int block_table_stride,
+                       const int32_t* context_lens, int num_seqs, int num_blocks,
+                       int block_size, int64_t* slot_mapping, void* stream);
+
+/*
+ * paged_token_slots -- slots of arbitrary (sequence, position) tokens, e.g. a
+ * prefill or a chunk of one: slot = block_tables[seq][pos/16] * 16 + pos % 16
+ * ([PA] "物理布局示意").
+ *   seq_ids, positions  int32 [num_tokens]
+ *   slot_mapping        int64 [num_tokens] out; -1 where seq_id is outside
+ *                       [0, num_seqs), pos is outside [0, block_table_stride*16),
+ *                       or the table entry is not in [0, num_blocks)
+ */
+int paged_token_slots(const int32_t* block_tables, int block_table_stride, int num_seqs,
+                      const int32_t* seq_ids, const int32_t* positions, int num_tokens,
+                      int num_blocks, int block_size, int64_t* slot_mapping, void* stream);
+
+/*
+ * paged_kv_write -- store new tokens' K and V into the paged pools.
+ *
+ * [PA] "PagedAttention 的设计" / [LC] StreamingKVCache.append: a new token's K and V
+ * for every KV head go to the slot the block table assigns it.  For FP8 pools
+ * ([PA] "量化原理") each (token, KV head) row of head_dim values is quantised with
+ *     scale = absmax / 448        (IEEE fp32 division, correctly rounded)
+ *     code  = E4M3FN(x / scale)   (fp32 division; round to nearest, ties to even,
+ *                                  saturating to +-448; absmax 0 -> scale 0, codes 0)
+ * and the scale is stored beside the codes.
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of src_dtype
+ *   kv_dtype       PKV_F32/BF16/F16 require src_dtype == kv_dtype (bytes are copied);
+ *                  PKV_FP8_E4M3 takes src_dtype F32, BF16 or F16 (finite values)
+ *   k_scale, v_scale   required for FP8, ignored otherwise
+ *   slot_mapping   int64 [num_tokens]; a slot < 0 or >= num_blocks*16 skips the token
+ * Two tokens with the same slot race (one of them wins).
+ */
+int paged_kv_write(const void* k_new, const void* v_new, int src_dtype,
+                   void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+                   const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                   int num_kv_heads, int head_dim, int block_size, void* stream);
+
+/*
+ * paged_decode_attn_workspace_size -- bytes of workspace paged_decode_attn needs.
+ * Pass the same num_seqs, num_q_heads, head_dim, max_context_len, num_sinks,
+ * window and (attn_mass != NULL) as the attention call.  Returns 0 for
+ * arguments the attention call would reject.
+ */
+size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                        int max_context_len, int num_sinks, int window,
+                                        int want_mass);
+
+/*
+ * paged_decode_attn -- single-token GQA decode attention over the paged pools.
+ *
+ * For sequence s of length L = context_lens[s] and query head h (KV head
+ * h / G, G = num_q_heads / num_kv_heads, [LC] MHA/GQA/MQA table):
+ *     z_p   = scale * dot(q[s][h], K[p])          for kept positions p
+ *     out   = sum_p softmax(z)_p * V[p]
+ * K[p], V[p] are read block by block through block_tables ([PA] "三大运行时组件":
+ * decode loads KV per block).  Kept positions ([LC] StreamingKVCache, [SO] 4.1):
+ *     window <= 0 : all p < L
+ *     window  > 0 : p < num_sinks  or  p >= L - window
+ * Blocks holding no kept position are not read, so their table entries may be
+ * anything (e.g. -1).
+ *
+ *   out            [num_seqs][num_q_heads][head_dim] of out_dtype (F32/BF16/F16)
+ *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (F32/BF16/F16)
+ *   kv_dtype       F32, BF16, F16 or FP8_E4M3 (then k_scale/v_scale are required)
+ *   block_tables   int32 [num_seqs][block_table_stride], stride >= ceil(max_context_len/16)
+ *   context_lens   int32 [num_seqs], 1 <= L <= max_context_len (host value)
+ *   num_q_heads / num_kv_heads in 1..16; head_dim 64 or 128; block_size 16
+ *   attn_mass      NULL, or float [num_seqs][attn_mass_stride] (stride >= max_context_len):
+ *                  for every kept position, += the H2O mass of this step
+ *                  ([LC] H2OEviction.update_scores): the attention probability
+ *                  averaged over all num_q_heads heads.  Other entries are untouched.
+ *   workspace      >= paged_decode_attn_workspace_size(...) bytes, 256-byte aligned
+ * Out-of-range device values never make the kernels touch memory outside the
+ * arrays above.  A sequence whose length is outside
+ * [1, min(max_context_len, 16*block_table_stride)] gets NaN in every output
+ * element and its attn_mass row is left alone; a sequence that needs a table
+ * entry outside [0, num_blocks) gets NaN outputs and NaN added to its kept
+ * attn_mass entries.
+ */
+int paged_decode_attn(void* out, int out_dtype,
+                      const void* q, int q_dtype,
+                      const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int kv_dtype,
+                      const int32_t* block_tables, int block_table_stride,
+                      const int32_t* context_lens, int max_context_len,
+                      int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
+                      int head_dim, int block_size, float scale,
+                      int num_sinks, int window,
+                      float* attn_mass, int attn_mass_stride,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_block_copy -- whole-block copies, the data half of copy-on-write.
+ *
+ * [PA] "三大运行时组件" and its copy_on_write snippet: before a sequence writes
+ * into a physical block that other sequences still share (refcount > 1), the
+ * block is copied to a private one.  Refcounts and table edits are host-side;
+ * this call copies K, V and (FP8) both scale tiles of every KV head.
+ *   block_pairs   int32 [num_pairs][2] = {src, dst}; a pair with an index outside
+ *                 [0, num_blocks) or src == dst is skipped.  Pairs run concurrently:
+ *                 a dst that is also another pair's src or dst races.
+ */
+int kv_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+                  const int32_t* block_pairs, int num_pairs, int num_blocks,
+                  int num_kv_heads, int head_dim, int block_size, void* stream);
+
+/*
+ * h2o_select -- H2O keep-set per sequence ([LC] H2OEviction.select).
+ *
+ * For L = kv_lens[s]:
+ *   L <= budget : keep positions 0..L-1
+ *   otherwise   : keep the last `recent` positions plus the (budget - recent)
+ *                 highest scores among positions [0, L - recent); equal scores
+ *                 go to the lower position, NaN ranks below every number,
+ *                 -0.0 equals +0.0.
+ * Output in ascending position order.
+ *   scores      float [num_seqs][scores_stride], stride >= max_kv_len
+ *   kv_lens     int32 [num_seqs], 1 <= L <= max_kv_len
+ *   keep_idx    int32 [num_seqs][budget] out, -1 after the kept positions
+ *   keep_count  int32 [num_seqs] out (-1 for a length outside [1, max_kv_len])
+ *   0 <= recent <= budget, budget >= 1
+ */
+int h2o_select(const float* scores, int scores_stride, const int32_t* kv_lens,
+               int num_seqs, int max_kv_len, int budget, int recent,
+               int32_t* keep_idx, int32_t* keep_count, void* stream);
+
+/* ---- measurement helpers (not part of the decode path) ------------------ */
+
+/*
+ * Kernel timing for benchmarks.  Between pkv_timing_begin(capacity) and
+ * pkv_timing_end(), each paged_decode_attn call records a HIP event pair on
+ * its stream around its main (per-partition) kernel, up to `capacity` calls.
+ * pkv_timing_end waits for the last event, writes the elapsed milliseconds of
+ * each recorded launch to ms_out (host, capacity floats), returns the count
+ * (or -1 on error).  Not thread-safe: one timing session per process.
+ */
+int pkv_timing_begin(int capacity);
+int pkv_timing_end(float* ms_out, int capacity);
+
+/*
+ * Streaming probes for roofline denominators: read `bytes` (multiple of 16)
+ * from src and fold them into sink[0..1023] (float, written), or copy bytes
+ * from src to dst.  Grid-stride kernels with 16-byte accesses.
+ */
+int pkv_probe_read(const void* src, size_t bytes, float* sink, void* stream);
+int pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

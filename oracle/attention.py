@@ -38,13 +38,13 @@ def decode_attention(q, K, V, scale: float, keep=None):
         raise ValueError("no key position to attend to")
     out = np.zeros((hq, d))
     probs = np.zeros((hq, L))
-    for h in range(hq):
-        g = h // group
-        z = scale * (K[idx, g, :] @ q[h])
-        w = np.exp(z - z.max())
-        pi = w / w.sum()
-        out[h] = pi @ V[idx, g, :]
-        probs[h, idx] = pi
+    for g in range(hkv):
+        heads = slice(g * group, (g + 1) * group)          # the query heads reading KV head g
+        z = scale * (K[idx, g, :] @ q[heads].T)           # [n_kept, G] logits
+        w = np.exp(z - z.max(axis=0))
+        pi = w / w.sum(axis=0)
+        out[heads] = pi.T @ V[idx, g, :]
+        probs[heads, idx] = pi.T
     return out, probs
 
 

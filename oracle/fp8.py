@@ -7,8 +7,8 @@ The page names only "E4M3".  Reading taken: the OCP 8-bit floating point
 format E4M3FN (bias 7, no infinities, S.1111.111 is NaN, largest finite 448),
 the one whose range matches a per-token scale of absmax/448.
 
-Encoding is written as a search, not bit manipulation: a value maps to the
-nearest finite E4M3FN value; of two equally near values the one with an even
+Encoding is written as a table search, not bit manipulation: a value maps
+to the nearest finite E4M3FN value; of two equally near values the one with an even
 code (mantissa LSB 0) wins; anything beyond 448 in magnitude maps to 448
 (saturation -- no NaN is produced from a finite input).
 """
@@ -37,7 +37,6 @@ def decode_table() -> np.ndarray:
 
 
 _TABLE = decode_table()
-_POS_CODES = np.arange(0x7F, dtype=np.int64)          # 0x00..0x7E: the 127 finite magnitudes
 _POS_VALUES = _TABLE[:0x7F]
 
 
@@ -46,26 +45,27 @@ def decode(codes: np.ndarray) -> np.ndarray:
     return _TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
-def encode(x: np.ndarray, chunk: int = 1 << 16) -> np.ndarray:
+def encode(x: np.ndarray) -> np.ndarray:
     """Round float values to E4M3FN codes: nearest finite value, ties to even code, saturate.
 
-    NaN maps to 0x7F.  The sign bit of the input is kept (-0.0 -> 0x80).
+    For each magnitude the two neighbouring finite values (below and above in
+    the sorted table of the 127 non-negative finite values) are compared; the
+    nearer one wins, an exact tie goes to the even code.  Magnitudes beyond
+    448 (and infinity) become 448.  NaN maps to 0x7F.  The sign bit of the
+    input is kept (-0.0 -> 0x80).
     """
     x = np.asarray(x, dtype=np.float64)
-    flat = x.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    for lo in range(0, flat.size, chunk):
-        v = flat[lo:lo + chunk]
-        mag = np.minimum(np.abs(v), E4M3_MAX)          # saturation: beyond 448 is 448
-        dist = np.abs(mag[:, None] - _POS_VALUES[None, :])          # [n, 127]
-        best = dist.min(axis=1, keepdims=True)
-        tied = dist == best
-        even = tied & ((_POS_CODES[None, :] & 1) == 0)
-        pick = np.where(even.any(axis=1), even.argmax(axis=1), tied.argmax(axis=1))
-        code = pick.astype(np.uint8) | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
-        code = np.where(np.isnan(v), NAN_CODE, code).astype(np.uint8)
-        out[lo:lo + chunk] = code
-    return out.reshape(x.shape)
+    mag = np.minimum(np.abs(x), E4M3_MAX)                   # saturation: beyond 448 is 448
+    mag = np.where(np.isnan(mag), 0.0, mag)
+    hi = np.clip(np.searchsorted(_POS_VALUES, mag, side="left"), 0, 0x7E)   # first value >= mag
+    lo = np.clip(hi - 1, 0, 0x7E)                                          # last value < mag
+    d_hi = np.abs(_POS_VALUES[hi] - mag)
+    d_lo = np.abs(mag - _POS_VALUES[lo])
+    pick = np.where(d_lo < d_hi, lo, hi)
+    tie = (d_lo == d_hi) & (lo != hi)
+    pick = np.where(tie, np.where(lo % 2 == 0, lo, hi), pick)
+    code = pick.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(NAN_CODE), code).astype(np.uint8)
 
 
 def quantize_per_token(x: np.ndarray):

@@ -1,0 +1,158 @@
+"""Host-side block allocator with reference counts and copy-on-write.
+
+Page "KV Cache 与 PagedAttention：显存复用与长上下文推理" (plumephp.com/ai-kv-cache-paged-attention):
+  "PagedAttention 的设计"  -- fixed 16-token blocks; one block table per request
+                             mapping logical to physical blocks; free blocks in
+                             one global pool; only a sequence's last block is
+                             partly filled.
+  "三大运行时组件"          -- the block allocator, the per-request table, and
+                             reference counts with copy-on-write: a block shared
+                             by several requests has its count raised, and a
+                             write into a shared block first copies it.
+  "共享场景的价值"          -- parallel samples of one prompt share its prefix;
+                             beam search shares until the fork.
+  copy_on_write snippet    -- new blocks start with refcount 1; the old block's
+                             count drops by one; the table entry is swapped.
+
+The tables here hold block ids; the GPU-side data copy of a COW is the
+kv_block_copy entry point, run by the caller with the (src, dst) pairs these
+methods return, before writing into the new block.
+"""
+from collections import deque
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+class OutOfBlocks(RuntimeError):
+    """The shared pool has no free block left."""
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        if block_size != BLOCK_SIZE:
+            raise ValueError("block_size must be 16")
+        if num_blocks < 1:
+            raise ValueError("num_blocks must be >= 1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.refcount = np.zeros(num_blocks, dtype=np.int32)
+        self._free = deque(range(num_blocks))
+        self.tables = {}          # seq id -> list of physical block ids
+        self.lens = {}            # seq id -> tokens held
+        self.cow_copies = 0
+
+    # ---- pool ---------------------------------------------------------------
+    def _alloc(self) -> int:
+        if not self._free:
+            raise OutOfBlocks(f"all {self.num_blocks} blocks are in use")
+        b = self._free.popleft()
+        self.refcount[b] = 1
+        return b
+
+    def _release(self, b: int) -> None:
+        if self.refcount[b] <= 0:
+            raise RuntimeError(f"block {b} released more often than referenced")
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self._free.append(b)
+
+    @property
+    def num_free(self) -> int:
+        return len(self._free)
+
+    # ---- sequences ------------------------------------------------------------
+    def add_sequence(self, seq, num_tokens: int = 0):
+        """Register a sequence holding num_tokens tokens; returns its block table."""
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} exists")
+        need = -(-num_tokens // self.block_size)
+        if need > self.num_free:
+            raise OutOfBlocks(f"sequence of {num_tokens} tokens needs {need} blocks, {self.num_free} free")
+        self.tables[seq] = [self._alloc() for _ in range(need)]
+        self.lens[seq] = num_tokens
+        return list(self.tables[seq])
+
+    def fork(self, parent, child):
+        """child shares every block of parent (refcounts + 1), as parallel samples of one prompt do."""
+        if child in self.tables:
+            raise KeyError(f"sequence {child} exists")
+        for b in self.tables[parent]:
+            self.refcount[b] += 1
+        self.tables[child] = list(self.tables[parent])
+        self.lens[child] = self.lens[parent]
+        return list(self.tables[child])
+
+    def copy_on_write(self, seq, logical_idx: int):
+        """Give seq a private copy of its logical block if the block is shared.
+
+        Returns (src, dst) for the device copy, or None if the block is not shared.
+        """
+        old = self.tables[seq][logical_idx]
+        if self.refcount[old] <= 1:
+            return None
+        new = self._alloc()
+        self.refcount[old] -= 1
+        self.tables[seq][logical_idx] = new
+        self.cow_copies += 1
+        return (old, new)
+
+    def append_tokens(self, seq, n: int = 1):
+        """Reserve slots for n new tokens of seq.
+
+        Returns (slots int64 [n], copies): copies are (src, dst) block pairs that
+        must be copied on the device before the new tokens are written, because
+        the block receiving them was shared.
+        """
+        slots = np.empty(n, dtype=np.int64)
+        copies = []
+        table = self.tables[seq]
+        for i in range(n):
+            pos = self.lens[seq]
+            lb = pos // self.block_size
+            if lb == len(table):
+                table.append(self._alloc())
+            else:
+                pair = self.copy_on_write(seq, lb)
+                if pair is not None:
+                    copies.append(pair)
+            slots[i] = table[lb] * self.block_size + pos % self.block_size
+            self.lens[seq] = pos + 1
+        return slots, copies
+
+    def free(self, seq) -> None:
+        for b in self.tables.pop(seq):
+            self._release(b)
+        del self.lens[seq]
+
+    # ---- views for the kernels --------------------------------------------------
+    def slot_mapping(self, seq, positions) -> np.ndarray:
+        """int64 slots of the given logical positions of seq."""
+        table = self.tables[seq]
+        pos = np.asarray(positions, dtype=np.int64)
+        if pos.size and (pos.min() < 0 or pos.max() >= self.lens[seq]):
+            raise IndexError("position outside the sequence")
+        blocks = np.asarray(table, dtype=np.int64)[pos // self.block_size]
+        return blocks * self.block_size + pos % self.block_size
+
+    def block_tables(self, seqs, width=None) -> np.ndarray:
+        """int32 [len(seqs)][width] tables, -1 beyond each sequence's blocks."""
+        width = width if width is not None else max((len(self.tables[s]) for s in seqs), default=0)
+        out = np.full((len(seqs), max(width, 1)), -1, dtype=np.int32)
+        for i, s in enumerate(seqs):
+            t = self.tables[s]
+            if len(t) > width:
+                raise ValueError(f"sequence {s} has {len(t)} blocks > width {width}")
+            out[i, : len(t)] = t
+        return out
+
+    def context_lens(self, seqs) -> np.ndarray:
+        return np.array([self.lens[s] for s in seqs], dtype=np.int32)
+
+    def stats(self) -> dict:
+        used = self.num_blocks - self.num_free
+        return {"free_blocks": self.num_free, "used_blocks": used,
+                "shared_blocks": int((self.refcount > 1).sum()), "cow_copies": self.cow_copies,
+                "internal_fragmentation_tokens": int(sum(len(t) * self.block_size - self.lens[s]
+                                                         for s, t in self.tables.items()))}

@@ -1,0 +1,310 @@
+// C ABI of the paged KV-cache library (declared in include/pagedkv.h).
+// Validates every scalar argument and pointer on the host before any HIP call,
+// then hands off to the launchers in launch.hpp.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+#include "geometry.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return status;
+}
+
+int ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+int device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PKV_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_kv_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
+bool valid_float_dtype(int d) { return d >= PKV_F32 && d <= PKV_F16; }
+
+struct Timing {
+  bool active = false;
+  int used = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+};
+Timing g_timing;
+
+// Shared checks of the attention geometry; returns PKV_OK or a status with g_error set.
+int check_attn_shape(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+                     int num_sinks) {
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PKV_EINVAL, "num_seqs %d outside [0, 65535]", num_seqs);
+  if (num_q_heads < 1 || num_kv_heads < 1) return fail(PKV_EINVAL, "head counts must be >= 1");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16)
+    return fail(PKV_EUNSUPPORTED, "query heads per KV head %d > 16", num_q_heads / num_kv_heads);
+  if (num_kv_heads > 65535) return fail(PKV_EINVAL, "num_kv_heads %d too large", num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (max_context_len < 1) return fail(PKV_EINVAL, "max_context_len %d < 1", max_context_len);
+  if (max_context_len > (1 << 30)) return fail(PKV_EINVAL, "max_context_len %d too large", max_context_len);
+  if (num_sinks < 0 || num_sinks > (1 << 30)) return fail(PKV_EINVAL, "num_sinks %d outside [0, 2^30]", num_sinks);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+const char* pkv_version(void) { return "pagedkv 0.1.0 gfx950"; }
+
+int paged_decode_slots(const int32_t* block_tables, int block_table_stride, const int32_t* context_lens,
+                       int num_seqs, int num_blocks, int block_size, int64_t* slot_mapping, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_seqs == 0) return ok();
+  if (!block_tables || !context_lens || !slot_mapping) return fail(PKV_EINVAL, "NULL array argument");
+  if (block_table_stride < 1) return fail(PKV_EINVAL, "block_table_stride %d < 1", block_table_stride);
+  if (block_table_stride > (1 << 26)) return fail(PKV_EINVAL, "block_table_stride %d too large", block_table_stride);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  return device_status(pkv::launch_decode_slots(block_tables, block_table_stride, context_lens, num_seqs, num_blocks,
+                                                slot_mapping, (hipStream_t)stream),
+                       "paged_decode_slots");
+}
+
+int paged_token_slots(const int32_t* block_tables, int block_table_stride, int num_seqs, const int32_t* seq_ids,
+                      const int32_t* positions, int num_tokens, int num_blocks, int block_size, int64_t* slot_mapping,
+                      void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_tokens == 0) return ok();
+  if (!block_tables || !seq_ids || !positions || !slot_mapping) return fail(PKV_EINVAL, "NULL array argument");
+  if (block_table_stride < 1 || block_table_stride > (1 << 26))
+    return fail(PKV_EINVAL, "block_table_stride %d outside [1, 2^26]", block_table_stride);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  return device_status(pkv::launch_token_slots(block_tables, block_table_stride, num_seqs, seq_ids, positions,
+                                               num_tokens, num_blocks, slot_mapping, (hipStream_t)stream),
+                       "paged_token_slots");
+}
+
+int paged_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool, float* k_scale,
+                   float* v_scale, int kv_dtype, const int64_t* slot_mapping, int num_tokens, int num_blocks,
+                   int num_kv_heads, int head_dim, int block_size, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (!valid_float_dtype(src_dtype)) return fail(PKV_EINVAL, "src_dtype %d", src_dtype);
+  if (kv_dtype != PKV_FP8_E4M3 && src_dtype != kv_dtype)
+    return fail(PKV_EUNSUPPORTED, "a non-FP8 pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (num_kv_heads < 1) return fail(PKV_EINVAL, "num_kv_heads %d < 1", num_kv_heads);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  if ((long long)num_tokens * num_kv_heads > (1LL << 32))
+    return fail(PKV_EINVAL, "num_tokens * num_kv_heads too large");
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return fail(PKV_EINVAL, "NULL array argument");
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
+  return device_status(pkv::launch_kv_write(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
+                                            slot_mapping, num_tokens, num_blocks, num_kv_heads, head_dim,
+                                            (hipStream_t)stream),
+                       "paged_kv_write");
+}
+
+size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                        int num_sinks, int window, int want_mass) {
+  if (num_seqs < 0 || num_q_heads < 1 || (head_dim != 64 && head_dim != 128) || max_context_len < 1 ||
+      max_context_len > (1 << 30) || num_sinks < 0 || num_sinks > (1 << 30) || window > (1 << 30))
+    return 0;
+  return pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, num_sinks, window,
+                                    want_mass != 0)
+      .total;
+}
+
+int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int kv_dtype, const int32_t* block_tables,
+                      int block_table_stride, const int32_t* context_lens, int max_context_len, int num_seqs,
+                      int num_blocks, int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale,
+                      int num_sinks, int window, float* attn_mass, int attn_mass_stride, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  int st = check_attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, num_sinks);
+  if (st != PKV_OK) return st;
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (!valid_float_dtype(q_dtype)) return fail(PKV_EINVAL, "q_dtype %d", q_dtype);
+  if (!valid_float_dtype(out_dtype)) return fail(PKV_EINVAL, "out_dtype %d", out_dtype);
+  if (!isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+  if (window > (1 << 30)) return fail(PKV_EINVAL, "window %d too large", window);
+  if (block_table_stride > (1 << 26)) return fail(PKV_EINVAL, "block_table_stride %d too large", block_table_stride);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  if (block_table_stride < (max_context_len + 15) / 16)
+    return fail(PKV_EINVAL, "block_table_stride %d < ceil(max_context_len / 16) = %d", block_table_stride,
+                (max_context_len + 15) / 16);
+  if (attn_mass != nullptr && attn_mass_stride < max_context_len)
+    return fail(PKV_EINVAL, "attn_mass_stride %d < max_context_len %d", attn_mass_stride, max_context_len);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "NULL array argument");
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
+  const pkv::WorkspaceLayout lay = pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                              num_sinks, window, attn_mass != nullptr);
+  if (workspace_bytes < lay.total)
+    return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+  if (lay.total > 0 && !workspace) return fail(PKV_EINVAL, "NULL workspace");
+  if (((uintptr_t)workspace & 255u) != 0) return fail(PKV_EINVAL, "workspace is not 256-byte aligned");
+  if ((uintptr_t)q % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16 ||
+      (k_scale && (uintptr_t)k_scale % 16) || (v_scale && (uintptr_t)v_scale % 16))
+    return fail(PKV_EINVAL, "q, pools and scales must be 16-byte aligned");
+
+  pkv::AttnArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.table_stride = block_table_stride;
+  a.context_lens = context_lens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_blocks = num_blocks;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_sinks = num_sinks;
+  a.window = window;
+  a.attn_mass = attn_mass;
+  a.mass_stride = attn_mass_stride;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
+  a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.stash = attn_mass ? reinterpret_cast<float*>(ws + lay.stash_off) : nullptr;
+  a.fin_ml = attn_mass ? reinterpret_cast<float*>(ws + lay.fin_off) : nullptr;
+  a.p_max = lay.p_max;
+  a.nv_pad = lay.nv_pad;
+
+  hipEvent_t eb = nullptr, ee = nullptr;
+  if (g_timing.active && g_timing.used < (int)g_timing.ev.size()) {
+    eb = g_timing.ev[g_timing.used].first;
+    ee = g_timing.ev[g_timing.used].second;
+    ++g_timing.used;
+  }
+  return device_status(pkv::launch_decode_attn(a, kv_dtype, q_dtype, head_dim, (hipStream_t)stream, eb, ee),
+                       "paged_decode_attn");
+}
+
+int kv_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype, const int32_t* block_pairs,
+                  int num_pairs, int num_blocks, int num_kv_heads, int head_dim, int block_size, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (num_pairs < 0 || num_pairs > 65535) return fail(PKV_EINVAL, "num_pairs %d outside [0, 65535]", num_pairs);
+  if (num_blocks < 1 || num_kv_heads < 1) return fail(PKV_EINVAL, "num_blocks and num_kv_heads must be >= 1");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !block_pairs) return fail(PKV_EINVAL, "NULL array argument");
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
+  if ((uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
+  return device_status(pkv::launch_block_copy(k_pool, v_pool, k_scale, v_scale, kv_dtype, block_pairs, num_pairs,
+                                              num_blocks, num_kv_heads, head_dim, (hipStream_t)stream),
+                       "kv_block_copy");
+}
+
+int h2o_select(const float* scores, int scores_stride, const int32_t* kv_lens, int num_seqs, int max_kv_len,
+               int budget, int recent, int32_t* keep_idx, int32_t* keep_count, void* stream) {
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (budget < 1) return fail(PKV_EINVAL, "budget %d < 1", budget);
+  if (recent < 0 || recent > budget) return fail(PKV_EINVAL, "recent %d outside [0, budget=%d]", recent, budget);
+  if (max_kv_len < 1) return fail(PKV_EINVAL, "max_kv_len %d < 1", max_kv_len);
+  if (scores_stride < max_kv_len) return fail(PKV_EINVAL, "scores_stride %d < max_kv_len %d", scores_stride, max_kv_len);
+  if (num_seqs == 0) return ok();
+  if (!scores || !kv_lens || !keep_idx || !keep_count) return fail(PKV_EINVAL, "NULL array argument");
+  if (num_seqs > (1 << 30)) return fail(PKV_EINVAL, "num_seqs too large");
+  return device_status(pkv::launch_h2o_select(scores, scores_stride, kv_lens, num_seqs, max_kv_len, budget, recent,
+                                              keep_idx, keep_count, (hipStream_t)stream),
+                       "h2o_select");
+}
+
+int pkv_timing_begin(int capacity) {
+  if (capacity < 1 || capacity > 100000) return fail(PKV_EINVAL, "capacity %d outside [1, 100000]", capacity);
+  if (g_timing.active) return fail(PKV_EINVAL, "a timing session is already open");
+  g_timing.ev.clear();
+  for (int i = 0; i < capacity; ++i) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e != hipSuccess) {
+      for (auto& p : g_timing.ev) {
+        (void)hipEventDestroy(p.first);
+        (void)hipEventDestroy(p.second);
+      }
+      g_timing.ev.clear();
+      return device_status(e, "hipEventCreate");
+    }
+    g_timing.ev.emplace_back(a, b);
+  }
+  g_timing.used = 0;
+  g_timing.active = true;
+  return ok();
+}
+
+int pkv_timing_end(float* ms_out, int capacity) {
+  if (!g_timing.active) {
+    fail(PKV_EINVAL, "no timing session open");
+    return -1;
+  }
+  g_timing.active = false;
+  int n = g_timing.used;
+  hipError_t e = hipSuccess;
+  if (n > 0) e = hipEventSynchronize(g_timing.ev[n - 1].second);
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_timing.ev[i].first, g_timing.ev[i].second);
+    if (ms_out && i < capacity) ms_out[i] = ms;
+  }
+  for (auto& p : g_timing.ev) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  g_timing.ev.clear();
+  g_timing.used = 0;
+  if (e != hipSuccess) {
+    device_status(e, "pkv_timing_end");
+    return -1;
+  }
+  ok();
+  return n < capacity ? n : capacity;
+}
+
+int pkv_probe_read(const void* src, size_t bytes, float* sink, void* stream) {
+  if (bytes % 16) return fail(PKV_EINVAL, "bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!src || !sink) return fail(PKV_EINVAL, "NULL array argument");
+  return device_status(pkv::launch_probe_read(src, bytes, sink, (hipStream_t)stream), "pkv_probe_read");
+}
+
+int pkv_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes % 16) return fail(PKV_EINVAL, "bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!src || !dst) return fail(PKV_EINVAL, "NULL array argument");
+  return device_status(pkv::launch_probe_copy(dst, src, bytes, (hipStream_t)stream), "pkv_probe_copy");
+}
+
+}  // extern "C"

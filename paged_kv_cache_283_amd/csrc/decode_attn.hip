@@ -1,0 +1,547 @@
+// Paged single-token decode attention for gfx950 (CDNA4).
+//
+// What is computed (page "长上下文优化：注意力稀疏化与 KV Cache 管理",
+// plumephp.com/llm-long-context-optimization: the MHA/GQA/MQA table and the
+// Flash sketch; page "KV Cache 与 PagedAttention：显存复用与长上下文推理",
+// plumephp.com/ai-kv-cache-paged-attention, "三大运行时组件": decode reads the
+// KV cache block by block through the block table):
+//   out[s][h] = sum_p softmax_p(scale * q[s][h] . K[p][h/G]) * V[p][h/G]
+// over the kept positions p of sequence s (geometry.hpp), plus, on request,
+// the H2O per-position mass (H2OEviction.update_scores in the first page):
+// the probabilities averaged over all query heads, added into a score row.
+//
+// How, on gfx950:
+//  * Work unit = (sequence, KV head, partition of 32 attended blocks).  One
+//    workgroup of 4 waves per unit; the waves take the partition's blocks
+//    round-robin and merge their softmax states through LDS at the end.  A
+//    second kernel merges partitions by log-sum-exp (skipped for sequences
+//    that fit one partition, whose workgroup writes the output directly).
+//  * Per 16-token block and wave, QK^T is one 16x16 MFMA tile: A = the block's
+//    K tile (row = token, 16-byte loads straight from the token-major pool
+//    tile), B = the GQA group's query rows (column = query head; the G <= 16
+//    rows of a group live in registers for the whole partition).  The
+//    accumulator gives lane (c, j) the logits of head c for tokens 4j..4j+3.
+//  * PV is a second MFMA per 16 head-dims: A = the dim-major V tile (lane
+//    (d, j) reads tokens 4j..4j+3 of dim d: one 8-byte load for bf16), B =
+//    the probabilities exactly as the QK accumulator left them in registers,
+//    so no LDS round trip or transpose sits between the two products.  The
+//    output accumulator again puts head c in lane column c, next to its
+//    running max and sum, so the online-softmax rescale is lane-local.
+//  * Probabilities are split into a high and a low 16-bit part and fed as two
+//    MFMAs, keeping ~16 mantissa bits; FP8 codes convert to bf16 exactly with
+//    the hardware converter, K's per-token scale multiplies the logit and V's
+//    multiplies the probability.
+//  * Logits are kept in base 2 (scale * log2 e folded in) and exponentiated
+//    with v_exp_f32.
+#include "device_common.hpp"
+#include "geometry.hpp"
+#include "launch.hpp"
+
+namespace pkv {
+
+namespace {
+
+template <int KVT>
+struct KvType {
+  static constexpr int kBytes = KVT == DT_F32 ? 4 : (KVT == DT_FP8 ? 1 : 2);
+  static constexpr bool kOp32 = KVT == DT_F32;   // fp32 MFMA operands
+  static constexpr bool kOpF16 = KVT == DT_F16;  // f16 MFMA operands (bf16 otherwise)
+};
+
+// Convert one float to the 16-bit MFMA operand type, and the residual.
+template <bool F16>
+__device__ __forceinline__ uint32_t to_op16(float f) {
+  if constexpr (F16) return f32_to_f16_bits(f);
+  else return f32_to_bf16_rne(f);
+}
+template <bool F16>
+__device__ __forceinline__ float from_op16(uint32_t b) {
+  if constexpr (F16) return f16_to_f32(b);
+  else return bf16_to_f32(b);
+}
+
+template <int QT>
+__device__ __forceinline__ float load_q_elem(const void* q, size_t idx) {
+  if constexpr (QT == DT_F32) return reinterpret_cast<const float*>(q)[idx];
+  else if constexpr (QT == DT_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(q)[idx]);
+  else return f16_to_f32(reinterpret_cast<const uint16_t*>(q)[idx]);
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_k32(const uint32_t* a, const uint32_t* b, f32x4 c) {
+  u32x4 av = {a[0], a[1], a[2], a[3]};
+  u32x4 bv = {b[0], b[1], b[2], b[3]};
+  if constexpr (F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, av), __builtin_bit_cast(f16x8, bv), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv), c, 0, 0, 0);
+  }
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma_k16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+  u32x2 av = {a0, a1};
+  u32x2 bv = {b0, b1};
+  if constexpr (F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av), __builtin_bit_cast(f16x4, bv), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, av), __builtin_bit_cast(s16x4, bv), c, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+// One workgroup = 4 waves = one (sequence, KV head, partition).
+template <int KVT, int QT, int D>
+__global__ void __launch_bounds__(256) attn_partition_kernel(const AttnArgs a) {
+  using KT = KvType<KVT>;
+  constexpr int EB = KT::kBytes;
+  constexpr bool OP32 = KT::kOp32;
+  constexpr bool F16 = KT::kOpF16;
+  constexpr int DPL = D / 4;              // QK contraction dims held per lane
+  constexpr int KW = DPL * EB / 4;        // K words per lane per block
+  constexpr int NT = D / 16;              // 16-dim output tiles
+  constexpr int VW = EB;                  // V words per lane per tile (4 tokens)
+  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16));
+  constexpr bool QSPLIT = (!OP32) && !QSAME;
+  constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
+
+  const int s = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int part = blockIdx.x;
+  const int hq = a.num_q_heads;
+  const int group = hq / a.num_kv_heads;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;                // MFMA row/column inside a 16x16 tile
+  const int j = lane >> 4;                // which 4-token / 1/4-of-dims slice
+  const int L = a.context_lens[s];
+  const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
+
+  if (L < 1 || L > len_cap) {
+    // Unusable length: poison this KV head's outputs once, touch nothing else.
+    if (part == 0) {
+      for (int idx = threadIdx.x; idx < group * D; idx += blockDim.x) {
+        const size_t hs = (size_t)s * hq + (size_t)kvh * group + idx / D;
+        store_out(a.out, hs * D + idx % D, a.out_dtype, __builtin_nanf(""));
+      }
+    }
+    return;
+  }
+  const KeepGeom geo = keep_geometry(L, a.num_sinks, a.window);
+  const int vb0 = part * kPartBlocks;
+  if (vb0 >= geo.n_virtual) return;
+  const int vb1 = min(vb0 + kPartBlocks, geo.n_virtual);
+  const int nparts = num_partitions(geo.n_virtual);
+  const int keep_lo = a.window > 0 ? L - a.window : 0;   // p >= keep_lo is kept
+  const int sinks = a.window > 0 ? a.num_sinks : 0;      // p < sinks is kept
+
+  // ---- the group's query rows as the QK B operand (column c = query head) ----
+  const int head = kvh * group + c;
+  const bool head_ok = c < group;
+  uint32_t qhi[QW];
+  uint32_t qlo[QSPLIT ? QW : 1];
+  float qf[OP32 ? DPL : 1];
+  {
+    const size_t qbase = ((size_t)s * hq + (head_ok ? head : 0)) * D + (size_t)j * DPL;
+    if constexpr (OP32) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) qf[e] = head_ok ? load_q_elem<QT>(a.q, qbase + e) : 0.f;
+    } else if constexpr (QSAME) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qbase);
+#pragma unroll
+      for (int w = 0; w < QW / 4; ++w) {
+        u32x4 v = head_ok ? src[w] : u32x4{0, 0, 0, 0};
+        qhi[4 * w + 0] = v[0]; qhi[4 * w + 1] = v[1]; qhi[4 * w + 2] = v[2]; qhi[4 * w + 3] = v[3];
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < QW; ++w) {
+        float f0 = head_ok ? load_q_elem<QT>(a.q, qbase + 2 * w) : 0.f;
+        float f1 = head_ok ? load_q_elem<QT>(a.q, qbase + 2 * w + 1) : 0.f;
+        uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
+        uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
+        uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
+        qhi[w] = h0 | (h1 << 16);
+        qlo[w] = l0 | (l1 << 16);
+      }
+    }
+  }
+
+  float m_run = -INFINITY;   // running max of this head's base-2 logits (same in all 4 rows)
+  float l_run = 0.f;         // this lane's share of the exp-sum
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
+  const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
+
+  for (int vb = vb0 + wave; vb < vb1; vb += kPartWaves) {
+    const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
+    const int phys = trow[lb];
+    if (phys < 0 || phys >= a.num_blocks) { bad = true; continue; }
+    const size_t tile = (size_t)phys * a.num_kv_heads + kvh;
+
+    // ---- loads: K row slice (token c, dims j*DPL..), V^T slices (dim c of each tile, tokens 4j..4j+3)
+    uint32_t kr[KW];
+    {
+      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (tile * kBlockSize + c) * (size_t)(D * EB) +
+                                                       (size_t)j * (DPL * EB));
+#pragma unroll
+      for (int w = 0; w < KW / 4; ++w) {
+        u32x4 v = kp[w];
+        kr[4 * w + 0] = v[0]; kr[4 * w + 1] = v[1]; kr[4 * w + 2] = v[2]; kr[4 * w + 3] = v[3];
+      }
+    }
+    uint32_t vr[NT][VW];
+    {
+      const uint8_t* vp = vbase + (tile * D + c) * (size_t)(kBlockSize * EB) + (size_t)j * (4 * EB);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint8_t* p = vp + (size_t)t * 16 * kBlockSize * EB;
+        if constexpr (VW == 1) {
+          vr[t][0] = *reinterpret_cast<const uint32_t*>(p);
+        } else if constexpr (VW == 2) {
+          u32x2 v = *reinterpret_cast<const u32x2*>(p);
+          vr[t][0] = v[0]; vr[t][1] = v[1];
+        } else {
+          u32x4 v = *reinterpret_cast<const u32x4*>(p);
+          vr[t][0] = v[0]; vr[t][1] = v[1]; vr[t][2] = v[2]; vr[t][3] = v[3];
+        }
+      }
+    }
+    f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (KVT == DT_FP8) {
+      ksc = *reinterpret_cast<const f32x4*>(a.k_scale + tile * kBlockSize + 4 * j);
+      vsc = *reinterpret_cast<const f32x4*>(a.v_scale + tile * kBlockSize + 4 * j);
+    }
+
+    // ---- S = K q^T: lane (c, j) receives head c's logits of tokens 4j..4j+3
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (OP32) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sacc = mfma_f32_k4(__uint_as_float(kr[e]), qf[e], sacc);
+    } else {
+#pragma unroll
+      for (int st = 0; st < DPL / 8; ++st) {
+        uint32_t av[4];
+        if constexpr (KVT == DT_FP8) {
+          fp8x4_to_bf16x4(kr[2 * st], av[0], av[1]);
+          fp8x4_to_bf16x4(kr[2 * st + 1], av[2], av[3]);
+        } else {
+          av[0] = kr[4 * st]; av[1] = kr[4 * st + 1]; av[2] = kr[4 * st + 2]; av[3] = kr[4 * st + 3];
+        }
+        sacc = mfma_k32<F16>(av, &qhi[4 * st], sacc);
+        if constexpr (QSPLIT) sacc = mfma_k32<F16>(av, &qlo[4 * st], sacc);
+      }
+    }
+
+    // ---- mask, online softmax (base 2)
+    const int p0 = lb * kBlockSize + 4 * j;
+    const int blk0 = lb * kBlockSize;
+    const bool full = (blk0 + kBlockSize <= L) && (blk0 + kBlockSize <= sinks || blk0 >= keep_lo);
+    float x[4];
+    bool valid[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + i;
+      valid[i] = p < L && (p < sinks || p >= keep_lo);
+      float z = sacc[i] * a.scale_log2;
+      if constexpr (KVT == DT_FP8) z *= ksc[i];
+      x[i] = valid[i] ? z : -INFINITY;
+    }
+    const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const float m_new = fmaxf(m_run, mb);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? fast_exp2(m_run - m_new) : 1.f;
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = live ? fast_exp2(x[i] - m_new) : 0.f;
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+
+    if (a.stash != nullptr && head_ok) {
+      f32x4 xv = {x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(a.stash + ((size_t)s * hq + head) * a.nv_pad + (size_t)vb * kBlockSize + 4 * j) = xv;
+    }
+
+    // ---- probabilities as the PV B operand (V's FP8 scale folded in)
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (KVT == DT_FP8) pv[i] = valid[i] ? pr[i] * vsc[i] : 0.f;
+      else pv[i] = pr[i];
+    }
+    if (!full) {
+      // Slots outside the keep-set may hold anything (NaN included): zero their V.
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (VW == 1) {
+          const uint32_t msk = (valid[0] ? 0xffu : 0u) | (valid[1] ? 0xff00u : 0u) |
+                               (valid[2] ? 0xff0000u : 0u) | (valid[3] ? 0xff000000u : 0u);
+          vr[t][0] &= msk;
+        } else if constexpr (VW == 2) {
+          vr[t][0] &= (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+          vr[t][1] &= (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vr[t][i] = valid[i] ? vr[t][i] : 0u;
+        }
+      }
+    }
+
+    // ---- O^T += V^T P^T: lane (c, j) accumulates head c, dims 16t + 4j + i
+    if constexpr (OP32) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t] = mfma_f32_k4(__uint_as_float(vr[t][r]), pv[r], acc[t]);
+      }
+    } else {
+      uint32_t ph[2], pl[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
+        uint32_t h0, h1;
+        if constexpr (F16) {
+          h0 = f32_to_f16_bits(f0);
+          h1 = f32_to_f16_bits(f1);
+        } else {
+          h0 = __float_as_uint(f0) >> 16;           // truncated high part
+          h1 = __float_as_uint(f1) >> 16;
+        }
+        const float r0 = f0 - from_op16<F16>(h0);
+        const float r1 = f1 - from_op16<F16>(h1);
+        uint32_t l0, l1;
+        if constexpr (F16) {
+          l0 = f32_to_f16_bits(r0);
+          l1 = f32_to_f16_bits(r1);
+        } else {
+          l0 = __float_as_uint(r0) >> 16;
+          l1 = __float_as_uint(r1) >> 16;
+        }
+        ph[w] = h0 | (h1 << 16);
+        pl[w] = l0 | (l1 << 16);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint32_t v0, v1;
+        if constexpr (KVT == DT_FP8) {
+          fp8x4_to_bf16x4(vr[t][0], v0, v1);
+        } else {
+          v0 = vr[t][0];
+          v1 = vr[t][1];
+        }
+        acc[t] = mfma_k16<F16>(v0, v1, ph[0], ph[1], acc[t]);
+        acc[t] = mfma_k16<F16>(v0, v1, pl[0], pl[1], acc[t]);
+      }
+    }
+  }
+
+  l_run = row_sum4(l_run);
+
+  // ---- merge the 4 waves' states through LDS
+  extern __shared__ float smem[];
+  float* s_acc = smem;                                  // [4][group][D]
+  float* s_ml = smem + kPartWaves * group * D;          // [4][group][2]
+  if (head_ok) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_acc[(wave * group + c) * D + 16 * t + 4 * j + i] = acc[t][i];
+    }
+    if (j == 0) {
+      s_ml[(wave * group + c) * 2 + 0] = m_run;
+      s_ml[(wave * group + c) * 2 + 1] = l_run;
+    }
+  }
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+
+  for (int idx = threadIdx.x; idx < group * D; idx += blockDim.x) {
+    const int cc = idx / D, d = idx % D;
+    float mw[kPartWaves];
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kPartWaves; ++w) {
+      mw[w] = s_ml[(w * group + cc) * 2];
+      M = fmaxf(M, mw[w]);
+    }
+    float lsum = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kPartWaves; ++w) {
+      const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+      lsum += f * s_ml[(w * group + cc) * 2 + 1];
+      o += f * s_acc[(w * group + cc) * D + d];
+    }
+    if (any_bad) lsum = __builtin_nanf("");
+    const size_t hs = (size_t)s * hq + (size_t)kvh * group + cc;
+    if (nparts == 1) {
+      store_out(a.out, hs * D + d, a.out_dtype, o / lsum);
+      if (d == 0 && a.fin_ml != nullptr) {
+        a.fin_ml[hs * 2 + 0] = M;
+        a.fin_ml[hs * 2 + 1] = lsum;
+      }
+    } else {
+      const size_t pi = hs * a.p_max + part;
+      a.part_acc[pi * D + d] = o;
+      if (d == 0) {
+        a.part_ml[pi * 2 + 0] = M;
+        a.part_ml[pi * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head) per wave.
+template <int D>
+__global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
+  const int s = blockIdx.y;
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= a.num_q_heads) return;
+  const int L = a.context_lens[s];
+  const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
+  if (L < 1 || L > len_cap) return;                 // the partition kernel wrote NaN
+  const int nparts = num_partitions(keep_geometry(L, a.num_sinks, a.window).n_virtual);
+  if (nparts <= 1) return;                          // written by the partition kernel
+  const size_t hs = (size_t)s * a.num_q_heads + h;
+  const float* ml = a.part_ml + hs * a.p_max * 2;
+  float M = -INFINITY;
+  for (int i = 0; i < nparts; ++i) M = fmaxf(M, ml[2 * i]);
+  constexpr int DL = D / 64;
+  float o[DL];
+#pragma unroll
+  for (int e = 0; e < DL; ++e) o[e] = 0.f;
+  float lsum = 0.f;
+  const float* pacc = a.part_acc + hs * a.p_max * D;
+  for (int i = 0; i < nparts; ++i) {
+    const float mi = ml[2 * i];
+    const float f = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+    lsum += f * ml[2 * i + 1];
+#pragma unroll
+    for (int e = 0; e < DL; ++e) o[e] += f * pacc[(size_t)i * D + e * 64 + lane];
+  }
+#pragma unroll
+  for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + e * 64 + lane, a.out_dtype, o[e] / lsum);
+  if (a.fin_ml != nullptr && lane == 0) {
+    a.fin_ml[hs * 2 + 0] = M;
+    a.fin_ml[hs * 2 + 1] = lsum;
+  }
+}
+
+// H2O mass: scores[s][p] += mean over query heads of exp2(x - M_h) / l_h, kept p only.
+__global__ void __launch_bounds__(256) attn_mass_kernel(const AttnArgs a) {
+  const int s = blockIdx.y;
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;   // attended (virtual) position
+  const int L = a.context_lens[s];
+  const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
+  if (L < 1 || L > len_cap) return;
+  const KeepGeom geo = keep_geometry(L, a.num_sinks, a.window);
+  if (v >= geo.n_virtual * kBlockSize) return;
+  const int p = logical_block(v / kBlockSize, geo.n_sink_blocks, geo.win_start) * kBlockSize + v % kBlockSize;
+  if (!is_kept(p, L, a.num_sinks, a.window)) return;
+  const int hq = a.num_q_heads;
+  float sum = 0.f;
+  for (int h = 0; h < hq; ++h) {
+    const size_t hs = (size_t)s * hq + h;
+    const float x = a.stash[hs * a.nv_pad + v];
+    sum += fast_exp2(x - a.fin_ml[hs * 2]) / a.fin_ml[hs * 2 + 1];
+  }
+  a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
+}
+
+namespace {
+
+template <int KVT, int QT, int D>
+hipError_t launch_partition(const AttnArgs& a, hipStream_t st) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const size_t smem = (size_t)kPartWaves * group * (D + 2) * sizeof(float);
+  dim3 grid(a.p_max, a.num_kv_heads, a.num_seqs);
+  hipLaunchKernelGGL((attn_partition_kernel<KVT, QT, D>), grid, dim3(256), smem, st, a);
+  return hipGetLastError();
+}
+
+template <int KVT, int QT>
+hipError_t dispatch_d(const AttnArgs& a, int d, hipStream_t st) {
+  return d == 64 ? launch_partition<KVT, QT, 64>(a, st) : launch_partition<KVT, QT, 128>(a, st);
+}
+
+template <int KVT>
+hipError_t dispatch_q(const AttnArgs& a, int q_dtype, int d, hipStream_t st) {
+  switch (q_dtype) {
+    case DT_F32: return dispatch_d<KVT, DT_F32>(a, d, st);
+    case DT_BF16: return dispatch_d<KVT, DT_BF16>(a, d, st);
+    default: return dispatch_d<KVT, DT_F16>(a, d, st);
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                      int num_sinks, int window, bool want_mass) {
+  WorkspaceLayout w{};
+  const int nv = max_virtual_blocks(max_context_len, num_sinks, window);
+  w.p_max = num_partitions(nv);
+  w.nv_pad = nv * kBlockSize;
+  const size_t bh = (size_t)num_seqs * num_q_heads;
+  size_t off = 0;
+  w.acc_off = off;
+  off = align256(off + bh * w.p_max * head_dim * sizeof(float));
+  w.ml_off = off;
+  off = align256(off + bh * w.p_max * 2 * sizeof(float));
+  if (want_mass) {
+    w.stash_off = off;
+    off = align256(off + bh * w.nv_pad * sizeof(float));
+    w.fin_off = off;
+    off = align256(off + bh * 2 * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int head_dim,
+                              hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (a.num_seqs == 0) return hipSuccess;
+  hipError_t err;
+  if (ev_begin) {
+    err = hipEventRecord(ev_begin, st);
+    if (err != hipSuccess) return err;
+  }
+  switch (kv_dtype) {
+    case DT_F32: err = dispatch_q<DT_F32>(a, q_dtype, head_dim, st); break;
+    case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st); break;
+    case DT_F16: err = dispatch_q<DT_F16>(a, q_dtype, head_dim, st); break;
+    default: err = dispatch_q<DT_FP8>(a, q_dtype, head_dim, st); break;
+  }
+  if (err != hipSuccess) return err;
+  if (ev_end) {
+    err = hipEventRecord(ev_end, st);
+    if (err != hipSuccess) return err;
+  }
+  if (a.p_max > 1) {
+    dim3 grid((a.num_q_heads + 3) / 4, a.num_seqs);
+    if (head_dim == 64) hipLaunchKernelGGL((attn_reduce_kernel<64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_reduce_kernel<128>), grid, dim3(256), 0, st, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.attn_mass != nullptr) {
+    dim3 grid((a.nv_pad + 255) / 256, a.num_seqs);
+    hipLaunchKernelGGL(attn_mass_kernel, grid, dim3(256), 0, st, a);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
+}  // namespace pkv

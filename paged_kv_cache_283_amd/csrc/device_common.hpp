@@ -1,0 +1,89 @@
+// Device-side helpers shared by the gfx950 kernels: dtype codes, vector types,
+// storage conversions and the wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "geometry.hpp"
+
+namespace pkv {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3 };
+
+constexpr int kWave = 64;          // CDNA wavefront width
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Element e (0/1) of a word holding two 16-bit values.
+__device__ __forceinline__ uint32_t half_word(uint32_t w, int e) { return e ? (w >> 16) : (w & 0xffffu); }
+
+// Four OCP E4M3FN codes (one word) -> four bf16 values (two words), exactly:
+// every E4M3 value is representable in bf16, so the upper half of the fp32
+// conversion is the bf16 encoding.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  lo = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+  hi = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+}
+
+// Wave64 butterfly reductions over lanes that differ in bits 4 and 5 of the
+// lane id (the four 16-lane rows of an MFMA accumulator).
+__device__ __forceinline__ float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  x = fmaxf(x, __shfl_xor(x, 32, kWave));
+  return x;
+}
+__device__ __forceinline__ float row_sum4(float x) {
+  x += __shfl_xor(x, 16, kWave);
+  x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Logical block of virtual (attended) block vb: sink blocks first, then the window.
+__device__ __forceinline__ int logical_block(int vb, int n_sink_blocks, int win_start) {
+  return vb < n_sink_blocks ? vb : win_start + (vb - n_sink_blocks);
+}
+
+// Store one float of an output row in the requested dtype.
+__device__ __forceinline__ void store_out(void* out, size_t idx, int dtype, float v) {
+  if (dtype == DT_F32) {
+    reinterpret_cast<float*>(out)[idx] = v;
+  } else if (dtype == DT_BF16) {
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_bf16_rne(v);
+  } else {
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)f32_to_f16_bits(v);
+  }
+}
+
+}  // namespace pkv

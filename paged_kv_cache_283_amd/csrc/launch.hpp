@@ -1,0 +1,70 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Arguments arrive here already validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AttnArgs {
+  void* out;
+  int out_dtype;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  int table_stride;
+  const int32_t* context_lens;
+  int max_context_len;
+  int num_seqs, num_blocks, num_q_heads, num_kv_heads;
+  float scale_log2;     // softmax scale * log2(e): logits are kept in base 2
+  int num_sinks, window;
+  float* attn_mass;
+  int mass_stride;
+  // workspace views
+  float* part_acc;      // [B][Hq][p_max][D]   unnormalised partial outputs
+  float* part_ml;       // [B][Hq][p_max][2]   partition max (base-2) and exp-sum
+  float* stash;         // [B][Hq][nv_pad]     base-2 logits per attended position (mass only)
+  float* fin_ml;        // [B][Hq][2]          global max and exp-sum (mass only)
+  int p_max;
+  int nv_pad;
+};
+
+struct WorkspaceLayout {
+  size_t acc_off, ml_off, stash_off, fin_off, total;
+  int p_max, nv_pad;
+};
+
+WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                      int num_sinks, int window, bool want_mass);
+
+hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int head_dim,
+                              hipStream_t stream, hipEvent_t ev_main_begin, hipEvent_t ev_main_end);
+
+hipError_t launch_decode_slots(const int32_t* tables, int stride, const int32_t* lens, int num_seqs,
+                               int num_blocks, int64_t* slots, hipStream_t stream);
+
+hipError_t launch_token_slots(const int32_t* tables, int stride, int num_seqs, const int32_t* seq_ids,
+                              const int32_t* positions, int num_tokens, int num_blocks, int64_t* slots,
+                              hipStream_t stream);
+
+hipError_t launch_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool,
+                           float* k_scale, float* v_scale, int kv_dtype, const int64_t* slots,
+                           int num_tokens, int num_blocks, int num_kv_heads, int head_dim, hipStream_t stream);
+
+hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+                             const int32_t* pairs, int num_pairs, int num_blocks, int num_kv_heads,
+                             int head_dim, hipStream_t stream);
+
+hipError_t launch_h2o_select(const float* scores, int stride, const int32_t* lens, int num_seqs,
+                             int max_len, int budget, int recent, int32_t* keep_idx, int32_t* keep_count,
+                             hipStream_t stream);
+
+hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
+hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,241 @@
+"""Python binding of the C ABI: torch tensors in, device pointers and the current HIP stream out.
+
+Argument marshalling only -- every step of the decode path runs in the gfx950
+kernels of libpagedkv.so.  Function names and argument meanings are those of
+include/pagedkv.h; shapes are read off the tensors.
+
+Storage dtypes: torch.float32 / bfloat16 / float16 pools hold those values;
+torch.uint8 or torch.float8_e4m3fn pools hold OCP E4M3FN codes with
+float32 scale tensors [num_blocks][num_kv_heads][16].
+"""
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+BLOCK_SIZE = 16
+
+_FLOAT_CODES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}
+
+
+def _fp8_dtypes():
+    out = {torch.uint8}
+    if hasattr(torch, "float8_e4m3fn"):
+        out.add(torch.float8_e4m3fn)
+    return out
+
+
+def float_code(dtype: torch.dtype) -> int:
+    try:
+        return _FLOAT_CODES[dtype]
+    except KeyError:
+        raise TypeError(f"expected float32, bfloat16 or float16, got {dtype}") from None
+
+
+def kv_code(dtype: torch.dtype) -> int:
+    if dtype in _fp8_dtypes():
+        return _lib.FP8_E4M3
+    return float_code(dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the HIP library must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the HIP library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Prepared:
+    """A library call with every argument already marshalled: calling it re-issues the same
+    launch on the same stream (for benchmark and serving loops that repeat a step)."""
+
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name, args):
+        self.name = name
+        self.fn = getattr(_lib.load(), name)
+        self.args = tuple(args)
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != _lib.OK:
+            _lib.check(self.name, status)
+
+
+def _issue(name, args, prepare):
+    if prepare:
+        return Prepared(name, args)
+    _lib.call(name, *args)
+    return None
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def paged_decode_slots(block_tables, context_lens, num_blocks, slot_mapping=None, stream=None, prepare=False):
+    """int64 slot of every sequence's newest token (position context_lens - 1); -1 where unusable."""
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    b = context_lens.shape[0]
+    if slot_mapping is None:
+        slot_mapping = torch.empty(b, dtype=torch.int64, device=context_lens.device)
+    p = _issue("paged_decode_slots", (_ptr(block_tables), block_tables.shape[1], _ptr(context_lens), b,
+                                      int(num_blocks), BLOCK_SIZE, _ptr(slot_mapping), _stream(stream)), prepare)
+    return p if prepare else slot_mapping
+
+
+def paged_token_slots(block_tables, seq_ids, positions, num_blocks, slot_mapping=None, stream=None):
+    """int64 slots of (seq_ids[t], positions[t]) tokens; -1 where unusable."""
+    _need(block_tables, torch.int32, "block_tables")
+    _need(seq_ids, torch.int32, "seq_ids")
+    _need(positions, torch.int32, "positions")
+    t = seq_ids.shape[0]
+    if positions.shape[0] != t:
+        raise ValueError("seq_ids and positions must have the same length")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(t, dtype=torch.int64, device=seq_ids.device)
+    _lib.call("paged_token_slots", _ptr(block_tables), block_tables.shape[1], block_tables.shape[0],
+              _ptr(seq_ids), _ptr(positions), t, int(num_blocks), BLOCK_SIZE, _ptr(slot_mapping), _stream(stream))
+    return slot_mapping
+
+
+def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_scale=None, stream=None,
+                   prepare=False):
+    """Store [T][Hkv][D] new K/V rows at their slots (FP8 pools quantise per row)."""
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    t, hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must match")
+    nb = k_pool.shape[0]
+    if tuple(k_pool.shape) != (nb, hkv, BLOCK_SIZE, d) or tuple(v_pool.shape) != (nb, hkv, d, BLOCK_SIZE):
+        raise ValueError(f"pools must be [NB][{hkv}][16][{d}] (K) and [NB][{hkv}][{d}][16] (V)")
+    if slot_mapping.shape[0] != t:
+        raise ValueError("slot_mapping must have one entry per token")
+    return _issue("paged_kv_write", (_ptr(k_new), _ptr(v_new), float_code(k_new.dtype), _ptr(k_pool),
+                                     _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
+                                     _ptr(slot_mapping), t, nb, hkv, d, BLOCK_SIZE, _stream(stream)), prepare)
+
+
+def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, device="cuda", fill_byte=None):
+    """(k_pool, v_pool, k_scale, v_scale) in the library's layout; scales are None unless kv_dtype is FP8
+    (torch.uint8 or torch.float8_e4m3fn).  fill_byte sets every byte (0xFF = NaN everywhere)."""
+    k = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), dtype=kv_dtype, device=device)
+    v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=kv_dtype, device=device)
+    ks = vs = None
+    if kv_code(kv_dtype) == _lib.FP8_E4M3:
+        ks = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)
+        vs = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)
+    if fill_byte is not None:
+        for t in (k, v, ks, vs):
+            if t is not None:
+                t.view(torch.uint8).fill_(fill_byte)
+    return k, v, ks, vs
+
+
+def write_positions(block_tables, seq_ids, positions, k_rows, v_rows, k_pool, v_pool, k_scale=None, v_scale=None,
+                    stream=None):
+    """Prefill-style write: token t = (seq_ids[t], positions[t]) with rows k_rows[t], v_rows[t]
+    (slots looked up on the GPU, then one cache write)."""
+    slots = paged_token_slots(block_tables, seq_ids, positions, k_pool.shape[0], stream=stream)
+    paged_kv_write(k_rows, v_rows, k_pool, v_pool, slots, k_scale, v_scale, stream=stream)
+    return slots
+
+
+def workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, num_sinks=0, window=0, want_mass=False):
+    return int(_lib.load().paged_decode_attn_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                             num_sinks, window, int(bool(want_mass))))
+
+
+def alloc_workspace(num_seqs, num_q_heads, head_dim, max_context_len, num_sinks=0, window=0,
+                    want_mass=False, device="cuda"):
+    n = workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, num_sinks, window, want_mass)
+    # torch's caching allocator returns 256-byte aligned blocks.
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
+                      k_scale=None, v_scale=None, num_sinks=0, window=0, attn_mass=None, workspace=None,
+                      stream=None, prepare=False):
+    """Decode attention of q [B][Hq][D] over the paged pools into out [B][Hq][D].
+
+    attn_mass (float32 [B][>= max_context_len]) receives += the H2O mass of the kept positions.
+    """
+    b, hq, d = q.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    if tuple(out.shape) != (b, hq, d):
+        raise ValueError("out must have q's shape")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mass_stride = 0
+    if attn_mass is not None:
+        _need(attn_mass, torch.float32, "attn_mass")
+        mass_stride = attn_mass.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(b, hq, d, max_context_len, num_sinks, window, attn_mass is not None, q.device)
+    args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
+            _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), int(max_context_len), b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), int(num_sinks),
+            int(window), _ptr(attn_mass), mass_stride, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    p = _issue("paged_decode_attn", args, prepare)
+    return p if prepare else out
+
+
+def kv_block_copy(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None, stream=None):
+    """Copy whole blocks per int32 [n][2] {src, dst} pair (the data half of copy-on-write)."""
+    _need(block_pairs, torch.int32, "block_pairs")
+    nb, hkv, _, d = k_pool.shape
+    _lib.call("kv_block_copy", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
+              _ptr(block_pairs), block_pairs.shape[0], nb, hkv, d, BLOCK_SIZE, _stream(stream))
+
+
+def h2o_select(scores, kv_lens, max_kv_len, budget, recent, keep_idx=None, keep_count=None, stream=None):
+    """H2O keep-set per sequence: (keep_idx int32 [B][budget] ascending, -1 padded; keep_count int32 [B])."""
+    _need(scores, torch.float32, "scores")
+    _need(kv_lens, torch.int32, "kv_lens")
+    b = kv_lens.shape[0]
+    if keep_idx is None:
+        keep_idx = torch.empty((b, budget), dtype=torch.int32, device=scores.device)
+    if keep_count is None:
+        keep_count = torch.empty(b, dtype=torch.int32, device=scores.device)
+    _lib.call("h2o_select", _ptr(scores), scores.shape[1], _ptr(kv_lens), b, int(max_kv_len), int(budget),
+              int(recent), _ptr(keep_idx), _ptr(keep_count), _stream(stream))
+    return keep_idx, keep_count
+
+
+def timing_begin(capacity):
+    _lib.call("pkv_timing_begin", int(capacity))
+
+
+def timing_end(capacity):
+    buf = (ctypes.c_float * capacity)()
+    n = _lib.load().pkv_timing_end(buf, capacity)
+    if n < 0:
+        _lib.check("pkv_timing_end", _lib.EDEVICE)
+    return [buf[i] for i in range(n)]
+
+
+def probe_read(src, sink, stream=None):
+    _lib.call("pkv_probe_read", _ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream))
+
+
+def probe_copy(dst, src, stream=None):
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst smaller than src")
+    _lib.call("pkv_probe_copy", _ptr(dst), _ptr(src), n, _stream(stream))
