@@ -23,11 +23,11 @@ if torch.cuda.is_available():
 TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "fp8": 1e-2}
 
 
-def _case_workload(kv, q, d, hq, hkv, seed, **kw):
+def _case_workload(kv, q, d, hq, hkv, seed, lens=(35, 70), **kw):
     src = "bf16" if kv == "fp8" else kv
     return dataclasses.replace(W.WORKLOADS["tiny"], name=f"t-{kv}-{q}-{d}", kv_dtype=kv, src_dtype=src, q_dtype=q,
                                head_dim=d, num_q_heads=hq, num_kv_heads=hkv, seed=seed, pool_blocks=None,
-                               extra_blocks=3, **kw)
+                               extra_blocks=3, lens=tuple(lens), num_seqs=len(lens), **kw)
 
 
 def _max_err(case, out, **kw):
@@ -74,7 +74,7 @@ def test_decode_and_token_slots_match_oracle():
 @pytest.mark.parametrize("kv,src,d", [("f32", "f32", 64), ("bf16", "bf16", 128), ("f16", "f16", 128),
                                       ("fp8", "bf16", 128), ("fp8", "f32", 64), ("fp8", "f16", 128)])
 def test_write_pool_bytes_bit_exact(kv, src, d):
-    w = dataclasses.replace(_case_workload(kv, "bf16", d, 8, 2, 91), src_dtype=src, lens=(35, 70, 16, 1))
+    w = dataclasses.replace(_case_workload(kv, "bf16", d, 8, 2, 91, lens=(35, 70, 16, 1)), src_dtype=src)
     case = H.Case(w)
     lay = case.lay
     # oracle pools: all bytes 0xFF, then the same tokens written by the oracle's own slot arithmetic

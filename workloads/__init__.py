@@ -105,6 +105,8 @@ def make_layout(w: Workload, lens=None, page_tables=None) -> Layout:
     rng = np.random.default_rng(w.seed)
     lens = lengths(w, rng) if lens is None else np.asarray(lens, dtype=np.int32)
     b = lens.shape[0]
+    if b != w.num_seqs:
+        raise ValueError(f"{b} lengths for a workload of {w.num_seqs} sequences")
     nblk = [-(-int(n) // BLOCK) for n in lens]
     width = w.table_width or max(nblk)
     mapped = []
