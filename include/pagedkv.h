@@ -28,8 +28,10 @@
  *
  * KV pool layout (one pool per layer; block_size is 16, [PA] "PagedAttention 的设计")
  * ---------------------------------------------------------------------------------
- *   k_pool  [num_blocks][num_kv_heads][16][head_dim]   token-major tile
- *   v_pool  [num_blocks][num_kv_heads][head_dim][16]   dim-major tile
+ *   k_pool  [num_blocks][num_kv_heads][head_dim/X][16][X]   K tile in 16-byte chunks:
+ *           X = 16 / element bytes (8 for BF16/F16, 16 for FP8, 4 for F32); element
+ *           (token o, dim d) of a tile is at [d / X][o][d % X]
+ *   v_pool  [num_blocks][num_kv_heads][head_dim][16]        dim-major tile
  *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 only)
  * A token at logical position p of a sequence lives in physical block
  * table[p / 16] at offset p % 16 ([PA] "物理布局示意", [LC] block-table sketch);

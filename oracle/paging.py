@@ -11,9 +11,12 @@ names at index j; physical blocks come from one shared pool.  What they leave
 open and is taken here as the storage convention (the same one the HIP
 library documents):
 
-  K pool  [num_blocks][num_kv_heads][16][head_dim]   token-major tile
-  V pool  [num_blocks][num_kv_heads][head_dim][16]   dim-major tile
-  scales  [num_blocks][num_kv_heads][16] float32     FP8 only, K and V separately
+  K pool  [num_blocks][num_kv_heads][head_dim/X][16][X]   X = 16 bytes of elements:
+                                                         8 for bf16/f16, 16 for fp8, 4 for f32
+  V pool  [num_blocks][num_kv_heads][head_dim][16]        dim-major tile
+  scales  [num_blocks][num_kv_heads][16] float32          FP8 only, K and V separately
+
+(K element (token o, dim d) of a block tile sits at chunk d // X, row o, lane d % X.)
 
 Storage dtypes are held here as raw numpy arrays: "f32" float32, "bf16" uint16
 bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes.
@@ -30,6 +33,11 @@ _STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "fp8": np.u
 
 def storage_dtype(kv_dtype: str):
     return _STORAGE[kv_dtype]
+
+
+def k_chunk(kv_dtype: str) -> int:
+    """Elements per 16-byte K chunk."""
+    return 16 // np.dtype(_STORAGE[kv_dtype]).itemsize
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -66,7 +74,8 @@ def slot(table_row, pos: int, num_blocks: int, block_size: int = BLOCK_SIZE) -> 
 def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, fill=0):
     """Allocate (k_pool, v_pool, k_scale, v_scale) in the documented layout; scales None unless fp8."""
     st = storage_dtype(kv_dtype)
-    k = np.full((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), fill, dtype=st)
+    x = k_chunk(kv_dtype)
+    k = np.full((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x), fill, dtype=st)
     v = np.full((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), fill, dtype=st)
     if kv_dtype == "fp8":
         ks = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
@@ -86,7 +95,7 @@ def write_tokens(pools, kv_dtype: str, k_src, v_src, src_dtype: str, table_rows,
     scale (fp8.quantize_per_token).  Mutates pools in place.
     """
     k_pool, v_pool, k_scale, v_scale = pools
-    nb = k_pool.shape[0]
+    nb, hkv, nc, _, x = k_pool.shape
     if kv_dtype == "fp8":
         if src_dtype == "fp8":
             raise ValueError("fp8 pools take f32/bf16/f16 sources")
@@ -98,12 +107,12 @@ def write_tokens(pools, kv_dtype: str, k_src, v_src, src_dtype: str, table_rows,
         b = physical_block(table_rows[s], p, nb)
         o = p % BLOCK_SIZE
         if kv_dtype == "fp8":
-            k_pool[b, :, o, :] = kq[t]
+            k_pool[b, :, :, o, :] = kq[t].reshape(hkv, nc, x)
             v_pool[b, :, :, o] = vq[t]
             k_scale[b, :, o] = ks[t]
             v_scale[b, :, o] = vs[t]
         else:
-            k_pool[b, :, o, :] = k_src[t]
+            k_pool[b, :, :, o, :] = np.asarray(k_src[t]).reshape(hkv, nc, x)
             v_pool[b, :, :, o] = v_src[t]
 
 
@@ -115,13 +124,13 @@ def gather_logical(pools, kv_dtype: str, table_row, positions, num_blocks=None):
     """
     k_pool, v_pool, k_scale, v_scale = pools
     nb = k_pool.shape[0] if num_blocks is None else num_blocks
-    hkv, d = k_pool.shape[1], k_pool.shape[3]
+    hkv, d = k_pool.shape[1], k_pool.shape[2] * k_pool.shape[4]
     K = np.empty((len(positions), hkv, d))
     V = np.empty((len(positions), hkv, d))
     for i, p in enumerate(positions):
         b = physical_block(table_row, int(p), nb)
         o = int(p) % BLOCK_SIZE
-        k = to_f64(k_pool[b, :, o, :], kv_dtype)
+        k = to_f64(k_pool[b, :, :, o, :].reshape(hkv, d), kv_dtype)
         v = to_f64(v_pool[b, :, :, o], kv_dtype)
         if kv_dtype == "fp8":
             k = k * k_scale[b, :, o].astype(np.float64)[:, None]

@@ -17,8 +17,9 @@
 //    second kernel merges partitions by log-sum-exp (skipped for sequences
 //    that fit one partition, whose workgroup writes the output directly).
 //  * Per 16-token block and wave, QK^T is one 16x16 MFMA tile: A = the block's
-//    K tile (row = token, 16-byte loads straight from the token-major pool
-//    tile), B = the GQA group's query rows (column = query head; the G <= 16
+//    K tile (row = token; the pool stores K in 16-byte chunks of 16 token rows,
+//    so every load instruction reads 1 KiB of contiguous memory straight into
+//    operand registers), B = the GQA group's query rows (column = query head; the G <= 16
 //    rows of a group live in registers for the whole partition).  The
 //    accumulator gives lane (c, j) the logits of head c for tokens 4j..4j+3.
 //  * PV is a second MFMA per 16 head-dims: A = the dim-major V tile (lane
@@ -93,11 +94,47 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// First head-dim of the 8 consecutive dims row group j contributes to QK step
+// st (16-bit and FP8 K: one 16x16x32 MFMA per step).  With 16-byte K chunks of
+// X elements, load u of row group j is chunk 4u + j.
+template <int KVT>
+__device__ __forceinline__ int qk_dim16(int st, int j) {
+  if constexpr (KVT == DT_FP8) return (4 * (st / 2) + j) * 16 + 8 * (st % 2);   // X = 16: two steps per chunk
+  else return (4 * st + j) * 8;                                               // X = 8: one step per chunk
+}
+// Head-dim row group j contributes to step st of the fp32 16x16x4 MFMA (X = 4).
+__device__ __forceinline__ int qk_dim_f32(int st, int j) { return (4 * (st / 4) + j) * 4 + st % 4; }
+
 }  // namespace
+
+// Slack (base-2 units) the running max may lag behind before accumulators are rescaled.
+constexpr float kRescaleSlack = 8.f;
+
+// Build-time tuning knobs (defaults are the measured choice).
+#ifndef PKV_ATTN_WAVES_PER_EU
+#define PKV_ATTN_WAVES_PER_EU 0      // 0: let the compiler pick the register budget
+#endif
+#ifndef PKV_ATTN_NT_LOADS
+#define PKV_ATTN_NT_LOADS 0          // 1: K/V tiles loaded with the non-temporal hint
+#endif
+#if PKV_ATTN_WAVES_PER_EU > 0
+#define PKV_ATTN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PKV_ATTN_WAVES_PER_EU)))
+#else
+#define PKV_ATTN_OCCUPANCY
+#endif
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+#if PKV_ATTN_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 // One workgroup = 4 waves = one (sequence, KV head, partition).
 template <int KVT, int QT, int D>
-__global__ void __launch_bounds__(256) attn_partition_kernel(const AttnArgs a) {
+__global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(const AttnArgs a) {
   using KT = KvType<KVT>;
   constexpr int EB = KT::kBytes;
   constexpr bool OP32 = KT::kOp32;
@@ -115,7 +152,7 @@ __global__ void __launch_bounds__(256) attn_partition_kernel(const AttnArgs a) {
   const int part = blockIdx.x;
   const int hq = a.num_q_heads;
   const int group = hq / a.num_kv_heads;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;                // MFMA row/column inside a 16x16 tile
   const int j = lane >> 4;                // which 4-token / 1/4-of-dims slice
@@ -147,32 +184,39 @@ __global__ void __launch_bounds__(256) attn_partition_kernel(const AttnArgs a) {
   uint32_t qlo[QSPLIT ? QW : 1];
   float qf[OP32 ? DPL : 1];
   {
-    const size_t qbase = ((size_t)s * hq + (head_ok ? head : 0)) * D + (size_t)j * DPL;
+    // Lane (c, j) holds, for QK step st, the same head-dims the K chunks of row
+    // group j carry in that step (qk_dim), so A and B agree on the contraction.
+    const size_t qrow = ((size_t)s * hq + (head_ok ? head : 0)) * D;
     if constexpr (OP32) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) qf[e] = head_ok ? load_q_elem<QT>(a.q, qbase + e) : 0.f;
+      for (int st = 0; st < DPL; ++st)
+        qf[st] = head_ok ? load_q_elem<QT>(a.q, qrow + qk_dim_f32(st, j)) : 0.f;
     } else if constexpr (QSAME) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.q) + qbase);
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + qrow;
 #pragma unroll
-      for (int w = 0; w < QW / 4; ++w) {
-        u32x4 v = head_ok ? src[w] : u32x4{0, 0, 0, 0};
-        qhi[4 * w + 0] = v[0]; qhi[4 * w + 1] = v[1]; qhi[4 * w + 2] = v[2]; qhi[4 * w + 3] = v[3];
+      for (int st = 0; st < QW / 4; ++st) {
+        const u32x4 v = head_ok ? *reinterpret_cast<const u32x4*>(qh + qk_dim16<KVT>(st, j)) : u32x4{0, 0, 0, 0};
+        qhi[4 * st + 0] = v[0]; qhi[4 * st + 1] = v[1]; qhi[4 * st + 2] = v[2]; qhi[4 * st + 3] = v[3];
       }
     } else {
 #pragma unroll
-      for (int w = 0; w < QW; ++w) {
-        float f0 = head_ok ? load_q_elem<QT>(a.q, qbase + 2 * w) : 0.f;
-        float f1 = head_ok ? load_q_elem<QT>(a.q, qbase + 2 * w + 1) : 0.f;
-        uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
-        uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
-        uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
-        qhi[w] = h0 | (h1 << 16);
-        qlo[w] = l0 | (l1 << 16);
+      for (int st = 0; st < QW / 4; ++st) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int d0 = qk_dim16<KVT>(st, j) + 2 * w;
+          const float f0 = head_ok ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
+          const float f1 = head_ok ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+          const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
+          const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
+          const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
+          qhi[4 * st + w] = h0 | (h1 << 16);
+          qlo[4 * st + w] = l0 | (l1 << 16);
+        }
       }
     }
   }
 
-  float m_run = -INFINITY;   // running max of this head's base-2 logits (same in all 4 rows)
+  float m_run = -INFINITY;   // reference max of this head's base-2 logits (same in all 4 rows)
   float l_run = 0.f;         // this lane's share of the exp-sum
   f32x4 acc[NT];
 #pragma unroll
@@ -183,151 +227,168 @@ __global__ void __launch_bounds__(256) attn_partition_kernel(const AttnArgs a) {
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
   const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
 
-  for (int vb = vb0 + wave; vb < vb1; vb += kPartWaves) {
-    const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
-    const int phys = trow[lb];
-    if (phys < 0 || phys >= a.num_blocks) { bad = true; continue; }
-    const size_t tile = (size_t)phys * a.num_kv_heads + kvh;
+  // This wave's blocks: vb0 + wave + 4 i.  Lane i fetches the i-th table entry
+  // once; each step broadcasts it with readlane, so no table load sits between
+  // a block and its K/V loads.
+  const int n_mine = vb0 + wave < vb1 ? (vb1 - vb0 - wave + kPartWaves - 1) / kPartWaves : 0;
+  int my_phys = -1;
+  if (lane < n_mine) my_phys = trow[logical_block(vb0 + wave + kPartWaves * lane, geo.n_sink_blocks, geo.win_start)];
 
-    // ---- loads: K row slice (token c, dims j*DPL..), V^T slices (dim c of each tile, tokens 4j..4j+3)
-    uint32_t kr[KW];
-    {
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + (tile * kBlockSize + c) * (size_t)(D * EB) +
-                                                       (size_t)j * (DPL * EB));
+  struct Regs {
+    uint32_t k[KW];
+    uint32_t v[NT][VW];
+    f32x4 ks, vs;
+    bool ok;
+  };
+
+  auto load = [&](Regs& r, int i) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, i);
+    r.ok = phys >= 0 && phys < a.num_blocks;
+    if (!r.ok) return;
+    const size_t tile = (size_t)phys * a.num_kv_heads + kvh;
+    // K tile [D/X][16][X]: load u gives lane (c, j) chunk 4u + j of token row c,
+    // and the 64 lanes of one load read 1 KiB of contiguous memory.
+    const uint8_t* kt = kbase + tile * (size_t)(kBlockSize * D * EB);
 #pragma unroll
-      for (int w = 0; w < KW / 4; ++w) {
-        u32x4 v = kp[w];
-        kr[4 * w + 0] = v[0]; kr[4 * w + 1] = v[1]; kr[4 * w + 2] = v[2]; kr[4 * w + 3] = v[3];
+    for (int w = 0; w < KW / 4; ++w) {
+      const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(kt + ((size_t)(4 * w + j) * kBlockSize + c) * 16));
+      r.k[4 * w + 0] = v[0]; r.k[4 * w + 1] = v[1]; r.k[4 * w + 2] = v[2]; r.k[4 * w + 3] = v[3];
+    }
+    const uint8_t* vp = vbase + (tile * D + c) * (size_t)(kBlockSize * EB) + (size_t)j * (4 * EB);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint8_t* q = vp + (size_t)t * 16 * kBlockSize * EB;
+      if constexpr (VW == 1) {
+        r.v[t][0] = load_stream(reinterpret_cast<const uint32_t*>(q));
+      } else if constexpr (VW == 2) {
+        const u32x2 v = load_stream(reinterpret_cast<const u32x2*>(q));
+        r.v[t][0] = v[0]; r.v[t][1] = v[1];
+      } else {
+        const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(q));
+        r.v[t][0] = v[0]; r.v[t][1] = v[1]; r.v[t][2] = v[2]; r.v[t][3] = v[3];
       }
     }
-    uint32_t vr[NT][VW];
-    {
-      const uint8_t* vp = vbase + (tile * D + c) * (size_t)(kBlockSize * EB) + (size_t)j * (4 * EB);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint8_t* p = vp + (size_t)t * 16 * kBlockSize * EB;
-        if constexpr (VW == 1) {
-          vr[t][0] = *reinterpret_cast<const uint32_t*>(p);
-        } else if constexpr (VW == 2) {
-          u32x2 v = *reinterpret_cast<const u32x2*>(p);
-          vr[t][0] = v[0]; vr[t][1] = v[1];
-        } else {
-          u32x4 v = *reinterpret_cast<const u32x4*>(p);
-          vr[t][0] = v[0]; vr[t][1] = v[1]; vr[t][2] = v[2]; vr[t][3] = v[3];
-        }
-      }
-    }
-    f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = {1.f, 1.f, 1.f, 1.f};
     if constexpr (KVT == DT_FP8) {
-      ksc = *reinterpret_cast<const f32x4*>(a.k_scale + tile * kBlockSize + 4 * j);
-      vsc = *reinterpret_cast<const f32x4*>(a.v_scale + tile * kBlockSize + 4 * j);
+      r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile * kBlockSize + 4 * j);
+      r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile * kBlockSize + 4 * j);
     }
+  };
+
+  auto compute = [&](Regs& r, int i) {
+    if (!r.ok) { bad = true; return; }
+    const int vb = vb0 + wave + kPartWaves * i;
+    const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
 
     // ---- S = K q^T: lane (c, j) receives head c's logits of tokens 4j..4j+3
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (OP32) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) sacc = mfma_f32_k4(__uint_as_float(kr[e]), qf[e], sacc);
+      for (int e = 0; e < DPL; ++e) sacc = mfma_f32_k4(__uint_as_float(r.k[e]), qf[e], sacc);
     } else {
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
         if constexpr (KVT == DT_FP8) {
-          fp8x4_to_bf16x4(kr[2 * st], av[0], av[1]);
-          fp8x4_to_bf16x4(kr[2 * st + 1], av[2], av[3]);
+          fp8x4_to_bf16x4(r.k[2 * st], av[0], av[1]);
+          fp8x4_to_bf16x4(r.k[2 * st + 1], av[2], av[3]);
         } else {
-          av[0] = kr[4 * st]; av[1] = kr[4 * st + 1]; av[2] = kr[4 * st + 2]; av[3] = kr[4 * st + 3];
+          av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
         }
         sacc = mfma_k32<F16>(av, &qhi[4 * st], sacc);
         if constexpr (QSPLIT) sacc = mfma_k32<F16>(av, &qlo[4 * st], sacc);
       }
     }
 
-    // ---- mask, online softmax (base 2)
-    const int p0 = lb * kBlockSize + 4 * j;
+    // ---- logits (base 2) with the keep-set mask
     const int blk0 = lb * kBlockSize;
     const bool full = (blk0 + kBlockSize <= L) && (blk0 + kBlockSize <= sinks || blk0 >= keep_lo);
     float x[4];
-    bool valid[4];
+    bool valid[4] = {true, true, true, true};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = p0 + i;
-      valid[i] = p < L && (p < sinks || p >= keep_lo);
-      float z = sacc[i] * a.scale_log2;
-      if constexpr (KVT == DT_FP8) z *= ksc[i];
-      x[i] = valid[i] ? z : -INFINITY;
-    }
-    const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const float m_new = fmaxf(m_run, mb);
-    const bool live = m_new != -INFINITY;
-    const float alpha = live ? fast_exp2(m_run - m_new) : 1.f;
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = live ? fast_exp2(x[i] - m_new) : 0.f;
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-
-    if (a.stash != nullptr && head_ok) {
-      f32x4 xv = {x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<f32x4*>(a.stash + ((size_t)s * hq + head) * a.nv_pad + (size_t)vb * kBlockSize + 4 * j) = xv;
-    }
-
-    // ---- probabilities as the PV B operand (V's FP8 scale folded in)
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (KVT == DT_FP8) pv[i] = valid[i] ? pr[i] * vsc[i] : 0.f;
-      else pv[i] = pr[i];
+    for (int e = 0; e < 4; ++e) {
+      x[e] = sacc[e] * a.scale_log2;
+      if constexpr (KVT == DT_FP8) x[e] *= r.ks[e];
     }
     if (!full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = blk0 + 4 * j + e;
+        valid[e] = p < L && (p < sinks || p >= keep_lo);
+        x[e] = valid[e] ? x[e] : -INFINITY;
+      }
       // Slots outside the keep-set may hold anything (NaN included): zero their V.
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if constexpr (VW == 1) {
           const uint32_t msk = (valid[0] ? 0xffu : 0u) | (valid[1] ? 0xff00u : 0u) |
                                (valid[2] ? 0xff0000u : 0u) | (valid[3] ? 0xff000000u : 0u);
-          vr[t][0] &= msk;
+          r.v[t][0] &= msk;
         } else if constexpr (VW == 2) {
-          vr[t][0] &= (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
-          vr[t][1] &= (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
+          r.v[t][0] &= (valid[0] ? 0xffffu : 0u) | (valid[1] ? 0xffff0000u : 0u);
+          r.v[t][1] &= (valid[2] ? 0xffffu : 0u) | (valid[3] ? 0xffff0000u : 0u);
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vr[t][i] = valid[i] ? vr[t][i] : 0u;
+          for (int e = 0; e < 4; ++e) r.v[t][e] = valid[e] ? r.v[t][e] : 0u;
         }
       }
     }
 
-    // ---- O^T += V^T P^T: lane (c, j) accumulates head c, dims 16t + 4j + i
+    // ---- online softmax with a slack: the reference max only moves (and the
+    // accumulators are rescaled) when a logit exceeds it by more than
+    // kRescaleSlack, so exp2 stays <= 2^kRescaleSlack and most blocks skip the
+    // rescale.  Any reference gives the same normalised result.
+    const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const bool need = mb > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float m_new = need ? mb : m_run;
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);   // 0 on the first block
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+      m_run = m_new;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[e] - mref);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+    if (a.stash != nullptr && head_ok) {
+      const f32x4 xv = {x[0], x[1], x[2], x[3]};
+      *reinterpret_cast<f32x4*>(a.stash + ((size_t)s * hq + head) * a.nv_pad + (size_t)vb * kBlockSize + 4 * j) = xv;
+    }
+
+    // ---- probabilities as the PV B operand (V's FP8 scale folded in)
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (KVT == DT_FP8) pv[e] = valid[e] ? pr[e] * r.vs[e] : 0.f;
+      else pv[e] = pr[e];
+    }
+
+    // ---- O^T += V^T P^T: lane (c, j) accumulates head c, dims 16t + 4j + e
     if constexpr (OP32) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t] = mfma_f32_k4(__uint_as_float(vr[t][r]), pv[r], acc[t]);
+        for (int e = 0; e < 4; ++e) acc[t] = mfma_f32_k4(__uint_as_float(r.v[t][e]), pv[e], acc[t]);
       }
     } else {
       uint32_t ph[2], pl[2];
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
-        uint32_t h0, h1;
+        uint32_t h0, h1, l0, l1;
         if constexpr (F16) {
           h0 = f32_to_f16_bits(f0);
           h1 = f32_to_f16_bits(f1);
+          l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
+          l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
         } else {
-          h0 = __float_as_uint(f0) >> 16;           // truncated high part
+          h0 = __float_as_uint(f0) >> 16;           // truncated high part, exact residual below
           h1 = __float_as_uint(f1) >> 16;
-        }
-        const float r0 = f0 - from_op16<F16>(h0);
-        const float r1 = f1 - from_op16<F16>(h1);
-        uint32_t l0, l1;
-        if constexpr (F16) {
-          l0 = f32_to_f16_bits(r0);
-          l1 = f32_to_f16_bits(r1);
-        } else {
-          l0 = __float_as_uint(r0) >> 16;
-          l1 = __float_as_uint(r1) >> 16;
+          l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
+          l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
         }
         ph[w] = h0 | (h1 << 16);
         pl[w] = l0 | (l1 << 16);
@@ -336,16 +397,28 @@ __global__ void __launch_bounds__(256) attn_partition_kernel(const AttnArgs a) {
       for (int t = 0; t < NT; ++t) {
         uint32_t v0, v1;
         if constexpr (KVT == DT_FP8) {
-          fp8x4_to_bf16x4(vr[t][0], v0, v1);
+          fp8x4_to_bf16x4(r.v[t][0], v0, v1);
         } else {
-          v0 = vr[t][0];
-          v1 = vr[t][1];
+          v0 = r.v[t][0];
+          v1 = r.v[t][1];
         }
         acc[t] = mfma_k16<F16>(v0, v1, ph[0], ph[1], acc[t]);
         acc[t] = mfma_k16<F16>(v0, v1, pl[0], pl[1], acc[t]);
       }
     }
+  };
+
+  // Software pipeline: block i+1's loads are in flight while block i computes.
+  Regs ra, rb;
+  int i = 0;
+  if (n_mine > 0) load(ra, 0);
+  for (; i + 1 < n_mine; i += 2) {
+    load(rb, i + 1);
+    compute(ra, i);
+    if (i + 2 < n_mine) load(ra, i + 2);
+    compute(rb, i + 1);
   }
+  if (i < n_mine) compute(ra, i);
 
   l_run = row_sum4(l_run);
 

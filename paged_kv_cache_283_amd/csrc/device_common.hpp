@@ -56,19 +56,37 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
 }
 
 // Wave64 butterfly reductions over lanes that differ in bits 4 and 5 of the
-// lane id (the four 16-lane rows of an MFMA accumulator).
+// lane id (the four 16-lane rows of an MFMA accumulator), with the gfx950
+// row-swap instructions: permlane16_swap(x, x) hands every lane the value of
+// its partner 16 lanes away in one of the two results and keeps its own in the
+// other, so max/sum of the pair is symmetric in the two; permlane32_swap does
+// the same for the partner 32 lanes away.
 __device__ __forceinline__ float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, kWave));
-  x = fmaxf(x, __shfl_xor(x, 32, kWave));
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float row_sum4(float x) {
-  x += __shfl_xor(x, 16, kWave);
-  x += __shfl_xor(x, 32, kWave);
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Element offset of K element (token o, dim d) inside a (block, KV head) tile
+// stored as [D/X][16][X] with X = 16 bytes of elements.
+template <int EB>
+__device__ __forceinline__ int k_chunk_offset(int o, int d) {
+  constexpr int X = 16 / EB;
+  return ((d / X) * kBlockSize + o) * X + d % X;
+}
 
 // Logical block of virtual (attended) block vb: sink blocks first, then the window.
 __device__ __forceinline__ int logical_block(int vb, int n_sink_blocks, int win_start) {

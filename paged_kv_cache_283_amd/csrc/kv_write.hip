@@ -6,8 +6,8 @@
 //     block table names for logical block p / 16, at offset p % 16;
 //   "量化原理" -- FP8 (E4M3) storage with per-token scales;
 //   "三大运行时组件" and copy_on_write -- a shared block is copied before a write.
-// Pool layout: K [NB][Hkv][16][D] token-major, V [NB][Hkv][D][16] dim-major,
-// FP8 scales [NB][Hkv][16].
+// Pool layout: K [NB][Hkv][D/X][16][X] (16-byte chunks of X elements),
+// V [NB][Hkv][D][16] dim-major, FP8 scales [NB][Hkv][16].
 #include "device_common.hpp"
 #include "fp8_e4m3.hpp"
 #include "launch.hpp"
@@ -86,7 +86,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
       const int d = e * 64 + lane;
       const uint32_t kc = ks == 0.f ? 0u : e4m3fn_encode(__fdiv_rn(kx[e], ks));
       const uint32_t vc = vs == 0.f ? 0u : e4m3fn_encode(__fdiv_rn(vx[e], vs));
-      kp[(tile * kBlockSize + o) * D + d] = (uint8_t)kc;
+      kp[tile * kBlockSize * D + k_chunk_offset<1>(o, d)] = (uint8_t)kc;
       vp[(tile * D + d) * kBlockSize + o] = (uint8_t)vc;
     }
     if (lane == 0) {
@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int d = e * 64 + lane;
-      kp[(tile * kBlockSize + o) * D + d] = ks[src + d];
+      kp[tile * kBlockSize * D + k_chunk_offset<sizeof(T)>(o, d)] = ks[src + d];
       vp[(tile * D + d) * kBlockSize + o] = vs[src + d];
     }
   }

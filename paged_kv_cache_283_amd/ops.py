@@ -6,7 +6,9 @@ include/pagedkv.h; shapes are read off the tensors.
 
 Storage dtypes: torch.float32 / bfloat16 / float16 pools hold those values;
 torch.uint8 or torch.float8_e4m3fn pools hold OCP E4M3FN codes with
-float32 scale tensors [num_blocks][num_kv_heads][16].
+float32 scale tensors [num_blocks][num_kv_heads][16].  Pool shapes:
+K [num_blocks][num_kv_heads][head_dim/X][16][X] (X = 16 bytes of elements),
+V [num_blocks][num_kv_heads][head_dim][16]; allocate_pools builds both.
 """
 import ctypes
 import math
@@ -80,6 +82,16 @@ def _issue(name, args, prepare):
     return None
 
 
+def k_chunk(dtype: torch.dtype) -> int:
+    """Elements per 16-byte chunk of the K pool layout [NB][Hkv][D/X][16][X]."""
+    return 16 // torch.empty((), dtype=dtype).element_size()
+
+
+def k_pool_shape(num_blocks, num_kv_heads, head_dim, dtype):
+    x = k_chunk(dtype)
+    return (num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x)
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -120,8 +132,8 @@ def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_s
     if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
         raise ValueError("k_new and v_new must match")
     nb = k_pool.shape[0]
-    if tuple(k_pool.shape) != (nb, hkv, BLOCK_SIZE, d) or tuple(v_pool.shape) != (nb, hkv, d, BLOCK_SIZE):
-        raise ValueError(f"pools must be [NB][{hkv}][16][{d}] (K) and [NB][{hkv}][{d}][16] (V)")
+    if tuple(k_pool.shape) != k_pool_shape(nb, hkv, d, k_pool.dtype) or tuple(v_pool.shape) != (nb, hkv, d, BLOCK_SIZE):
+        raise ValueError(f"pools must be {k_pool_shape(nb, hkv, d, k_pool.dtype)} (K) and [NB][{hkv}][{d}][16] (V)")
     if slot_mapping.shape[0] != t:
         raise ValueError("slot_mapping must have one entry per token")
     return _issue("paged_kv_write", (_ptr(k_new), _ptr(v_new), float_code(k_new.dtype), _ptr(k_pool),
@@ -132,7 +144,7 @@ def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_s
 def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, device="cuda", fill_byte=None):
     """(k_pool, v_pool, k_scale, v_scale) in the library's layout; scales are None unless kv_dtype is FP8
     (torch.uint8 or torch.float8_e4m3fn).  fill_byte sets every byte (0xFF = NaN everywhere)."""
-    k = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE, head_dim), dtype=kv_dtype, device=device)
+    k = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
     v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=kv_dtype, device=device)
     ks = vs = None
     if kv_code(kv_dtype) == _lib.FP8_E4M3:
@@ -199,7 +211,8 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_co
 def kv_block_copy(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None, stream=None):
     """Copy whole blocks per int32 [n][2] {src, dst} pair (the data half of copy-on-write)."""
     _need(block_pairs, torch.int32, "block_pairs")
-    nb, hkv, _, d = k_pool.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    d = k_pool.shape[2] * k_pool.shape[4]
     _lib.call("kv_block_copy", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
               _ptr(block_pairs), block_pairs.shape[0], nb, hkv, d, BLOCK_SIZE, _stream(stream))
 

@@ -19,6 +19,12 @@ def poisoned(shape, dtype, device=DEV):
     return t
 
 
+def k_token_rows(k_pool):
+    """View of a K pool as [num_blocks * 16][Hkv][D] token rows (a copy)."""
+    nb, hkv, nc, bs, x = k_pool.shape
+    return k_pool.permute(0, 3, 1, 2, 4).reshape(nb * bs, hkv, nc * x)
+
+
 def make_pools(w, num_blocks, device=DEV):
     """Pools of the workload's shape, every byte 0xFF (NaN) so unwritten slots poison any read."""
     return ops.allocate_pools(num_blocks, w.num_kv_heads, w.head_dim, W.storage_dtype(w.kv_dtype), device, 0xFF)

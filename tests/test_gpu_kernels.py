@@ -114,13 +114,10 @@ def test_fp8_encoder_on_crafted_values():
     rows[:, 0] = 448.0
     k = torch.from_numpy(rows.reshape(n, 1, d)).cuda()
     nb = -(-n // 16)
-    kp = H.poisoned((nb, 1, 16, d), torch.uint8)
-    vp = H.poisoned((nb, 1, d, 16), torch.uint8)
-    ks = H.poisoned((nb, 1, 16), torch.float32)
-    vs = H.poisoned((nb, 1, 16), torch.float32)
+    kp, vp, ks, vs = ops.allocate_pools(nb, 1, d, torch.uint8, "cuda", fill_byte=0xFF)
     ops.paged_kv_write(k, k, kp, vp, torch.arange(n, dtype=torch.int64).cuda(), ks, vs)
     assert torch.all(ks.view(-1)[:n] == 1.0)
-    codes = kp.view(nb * 16, d)[:n].cpu().numpy()
+    codes = H.k_token_rows(kp).view(nb * 16, d)[:n].cpu().numpy()
     assert np.array_equal(codes, fp8.encode(rows))
     vcodes = vp.view(nb, d, 16).permute(0, 2, 1).reshape(nb * 16, d)[:n].cpu().numpy()
     assert np.array_equal(vcodes, codes)
@@ -129,18 +126,15 @@ def test_fp8_encoder_on_crafted_values():
 def test_fp8_zero_rows_and_skipped_slots():
     k = torch.zeros((3, 2, 64), dtype=torch.bfloat16, device="cuda")
     k[1, 1, 5] = -3.0
-    kp = H.poisoned((2, 2, 16, 64), torch.uint8)
-    vp = H.poisoned((2, 2, 64, 16), torch.uint8)
-    ks = H.poisoned((2, 2, 16), torch.float32)
-    vs = H.poisoned((2, 2, 16), torch.float32)
+    kp, vp, ks, vs = ops.allocate_pools(2, 2, 64, torch.uint8, "cuda", fill_byte=0xFF)
     ops.paged_kv_write(k, k, kp, vp, torch.tensor([3, -1, 40], dtype=torch.int64).cuda(), ks, vs)
     # token 0 -> slot 3 (all zero: scale 0, codes 0); token 1 skipped (-1); token 2 out of the pool, skipped
-    assert torch.all(kp[0, :, 3] == 0) and torch.all(vp[0, :, :, 3] == 0)
+    assert torch.all(kp[0, :, :, 3] == 0) and torch.all(vp[0, :, :, 3] == 0)
     assert torch.all(ks[0, :, 3] == 0) and torch.all(vs[0, :, 3] == 0)
     for t in (kp, vp, ks.view(torch.uint8), vs.view(torch.uint8)):
         left = t.clone().view(torch.uint8)
         if t is kp:
-            left[0, :, 3] = 0xFF
+            left[0, :, :, 3] = 0xFF
         elif t is vp:
             left[0, :, :, 3] = 0xFF
         else:
@@ -305,7 +299,7 @@ def test_copy_on_write(kv):
 
 
 def test_block_copy_skips_invalid_pairs():
-    kp = torch.arange(4 * 2 * 16 * 64, dtype=torch.float32, device="cuda").view(4, 2, 16, 64)
+    kp = torch.arange(4 * 2 * 16 * 64, dtype=torch.float32, device="cuda").view(4, 2, 16, 16, 4)
     vp = kp.clone().view(4, 2, 64, 16)
     ref_k, ref_v = kp.clone(), vp.clone()
     pairs = torch.tensor([[0, 0], [-1, 2], [1, 9], [2, 3]], dtype=torch.int32).cuda()

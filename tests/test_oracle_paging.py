@@ -52,10 +52,11 @@ def test_layout_is_a_bijection(kv_dtype):
     k, v = pools[0], pools[1]
     assert sorted(k.ravel().tolist()) == sorted(vals.ravel().tolist())
     assert sorted(v.ravel().tolist()) == sorted((vals + 0.5).ravel().tolist())
-    # K tile is token-major, V tile dim-major: token p, head h, dim i
+    # K tile in 16-byte chunks (4 floats) of 16 token rows, V tile dim-major: token p, head h, dim i
     p, h, i = 37, 1, 5
     b, o = table[p // 16], p % 16
-    assert k[b, h, o, i] == vals[p, h, i]
+    assert k.shape == (nb, hkv, d // 4, 16, 4)
+    assert k[b, h, i // 4, o, i % 4] == vals[p, h, i]
     assert v[b, h, i, o] == vals[p, h, i] + 0.5
 
 
@@ -105,7 +106,7 @@ def test_bf16_storage_decode():
 
 def test_copy_blocks_is_copy_on_write_data_half():
     rng = np.random.default_rng(5)
-    pools = paging.new_pools(6, 2, 8, "fp8")
+    pools = paging.new_pools(6, 2, 16, "fp8")
     for a in pools:
         a[...] = rng.integers(0, 120, a.shape).astype(a.dtype)
     before = [a.copy() for a in pools]
@@ -115,7 +116,7 @@ def test_copy_blocks_is_copy_on_write_data_half():
         keep = [i for i in range(6) if i != 4]
         assert np.array_equal(a[keep], b[keep])                 # nothing else touched
     # a later write into the copy leaves the shared original alone
-    k = np.ones((1, 2, 8), np.float32)
+    k = np.ones((1, 2, 16), np.float32)
     paging.write_tokens(pools, "fp8", k, k, "f32", [[4]], [0], [3])
     assert np.array_equal(pools[0][1], before[0][1])
     assert not np.array_equal(pools[0][4], before[0][1])
