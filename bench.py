@@ -134,6 +134,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-only", action="store_true", help="run only the HBM read/copy probes")
+    ap.add_argument("--contiguous-blocks", action="store_true", help="hand out physical blocks in order "
+                    "instead of the shuffled placement (comparison only)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -183,7 +185,7 @@ def main():
 
     # ---- workload: pools filled through the library's own write path (untimed prefill)
     w = W.WORKLOADS[args.workload]
-    lay = W.make_layout(w)
+    lay = W.make_layout(w, shuffle=not args.contiguous_blocks)
     tables = torch.from_numpy(lay.tables).to(dev)
     lens = torch.from_numpy(lay.lens).to(dev)
     layers = w.num_layers
@@ -269,7 +271,8 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "kv_dtype": w.kv_dtype, "block_size": 16, "max_context_len": lay.max_len,
                    "attended_tokens_per_layer": n_tok, "num_sinks": w.num_sinks, "window": w.window,
-                   "pool_replicas_rotated": replicas},
+                   "pool_replicas_rotated": replicas,
+                   "block_placement": "contiguous" if args.contiguous_blocks else "shuffled"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "tokens_per_s": round(w.num_seqs / (step_ms * 1e-3), 1),

@@ -11,7 +11,7 @@
 #include <utility>
 #include <vector>
 
-#include "../../include/pagedkv.h"
+#include "pagedkv.h"
 #include "geometry.hpp"
 #include "launch.hpp"
 
@@ -164,6 +164,8 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
   if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
   const pkv::WorkspaceLayout lay = pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len,
                                                               num_sinks, window, attn_mass != nullptr);
+  if (lay.p_max > 65535)
+    return fail(PKV_EUNSUPPORTED, "max_context_len %d needs %d partitions (> 65535)", max_context_len, lay.p_max);
   if (workspace_bytes < lay.total)
     return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   if (lay.total > 0 && !workspace) return fail(PKV_EINVAL, "NULL workspace");

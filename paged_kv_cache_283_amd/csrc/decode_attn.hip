@@ -114,6 +114,9 @@ constexpr float kRescaleSlack = 8.f;
 #ifndef PKV_ATTN_WAVES_PER_EU
 #define PKV_ATTN_WAVES_PER_EU 0      // 0: let the compiler pick the register budget
 #endif
+#ifndef PKV_ATTN_PIPE
+#define PKV_ATTN_PIPE 3              // K/V register buffers per wave: blocks in flight = PIPE - 1
+#endif
 #ifndef PKV_ATTN_NT_LOADS
 #define PKV_ATTN_NT_LOADS 0          // 1: K/V tiles loaded with the non-temporal hint
 #endif
@@ -147,9 +150,13 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
 
-  const int s = blockIdx.z;
-  const int kvh = blockIdx.y;
-  const int part = blockIdx.x;
+  // Grid (KV head, sequence, partition) with the KV head fastest: consecutive
+  // workgroup ids go to the 8 XCDs in turn, so each XCD gets every 8th
+  // (sequence, KV head) pair -- an even share of the work -- and partitions
+  // that a short sequence does not have (exit at once) dispatch last.
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int part = blockIdx.z;
   const int hq = a.num_q_heads;
   const int group = hq / a.num_kv_heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -408,6 +415,7 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
     }
   };
 
+#if PKV_ATTN_PIPE == 2
   // Software pipeline: block i+1's loads are in flight while block i computes.
   Regs ra, rb;
   int i = 0;
@@ -419,6 +427,23 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
     compute(rb, i + 1);
   }
   if (i < n_mine) compute(ra, i);
+#else
+  // Software pipeline: blocks i+1 and i+2 are in flight while block i computes.
+  Regs r0, r1, r2;
+  int i = 0;
+  if (n_mine > 0) load(r0, 0);
+  if (n_mine > 1) load(r1, 1);
+  for (; i + 2 < n_mine; i += 3) {
+    load(r2, i + 2);
+    compute(r0, i);
+    if (i + 3 < n_mine) load(r0, i + 3);
+    compute(r1, i + 1);
+    if (i + 4 < n_mine) load(r1, i + 4);
+    compute(r2, i + 2);
+  }
+  if (i < n_mine) compute(r0, i);
+  if (i + 1 < n_mine) compute(r1, i + 1);
+#endif
 
   l_run = row_sum4(l_run);
 
@@ -538,7 +563,7 @@ template <int KVT, int QT, int D>
 hipError_t launch_partition(const AttnArgs& a, hipStream_t st) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const size_t smem = (size_t)kPartWaves * group * (D + 2) * sizeof(float);
-  dim3 grid(a.p_max, a.num_kv_heads, a.num_seqs);
+  dim3 grid(a.num_kv_heads, a.num_seqs, a.p_max);
   hipLaunchKernelGGL((attn_partition_kernel<KVT, QT, D>), grid, dim3(256), smem, st, a);
   return hipGetLastError();
 }

@@ -17,7 +17,10 @@
 namespace pkv {
 
 constexpr int kBlockSize = 16;    // tokens per physical block
-constexpr int kPartBlocks = 32;   // attended blocks per partition (512 tokens)
+#ifndef PKV_PART_BLOCKS
+#define PKV_PART_BLOCKS 32
+#endif
+constexpr int kPartBlocks = PKV_PART_BLOCKS;   // attended blocks per partition (512 tokens)
 constexpr int kPartWaves = 4;     // waves per partition workgroup
 
 struct KeepGeom {

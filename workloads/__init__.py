@@ -100,8 +100,9 @@ def lengths(w: Workload, rng=None) -> np.ndarray:
     return rng.integers(lo, hi + 1, size=w.num_seqs).astype(np.int32)
 
 
-def make_layout(w: Workload, lens=None, page_tables=None) -> Layout:
-    """Seeded block tables: physical ids drawn from one permutation of the pool."""
+def make_layout(w: Workload, lens=None, page_tables=None, shuffle=True) -> Layout:
+    """Seeded block tables: physical ids drawn from one permutation of the pool
+    (shuffle=False hands them out in order, a contiguous placement for comparison)."""
     rng = np.random.default_rng(w.seed)
     lens = lengths(w, rng) if lens is None else np.asarray(lens, dtype=np.int32)
     b = lens.shape[0]
@@ -120,7 +121,7 @@ def make_layout(w: Workload, lens=None, page_tables=None) -> Layout:
     nb = w.pool_blocks or (need + w.extra_blocks)
     if nb < need:
         raise ValueError("pool too small for the layout")
-    perm = rng.permutation(nb).astype(np.int32)
+    perm = rng.permutation(nb).astype(np.int32) if shuffle else np.arange(nb, dtype=np.int32)
     tables = np.full((b, width), -1, dtype=np.int32)
     at = 0
     for s in range(b):
