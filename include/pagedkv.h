@@ -155,6 +155,8 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
  *                  ([LC] H2OEviction.update_scores): the attention probability
  *                  averaged over all num_q_heads heads.  Other entries are untouched.
  *   workspace      >= paged_decode_attn_workspace_size(...) bytes, 256-byte aligned
+ * num_seqs * (blocks one sequence of max_context_len attends) must stay <= 2^30
+ * (PKV_EUNSUPPORTED otherwise).
  * Out-of-range device values never make the kernels touch memory outside the
  * arrays above.  A sequence whose length is outside
  * [1, min(max_context_len, 16*block_table_stride)] gets NaN in every output

@@ -156,6 +156,9 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
   if (block_table_stride < (max_context_len + 15) / 16)
     return fail(PKV_EINVAL, "block_table_stride %d < ceil(max_context_len / 16) = %d", block_table_stride,
                 (max_context_len + 15) / 16);
+  if ((long long)num_seqs * pkv::max_virtual_blocks(max_context_len, num_sinks, window) > (1LL << 30))
+    return fail(PKV_EUNSUPPORTED, "num_seqs %d x attended blocks of max_context_len %d exceeds 2^30", num_seqs,
+                max_context_len);
   if (attn_mass != nullptr && attn_mass_stride < max_context_len)
     return fail(PKV_EINVAL, "attn_mass_stride %d < max_context_len %d", attn_mass_stride, max_context_len);
   if (num_seqs == 0) return ok();
@@ -198,6 +201,8 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
   char* ws = reinterpret_cast<char*>(workspace);
   a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
   a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.hdr = reinterpret_cast<pkv::StreamHdr*>(ws + lay.hdr_off);
+  a.seq_prefix = reinterpret_cast<int*>(ws + lay.prefix_off);
   a.stash = attn_mass ? reinterpret_cast<float*>(ws + lay.stash_off) : nullptr;
   a.fin_ml = attn_mass ? reinterpret_cast<float*>(ws + lay.fin_off) : nullptr;
   a.p_max = lay.p_max;

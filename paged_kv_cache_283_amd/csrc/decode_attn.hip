@@ -11,16 +11,18 @@
 // the probabilities averaged over all query heads, added into a score row.
 //
 // How, on gfx950:
-//  * Work unit = (sequence, KV head, partition of 32 attended blocks).  One
-//    workgroup of 4 waves per unit; the waves take the partition's blocks
-//    round-robin and merge their softmax states through LDS at the end.  A
-//    second kernel merges partitions by log-sum-exp (skipped for sequences
-//    that fit one partition, whose workgroup writes the output directly).
+//  * One persistent launch of single-wave workgroups, as many as the GPU holds.
+//    The attended blocks of the whole batch are cut into equal ranges; a wave
+//    streams its range for one KV head through a software pipeline and writes
+//    the output of every sequence it covers whole, or a partial softmax state
+//    for a sequence cut at a range boundary.  A second kernel merges those
+//    partials by log-sum-exp.  Equal ranges keep every wave busy for the same
+//    time whatever the mix of context lengths.
 //  * Per 16-token block and wave, QK^T is one 16x16 MFMA tile: A = the block's
 //    K tile (row = token; the pool stores K in 16-byte chunks of 16 token rows,
 //    so every load instruction reads 1 KiB of contiguous memory straight into
 //    operand registers), B = the GQA group's query rows (column = query head; the G <= 16
-//    rows of a group live in registers for the whole partition).  The
+//    rows of a group live in registers for the whole segment).  The
 //    accumulator gives lane (c, j) the logits of head c for tokens 4j..4j+3.
 //  * PV is a second MFMA per 16 head-dims: A = the dim-major V tile (lane
 //    (d, j) reads tokens 4j..4j+3 of dim d: one 8-byte load for bf16), B =
@@ -34,6 +36,10 @@
 //    multiplies the probability.
 //  * Logits are kept in base 2 (scale * log2 e folded in) and exponentiated
 //    with v_exp_f32.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "device_common.hpp"
 #include "geometry.hpp"
 #include "launch.hpp"
@@ -111,19 +117,17 @@ __device__ __forceinline__ int qk_dim_f32(int st, int j) { return (4 * (st / 4) 
 constexpr float kRescaleSlack = 8.f;
 
 // Build-time tuning knobs (defaults are the measured choice).
-#ifndef PKV_ATTN_WAVES_PER_EU
-#define PKV_ATTN_WAVES_PER_EU 0      // 0: let the compiler pick the register budget
-#endif
 #ifndef PKV_ATTN_PIPE
 #define PKV_ATTN_PIPE 3              // K/V register buffers per wave: blocks in flight = PIPE - 1
 #endif
 #ifndef PKV_ATTN_NT_LOADS
 #define PKV_ATTN_NT_LOADS 0          // 1: K/V tiles loaded with the non-temporal hint
 #endif
-#if PKV_ATTN_WAVES_PER_EU > 0
-#define PKV_ATTN_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PKV_ATTN_WAVES_PER_EU)))
-#else
-#define PKV_ATTN_OCCUPANCY
+#ifndef PKV_ATTN_WAVES_PER_CU
+#define PKV_ATTN_WAVES_PER_CU 0      // waves launched per CU (0: as many as fit)
+#endif
+#ifndef PKV_ATTN_HEAD_FAST
+#define PKV_ATTN_HEAD_FAST 1         // 1: workgroup id = range * KV heads + head; 0: head-major
 #endif
 
 template <typename T>
@@ -135,9 +139,24 @@ __device__ __forceinline__ T load_stream(const T* p) {
 #endif
 }
 
-// One workgroup = 4 waves = one (sequence, KV head, partition).
+// Partial-output slot of a segment starting at attended block vb of its
+// sequence: 0 for the first segment, vb / kPartBlocks + 1 for one starting at a
+// range cut.  Cuts are at least kPartBlocks apart, so slots are distinct; the
+// largest is ceil(blocks / kPartBlocks).
+__device__ __forceinline__ int partial_slot(int vb) { return vb == 0 ? 0 : vb / kPartBlocks + 1; }
+
+// Attended blocks of a sequence of length L (0 for an unusable length).
+__device__ __forceinline__ int attended_blocks(const AttnArgs& a, int L) {
+  const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
+  return (L < 1 || L > len_cap) ? 0 : keep_geometry(L, a.num_sinks, a.window).n_virtual;
+}
+
+// One wave attends the GQA group of KV head kvh of sequence s over attended
+// blocks [seg_vb0, seg_vb1) and writes the normalised output (the segment is the
+// whole sequence) or a partial (running max, exp-sum, unnormalised output) in
+// slot partial_slot(seg_vb0).
 template <int KVT, int QT, int D>
-__global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(const AttnArgs a) {
+__device__ __forceinline__ void wave_segment(const AttnArgs& a, int s, int kvh, int L, int seg_vb0, int seg_vb1) {
   using KT = KvType<KVT>;
   constexpr int EB = KT::kBytes;
   constexpr bool OP32 = KT::kOp32;
@@ -150,37 +169,13 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
 
-  // Grid (KV head, sequence, partition) with the KV head fastest: consecutive
-  // workgroup ids go to the 8 XCDs in turn, so each XCD gets every 8th
-  // (sequence, KV head) pair -- an even share of the work -- and partitions
-  // that a short sequence does not have (exit at once) dispatch last.
-  const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
-  const int part = blockIdx.z;
   const int hq = a.num_q_heads;
   const int group = hq / a.num_kv_heads;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;                // MFMA row/column inside a 16x16 tile
   const int j = lane >> 4;                // which 4-token / 1/4-of-dims slice
-  const int L = a.context_lens[s];
-  const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
-
-  if (L < 1 || L > len_cap) {
-    // Unusable length: poison this KV head's outputs once, touch nothing else.
-    if (part == 0) {
-      for (int idx = threadIdx.x; idx < group * D; idx += blockDim.x) {
-        const size_t hs = (size_t)s * hq + (size_t)kvh * group + idx / D;
-        store_out(a.out, hs * D + idx % D, a.out_dtype, __builtin_nanf(""));
-      }
-    }
-    return;
-  }
   const KeepGeom geo = keep_geometry(L, a.num_sinks, a.window);
-  const int vb0 = part * kPartBlocks;
-  if (vb0 >= geo.n_virtual) return;
-  const int vb1 = min(vb0 + kPartBlocks, geo.n_virtual);
-  const int nparts = num_partitions(geo.n_virtual);
+  const bool whole = seg_vb0 == 0 && seg_vb1 == geo.n_virtual;
   const int keep_lo = a.window > 0 ? L - a.window : 0;   // p >= keep_lo is kept
   const int sinks = a.window > 0 ? a.num_sinks : 0;      // p < sinks is kept
 
@@ -234,19 +229,15 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
   const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
 
-  // This wave's blocks: vb0 + wave + 4 i.  Lane i fetches the i-th table entry
-  // once; each step broadcasts it with readlane, so no table load sits between
-  // a block and its K/V loads.
-  const int n_mine = vb0 + wave < vb1 ? (vb1 - vb0 - wave + kPartWaves - 1) / kPartWaves : 0;
-  int my_phys = -1;
-  if (lane < n_mine) my_phys = trow[logical_block(vb0 + wave + kPartWaves * lane, geo.n_sink_blocks, geo.win_start)];
-
   struct Regs {
     uint32_t k[KW];
     uint32_t v[NT][VW];
     f32x4 ks, vs;
     bool ok;
   };
+
+  int sub0 = seg_vb0;   // first block of the current batch (at most 64 blocks)
+  int my_phys = -1;     // lane i: physical block of the batch's i-th block
 
   auto load = [&](Regs& r, int i) {
     const int phys = __builtin_amdgcn_readlane(my_phys, i);
@@ -283,7 +274,7 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
 
   auto compute = [&](Regs& r, int i) {
     if (!r.ok) { bad = true; return; }
-    const int vb = vb0 + wave + kPartWaves * i;
+    const int vb = sub0 + i;
     const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
 
     // ---- S = K q^T: lane (c, j) receives head c's logits of tokens 4j..4j+3
@@ -415,118 +406,211 @@ __global__ void __launch_bounds__(256) PKV_ATTN_OCCUPANCY attn_partition_kernel(
     }
   };
 
-#if PKV_ATTN_PIPE == 2
-  // Software pipeline: block i+1's loads are in flight while block i computes.
-  Regs ra, rb;
-  int i = 0;
-  if (n_mine > 0) load(ra, 0);
-  for (; i + 1 < n_mine; i += 2) {
-    load(rb, i + 1);
-    compute(ra, i);
-    if (i + 2 < n_mine) load(ra, i + 2);
-    compute(rb, i + 1);
-  }
-  if (i < n_mine) compute(ra, i);
+  for (; sub0 < seg_vb1; sub0 += kWave) {
+    // Lane i fetches the table entry of the batch's i-th block once; each step
+    // broadcasts it with readlane, so no table load sits between a block and
+    // its K/V loads.
+    const int n_mine = min(kWave, seg_vb1 - sub0);
+    my_phys = -1;
+    if (lane < n_mine) my_phys = trow[logical_block(sub0 + lane, geo.n_sink_blocks, geo.win_start)];
+#if PKV_ATTN_PIPE == 1
+    Regs r0;
+    for (int i = 0; i < n_mine; ++i) {
+      load(r0, i);
+      compute(r0, i);
+    }
+#elif PKV_ATTN_PIPE == 2
+    // Software pipeline: block i+1's loads are in flight while block i computes.
+    Regs ra, rb;
+    int i = 0;
+    if (n_mine > 0) load(ra, 0);
+    for (; i + 1 < n_mine; i += 2) {
+      load(rb, i + 1);
+      compute(ra, i);
+      if (i + 2 < n_mine) load(ra, i + 2);
+      compute(rb, i + 1);
+    }
+    if (i < n_mine) compute(ra, i);
 #else
-  // Software pipeline: blocks i+1 and i+2 are in flight while block i computes.
-  Regs r0, r1, r2;
-  int i = 0;
-  if (n_mine > 0) load(r0, 0);
-  if (n_mine > 1) load(r1, 1);
-  for (; i + 2 < n_mine; i += 3) {
-    load(r2, i + 2);
-    compute(r0, i);
-    if (i + 3 < n_mine) load(r0, i + 3);
-    compute(r1, i + 1);
-    if (i + 4 < n_mine) load(r1, i + 4);
-    compute(r2, i + 2);
-  }
-  if (i < n_mine) compute(r0, i);
-  if (i + 1 < n_mine) compute(r1, i + 1);
+    // Software pipeline: blocks i+1 and i+2 are in flight while block i computes.
+    Regs r0, r1, r2;
+    int i = 0;
+    if (n_mine > 0) load(r0, 0);
+    if (n_mine > 1) load(r1, 1);
+    for (; i + 2 < n_mine; i += 3) {
+      load(r2, i + 2);
+      compute(r0, i);
+      if (i + 3 < n_mine) load(r0, i + 3);
+      compute(r1, i + 1);
+      if (i + 4 < n_mine) load(r1, i + 4);
+      compute(r2, i + 2);
+    }
+    if (i < n_mine) compute(r0, i);
+    if (i + 1 < n_mine) compute(r1, i + 1);
 #endif
+  }
 
-  l_run = row_sum4(l_run);
-
-  // ---- merge the 4 waves' states through LDS
-  extern __shared__ float smem[];
-  float* s_acc = smem;                                  // [4][group][D]
-  float* s_ml = smem + kPartWaves * group * D;          // [4][group][2]
-  if (head_ok) {
+  l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
+  if (bad) l_run = __builtin_nanf("");
+  if (!head_ok) return;
+  // lane (c, j) holds head c's output dims 16 t + 4 j + e
+  const size_t hs = (size_t)s * hq + head;
+  if (whole) {
+    const float inv = 1.f / l_run;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[(wave * group + c) * D + 16 * t + 4 * j + i] = acc[t][i];
+      for (int e = 0; e < 4; ++e) store_out(a.out, hs * D + 16 * t + 4 * j + e, a.out_dtype, acc[t][e] * inv);
     }
+    if (j == 0 && a.fin_ml != nullptr) {
+      a.fin_ml[hs * 2 + 0] = m_run;
+      a.fin_ml[hs * 2 + 1] = l_run;
+    }
+  } else {
+    const size_t pi = hs * a.p_max + partial_slot(seg_vb0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(a.part_acc + pi * D + 16 * t + 4 * j) = acc[t];
     if (j == 0) {
-      s_ml[(wave * group + c) * 2 + 0] = m_run;
-      s_ml[(wave * group + c) * 2 + 1] = l_run;
-    }
-  }
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
-
-  for (int idx = threadIdx.x; idx < group * D; idx += blockDim.x) {
-    const int cc = idx / D, d = idx % D;
-    float mw[kPartWaves];
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kPartWaves; ++w) {
-      mw[w] = s_ml[(w * group + cc) * 2];
-      M = fmaxf(M, mw[w]);
-    }
-    float lsum = 0.f, o = 0.f;
-#pragma unroll
-    for (int w = 0; w < kPartWaves; ++w) {
-      const float f = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
-      lsum += f * s_ml[(w * group + cc) * 2 + 1];
-      o += f * s_acc[(w * group + cc) * D + d];
-    }
-    if (any_bad) lsum = __builtin_nanf("");
-    const size_t hs = (size_t)s * hq + (size_t)kvh * group + cc;
-    if (nparts == 1) {
-      store_out(a.out, hs * D + d, a.out_dtype, o / lsum);
-      if (d == 0 && a.fin_ml != nullptr) {
-        a.fin_ml[hs * 2 + 0] = M;
-        a.fin_ml[hs * 2 + 1] = lsum;
-      }
-    } else {
-      const size_t pi = hs * a.p_max + part;
-      a.part_acc[pi * D + d] = o;
-      if (d == 0) {
-        a.part_ml[pi * 2 + 0] = M;
-        a.part_ml[pi * 2 + 1] = lsum;
-      }
+      a.part_ml[pi * 2 + 0] = m_run;
+      a.part_ml[pi * 2 + 1] = l_run;
     }
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head) per wave.
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ int wave_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Persistent decode attention with single-wave workgroups, as many as the GPU
+// holds at once.
+//
+// The attended blocks of all sequences form one sequence-major list, cut into
+// n_ranges ranges of R blocks (R >= kPartBlocks).  Workgroup w takes one range
+// for one KV head; with the head-fastest order the KV heads of a range -- whose
+// tiles sit side by side in the pool -- are read at the same time, and since
+// workgroup ids go to the 8 XCDs in turn every XCD gets the same share.  A
+// range is cut at sequence boundaries into segments: a segment that is a whole
+// sequence writes the output directly, the others write partials that
+// attn_reduce_kernel merges.  Cuts inside a sequence are multiples of R, so
+// partial slots (partial_slot) are distinct.
+template <int KVT, int QT, int D>
+__global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
+  const int hkv = a.num_kv_heads;
+  const int B = a.num_seqs;
+  const int lane = threadIdx.x;
+  const int n_ranges = gridDim.x / hkv;
+#if PKV_ATTN_HEAD_FAST
+  const int r = blockIdx.x / hkv;
+  const int kvh = blockIdx.x % hkv;
+#else
+  const int r = blockIdx.x % n_ranges;
+  const int kvh = blockIdx.x / n_ranges;
+#endif
+
+  // Pass 1: total attended blocks; workgroup 0 records the per-sequence prefix
+  // and R for the merge kernel; NaN outputs for unusable lengths.
+  int total = 0;
+  for (int base = 0; base < B; base += kWave) {
+    const int sq = base + lane;
+    const int nva = sq < B ? attended_blocks(a, a.context_lens[sq]) : 0;
+    const int incl = wave_scan(nva);
+    if (blockIdx.x == 0 && sq < B) a.seq_prefix[sq] = total + incl - nva;
+    if (sq < B && nva == 0 && sq % (int)gridDim.x == (int)blockIdx.x) {
+      for (int idx = 0; idx < a.num_q_heads * D; ++idx)
+        store_out(a.out, (size_t)sq * a.num_q_heads * D + idx, a.out_dtype, __builtin_nanf(""));
+    }
+    total += __shfl(incl, kWave - 1, kWave);
+  }
+  int per = (int)(((long long)total + n_ranges - 1) / n_ranges);
+  if (per < kPartBlocks) per = kPartBlocks;
+  if (blockIdx.x == 0 && lane == 0) {
+    a.seq_prefix[B] = total;
+    a.hdr->per = per;
+  }
+  const long long u0 = (long long)r * per;
+  if (u0 >= total) return;
+  const long long u1 = min(u0 + per, (long long)total);
+
+  // Pass 2: the sequence holding block u0, and its prefix.
+  int sq = -1, prefix = 0, run = 0;
+  for (int base = 0; base < B && sq < 0; base += kWave) {
+    const int q = base + lane;
+    const int nva = q < B ? attended_blocks(a, a.context_lens[q]) : 0;
+    const int incl = wave_scan(nva);
+    const int excl = run + incl - nva;
+    const unsigned long long hit = __ballot(nva > 0 && excl <= u0 && u0 < excl + nva);
+    if (hit != 0ull) {
+      const int src = __ffsll((long long)hit) - 1;
+      sq = base + src;
+      prefix = __shfl(excl, src, kWave);
+    }
+    run += __shfl(incl, kWave - 1, kWave);
+  }
+  sq = __builtin_amdgcn_readfirstlane(sq);
+  prefix = __builtin_amdgcn_readfirstlane(prefix);
+
+  long long u = u0;
+  while (u < u1) {
+    const int L = a.context_lens[sq];
+    const int nva = attended_blocks(a, L);
+    const int vb = (int)(u - prefix);
+    const int cnt = (int)min((long long)(nva - vb), u1 - u);
+    wave_segment<KVT, QT, D>(a, sq, kvh, L, vb, vb + cnt);
+    u += cnt;
+    if (u < u1) {
+      // next sequence with attended blocks (one exists: u < total)
+      prefix += nva;
+      ++sq;
+      while (attended_blocks(a, a.context_lens[sq]) == 0) ++sq;
+    }
+  }
+}
+
+// Log-sum-exp merge of one (sequence, query head) per wave: the partials of the
+// segments the sequence was cut into (block 0 and every multiple of R inside
+// the sequence's span of the block list).  A sequence that was one segment
+// already has its output.
 template <int D>
 __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
   const int s = blockIdx.y;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (h >= a.num_q_heads) return;
-  const int L = a.context_lens[s];
-  const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
-  if (L < 1 || L > len_cap) return;                 // the partition kernel wrote NaN
-  const int nparts = num_partitions(keep_geometry(L, a.num_sinks, a.window).n_virtual);
-  if (nparts <= 1) return;                          // written by the partition kernel
+  const int nva = attended_blocks(a, a.context_lens[s]);
+  if (nva == 0) return;                             // NaN already written
+  const int per = a.hdr->per;
+  const int base = a.seq_prefix[s];
+  const int end = base + nva;
+  const int c0 = (base / per + 1) * per;            // first cut after the sequence start
+  if (c0 >= end) return;                            // one segment: written directly
   const size_t hs = (size_t)s * a.num_q_heads + h;
   const float* ml = a.part_ml + hs * a.p_max * 2;
-  float M = -INFINITY;
-  for (int i = 0; i < nparts; ++i) M = fmaxf(M, ml[2 * i]);
+  const float* pacc = a.part_acc + hs * a.p_max * D;
+  float M = ml[0];
+  for (int b = c0; b < end; b += per) M = fmaxf(M, ml[2 * partial_slot(b - base)]);
   constexpr int DL = D / 64;
   float o[DL];
+  float lsum;
+  {
+    const float f = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
+    lsum = f * ml[1];
 #pragma unroll
-  for (int e = 0; e < DL; ++e) o[e] = 0.f;
-  float lsum = 0.f;
-  const float* pacc = a.part_acc + hs * a.p_max * D;
-  for (int i = 0; i < nparts; ++i) {
-    const float mi = ml[2 * i];
+    for (int e = 0; e < DL; ++e) o[e] = f * pacc[e * 64 + lane];
+  }
+  for (int b = c0; b < end; b += per) {
+    const int slot = partial_slot(b - base);
+    const float mi = ml[2 * slot];
     const float f = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
-    lsum += f * ml[2 * i + 1];
+    lsum += f * ml[2 * slot + 1];
 #pragma unroll
-    for (int e = 0; e < DL; ++e) o[e] += f * pacc[(size_t)i * D + e * 64 + lane];
+    for (int e = 0; e < DL; ++e) o[e] += f * pacc[(size_t)slot * D + e * 64 + lane];
   }
 #pragma unroll
   for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + e * 64 + lane, a.out_dtype, o[e] / lsum);
@@ -559,26 +643,53 @@ __global__ void __launch_bounds__(256) attn_mass_kernel(const AttnArgs a) {
 
 namespace {
 
+// Single-wave workgroups launched: per CU, as many as fit (or the build-time
+// count), times the CU count; cached per device.
 template <int KVT, int QT, int D>
-hipError_t launch_partition(const AttnArgs& a, hipStream_t st) {
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const size_t smem = (size_t)kPartWaves * group * (D + 2) * sizeof(float);
-  dim3 grid(a.num_kv_heads, a.num_seqs, a.p_max);
-  hipLaunchKernelGGL((attn_partition_kernel<KVT, QT, D>), grid, dim3(256), smem, st, a);
-  return hipGetLastError();
+int resident_waves() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wave_kernel<KVT, QT, D>, kWave, 0) != hipSuccess)
+    return 0;
+  if (per_cu < 1) per_cu = 1;
+  if (PKV_ATTN_WAVES_PER_CU > 0 && PKV_ATTN_WAVES_PER_CU < per_cu) per_cu = PKV_ATTN_WAVES_PER_CU;
+  const int n = cus * per_cu;
+  cache[dev] = n;
+  return n;
+}
+
+template <int KVT, int QT, int D>
+hipError_t launch_partition(const AttnArgs& a, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  const int waves = resident_waves<KVT, QT, D>();
+  if (waves <= 0) return hipErrorInvalidDevice;
+  const int n_ranges = waves / a.num_kv_heads > 0 ? waves / a.num_kv_heads : 1;
+  hipError_t err = hipSuccess;
+  if (ev_begin) err = hipEventRecord(ev_begin, st);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((attn_wave_kernel<KVT, QT, D>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st, a);
+  err = hipGetLastError();
+  if (err == hipSuccess && ev_end) err = hipEventRecord(ev_end, st);
+  return err;
 }
 
 template <int KVT, int QT>
-hipError_t dispatch_d(const AttnArgs& a, int d, hipStream_t st) {
-  return d == 64 ? launch_partition<KVT, QT, 64>(a, st) : launch_partition<KVT, QT, 128>(a, st);
+hipError_t dispatch_d(const AttnArgs& a, int d, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
+  return d == 64 ? launch_partition<KVT, QT, 64>(a, st, eb, ee) : launch_partition<KVT, QT, 128>(a, st, eb, ee);
 }
 
 template <int KVT>
-hipError_t dispatch_q(const AttnArgs& a, int q_dtype, int d, hipStream_t st) {
+hipError_t dispatch_q(const AttnArgs& a, int q_dtype, int d, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
   switch (q_dtype) {
-    case DT_F32: return dispatch_d<KVT, DT_F32>(a, d, st);
-    case DT_BF16: return dispatch_d<KVT, DT_BF16>(a, d, st);
-    default: return dispatch_d<KVT, DT_F16>(a, d, st);
+    case DT_F32: return dispatch_d<KVT, DT_F32>(a, d, st, eb, ee);
+    case DT_BF16: return dispatch_d<KVT, DT_BF16>(a, d, st, eb, ee);
+    default: return dispatch_d<KVT, DT_F16>(a, d, st, eb, ee);
   }
 }
 
@@ -590,7 +701,7 @@ WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_di
                                       int num_sinks, int window, bool want_mass) {
   WorkspaceLayout w{};
   const int nv = max_virtual_blocks(max_context_len, num_sinks, window);
-  w.p_max = num_partitions(nv);
+  w.p_max = num_partitions(nv) + 1;   // partial_slot() is at most ceil(blocks / kPartBlocks)
   w.nv_pad = nv * kBlockSize;
   const size_t bh = (size_t)num_seqs * num_q_heads;
   size_t off = 0;
@@ -598,6 +709,10 @@ WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_di
   off = align256(off + bh * w.p_max * head_dim * sizeof(float));
   w.ml_off = off;
   off = align256(off + bh * w.p_max * 2 * sizeof(float));
+  w.hdr_off = off;
+  off = align256(off + sizeof(StreamHdr));
+  w.prefix_off = off;
+  off = align256(off + ((size_t)num_seqs + 1) * sizeof(int));
   if (want_mass) {
     w.stash_off = off;
     off = align256(off + bh * w.nv_pad * sizeof(float));
@@ -612,22 +727,14 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
                               hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (a.num_seqs == 0) return hipSuccess;
   hipError_t err;
-  if (ev_begin) {
-    err = hipEventRecord(ev_begin, st);
-    if (err != hipSuccess) return err;
-  }
   switch (kv_dtype) {
-    case DT_F32: err = dispatch_q<DT_F32>(a, q_dtype, head_dim, st); break;
-    case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st); break;
-    case DT_F16: err = dispatch_q<DT_F16>(a, q_dtype, head_dim, st); break;
-    default: err = dispatch_q<DT_FP8>(a, q_dtype, head_dim, st); break;
+    case DT_F32: err = dispatch_q<DT_F32>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    case DT_F16: err = dispatch_q<DT_F16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    default: err = dispatch_q<DT_FP8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
   }
   if (err != hipSuccess) return err;
-  if (ev_end) {
-    err = hipEventRecord(ev_end, st);
-    if (err != hipSuccess) return err;
-  }
-  if (a.p_max > 1) {
+  {
     dim3 grid((a.num_q_heads + 3) / 4, a.num_seqs);
     if (head_dim == 64) hipLaunchKernelGGL((attn_reduce_kernel<64>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_reduce_kernel<128>), grid, dim3(256), 0, st, a);

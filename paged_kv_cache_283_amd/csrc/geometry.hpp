@@ -18,10 +18,9 @@ namespace pkv {
 
 constexpr int kBlockSize = 16;    // tokens per physical block
 #ifndef PKV_PART_BLOCKS
-#define PKV_PART_BLOCKS 32
+#define PKV_PART_BLOCKS 16
 #endif
-constexpr int kPartBlocks = PKV_PART_BLOCKS;   // attended blocks per partition (512 tokens)
-constexpr int kPartWaves = 4;     // waves per partition workgroup
+constexpr int kPartBlocks = PKV_PART_BLOCKS;   // attended blocks per partial-output slot (256 tokens)
 
 struct KeepGeom {
   int n_sink_blocks;  // virtual blocks [0, n_sink_blocks) are logical blocks 0..n_sink_blocks-1

@@ -8,6 +8,12 @@
 
 namespace pkv {
 
+// Per-call schedule the attention kernel hands to the merge kernel (workspace).
+struct StreamHdr {
+  int per;               // attended blocks per range (R)
+  int pad[3];
+};
+
 struct AttnArgs {
   void* out;
   int out_dtype;
@@ -30,12 +36,14 @@ struct AttnArgs {
   float* part_ml;       // [B][Hq][p_max][2]   partition max (base-2) and exp-sum
   float* stash;         // [B][Hq][nv_pad]     base-2 logits per attended position (mass only)
   float* fin_ml;        // [B][Hq][2]          global max and exp-sum (mass only)
+  StreamHdr* hdr;       // schedule of this call
+  int* seq_prefix;      // [B + 1]  attended-block prefix per sequence, then the total
   int p_max;
   int nv_pad;
 };
 
 struct WorkspaceLayout {
-  size_t acc_off, ml_off, stash_off, fin_off, total;
+  size_t acc_off, ml_off, hdr_off, prefix_off, stash_off, fin_off, total;
   int p_max, nv_pad;
 };
 
