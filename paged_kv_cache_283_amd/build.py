@@ -35,7 +35,9 @@ def hipcc() -> str:
 
 def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    # HIP sources: MFMA accumulators stay in VGPRs (no AGPR copies around the
+    # VALU work on them).
+    lang = ["-x", "hip", "-mllvm", "-amdgpu-mfma-vgpr-form"] if src.endswith(".hip") else []
     cmd = [hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

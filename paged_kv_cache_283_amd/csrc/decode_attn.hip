@@ -118,13 +118,16 @@ constexpr float kRescaleSlack = 8.f;
 
 // Build-time tuning knobs (defaults are the measured choice).
 #ifndef PKV_ATTN_PIPE
-#define PKV_ATTN_PIPE 3              // K/V register buffers per wave: blocks in flight = PIPE - 1
+#define PKV_ATTN_PIPE 3              // K/V register buffers per wave (2 or 3): blocks in flight = PIPE - 1
 #endif
 #ifndef PKV_ATTN_NT_LOADS
-#define PKV_ATTN_NT_LOADS 0          // 1: K/V tiles loaded with the non-temporal hint
+#define PKV_ATTN_NT_LOADS 1          // 1: K/V tiles loaded with the non-temporal hint (read once)
 #endif
 #ifndef PKV_ATTN_WAVES_PER_CU
-#define PKV_ATTN_WAVES_PER_CU 0      // waves launched per CU (0: as many as fit)
+#define PKV_ATTN_WAVES_PER_CU 4      // waves launched per CU, one per SIMD (0: as many as fit)
+#endif
+#ifndef PKV_ATTN_WAVES_PER_CU_FP8
+#define PKV_ATTN_WAVES_PER_CU_FP8 8  // the same for FP8 pools (two per SIMD)
 #endif
 #ifndef PKV_ATTN_HEAD_FAST
 #define PKV_ATTN_HEAD_FAST 1         // 1: workgroup id = range * KV heads + head; 0: head-major
@@ -138,6 +141,9 @@ __device__ __forceinline__ T load_stream(const T* p) {
   return *p;
 #endif
 }
+
+// Table entries staged in LDS per chunk of a segment.
+constexpr int kTabBlocks = 1024;
 
 // Partial-output slot of a segment starting at attended block vb of its
 // sequence: 0 for the first segment, vb / kPartBlocks + 1 for one starting at a
@@ -156,7 +162,8 @@ __device__ __forceinline__ int attended_blocks(const AttnArgs& a, int L) {
 // whole sequence) or a partial (running max, exp-sum, unnormalised output) in
 // slot partial_slot(seg_vb0).
 template <int KVT, int QT, int D>
-__device__ __forceinline__ void wave_segment(const AttnArgs& a, int s, int kvh, int L, int seg_vb0, int seg_vb1) {
+__device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int s, int kvh, int L, int seg_vb0,
+                                             int seg_vb1) {
   using KT = KvType<KVT>;
   constexpr int EB = KT::kBytes;
   constexpr bool OP32 = KT::kOp32;
@@ -236,14 +243,14 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int s, int kvh, 
     bool ok;
   };
 
-  int sub0 = seg_vb0;   // first block of the current batch (at most 64 blocks)
-  int my_phys = -1;     // lane i: physical block of the batch's i-th block
+  int c0 = seg_vb0;     // first block of the current table chunk (s_tab[i] = entry of block c0 + i)
 
   auto load = [&](Regs& r, int i) {
-    const int phys = __builtin_amdgcn_readlane(my_phys, i);
+    const int phys = __builtin_amdgcn_readfirstlane(s_tab[i]);
     r.ok = phys >= 0 && phys < a.num_blocks;
-    if (!r.ok) return;
-    const size_t tile = (size_t)phys * a.num_kv_heads + kvh;
+    // An entry outside the pool reads block 0 instead (in bounds) and marks the
+    // result bad; no branch around the loads keeps the wait counts exact.
+    const size_t tile = (size_t)(r.ok ? phys : 0) * a.num_kv_heads + kvh;
     // K tile [D/X][16][X]: load u gives lane (c, j) chunk 4u + j of token row c,
     // and the 64 lanes of one load read 1 KiB of contiguous memory.
     const uint8_t* kt = kbase + tile * (size_t)(kBlockSize * D * EB);
@@ -273,8 +280,8 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int s, int kvh, 
   };
 
   auto compute = [&](Regs& r, int i) {
-    if (!r.ok) { bad = true; return; }
-    const int vb = sub0 + i;
+    bad |= !r.ok;   // outputs become NaN; the block is still computed
+    const int vb = c0 + i;
     const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
 
     // ---- S = K q^T: lane (c, j) receives head c's logits of tokens 4j..4j+3
@@ -406,48 +413,51 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int s, int kvh, 
     }
   };
 
-  for (; sub0 < seg_vb1; sub0 += kWave) {
-    // Lane i fetches the table entry of the batch's i-th block once; each step
-    // broadcasts it with readlane, so no table load sits between a block and
-    // its K/V loads.
-    const int n_mine = min(kWave, seg_vb1 - sub0);
-    my_phys = -1;
-    if (lane < n_mine) my_phys = trow[logical_block(sub0 + lane, geo.n_sink_blocks, geo.win_start)];
-#if PKV_ATTN_PIPE == 1
-    Regs r0;
-    for (int i = 0; i < n_mine; ++i) {
-      load(r0, i);
-      compute(r0, i);
-    }
-#elif PKV_ATTN_PIPE == 2
+  for (; c0 < seg_vb1; c0 += kTabBlocks) {
+    // The chunk's table entries go to LDS first: the loop reads them with LDS
+    // loads, whose wait counter is separate from the K/V loads', so the
+    // compiler can wait for exactly the block about to be computed.
+    const int n = min(kTabBlocks, seg_vb1 - c0);
+    for (int k = lane; k < n; k += kWave) s_tab[k] = trow[logical_block(c0 + k, geo.n_sink_blocks, geo.win_start)];
+    __syncthreads();
+#if PKV_ATTN_PIPE == 2
     // Software pipeline: block i+1's loads are in flight while block i computes.
     Regs ra, rb;
     int i = 0;
-    if (n_mine > 0) load(ra, 0);
-    for (; i + 1 < n_mine; i += 2) {
+    if (n > 0) load(ra, 0);
+    for (; i + 2 < n; i += 2) {   // steady state: every load unconditional
       load(rb, i + 1);
       compute(ra, i);
-      if (i + 2 < n_mine) load(ra, i + 2);
+      load(ra, i + 2);
       compute(rb, i + 1);
     }
-    if (i < n_mine) compute(ra, i);
+    // at most 2 blocks left; ra holds block i
+    if (i + 1 < n) load(rb, i + 1);
+    if (i < n) compute(ra, i);
+    if (i + 1 < n) compute(rb, i + 1);
 #else
     // Software pipeline: blocks i+1 and i+2 are in flight while block i computes.
     Regs r0, r1, r2;
     int i = 0;
-    if (n_mine > 0) load(r0, 0);
-    if (n_mine > 1) load(r1, 1);
-    for (; i + 2 < n_mine; i += 3) {
+    if (n > 0) load(r0, 0);
+    if (n > 1) load(r1, 1);
+    for (; i + 4 < n; i += 3) {   // steady state: every load unconditional
       load(r2, i + 2);
       compute(r0, i);
-      if (i + 3 < n_mine) load(r0, i + 3);
+      load(r0, i + 3);
       compute(r1, i + 1);
-      if (i + 4 < n_mine) load(r1, i + 4);
+      load(r1, i + 4);
       compute(r2, i + 2);
     }
-    if (i < n_mine) compute(r0, i);
-    if (i + 1 < n_mine) compute(r1, i + 1);
+    // at most 4 blocks left; r0, r1 hold blocks i, i+1 where they exist
+    if (i + 2 < n) load(r2, i + 2);
+    if (i < n) compute(r0, i);
+    if (i + 3 < n) load(r0, i + 3);
+    if (i + 1 < n) compute(r1, i + 1);
+    if (i + 2 < n) compute(r2, i + 2);
+    if (i + 3 < n) compute(r0, i + 3);
 #endif
+    __syncthreads();   // s_tab is rewritten by the next chunk
   }
 
   l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
@@ -502,6 +512,7 @@ __device__ __forceinline__ int wave_scan(int v) {
 // partial slots (partial_slot) are distinct.
 template <int KVT, int QT, int D>
 __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
+  __shared__ int s_tab[kTabBlocks];
   const int hkv = a.num_kv_heads;
   const int B = a.num_seqs;
   const int lane = threadIdx.x;
@@ -562,7 +573,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     const int nva = attended_blocks(a, L);
     const int vb = (int)(u - prefix);
     const int cnt = (int)min((long long)(nva - vb), u1 - u);
-    wave_segment<KVT, QT, D>(a, sq, kvh, L, vb, vb + cnt);
+    wave_segment<KVT, QT, D>(a, s_tab, sq, kvh, L, vb, vb + cnt);
     u += cnt;
     if (u < u1) {
       // next sequence with attended blocks (one exists: u < total)
@@ -659,7 +670,8 @@ int resident_waves() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wave_kernel<KVT, QT, D>, kWave, 0) != hipSuccess)
     return 0;
   if (per_cu < 1) per_cu = 1;
-  if (PKV_ATTN_WAVES_PER_CU > 0 && PKV_ATTN_WAVES_PER_CU < per_cu) per_cu = PKV_ATTN_WAVES_PER_CU;
+  const int want = KVT == DT_FP8 ? PKV_ATTN_WAVES_PER_CU_FP8 : PKV_ATTN_WAVES_PER_CU;
+  if (want > 0 && want < per_cu) per_cu = want;
   const int n = cus * per_cu;
   cache[dev] = n;
   return n;

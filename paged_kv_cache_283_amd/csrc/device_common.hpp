@@ -45,14 +45,13 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
 // Element e (0/1) of a word holding two 16-bit values.
 __device__ __forceinline__ uint32_t half_word(uint32_t w, int e) { return e ? (w >> 16) : (w & 0xffffu); }
 
-// Four OCP E4M3FN codes (one word) -> four bf16 values (two words), exactly:
-// every E4M3 value is representable in bf16, so the upper half of the fp32
-// conversion is the bf16 encoding.
+// Four OCP E4M3FN codes (one word) -> four bf16 values (two words; byte 0 in
+// the low half of lo), exactly: every E4M3 value is a bf16 value.  The gfx950
+// v_cvt_scalef32_pk_bf16_fp8 converts two codes per instruction (scale 1; the
+// NaN codes give NaN).
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-  lo = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
-  hi = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 // Wave64 butterfly reductions over lanes that differ in bits 4 and 5 of the
