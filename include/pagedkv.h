@@ -31,7 +31,10 @@
  *   k_pool  [num_blocks][num_kv_heads][head_dim/X][16][X]   K tile in 16-byte chunks:
  *           X = 16 / element bytes (8 for BF16/F16, 16 for FP8, 4 for F32); element
  *           (token o, dim d) of a tile is at [d / X][o][d % X]
- *   v_pool  [num_blocks][num_kv_heads][head_dim][16]        dim-major tile
+ *   v_pool  [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4]   V tile in 16-byte
+ *           chunks: Y = 4 / element bytes (2 for BF16/F16, 4 for FP8, 1 for F32);
+ *           element (token o, dim d), t = d / 16, is at [t / Y][d % 16][o / 4][t % Y][o % 4]
+ *           (each chunk: 4 consecutive tokens of Y dims that are 16 apart)
  *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 only)
  * A token at logical position p of a sequence lives in physical block
  * table[p / 16] at offset p % 16 ([PA] "物理布局示意", [LC] block-table sketch);

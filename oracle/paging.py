@@ -11,12 +11,16 @@ names at index j; physical blocks come from one shared pool.  What they leave
 open and is taken here as the storage convention (the same one the HIP
 library documents):
 
-  K pool  [num_blocks][num_kv_heads][head_dim/X][16][X]   X = 16 bytes of elements:
-                                                         8 for bf16/f16, 16 for fp8, 4 for f32
-  V pool  [num_blocks][num_kv_heads][head_dim][16]        dim-major tile
-  scales  [num_blocks][num_kv_heads][16] float32          FP8 only, K and V separately
+  K pool  [num_blocks][num_kv_heads][head_dim/X][16][X]          X = 16 bytes of elements:
+                                                                8 for bf16/f16, 16 for fp8, 4 for f32
+  V pool  [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4] Y = 4 / bytes per element:
+                                                                2 for bf16/f16, 4 for fp8, 1 for f32
+  scales  [num_blocks][num_kv_heads][16] float32                 FP8 only, K and V separately
 
-(K element (token o, dim d) of a block tile sits at chunk d // X, row o, lane d % X.)
+(K element (token o, dim d) of a block tile sits at chunk d // X, row o, lane
+d % X.  V element (token o, dim d), with t = d // 16, sits at index
+[t // Y][d % 16][o // 4][t % Y][o % 4]: each 16-byte chunk holds 4 consecutive
+tokens of Y dims 16 apart.)
 
 Storage dtypes are held here as raw numpy arrays: "f32" float32, "bf16" uint16
 bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes.
@@ -71,12 +75,37 @@ def slot(table_row, pos: int, num_blocks: int, block_size: int = BLOCK_SIZE) -> 
     return physical_block(table_row, pos, num_blocks, block_size) * block_size + pos % block_size
 
 
+def v_chunk_dims(kv_dtype: str) -> int:
+    """Dims (16 apart) per 16-byte V chunk of 4 tokens."""
+    return 4 // np.dtype(_STORAGE[kv_dtype]).itemsize
+
+
+def _v_groups(head_dim: int, kv_dtype: str) -> int:
+    y = v_chunk_dims(kv_dtype)
+    if head_dim % (16 * y):
+        raise ValueError(f"head_dim {head_dim} is not a multiple of {16 * y} ({kv_dtype} V chunks)")
+    return head_dim // (16 * y)
+
+
+def _v_put(v_tile_o, row, kv_dtype):
+    """Store row[Hkv][D] into the V chunks of one token offset: view [Hkv][G][16][Y]."""
+    hkv, g, c, y = v_tile_o.shape
+    v_tile_o[...] = np.asarray(row).reshape(hkv, g, y, c).transpose(0, 1, 3, 2)
+
+
+def _v_get(v_tile_o):
+    """Inverse of _v_put: [Hkv][G][16][Y] chunk view -> [Hkv][D]."""
+    hkv, g, c, y = v_tile_o.shape
+    return v_tile_o.transpose(0, 1, 3, 2).reshape(hkv, g * y * c)
+
+
 def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, fill=0):
     """Allocate (k_pool, v_pool, k_scale, v_scale) in the documented layout; scales None unless fp8."""
     st = storage_dtype(kv_dtype)
     x = k_chunk(kv_dtype)
+    y = v_chunk_dims(kv_dtype)
     k = np.full((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x), fill, dtype=st)
-    v = np.full((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), fill, dtype=st)
+    v = np.full((num_blocks, num_kv_heads, _v_groups(head_dim, kv_dtype), 16, 4, y, 4), fill, dtype=st)
     if kv_dtype == "fp8":
         ks = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
         vs = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
@@ -108,12 +137,12 @@ def write_tokens(pools, kv_dtype: str, k_src, v_src, src_dtype: str, table_rows,
         o = p % BLOCK_SIZE
         if kv_dtype == "fp8":
             k_pool[b, :, :, o, :] = kq[t].reshape(hkv, nc, x)
-            v_pool[b, :, :, o] = vq[t]
+            _v_put(v_pool[b, :, :, :, o // 4, :, o % 4], vq[t], kv_dtype)
             k_scale[b, :, o] = ks[t]
             v_scale[b, :, o] = vs[t]
         else:
             k_pool[b, :, :, o, :] = np.asarray(k_src[t]).reshape(hkv, nc, x)
-            v_pool[b, :, :, o] = v_src[t]
+            _v_put(v_pool[b, :, :, :, o // 4, :, o % 4], v_src[t], kv_dtype)
 
 
 def gather_logical(pools, kv_dtype: str, table_row, positions, num_blocks=None):
@@ -131,7 +160,7 @@ def gather_logical(pools, kv_dtype: str, table_row, positions, num_blocks=None):
         b = physical_block(table_row, int(p), nb)
         o = int(p) % BLOCK_SIZE
         k = to_f64(k_pool[b, :, :, o, :].reshape(hkv, d), kv_dtype)
-        v = to_f64(v_pool[b, :, :, o], kv_dtype)
+        v = to_f64(_v_get(v_pool[b, :, :, :, o // 4, :, o % 4]), kv_dtype)
         if kv_dtype == "fp8":
             k = k * k_scale[b, :, o].astype(np.float64)[:, None]
             v = v * v_scale[b, :, o].astype(np.float64)[:, None]

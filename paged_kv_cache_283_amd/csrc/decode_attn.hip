@@ -25,7 +25,8 @@
 //    rows of a group live in registers for the whole segment).  The
 //    accumulator gives lane (c, j) the logits of head c for tokens 4j..4j+3.
 //  * PV is a second MFMA per 16 head-dims: A = the dim-major V tile (lane
-//    (d, j) reads tokens 4j..4j+3 of dim d: one 8-byte load for bf16), B =
+//    (d, j) holds tokens 4j..4j+3 of dim d; V is stored in 16-byte chunks that
+//    give each lane this for 16 / (4 bytes per element) tiles at once), B =
 //    the probabilities exactly as the QK accumulator left them in registers,
 //    so no LDS round trip or transpose sits between the two products.  The
 //    output accumulator again puts head c in lane column c, next to its
@@ -259,19 +260,15 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
       const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(kt + ((size_t)(4 * w + j) * kBlockSize + c) * 16));
       r.k[4 * w + 0] = v[0]; r.k[4 * w + 1] = v[1]; r.k[4 * w + 2] = v[2]; r.k[4 * w + 3] = v[3];
     }
-    const uint8_t* vp = vbase + (tile * D + c) * (size_t)(kBlockSize * EB) + (size_t)j * (4 * EB);
+    // V tile in 16-byte chunks: load g gives lane (c, j) tokens 4j..4j+3 of
+    // dims 16 t + c for the Y = 4 / EB tiles t = g Y .. g Y + Y - 1, which is
+    // words [4 g, 4 g + 4) of r.v in [tile][word] order; 1 KiB per load.
+    const uint8_t* vt = vbase + tile * (size_t)(kBlockSize * D * EB);
+    uint32_t* vw = &r.v[0][0];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint8_t* q = vp + (size_t)t * 16 * kBlockSize * EB;
-      if constexpr (VW == 1) {
-        r.v[t][0] = load_stream(reinterpret_cast<const uint32_t*>(q));
-      } else if constexpr (VW == 2) {
-        const u32x2 v = load_stream(reinterpret_cast<const u32x2*>(q));
-        r.v[t][0] = v[0]; r.v[t][1] = v[1];
-      } else {
-        const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(q));
-        r.v[t][0] = v[0]; r.v[t][1] = v[1]; r.v[t][2] = v[2]; r.v[t][3] = v[3];
-      }
+    for (int g = 0; g < NT * VW / 4; ++g) {
+      const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(vt + ((size_t)(g * 16 + c) * 4 + j) * 16));
+      vw[4 * g + 0] = v[0]; vw[4 * g + 1] = v[1]; vw[4 * g + 2] = v[2]; vw[4 * g + 3] = v[3];
     }
     if constexpr (KVT == DT_FP8) {
       r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile * kBlockSize + 4 * j);

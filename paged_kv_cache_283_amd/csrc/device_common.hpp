@@ -87,6 +87,17 @@ __device__ __forceinline__ int k_chunk_offset(int o, int d) {
   return ((d / X) * kBlockSize + o) * X + d % X;
 }
 
+// Element offset of V element (token o, dim d) inside a (block, KV head) tile
+// stored in 16-byte chunks: chunk (g, c, j) holds tokens 4j..4j+3 of the Y = 4/EB
+// dims 16 (g Y + u) + c, u < Y (u-major, then token), i.e. the tile is
+// [D/(16 Y)][16][4][Y][4].  One lane's chunk is the PV operand of Y MFMA tiles.
+template <int EB>
+__device__ __forceinline__ int v_chunk_offset(int o, int d) {
+  constexpr int Y = 4 / EB;
+  const int t = d / 16;
+  return ((((t / Y) * 16 + d % 16) * 4 + o / 4) * Y + t % Y) * 4 + o % 4;
+}
+
 // Logical block of virtual (attended) block vb: sink blocks first, then the window.
 __device__ __forceinline__ int logical_block(int vb, int n_sink_blocks, int win_start) {
   return vb < n_sink_blocks ? vb : win_start + (vb - n_sink_blocks);

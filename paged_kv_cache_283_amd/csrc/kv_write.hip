@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
       const uint32_t kc = ks == 0.f ? 0u : e4m3fn_encode(__fdiv_rn(kx[e], ks));
       const uint32_t vc = vs == 0.f ? 0u : e4m3fn_encode(__fdiv_rn(vx[e], vs));
       kp[tile * kBlockSize * D + k_chunk_offset<1>(o, d)] = (uint8_t)kc;
-      vp[(tile * D + d) * kBlockSize + o] = (uint8_t)vc;
+      vp[tile * kBlockSize * D + v_chunk_offset<1>(o, d)] = (uint8_t)vc;
     }
     if (lane == 0) {
       k_scale[tile * kBlockSize + o] = ks;
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
     for (int e = 0; e < PER; ++e) {
       const int d = e * 64 + lane;
       kp[tile * kBlockSize * D + k_chunk_offset<sizeof(T)>(o, d)] = ks[src + d];
-      vp[(tile * D + d) * kBlockSize + o] = vs[src + d];
+      vp[tile * kBlockSize * D + v_chunk_offset<sizeof(T)>(o, d)] = vs[src + d];
     }
   }
 }

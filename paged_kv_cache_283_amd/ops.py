@@ -8,7 +8,8 @@ Storage dtypes: torch.float32 / bfloat16 / float16 pools hold those values;
 torch.uint8 or torch.float8_e4m3fn pools hold OCP E4M3FN codes with
 float32 scale tensors [num_blocks][num_kv_heads][16].  Pool shapes:
 K [num_blocks][num_kv_heads][head_dim/X][16][X] (X = 16 bytes of elements),
-V [num_blocks][num_kv_heads][head_dim][16]; allocate_pools builds both.
+V [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4] (Y = 4 / element bytes);
+allocate_pools builds both.
 """
 import ctypes
 import math
@@ -92,6 +93,18 @@ def k_pool_shape(num_blocks, num_kv_heads, head_dim, dtype):
     return (num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x)
 
 
+def v_chunk_dims(dtype: torch.dtype) -> int:
+    """Dims (16 apart) per 16-byte chunk of the V pool layout [NB][Hkv][D/(16Y)][16][4][Y][4]."""
+    return 4 // torch.empty((), dtype=dtype).element_size()
+
+
+def v_pool_shape(num_blocks, num_kv_heads, head_dim, dtype):
+    y = v_chunk_dims(dtype)
+    if head_dim % (16 * y):
+        raise ValueError(f"head_dim {head_dim} is not a multiple of {16 * y}")
+    return (num_blocks, num_kv_heads, head_dim // (16 * y), BLOCK_SIZE, 4, y, 4)
+
+
 def _need(t, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -132,8 +145,10 @@ def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_s
     if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
         raise ValueError("k_new and v_new must match")
     nb = k_pool.shape[0]
-    if tuple(k_pool.shape) != k_pool_shape(nb, hkv, d, k_pool.dtype) or tuple(v_pool.shape) != (nb, hkv, d, BLOCK_SIZE):
-        raise ValueError(f"pools must be {k_pool_shape(nb, hkv, d, k_pool.dtype)} (K) and [NB][{hkv}][{d}][16] (V)")
+    if (tuple(k_pool.shape) != k_pool_shape(nb, hkv, d, k_pool.dtype)
+            or tuple(v_pool.shape) != v_pool_shape(nb, hkv, d, v_pool.dtype)):
+        raise ValueError(f"pools must be {k_pool_shape(nb, hkv, d, k_pool.dtype)} (K) and "
+                         f"{v_pool_shape(nb, hkv, d, v_pool.dtype)} (V)")
     if slot_mapping.shape[0] != t:
         raise ValueError("slot_mapping must have one entry per token")
     return _issue("paged_kv_write", (_ptr(k_new), _ptr(v_new), float_code(k_new.dtype), _ptr(k_pool),
@@ -145,7 +160,7 @@ def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, 
     """(k_pool, v_pool, k_scale, v_scale) in the library's layout; scales are None unless kv_dtype is FP8
     (torch.uint8 or torch.float8_e4m3fn).  fill_byte sets every byte (0xFF = NaN everywhere)."""
     k = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
-    v = torch.empty((num_blocks, num_kv_heads, head_dim, BLOCK_SIZE), dtype=kv_dtype, device=device)
+    v = torch.empty(v_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
     ks = vs = None
     if kv_code(kv_dtype) == _lib.FP8_E4M3:
         ks = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)

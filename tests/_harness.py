@@ -25,6 +25,12 @@ def k_token_rows(k_pool):
     return k_pool.permute(0, 3, 1, 2, 4).reshape(nb * bs, hkv, nc * x)
 
 
+def v_token_rows(v_pool):
+    """View of a V pool [NB][Hkv][G][16][4][Y][4] as [num_blocks * 16][Hkv][D] token rows (a copy)."""
+    nb, hkv, g, c, j, y, e = v_pool.shape
+    return v_pool.permute(0, 4, 6, 1, 2, 5, 3).reshape(nb * j * e, hkv, g * y * c)
+
+
 def make_pools(w, num_blocks, device=DEV):
     """Pools of the workload's shape, every byte 0xFF (NaN) so unwritten slots poison any read."""
     return ops.allocate_pools(num_blocks, w.num_kv_heads, w.head_dim, W.storage_dtype(w.kv_dtype), device, 0xFF)

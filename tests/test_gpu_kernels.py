@@ -119,7 +119,7 @@ def test_fp8_encoder_on_crafted_values():
     assert torch.all(ks.view(-1)[:n] == 1.0)
     codes = H.k_token_rows(kp).view(nb * 16, d)[:n].cpu().numpy()
     assert np.array_equal(codes, fp8.encode(rows))
-    vcodes = vp.view(nb, d, 16).permute(0, 2, 1).reshape(nb * 16, d)[:n].cpu().numpy()
+    vcodes = H.v_token_rows(vp).view(nb * 16, d)[:n].cpu().numpy()
     assert np.array_equal(vcodes, codes)
 
 
@@ -129,16 +129,16 @@ def test_fp8_zero_rows_and_skipped_slots():
     kp, vp, ks, vs = ops.allocate_pools(2, 2, 64, torch.uint8, "cuda", fill_byte=0xFF)
     ops.paged_kv_write(k, k, kp, vp, torch.tensor([3, -1, 40], dtype=torch.int64).cuda(), ks, vs)
     # token 0 -> slot 3 (all zero: scale 0, codes 0); token 1 skipped (-1); token 2 out of the pool, skipped
-    assert torch.all(kp[0, :, :, 3] == 0) and torch.all(vp[0, :, :, 3] == 0)
+    krows, vrows = H.k_token_rows(kp), H.v_token_rows(vp)           # [32 slots][2][64]
+    assert torch.all(krows[3] == 0) and torch.all(vrows[3] == 0)
     assert torch.all(ks[0, :, 3] == 0) and torch.all(vs[0, :, 3] == 0)
-    for t in (kp, vp, ks.view(torch.uint8), vs.view(torch.uint8)):
-        left = t.clone().view(torch.uint8)
-        if t is kp:
-            left[0, :, :, 3] = 0xFF
-        elif t is vp:
-            left[0, :, :, 3] = 0xFF
-        else:
-            left.view(2, 2, 16, 4)[0, :, 3] = 0xFF
+    for rows in (krows, vrows):
+        left = rows.clone()
+        left[3] = 0xFF
+        assert torch.all(left == 0xFF)
+    for t in (ks.view(torch.uint8), vs.view(torch.uint8)):
+        left = t.clone()
+        left.view(2, 2, 16, 4)[0, :, 3] = 0xFF
         assert torch.all(left == 0xFF)
 
 

@@ -156,14 +156,14 @@ def test_mass_is_a_distribution_and_matches_torch_softmax():
 
 def test_unmapped_read_raises_but_dropped_blocks_are_not_read():
     rng = np.random.default_rng(1)
-    pools = paging.new_pools(8, 1, 8, "f32", fill=np.nan)
+    pools = paging.new_pools(8, 1, 16, "f32", fill=np.nan)
     L, S, W = 100, 4, 20
     table = [-1] * 7
     table[0], table[5], table[6] = 3, 4, 5                    # blocks {0} and {5, 6} hold the keep-set
     keep_pos = np.nonzero(policies.streaming_keep(L, S, W))[0]
-    k = rng.standard_normal((len(keep_pos), 1, 8)).astype(np.float32)
+    k = rng.standard_normal((len(keep_pos), 1, 16)).astype(np.float32)
     paging.write_tokens(pools, "f32", k, k, "f32", [table], [0] * len(keep_pos), keep_pos.tolist())
-    out, probs = attention.paged_decode(pools, "f32", rng.standard_normal((2, 8)), table, L, 0.3, S, W)
+    out, probs = attention.paged_decode(pools, "f32", rng.standard_normal((2, 16)), table, L, 0.3, S, W)
     assert np.all(np.isfinite(out)) and np.all(probs[:, ~policies.streaming_keep(L, S, W)] == 0)
     with pytest.raises(IndexError):
-        attention.paged_decode(pools, "f32", rng.standard_normal((2, 8)), table, L, 0.3)
+        attention.paged_decode(pools, "f32", rng.standard_normal((2, 16)), table, L, 0.3)

@@ -42,22 +42,40 @@ def test_unmapped_entry_raises():
 
 @pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "f16"])
 def test_layout_is_a_bijection(kv_dtype):
-    """Filling every slot of a pool with distinct tokens writes every pool element exactly once."""
-    nb, hkv, d = 3, 2, 8
-    pools = paging.new_pools(nb, hkv, d, "f32")
+    """Filling every slot of a pool with distinct raw values writes every pool element exactly once,
+    at the index the documented layout formula gives."""
+    nb, hkv, d = 2, 1, 64
+    st = paging.storage_dtype(kv_dtype)
+    pools = paging.new_pools(nb, hkv, d, kv_dtype)
     n = nb * 16
-    vals = np.arange(1, n * hkv * d + 1, dtype=np.float32).reshape(n, hkv, d)
-    table = [2, 0, 1]
-    paging.write_tokens(pools, "f32", vals, vals + 0.5, "f32", [table], [0] * n, list(range(n)))
+    vals = np.arange(1, n * hkv * d + 1).astype(st).reshape(n, hkv, d)     # <= 2048: exact in f16
+    assert len(np.unique(vals)) == vals.size
+    table = [1, 0]
+    paging.write_tokens(pools, kv_dtype, vals, vals[::-1].copy(), kv_dtype, [table], [0] * n, list(range(n)))
     k, v = pools[0], pools[1]
     assert sorted(k.ravel().tolist()) == sorted(vals.ravel().tolist())
-    assert sorted(v.ravel().tolist()) == sorted((vals + 0.5).ravel().tolist())
-    # K tile in 16-byte chunks (4 floats) of 16 token rows, V tile dim-major: token p, head h, dim i
-    p, h, i = 37, 1, 5
-    b, o = table[p // 16], p % 16
-    assert k.shape == (nb, hkv, d // 4, 16, 4)
-    assert k[b, h, i // 4, o, i % 4] == vals[p, h, i]
-    assert v[b, h, i, o] == vals[p, h, i] + 0.5
+    assert sorted(v.ravel().tolist()) == sorted(vals.ravel().tolist())
+    x, y = 16 // np.dtype(st).itemsize, 4 // np.dtype(st).itemsize
+    assert k.shape == (nb, hkv, d // x, 16, x) and v.shape == (nb, hkv, d // (16 * y), 16, 4, y, 4)
+    for p, h, i in [(0, 0, 0), (17, 0, 5), (31, 0, 63), (9, 0, 40), (22, 0, 17)]:
+        b, o, t = table[p // 16], p % 16, i // 16
+        assert k[b, h, i // x, o, i % x] == vals[p, h, i]                      # K: chunk i // X, row o
+        assert v[b, h, t // y, i % 16, o // 4, t % y, o % 4] == vals[n - 1 - p, h, i]   # V chunk
+
+
+def test_fp8_v_layout_single_element():
+    """One non-zero V element per row quantises to the code of 448 (0x7E), found at the layout's index."""
+    nb, hkv, d = 1, 2, 128
+    for p, h, i in [(0, 0, 0), (5, 1, 77), (15, 0, 127), (10, 1, 33)]:
+        pools = paging.new_pools(nb, hkv, d, "fp8")
+        row = np.zeros((1, hkv, d), np.float32)
+        row[0, h, i] = 3.0
+        paging.write_tokens(pools, "fp8", row, row, "f32", [[0]], [0], [p])
+        v = pools[1]
+        hits = np.argwhere(v == 0x7E)
+        t = i // 16
+        assert hits.tolist() == [[0, h, t // 4, i % 16, p // 4, t % 4, p % 4]]
+        assert np.argwhere(pools[0] == 0x7E).tolist() == [[0, h, i // 16, p, i % 16]]
 
 
 def _src(rng, shape, dtype):
@@ -75,7 +93,7 @@ def _src(rng, shape, dtype):
                                                 ("fp8", "bf16"), ("fp8", "f32"), ("fp8", "f16")])
 def test_write_then_gather_roundtrip(kv_dtype, src_dtype):
     rng = np.random.default_rng(3)
-    nb, hkv, d = 12, 2, 16
+    nb, hkv, d = 12, 2, 64
     lens = [35, 70]
     perm = rng.permutation(nb)
     tables = [list(perm[0:3]), list(perm[3:8])]
@@ -106,7 +124,7 @@ def test_bf16_storage_decode():
 
 def test_copy_blocks_is_copy_on_write_data_half():
     rng = np.random.default_rng(5)
-    pools = paging.new_pools(6, 2, 16, "fp8")
+    pools = paging.new_pools(6, 2, 64, "fp8")
     for a in pools:
         a[...] = rng.integers(0, 120, a.shape).astype(a.dtype)
     before = [a.copy() for a in pools]
@@ -116,7 +134,7 @@ def test_copy_blocks_is_copy_on_write_data_half():
         keep = [i for i in range(6) if i != 4]
         assert np.array_equal(a[keep], b[keep])                 # nothing else touched
     # a later write into the copy leaves the shared original alone
-    k = np.ones((1, 2, 16), np.float32)
+    k = np.ones((1, 2, 64), np.float32)
     paging.write_tokens(pools, "fp8", k, k, "f32", [[4]], [0], [3])
     assert np.array_equal(pools[0][1], before[0][1])
     assert not np.array_equal(pools[0][4], before[0][1])
