@@ -7,6 +7,7 @@ import torch
 
 import workloads as W
 from oracle import attention, fp8, paging, policies
+from workloads.device import fill, logical_rows, make_pools, newest_rows  # noqa: F401  (re-exported)
 from paged_kv_cache_283_amd import ops
 
 DEV = "cuda"
@@ -31,44 +32,8 @@ def v_token_rows(v_pool):
     return v_pool.permute(0, 4, 6, 1, 2, 5, 3).reshape(nb * j * e, hkv, g * y * c)
 
 
-def make_pools(w, num_blocks, device=DEV):
-    """Pools of the workload's shape, every byte 0xFF (NaN) so unwritten slots poison any read."""
-    return ops.allocate_pools(num_blocks, w.num_kv_heads, w.head_dim, W.storage_dtype(w.kv_dtype), device, 0xFF)
-
-
-def fill(w, lay, pools, ksrc, vsrc, tables_dev, chunk=1 << 18, hold_last=False):
-    """Write every data position of the layout through paged_token_slots + paged_kv_write
-    (with hold_last, each sequence's newest position is left for a decode step)."""
-    seq, pos, rows = lay.fill_tokens()
-    if hold_last:
-        keep = pos != lay.lens[seq] - 1
-        seq, pos, rows = seq[keep], pos[keep], rows[keep]
-    k_pool, v_pool, ks, vs = pools
-    dev = tables_dev.device
-    for lo in range(0, seq.size, chunk):
-        sl = slice(lo, lo + chunk)
-        r_t = torch.from_numpy(rows[sl]).to(ksrc.device)
-        ops.write_positions(tables_dev, torch.from_numpy(seq[sl]).to(dev), torch.from_numpy(pos[sl]).to(dev),
-                            ksrc.index_select(0, r_t).contiguous(), vsrc.index_select(0, r_t).contiguous(),
-                            k_pool, v_pool, ks, vs)
-
-
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
-
-
-def logical_rows(lay, s, positions):
-    """Source rows of the given logical positions of sequence s."""
-    pos = lay.data_pos[s]
-    i = np.searchsorted(pos, positions)
-    assert np.array_equal(pos[i], positions), "a kept position carries no data"
-    return lay.data_row[s][i]
-
-
-def newest_rows(lay):
-    """int64 source row of each sequence's newest position."""
-    return np.array([logical_rows(lay, s, np.array([int(lay.lens[s]) - 1]))[0] for s in range(lay.lens.shape[0])],
-                    dtype=np.int64)
 
 
 def oracle_seq(w, lay, s, q_s, k_rows, v_rows, scale=None, num_sinks=0, window=0):
