@@ -219,7 +219,7 @@ int h2o_select(const float* scores, int scores_stride, const int32_t* kv_lens,
 /*
  * Kernel timing for benchmarks.  Between pkv_timing_begin(capacity) and
  * pkv_timing_end(), each paged_decode_attn call records a HIP event pair on
- * its stream around its main (per-partition) kernel, up to `capacity` calls.
+ * its stream around its main attention kernel, up to `capacity` calls.
  * pkv_timing_end waits for the last event, writes the elapsed milliseconds of
  * each recorded launch to ms_out (host, capacity floats), returns the count
  * (or -1 on error).  Not thread-safe: one timing session per process.

@@ -168,7 +168,7 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
   const pkv::WorkspaceLayout lay = pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len,
                                                               num_sinks, window, attn_mass != nullptr);
   if (lay.p_max > 65535)
-    return fail(PKV_EUNSUPPORTED, "max_context_len %d needs %d partitions (> 65535)", max_context_len, lay.p_max);
+    return fail(PKV_EUNSUPPORTED, "max_context_len %d needs %d partial slots (> 65535)", max_context_len, lay.p_max);
   if (workspace_bytes < lay.total)
     return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
   if (lay.total > 0 && !workspace) return fail(PKV_EINVAL, "NULL workspace");
