@@ -45,8 +45,6 @@ __host__ __device__ inline int max_virtual_blocks(int max_len, int num_sinks, in
   return nb < bound ? nb : bound;
 }
 
-// Number of kPartBlocks-block slots covering n_virtual blocks (the partial
-// slots of a cut sequence are at most this many plus one).
 __host__ __device__ inline int num_partitions(int n_virtual) {
   return (n_virtual + kPartBlocks - 1) / kPartBlocks;
 }

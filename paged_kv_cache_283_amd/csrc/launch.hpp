@@ -33,7 +33,7 @@ struct AttnArgs {
   int mass_stride;
   // workspace views
   float* part_acc;      // [B][Hq][p_max][D]   unnormalised partial outputs
-  float* part_ml;       // [B][Hq][p_max][2]   segment max (base-2) and exp-sum
+  float* part_ml;       // [B][Hq][p_max][2]   partition max (base-2) and exp-sum
   float* stash;         // [B][Hq][nv_pad]     base-2 logits per attended position (mass only)
   float* fin_ml;        // [B][Hq][2]          global max and exp-sum (mass only)
   StreamHdr* hdr;       // schedule of this call
