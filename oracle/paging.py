@@ -181,3 +181,31 @@ def copy_blocks(pools, pairs):
             continue
         for src, dst in pairs:
             arr[dst] = arr[src]
+
+
+def compact(pools, kv_dtype: str, src_table_row, keep_positions, dst_table_row, num_blocks=None):
+    """Apply an eviction keep-set: the token at logical position keep_positions[i]
+    of the source table moves to logical position i of the destination table
+    (stored bytes of K, V and, for fp8, both scales, all KV heads).
+
+    This is the storage half of evicting tokens ([SO] 4.2 evict_tokens returns
+    the cache restricted to the kept indices; [LC] StreamingKVCache keeps
+    sinks + window the same way): the kept tokens become a dense prefix of
+    fresh blocks, so the cache shrinks to ceil(n / 16) blocks.  Every source is
+    read before any destination is written.  Mutates pools in place.
+    """
+    k_pool, v_pool, k_scale, v_scale = pools
+    nb = k_pool.shape[0] if num_blocks is None else num_blocks
+    src = [(physical_block(src_table_row, int(p), nb), int(p) % BLOCK_SIZE) for p in keep_positions]
+    rows = []
+    for b, o in src:
+        rows.append((k_pool[b, :, :, o, :].copy(), v_pool[b, :, :, :, o // 4, :, o % 4].copy(),
+                     None if k_scale is None else k_scale[b, :, o].copy(),
+                     None if v_scale is None else v_scale[b, :, o].copy()))
+    for i, (k, v, ks, vs) in enumerate(rows):
+        b, o = physical_block(dst_table_row, i, nb), i % BLOCK_SIZE
+        k_pool[b, :, :, o, :] = k
+        v_pool[b, :, :, :, o // 4, :, o % 4] = v
+        if k_scale is not None:
+            k_scale[b, :, o] = ks
+            v_scale[b, :, o] = vs

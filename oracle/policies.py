@@ -4,7 +4,11 @@
        StreamingKVCache snippet (defaults 4 sinks, window 4096) and H2OEviction
        snippet (defaults budget 2048, recent 512; update_scores, select).
 [SO] = page "系统优化", section 4.1 "StreamingLLM 详解": keep the first few tokens
-       (usually 4) plus the most recent W.
+       (usually 4) plus the most recent W; section 4.2 "KV Cache 淘汰", the H2O
+       pseudocode evict_tokens: keep the `budget` highest accumulated scores.
+[PA] = page "KV Cache 与 PagedAttention：显存复用与长上下文推理", the 组合 snippet
+       should_cache: a position is cached if it is one of the first sink_size,
+       if it is recent, or if it is among the h2o_size highest scores.
 
 Readings where the pages are silent or inconsistent:
   * window counts the most recent W positions including the token being
@@ -16,6 +20,15 @@ Readings where the pages are silent or inconsistent:
     number; if the context is no longer than the budget everything is kept;
   * heavy hitters are drawn only from positions before the recent window and
     the result is returned in ascending position order.
+  * keep_select covers the three rules with one shape: forced positions (the
+    first num_sinks and the last `recent`) united with the `heavy` highest
+    scores of a candidate set -- the positions that are not forced
+    (H2OEviction.select, with num_sinks = 0) or every position (should_cache
+    ranks all scores; evict_tokens has nothing forced).  should_cache's
+    heavy set may overlap the forced ones, so it keeps at most
+    sink + window + h2o positions.  Kept tokens are listed in ascending position
+    order for every rule (evict_tokens' gather in score order is a detail of
+    the gather; decode attention does not depend on the order of its keys).
 """
 
 import numpy as np
@@ -51,3 +64,28 @@ def h2o_select(scores, kv_len: int, budget: int, recent: int) -> np.ndarray:
     order = np.lexsort((np.arange(cand), -s))   # score high -> low, then position low -> high
     heavy = np.sort(order[: budget - recent])
     return np.concatenate([heavy, np.arange(cand, kv_len)]).astype(np.int64)
+
+
+CANDIDATES = ("rest", "all")
+
+
+def keep_select(scores, kv_len: int, num_sinks: int, recent: int, heavy: int, candidates: str) -> np.ndarray:
+    """Positions kept by an eviction rule, ascending (int64).
+
+    forced  = {p < num_sinks} | {p >= kv_len - recent}
+    C       = positions not forced ("rest") or all of [0, kv_len) ("all")
+    heavy_s = the `heavy` highest scores in C (all of C if it is smaller),
+              higher score first, then lower position; NaN ranks like -inf
+    keep    = forced | heavy_s
+    """
+    if min(num_sinks, recent, heavy) < 0 or candidates not in CANDIDATES:
+        raise ValueError("need num_sinks, recent, heavy >= 0 and candidates in ('rest', 'all')")
+    p = np.arange(kv_len)
+    forced = (p < num_sinks) | (p >= kv_len - recent)
+    cand = p[~forced] if candidates == "rest" else p
+    s = np.asarray(scores[:kv_len], dtype=np.float64)[cand]
+    s = np.where(np.isnan(s), -np.inf, s)
+    order = np.lexsort((cand, -s))               # score high -> low, then position low -> high
+    keep = forced.copy()
+    keep[cand[order[:heavy]]] = True
+    return p[keep].astype(np.int64)

@@ -138,3 +138,40 @@ def test_copy_blocks_is_copy_on_write_data_half():
     paging.write_tokens(pools, "fp8", k, k, "f32", [[4]], [0], [3])
     assert np.array_equal(pools[0][1], before[0][1])
     assert not np.array_equal(pools[0][4], before[0][1])
+
+
+@pytest.mark.parametrize("kv_dtype,src_dtype", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "bf16")])
+def test_compact_moves_kept_tokens_to_a_dense_prefix(kv_dtype, src_dtype):
+    """After compaction, logical position i of the new table holds exactly what keep[i] held,
+    no block outside the destination changes, and attention over the compacted cache equals
+    attention over the original cache restricted to the kept positions."""
+    from oracle import attention, policies
+    rng = np.random.default_rng(7)
+    nb, hkv, d, L = 24, 2, 64, 150
+    perm = rng.permutation(nb)
+    src_table = list(perm[:10])                       # 150 tokens in 10 blocks
+    pools = paging.new_pools(nb, hkv, d, kv_dtype)
+    for a in pools:
+        if a is not None:
+            a.view(np.uint8)[...] = rng.integers(0, 256, a.view(np.uint8).shape, dtype=np.uint8)
+    k, v = _src(rng, (L, hkv, d), src_dtype), _src(rng, (L, hkv, d), src_dtype)
+    paging.write_tokens(pools, kv_dtype, k, v, src_dtype, [src_table], [0] * L, list(range(L)))
+    keep = policies.keep_select(rng.random(L), L, 4, 16, 20, "all")
+    n = len(keep)
+    dst_table = list(perm[10:10 + -(-n // 16)])
+    before = [None if a is None else a.copy() for a in pools]
+    K0, V0 = paging.gather_logical(pools, kv_dtype, src_table, keep)
+    paging.compact(pools, kv_dtype, src_table, keep, dst_table)
+    K1, V1 = paging.gather_logical(pools, kv_dtype, dst_table, np.arange(n))
+    assert np.array_equal(K0, K1) and np.array_equal(V0, V1)
+    others = [b for b in range(nb) if b not in dst_table]
+    for a, b0 in zip(pools, before):
+        if a is not None:
+            assert np.array_equal(a[others].view(np.uint8), b0[others].view(np.uint8))   # bytes: NaN patterns too
+    q = rng.standard_normal((4, d))
+    out_c, _ = attention.paged_decode(pools, kv_dtype, q, dst_table, n, 0.125)
+    Kf, Vf = paging.gather_logical(before, kv_dtype, src_table, np.arange(L))
+    mask = np.zeros(L, bool)
+    mask[keep] = True
+    out_r, _ = attention.decode_attention(q, Kf, Vf, 0.125, keep=mask)
+    assert np.array_equal(out_c, out_r)

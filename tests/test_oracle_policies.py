@@ -103,3 +103,88 @@ def test_accumulate_growing_context():
 def test_select_rejects_bad_budget():
     with pytest.raises(ValueError):
         policies.h2o_select(np.zeros(5), 5, 2, 3)
+
+
+# ---------------------------------------------------------------------------- keep_select
+
+def _brute_keep(scores, L, sinks, recent, heavy, candidates):
+    """Rank counting: p is a heavy hitter iff fewer than `heavy` candidates outrank it."""
+    s = [(-np.inf if np.isnan(x) else x) for x in scores[:L]]
+    forced = [p < sinks or p >= L - recent for p in range(L)]
+    cand = [p for p in range(L) if candidates == "all" or not forced[p]]
+    keep = []
+    for p in range(L):
+        if forced[p]:
+            keep.append(p)
+            continue
+        if p in cand or candidates == "all":
+            better = sum(1 for q in cand if s[q] > s[p] or (s[q] == s[p] and q < p))
+            if better < heavy:
+                keep.append(p)
+    return keep
+
+
+def test_keep_select_matches_rank_brute_force_with_ties():
+    rng = np.random.default_rng(283)
+    for trial in range(400):
+        L = int(rng.integers(1, 50))
+        sinks, recent, heavy = (int(x) for x in rng.integers(0, 20, 3))
+        mode = policies.CANDIDATES[trial % 2]
+        scores = rng.integers(0, 4, size=64).astype(np.float64)
+        if trial % 5 == 0:
+            scores[rng.integers(0, 64, 4)] = np.nan
+        if trial % 9 == 0:
+            scores[rng.integers(0, 64, 4)] = -0.0
+        got = policies.keep_select(scores, L, sinks, recent, heavy, mode).tolist()
+        assert got == _brute_keep(scores, L, sinks, recent, heavy, mode), (L, sinks, recent, heavy, mode)
+        assert got == sorted(set(got))
+
+
+def test_keep_select_rest_without_sinks_is_h2o_select():
+    rng = np.random.default_rng(17)
+    for _ in range(200):
+        L = int(rng.integers(1, 60))
+        budget = int(rng.integers(0, 40))
+        recent = int(rng.integers(0, budget + 1))
+        scores = rng.integers(0, 5, size=64).astype(np.float64)
+        assert (policies.keep_select(scores, L, 0, recent, budget - recent, "rest").tolist()
+                == policies.h2o_select(scores, L, budget, recent).tolist())
+
+
+def test_keep_select_is_the_page_should_cache_predicate():
+    """PA 组合: cached iff p < sink_size, or recent, or p in scores.argsort()[-h2o_size:] (distinct scores)."""
+    c = GOLD["combined_policy"]
+    sink_size, window_size = c["sinks"], c["window"]
+    h2o_size = c["total"] - sink_size - window_size
+    assert h2o_size == c["heavy"]
+    rng = np.random.default_rng(512)
+    for L in (1, 5, 200, 300, 511, 512, 513, 1000, 4096):
+        scores = rng.permutation(L).astype(np.float64) / L           # distinct: argsort is unambiguous
+        top = set(np.argsort(scores)[-h2o_size:].tolist()) if h2o_size else set()
+
+        def should_cache(pos, is_recent):
+            if pos < sink_size or is_recent:
+                return True
+            return pos in top
+
+        page = [p for p in range(L) if should_cache(p, p >= L - window_size)]
+        got = policies.keep_select(scores, L, sink_size, window_size, h2o_size, "all").tolist()
+        assert got == page, L
+        assert len(got) <= c["total"]
+
+
+def test_keep_select_is_the_page_evict_tokens():
+    """SO 4.2 evict_tokens: the `budget` highest accumulated scores (torch.topk), nothing forced."""
+    rng = np.random.default_rng(42)
+    for L, budget in ((100, 10), (8192, 2048), (300, 300), (50, 80)):
+        scores = torch.from_numpy(rng.random(L))
+        top = scores.topk(min(budget, L)).indices.tolist()
+        got = policies.keep_select(scores.numpy(), L, 0, 0, budget, "all").tolist()
+        assert got == sorted(top)
+
+
+def test_keep_select_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        policies.keep_select(np.zeros(4), 4, -1, 0, 1, "all")
+    with pytest.raises(ValueError):
+        policies.keep_select(np.zeros(4), 4, 0, 0, 1, "middle")
