@@ -214,6 +214,64 @@ int h2o_select(const float* scores, int scores_stride, const int32_t* kv_lens,
                int num_seqs, int max_kv_len, int budget, int recent,
                int32_t* keep_idx, int32_t* keep_count, void* stream);
 
+/* Candidate sets of kv_keep_select. */
+typedef enum {
+  PKV_CAND_REST = 0,  /* positions that are not forced ([LC] H2OEviction.select) */
+  PKV_CAND_ALL = 1    /* every position ([PA] 组合 should_cache; [SO] 4.2 evict_tokens) */
+} pkv_candidates;
+
+/*
+ * kv_keep_select -- keep-set of an eviction rule per sequence.
+ *
+ * For L = kv_lens[s]:
+ *   forced(p) = p < num_sinks  or  p >= L - recent
+ *   C         = PKV_CAND_REST: the positions of [0, L) that are not forced
+ *               PKV_CAND_ALL : all of [0, L)
+ *   heavy set = the `heavy` highest scores[s][p] over p in C (all of C if it is
+ *               smaller); equal scores go to the lower position, NaN ranks
+ *               below every number, -0.0 equals +0.0
+ *   kept      = forced positions united with the heavy set
+ * The three rules of the pages are instances: H2OEviction.select
+ * ([LC]; = h2o_select) is (0, recent, budget - recent, REST); should_cache ([PA]
+ * 组合: sinks 4, window 256, 512 in total) is (4, 256, 252, ALL), whose heavy set
+ * may overlap the forced positions; evict_tokens ([SO] 4.2) is (0, 0, budget, ALL).
+ *   scores      float [num_seqs][scores_stride], stride >= max_kv_len
+ *   kv_lens     int32 [num_seqs], 1 <= L <= max_kv_len
+ *   keep_idx    int32 [num_seqs][keep_stride] out: kept positions ascending, then -1;
+ *               keep_stride >= min(num_sinks + recent + heavy, max_kv_len)
+ *   keep_count  int32 [num_seqs] out (-1 for a length outside [1, max_kv_len])
+ */
+int kv_keep_select(const float* scores, int scores_stride, const int32_t* kv_lens,
+                   int num_seqs, int max_kv_len, int num_sinks, int recent, int heavy,
+                   int candidates, int32_t* keep_idx, int keep_stride, int32_t* keep_count,
+                   void* stream);
+
+/*
+ * kv_compact -- apply a keep-set: move each sequence's kept tokens to a dense
+ * prefix of fresh blocks ([SO] 4.2 evict_tokens returns the cache restricted to
+ * the kept indices; [LC] StreamingKVCache drops the middle of the cache).
+ *
+ * For sequence s and i < n = keep_count[s]: the token at logical position
+ * keep_idx[s][i] of src_tables[s] is copied -- K, V and, for FP8, both scales,
+ * all KV heads -- to logical position i of dst_tables[s].  The sequence then
+ * holds n tokens in ceil(n / 16) destination blocks; the host releases the
+ * source blocks (BlockManager.compact).
+ *   src_tables, dst_tables  int32 [num_seqs][src_stride], [num_seqs][dst_stride]
+ *   keep_idx     int32 [num_seqs][keep_stride]; keep_count int32 [num_seqs]
+ * Destination slots must not be source slots of a token copied in the same call
+ * (use fresh blocks); otherwise the result is undefined.  Slots of the last
+ * destination block beyond n are left as they were.  A sequence whose count is
+ * outside [0, min(keep_stride, 16 * dst_stride)] is skipped; a kept position
+ * outside [0, 16 * src_stride) or whose source table entry is outside
+ * [0, num_blocks) writes NaN bytes (0xFF; NaN scales) for that token; a
+ * destination entry outside [0, num_blocks) skips that block.
+ */
+int kv_compact(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+               const int32_t* src_tables, int src_stride, const int32_t* dst_tables, int dst_stride,
+               const int32_t* keep_idx, int keep_stride, const int32_t* keep_count,
+               int num_seqs, int num_blocks, int num_kv_heads, int head_dim, int block_size,
+               void* stream);
+
 /* ---- measurement helpers (not part of the decode path) ------------------ */
 
 /*

@@ -15,6 +15,7 @@ STATUS_NAMES = {OK: "PKV_OK", EINVAL: "PKV_EINVAL", EUNSUPPORTED: "PKV_EUNSUPPOR
 
 # pkv_dtype
 F32, BF16, F16, FP8_E4M3 = range(4)
+CAND_REST, CAND_ALL = range(2)
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -33,6 +34,8 @@ SIGNATURES = {
                                _F, _I, _I, _P, _I, _P, _Z, _P]),
     "kv_block_copy": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
     "h2o_select": (_I, [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P]),
+    "kv_keep_select": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P]),
+    "kv_compact": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
     "pkv_timing_begin": (_I, [_I]),
     "pkv_timing_end": (_I, [ctypes.POINTER(ctypes.c_float), _I]),
     "pkv_probe_read": (_I, [_P, _Z, _P, _P]),

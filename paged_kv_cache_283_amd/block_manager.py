@@ -121,6 +121,28 @@ class BlockManager:
             self.lens[seq] = pos + 1
         return slots, copies
 
+    def compact(self, seq, num_kept: int):
+        """Give seq fresh blocks for a dense prefix of num_kept tokens (eviction).
+
+        Returns (old_table, new_table): the caller enqueues kv_compact from
+        old_table to new_table with the keep-set.  The old blocks are released
+        here (shared ones only lose this reference), so a later allocation may
+        hand them out again: device work that writes them must be enqueued
+        after the kv_compact call on the same stream.
+        """
+        if num_kept < 0 or num_kept > self.lens[seq]:
+            raise ValueError(f"num_kept {num_kept} outside [0, {self.lens[seq]}]")
+        need = -(-num_kept // self.block_size)
+        if need > self.num_free:
+            raise OutOfBlocks(f"compaction to {num_kept} tokens needs {need} blocks, {self.num_free} free")
+        old = self.tables[seq]
+        new = [self._alloc() for _ in range(need)]
+        for b in old:
+            self._release(b)
+        self.tables[seq] = new
+        self.lens[seq] = num_kept
+        return list(old), list(new)
+
     def free(self, seq) -> None:
         for b in self.tables.pop(seq):
             self._release(b)

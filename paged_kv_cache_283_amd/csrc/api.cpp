@@ -244,9 +244,56 @@ int h2o_select(const float* scores, int scores_stride, const int32_t* kv_lens, i
   if (num_seqs == 0) return ok();
   if (!scores || !kv_lens || !keep_idx || !keep_count) return fail(PKV_EINVAL, "NULL array argument");
   if (num_seqs > (1 << 30)) return fail(PKV_EINVAL, "num_seqs too large");
-  return device_status(pkv::launch_h2o_select(scores, scores_stride, kv_lens, num_seqs, max_kv_len, budget, recent,
-                                              keep_idx, keep_count, (hipStream_t)stream),
+  return device_status(pkv::launch_keep_select(scores, scores_stride, kv_lens, num_seqs, max_kv_len, 0, recent,
+                                               budget - recent, PKV_CAND_REST, keep_idx, budget, keep_count,
+                                               (hipStream_t)stream),
                        "h2o_select");
+}
+
+int kv_keep_select(const float* scores, int scores_stride, const int32_t* kv_lens, int num_seqs, int max_kv_len,
+                   int num_sinks, int recent, int heavy, int candidates, int32_t* keep_idx, int keep_stride,
+                   int32_t* keep_count, void* stream) {
+  if (num_seqs < 0 || num_seqs > (1 << 30)) return fail(PKV_EINVAL, "num_seqs %d outside [0, 2^30]", num_seqs);
+  if (num_sinks < 0 || recent < 0 || heavy < 0)
+    return fail(PKV_EINVAL, "num_sinks %d, recent %d, heavy %d must be >= 0", num_sinks, recent, heavy);
+  if (candidates != PKV_CAND_REST && candidates != PKV_CAND_ALL) return fail(PKV_EINVAL, "candidates %d", candidates);
+  if (max_kv_len < 1 || max_kv_len > (1 << 30)) return fail(PKV_EINVAL, "max_kv_len %d outside [1, 2^30]", max_kv_len);
+  if (scores_stride < max_kv_len) return fail(PKV_EINVAL, "scores_stride %d < max_kv_len %d", scores_stride, max_kv_len);
+  const long long most = (long long)num_sinks + recent + heavy;
+  const long long need = most < max_kv_len ? most : max_kv_len;
+  if (keep_stride < need || keep_stride < 1 || keep_stride > (1 << 30))
+    return fail(PKV_EINVAL, "keep_stride %d < min(num_sinks + recent + heavy, max_kv_len) = %lld (or > 2^30)",
+                keep_stride, need);
+  if (num_seqs == 0) return ok();
+  if (!scores || !kv_lens || !keep_idx || !keep_count) return fail(PKV_EINVAL, "NULL array argument");
+  return device_status(pkv::launch_keep_select(scores, scores_stride, kv_lens, num_seqs, max_kv_len, num_sinks, recent,
+                                               heavy, candidates, keep_idx, keep_stride, keep_count,
+                                               (hipStream_t)stream),
+                       "kv_keep_select");
+}
+
+int kv_compact(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype, const int32_t* src_tables,
+               int src_stride, const int32_t* dst_tables, int dst_stride, const int32_t* keep_idx, int keep_stride,
+               const int32_t* keep_count, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
+               int block_size, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PKV_EINVAL, "num_seqs %d outside [0, 65535]", num_seqs);
+  if (num_kv_heads < 1 || num_kv_heads > 65535) return fail(PKV_EINVAL, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  if (src_stride < 1 || src_stride > (1 << 26) || dst_stride < 1 || dst_stride > (1 << 26))
+    return fail(PKV_EINVAL, "table strides %d, %d outside [1, 2^26]", src_stride, dst_stride);
+  if (keep_stride < 0 || keep_stride > (1 << 30)) return fail(PKV_EINVAL, "keep_stride %d outside [0, 2^30]", keep_stride);
+  if (num_seqs == 0 || keep_stride == 0) return ok();
+  if (!k_pool || !v_pool || !src_tables || !dst_tables || !keep_idx || !keep_count)
+    return fail(PKV_EINVAL, "NULL array argument");
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
+  if ((uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
+  return device_status(pkv::launch_kv_compact(k_pool, v_pool, k_scale, v_scale, kv_dtype, src_tables, src_stride,
+                                              dst_tables, dst_stride, keep_idx, keep_stride, keep_count, num_seqs,
+                                              num_blocks, num_kv_heads, head_dim, (hipStream_t)stream),
+                       "kv_compact");
 }
 
 int pkv_timing_begin(int capacity) {

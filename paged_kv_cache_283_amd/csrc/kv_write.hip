@@ -7,7 +7,8 @@
 //   "量化原理" -- FP8 (E4M3) storage with per-token scales;
 //   "三大运行时组件" and copy_on_write -- a shared block is copied before a write.
 // Pool layout: K [NB][Hkv][D/X][16][X] (16-byte chunks of X elements),
-// V [NB][Hkv][D][16] dim-major, FP8 scales [NB][Hkv][16].
+// V [NB][Hkv][D/(16Y)][16][4][Y][4] (16-byte chunks of 4 tokens x Y dims), FP8 scales
+// [NB][Hkv][16].
 #include "device_common.hpp"
 #include "fp8_e4m3.hpp"
 #include "launch.hpp"

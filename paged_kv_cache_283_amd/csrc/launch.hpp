@@ -68,9 +68,14 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* 
                              const int32_t* pairs, int num_pairs, int num_blocks, int num_kv_heads,
                              int head_dim, hipStream_t stream);
 
-hipError_t launch_h2o_select(const float* scores, int stride, const int32_t* lens, int num_seqs,
-                             int max_len, int budget, int recent, int32_t* keep_idx, int32_t* keep_count,
-                             hipStream_t stream);
+hipError_t launch_keep_select(const float* scores, int stride, const int32_t* lens, int num_seqs, int max_len,
+                              int num_sinks, int recent, int heavy, int all_candidates, int32_t* keep_idx,
+                              int keep_stride, int32_t* keep_count, hipStream_t stream);
+
+hipError_t launch_kv_compact(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+                             const int32_t* src_tables, int src_stride, const int32_t* dst_tables, int dst_stride,
+                             const int32_t* keep_idx, int keep_stride, const int32_t* keep_count, int num_seqs,
+                             int num_blocks, int num_kv_heads, int head_dim, hipStream_t stream);
 
 hipError_t launch_probe_read(const void* src, size_t bytes, float* sink, hipStream_t stream);
 hipError_t launch_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);

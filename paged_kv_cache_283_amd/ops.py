@@ -246,6 +246,45 @@ def h2o_select(scores, kv_lens, max_kv_len, budget, recent, keep_idx=None, keep_
     return keep_idx, keep_count
 
 
+_CANDIDATES = {"rest": _lib.CAND_REST, "all": _lib.CAND_ALL}
+
+
+def keep_select(scores, kv_lens, max_kv_len, num_sinks, recent, heavy, candidates="rest", keep_idx=None,
+                keep_count=None, stream=None):
+    """Eviction keep-set per sequence (kv_keep_select): forced sinks + recent window united with the
+    `heavy` top scores of the non-forced ("rest") or of all ("all") positions.
+    Returns (keep_idx int32 [B][stride] ascending, -1 padded; keep_count int32 [B])."""
+    _need(scores, torch.float32, "scores")
+    _need(kv_lens, torch.int32, "kv_lens")
+    b = kv_lens.shape[0]
+    if keep_idx is None:
+        width = max(1, min(int(num_sinks) + int(recent) + int(heavy), int(max_kv_len)))
+        keep_idx = torch.empty((b, width), dtype=torch.int32, device=scores.device)
+    if keep_count is None:
+        keep_count = torch.empty(b, dtype=torch.int32, device=scores.device)
+    _lib.call("kv_keep_select", _ptr(scores), scores.shape[1], _ptr(kv_lens), b, int(max_kv_len), int(num_sinks),
+              int(recent), int(heavy), _CANDIDATES[candidates], _ptr(keep_idx), keep_idx.shape[1], _ptr(keep_count),
+              _stream(stream))
+    return keep_idx, keep_count
+
+
+def kv_compact(k_pool, v_pool, src_tables, dst_tables, keep_idx, keep_count, k_scale=None, v_scale=None,
+               stream=None):
+    """Move each sequence's kept tokens (keep_idx, keep_count) from their slots under src_tables to
+    positions 0..n-1 under dst_tables (fresh blocks)."""
+    for t, n in ((src_tables, "src_tables"), (dst_tables, "dst_tables"), (keep_idx, "keep_idx"),
+                 (keep_count, "keep_count")):
+        _need(t, torch.int32, n)
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    d = k_pool.shape[2] * k_pool.shape[4]
+    b = keep_count.shape[0]
+    if src_tables.shape[0] != b or dst_tables.shape[0] != b or keep_idx.shape[0] != b:
+        raise ValueError("tables, keep_idx and keep_count must have one row per sequence")
+    _lib.call("kv_compact", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
+              _ptr(src_tables), src_tables.shape[1], _ptr(dst_tables), dst_tables.shape[1], _ptr(keep_idx),
+              keep_idx.shape[1], _ptr(keep_count), b, nb, hkv, d, BLOCK_SIZE, _stream(stream))
+
+
 def timing_begin(capacity):
     _lib.call("pkv_timing_begin", int(capacity))
 

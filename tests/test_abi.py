@@ -120,3 +120,27 @@ def test_copy_select_slots_probe_validation():
     assert lib.pkv_probe_copy(None, FAKE, 16, None) == _lib.EINVAL
     assert lib.pkv_timing_begin(0) == _lib.EINVAL
     assert lib.pkv_timing_end(None, 0) == -1
+
+
+def test_keep_select_and_compact_validation():
+    lib = _lib.load()
+    ks = lib.kv_keep_select
+    #        scores stride lens  B  max  S  R  H  cand keep  kstride count stream
+    assert ks(FAKE, 100, FAKE, 4, 100, -1, 8, 8, 1, FAKE, 20, FAKE, None) == _lib.EINVAL     # negative sinks
+    assert ks(FAKE, 100, FAKE, 4, 100, 4, 8, 8, 2, FAKE, 20, FAKE, None) == _lib.EINVAL      # candidates
+    assert ks(FAKE, 100, FAKE, 4, 100, 4, 8, 8, 0, FAKE, 19, FAKE, None) == _lib.EINVAL      # stride < 20
+    assert ks(FAKE, 100, FAKE, 4, 10, 4, 8, 8, 0, FAKE, 9, FAKE, None) == _lib.EINVAL        # < min(20, max len 10)
+    assert ks(FAKE, 50, FAKE, 4, 100, 4, 8, 8, 0, FAKE, 20, FAKE, None) == _lib.EINVAL       # scores stride < max len
+    assert ks(FAKE, 100, FAKE, 0, 100, 4, 8, 8, 0, FAKE, 20, FAKE, None) == _lib.OK          # no sequences
+    assert ks(None, 100, FAKE, 2, 100, 4, 8, 8, 0, FAKE, 20, FAKE, None) == _lib.EINVAL      # NULL scores
+    c = lib.kv_compact
+    #       k     v     ksc   vsc  dt src  ss  dst  ds keep kst count B  NB  H  D   bs
+    assert c(FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 2, 64, 8, 128, 8, None) == _lib.EUNSUPPORTED
+    assert c(FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 2, 64, 8, 96, 16, None) == _lib.EUNSUPPORTED
+    assert c(FAKE, FAKE, None, None, 3, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 2, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert c(FAKE, FAKE, None, None, 1, FAKE, 0, FAKE, 8, FAKE, 32, FAKE, 2, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert c(FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, -1, FAKE, 2, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert c(FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 70000, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert c(FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 0, 64, 8, 128, 16, None) == _lib.OK
+    assert c(ctypes.c_void_p(0x100008), FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 2, 64, 8, 128, 16,
+             None) == _lib.EINVAL                                                               # misaligned pool

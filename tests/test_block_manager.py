@@ -104,3 +104,24 @@ def test_block_tables_and_lens():
     t = bm.block_tables(["x", "y"], width=3)
     assert t.dtype == np.int32 and t.shape == (2, 3) and t[1, 1] == -1 and t[0, 2] == -1
     assert bm.context_lens(["x", "y"]).tolist() == [20, 5]
+
+
+def test_compact_swaps_in_fresh_blocks_and_releases_the_old():
+    bm = BlockManager(12)
+    bm.add_sequence("a", 70)                  # 5 blocks
+    bm.fork("a", "b")                         # shared: refcount 2
+    free_before = bm.num_free
+    old, new = bm.compact("a", 20)            # keep 20 tokens -> 2 fresh blocks
+    assert len(old) == 5 and len(new) == 2 and not set(old) & set(new)
+    assert bm.tables["a"] == new and bm.lens["a"] == 20
+    assert bm.num_free == free_before - 2     # old blocks still held by "b"
+    assert all(bm.refcount[x] == 1 for x in old) and all(bm.refcount[x] == 1 for x in new)
+    bm.free("b")
+    assert bm.num_free == 12 - 2
+    _, new2 = bm.compact("a", 0)              # evict everything
+    assert new2 == [] and bm.num_free == 12
+    with pytest.raises(ValueError):
+        bm.compact("a", 1)
+    bm.add_sequence("c", 16 * 12)
+    with pytest.raises(OutOfBlocks):
+        bm.compact("c", 16)                   # no free block left for the copy

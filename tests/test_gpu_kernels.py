@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import fp8, paging, policies
+from oracle import attention, fp8, paging, policies
 from paged_kv_cache_283_amd import ops
 
 pytestmark = pytest.mark.gpu
@@ -371,3 +371,147 @@ def test_h2o_select_bit_exact():
     bad[8] = maxl + 1
     idx, cnt = ops.h2o_select(torch.from_numpy(scores).cuda(), bad, maxl, budget, recent)
     assert cnt[7].item() == -1 and cnt[8].item() == -1 and torch.all(idx[7:9] == -1)
+
+
+# ---------------------------------------------------------------------------- eviction: keep-set + compaction
+
+KEEP_RULES = [(4, 256, 252, "all"),      # should_cache (PA 组合)
+              (0, 150, 450, "rest"),     # H2OEviction.select, budget 600
+              (4, 64, 100, "rest"),      # sinks + window + heavy hitters of the middle
+              (0, 0, 600, "all"),        # evict_tokens, budget 600
+              (2, 0, 0, "rest"), (0, 600, 0, "rest"), (1, 1, 1, "all")]
+
+
+def test_keep_select_bit_exact():
+    rng = np.random.default_rng(55)
+    B, maxl = 24, 3000
+    scores = rng.integers(0, 50, size=(B, maxl)).astype(np.float32) / 7       # many ties
+    scores[3, :100] = np.nan
+    scores[4, :] = -0.0
+    scores[4, ::3] = 0.0
+    scores[5] = rng.random(maxl).astype(np.float32)
+    scores[6, 10] = np.inf
+    scores[9, 2000:] = -np.inf
+    lens = rng.integers(1, maxl + 1, size=B).astype(np.int32)
+    lens[0], lens[1], lens[2], lens[10] = 1, 600, 601, 3
+    sc, ln = torch.from_numpy(scores).cuda(), torch.from_numpy(lens).cuda()
+    for sinks, recent, heavy, mode in KEEP_RULES:
+        idx, cnt = ops.keep_select(sc, ln, maxl, sinks, recent, heavy, mode)
+        idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+        for s in range(B):
+            ref = policies.keep_select(scores[s], int(lens[s]), sinks, recent, heavy, mode)
+            assert cnt[s] == ref.size, (sinks, recent, heavy, mode, s)
+            assert idx[s, : ref.size].tolist() == ref.tolist(), (sinks, recent, heavy, mode, s)
+            assert np.all(idx[s, ref.size:] == -1)
+    bad = ln.clone()
+    bad[7], bad[8] = 0, maxl + 1
+    idx, cnt = ops.keep_select(sc, bad, maxl, 4, 256, 252, "all")
+    assert cnt[7].item() == -1 and cnt[8].item() == -1 and torch.all(idx[7:9] == -1)
+
+
+_NP = {torch.float32: np.float32, torch.bfloat16: np.uint16, torch.float16: np.float16, torch.uint8: np.uint8}
+
+
+def _host_pools(pools, kv):
+    """Host copies of device pools as the oracle's storage arrays (same shapes, same bytes)."""
+    return [None if t is None else t.detach().cpu().contiguous().view(torch.uint8).numpy().view(
+        _NP[t.dtype]).reshape(t.shape) for t in pools]
+
+
+@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("fp8", 128), ("fp8", 64)])
+def test_compact_pool_bytes_bit_exact(kv, d):
+    """kv_compact moves kept tokens exactly as the oracle's compact does; no other byte changes."""
+    lens = (35, 70, 300, 1, 129)
+    w = dataclasses.replace(_case_workload(kv, "bf16", d, 8, 2, 77, lens=lens), extra_blocks=40)
+    case = H.Case(w)
+    lay = case.lay
+    rng = np.random.default_rng(8)
+    keeps = [policies.keep_select(rng.random(L), L, 4, 16, 20, "all") for L in lens]
+    keeps[1] = np.arange(70)                          # keep all (a full copy)
+    keeps[3] = np.array([], dtype=np.int64)           # evict everything
+    stride = max(1, max(k.size for k in keeps))
+    keep_idx = np.full((len(lens), stride), -1, np.int32)
+    for s, k in enumerate(keeps):
+        keep_idx[s, : k.size] = k
+    counts = np.array([k.size for k in keeps], np.int32)
+    free = list(lay.unused_blocks)
+    dst_w = max(1, -(-stride // 16))
+    dst = np.full((len(lens), dst_w), -1, np.int32)
+    for s, k in enumerate(keeps):
+        for j in range(-(-k.size // 16)):
+            dst[s, j] = free.pop()
+    ref = _host_pools(case.pools, kv)
+    for s in range(len(lens)):
+        paging.compact(ref, kv, lay.tables[s], keeps[s], dst[s], lay.num_blocks)
+    k, v, ks, vs = case.pools
+    ops.kv_compact(k, v, case.tables, torch.from_numpy(dst).cuda(), torch.from_numpy(keep_idx).cuda(),
+                   torch.from_numpy(counts).cuda(), ks, vs)
+    for got, exp in zip(case.pools, ref):
+        if exp is None:
+            continue
+        assert np.array_equal(got.cpu().contiguous().view(torch.uint8).numpy().reshape(-1),
+                              exp.view(np.uint8).reshape(-1))
+
+
+def test_compact_skips_and_poisons_invalid_entries():
+    w = dataclasses.replace(_case_workload("bf16", "bf16", 64, 8, 2, 78, lens=(40, 40)), extra_blocks=8)
+    case = H.Case(w)
+    lay = case.lay
+    free = list(lay.unused_blocks)
+    keep_idx = torch.tensor([[0, 1, 5000, 3], [0, 1, 2, 3]], dtype=torch.int32).cuda()   # 5000: outside the table
+    dst = torch.tensor([[free[0]], [lay.num_blocks + 5]], dtype=torch.int32).cuda()     # seq 1: bad destination
+    counts = torch.tensor([4, 4], dtype=torch.int32).cuda()
+    before = [t.clone() for t in case.pools if t is not None]
+    k, v, _, _ = case.pools
+    ops.kv_compact(k, v, case.tables, dst, keep_idx, counts)
+    krows, vrows = H.k_token_rows(k), H.v_token_rows(v)
+    b0 = int(free[0])
+    assert torch.all(krows[b0 * 16 + 2].view(torch.int16) == -1) and torch.all(vrows[b0 * 16 + 2].view(torch.int16) == -1)
+    for o, p in ((0, 0), (1, 1), (3, 3)):
+        src = int(lay.tables[0, p // 16]) * 16 + p % 16
+        assert torch.equal(krows[b0 * 16 + o], H.k_token_rows(before[0])[src])
+        assert torch.equal(vrows[b0 * 16 + o], H.v_token_rows(before[1])[src])
+    # only block b0's first four slots changed
+    changed = (krows.view(torch.int16) != H.k_token_rows(before[0]).view(torch.int16)).any(-1).any(-1)
+    assert set(torch.nonzero(changed).flatten().tolist()) <= {b0 * 16 + i for i in range(4)}
+    # a count above the stride skips the sequence entirely
+    ops.kv_compact(k, v, case.tables, dst, keep_idx, torch.tensor([9, 0], dtype=torch.int32).cuda())
+    assert torch.equal(H.k_token_rows(k).view(torch.int16), krows.view(torch.int16))   # bits (NaN included)
+
+
+def test_eviction_end_to_end_mass_select_compact_attend():
+    """Decode with H2O mass -> should_cache keep-set on the GPU -> compaction into fresh blocks ->
+    decode over the compacted cache equals the oracle's attention over its own keep-set."""
+    lens = (600, 1200, 90, 2000)
+    w = dataclasses.replace(_case_workload("bf16", "bf16", 128, 32, 8, 79, lens=lens), extra_blocks=140)
+    case = H.Case(w)
+    lay = case.lay
+    L = lay.max_len
+    scores = torch.zeros((len(lens), L), dtype=torch.float32, device="cuda")
+    case.attend(attn_mass=scores)
+    idx, cnt = ops.keep_select(scores, case.lens, L, 4, 256, 252, "all")
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    free = list(lay.unused_blocks)
+    dst = np.full((len(lens), 32), -1, np.int32)
+    ref_keeps = []
+    for s, Ls in enumerate(lens):
+        _, probs = case.oracle(s)
+        ref_keep = policies.keep_select(probs.mean(axis=0), Ls, 4, 256, 252, "all")
+        assert idx_h[s, : cnt_h[s]].tolist() == ref_keep.tolist(), s
+        ref_keeps.append(ref_keep)
+        for j in range(-(-int(cnt_h[s]) // 16)):
+            dst[s, j] = free.pop()
+    k, v, ks, vs = case.pools
+    dst_t = torch.from_numpy(dst).cuda()
+    ops.kv_compact(k, v, case.tables, dst_t, idx, cnt, ks, vs)
+    q = W.queries(w, step=1, device="cuda")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn(out, q, k, v, dst_t, cnt, 512, k_scale=ks, v_scale=vs)
+    worst = 0.0
+    for s in range(len(lens)):
+        rows = torch.from_numpy(H.logical_rows(lay, s, ref_keeps[s])).to(case.ksrc.device)
+        kr, vr = H.to_f64(case.ksrc.index_select(0, rows)), H.to_f64(case.vsrc.index_select(0, rows))
+        ref, _ = attention.decode_attention(H.to_f64(q[s]), kr, vr, 1 / math.sqrt(w.head_dim))
+        worst = max(worst, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
+    print(f"eviction end to end: kept {cnt_h.tolist()}, max abs err {worst:.3e}")
+    assert worst <= 2e-3
