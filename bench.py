@@ -128,6 +128,80 @@ def cpu_baseline(w, lay, ksrc, vsrc, q, seconds):
             "seconds": round(dt, 2)}
 
 
+def bench_evict(args, dev, stream, read_gbs, copy_gbs):
+    """Eviction step on the h2o workload: kv_keep_select (H2OEviction.select: budget 2048, recent 512)
+    then kv_compact of every sequence's kept tokens into fresh blocks.  The scores come from one
+    untimed decode step with the H2O mass.  Bytes: compaction reads and writes each kept token's K and
+    V (all KV heads); the select reads the score rows and writes the keep lists."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads import device as H
+    from paged_kv_cache_283_amd import ops
+
+    base = W.WORKLOADS["h2o"]
+    per_seq = -(-base.budget // 16)
+    w = dataclasses.replace(base, extra_blocks=base.num_seqs * per_seq)
+    lay = W.make_layout(w)
+    tables = torch.from_numpy(lay.tables).to(dev)
+    lens = torch.from_numpy(lay.lens).to(dev)
+    pools = H.make_pools(w, lay.num_blocks)
+    ksrc, vsrc = W.kv_source(w, lay, device=dev)
+    H.fill(w, lay, pools, ksrc, vsrc, tables)
+    del ksrc, vsrc
+    k, v, ks, vs = pools
+    q = W.queries(w, device=dev)
+    L = lay.max_len
+    scores = torch.zeros((w.num_seqs, L), dtype=torch.float32, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ops.paged_decode_attn(out, q, k, v, tables, lens, L, k_scale=ks, v_scale=vs, attn_mass=scores)
+    free = np.asarray(lay.unused_blocks, dtype=np.int32)[: w.num_seqs * per_seq]
+    dst = torch.from_numpy(free.reshape(w.num_seqs, per_seq).copy()).to(dev)
+    keep_idx = torch.empty((w.num_seqs, w.budget), dtype=torch.int32, device=dev)
+    keep_count = torch.empty(w.num_seqs, dtype=torch.int32, device=dev)
+    rule = (0, w.recent, w.budget - w.recent, "rest")
+
+    def step(ev):
+        ev[0].record(stream)
+        ops.keep_select(scores, lens, L, *rule, keep_idx=keep_idx, keep_count=keep_count, stream=stream)
+        ev[1].record(stream)
+        ops.kv_compact(k, v, tables, dst, keep_idx, keep_count, ks, vs, stream=stream)
+        ev[2].record(stream)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(evs[0])
+    torch.cuda.synchronize()
+    ops.probe_read(torch.empty(1 << 30, dtype=torch.uint8, device=dev), torch.zeros(1024, device=dev))
+    for ev in evs:                  # enqueued behind a 1 GiB read so no launch gap enters the events
+        step(ev)
+    torch.cuda.synchronize()
+    sel_ms = [ev[0].elapsed_time(ev[1]) for ev in evs]
+    cmp_ms = [ev[1].elapsed_time(ev[2]) for ev in evs]
+    kept = int(keep_count.sum().item())
+    eb = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}[w.kv_dtype]
+    tok_bytes = w.num_kv_heads * w.head_dim * eb * 2 + (w.num_kv_heads * 8 if w.kv_dtype == "fp8" else 0)
+    moved = 2 * kept * tok_bytes                          # read + write of every kept token
+    sel_bytes = int(lens.sum().item()) * 4 + w.num_seqs * w.budget * 4
+    t_sel, t_cmp = float(np.median(sel_ms)), float(np.median(cmp_ms))
+    achieved = moved / (t_cmp * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "eviction step: H2O keep-set + compaction into fresh blocks, GB/s moved",
+        "value": round(moved / ((t_sel + t_cmp) * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_sel + t_cmp, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": "h2o-8k-evict", "batch": w.num_seqs, "context": L, "budget": w.budget,
+                   "recent": w.recent, "kept_tokens": kept, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "keep_select_us": round(1e3 * t_sel, 2), "keep_select_bytes": sel_bytes,
+        "compact_us": round(1e3 * t_cmp, 2), "compact_bytes": moved,
+        "probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +215,8 @@ def main():
     ap.add_argument("--probe-only", action="store_true", help="run only the HBM read/copy probes")
     ap.add_argument("--contiguous-blocks", action="store_true", help="hand out physical blocks in order "
                     "instead of the shuffled placement (comparison only)")
+    ap.add_argument("--op", default="decode", choices=("decode", "evict"),
+                    help="decode: the decode step (default); evict: H2O keep-set + compaction on the h2o workload")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -186,6 +262,10 @@ def main():
     if args.probe_only:
         print(json.dumps({"probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1),
                           "copy_bytes_per_launch": 2 * (probe_n // 4)}))
+        return
+
+    if args.op == "evict":
+        bench_evict(args, dev, stream, read_gbs, copy_gbs)
         return
 
     # ---- workload: pools filled through the library's own write path (untimed prefill)
