@@ -3,7 +3,7 @@
 
 A step is one decode step of one layer over the whole batch, every kernel of
 the path on the GPU with all inputs resident in HBM:
-  paged_decode_slots -> paged_kv_write (the new token of every sequence)
+  paged_kv_append (the new token of every sequence, slot from its table)
   -> paged_decode_attn (persistent attention kernel + log-sum-exp merge).
 Default workload: the Llama-3-8B-shaped layer (64 sequences, lengths U{512..8192},
 32 q / 8 KV heads, head_dim 128, bf16 KV, shuffled 16-token blocks).
@@ -289,7 +289,6 @@ def main():
     k_new, v_new = ksrc.index_select(0, r).contiguous(), vsrc.index_select(0, r).contiguous()
     q = W.queries(w, device=dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32, device=dev)
-    slots = torch.empty(w.num_seqs, dtype=torch.int64, device=dev)
     ws = ops.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, lay.max_len, w.num_sinks, w.window,
                              False, dev)
     torch.cuda.synchronize()
@@ -298,8 +297,7 @@ def main():
     for p in pools:
         k, v, ks, vs = p
         launches.append((
-            ops.paged_decode_slots(tables, lens, lay.num_blocks, slot_mapping=slots, stream=stream, prepare=True),
-            ops.paged_kv_write(k_new, v_new, k, v, slots, ks, vs, stream=stream, prepare=True),
+            ops.paged_kv_append(k_new, v_new, k, v, tables, lens, ks, vs, stream=stream, prepare=True),
             ops.paged_decode_attn(out, q, k, v, tables, lens, lay.max_len, k_scale=ks, v_scale=vs,
                                   num_sinks=w.num_sinks, window=w.window, workspace=ws, stream=stream,
                                   prepare=True)))

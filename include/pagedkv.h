@@ -124,6 +124,23 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype,
                    int num_kv_heads, int head_dim, int block_size, void* stream);
 
 /*
+ * paged_kv_append -- the decode step's cache write in one call: for every
+ * sequence s, the new token (k_new[s], v_new[s]) goes to logical position
+ * context_lens[s] - 1 through block_tables[s] ([PA] "PagedAttention 的设计": the
+ * token lands in block table[p / 16] at offset p % 16).  Same stores, FP8
+ * quantisation and dtype rules as paged_kv_write with the slots that
+ * paged_decode_slots computes; a sequence whose slot would be -1 there (length
+ * outside [1, 16 * stride], table entry outside [0, num_blocks)) is skipped.
+ *   k_new, v_new   [num_seqs][num_kv_heads][head_dim] of src_dtype
+ *   block_tables   int32 [num_seqs][block_table_stride]; context_lens int32 [num_seqs]
+ */
+int paged_kv_append(const void* k_new, const void* v_new, int src_dtype,
+                    void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+                    const int32_t* block_tables, int block_table_stride, const int32_t* context_lens,
+                    int num_seqs, int num_blocks, int num_kv_heads, int head_dim, int block_size,
+                    void* stream);
+
+/*
  * paged_decode_attn_workspace_size -- bytes of workspace paged_decode_attn needs.
  * Pass the same num_seqs, num_q_heads, head_dim, max_context_len, num_sinks,
  * window and (attn_mass != NULL) as the attention call.  Returns 0 for

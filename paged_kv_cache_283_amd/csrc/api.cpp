@@ -127,6 +127,32 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_
                        "paged_kv_write");
 }
 
+int paged_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool, float* k_scale,
+                    float* v_scale, int kv_dtype, const int32_t* block_tables, int block_table_stride,
+                    const int32_t* context_lens, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
+                    int block_size, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (!valid_float_dtype(src_dtype)) return fail(PKV_EINVAL, "src_dtype %d", src_dtype);
+  if (kv_dtype != PKV_FP8_E4M3 && src_dtype != kv_dtype)
+    return fail(PKV_EUNSUPPORTED, "a non-FP8 pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
+  if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
+  if (num_kv_heads < 1) return fail(PKV_EINVAL, "num_kv_heads %d < 1", num_kv_heads);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  if (block_table_stride < 1 || block_table_stride > (1 << 26))
+    return fail(PKV_EINVAL, "block_table_stride %d outside [1, 2^26]", block_table_stride);
+  if ((long long)num_seqs * num_kv_heads > (1LL << 32)) return fail(PKV_EINVAL, "num_seqs * num_kv_heads too large");
+  if (num_seqs == 0) return ok();
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "NULL array argument");
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
+  return device_status(pkv::launch_kv_append(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
+                                             block_tables, block_table_stride, context_lens, num_seqs, num_blocks,
+                                             num_kv_heads, head_dim, (hipStream_t)stream),
+                       "paged_kv_append");
+}
+
 size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
                                         int num_sinks, int window, int want_mass) {
   if (num_seqs < 0 || num_q_heads < 1 || (head_dim != 64 && head_dim != 128) || max_context_len < 1 ||

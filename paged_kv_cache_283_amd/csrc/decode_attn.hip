@@ -584,7 +584,9 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
 // Log-sum-exp merge of one (sequence, query head) per wave: the partials of the
 // segments the sequence was cut into (block 0 and every multiple of R inside
 // the sequence's span of the block list).  A sequence that was one segment
-// already has its output.
+// already has its output.  Lane i takes segment i (64 at a time): wave max of
+// the segment maxima, weights exp2(m_i - M), then every lane sums its output
+// dims over the segments with the weights broadcast.
 template <int D>
 __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
   const int s = blockIdx.y;
@@ -598,33 +600,46 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
   const int end = base + nva;
   const int c0 = (base / per + 1) * per;            // first cut after the sequence start
   if (c0 >= end) return;                            // one segment: written directly
+  const int n = 1 + (end - c0 + per - 1) / per;     // segments of this sequence
+  auto seg_slot = [&](int i) { return i == 0 ? 0 : partial_slot(c0 + (i - 1) * per - base); };
   const size_t hs = (size_t)s * a.num_q_heads + h;
   const float* ml = a.part_ml + hs * a.p_max * 2;
   const float* pacc = a.part_acc + hs * a.p_max * D;
-  float M = ml[0];
-  for (int b = c0; b < end; b += per) M = fmaxf(M, ml[2 * partial_slot(b - base)]);
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += kWave) M = fmaxf(M, ml[2 * seg_slot(i)]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
   constexpr int DL = D / 64;
-  float o[DL];
-  float lsum;
-  {
-    const float f = ml[0] == -INFINITY ? 0.f : fast_exp2(ml[0] - M);
-    lsum = f * ml[1];
+  float o_acc[DL];
 #pragma unroll
-    for (int e = 0; e < DL; ++e) o[e] = f * pacc[e * 64 + lane];
+  for (int e = 0; e < DL; ++e) o_acc[e] = 0.f;
+  float lpart = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + lane;
+    int sl = 0;
+    float f = 0.f;
+    if (i < n) {
+      sl = seg_slot(i);
+      const float mi = ml[2 * sl];
+      f = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
+      lpart += f * ml[2 * sl + 1];
+    }
+    const int cnt = min(kWave, n - i0);
+#pragma unroll 4
+    for (int k = 0; k < cnt; ++k) {
+      const float fk = __shfl(f, k, kWave);
+      const int sk = __shfl(sl, k, kWave);
+#pragma unroll
+      for (int e = 0; e < DL; ++e) o_acc[e] += fk * pacc[(size_t)sk * D + e * 64 + lane];
+    }
   }
-  for (int b = c0; b < end; b += per) {
-    const int slot = partial_slot(b - base);
-    const float mi = ml[2 * slot];
-    const float f = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
-    lsum += f * ml[2 * slot + 1];
 #pragma unroll
-    for (int e = 0; e < DL; ++e) o[e] += f * pacc[(size_t)slot * D + e * 64 + lane];
-  }
+  for (int o = 32; o >= 1; o >>= 1) lpart += __shfl_xor(lpart, o, kWave);
 #pragma unroll
-  for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + e * 64 + lane, a.out_dtype, o[e] / lsum);
+  for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + e * 64 + lane, a.out_dtype, o_acc[e] / lpart);
   if (a.fin_ml != nullptr && lane == 0) {
     a.fin_ml[hs * 2 + 0] = M;
-    a.fin_ml[hs * 2 + 1] = lsum;
+    a.fin_ml[hs * 2 + 1] = lpart;
   }
 }
 

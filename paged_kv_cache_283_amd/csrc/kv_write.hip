@@ -50,17 +50,34 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Where token t goes: slots[t], or -- for the decode append -- position
+// lens[t] - 1 of sequence t through its table row.
+struct SlotSource {
+  const int64_t* slots;    // non-null: explicit slots
+  const int32_t* tables;   // else: decode append
+  const int32_t* lens;
+  int stride;
+};
+
+__device__ __forceinline__ int64_t token_slot(const SlotSource& ss, int t, int num_blocks) {
+  if (ss.slots != nullptr) return ss.slots[t];
+  const int L = ss.lens[t];
+  if (L < 1 || L > ss.stride * kBlockSize) return -1;
+  const int b = ss.tables[(size_t)t * ss.stride + (L - 1) / kBlockSize];
+  return (b < 0 || b >= num_blocks) ? (int64_t)-1 : (int64_t)b * kBlockSize + (L - 1) % kBlockSize;
+}
+
 // One wave per (token, KV head) row; K and V of the row handled together.
 template <int SRC, int KVT, int D>
 __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                                                     float* k_scale, float* v_scale, const int64_t* slots,
+                                                     float* k_scale, float* v_scale, const SlotSource ss,
                                                      int num_tokens, int num_blocks, int num_kv_heads) {
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (long)num_tokens * num_kv_heads) return;
   const int t = (int)(row / num_kv_heads);
   const int h = (int)(row % num_kv_heads);
-  const int64_t slot = slots[t];
+  const int64_t slot = token_slot(ss, t, num_blocks);
   if (slot < 0 || slot >= (int64_t)num_blocks * kBlockSize) return;
   const size_t tile = (size_t)(slot / kBlockSize) * num_kv_heads + h;
   const int o = (int)(slot % kBlockSize);
@@ -137,17 +154,34 @@ namespace {
 
 template <int SRC, int KVT>
 hipError_t write_d(const void* k_new, const void* v_new, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
-                   const int64_t* slots, int num_tokens, int num_blocks, int num_kv_heads, int head_dim,
+                   const SlotSource& ss, int num_tokens, int num_blocks, int num_kv_heads, int head_dim,
                    hipStream_t st) {
   const long rows = (long)num_tokens * num_kv_heads;
   dim3 grid((unsigned)((rows + 3) / 4));
   if (head_dim == 64)
     hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, 64>), grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool, k_scale,
-                       v_scale, slots, num_tokens, num_blocks, num_kv_heads);
+                       v_scale, ss, num_tokens, num_blocks, num_kv_heads);
   else
     hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, 128>), grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                       k_scale, v_scale, slots, num_tokens, num_blocks, num_kv_heads);
+                       k_scale, v_scale, ss, num_tokens, num_blocks, num_kv_heads);
   return hipGetLastError();
+}
+
+hipError_t write_any(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool, float* k_scale,
+                     float* v_scale, int kv_dtype, const SlotSource& ss, int num_tokens, int num_blocks,
+                     int num_kv_heads, int head_dim, hipStream_t st) {
+  if (num_tokens == 0) return hipSuccess;
+#define PKV_WRITE(S, K) write_d<S, K>(k_new, v_new, k_pool, v_pool, k_scale, v_scale, ss, num_tokens, num_blocks, \
+                                      num_kv_heads, head_dim, st)
+  if (kv_dtype == DT_FP8) {
+    if (src_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_FP8);
+    if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_FP8);
+    return PKV_WRITE(DT_F16, DT_FP8);
+  }
+  if (kv_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_F32);
+  if (kv_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_BF16);
+  return PKV_WRITE(DT_F16, DT_F16);
+#undef PKV_WRITE
 }
 
 }  // namespace
@@ -172,18 +206,18 @@ hipError_t launch_token_slots(const int32_t* tables, int stride, int num_seqs, c
 hipError_t launch_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool,
                            float* k_scale, float* v_scale, int kv_dtype, const int64_t* slots, int num_tokens,
                            int num_blocks, int num_kv_heads, int head_dim, hipStream_t st) {
-  if (num_tokens == 0) return hipSuccess;
-#define PKV_WRITE(S, K) write_d<S, K>(k_new, v_new, k_pool, v_pool, k_scale, v_scale, slots, num_tokens, num_blocks, \
-                                      num_kv_heads, head_dim, st)
-  if (kv_dtype == DT_FP8) {
-    if (src_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_FP8);
-    if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_FP8);
-    return PKV_WRITE(DT_F16, DT_FP8);
-  }
-  if (kv_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_F32);
-  if (kv_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_BF16);
-  return PKV_WRITE(DT_F16, DT_F16);
-#undef PKV_WRITE
+  const SlotSource ss{slots, nullptr, nullptr, 0};
+  return write_any(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype, ss, num_tokens, num_blocks,
+                   num_kv_heads, head_dim, st);
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool,
+                            float* k_scale, float* v_scale, int kv_dtype, const int32_t* tables, int stride,
+                            const int32_t* lens, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
+                            hipStream_t st) {
+  const SlotSource ss{nullptr, tables, lens, stride};
+  return write_any(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype, ss, num_seqs, num_blocks,
+                   num_kv_heads, head_dim, st);
 }
 
 hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,

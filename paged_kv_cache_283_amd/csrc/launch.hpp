@@ -64,6 +64,11 @@ hipError_t launch_kv_write(const void* k_new, const void* v_new, int src_dtype, 
                            float* k_scale, float* v_scale, int kv_dtype, const int64_t* slots,
                            int num_tokens, int num_blocks, int num_kv_heads, int head_dim, hipStream_t stream);
 
+hipError_t launch_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k_pool, void* v_pool,
+                            float* k_scale, float* v_scale, int kv_dtype, const int32_t* tables, int stride,
+                            const int32_t* lens, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
+                            hipStream_t stream);
+
 hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
                              const int32_t* pairs, int num_pairs, int num_blocks, int num_kv_heads,
                              int head_dim, hipStream_t stream);

@@ -156,6 +156,26 @@ def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_s
                                      _ptr(slot_mapping), t, nb, hkv, d, BLOCK_SIZE, _stream(stream)), prepare)
 
 
+def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, context_lens, k_scale=None, v_scale=None,
+                    stream=None, prepare=False):
+    """Decode-step write: token s of k_new/v_new [B][Hkv][D] to position context_lens[s] - 1 of sequence s."""
+    b, hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must match")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    nb = k_pool.shape[0]
+    if (tuple(k_pool.shape) != k_pool_shape(nb, hkv, d, k_pool.dtype)
+            or tuple(v_pool.shape) != v_pool_shape(nb, hkv, d, v_pool.dtype)):
+        raise ValueError("pool shapes do not match k_new")
+    if context_lens.shape[0] != b or block_tables.shape[0] != b:
+        raise ValueError("one table row and one length per sequence")
+    return _issue("paged_kv_append", (_ptr(k_new), _ptr(v_new), float_code(k_new.dtype), _ptr(k_pool), _ptr(v_pool),
+                                      _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype), _ptr(block_tables),
+                                      block_tables.shape[1], _ptr(context_lens), b, nb, hkv, d, BLOCK_SIZE,
+                                      _stream(stream)), prepare)
+
+
 def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, device="cuda", fill_byte=None):
     """(k_pool, v_pool, k_scale, v_scale) in the library's layout; scales are None unless kv_dtype is FP8
     (torch.uint8 or torch.float8_e4m3fn).  fill_byte sets every byte (0xFF = NaN everywhere)."""

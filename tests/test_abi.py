@@ -144,3 +144,16 @@ def test_keep_select_and_compact_validation():
     assert c(FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 0, 64, 8, 128, 16, None) == _lib.OK
     assert c(ctypes.c_void_p(0x100008), FAKE, None, None, 1, FAKE, 8, FAKE, 8, FAKE, 32, FAKE, 2, 64, 8, 128, 16,
              None) == _lib.EINVAL                                                               # misaligned pool
+
+
+def test_append_validation():
+    lib = _lib.load()
+    ap = lib.paged_kv_append
+    #        k     v   src  kp    vp   ks    vs  kv tables stride lens  B  NB  H  D    bs
+    assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 4, 64, 8, 128, 8, None) == _lib.EUNSUPPORTED
+    assert ap(FAKE, FAKE, 0, FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 4, 64, 8, 128, 16, None) == _lib.EUNSUPPORTED
+    assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 3, FAKE, 8, FAKE, 4, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, FAKE, 0, FAKE, 4, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, -1, 64, 8, 128, 16, None) == _lib.EINVAL
+    assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 0, 64, 8, 128, 16, None) == _lib.OK
+    assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, None, 8, FAKE, 4, 64, 8, 128, 16, None) == _lib.EINVAL

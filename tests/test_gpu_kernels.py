@@ -515,3 +515,31 @@ def test_eviction_end_to_end_mass_select_compact_attend():
         worst = max(worst, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
     print(f"eviction end to end: kept {cnt_h.tolist()}, max abs err {worst:.3e}")
     assert worst <= 2e-3
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+def test_append_equals_slots_then_write(kv):
+    """paged_kv_append stores exactly what paged_decode_slots + paged_kv_write store, and skips the
+    sequences whose decode slot is -1."""
+    d = 64 if kv == "f32" else 128
+    w = dataclasses.replace(_case_workload(kv, "f32" if kv == "f32" else "bf16", d, 8, 2, 93,
+                                           lens=(35, 70, 16, 1, 200)), extra_blocks=4)
+    a, b = H.Case(w, hold_last=True), H.Case(w, hold_last=True)
+    lens = a.lens.clone()
+    lens[3] = 0                                    # invalid length: skipped by both
+    tables = a.tables.clone()
+    tables[4, (int(lens[4]) - 1) // 16] = a.lay.num_blocks + 7   # table entry outside the pool: skipped
+    k_new, v_new = a.newest_rows()
+    ka, va, ksa, vsa = a.pools
+    kb, vb, ksb, vsb = b.pools
+    ops.paged_kv_append(k_new, v_new, ka, va, tables, lens, ksa, vsa)
+    slots = ops.paged_decode_slots(tables, lens, b.lay.num_blocks)
+    assert slots[3].item() == -1 and slots[4].item() == -1
+    ops.paged_kv_write(k_new, v_new, kb, vb, slots, ksb, vsb)
+    for x, y in zip(a.pools, b.pools):
+        if x is not None:
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    out = a.attend()                                # and the appended tokens are attended correctly
+    for s in (0, 1, 2):
+        ref, _ = a.oracle(s)
+        assert np.max(np.abs(H.to_f64(out[s]) - ref)) <= TOL[kv]
