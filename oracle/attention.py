@@ -8,10 +8,19 @@
 [PA] = page "KV Cache 与 PagedAttention：显存复用与长上下文推理": decode reads KV block by block
        through the block table ("三大运行时组件"), so paging does not change the result.
 
+[SO] = page "系统优化", 4.5 "Chunked Prefill" and "分页 KV Cache + 前缀缓存": a long prompt
+       is processed in chunks interleaved with decode steps, over a paged
+       cache whose prefix may be shared; [PA] "共享场景的价值": a prefix-cache hit
+       skips the prefill of the shared part.
+
 Readings where the pages are silent:
   * query head h uses KV head h // G, G = n_heads / n_kv_heads (contiguous groups);
   * softmax scale is an argument (1/sqrt(head_dim) in every workload here);
-  * the decoded token is already in the cache and attends to itself.
+  * the decoded token is already in the cache and attends to itself;
+  * a prefill chunk of n_q tokens is the last n_q positions of the sequence,
+    already written to the cache; its token i (position p = L - n_q + i)
+    attends causally to positions 0..p, i.e. everything before the chunk
+    (the cached or shared prefix) and the chunk up to itself.
 """
 
 import numpy as np
@@ -74,3 +83,28 @@ def paged_decode(pools, kv_dtype: str, q, table_row, context_len: int, scale: fl
     V = np.zeros((context_len, hkv, d))
     K[pos], V[pos] = Kk, Vk
     return decode_attention(q, K, V, scale, keep)
+
+
+def prefill_attention(q, K, V, scale: float):
+    """Causal attention of the last n_q positions of a sequence over its whole context.
+
+    q [n_q][Hq][D]; K, V [L][Hkv][D] with L >= n_q.  Query i sits at position
+    L - n_q + i and attends to positions 0..L - n_q + i: each row is the decode
+    attention of that token over the context cut after it.  Returns out
+    [n_q][Hq][D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q, L = q.shape[0], np.asarray(K).shape[0]
+    if n_q < 1 or n_q > L:
+        raise ValueError("need 1 <= n_q <= L")
+    out = np.empty(q.shape)
+    for i in range(n_q):
+        p = L - n_q + i
+        out[i], _ = decode_attention(q[i], K[: p + 1], V[: p + 1], scale)
+    return out
+
+
+def paged_prefill(pools, kv_dtype: str, q, table_row, context_len: int, scale: float, num_blocks=None):
+    """prefill_attention of one sequence whose context is read through its block table."""
+    K, V = paging.gather_logical(pools, kv_dtype, table_row, np.arange(context_len), num_blocks)
+    return prefill_attention(q, K, V, scale)

@@ -167,3 +167,57 @@ def test_unmapped_read_raises_but_dropped_blocks_are_not_read():
     assert np.all(np.isfinite(out)) and np.all(probs[:, ~policies.streaming_keep(L, S, W)] == 0)
     with pytest.raises(IndexError):
         attention.paged_decode(pools, "f32", rng.standard_normal((2, 16)), table, L, 0.3)
+
+
+# ---------------------------------------------------------------------------- multi-query (chunked prefill)
+
+def test_prefill_single_query_is_decode():
+    rng = np.random.default_rng(11)
+    K, V = rng.standard_normal((40, 2, 16)), rng.standard_normal((40, 2, 16))
+    q = rng.standard_normal((1, 8, 16))
+    out = attention.prefill_attention(q, K, V, 0.25)
+    ref, _ = attention.decode_attention(q[0], K, V, 0.25)
+    assert np.array_equal(out[0], ref)
+
+
+@pytest.mark.parametrize("prefix,n_q,hq,hkv", [(0, 37, 8, 2), (50, 20, 4, 4), (100, 1, 8, 1), (3, 64, 16, 2)])
+def test_prefill_matches_torch_sdpa_with_bottom_right_causal_mask(prefix, n_q, hq, hkv):
+    """torch SDPA in float64 with the causal mask aligned to the end of the context (query i at
+    position prefix + i sees keys 0..prefix + i); prefix 0 is SDPA's own is_causal."""
+    rng = np.random.default_rng(prefix + n_q)
+    L, d = prefix + n_q, 32
+    K, V = rng.standard_normal((L, hkv, d)), rng.standard_normal((L, hkv, d))
+    q = rng.standard_normal((n_q, hq, d))
+    out = attention.prefill_attention(q, K, V, 1 / math.sqrt(d))
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]            # [1, Hq, n_q, D]
+    tk = torch.from_numpy(K).permute(1, 0, 2)[None]
+    tv = torch.from_numpy(V).permute(1, 0, 2)[None]
+    mask = torch.arange(L)[None, :] <= (prefix + torch.arange(n_q))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, enable_gqa=True)
+    assert np.max(np.abs(out - ref[0].permute(1, 0, 2).numpy())) <= 1e-12
+    if prefix == 0:
+        ref2 = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True)
+        assert np.max(np.abs(out - ref2[0].permute(1, 0, 2).numpy())) <= 1e-12
+
+
+def test_prefill_scalar_fsum_and_paging():
+    """Tiny case by scalar math.fsum, and the paged version through a shuffled table is identical."""
+    rng = np.random.default_rng(12)
+    L, n_q, hq, hkv, d = 21, 5, 4, 2, 16
+    K, V = rng.standard_normal((L, hkv, d)), rng.standard_normal((L, hkv, d))
+    q = rng.standard_normal((n_q, hq, d))
+    out = attention.prefill_attention(q, K, V, 0.3)
+    for i in range(n_q):
+        keep = np.arange(L) <= L - n_q + i
+        ref = _scalar_attention(q[i], K, V, 0.3, keep)
+        assert np.max(np.abs(out[i] - ref)) <= 1e-13
+    pools = paging.new_pools(6, hkv, d, "f32", fill=np.nan)
+    table = [4, 1]
+    paging.write_tokens(pools, "f32", K.astype(np.float32), V.astype(np.float32), "f32", [table], [0] * L,
+                        list(range(L)))
+    got = attention.paged_prefill(pools, "f32", q, table, L, 0.3)
+    exp = attention.prefill_attention(q, K.astype(np.float32).astype(np.float64),
+                                      V.astype(np.float32).astype(np.float64), 0.3)
+    assert np.array_equal(got, exp)
+    with pytest.raises(ValueError):
+        attention.prefill_attention(q, K[:3], V[:3], 0.3)
