@@ -197,6 +197,38 @@ int paged_decode_attn(void* out, int out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_prefill_attn -- causal multi-query attention over the paged cache: the
+ * chunked prefill of a long prompt ([SO] 4.5 "Chunked Prefill") or the
+ * continuation of a request whose prefix came from the prefix cache ([PA]
+ * "共享场景的价值": a hit skips the prefill of the shared part; [SO] 4.5
+ * "分页 KV Cache + 前缀缓存").
+ *
+ * Sequence s owns query rows [query_start[s], query_start[s+1]) of q and out;
+ * with n = query_start[s+1] - query_start[s] and L = context_lens[s], these are
+ * its last n positions, whose K/V are already in the cache (write them first,
+ * e.g. paged_token_slots + paged_kv_write).  Row i (position p = L - n + i) and
+ * query head h (KV head h / G) attend to positions 0..p:
+ *     out = sum_{t <= p} softmax_t(scale * q . K[t]) * V[t]
+ *   q, out         [num_tokens][num_q_heads][head_dim]; q_dtype / out_dtype F32, BF16, F16
+ *   query_start    int32 [num_seqs + 1], non-decreasing, query_start[num_seqs] <= num_tokens
+ *   context_lens   int32 [num_seqs], n <= L <= max_context_len
+ *   max_query_len  >= every n (sizes the grid)
+ *   G = num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}; head_dim 64 or 128
+ * No sinks/window here and no workspace.  A sequence whose rows fall outside
+ * [0, num_tokens) is skipped; one with L < n, L > max_context_len or L >
+ * 16 * stride, or that needs a table entry outside [0, num_blocks), gets NaN
+ * in its rows.  Rows not owned by any sequence are left untouched.
+ */
+int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype,
+                       const void* k_pool, const void* v_pool,
+                       const float* k_scale, const float* v_scale, int kv_dtype,
+                       const int32_t* block_tables, int block_table_stride,
+                       const int32_t* context_lens, const int32_t* query_start,
+                       int num_tokens, int max_context_len, int max_query_len,
+                       int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
+                       int head_dim, int block_size, float scale, void* stream);
+
+/*
  * kv_block_copy -- whole-block copies, the data half of copy-on-write.
  *
  * [PA] "三大运行时组件" and its copy_on_write snippet: before a sequence writes

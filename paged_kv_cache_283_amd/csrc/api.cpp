@@ -244,6 +244,64 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
                        "paged_decode_attn");
 }
 
+int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                       const float* k_scale, const float* v_scale, int kv_dtype, const int32_t* block_tables,
+                       int block_table_stride, const int32_t* context_lens, const int32_t* query_start,
+                       int num_tokens, int max_context_len, int max_query_len, int num_seqs, int num_blocks,
+                       int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PKV_EINVAL, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
+  const int g = num_q_heads / num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16)
+    return fail(PKV_EUNSUPPORTED, "%d query heads per KV head (built: 1, 2, 4, 8, 16)", g);
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (!valid_float_dtype(q_dtype)) return fail(PKV_EINVAL, "q_dtype %d", q_dtype);
+  if (!valid_float_dtype(out_dtype)) return fail(PKV_EINVAL, "out_dtype %d", out_dtype);
+  if (!isfinite(scale)) return fail(PKV_EINVAL, "scale is not finite");
+  if (num_seqs < 0 || num_seqs > 65535) return fail(PKV_EINVAL, "num_seqs %d outside [0, 65535]", num_seqs);
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
+  if (max_context_len < 1 || max_context_len > (1 << 30))
+    return fail(PKV_EINVAL, "max_context_len %d outside [1, 2^30]", max_context_len);
+  if (max_query_len < 1 || max_query_len > max_context_len)
+    return fail(PKV_EINVAL, "max_query_len %d outside [1, max_context_len]", max_query_len);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
+  if (block_table_stride < (max_context_len + 15) / 16 || block_table_stride > (1 << 26))
+    return fail(PKV_EINVAL, "block_table_stride %d < ceil(max_context_len / 16) (or > 2^26)", block_table_stride);
+  const long long tiles = (max_query_len + 4LL * (16 / g) - 1) / (4LL * (16 / g));
+  if (tiles * num_seqs * num_kv_heads > (1LL << 31) - 1) return fail(PKV_EINVAL, "grid too large");
+  if (num_seqs == 0 || num_tokens == 0) return ok();
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return fail(PKV_EINVAL, "NULL array argument");
+  if (kv_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8 pools need k_scale and v_scale");
+  if ((uintptr_t)q % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16 ||
+      (k_scale && (uintptr_t)k_scale % 16) || (v_scale && (uintptr_t)v_scale % 16))
+    return fail(PKV_EINVAL, "q, pools and scales must be 16-byte aligned");
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.table_stride = block_table_stride;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_tokens = num_tokens;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_blocks = num_blocks;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.tiles_per_pair = (int)tiles;
+  return device_status(pkv::launch_prefill_attn(a, kv_dtype, q_dtype, head_dim, (hipStream_t)stream),
+                       "paged_prefill_attn");
+}
+
 int kv_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype, const int32_t* block_pairs,
                   int num_pairs, int num_blocks, int num_kv_heads, int head_dim, int block_size, void* stream) {
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);

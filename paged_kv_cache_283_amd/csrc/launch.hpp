@@ -42,6 +42,28 @@ struct AttnArgs {
   int nv_pad;
 };
 
+// Causal multi-query attention over the paged cache (chunked prefill).
+struct PrefillArgs {
+  void* out;
+  int out_dtype;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  int table_stride;
+  const int32_t* context_lens;
+  const int32_t* query_start;   // [B + 1]: query rows of sequence s are [query_start[s], query_start[s + 1])
+  int num_tokens;               // rows of q and out
+  int max_context_len;
+  int num_seqs, num_blocks, num_q_heads, num_kv_heads;
+  float scale_log2;
+  int tiles_per_pair;           // workgroups per (sequence, KV head): ceil(max_query_len / (4 * 16 / G))
+};
+
+hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim, hipStream_t stream);
+
 struct WorkspaceLayout {
   size_t acc_off, ml_off, hdr_off, prefix_off, stash_off, fin_off, total;
   int p_max, nv_pad;

@@ -1,0 +1,354 @@
+// Causal multi-query attention over a paged KV cache for gfx950: the chunked
+// prefill of a long prompt, or the continuation of a request whose prefix came
+// from the prefix cache.
+//
+// Page "系统优化" 4.5 ("Chunked Prefill": a long prompt is processed in chunks
+// interleaved with decode steps; "分页 KV Cache + 前缀缓存": the cache is paged and
+// prefixes are shared) and page "KV Cache 与 PagedAttention：显存复用与长上下文推理",
+// "共享场景的价值" (a prefix-cache hit skips the prefill of the shared part).
+// The chunk of n_q query tokens of sequence s is its last n_q positions, whose
+// K/V are already in the cache; query i (position p_i = L - n_q + i) attends to
+// positions 0..p_i:
+//   out[i][h] = sum_{p <= p_i} softmax_p(scale * q[i][h] . K[p][h/G]) * V[p][h/G]
+//
+// How, on gfx950: the decode kernel's MFMA tile with its 16 B-operand columns
+// used as (query token, head) pairs -- 16/G tokens x G heads per wave -- so a
+// wave computes S = K q^T for 16 query rows with one 16x16x32 MFMA per 32 head
+// dims and PV with the probabilities straight from the QK accumulator.  Each
+// column carries its own causal limit (a per-lane mask on the logits).  A
+// workgroup is 4 waves = 4 * 16/G consecutive query tokens of one (sequence,
+// KV head); its waves walk the same blocks, so the tiles come from HBM once
+// and from the caches for the other waves.  Work is split by query token only:
+// every wave covers the whole causal range of its tokens.
+#include "device_common.hpp"
+#include "launch.hpp"
+#include "mfma_ops.hpp"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfTab = 1024;              // table entries staged per wave and chunk
+constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators are rescaled
+
+}  // namespace
+
+template <int KVT, int QT, int D>
+__global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
+  using KT = KvType<KVT>;
+  constexpr int EB = KT::kBytes;
+  constexpr bool OP32 = KT::kOp32;
+  constexpr bool F16 = KT::kOpF16;
+  constexpr int DPL = D / 4;
+  constexpr int KW = DPL * EB / 4;
+  constexpr int NT = D / 16;
+  constexpr int VW = EB;
+  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16));
+  constexpr bool QSPLIT = (!OP32) && !QSAME;
+  constexpr int QW = OP32 ? 1 : DPL / 2;
+  __shared__ int s_tab_all[kPfWaves][kPfTab];
+
+  const int hq = a.num_q_heads;
+  const int hkv = a.num_kv_heads;
+  const int group = hq / hkv;
+  const int tpw = 16 / group;                    // query tokens per wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+  int* s_tab = s_tab_all[wave];
+
+  // Workgroup -> (sequence, KV head, tile).  With a pair count divisible by 8,
+  // all tiles of a (sequence, KV head) go to one XCD (ids are dealt to the 8
+  // XCDs in turn), so the waves re-reading its blocks share that XCD's L2.
+  const int tiles = a.tiles_per_pair;
+  const int pairs = a.num_seqs * hkv;
+  int pair, tile;
+  if ((pairs & 7) == 0) {
+    const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
+    pair = (k / tiles) * 8 + xcd;
+    tile = k % tiles;
+  } else {
+    pair = blockIdx.x / tiles;
+    tile = blockIdx.x % tiles;
+  }
+  const int s = pair / hkv, kvh = pair % hkv;
+  const int q0 = a.query_start[s];
+  const int n_q = a.query_start[s + 1] - q0;
+  const int L = a.context_lens[s];
+  const int t0 = (tile * kPfWaves + wave) * tpw;   // first query token of this wave
+  if (q0 < 0 || n_q < 1 || n_q > a.num_tokens - q0 || t0 >= n_q) return;   // rows outside q/out: skip
+  const int prefix = L - n_q;
+  const bool seq_ok = L >= n_q && L <= a.max_context_len && L <= a.table_stride * kBlockSize;
+
+  // ---- column c = (query token t0 + c / G, head kvh * G + c % G)
+  const int tok = t0 + c / group;
+  const bool col_ok = tok < n_q;
+  const int head = kvh * group + c % group;
+  const int pos = col_ok ? prefix + tok : -1;     // causal limit of the column (-1: no keys)
+  const size_t qrow = ((size_t)(q0 + (col_ok ? tok : 0)) * hq + head) * D;
+  uint32_t qhi[QW];
+  uint32_t qlo[QSPLIT ? QW : 1];
+  float qf[OP32 ? DPL : 1];
+  if constexpr (OP32) {
+#pragma unroll
+    for (int st = 0; st < DPL; ++st) qf[st] = col_ok ? load_q_elem<QT>(a.q, qrow + qk_dim_f32(st, j)) : 0.f;
+  } else if constexpr (QSAME) {
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + qrow;
+#pragma unroll
+    for (int st = 0; st < QW / 4; ++st) {
+      const u32x4 v = col_ok ? *reinterpret_cast<const u32x4*>(qh + qk_dim16<KVT>(st, j)) : u32x4{0, 0, 0, 0};
+      qhi[4 * st + 0] = v[0]; qhi[4 * st + 1] = v[1]; qhi[4 * st + 2] = v[2]; qhi[4 * st + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < QW / 4; ++st) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d0 = qk_dim16<KVT>(st, j) + 2 * w;
+        const float f0 = col_ok ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
+        const float f1 = col_ok ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+        const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
+        const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
+        const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
+        qhi[4 * st + w] = h0 | (h1 << 16);
+        qlo[4 * st + w] = l0 | (l1 << 16);
+      }
+    }
+  }
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool bad = !seq_ok;
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
+  const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
+  // Keys the wave needs: 0 .. prefix + last token of the wave; keys below
+  // prefix + t0 are visible to every column (no mask there).
+  const int t_last = min(t0 + tpw, n_q) - 1;
+  const int n_blocks = seq_ok ? (prefix + t_last) / kBlockSize + 1 : 0;
+  const int all_visible = prefix + t0;             // keys p < this are seen by all columns
+  int c0 = 0;
+
+  struct Regs {
+    uint32_t k[KW];
+    uint32_t v[NT][VW];
+    f32x4 ks, vs;
+    bool ok;
+  };
+
+  auto load = [&](Regs& r, int i) {
+    const int phys = __builtin_amdgcn_readfirstlane(s_tab[i]);
+    r.ok = phys >= 0 && phys < a.num_blocks;
+    const size_t tile_i = (size_t)(r.ok ? phys : 0) * hkv + kvh;   // block 0 stands in for a bad entry
+    const uint8_t* kt = kbase + tile_i * (size_t)(kBlockSize * D * EB);
+#pragma unroll
+    for (int w = 0; w < KW / 4; ++w) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(kt + ((size_t)(4 * w + j) * kBlockSize + c) * 16);
+      r.k[4 * w + 0] = v[0]; r.k[4 * w + 1] = v[1]; r.k[4 * w + 2] = v[2]; r.k[4 * w + 3] = v[3];
+    }
+    const uint8_t* vt = vbase + tile_i * (size_t)(kBlockSize * D * EB);
+    uint32_t* vw = &r.v[0][0];
+#pragma unroll
+    for (int g = 0; g < NT * VW / 4; ++g) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(vt + ((size_t)(g * 16 + c) * 4 + j) * 16);
+      vw[4 * g + 0] = v[0]; vw[4 * g + 1] = v[1]; vw[4 * g + 2] = v[2]; vw[4 * g + 3] = v[3];
+    }
+    if constexpr (KVT == DT_FP8) {
+      r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile_i * kBlockSize + 4 * j);
+      r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile_i * kBlockSize + 4 * j);
+    }
+  };
+
+  auto compute = [&](Regs& r, int i) {
+    bad |= !r.ok;
+    const int blk0 = (c0 + i) * kBlockSize;
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (OP32) {
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) sacc = mfma_f32_k4(__uint_as_float(r.k[e]), qf[e], sacc);
+    } else {
+#pragma unroll
+      for (int st = 0; st < DPL / 8; ++st) {
+        uint32_t av[4];
+        if constexpr (KVT == DT_FP8) {
+          fp8x4_to_bf16x4(r.k[2 * st], av[0], av[1]);
+          fp8x4_to_bf16x4(r.k[2 * st + 1], av[2], av[3]);
+        } else {
+          av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
+        }
+        sacc = mfma_k32<F16>(av, &qhi[4 * st], sacc);
+        if constexpr (QSPLIT) sacc = mfma_k32<F16>(av, &qlo[4 * st], sacc);
+      }
+    }
+    // logits (base 2); keys past the column's position get -inf, keys past the
+    // context (the unused tail of the last block) also get V zeroed
+    const bool full = blk0 + kBlockSize <= all_visible;
+    float x[4];
+    bool in_ctx[4] = {true, true, true, true};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = sacc[e] * a.scale_log2;
+      if constexpr (KVT == DT_FP8) x[e] *= r.ks[e];
+    }
+    if (!full) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int p = blk0 + 4 * j + e;
+        in_ctx[e] = p < L;
+        x[e] = p <= pos ? x[e] : -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (VW == 1) {
+          const uint32_t msk = (in_ctx[0] ? 0xffu : 0u) | (in_ctx[1] ? 0xff00u : 0u) |
+                               (in_ctx[2] ? 0xff0000u : 0u) | (in_ctx[3] ? 0xff000000u : 0u);
+          r.v[t][0] &= msk;
+        } else if constexpr (VW == 2) {
+          r.v[t][0] &= (in_ctx[0] ? 0xffffu : 0u) | (in_ctx[1] ? 0xffff0000u : 0u);
+          r.v[t][1] &= (in_ctx[2] ? 0xffffu : 0u) | (in_ctx[3] ? 0xffff0000u : 0u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r.v[t][e] = in_ctx[e] ? r.v[t][e] : 0u;
+        }
+      }
+    }
+    const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const bool need = mb > m_run + kPfRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+      const float m_new = need ? mb : m_run;
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+      m_run = m_new;
+    }
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[e] - mref);
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (KVT == DT_FP8) pv[e] = in_ctx[e] ? pr[e] * r.vs[e] : 0.f;
+      else pv[e] = pr[e];
+    }
+    if constexpr (OP32) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t] = mfma_f32_k4(__uint_as_float(r.v[t][e]), pv[e], acc[t]);
+      }
+    } else {
+      uint32_t ph[2], pl[2];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
+        uint32_t h0, h1, l0, l1;
+        if constexpr (F16) {
+          h0 = f32_to_f16_bits(f0);
+          h1 = f32_to_f16_bits(f1);
+          l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
+          l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
+        } else {
+          h0 = __float_as_uint(f0) >> 16;
+          h1 = __float_as_uint(f1) >> 16;
+          l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
+          l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
+        }
+        ph[w] = h0 | (h1 << 16);
+        pl[w] = l0 | (l1 << 16);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint32_t v0, v1;
+        if constexpr (KVT == DT_FP8) {
+          fp8x4_to_bf16x4(r.v[t][0], v0, v1);
+        } else {
+          v0 = r.v[t][0];
+          v1 = r.v[t][1];
+        }
+        acc[t] = mfma_k16<F16>(v0, v1, ph[0], ph[1], acc[t]);
+        acc[t] = mfma_k16<F16>(v0, v1, pl[0], pl[1], acc[t]);
+      }
+    }
+  };
+
+  for (; c0 < n_blocks; c0 += kPfTab) {
+    const int n = min(kPfTab, n_blocks - c0);
+    for (int k = lane; k < n; k += kWave) s_tab[k] = trow[c0 + k];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    Regs r0, r1, r2;
+    int i = 0;
+    if (n > 0) load(r0, 0);
+    if (n > 1) load(r1, 1);
+    for (; i + 4 < n; i += 3) {
+      load(r2, i + 2);
+      compute(r0, i);
+      load(r0, i + 3);
+      compute(r1, i + 1);
+      load(r1, i + 4);
+      compute(r2, i + 2);
+    }
+    if (i + 2 < n) load(r2, i + 2);
+    if (i < n) compute(r0, i);
+    if (i + 3 < n) load(r0, i + 3);
+    if (i + 1 < n) compute(r1, i + 1);
+    if (i + 2 < n) compute(r2, i + 2);
+    if (i + 3 < n) compute(r0, i + 3);
+    __builtin_amdgcn_wave_barrier();   // the next chunk rewrites this wave's s_tab
+  }
+
+  l_run = row_sum4(l_run);
+  if (bad) l_run = __builtin_nanf("");
+  if (!col_ok) return;
+  const size_t orow = ((size_t)(q0 + tok) * hq + head) * D;
+  const float inv = 1.f / l_run;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, acc[t][e] * inv);
+  }
+}
+
+namespace {
+
+template <int KVT, int QT>
+hipError_t prefill_d(const PrefillArgs& a, int d, hipStream_t st) {
+  const int pairs = a.num_seqs * a.num_kv_heads;
+  const dim3 grid((unsigned)pairs * a.tiles_per_pair);
+  if (d == 64) hipLaunchKernelGGL((prefill_kernel<KVT, QT, 64>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((prefill_kernel<KVT, QT, 128>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int KVT>
+hipError_t prefill_q(const PrefillArgs& a, int q_dtype, int d, hipStream_t st) {
+  switch (q_dtype) {
+    case DT_F32: return prefill_d<KVT, DT_F32>(a, d, st);
+    case DT_BF16: return prefill_d<KVT, DT_BF16>(a, d, st);
+    default: return prefill_d<KVT, DT_F16>(a, d, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim, hipStream_t st) {
+  if (a.num_seqs == 0 || a.tiles_per_pair == 0) return hipSuccess;
+  switch (kv_dtype) {
+    case DT_F32: return prefill_q<DT_F32>(a, q_dtype, head_dim, st);
+    case DT_BF16: return prefill_q<DT_BF16>(a, q_dtype, head_dim, st);
+    case DT_F16: return prefill_q<DT_F16>(a, q_dtype, head_dim, st);
+    default: return prefill_q<DT_FP8>(a, q_dtype, head_dim, st);
+  }
+}
+
+}  // namespace pkv

@@ -243,6 +243,27 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     return p if prepare else out
 
 
+def paged_prefill_attn(out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_context_len,
+                       max_query_len, scale=None, k_scale=None, v_scale=None, stream=None, prepare=False):
+    """Causal multi-query attention: q/out [T][Hq][D]; sequence s owns rows
+    [query_start[s], query_start[s+1]), its last positions of a context of context_lens[s] tokens."""
+    t, hq, d = q.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    if tuple(out.shape) != (t, hq, d):
+        raise ValueError("out must have q's shape")
+    for x, n in ((block_tables, "block_tables"), (context_lens, "context_lens"), (query_start, "query_start")):
+        _need(x, torch.int32, n)
+    b = context_lens.shape[0]
+    if query_start.shape[0] != b + 1 or block_tables.shape[0] != b:
+        raise ValueError("query_start needs num_seqs + 1 entries and block_tables one row per sequence")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
+            _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), _ptr(query_start), t, int(max_context_len), int(max_query_len), b, nb, hq, hkv, d,
+            BLOCK_SIZE, float(scale), _stream(stream))
+    return _issue("paged_prefill_attn", args, prepare)
+
+
 def kv_block_copy(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None, stream=None):
     """Copy whole blocks per int32 [n][2] {src, dst} pair (the data half of copy-on-write)."""
     _need(block_pairs, torch.int32, "block_pairs")

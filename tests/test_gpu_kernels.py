@@ -543,3 +543,89 @@ def test_append_equals_slots_then_write(kv):
     for s in (0, 1, 2):
         ref, _ = a.oracle(s)
         assert np.max(np.abs(H.to_f64(out[s]) - ref)) <= TOL[kv]
+
+
+# ---------------------------------------------------------------------------- multi-query (chunked prefill)
+
+def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):
+    w = _case_workload(kv, q, d, hq, hkv, seed, lens=lens)
+    case = H.Case(w)
+    g = torch.Generator().manual_seed(seed)
+    T = int(sum(n_qs))
+    qt = torch.randn((T, hq, d), generator=g).to(W.storage_dtype(q) if q != "f32" else torch.float32).cuda()
+    qs = torch.tensor(np.concatenate([[0], np.cumsum(n_qs)]).astype(np.int32)).cuda()
+    return w, case, qt, qs
+
+
+def _prefill_oracle(w, case, qt, qs, s):
+    L = int(case.lay.lens[s])
+    kr, vr = H.kept_source(w, case.lay, s, case.ksrc, case.vsrc)
+    if w.kv_dtype == "fp8":
+        kc, ksc = fp8.quantize_per_token(kr.astype(np.float32))
+        vc, vsc = fp8.quantize_per_token(vr.astype(np.float32))
+        kr, vr = fp8.dequantize_per_token(kc, ksc), fp8.dequantize_per_token(vc, vsc)
+    a, b = int(qs[s]), int(qs[s + 1])
+    return attention.prefill_attention(H.to_f64(qt[a:b]), kr, vr, 1 / math.sqrt(w.head_dim))
+
+
+PREFILL_GRID = [
+    # kv, q, d, hq, hkv
+    ("bf16", "bf16", 128, 32, 8),     # G = 4: 4 query tokens per wave
+    ("fp8", "bf16", 128, 32, 8),
+    ("f32", "f32", 64, 8, 2),
+    ("f16", "f16", 128, 16, 16),      # G = 1: 16 query tokens per wave
+    ("bf16", "f32", 64, 16, 2),       # G = 8, split query operand
+    ("bf16", "bf16", 128, 16, 1),     # G = 16: one token per wave
+]
+
+
+@pytest.mark.parametrize("kv,q,d,hq,hkv", PREFILL_GRID)
+def test_prefill_matches_oracle(kv, q, d, hq, hkv):
+    lens = (70, 300, 17, 129, 1)
+    n_qs = (70, 37, 1, 64, 1)          # whole prompt, chunk after a prefix, single token, ragged tails
+    w, case, qt, qs = _prefill_case(kv, q, d, hq, hkv, 101, lens, n_qs)
+    out = torch.full(qt.shape, float("nan"), dtype=torch.float32, device="cuda")
+    k, v, ks, vs = case.pools
+    ops.paged_prefill_attn(out, qt, k, v, case.tables, case.lens, qs, case.lay.max_len, max(n_qs),
+                           k_scale=ks, v_scale=vs)
+    worst = 0.0
+    for s in range(len(lens)):
+        ref = _prefill_oracle(w, case, qt, qs, s)
+        a, b = int(qs[s]), int(qs[s + 1])
+        worst = max(worst, float(np.max(np.abs(H.to_f64(out[a:b]) - ref))))
+    print(f"prefill {kv}/{q} d{d} {hq}/{hkv}: max abs err {worst:.3e}")
+    assert worst <= TOL[kv]
+
+
+def test_prefill_last_row_equals_decode():
+    """The last query row of a chunk attends to the whole context: it is the decode step's attention."""
+    lens = (200, 1000)
+    n_qs = (50, 9)
+    w, case, qt, qs = _prefill_case("bf16", "bf16", 128, 32, 8, 102, lens, n_qs)
+    out = torch.empty(qt.shape, dtype=torch.float32, device="cuda")
+    k, v, _, _ = case.pools
+    ops.paged_prefill_attn(out, qt, k, v, case.tables, case.lens, qs, case.lay.max_len, 50)
+    last = qt[qs[1:].long() - 1].contiguous()
+    dec = torch.empty(last.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn(dec, last, k, v, case.tables, case.lens, case.lay.max_len)
+    assert torch.max(torch.abs(dec - out[qs[1:].long() - 1])).item() <= 1e-5
+
+
+def test_prefill_invalid_sequences():
+    lens = (40, 40, 40)
+    n_qs = (8, 8, 8)
+    w, case, qt, qs = _prefill_case("bf16", "bf16", 64, 8, 2, 103, lens, n_qs)
+    lens_bad = case.lens.clone()
+    lens_bad[1] = 5                                   # shorter than its chunk: NaN rows
+    tables = case.tables.clone()
+    tables[2, 0] = case.lay.num_blocks + 3            # a block outside the pool: NaN rows
+    out = torch.zeros(qt.shape, dtype=torch.float32, device="cuda")
+    k, v, _, _ = case.pools
+    ops.paged_prefill_attn(out, qt, k, v, tables, lens_bad, qs, case.lay.max_len, 8)
+    assert torch.all(torch.isfinite(out[0:8])) and torch.all(torch.isnan(out[8:24]))
+    # rows outside [0, num_tokens): the sequence is skipped, nothing written
+    qs_bad = qs.clone()
+    qs_bad[3] = 30
+    out2 = torch.zeros(qt.shape, dtype=torch.float32, device="cuda")
+    ops.paged_prefill_attn(out2, qt, k, v, case.tables, case.lens, qs_bad, case.lay.max_len, 8)
+    assert torch.all(out2[16:24] == 0) and torch.all(torch.isfinite(out2[:16]))
