@@ -202,6 +202,67 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
         "probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1)}), flush=True)
 
 
+MFMA_PEAK_BF16_TFLOPS = 2500.0
+
+
+def bench_prefill(args, dev, stream):
+    """Chunked prefill on the prefill workload: 4 sequences whose last 2048 tokens (after a 6144-token
+    cached prefix, 8192 batched tokens in all) attend causally over the paged cache.  Algorithmic work:
+    4 * D flops per (query token, attended key, query head) -- 2 D for q.k and 2 D for p.v."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads import device as H
+    from paged_kv_cache_283_amd import ops
+
+    w = W.WORKLOADS["prefill"]
+    lay = W.make_layout(w)
+    tables = torch.from_numpy(lay.tables).to(dev)
+    lens = torch.from_numpy(lay.lens).to(dev)
+    pools = H.make_pools(w, lay.num_blocks)
+    ksrc, vsrc = W.kv_source(w, lay, device=dev)
+    H.fill(w, lay, pools, ksrc, vsrc, tables)
+    del ksrc, vsrc
+    k, v, ks, vs = pools
+    q, start = W.chunk_queries(w, device=dev)
+    qs = torch.from_numpy(start).to(dev)
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    call = ops.paged_prefill_attn(out, q, k, v, tables, lens, qs, lay.max_len, w.chunk, k_scale=ks, v_scale=vs,
+                                  stream=stream, prepare=True)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for ev in evs:
+        ev[0].record(stream)
+        call()
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([ev[0].elapsed_time(ev[1]) for ev in evs])
+    pairs = 0
+    for L in lay.lens:
+        pre = int(L) - w.chunk
+        pairs += w.chunk * pre + w.chunk * (w.chunk + 1) // 2      # keys attended by the chunk's rows
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    t = float(np.median(ms))
+    tflops = flops / (t * 1e-3) / 1e12
+    kv_bytes = int(lay.lens.sum()) * w.num_kv_heads * 2 * w.head_dim * 2
+    print(json.dumps({
+        "metric": "chunked prefill over the paged cache: causal multi-query attention TFLOP/s",
+        "value": round(tflops, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": "prefill-4x2048-after-6144", "batch": w.num_seqs, "chunk": w.chunk,
+                   "context": int(lay.max_len), "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "batched_tokens": w.num_seqs * w.chunk},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "flops_per_step": flops, "prefill_kernel_avg_us": round(1e3 * float(np.mean(ms)), 2),
+        "prefill_kernel_min_us": round(1e3 * float(ms.min()), 2), "kv_bytes_in_context": kv_bytes,
+        "tokens_per_s": round(w.num_seqs * w.chunk / (t * 1e-3), 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,8 +276,9 @@ def main():
     ap.add_argument("--probe-only", action="store_true", help="run only the HBM read/copy probes")
     ap.add_argument("--contiguous-blocks", action="store_true", help="hand out physical blocks in order "
                     "instead of the shuffled placement (comparison only)")
-    ap.add_argument("--op", default="decode", choices=("decode", "evict"),
-                    help="decode: the decode step (default); evict: H2O keep-set + compaction on the h2o workload")
+    ap.add_argument("--op", default="decode", choices=("decode", "evict", "prefill"),
+                    help="decode: the decode step (default); evict: H2O keep-set + compaction on the h2o "
+                         "workload; prefill: causal multi-query attention on the prefill workload")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -266,6 +328,9 @@ def main():
 
     if args.op == "evict":
         bench_evict(args, dev, stream, read_gbs, copy_gbs)
+        return
+    if args.op == "prefill":
+        bench_prefill(args, dev, stream)
         return
 
     # ---- workload: pools filled through the library's own write path (untimed prefill)

@@ -49,11 +49,13 @@ class Workload:
     shared_prefix: Tuple[int, int] = (0, 0)     # (sequences, leading blocks) shared by seqs 0..n-1
     extra_blocks: int = 1                       # unreferenced (poisoned) blocks in the pool
     pool_blocks: Optional[int] = None           # fixed pool size (else just enough + extra)
+    chunk: int = 0                              # multi-query: query tokens per sequence (its last positions)
 
 
 WORKLOADS = {
     "tiny": Workload("tiny", 2, 8, 2, 64, "f32", "f32", "f32", 2831, lens=(35, 70), pool_blocks=16),
     "llama3": Workload("llama3", 64, 32, 8, 128, "bf16", "bf16", "bf16", 2832, len_range=(512, 8192)),
+    "prefill": Workload("prefill", 4, 32, 8, 128, "bf16", "bf16", "bf16", 2836, lens=(8192,) * 4, chunk=2048),
     "fp8long": Workload("fp8long", 16, 32, 8, 128, "fp8", "bf16", "bf16", 2833, lens=(32768,) * 16,
                         shared_prefix=(4, 128)),
     "streaming": Workload("streaming", 32, 32, 8, 128, "bf16", "bf16", "bf16", 2834, lens=(131072,) * 32,
@@ -190,6 +192,14 @@ def kv_source(w: Workload, lay: Layout, layer: int = 0, device="cpu"):
 
 def queries(w: Workload, layer: int = 0, step: int = 0, device="cpu"):
     return randn((w.num_seqs, w.num_q_heads, w.head_dim), w.q_dtype, w.seed * 1000 + 7 * layer + step + 17, device)
+
+
+def chunk_queries(w: Workload, device="cpu"):
+    """Multi-query rows [num_seqs * chunk][Hq][D] (sequence-major) and query_start int32 [num_seqs + 1]."""
+    import numpy as np
+    q = randn((w.num_seqs * w.chunk, w.num_q_heads, w.head_dim), w.q_dtype, w.seed * 1000 + 29, device)
+    start = np.arange(w.num_seqs + 1, dtype=np.int32) * w.chunk
+    return q, start
 
 
 def storage_dtype(kv_dtype: str):
