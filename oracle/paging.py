@@ -12,10 +12,10 @@ open and is taken here as the storage convention (the same one the HIP
 library documents):
 
   K pool  [num_blocks][num_kv_heads][head_dim/X][16][X]          X = 16 bytes of elements:
-                                                                8 for bf16/f16, 16 for fp8, 4 for f32
+                                                                8 for bf16/f16, 16 for fp8/int8, 4 for f32
   V pool  [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4] Y = 4 / bytes per element:
-                                                                2 for bf16/f16, 4 for fp8, 1 for f32
-  scales  [num_blocks][num_kv_heads][16] float32                 FP8 only, K and V separately
+                                                                2 for bf16/f16, 4 for fp8/int8, 1 for f32
+  scales  [num_blocks][num_kv_heads][16] float32                 fp8 and int8 only, K and V separately
 
 (K element (token o, dim d) of a block tile sits at chunk d // X, row o, lane
 d % X.  V element (token o, dim d), with t = d // 16, sits at index
@@ -23,16 +23,21 @@ d % X.  V element (token o, dim d), with t = d // 16, sits at index
 tokens of Y dims 16 apart.)
 
 Storage dtypes are held here as raw numpy arrays: "f32" float32, "bf16" uint16
-bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes.
+bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes, "int8" int8 codes.
 """
 
 import numpy as np
 
-from . import fp8
+from . import fp8, int8
 
 BLOCK_SIZE = 16
-DTYPES = ("f32", "bf16", "f16", "fp8")
-_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "fp8": np.uint8}
+DTYPES = ("f32", "bf16", "f16", "fp8", "int8")
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "fp8": np.uint8, "int8": np.int8}
+_CODECS = {"fp8": fp8, "int8": int8}       # quantised storage: codes + one scale per (token, KV head)
+
+
+def quantised(kv_dtype: str) -> bool:
+    return kv_dtype in _CODECS
 
 
 def storage_dtype(kv_dtype: str):
@@ -56,6 +61,8 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if dtype == "fp8":
         return fp8.decode(a)
+    if dtype == "int8":
+        return int8.decode(a)
     raise ValueError(dtype)
 
 
@@ -106,7 +113,7 @@ def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, 
     y = v_chunk_dims(kv_dtype)
     k = np.full((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x), fill, dtype=st)
     v = np.full((num_blocks, num_kv_heads, _v_groups(head_dim, kv_dtype), 16, 4, y, 4), fill, dtype=st)
-    if kv_dtype == "fp8":
+    if quantised(kv_dtype):
         ks = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
         vs = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
     else:
@@ -125,17 +132,18 @@ def write_tokens(pools, kv_dtype: str, k_src, v_src, src_dtype: str, table_rows,
     """
     k_pool, v_pool, k_scale, v_scale = pools
     nb, hkv, nc, _, x = k_pool.shape
-    if kv_dtype == "fp8":
-        if src_dtype == "fp8":
-            raise ValueError("fp8 pools take f32/bf16/f16 sources")
-        kq, ks = fp8.quantize_per_token(to_f64(k_src, src_dtype).astype(np.float32))
-        vq, vs = fp8.quantize_per_token(to_f64(v_src, src_dtype).astype(np.float32))
+    if quantised(kv_dtype):
+        if quantised(src_dtype):
+            raise ValueError("fp8/int8 pools take f32/bf16/f16 sources")
+        codec = _CODECS[kv_dtype]
+        kq, ks = codec.quantize_per_token(to_f64(k_src, src_dtype).astype(np.float32))
+        vq, vs = codec.quantize_per_token(to_f64(v_src, src_dtype).astype(np.float32))
     elif src_dtype != kv_dtype:
         raise ValueError("a non-fp8 pool stores source bytes of its own dtype")
     for t, (s, p) in enumerate(zip(seq_ids, positions)):
         b = physical_block(table_rows[s], p, nb)
         o = p % BLOCK_SIZE
-        if kv_dtype == "fp8":
+        if quantised(kv_dtype):
             k_pool[b, :, :, o, :] = kq[t].reshape(hkv, nc, x)
             _v_put(v_pool[b, :, :, :, o // 4, :, o % 4], vq[t], kv_dtype)
             k_scale[b, :, o] = ks[t]
@@ -161,7 +169,7 @@ def gather_logical(pools, kv_dtype: str, table_row, positions, num_blocks=None):
         o = int(p) % BLOCK_SIZE
         k = to_f64(k_pool[b, :, :, o, :].reshape(hkv, d), kv_dtype)
         v = to_f64(_v_get(v_pool[b, :, :, :, o // 4, :, o % 4]), kv_dtype)
-        if kv_dtype == "fp8":
+        if quantised(kv_dtype):
             k = k * k_scale[b, :, o].astype(np.float64)[:, None]
             v = v * v_scale[b, :, o].astype(np.float64)[:, None]
         K[i], V[i] = k, v
