@@ -35,12 +35,12 @@
  *           chunks: Y = 4 / element bytes (2 for BF16/F16, 4 for FP8, 1 for F32);
  *           element (token o, dim d), t = d / 16, is at [t / Y][d % 16][o / 4][t % Y][o % 4]
  *           (each chunk: 4 consecutive tokens of Y dims that are 16 apart)
- *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 only)
+ *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 and PKV_INT8 only)
  * A token at logical position p of a sequence lives in physical block
  * table[p / 16] at offset p % 16 ([PA] "物理布局示意", [LC] block-table sketch);
- * its flat slot is block * 16 + offset.  With FP8 the stored value is
+ * its flat slot is block * 16 + offset.  With FP8 or INT8 the stored value is
  * decode(code) * scale, one scale per (token, KV head) for K and one for V
- * ([PA] "量化原理": per-token scaling).
+ * ([PA] "量化原理": INT8 or FP8 halve the KV bytes; per-token scaling).
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -64,7 +64,8 @@ typedef enum {
   PKV_F32 = 0,
   PKV_BF16 = 1,
   PKV_F16 = 2,
-  PKV_FP8_E4M3 = 3       /* OCP E4M3FN: bias 7, max 448, no infinities, 0x7F/0xFF = NaN */
+  PKV_FP8_E4M3 = 3,      /* OCP E4M3FN: bias 7, max 448, no infinities, 0x7F/0xFF = NaN */
+  PKV_INT8 = 4           /* two's-complement int8 codes in [-127, 127] */
 } pkv_dtype;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -110,10 +111,13 @@ int paged_token_slots(const int32_t* block_tables, int block_table_stride, int n
  *     scale = absmax / 448        (IEEE fp32 division, correctly rounded)
  *     code  = E4M3FN(x / scale)   (fp32 division; round to nearest, ties to even,
  *                                  saturating to +-448; absmax 0 -> scale 0, codes 0)
+ * and for INT8 pools with
+ *     scale = absmax / 127,  code = clamp(rint(x / scale), -127, 127)
+ *                                 (fp32 division; nearest integer, ties to even)
  * and the scale is stored beside the codes.
  *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of src_dtype
  *   kv_dtype       PKV_F32/BF16/F16 require src_dtype == kv_dtype (bytes are copied);
- *                  PKV_FP8_E4M3 takes src_dtype F32, BF16 or F16 (finite values)
+ *                  PKV_FP8_E4M3 and PKV_INT8 take src_dtype F32, BF16 or F16 (finite values)
  *   k_scale, v_scale   required for FP8, ignored otherwise
  *   slot_mapping   int64 [num_tokens]; a slot < 0 or >= num_blocks*16 skips the token
  * Two tokens with the same slot race (one of them wins).
@@ -166,7 +170,7 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
  *
  *   out            [num_seqs][num_q_heads][head_dim] of out_dtype (F32/BF16/F16)
  *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (F32/BF16/F16)
- *   kv_dtype       F32, BF16, F16 or FP8_E4M3 (then k_scale/v_scale are required)
+ *   kv_dtype       F32, BF16, F16, FP8_E4M3 or INT8 (then k_scale/v_scale are required)
  *   block_tables   int32 [num_seqs][block_table_stride], stride >= ceil(max_context_len/16)
  *   context_lens   int32 [num_seqs], 1 <= L <= max_context_len (host value)
  *   num_q_heads / num_kv_heads in 1..16; head_dim 64 or 128; block_size 16

@@ -62,7 +62,7 @@ constexpr float kRescaleSlack = 8.f;
 #define PKV_ATTN_WAVES_PER_CU 4      // waves launched per CU, one per SIMD (0: as many as fit)
 #endif
 #ifndef PKV_ATTN_WAVES_PER_CU_FP8
-#define PKV_ATTN_WAVES_PER_CU_FP8 8  // the same for FP8 pools (two per SIMD)
+#define PKV_ATTN_WAVES_PER_CU_FP8 8  // the same for 8-bit (FP8, INT8) pools (two per SIMD)
 #endif
 #ifndef PKV_ATTN_HEAD_FAST
 #define PKV_ATTN_HEAD_FAST 1         // 1: workgroup id = range * KV heads + head; 0: head-major
@@ -204,7 +204,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
       const u32x4 v = load_stream(reinterpret_cast<const u32x4*>(vt + ((size_t)(g * 16 + c) * 4 + j) * 16));
       vw[4 * g + 0] = v[0]; vw[4 * g + 1] = v[1]; vw[4 * g + 2] = v[2]; vw[4 * g + 3] = v[3];
     }
-    if constexpr (KVT == DT_FP8) {
+    if constexpr (is_quantised(KVT)) {
       r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile * kBlockSize + 4 * j);
       r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile * kBlockSize + 4 * j);
     }
@@ -224,9 +224,9 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
-        if constexpr (KVT == DT_FP8) {
-          fp8x4_to_bf16x4(r.k[2 * st], av[0], av[1]);
-          fp8x4_to_bf16x4(r.k[2 * st + 1], av[2], av[3]);
+        if constexpr (is_quantised(KVT)) {
+          code8x4_to_bf16x4<KVT>(r.k[2 * st], av[0], av[1]);
+          code8x4_to_bf16x4<KVT>(r.k[2 * st + 1], av[2], av[3]);
         } else {
           av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
         }
@@ -243,7 +243,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x[e] = sacc[e] * a.scale_log2;
-      if constexpr (KVT == DT_FP8) x[e] *= r.ks[e];
+      if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
     }
     if (!full) {
 #pragma unroll
@@ -298,7 +298,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     float pv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (KVT == DT_FP8) pv[e] = valid[e] ? pr[e] * r.vs[e] : 0.f;
+      if constexpr (is_quantised(KVT)) pv[e] = valid[e] ? pr[e] * r.vs[e] : 0.f;
       else pv[e] = pr[e];
     }
 
@@ -332,8 +332,8 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t v0, v1;
-        if constexpr (KVT == DT_FP8) {
-          fp8x4_to_bf16x4(r.v[t][0], v0, v1);
+        if constexpr (is_quantised(KVT)) {
+          code8x4_to_bf16x4<KVT>(r.v[t][0], v0, v1);
         } else {
           v0 = r.v[t][0];
           v1 = r.v[t][1];
@@ -616,7 +616,7 @@ int resident_waves() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wave_kernel<KVT, QT, D>, kWave, 0) != hipSuccess)
     return 0;
   if (per_cu < 1) per_cu = 1;
-  const int want = KVT == DT_FP8 ? PKV_ATTN_WAVES_PER_CU_FP8 : PKV_ATTN_WAVES_PER_CU;
+  const int want = is_quantised(KVT) ? PKV_ATTN_WAVES_PER_CU_FP8 : PKV_ATTN_WAVES_PER_CU;
   if (want > 0 && want < per_cu) per_cu = want;
   const int n = cus * per_cu;
   cache[dev] = n;
@@ -689,7 +689,8 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
     case DT_F32: err = dispatch_q<DT_F32>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_F16: err = dispatch_q<DT_F16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
-    default: err = dispatch_q<DT_FP8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    case DT_FP8: err = dispatch_q<DT_FP8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    default: err = dispatch_q<DT_INT8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
   }
   if (err != hipSuccess) return err;
   {

@@ -9,7 +9,10 @@
 
 namespace pkv {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3, DT_INT8 = 4 };
+
+// Storage formats with 8-bit codes and one scale per (token, KV head).
+__host__ __device__ constexpr bool is_quantised(int kv) { return kv == DT_FP8 || kv == DT_INT8; }
 
 constexpr int kWave = 64;          // CDNA wavefront width
 
@@ -52,6 +55,27 @@ __device__ __forceinline__ uint32_t half_word(uint32_t w, int e) { return e ? (w
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+}
+
+// Four int8 codes (one word, two's complement) -> four bf16 values (two words;
+// byte 0 in the low half of lo), exactly: |code| <= 128 needs 8 significant
+// bits.  XOR 0x80 turns each code into code + 128 as an unsigned byte, which
+// v_cvt_f32_ubyte* converts; subtracting 128 is exact.
+__device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t b = w ^ 0x80808080u;
+  const float f0 = (float)(b & 0xffu) - 128.f;
+  const float f1 = (float)((b >> 8) & 0xffu) - 128.f;
+  const float f2 = (float)((b >> 16) & 0xffu) - 128.f;
+  const float f3 = (float)(b >> 24) - 128.f;
+  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+}
+
+// 8-bit codes of storage format KV -> bf16 operands.
+template <int KV>
+__device__ __forceinline__ void code8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  if constexpr (KV == DT_INT8) int8x4_to_bf16x4(w, lo, hi);
+  else fp8x4_to_bf16x4(w, lo, hi);
 }
 
 // Wave64 butterfly reductions over lanes that differ in bits 4 and 5 of the

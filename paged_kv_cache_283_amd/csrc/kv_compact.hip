@@ -135,13 +135,14 @@ hipError_t launch_kv_compact(void* k_pool, void* v_pool, float* k_scale, float* 
                              const int32_t* keep_idx, int keep_stride, const int32_t* keep_count, int num_seqs,
                              int num_blocks, int num_kv_heads, int head_dim, hipStream_t st) {
   if (num_seqs == 0 || keep_stride == 0) return hipSuccess;
-  float* ks = kv_dtype == DT_FP8 ? k_scale : nullptr;
-  float* vs = kv_dtype == DT_FP8 ? v_scale : nullptr;
+  float* ks = is_quantised(kv_dtype) ? k_scale : nullptr;
+  float* vs = is_quantised(kv_dtype) ? v_scale : nullptr;
   switch (kv_dtype) {
     case DT_F32:
       return compact_d<4>(k_pool, v_pool, ks, vs, src_tables, src_stride, dst_tables, dst_stride, keep_idx,
                           keep_stride, keep_count, num_seqs, num_blocks, num_kv_heads, head_dim, st);
     case DT_FP8:
+    case DT_INT8:
       return compact_d<1>(k_pool, v_pool, ks, vs, src_tables, src_stride, dst_tables, dst_stride, keep_idx,
                           keep_stride, keep_count, num_seqs, num_blocks, num_kv_heads, head_dim, st);
     default:

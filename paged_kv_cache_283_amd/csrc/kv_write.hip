@@ -4,7 +4,7 @@
 // Page "KV Cache 与 PagedAttention：显存复用与长上下文推理" (plumephp.com/ai-kv-cache-paged-attention):
 //   "PagedAttention 的设计" -- a token lives in the physical block its sequence's
 //     block table names for logical block p / 16, at offset p % 16;
-//   "量化原理" -- FP8 (E4M3) storage with per-token scales;
+//   "量化原理" -- FP8 (E4M3) or INT8 storage with per-token scales;
 //   "三大运行时组件" and copy_on_write -- a shared block is copied before a write.
 // Pool layout: K [NB][Hkv][D/X][16][X] (16-byte chunks of X elements),
 // V [NB][Hkv][D/(16Y)][16][4][Y][4] (16-byte chunks of 4 tokens x Y dims), FP8 scales
@@ -42,6 +42,19 @@ __device__ __forceinline__ float src_to_f32(const void* p, size_t i) {
   if constexpr (SRC == DT_F32) return reinterpret_cast<const float*>(p)[i];
   else if constexpr (SRC == DT_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
   else return f16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+}
+
+// One 8-bit code of the quotient x / scale: E4M3FN (round to nearest even,
+// saturating to +-448) or INT8 (nearest integer, ties to even -- v_rndne_f32 --
+// saturated to +-127, two's complement).
+template <int KVT>
+__device__ __forceinline__ uint32_t encode8(float q) {
+  if constexpr (KVT == DT_INT8) {
+    const float r = fminf(fmaxf(__builtin_rintf(q), -127.f), 127.f);
+    return (uint32_t)(int32_t)r & 0xffu;
+  } else {
+    return e4m3fn_encode(q);
+  }
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -83,7 +96,8 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
   const int o = (int)(slot % kBlockSize);
   const size_t src = (size_t)row * D;
   constexpr int PER = D / 64;
-  if constexpr (KVT == DT_FP8) {
+  if constexpr (is_quantised(KVT)) {
+    constexpr float kMaxCode = KVT == DT_INT8 ? 127.f : 448.f;
     float kx[PER], vx[PER];
     float kmax = 0.f, vmax = 0.f;
 #pragma unroll
@@ -95,15 +109,15 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
     }
     kmax = wave_max(kmax);
     vmax = wave_max(vmax);
-    const float ks = __fdiv_rn(kmax, 448.f);
-    const float vs = __fdiv_rn(vmax, 448.f);
+    const float ks = __fdiv_rn(kmax, kMaxCode);
+    const float vs = __fdiv_rn(vmax, kMaxCode);
     uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool);
     uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int d = e * 64 + lane;
-      const uint32_t kc = ks == 0.f ? 0u : e4m3fn_encode(__fdiv_rn(kx[e], ks));
-      const uint32_t vc = vs == 0.f ? 0u : e4m3fn_encode(__fdiv_rn(vx[e], vs));
+      const uint32_t kc = ks == 0.f ? 0u : encode8<KVT>(__fdiv_rn(kx[e], ks));
+      const uint32_t vc = vs == 0.f ? 0u : encode8<KVT>(__fdiv_rn(vx[e], vs));
       kp[tile * kBlockSize * D + k_chunk_offset<1>(o, d)] = (uint8_t)kc;
       vp[tile * kBlockSize * D + v_chunk_offset<1>(o, d)] = (uint8_t)vc;
     }
@@ -178,6 +192,11 @@ hipError_t write_any(const void* k_new, const void* v_new, int src_dtype, void* 
     if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_FP8);
     return PKV_WRITE(DT_F16, DT_FP8);
   }
+  if (kv_dtype == DT_INT8) {
+    if (src_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_INT8);
+    if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_INT8);
+    return PKV_WRITE(DT_F16, DT_INT8);
+  }
   if (kv_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_F32);
   if (kv_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_BF16);
   return PKV_WRITE(DT_F16, DT_F16);
@@ -224,14 +243,14 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* 
                              const int32_t* pairs, int num_pairs, int num_blocks, int num_kv_heads, int head_dim,
                              hipStream_t st) {
   if (num_pairs == 0) return hipSuccess;
-  const int eb = kv_dtype == DT_F32 ? 4 : (kv_dtype == DT_FP8 ? 1 : 2);
+  const int eb = kv_dtype == DT_F32 ? 4 : (is_quantised(kv_dtype) ? 1 : 2);
   const size_t block_bytes = (size_t)num_kv_heads * kBlockSize * head_dim * eb;
   const int scale_floats = num_kv_heads * kBlockSize;
   const unsigned chunks = (unsigned)((block_bytes / 16 + 255) / 256);
   dim3 grid(chunks < 64 ? chunks : 64, num_pairs);
   hipLaunchKernelGGL(block_copy_kernel, grid, dim3(256), 0, st, reinterpret_cast<uint8_t*>(k_pool),
-                     reinterpret_cast<uint8_t*>(v_pool), kv_dtype == DT_FP8 ? k_scale : nullptr,
-                     kv_dtype == DT_FP8 ? v_scale : nullptr, pairs, num_blocks, block_bytes, scale_floats);
+                     reinterpret_cast<uint8_t*>(v_pool), is_quantised(kv_dtype) ? k_scale : nullptr,
+                     is_quantised(kv_dtype) ? v_scale : nullptr, pairs, num_blocks, block_bytes, scale_floats);
   return hipGetLastError();
 }
 

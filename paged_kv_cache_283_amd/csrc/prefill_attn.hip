@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(vt + ((size_t)(g * 16 + c) * 4 + j) * 16);
       vw[4 * g + 0] = v[0]; vw[4 * g + 1] = v[1]; vw[4 * g + 2] = v[2]; vw[4 * g + 3] = v[3];
     }
-    if constexpr (KVT == DT_FP8) {
+    if constexpr (is_quantised(KVT)) {
       r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile_i * kBlockSize + 4 * j);
       r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile_i * kBlockSize + 4 * j);
     }
@@ -176,9 +176,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
-        if constexpr (KVT == DT_FP8) {
-          fp8x4_to_bf16x4(r.k[2 * st], av[0], av[1]);
-          fp8x4_to_bf16x4(r.k[2 * st + 1], av[2], av[3]);
+        if constexpr (is_quantised(KVT)) {
+          code8x4_to_bf16x4<KVT>(r.k[2 * st], av[0], av[1]);
+          code8x4_to_bf16x4<KVT>(r.k[2 * st + 1], av[2], av[3]);
         } else {
           av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
         }
@@ -194,7 +194,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       x[e] = sacc[e] * a.scale_log2;
-      if constexpr (KVT == DT_FP8) x[e] *= r.ks[e];
+      if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
     }
     if (!full) {
 #pragma unroll
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     float pv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (KVT == DT_FP8) pv[e] = in_ctx[e] ? pr[e] * r.vs[e] : 0.f;
+      if constexpr (is_quantised(KVT)) pv[e] = in_ctx[e] ? pr[e] * r.vs[e] : 0.f;
       else pv[e] = pr[e];
     }
     if constexpr (OP32) {
@@ -268,8 +268,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t v0, v1;
-        if constexpr (KVT == DT_FP8) {
-          fp8x4_to_bf16x4(r.v[t][0], v0, v1);
+        if constexpr (is_quantised(KVT)) {
+          code8x4_to_bf16x4<KVT>(r.v[t][0], v0, v1);
         } else {
           v0 = r.v[t][0];
           v1 = r.v[t][1];
@@ -347,7 +347,8 @@ hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, 
     case DT_F32: return prefill_q<DT_F32>(a, q_dtype, head_dim, st);
     case DT_BF16: return prefill_q<DT_BF16>(a, q_dtype, head_dim, st);
     case DT_F16: return prefill_q<DT_F16>(a, q_dtype, head_dim, st);
-    default: return prefill_q<DT_FP8>(a, q_dtype, head_dim, st);
+    case DT_FP8: return prefill_q<DT_FP8>(a, q_dtype, head_dim, st);
+    default: return prefill_q<DT_INT8>(a, q_dtype, head_dim, st);
   }
 }
 

@@ -5,8 +5,9 @@ kernels of libpagedkv.so.  Function names and argument meanings are those of
 include/pagedkv.h; shapes are read off the tensors.
 
 Storage dtypes: torch.float32 / bfloat16 / float16 pools hold those values;
-torch.uint8 or torch.float8_e4m3fn pools hold OCP E4M3FN codes with
-float32 scale tensors [num_blocks][num_kv_heads][16].  Pool shapes:
+torch.uint8 or torch.float8_e4m3fn pools hold OCP E4M3FN codes and torch.int8
+pools hold INT8 codes, both with float32 scale tensors
+[num_blocks][num_kv_heads][16].  Pool shapes:
 K [num_blocks][num_kv_heads][head_dim/X][16][X] (X = 16 bytes of elements),
 V [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4] (Y = 4 / element bytes);
 allocate_pools builds both.
@@ -38,9 +39,18 @@ def float_code(dtype: torch.dtype) -> int:
 
 
 def kv_code(dtype: torch.dtype) -> int:
+    """Storage code of a pool dtype: float32/bfloat16/float16 values, uint8 (or float8_e4m3fn) E4M3FN
+    codes, int8 codes."""
     if dtype in _fp8_dtypes():
         return _lib.FP8_E4M3
+    if dtype == torch.int8:
+        return _lib.INT8
     return float_code(dtype)
+
+
+def quantised(dtype: torch.dtype) -> bool:
+    """Pools of 8-bit codes carry one float32 scale per (token, KV head)."""
+    return kv_code(dtype) in (_lib.FP8_E4M3, _lib.INT8)
 
 
 def _ptr(t):
@@ -182,7 +192,7 @@ def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, 
     k = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
     v = torch.empty(v_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
     ks = vs = None
-    if kv_code(kv_dtype) == _lib.FP8_E4M3:
+    if quantised(kv_dtype):
         ks = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)
         vs = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)
     if fill_byte is not None:

@@ -20,11 +20,11 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from tests import _harness as H
 
-TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "fp8": 1e-2}
+TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "fp8": 1e-2, "int8": 1e-2}
 
 
 def _case_workload(kv, q, d, hq, hkv, seed, lens=(35, 70), **kw):
-    src = "bf16" if kv == "fp8" else kv
+    src = "bf16" if kv in ("fp8", "int8") else kv
     return dataclasses.replace(W.WORKLOADS["tiny"], name=f"t-{kv}-{q}-{d}", kv_dtype=kv, src_dtype=src, q_dtype=q,
                                head_dim=d, num_q_heads=hq, num_kv_heads=hkv, seed=seed, pool_blocks=None,
                                extra_blocks=3, lens=tuple(lens), num_seqs=len(lens), **kw)
@@ -72,7 +72,8 @@ def test_decode_and_token_slots_match_oracle():
 # ---------------------------------------------------------------------------- write
 
 @pytest.mark.parametrize("kv,src,d", [("f32", "f32", 64), ("bf16", "bf16", 128), ("f16", "f16", 128),
-                                      ("fp8", "bf16", 128), ("fp8", "f32", 64), ("fp8", "f16", 128)])
+                                      ("fp8", "bf16", 128), ("fp8", "f32", 64), ("fp8", "f16", 128),
+                                      ("int8", "bf16", 128), ("int8", "f32", 64), ("int8", "f16", 128)])
 def test_write_pool_bytes_bit_exact(kv, src, d):
     w = dataclasses.replace(_case_workload(kv, "bf16", d, 8, 2, 91, lens=(35, 70, 16, 1)), src_dtype=src)
     case = H.Case(w)
@@ -157,6 +158,8 @@ GRID = [
     ("fp8", "bf16", 128, 32, 8),
     ("fp8", "f32", 64, 8, 8),
     ("fp8", "f16", 128, 16, 2),
+    ("int8", "bf16", 128, 32, 8),
+    ("int8", "f32", 64, 8, 2),
 ]
 LENS = (1, 15, 16, 17, 35, 70, 511, 512, 513, 1100, 2049)
 
@@ -271,7 +274,7 @@ def test_invalid_device_values_poison_only_their_sequence():
 
 # ---------------------------------------------------------------------------- copy-on-write
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_copy_on_write(kv):
     """Four sequences share four blocks; seq 3 gets a private copy of its last block (a COW)."""
     w = dataclasses.replace(_case_workload(kv, "bf16", 128, 32, 8, 21, lens=(64,) * 4), shared_prefix=(4, 4),
@@ -409,7 +412,8 @@ def test_keep_select_bit_exact():
     assert cnt[7].item() == -1 and cnt[8].item() == -1 and torch.all(idx[7:9] == -1)
 
 
-_NP = {torch.float32: np.float32, torch.bfloat16: np.uint16, torch.float16: np.float16, torch.uint8: np.uint8}
+_NP = {torch.float32: np.float32, torch.bfloat16: np.uint16, torch.float16: np.float16, torch.uint8: np.uint8,
+       torch.int8: np.int8}
 
 
 def _host_pools(pools, kv):
@@ -418,7 +422,7 @@ def _host_pools(pools, kv):
         _NP[t.dtype]).reshape(t.shape) for t in pools]
 
 
-@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("fp8", 128), ("fp8", 64)])
+@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("fp8", 128), ("fp8", 64), ("int8", 128)])
 def test_compact_pool_bytes_bit_exact(kv, d):
     """kv_compact moves kept tokens exactly as the oracle's compact does; no other byte changes."""
     lens = (35, 70, 300, 1, 129)
@@ -517,7 +521,7 @@ def test_eviction_end_to_end_mass_select_compact_attend():
     assert worst <= 2e-3
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32", "int8"])
 def test_append_equals_slots_then_write(kv):
     """paged_kv_append stores exactly what paged_decode_slots + paged_kv_write store, and skips the
     sequences whose decode slot is -1."""
@@ -560,10 +564,7 @@ def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):
 def _prefill_oracle(w, case, qt, qs, s):
     L = int(case.lay.lens[s])
     kr, vr = H.kept_source(w, case.lay, s, case.ksrc, case.vsrc)
-    if w.kv_dtype == "fp8":
-        kc, ksc = fp8.quantize_per_token(kr.astype(np.float32))
-        vc, vsc = fp8.quantize_per_token(vr.astype(np.float32))
-        kr, vr = fp8.dequantize_per_token(kc, ksc), fp8.dequantize_per_token(vc, vsc)
+    kr, vr = H.stored_values(w.kv_dtype, kr), H.stored_values(w.kv_dtype, vr)
     a, b = int(qs[s]), int(qs[s + 1])
     return attention.prefill_attention(H.to_f64(qt[a:b]), kr, vr, 1 / math.sqrt(w.head_dim))
 
@@ -572,6 +573,7 @@ PREFILL_GRID = [
     # kv, q, d, hq, hkv
     ("bf16", "bf16", 128, 32, 8),     # G = 4: 4 query tokens per wave
     ("fp8", "bf16", 128, 32, 8),
+    ("int8", "bf16", 128, 32, 8),
     ("f32", "f32", 64, 8, 2),
     ("f16", "f16", 128, 16, 16),      # G = 1: 16 query tokens per wave
     ("bf16", "f32", 64, 16, 2),       # G = 8, split query operand

@@ -32,7 +32,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str                  # "f32" | "bf16" | "f16" | "fp8"
+    kv_dtype: str                  # "f32" | "bf16" | "f16" | "fp8" | "int8"
     src_dtype: str                 # dtype of the new K/V rows written into the cache
     q_dtype: str
     seed: int
@@ -204,4 +204,5 @@ def chunk_queries(w: Workload, device="cpu"):
 
 def storage_dtype(kv_dtype: str):
     torch = _torch()
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.uint8}[kv_dtype]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.uint8,
+            "int8": torch.int8}[kv_dtype]
