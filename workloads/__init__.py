@@ -58,6 +58,7 @@ WORKLOADS = {
     "prefill": Workload("prefill", 4, 32, 8, 128, "bf16", "bf16", "bf16", 2836, lens=(8192,) * 4, chunk=2048),
     "fp8long": Workload("fp8long", 16, 32, 8, 128, "fp8", "bf16", "bf16", 2833, lens=(32768,) * 16,
                         shared_prefix=(4, 128)),
+    "int8long": Workload("int8long", 16, 32, 8, 128, "int8", "bf16", "bf16", 2837, lens=(32768,) * 16),
     "streaming": Workload("streaming", 32, 32, 8, 128, "bf16", "bf16", "bf16", 2834, lens=(131072,) * 32,
                           num_sinks=4, window=4096, table_width=8192,
                           mapped_ranges=((0, 1), (7936, 8192)), extra_blocks=0),
