@@ -18,7 +18,8 @@ The tables here hold block ids; the GPU-side data copy of a COW is the
 kv_block_copy entry point, run by the caller with the (src, dst) pairs these
 methods return, before writing into the new block.
 """
-from collections import deque
+import hashlib
+from collections import OrderedDict, deque
 
 import numpy as np
 
@@ -178,3 +179,152 @@ class BlockManager:
                 "shared_blocks": int((self.refcount > 1).sum()), "cow_copies": self.cow_copies,
                 "internal_fragmentation_tokens": int(sum(len(t) * self.block_size - self.lens[s]
                                                          for s, t in self.tables.items()))}
+
+
+class PrefixCachingBlockManager(BlockManager):
+    """BlockManager whose full blocks are also found by the token prefix they complete.
+
+    Page "KV Cache 与 PagedAttention：显存复用与长上下文推理", "共享场景的价值": requests that
+    share a system prompt, a RAG document or a conversation history can share
+    its KV; with vLLM-style prefix caching a request that arrives is matched
+    block by block against cached prefixes, and a hit skips the prefill of the
+    shared part ("按 token 前缀匹配缓存块，命中则跳过 prefill"); cached blocks are shared
+    physically, with reference counts and copy-on-write.  The page also advises
+    putting reused text first, since matching is by prefix.
+
+    Design: each full block is keyed by a chained digest, hash(parent key,
+    its 16 token ids), so a key names the whole prefix up to the end of that
+    block.  Blocks are registered once their KV is written (`commit`).  A
+    cached block whose last user frees it keeps its contents and its key and
+    waits in an LRU list; allocation takes never-cached free blocks first and
+    then evicts the least recently freed cached block.  Only full blocks are
+    shared, and writes only ever go to a sequence's partial last block, so a
+    shared block is never written.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        super().__init__(num_blocks, block_size)
+        self._by_key = {}               # prefix key -> block
+        self._key_of = {}               # block -> prefix key
+        self._evictable = OrderedDict()  # cached blocks with refcount 0, least recently freed first
+        self.tokens = {}                # seq -> token ids held
+        self.hits = 0                   # blocks reused from the cache
+        self.evictions = 0
+
+    @staticmethod
+    def block_key(parent, tokens) -> bytes:
+        """Chained key of a full block: digest of the parent key and the block's token ids."""
+        h = hashlib.blake2b(digest_size=16)
+        h.update(parent if parent is not None else b"\x00")
+        h.update(np.asarray(tokens, dtype=np.int64).tobytes())
+        return h.digest()
+
+    def _keys(self, tokens):
+        keys, parent = [], None
+        for i in range(len(tokens) // self.block_size):
+            parent = self.block_key(parent, tokens[i * self.block_size:(i + 1) * self.block_size])
+            keys.append(parent)
+        return keys
+
+    # ---- pool: free blocks first, then the least recently freed cached block
+    def _alloc(self) -> int:
+        if not self._free and self._evictable:
+            b, _ = self._evictable.popitem(last=False)
+            del self._by_key[self._key_of.pop(b)]
+            self._free.append(b)
+            self.evictions += 1
+        return super()._alloc()
+
+    def _release(self, b: int) -> None:
+        if self.refcount[b] <= 0:
+            raise RuntimeError(f"block {b} released more often than referenced")
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            if b in self._key_of:
+                self._evictable[b] = None       # keep contents and key; reusable until evicted
+            else:
+                self._free.append(b)
+
+    @property
+    def num_free(self) -> int:
+        return len(self._free) + len(self._evictable)
+
+    @property
+    def num_cached(self) -> int:
+        return len(self._key_of)
+
+    # ---- sequences ------------------------------------------------------------
+    def match_prefix(self, tokens):
+        """Cached blocks holding the longest block-aligned prefix of tokens."""
+        out = []
+        for k in self._keys(tokens):
+            b = self._by_key.get(k)
+            if b is None:
+                break
+            out.append(b)
+        return out
+
+    def add_cached_sequence(self, seq, tokens):
+        """Register seq with its prompt tokens, reusing cached blocks for the longest cached prefix.
+
+        Returns (table, num_cached_tokens): the KV of positions < num_cached_tokens
+        is already in the pool; the caller prefills only the rest.  At least the
+        last prompt token is always left to compute (its query is needed).
+        """
+        if seq in self.tables:
+            raise KeyError(f"sequence {seq} exists")
+        tokens = list(tokens)
+        hits = self.match_prefix(tokens)
+        if hits and len(hits) * self.block_size >= len(tokens):
+            hits = hits[:-1]
+        need = -(-len(tokens) // self.block_size) - len(hits)
+        for b in hits:                       # take the hits first so allocation cannot evict them
+            if self.refcount[b] == 0:
+                del self._evictable[b]
+            self.refcount[b] += 1
+        if need > self.num_free:
+            for b in hits:
+                self._release(b)
+            raise OutOfBlocks(f"sequence of {len(tokens)} tokens needs {need} new blocks, {self.num_free} free")
+        self.tables[seq] = hits + [self._alloc() for _ in range(need)]
+        self.lens[seq] = len(tokens)
+        self.tokens[seq] = tokens
+        self.hits += len(hits)
+        return list(self.tables[seq]), len(hits) * self.block_size
+
+    def commit(self, seq):
+        """Make seq's full blocks findable (call once their KV has been written)."""
+        table = self.tables[seq]
+        for i, k in enumerate(self._keys(self.tokens[seq][: self.lens[seq]])):
+            b = table[i]
+            if k in self._by_key or b in self._key_of:
+                continue                     # already cached (shared) or registered under its key
+            self._by_key[k] = b
+            self._key_of[b] = k
+
+    def append_tokens(self, seq, n: int = 1, token_ids=None):
+        if token_ids is not None:
+            if len(token_ids) != n:
+                raise ValueError("one token id per appended token")
+            self.tokens.setdefault(seq, []).extend(int(t) for t in token_ids)
+        return super().append_tokens(seq, n)
+
+    def fork(self, parent, child):
+        table = super().fork(parent, child)
+        self.tokens[child] = list(self.tokens.get(parent, []))
+        return table
+
+    def compact(self, seq, num_kept: int):
+        # kept tokens are a new sequence of positions: the prefix keys no longer describe them
+        self.tokens.pop(seq, None)
+        return super().compact(seq, num_kept)
+
+    def free(self, seq) -> None:
+        super().free(seq)
+        self.tokens.pop(seq, None)
+
+    def stats(self) -> dict:
+        out = super().stats()
+        out.update(cached_blocks=self.num_cached, evictable_blocks=len(self._evictable),
+                   prefix_hits=self.hits, evictions=self.evictions)
+        return out
