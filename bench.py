@@ -264,6 +264,53 @@ def bench_prefill(args, dev, stream):
         "tokens_per_s": round(w.num_seqs * w.chunk / (t * 1e-3), 1)}), flush=True)
 
 
+HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args, dev, stream):
+    """Block swap over the host link: 4096 blocks of the Llama-3-8B layer shape (8 KV heads, head_dim 128,
+    bf16: 64 KiB per block, 256 MiB in all) from scattered pool blocks to a pinned host arena and back."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_283_amd import ops
+
+    n, nb, hkv, d = 4096, 8192, 8, 128
+    pools = ops.allocate_pools(nb, hkv, d, torch.bfloat16, dev, fill_byte=0x3C)
+    arena = ops.allocate_host_arena(n, hkv, d, torch.bfloat16)
+    rng = np.random.default_rng(2838)
+    blocks = rng.permutation(nb)[:n].astype(np.int32)
+    pairs = torch.from_numpy(np.stack([blocks, np.arange(n, dtype=np.int32)], 1)).to(dev)
+    out_call = ops.kv_swap(pools, arena, pairs, True, stream=stream, prepare=True)
+    in_call = ops.kv_swap(pools, arena, pairs, False, stream=stream, prepare=True)
+    for _ in range(args.warmup):
+        out_call()
+        in_call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for ev in evs:
+        ev[0].record(stream)
+        out_call()
+        ev[1].record(stream)
+        in_call()
+        ev[2].record(stream)
+    torch.cuda.synchronize()
+    t_out = float(np.median([ev[0].elapsed_time(ev[1]) for ev in evs]))
+    t_in = float(np.median([ev[1].elapsed_time(ev[2]) for ev in evs]))
+    nbytes = n * hkv * 16 * d * 2 * 2
+    out_gbs, in_gbs = nbytes / (t_out * 1e-3) / 1e9, nbytes / (t_in * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "KV block swap over the host link: GB/s out (pool -> pinned host) and in",
+        "value": round(2 * nbytes / ((t_out + t_in) * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t_out + t_in, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "swap-4096-blocks-llama3-layer", "blocks": n, "bytes_each_way": nbytes},
+        "roofline": {"bound": "link", "achieved": round(max(out_gbs, in_gbs), 2), "peak": HOST_LINK_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(max(out_gbs, in_gbs) / HOST_LINK_PEAK_GBS, 4), "traffic": None},
+        "swap_out_gbs": round(out_gbs, 2), "swap_in_gbs": round(in_gbs, 2),
+        "swap_out_ms": round(t_out, 4), "swap_in_ms": round(t_in, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,9 +324,10 @@ def main():
     ap.add_argument("--probe-only", action="store_true", help="run only the HBM read/copy probes")
     ap.add_argument("--contiguous-blocks", action="store_true", help="hand out physical blocks in order "
                     "instead of the shuffled placement (comparison only)")
-    ap.add_argument("--op", default="decode", choices=("decode", "evict", "prefill"),
+    ap.add_argument("--op", default="decode", choices=("decode", "evict", "prefill", "swap"),
                     help="decode: the decode step (default); evict: H2O keep-set + compaction on the h2o "
-                         "workload; prefill: causal multi-query attention on the prefill workload")
+                         "workload; prefill: causal multi-query attention on the prefill workload; swap: "
+                         "4096 blocks to pinned host memory and back")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -332,6 +380,9 @@ def main():
         return
     if args.op == "prefill":
         bench_prefill(args, dev, stream)
+        return
+    if args.op == "swap":
+        bench_swap(args, dev, stream)
         return
 
     # ---- workload: pools filled through the library's own write path (untimed prefill)

@@ -233,6 +233,30 @@ int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype,
                        int head_dim, int block_size, float scale, void* stream);
 
 /*
+ * kv_swap -- move whole blocks between the pool and a pinned host arena ([PA]
+ * "三大运行时组件": the block allocator can swap blocks out to CPU RAM; [SO] 4.5
+ * "CPU Offloading": inactive requests' KV waits in CPU memory and comes back
+ * when needed).
+ *
+ * For each pair {block, slot} of block_slot_pairs: to_host = 1 copies pool
+ * block `block` (K and V tiles of every KV head, and for FP8/INT8 both scale
+ * rows) to host slot `slot`; to_host = 0 copies slot `slot` back into pool
+ * block `block`.  The host arena mirrors the pool layout:
+ *   host_k, host_v             [host_slots][num_kv_heads][tile] (same tile bytes as the pool)
+ *   host_k_scale, host_v_scale float [host_slots][num_kv_heads][16] (FP8/INT8 only)
+ * and must be pinned, device-accessible memory (hipHostMalloc, or torch
+ * pin_memory), which the kernel reads or writes directly.
+ *   block_slot_pairs  int32 [num_pairs][2], device memory
+ * A pair whose block or slot is out of range is skipped.  Pairs that name the
+ * same block or slot twice race.  The copy is ordered on `stream`: host code
+ * may touch the arena only after synchronising with it.
+ */
+int kv_swap(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+            void* host_k, void* host_v, float* host_k_scale, float* host_v_scale,
+            const int32_t* block_slot_pairs, int num_pairs, int num_blocks, int host_slots,
+            int num_kv_heads, int head_dim, int block_size, int to_host, void* stream);
+
+/*
  * kv_block_copy -- whole-block copies, the data half of copy-on-write.
  *
  * [PA] "三大运行时组件" and its copy_on_write snippet: before a sequence writes

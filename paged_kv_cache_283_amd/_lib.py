@@ -37,6 +37,7 @@ SIGNATURES = {
     "paged_kv_append": (_I, [_P, _P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
     "paged_prefill_attn": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                 _I, _I, _F, _P]),
+    "kv_swap": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "kv_keep_select": (_I, [_P, _I, _P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P]),
     "kv_compact": (_I, [_P, _P, _P, _P, _I, _P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _P]),
     "pkv_timing_begin": (_I, [_I]),

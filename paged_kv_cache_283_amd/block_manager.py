@@ -30,6 +30,28 @@ class OutOfBlocks(RuntimeError):
     """The shared pool has no free block left."""
 
 
+class HostBlockStore:
+    """Slots of a pinned host arena that hold swapped-out blocks (one slot per block)."""
+
+    def __init__(self, num_slots: int):
+        if num_slots < 1:
+            raise ValueError("num_slots must be >= 1")
+        self.num_slots = num_slots
+        self._free = deque(range(num_slots))
+
+    @property
+    def num_free(self) -> int:
+        return len(self._free)
+
+    def alloc(self, n: int):
+        if n > len(self._free):
+            raise OutOfBlocks(f"host arena: {n} slots needed, {len(self._free)} free")
+        return [self._free.popleft() for _ in range(n)]
+
+    def release(self, slots) -> None:
+        self._free.extend(slots)
+
+
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
         if block_size != BLOCK_SIZE:
@@ -42,6 +64,7 @@ class BlockManager:
         self._free = deque(range(num_blocks))
         self.tables = {}          # seq id -> list of physical block ids
         self.lens = {}            # seq id -> tokens held
+        self.swapped = {}         # seq id -> (host slots, tokens held) while swapped out
         self.cow_copies = 0
 
     # ---- pool ---------------------------------------------------------------
@@ -143,6 +166,40 @@ class BlockManager:
         self.tables[seq] = new
         self.lens[seq] = num_kept
         return list(old), list(new)
+
+    def swap_out(self, seq, store: HostBlockStore):
+        """Move seq out of the pool ([PA] 三大运行时组件: blocks can be swapped out to CPU RAM).
+
+        Returns pairs (block, host slot) for kv_swap(..., to_host=True).  The
+        pool blocks are released here (a shared block only loses this
+        reference); device work that writes them must be enqueued after the
+        swap on the same stream.
+        """
+        table = self.tables[seq]
+        slots = store.alloc(len(table))
+        pairs = list(zip(table, slots))
+        for b in table:
+            self._release(b)
+        del self.tables[seq]
+        self.swapped[seq] = (slots, self.lens.pop(seq))
+        return pairs
+
+    def swap_in(self, seq, store: HostBlockStore):
+        """Bring a swapped-out seq back into fresh blocks.
+
+        Returns pairs (block, host slot) for kv_swap(..., to_host=False); the
+        host slots return to the store (later swaps that reuse them are
+        ordered after this one on the same stream).
+        """
+        slots, n_tok = self.swapped[seq]
+        if len(slots) > self.num_free:
+            raise OutOfBlocks(f"swap-in of {len(slots)} blocks, {self.num_free} free")
+        del self.swapped[seq]
+        table = [self._alloc() for _ in slots]
+        self.tables[seq] = table
+        self.lens[seq] = n_tok
+        store.release(slots)
+        return list(zip(table, slots))
 
     def free(self, seq) -> None:
         for b in self.tables.pop(seq):

@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["decode_attn.hip", "prefill_attn.hip", "kv_write.hip", "kv_compact.hip", "keep_select.hip", "probe.hip"]
+HIP_SOURCES = ["decode_attn.hip", "prefill_attn.hip", "kv_write.hip", "kv_compact.hip", "kv_swap.hip", "keep_select.hip",
+               "probe.hip"]
 HOST_SOURCES = ["api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]

@@ -303,6 +303,28 @@ int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype, con
                        "paged_prefill_attn");
 }
 
+int kv_swap(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype, void* host_k, void* host_v,
+            float* host_k_scale, float* host_v_scale, const int32_t* block_slot_pairs, int num_pairs, int num_blocks,
+            int host_slots, int num_kv_heads, int head_dim, int block_size, int to_host, void* stream) {
+  if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
+  if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
+  if (to_host != 0 && to_host != 1) return fail(PKV_EINVAL, "to_host %d is neither 0 nor 1", to_host);
+  if (num_pairs < 0 || num_pairs > (1 << 24)) return fail(PKV_EINVAL, "num_pairs %d outside [0, 2^24]", num_pairs);
+  if (num_blocks < 1 || host_slots < 1 || num_kv_heads < 1)
+    return fail(PKV_EINVAL, "num_blocks, host_slots and num_kv_heads must be >= 1");
+  if (num_pairs == 0) return ok();
+  if (!k_pool || !v_pool || !host_k || !host_v || !block_slot_pairs) return fail(PKV_EINVAL, "NULL array argument");
+  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale || !host_k_scale || !host_v_scale))
+    return fail(PKV_EINVAL, "FP8/INT8 pools need device and host scales");
+  if ((uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16 || (uintptr_t)host_k % 16 || (uintptr_t)host_v % 16)
+    return fail(PKV_EINVAL, "pools and host arenas must be 16-byte aligned");
+  return device_status(pkv::launch_kv_swap(k_pool, v_pool, k_scale, v_scale, kv_dtype, host_k, host_v, host_k_scale,
+                                           host_v_scale, block_slot_pairs, num_pairs, num_blocks, host_slots,
+                                           num_kv_heads, head_dim, to_host, (hipStream_t)stream),
+                       "kv_swap");
+}
+
 int kv_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype, const int32_t* block_pairs,
                   int num_pairs, int num_blocks, int num_kv_heads, int head_dim, int block_size, void* stream) {
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);

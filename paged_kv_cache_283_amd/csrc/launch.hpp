@@ -91,6 +91,11 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, int src_dtype,
                             const int32_t* lens, int num_seqs, int num_blocks, int num_kv_heads, int head_dim,
                             hipStream_t stream);
 
+hipError_t launch_kv_swap(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype, void* host_k,
+                          void* host_v, float* host_k_scale, float* host_v_scale, const int32_t* pairs, int num_pairs,
+                          int num_blocks, int host_slots, int num_kv_heads, int head_dim, int to_host,
+                          hipStream_t stream);
+
 hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
                              const int32_t* pairs, int num_pairs, int num_blocks, int num_kv_heads,
                              int head_dim, hipStream_t stream);

@@ -274,6 +274,40 @@ def paged_prefill_attn(out, q, k_pool, v_pool, block_tables, context_lens, query
     return _issue("paged_prefill_attn", args, prepare)
 
 
+def _host_ptr(t):
+    if t is None:
+        return None
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("host arenas must be pinned CPU tensors (pin_memory=True)")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def allocate_host_arena(num_slots, num_kv_heads, head_dim, kv_dtype=torch.bfloat16):
+    """Pinned host (k, v, k_scale, v_scale) mirroring the pool layout with num_slots blocks."""
+    k = torch.empty(k_pool_shape(num_slots, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, pin_memory=True)
+    v = torch.empty(v_pool_shape(num_slots, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, pin_memory=True)
+    ks = vs = None
+    if quantised(kv_dtype):
+        ks = torch.empty((num_slots, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, pin_memory=True)
+        vs = torch.empty((num_slots, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, pin_memory=True)
+    return k, v, ks, vs
+
+
+def kv_swap(pools, arena, block_slot_pairs, to_host, stream=None, prepare=False):
+    """Copy pool blocks to host slots (to_host=True) or back, for int32 pairs [n][2] {block, slot}."""
+    k, v, ks, vs = pools
+    hk, hv, hks, hvs = arena
+    _need(block_slot_pairs, torch.int32, "block_slot_pairs")
+    if hk.dtype != k.dtype or tuple(hk.shape[1:]) != tuple(k.shape[1:]) or tuple(hv.shape[1:]) != tuple(v.shape[1:]):
+        raise ValueError("the host arena must mirror the pool layout")
+    nb, hkv = k.shape[0], k.shape[1]
+    d = k.shape[2] * k.shape[4]
+    args = (_ptr(k), _ptr(v), _ptr(ks), _ptr(vs), kv_code(k.dtype), _host_ptr(hk), _host_ptr(hv), _host_ptr(hks),
+            _host_ptr(hvs), _ptr(block_slot_pairs), block_slot_pairs.shape[0], nb, hk.shape[0], hkv, d, BLOCK_SIZE,
+            1 if to_host else 0, _stream(stream))
+    return _issue("kv_swap", args, prepare)
+
+
 def kv_block_copy(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None, stream=None):
     """Copy whole blocks per int32 [n][2] {src, dst} pair (the data half of copy-on-write)."""
     _need(block_pairs, torch.int32, "block_pairs")

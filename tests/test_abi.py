@@ -157,3 +157,16 @@ def test_append_validation():
     assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, -1, 64, 8, 128, 16, None) == _lib.EINVAL
     assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, FAKE, 8, FAKE, 0, 64, 8, 128, 16, None) == _lib.OK
     assert ap(FAKE, FAKE, 1, FAKE, FAKE, None, None, 1, None, 8, FAKE, 4, 64, 8, 128, 16, None) == _lib.EINVAL
+
+
+def test_swap_validation():
+    lib = _lib.load()
+    sw = lib.kv_swap
+    #        k     v    ks    vs   dt  hk    hv    hks   hvs  pairs n  NB slots H  D   bs dir
+    assert sw(FAKE, FAKE, None, None, 1, FAKE, FAKE, None, None, FAKE, 4, 64, 8, 8, 128, 8, 1, None) == _lib.EUNSUPPORTED
+    assert sw(FAKE, FAKE, None, None, 1, FAKE, FAKE, None, None, FAKE, 4, 64, 8, 8, 128, 16, 2, None) == _lib.EINVAL
+    assert sw(FAKE, FAKE, None, None, 3, FAKE, FAKE, None, None, FAKE, 4, 64, 8, 8, 128, 16, 1, None) == _lib.EINVAL
+    assert sw(FAKE, FAKE, None, None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 8, 8, 128, 16, 1, None) == _lib.EINVAL
+    assert sw(FAKE, FAKE, None, None, 1, FAKE, FAKE, None, None, FAKE, 4, 64, 0, 8, 128, 16, 1, None) == _lib.EINVAL
+    assert sw(FAKE, FAKE, None, None, 1, FAKE, FAKE, None, None, FAKE, 0, 64, 8, 8, 128, 16, 1, None) == _lib.OK
+    assert sw(FAKE, FAKE, None, None, 1, None, FAKE, None, None, FAKE, 4, 64, 8, 8, 128, 16, 0, None) == _lib.EINVAL

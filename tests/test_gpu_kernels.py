@@ -676,3 +676,41 @@ def test_prefix_cache_hit_prefills_only_the_suffix():
     err = max(float(np.max(np.abs(H.to_f64(out[0:1]) - ref_a))), float(np.max(np.abs(H.to_f64(out[1:301]) - ref_b))))
     print(f"prefix cache: b reused {cached_b} tokens, max abs err {err:.3e}")
     assert err <= 2e-3
+
+
+# ---------------------------------------------------------------------------- swap to host
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
+def test_swap_out_and_back_into_other_blocks(kv):
+    """A sequence's blocks go to pinned host slots byte for byte, its pool blocks are overwritten,
+    and after swapping back into different blocks its attention is bit-identical."""
+    w = dataclasses.replace(_case_workload(kv, "bf16", 128, 32, 8, 131, lens=(100, 300, 50)), extra_blocks=24)
+    case = H.Case(w)
+    lay = case.lay
+    before = case.attend()
+    pools = case.pools
+    arena = ops.allocate_host_arena(32, 8, 128, pools[0].dtype)
+    nblk = -(-300 // 16)
+    src = lay.tables[1, :nblk].astype(np.int32)
+    slots = np.arange(5, 5 + nblk, dtype=np.int32)[::-1].copy()
+    ops.kv_swap(pools, arena, torch.from_numpy(np.stack([src, slots], 1)).cuda(), to_host=True)
+    torch.cuda.synchronize()
+    for p, a in zip(pools, arena):
+        if p is not None:
+            assert torch.equal(a[torch.from_numpy(slots).long()].view(torch.uint8),
+                               p[torch.from_numpy(src).long()].cpu().view(torch.uint8))
+    for p in pools:                                   # the pool blocks are reused by someone else
+        if p is not None:
+            p.view(torch.uint8)[torch.from_numpy(src).long()] = 0xFF
+    dst = np.asarray(lay.unused_blocks[:nblk], dtype=np.int32)
+    ops.kv_swap(pools, arena, torch.from_numpy(np.stack([dst, slots], 1)).cuda(), to_host=False)
+    tables = case.tables.clone()
+    tables[1, :nblk] = torch.from_numpy(dst).cuda()
+    after = torch.empty_like(before)
+    k, v, ks, vs = pools
+    ops.paged_decode_attn(after, case.q, k, v, tables, case.lens, lay.max_len, k_scale=ks, v_scale=vs)
+    assert torch.equal(before, after)
+    # out-of-range pairs are skipped
+    ops.kv_swap(pools, arena, torch.tensor([[-1, 0], [0, 99], [lay.num_blocks, 1]], dtype=torch.int32).cuda(),
+                to_host=True)
+    torch.cuda.synchronize()
