@@ -30,7 +30,7 @@ METRIC = "paged decode attn: KV GB/s read (% of HBM peak) and decode tokens/s, 1
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ("paged_kv_cache_283_amd/csrc/decode_attn.hip", "paged_kv_cache_283_amd/csrc/device_common.hpp",
                   "paged_kv_cache_283_amd/csrc/geometry.hpp", "paged_kv_cache_283_amd/csrc/launch.hpp",
-                  "paged_kv_cache_283_amd/build.py")
+                  "paged_kv_cache_283_amd/csrc/mfma_ops.hpp", "paged_kv_cache_283_amd/build.py")
 WORKLOAD_NAMES = {"llama3": "llama3-8b-layer-decode", "fp8long": "fp8-kv-32k-shared-prefix",
                   "int8long": "int8-kv-32k",
                   "streaming": "streamingllm-131k-sinks4-window4096", "h2o": "h2o-8k-mass",
