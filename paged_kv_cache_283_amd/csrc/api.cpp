@@ -299,7 +299,7 @@ int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype, con
   a.num_kv_heads = num_kv_heads;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.tiles_per_pair = (int)tiles;
-  return device_status(pkv::launch_prefill_attn(a, kv_dtype, q_dtype, head_dim, (hipStream_t)stream),
+  return device_status(pkv::launch_prefill_attn(a, kv_dtype, q_dtype, head_dim, max_query_len, (hipStream_t)stream),
                        "paged_prefill_attn");
 }
 

@@ -59,10 +59,11 @@ struct PrefillArgs {
   int max_context_len;
   int num_seqs, num_blocks, num_q_heads, num_kv_heads;
   float scale_log2;
-  int tiles_per_pair;           // workgroups per (sequence, KV head): ceil(max_query_len / (4 * 16 / G))
+  int tiles_per_pair;           // workgroups per (sequence, KV head), set by the launcher
 };
 
-hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim, hipStream_t stream);
+hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim, int max_query_len,
+                               hipStream_t stream);
 
 struct WorkspaceLayout {
   size_t acc_off, ml_off, hdr_off, prefix_off, stash_off, fin_off, total;

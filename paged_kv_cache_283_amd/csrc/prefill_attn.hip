@@ -15,11 +15,14 @@
 // used as (query token, head) pairs -- 16/G tokens x G heads per wave -- so a
 // wave computes S = K q^T for 16 query rows with one 16x16x32 MFMA per 32 head
 // dims and PV with the probabilities straight from the QK accumulator.  Each
-// column carries its own causal limit (a per-lane mask on the logits).  A
-// workgroup is 4 waves = 4 * 16/G consecutive query tokens of one (sequence,
-// KV head); its waves walk the same blocks, so the tiles come from HBM once
-// and from the caches for the other waves.  Work is split by query token only:
-// every wave covers the whole causal range of its tokens.
+// column carries its own causal limit (a per-lane mask on the logits).  For
+// long chunks a wave carries several such 16-column sets (PKV_PREFILL_SETS):
+// each K/V tile it loads feeds one MFMA per set, so the tiles pulled from L2
+// per query token drop by that factor.  A workgroup is 4 waves of consecutive
+// query tokens of one (sequence, KV head); its waves walk the same blocks, so
+// the tiles come from HBM once and from the caches for the other waves.  Work
+// is split by query token only: every wave covers the whole causal range of
+// its tokens.
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_ops.hpp"
@@ -34,7 +37,18 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 
 }  // namespace
 
-template <int KVT, int QT, int D>
+#ifndef PKV_PREFILL_SETS
+#define PKV_PREFILL_SETS 2                // 16-column query sets per wave for long chunks
+#endif
+#ifndef PKV_PREFILL_PIPE
+#define PKV_PREFILL_PIPE 2                // K/V register buffers per wave (2 or 3); 2 keeps two waves per SIMD
+#endif
+
+namespace {
+
+}  // namespace
+
+template <int KVT, int QT, int D, int CS>
 __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   using KT = KvType<KVT>;
   constexpr int EB = KT::kBytes;
@@ -52,7 +66,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   const int hq = a.num_q_heads;
   const int hkv = a.num_kv_heads;
   const int group = hq / hkv;
-  const int tpw = 16 / group;                    // query tokens per wave
+  const int tpw = 16 / group;                    // query tokens per column set
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
@@ -77,62 +91,72 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   const int q0 = a.query_start[s];
   const int n_q = a.query_start[s + 1] - q0;
   const int L = a.context_lens[s];
-  const int t0 = (tile * kPfWaves + wave) * tpw;   // first query token of this wave
+  const int t0 = (tile * kPfWaves + wave) * CS * tpw;   // first query token of this wave
   if (q0 < 0 || n_q < 1 || n_q > a.num_tokens - q0 || t0 >= n_q) return;   // rows outside q/out: skip
   const int prefix = L - n_q;
   const bool seq_ok = L >= n_q && L <= a.max_context_len && L <= a.table_stride * kBlockSize;
 
-  // ---- column c = (query token t0 + c / G, head kvh * G + c % G)
-  const int tok = t0 + c / group;
-  const bool col_ok = tok < n_q;
+  // ---- column c of set cs = (query token t0 + cs * tpw + c / G, head kvh * G + c % G)
   const int head = kvh * group + c % group;
-  const int pos = col_ok ? prefix + tok : -1;     // causal limit of the column (-1: no keys)
-  const size_t qrow = ((size_t)(q0 + (col_ok ? tok : 0)) * hq + head) * D;
-  uint32_t qhi[QW];
-  uint32_t qlo[QSPLIT ? QW : 1];
-  float qf[OP32 ? DPL : 1];
-  if constexpr (OP32) {
+  int tok[CS], pos[CS];
+  bool col_ok[CS];
+  uint32_t qhi[CS][QW];
+  uint32_t qlo[CS][QSPLIT ? QW : 1];
+  float qf[CS][OP32 ? DPL : 1];
 #pragma unroll
-    for (int st = 0; st < DPL; ++st) qf[st] = col_ok ? load_q_elem<QT>(a.q, qrow + qk_dim_f32(st, j)) : 0.f;
-  } else if constexpr (QSAME) {
-    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + qrow;
+  for (int cs = 0; cs < CS; ++cs) {
+    tok[cs] = t0 + cs * tpw + c / group;
+    col_ok[cs] = tok[cs] < n_q;
+    pos[cs] = col_ok[cs] ? prefix + tok[cs] : -1;    // causal limit of the column (-1: no keys)
+    const size_t qrow = ((size_t)(q0 + (col_ok[cs] ? tok[cs] : 0)) * hq + head) * D;
+    if constexpr (OP32) {
 #pragma unroll
-    for (int st = 0; st < QW / 4; ++st) {
-      const u32x4 v = col_ok ? *reinterpret_cast<const u32x4*>(qh + qk_dim16<KVT>(st, j)) : u32x4{0, 0, 0, 0};
-      qhi[4 * st + 0] = v[0]; qhi[4 * st + 1] = v[1]; qhi[4 * st + 2] = v[2]; qhi[4 * st + 3] = v[3];
-    }
-  } else {
+      for (int st = 0; st < DPL; ++st)
+        qf[cs][st] = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + qk_dim_f32(st, j)) : 0.f;
+    } else if constexpr (QSAME) {
+      const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + qrow;
 #pragma unroll
-    for (int st = 0; st < QW / 4; ++st) {
+      for (int st = 0; st < QW / 4; ++st) {
+        const u32x4 v = col_ok[cs] ? *reinterpret_cast<const u32x4*>(qh + qk_dim16<KVT>(st, j)) : u32x4{0, 0, 0, 0};
+        qhi[cs][4 * st + 0] = v[0]; qhi[cs][4 * st + 1] = v[1]; qhi[cs][4 * st + 2] = v[2]; qhi[cs][4 * st + 3] = v[3];
+      }
+    } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d0 = qk_dim16<KVT>(st, j) + 2 * w;
-        const float f0 = col_ok ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
-        const float f1 = col_ok ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
-        const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
-        const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
-        const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
-        qhi[4 * st + w] = h0 | (h1 << 16);
-        qlo[4 * st + w] = l0 | (l1 << 16);
+      for (int st = 0; st < QW / 4; ++st) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int d0 = qk_dim16<KVT>(st, j) + 2 * w;
+          const float f0 = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
+          const float f1 = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+          const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
+          const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
+          const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
+          qhi[cs][4 * st + w] = h0 | (h1 << 16);
+          qlo[cs][4 * st + w] = l0 | (l1 << 16);
+        }
       }
     }
   }
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 acc[NT];
+  float m_run[CS], l_run[CS];
+  f32x4 acc[CS][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cs = 0; cs < CS; ++cs) {
+    m_run[cs] = -INFINITY;
+    l_run[cs] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[cs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   bool bad = !seq_ok;
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
   const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
-  // Keys the wave needs: 0 .. prefix + last token of the wave; keys below
-  // prefix + t0 are visible to every column (no mask there).
-  const int t_last = min(t0 + tpw, n_q) - 1;
+  // Keys the wave needs: 0 .. prefix + its last token; keys below prefix + t0
+  // are visible to every column (no mask there).
+  const int t_last = min(t0 + CS * tpw, n_q) - 1;
   const int n_blocks = seq_ok ? (prefix + t_last) / kBlockSize + 1 : 0;
-  const int all_visible = prefix + t0;             // keys p < this are seen by all columns
+  const int all_visible = prefix + t0;
   int c0 = 0;
 
   struct Regs {
@@ -168,10 +192,16 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   auto compute = [&](Regs& r, int i) {
     bad |= !r.ok;
     const int blk0 = (c0 + i) * kBlockSize;
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+    // ---- S = K q^T for every column set, sharing the converted K operand
+    f32x4 sacc[CS];
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) sacc[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (OP32) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) sacc = mfma_f32_k4(__uint_as_float(r.k[e]), qf[e], sacc);
+      for (int e = 0; e < DPL; ++e) {
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) sacc[cs] = mfma_f32_k4(__uint_as_float(r.k[e]), qf[cs][e], sacc[cs]);
+      }
     } else {
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
@@ -182,27 +212,19 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         } else {
           av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
         }
-        sacc = mfma_k32<F16>(av, &qhi[4 * st], sacc);
-        if constexpr (QSPLIT) sacc = mfma_k32<F16>(av, &qlo[4 * st], sacc);
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) {
+          sacc[cs] = mfma_k32<F16>(av, &qhi[cs][4 * st], sacc[cs]);
+          if constexpr (QSPLIT) sacc[cs] = mfma_k32<F16>(av, &qlo[cs][4 * st], sacc[cs]);
+        }
       }
     }
-    // logits (base 2); keys past the column's position get -inf, keys past the
-    // context (the unused tail of the last block) also get V zeroed
+    // ---- keys past the context (the unused tail of the last block): V zeroed
     const bool full = blk0 + kBlockSize <= all_visible;
-    float x[4];
     bool in_ctx[4] = {true, true, true, true};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[e] = sacc[e] * a.scale_log2;
-      if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
-    }
     if (!full) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int p = blk0 + 4 * j + e;
-        in_ctx[e] = p < L;
-        x[e] = p <= pos ? x[e] : -INFINITY;
-      }
+      for (int e = 0; e < 4; ++e) in_ctx[e] = blk0 + 4 * j + e < L;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if constexpr (VW == 1) {
@@ -218,53 +240,70 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         }
       }
     }
-    const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-    const bool need = mb > m_run + kPfRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-      const float m_new = need ? mb : m_run;
-      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
+    // ---- per column set: causal mask, online softmax, probabilities as PV operands
+    uint32_t ph[CS][2], pl[CS][2];
+    float pvv[CS][4];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-      m_run = m_new;
+    for (int cs = 0; cs < CS; ++cs) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = sacc[cs][e] * a.scale_log2;
+        if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
+        if (!full) x[e] = blk0 + 4 * j + e <= pos[cs] ? x[e] : -INFINITY;
+      }
+      const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      const bool need = mb > m_run[cs] + kPfRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+        const float m_new = need ? mb : m_run[cs];
+        const float alpha = m_new == m_run[cs] ? 1.f : fast_exp2(m_run[cs] - m_new);
+        l_run[cs] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[cs][t] *= alpha;
+        m_run[cs] = m_new;
+      }
+      const float mref = m_run[cs] == -INFINITY ? 0.f : m_run[cs];
+      float pr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[e] - mref);
+      l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (is_quantised(KVT)) pvv[cs][e] = in_ctx[e] ? pr[e] * r.vs[e] : 0.f;
+        else pvv[cs][e] = pr[e];
+      }
+      if constexpr (!OP32) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const float f0 = pvv[cs][2 * w], f1 = pvv[cs][2 * w + 1];
+          uint32_t h0, h1, l0, l1;
+          if constexpr (F16) {
+            h0 = f32_to_f16_bits(f0);
+            h1 = f32_to_f16_bits(f1);
+            l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
+            l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
+          } else {
+            h0 = __float_as_uint(f0) >> 16;
+            h1 = __float_as_uint(f1) >> 16;
+            l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
+            l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
+          }
+          ph[cs][w] = h0 | (h1 << 16);
+          pl[cs][w] = l0 | (l1 << 16);
+        }
+      }
     }
-    const float mref = m_run == -INFINITY ? 0.f : m_run;
-    float pr[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[e] - mref);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    float pv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (is_quantised(KVT)) pv[e] = in_ctx[e] ? pr[e] * r.vs[e] : 0.f;
-      else pv[e] = pr[e];
-    }
+    // ---- O^T += V^T P^T per set, sharing the converted V operand
     if constexpr (OP32) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[t] = mfma_f32_k4(__uint_as_float(r.v[t][e]), pv[e], acc[t]);
+        for (int e = 0; e < 4; ++e) {
+#pragma unroll
+          for (int cs = 0; cs < CS; ++cs) acc[cs][t] = mfma_f32_k4(__uint_as_float(r.v[t][e]), pvv[cs][e], acc[cs][t]);
+        }
       }
     } else {
-      uint32_t ph[2], pl[2];
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
-        uint32_t h0, h1, l0, l1;
-        if constexpr (F16) {
-          h0 = f32_to_f16_bits(f0);
-          h1 = f32_to_f16_bits(f1);
-          l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
-          l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
-        } else {
-          h0 = __float_as_uint(f0) >> 16;
-          h1 = __float_as_uint(f1) >> 16;
-          l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
-          l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
-        }
-        ph[w] = h0 | (h1 << 16);
-        pl[w] = l0 | (l1 << 16);
-      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t v0, v1;
@@ -274,8 +313,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           v0 = r.v[t][0];
           v1 = r.v[t][1];
         }
-        acc[t] = mfma_k16<F16>(v0, v1, ph[0], ph[1], acc[t]);
-        acc[t] = mfma_k16<F16>(v0, v1, pl[0], pl[1], acc[t]);
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) {
+          acc[cs][t] = mfma_k16<F16>(v0, v1, ph[cs][0], ph[cs][1], acc[cs][t]);
+          acc[cs][t] = mfma_k16<F16>(v0, v1, pl[cs][0], pl[cs][1], acc[cs][t]);
+        }
       }
     }
   };
@@ -286,6 +328,20 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#if PKV_PREFILL_PIPE == 2
+    Regs ra, rb;
+    int i = 0;
+    if (n > 0) load(ra, 0);
+    for (; i + 2 < n; i += 2) {
+      load(rb, i + 1);
+      compute(ra, i);
+      load(ra, i + 2);
+      compute(rb, i + 1);
+    }
+    if (i + 1 < n) load(rb, i + 1);
+    if (i < n) compute(ra, i);
+    if (i + 1 < n) compute(rb, i + 1);
+#else
     Regs r0, r1, r2;
     int i = 0;
     if (n > 0) load(r0, 0);
@@ -304,51 +360,66 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     if (i + 1 < n) compute(r1, i + 1);
     if (i + 2 < n) compute(r2, i + 2);
     if (i + 3 < n) compute(r0, i + 3);
+#endif
     __builtin_amdgcn_wave_barrier();   // the next chunk rewrites this wave's s_tab
   }
 
-  l_run = row_sum4(l_run);
-  if (bad) l_run = __builtin_nanf("");
-  if (!col_ok) return;
-  const size_t orow = ((size_t)(q0 + tok) * hq + head) * D;
-  const float inv = 1.f / l_run;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int cs = 0; cs < CS; ++cs) {
+    float l = row_sum4(l_run[cs]);
+    if (bad) l = __builtin_nanf("");
+    if (!col_ok[cs]) continue;
+    const size_t orow = ((size_t)(q0 + tok[cs]) * hq + head) * D;
+    const float inv = 1.f / l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, acc[t][e] * inv);
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, acc[cs][t][e] * inv);
+    }
   }
 }
 
 namespace {
 
 template <int KVT, int QT>
-hipError_t prefill_d(const PrefillArgs& a, int d, hipStream_t st) {
+hipError_t prefill_d(PrefillArgs a, int d, int max_query_len, hipStream_t st) {
+  // Column sets per wave: PKV_PREFILL_SETS for chunks long enough to fill them, else one.
+  const int tpw = 16 / (a.num_q_heads / a.num_kv_heads);
+  const bool wide = max_query_len >= kPfWaves * tpw * PKV_PREFILL_SETS;
+  const int per_wg = kPfWaves * tpw * (wide ? PKV_PREFILL_SETS : 1);
+  a.tiles_per_pair = (max_query_len + per_wg - 1) / per_wg;
   const int pairs = a.num_seqs * a.num_kv_heads;
   const dim3 grid((unsigned)pairs * a.tiles_per_pair);
-  if (d == 64) hipLaunchKernelGGL((prefill_kernel<KVT, QT, 64>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((prefill_kernel<KVT, QT, 128>), grid, dim3(256), 0, st, a);
+  if (wide) {
+    if (d == 64) hipLaunchKernelGGL((prefill_kernel<KVT, QT, 64, PKV_PREFILL_SETS>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((prefill_kernel<KVT, QT, 128, PKV_PREFILL_SETS>), grid, dim3(256), 0, st, a);
+  } else {
+    if (d == 64) hipLaunchKernelGGL((prefill_kernel<KVT, QT, 64, 1>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((prefill_kernel<KVT, QT, 128, 1>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
 template <int KVT>
-hipError_t prefill_q(const PrefillArgs& a, int q_dtype, int d, hipStream_t st) {
+hipError_t prefill_q(const PrefillArgs& a, int q_dtype, int d, int mq, hipStream_t st) {
   switch (q_dtype) {
-    case DT_F32: return prefill_d<KVT, DT_F32>(a, d, st);
-    case DT_BF16: return prefill_d<KVT, DT_BF16>(a, d, st);
-    default: return prefill_d<KVT, DT_F16>(a, d, st);
+    case DT_F32: return prefill_d<KVT, DT_F32>(a, d, mq, st);
+    case DT_BF16: return prefill_d<KVT, DT_BF16>(a, d, mq, st);
+    default: return prefill_d<KVT, DT_F16>(a, d, mq, st);
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim, hipStream_t st) {
-  if (a.num_seqs == 0 || a.tiles_per_pair == 0) return hipSuccess;
+hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, int head_dim, int max_query_len,
+                               hipStream_t st) {
+  if (a.num_seqs == 0 || max_query_len < 1) return hipSuccess;
   switch (kv_dtype) {
-    case DT_F32: return prefill_q<DT_F32>(a, q_dtype, head_dim, st);
-    case DT_BF16: return prefill_q<DT_BF16>(a, q_dtype, head_dim, st);
-    case DT_F16: return prefill_q<DT_F16>(a, q_dtype, head_dim, st);
-    case DT_FP8: return prefill_q<DT_FP8>(a, q_dtype, head_dim, st);
-    default: return prefill_q<DT_INT8>(a, q_dtype, head_dim, st);
+    case DT_F32: return prefill_q<DT_F32>(a, q_dtype, head_dim, max_query_len, st);
+    case DT_BF16: return prefill_q<DT_BF16>(a, q_dtype, head_dim, max_query_len, st);
+    case DT_F16: return prefill_q<DT_F16>(a, q_dtype, head_dim, max_query_len, st);
+    case DT_FP8: return prefill_q<DT_FP8>(a, q_dtype, head_dim, max_query_len, st);
+    default: return prefill_q<DT_INT8>(a, q_dtype, head_dim, max_query_len, st);
   }
 }
 
