@@ -51,3 +51,10 @@ def quantize_per_token(x: np.ndarray):
 def dequantize_per_token(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     """codes [..., D] int8 and scales [...] float32 -> float64 values (exact products)."""
     return decode(codes) * np.asarray(scale, dtype=np.float64)[..., None]
+
+
+def quantize_per_channel(x: np.ndarray, channel_scale: np.ndarray) -> np.ndarray:
+    """Codes of x [..., Hkv, D] with static scales [Hkv, D]: encode(float32(x / scale)), the quotient
+    an IEEE single-precision division (values beyond the code range saturate to +-127)."""
+    q = (np.asarray(x, dtype=np.float32) / np.asarray(channel_scale, dtype=np.float32)).astype(np.float32)
+    return encode(q)

@@ -16,6 +16,8 @@ library documents):
   V pool  [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4] Y = 4 / bytes per element:
                                                                 2 for bf16/f16, 4 for fp8/int8, 1 for f32
   scales  [num_blocks][num_kv_heads][16] float32                 fp8 and int8 only, K and V separately
+  channel scales [num_kv_heads][head_dim] float32                fp8_ch and int8_ch: static, given by the
+                                                                caller, one per (KV head, channel)
 
 (K element (token o, dim d) of a block tile sits at chunk d // X, row o, lane
 d % X.  V element (token o, dim d), with t = d // 16, sits at index
@@ -23,7 +25,8 @@ d % X.  V element (token o, dim d), with t = d // 16, sits at index
 tokens of Y dims 16 apart.)
 
 Storage dtypes are held here as raw numpy arrays: "f32" float32, "bf16" uint16
-bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes, "int8" int8 codes.
+bit patterns, "f16" float16, "fp8" uint8 E4M3FN codes, "int8" int8 codes; "fp8_ch" and
+"int8_ch" hold the same codes scaled per channel instead of per token.
 """
 
 import numpy as np
@@ -31,13 +34,21 @@ import numpy as np
 from . import fp8, int8
 
 BLOCK_SIZE = 16
-DTYPES = ("f32", "bf16", "f16", "fp8", "int8")
-_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "fp8": np.uint8, "int8": np.int8}
+DTYPES = ("f32", "bf16", "f16", "fp8", "int8", "fp8_ch", "int8_ch")
+_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.float16, "fp8": np.uint8, "int8": np.int8,
+            "fp8_ch": np.uint8, "int8_ch": np.int8}
 _CODECS = {"fp8": fp8, "int8": int8}       # quantised storage: codes + one scale per (token, KV head)
+_CHANNEL = {"fp8_ch": fp8, "int8_ch": int8}  # codes + one static scale per (KV head, channel)
 
 
 def quantised(kv_dtype: str) -> bool:
+    """Codes with one scale per (token, KV head), stored beside them in the pool."""
     return kv_dtype in _CODECS
+
+
+def channel_scaled(kv_dtype: str) -> bool:
+    """Codes with static per-(KV head, channel) scales given by the caller."""
+    return kv_dtype in _CHANNEL
 
 
 def storage_dtype(kv_dtype: str):
@@ -59,9 +70,9 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         bits = a.astype(np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
-    if dtype == "fp8":
+    if dtype in ("fp8", "fp8_ch"):
         return fp8.decode(a)
-    if dtype == "int8":
+    if dtype in ("int8", "int8_ch"):
         return int8.decode(a)
     raise ValueError(dtype)
 
@@ -106,8 +117,10 @@ def _v_get(v_tile_o):
     return v_tile_o.transpose(0, 1, 3, 2).reshape(hkv, g * y * c)
 
 
-def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, fill=0):
-    """Allocate (k_pool, v_pool, k_scale, v_scale) in the documented layout; scales None unless fp8."""
+def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, fill=0, k_channel=None,
+              v_channel=None):
+    """Allocate (k_pool, v_pool, k_scale, v_scale) in the documented layout.  The scales are per-token
+    arrays for fp8/int8, the given per-channel arrays [Hkv][D] for fp8_ch/int8_ch, else None."""
     st = storage_dtype(kv_dtype)
     x = k_chunk(kv_dtype)
     y = v_chunk_dims(kv_dtype)
@@ -116,6 +129,11 @@ def new_pools(num_blocks: int, num_kv_heads: int, head_dim: int, kv_dtype: str, 
     if quantised(kv_dtype):
         ks = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
         vs = np.zeros((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=np.float32)
+    elif channel_scaled(kv_dtype):
+        if k_channel is None or v_channel is None:
+            raise ValueError("fp8_ch/int8_ch pools need k_channel and v_channel [Hkv][D]")
+        ks = np.asarray(k_channel, dtype=np.float32).reshape(num_kv_heads, head_dim)
+        vs = np.asarray(v_channel, dtype=np.float32).reshape(num_kv_heads, head_dim)
     else:
         ks = vs = None
     return k, v, ks, vs
@@ -127,27 +145,35 @@ def write_tokens(pools, kv_dtype: str, k_src, v_src, src_dtype: str, table_rows,
     k_src, v_src: [T][Hkv][D] raw source arrays in src_dtype.  Token t belongs
     to sequence seq_ids[t] at logical position positions[t].  For f32/bf16/f16
     pools the source dtype must equal the pool dtype and the bytes are stored
-    unchanged; for fp8 pools each (token, KV head) row is quantised with its own
-    scale (fp8.quantize_per_token).  Mutates pools in place.
+    unchanged; for fp8/int8 pools each (token, KV head) row is quantised with its
+    own scale (quantize_per_token); for fp8_ch/int8_ch pools each element is
+    divided by its channel's static scale and encoded (quantize_per_channel).
+    Mutates pools in place.
     """
     k_pool, v_pool, k_scale, v_scale = pools
     nb, hkv, nc, _, x = k_pool.shape
-    if quantised(kv_dtype):
-        if quantised(src_dtype):
+    if quantised(kv_dtype) or channel_scaled(kv_dtype):
+        if quantised(src_dtype) or channel_scaled(src_dtype):
             raise ValueError("fp8/int8 pools take f32/bf16/f16 sources")
+    if quantised(kv_dtype):
         codec = _CODECS[kv_dtype]
         kq, ks = codec.quantize_per_token(to_f64(k_src, src_dtype).astype(np.float32))
         vq, vs = codec.quantize_per_token(to_f64(v_src, src_dtype).astype(np.float32))
+    elif channel_scaled(kv_dtype):
+        codec = _CHANNEL[kv_dtype]
+        kq = codec.quantize_per_channel(to_f64(k_src, src_dtype).astype(np.float32), k_scale)
+        vq = codec.quantize_per_channel(to_f64(v_src, src_dtype).astype(np.float32), v_scale)
     elif src_dtype != kv_dtype:
         raise ValueError("a non-fp8 pool stores source bytes of its own dtype")
     for t, (s, p) in enumerate(zip(seq_ids, positions)):
         b = physical_block(table_rows[s], p, nb)
         o = p % BLOCK_SIZE
-        if quantised(kv_dtype):
+        if quantised(kv_dtype) or channel_scaled(kv_dtype):
             k_pool[b, :, :, o, :] = kq[t].reshape(hkv, nc, x)
             _v_put(v_pool[b, :, :, :, o // 4, :, o % 4], vq[t], kv_dtype)
-            k_scale[b, :, o] = ks[t]
-            v_scale[b, :, o] = vs[t]
+            if quantised(kv_dtype):
+                k_scale[b, :, o] = ks[t]
+                v_scale[b, :, o] = vs[t]
         else:
             k_pool[b, :, :, o, :] = np.asarray(k_src[t]).reshape(hkv, nc, x)
             _v_put(v_pool[b, :, :, :, o // 4, :, o % 4], v_src[t], kv_dtype)
@@ -172,6 +198,9 @@ def gather_logical(pools, kv_dtype: str, table_row, positions, num_blocks=None):
         if quantised(kv_dtype):
             k = k * k_scale[b, :, o].astype(np.float64)[:, None]
             v = v * v_scale[b, :, o].astype(np.float64)[:, None]
+        elif channel_scaled(kv_dtype):
+            k = k * k_scale.astype(np.float64)
+            v = v * v_scale.astype(np.float64)
         K[i], V[i] = k, v
     return K, V
 
@@ -184,9 +213,11 @@ def copy_blocks(pools, pairs):
     still reference, its contents go to a fresh private block.  Pairs apply in
     order.
     """
+    nb = pools[0].shape[0]
     for arr in pools:
-        if arr is None:
+        if arr is None or arr.ndim == 2:      # absent, or static per-channel scales (not per block)
             continue
+        assert arr.shape[0] == nb
         for src, dst in pairs:
             arr[dst] = arr[src]
 
@@ -207,13 +238,14 @@ def compact(pools, kv_dtype: str, src_table_row, keep_positions, dst_table_row, 
     src = [(physical_block(src_table_row, int(p), nb), int(p) % BLOCK_SIZE) for p in keep_positions]
     rows = []
     for b, o in src:
+        per_token = k_scale is not None and k_scale.ndim == 3
         rows.append((k_pool[b, :, :, o, :].copy(), v_pool[b, :, :, :, o // 4, :, o % 4].copy(),
-                     None if k_scale is None else k_scale[b, :, o].copy(),
-                     None if v_scale is None else v_scale[b, :, o].copy()))
+                     k_scale[b, :, o].copy() if per_token else None,
+                     v_scale[b, :, o].copy() if per_token else None))
     for i, (k, v, ks, vs) in enumerate(rows):
         b, o = physical_block(dst_table_row, i, nb), i % BLOCK_SIZE
         k_pool[b, :, :, o, :] = k
         v_pool[b, :, :, :, o // 4, :, o % 4] = v
-        if k_scale is not None:
+        if ks is not None:
             k_scale[b, :, o] = ks
             v_scale[b, :, o] = vs
