@@ -32,7 +32,7 @@ KERNEL_SOURCES = ("paged_kv_cache_283_amd/csrc/decode_attn.hip", "paged_kv_cache
                   "paged_kv_cache_283_amd/csrc/geometry.hpp", "paged_kv_cache_283_amd/csrc/launch.hpp",
                   "paged_kv_cache_283_amd/csrc/mfma_ops.hpp", "paged_kv_cache_283_amd/build.py")
 WORKLOAD_NAMES = {"llama3": "llama3-8b-layer-decode", "fp8long": "fp8-kv-32k-shared-prefix",
-                  "int8long": "int8-kv-32k",
+                  "int8long": "int8-kv-32k", "fp8chlong": "fp8-per-channel-kv-32k",
                   "streaming": "streamingllm-131k-sinks4-window4096", "h2o": "h2o-8k-mass",
                   "llama2": "llama2-70b-80-layer-decode", "tiny": "tiny-paged-decode"}
 
@@ -66,9 +66,13 @@ def read_traffic(workload):
         return None, None
 
 
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "int8": 1, "fp8_ch": 1, "int8_ch": 1}
+
+
 def kv_bytes_per_token(w):
-    eb = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
-    per = w.num_kv_heads * 2 * w.head_dim * eb
+    """K + V bytes of one token, all KV heads, with per-token scales (static per-channel scales are
+    read once per segment, not per token)."""
+    per = w.num_kv_heads * 2 * w.head_dim * ELEM_BYTES[w.kv_dtype]
     if w.kv_dtype in ("fp8", "int8"):
         per += w.num_kv_heads * 2 * 4
     return per
@@ -183,8 +187,7 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
     sel_ms = [ev[0].elapsed_time(ev[1]) for ev in evs]
     cmp_ms = [ev[1].elapsed_time(ev[2]) for ev in evs]
     kept = int(keep_count.sum().item())
-    eb = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "int8": 1}[w.kv_dtype]
-    tok_bytes = w.num_kv_heads * w.head_dim * eb * 2 + (w.num_kv_heads * 8 if w.kv_dtype in ("fp8", "int8") else 0)
+    tok_bytes = kv_bytes_per_token(w)
     moved = 2 * kept * tok_bytes                          # read + write of every kept token
     sel_bytes = int(lens.sum().item()) * 4 + w.num_seqs * w.budget * 4
     t_sel, t_cmp = float(np.median(sel_ms)), float(np.median(cmp_ms))

@@ -35,12 +35,19 @@
  *           chunks: Y = 4 / element bytes (2 for BF16/F16, 4 for FP8, 1 for F32);
  *           element (token o, dim d), t = d / 16, is at [t / Y][d % 16][o / 4][t % Y][o % 4]
  *           (each chunk: 4 consecutive tokens of Y dims that are 16 apart)
- *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 and PKV_INT8 only)
+ *   k_scale, v_scale  float [num_blocks][num_kv_heads][16]   (PKV_FP8_E4M3 and PKV_INT8: per token)
+ *                     float [num_kv_heads][head_dim]         (the _CHANNEL formats: per channel)
  * A token at logical position p of a sequence lives in physical block
  * table[p / 16] at offset p % 16 ([PA] "物理布局示意", [LC] block-table sketch);
  * its flat slot is block * 16 + offset.  With FP8 or INT8 the stored value is
  * decode(code) * scale, one scale per (token, KV head) for K and one for V
- * ([PA] "量化原理": INT8 or FP8 halve the KV bytes; per-token scaling).
+ * ([PA] "量化原理": INT8 or FP8 halve the KV bytes; per-token scaling).  The
+ * _CHANNEL formats store the same codes with one static scale per (KV head,
+ * channel) instead ([PA] "量化原理": per-channel scaling): the value of
+ * element (token, h, d) is decode(code) * scale[h][d].  The caller owns and
+ * fills these arrays (e.g. from calibration); scales must be positive and
+ * finite, and they live outside the pool: block copy, compaction and swap
+ * move codes only.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -65,7 +72,9 @@ typedef enum {
   PKV_BF16 = 1,
   PKV_F16 = 2,
   PKV_FP8_E4M3 = 3,      /* OCP E4M3FN: bias 7, max 448, no infinities, 0x7F/0xFF = NaN */
-  PKV_INT8 = 4           /* two's-complement int8 codes in [-127, 127] */
+  PKV_INT8 = 4,          /* two's-complement int8 codes in [-127, 127] */
+  PKV_FP8_E4M3_CHANNEL = 5,  /* E4M3FN codes, static per-(KV head, channel) scales */
+  PKV_INT8_CHANNEL = 6       /* int8 codes, static per-(KV head, channel) scales */
 } pkv_dtype;
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -114,11 +123,14 @@ int paged_token_slots(const int32_t* block_tables, int block_table_stride, int n
  * and for INT8 pools with
  *     scale = absmax / 127,  code = clamp(rint(x / scale), -127, 127)
  *                                 (fp32 division; nearest integer, ties to even)
- * and the scale is stored beside the codes.
+ * and the scale is stored beside the codes.  The _CHANNEL formats store
+ *     code  = E4M3FN(x / scale[h][d])  or  clamp(rint(x / scale[h][d]), -127, 127)
+ *                                 (fp32 division) and leave the scales alone.
  *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of src_dtype
  *   kv_dtype       PKV_F32/BF16/F16 require src_dtype == kv_dtype (bytes are copied);
- *                  PKV_FP8_E4M3 and PKV_INT8 take src_dtype F32, BF16 or F16 (finite values)
- *   k_scale, v_scale   required for FP8, ignored otherwise
+ *                  the 8-bit formats take src_dtype F32, BF16 or F16 (finite values)
+ *   k_scale, v_scale   required for the 8-bit formats (written for per-token
+ *                  formats, read for _CHANNEL ones), ignored otherwise
  *   slot_mapping   int64 [num_tokens]; a slot < 0 or >= num_blocks*16 skips the token
  * Two tokens with the same slot race (one of them wins).
  */
@@ -170,7 +182,8 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
  *
  *   out            [num_seqs][num_q_heads][head_dim] of out_dtype (F32/BF16/F16)
  *   q              [num_seqs][num_q_heads][head_dim] of q_dtype (F32/BF16/F16)
- *   kv_dtype       F32, BF16, F16, FP8_E4M3 or INT8 (then k_scale/v_scale are required)
+ *   kv_dtype       F32, BF16, F16, or an 8-bit format (then k_scale/v_scale are required;
+ *                  _CHANNEL scales are folded into q and the output, not applied per key)
  *   block_tables   int32 [num_seqs][block_table_stride], stride >= ceil(max_context_len/16)
  *   context_lens   int32 [num_seqs], 1 <= L <= max_context_len (host value)
  *   num_q_heads / num_kv_heads in 1..16; head_dim 64 or 128; block_size 16
@@ -239,11 +252,11 @@ int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype,
  * when needed).
  *
  * For each pair {block, slot} of block_slot_pairs: to_host = 1 copies pool
- * block `block` (K and V tiles of every KV head, and for FP8/INT8 both scale
- * rows) to host slot `slot`; to_host = 0 copies slot `slot` back into pool
+ * block `block` (K and V tiles of every KV head, and for the per-token FP8/INT8
+ * formats both scale rows) to host slot `slot`; to_host = 0 copies slot `slot` back into pool
  * block `block`.  The host arena mirrors the pool layout:
  *   host_k, host_v             [host_slots][num_kv_heads][tile] (same tile bytes as the pool)
- *   host_k_scale, host_v_scale float [host_slots][num_kv_heads][16] (FP8/INT8 only)
+ *   host_k_scale, host_v_scale float [host_slots][num_kv_heads][16] (per-token FP8/INT8 only)
  * and must be pinned, device-accessible memory (hipHostMalloc, or torch
  * pin_memory), which the kernel reads or writes directly.
  *   block_slot_pairs  int32 [num_pairs][2], device memory
@@ -262,7 +275,7 @@ int kv_swap(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_d
  * [PA] "三大运行时组件" and its copy_on_write snippet: before a sequence writes
  * into a physical block that other sequences still share (refcount > 1), the
  * block is copied to a private one.  Refcounts and table edits are host-side;
- * this call copies K, V and (FP8) both scale tiles of every KV head.
+ * this call copies K, V and (per-token FP8/INT8) both scale tiles of every KV head.
  *   block_pairs   int32 [num_pairs][2] = {src, dst}; a pair with an index outside
  *                 [0, num_blocks) or src == dst is skipped.  Pairs run concurrently:
  *                 a dst that is also another pair's src or dst races.
@@ -329,7 +342,7 @@ int kv_keep_select(const float* scores, int scores_stride, const int32_t* kv_len
  * the kept indices; [LC] StreamingKVCache drops the middle of the cache).
  *
  * For sequence s and i < n = keep_count[s]: the token at logical position
- * keep_idx[s][i] of src_tables[s] is copied -- K, V and, for FP8, both scales,
+ * keep_idx[s][i] of src_tables[s] is copied -- K, V and, for per-token FP8/INT8, both scales,
  * all KV heads -- to logical position i of dst_tables[s].  The sequence then
  * holds n tokens in ceil(n / 16) destination blocks; the host releases the
  * source blocks (BlockManager.compact).

@@ -14,7 +14,7 @@ STATUS_NAMES = {OK: "PKV_OK", EINVAL: "PKV_EINVAL", EUNSUPPORTED: "PKV_EUNSUPPOR
                 EWORKSPACE: "PKV_EWORKSPACE", EDEVICE: "PKV_EDEVICE"}
 
 # pkv_dtype
-F32, BF16, F16, FP8_E4M3, INT8 = range(5)
+F32, BF16, F16, FP8_E4M3, INT8, FP8_E4M3_CHANNEL, INT8_CHANNEL = range(7)
 CAND_REST, CAND_ALL = range(2)
 
 _P = ctypes.c_void_p

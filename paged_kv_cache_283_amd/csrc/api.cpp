@@ -39,8 +39,13 @@ int device_status(hipError_t e, const char* what) {
   return fail(PKV_EDEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-bool valid_kv_dtype(int d) { return d >= PKV_F32 && d <= PKV_INT8; }
+bool valid_kv_dtype(int d) { return d >= PKV_F32 && d <= PKV_INT8_CHANNEL; }
+// Per-token scales stored per block.
 bool quantised_kv(int d) { return d == PKV_FP8_E4M3 || d == PKV_INT8; }
+// Static per-(KV head, channel) scales.
+bool channel_kv(int d) { return d == PKV_FP8_E4M3_CHANNEL || d == PKV_INT8_CHANNEL; }
+// 8-bit codes of either kind: any float source is quantised.
+bool code8_kv(int d) { return quantised_kv(d) || channel_kv(d); }
 bool valid_float_dtype(int d) { return d >= PKV_F32 && d <= PKV_F16; }
 
 struct Timing {
@@ -112,7 +117,7 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
   if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
   if (!valid_float_dtype(src_dtype)) return fail(PKV_EINVAL, "src_dtype %d", src_dtype);
-  if (!quantised_kv(kv_dtype) && src_dtype != kv_dtype)
+  if (!code8_kv(kv_dtype) && src_dtype != kv_dtype)
     return fail(PKV_EUNSUPPORTED, "a non-quantised pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
   if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
   if (num_kv_heads < 1) return fail(PKV_EINVAL, "num_kv_heads %d < 1", num_kv_heads);
@@ -121,7 +126,7 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_
     return fail(PKV_EINVAL, "num_tokens * num_kv_heads too large");
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return fail(PKV_EINVAL, "NULL array argument");
-  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
+  if (code8_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
   return device_status(pkv::launch_kv_write(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                             slot_mapping, num_tokens, num_blocks, num_kv_heads, head_dim,
                                             (hipStream_t)stream),
@@ -136,7 +141,7 @@ int paged_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "head_dim %d (built: 64, 128)", head_dim);
   if (!valid_kv_dtype(kv_dtype)) return fail(PKV_EINVAL, "kv_dtype %d", kv_dtype);
   if (!valid_float_dtype(src_dtype)) return fail(PKV_EINVAL, "src_dtype %d", src_dtype);
-  if (!quantised_kv(kv_dtype) && src_dtype != kv_dtype)
+  if (!code8_kv(kv_dtype) && src_dtype != kv_dtype)
     return fail(PKV_EUNSUPPORTED, "a non-quantised pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
   if (num_kv_heads < 1) return fail(PKV_EINVAL, "num_kv_heads %d < 1", num_kv_heads);
@@ -147,7 +152,7 @@ int paged_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k
   if (num_seqs == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "NULL array argument");
-  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
+  if (code8_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
   return device_status(pkv::launch_kv_append(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                              block_tables, block_table_stride, context_lens, num_seqs, num_blocks,
                                              num_kv_heads, head_dim, (hipStream_t)stream),
@@ -191,7 +196,7 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
   if (num_seqs == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "NULL array argument");
-  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
+  if (code8_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
   const pkv::WorkspaceLayout lay = pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len,
                                                               num_sinks, window, attn_mass != nullptr);
   if (lay.p_max > 65535)
@@ -275,7 +280,7 @@ int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype, con
   if (num_seqs == 0 || num_tokens == 0) return ok();
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return fail(PKV_EINVAL, "NULL array argument");
-  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
+  if (code8_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
   if ((uintptr_t)q % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16 ||
       (k_scale && (uintptr_t)k_scale % 16) || (v_scale && (uintptr_t)v_scale % 16))
     return fail(PKV_EINVAL, "q, pools and scales must be 16-byte aligned");
@@ -334,7 +339,8 @@ int kv_block_copy(void* k_pool, void* v_pool, float* k_scale, float* v_scale, in
   if (num_blocks < 1 || num_kv_heads < 1) return fail(PKV_EINVAL, "num_blocks and num_kv_heads must be >= 1");
   if (num_pairs == 0) return ok();
   if (!k_pool || !v_pool || !block_pairs) return fail(PKV_EINVAL, "NULL array argument");
-  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
+  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_EINVAL, "FP8/INT8 pools with per-token scales need k_scale and v_scale");
   if ((uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
   return device_status(pkv::launch_block_copy(k_pool, v_pool, k_scale, v_scale, kv_dtype, block_pairs, num_pairs,
                                               num_blocks, num_kv_heads, head_dim, (hipStream_t)stream),
@@ -395,7 +401,8 @@ int kv_compact(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int k
   if (num_seqs == 0 || keep_stride == 0) return ok();
   if (!k_pool || !v_pool || !src_tables || !dst_tables || !keep_idx || !keep_count)
     return fail(PKV_EINVAL, "NULL array argument");
-  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
+  if (quantised_kv(kv_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_EINVAL, "FP8/INT8 pools with per-token scales need k_scale and v_scale");
   if ((uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16) return fail(PKV_EINVAL, "pools must be 16-byte aligned");
   return device_status(pkv::launch_kv_compact(k_pool, v_pool, k_scale, v_scale, kv_dtype, src_tables, src_stride,
                                               dst_tables, dst_stride, keep_idx, keep_stride, keep_count, num_seqs,

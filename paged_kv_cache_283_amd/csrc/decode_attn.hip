@@ -107,7 +107,8 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   constexpr int KW = DPL * EB / 4;        // K words per lane per block
   constexpr int NT = D / 16;              // 16-dim output tiles
   constexpr int VW = EB;                  // V words per lane per tile (4 tokens)
-  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16));
+  constexpr bool CH = is_channel_scaled(KVT);   // static per-channel scales, folded into q and the output
+  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16)) && !CH;
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
 
@@ -148,8 +149,12 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int d0 = qk_dim16<KVT>(st, j) + 2 * w;
-          const float f0 = head_ok ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
-          const float f1 = head_ok ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+          float f0 = head_ok ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
+          float f1 = head_ok ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+          if constexpr (CH) {   // q . (code * s) = (q * s) . code, with q * s carried as hi + lo
+            f0 *= a.k_scale[(size_t)kvh * D + d0];
+            f1 *= a.k_scale[(size_t)kvh * D + d0 + 1];
+          }
           const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
           const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
           const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
@@ -224,7 +229,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
-        if constexpr (is_quantised(KVT)) {
+        if constexpr (is_code8(KVT)) {
           code8x4_to_bf16x4<KVT>(r.k[2 * st], av[0], av[1]);
           code8x4_to_bf16x4<KVT>(r.k[2 * st + 1], av[2], av[3]);
         } else {
@@ -332,7 +337,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t v0, v1;
-        if constexpr (is_quantised(KVT)) {
+        if constexpr (is_code8(KVT)) {
           code8x4_to_bf16x4<KVT>(r.v[t][0], v0, v1);
         } else {
           v0 = r.v[t][0];
@@ -394,6 +399,13 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
   if (bad) l_run = __builtin_nanf("");
   if (!head_ok) return;
+  if constexpr (CH) {   // V's channel scales: sum_p P_p (code_p * s) = s * sum_p P_p code_p
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 vsc = *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)kvh * D + 16 * t + 4 * j);
+      acc[t] *= vsc;
+    }
+  }
   // lane (c, j) holds head c's output dims 16 t + 4 j + e
   const size_t hs = (size_t)s * hq + head;
   if (whole) {
@@ -616,7 +628,7 @@ int resident_waves() {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wave_kernel<KVT, QT, D>, kWave, 0) != hipSuccess)
     return 0;
   if (per_cu < 1) per_cu = 1;
-  const int want = is_quantised(KVT) ? PKV_ATTN_WAVES_PER_CU_FP8 : PKV_ATTN_WAVES_PER_CU;
+  const int want = is_code8(KVT) ? PKV_ATTN_WAVES_PER_CU_FP8 : PKV_ATTN_WAVES_PER_CU;
   if (want > 0 && want < per_cu) per_cu = want;
   const int n = cus * per_cu;
   cache[dev] = n;
@@ -690,7 +702,9 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
     case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_F16: err = dispatch_q<DT_F16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_FP8: err = dispatch_q<DT_FP8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
-    default: err = dispatch_q<DT_INT8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    case DT_INT8: err = dispatch_q<DT_INT8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    case DT_FP8_CH: err = dispatch_q<DT_FP8_CH>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    default: err = dispatch_q<DT_INT8_CH>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
   }
   if (err != hipSuccess) return err;
   {

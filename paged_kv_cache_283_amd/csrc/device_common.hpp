@@ -9,10 +9,16 @@
 
 namespace pkv {
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3, DT_INT8 = 4 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2, DT_FP8 = 3, DT_INT8 = 4, DT_FP8_CH = 5, DT_INT8_CH = 6 };
 
-// Storage formats with 8-bit codes and one scale per (token, KV head).
+// Storage formats with 8-bit codes and one scale per (token, KV head), stored per block.
 __host__ __device__ constexpr bool is_quantised(int kv) { return kv == DT_FP8 || kv == DT_INT8; }
+// Storage formats with 8-bit codes and one static scale per (KV head, channel).
+__host__ __device__ constexpr bool is_channel_scaled(int kv) { return kv == DT_FP8_CH || kv == DT_INT8_CH; }
+// Any 8-bit code format.
+__host__ __device__ constexpr bool is_code8(int kv) { return is_quantised(kv) || is_channel_scaled(kv); }
+// The code set of an 8-bit format: DT_FP8 (E4M3FN) or DT_INT8.
+__host__ __device__ constexpr int code_set(int kv) { return (kv == DT_INT8 || kv == DT_INT8_CH) ? DT_INT8 : DT_FP8; }
 
 constexpr int kWave = 64;          // CDNA wavefront width
 
@@ -74,7 +80,7 @@ __device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint3
 // 8-bit codes of storage format KV -> bf16 operands.
 template <int KV>
 __device__ __forceinline__ void code8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  if constexpr (KV == DT_INT8) int8x4_to_bf16x4(w, lo, hi);
+  if constexpr (code_set(KV) == DT_INT8) int8x4_to_bf16x4(w, lo, hi);
   else fp8x4_to_bf16x4(w, lo, hi);
 }
 

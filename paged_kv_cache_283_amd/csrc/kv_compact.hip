@@ -143,6 +143,8 @@ hipError_t launch_kv_compact(void* k_pool, void* v_pool, float* k_scale, float* 
                           keep_stride, keep_count, num_seqs, num_blocks, num_kv_heads, head_dim, st);
     case DT_FP8:
     case DT_INT8:
+    case DT_FP8_CH:
+    case DT_INT8_CH:
       return compact_d<1>(k_pool, v_pool, ks, vs, src_tables, src_stride, dst_tables, dst_stride, keep_idx,
                           keep_stride, keep_count, num_seqs, num_blocks, num_kv_heads, head_dim, st);
     default:

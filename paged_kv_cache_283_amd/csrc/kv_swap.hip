@@ -60,7 +60,7 @@ hipError_t launch_kv_swap(void* k_pool, void* v_pool, float* k_scale, float* v_s
                           int num_blocks, int host_slots, int num_kv_heads, int head_dim, int to_host,
                           hipStream_t st) {
   if (num_pairs == 0) return hipSuccess;
-  const int eb = kv_dtype == DT_F32 ? 4 : (is_quantised(kv_dtype) ? 1 : 2);
+  const int eb = kv_dtype == DT_F32 ? 4 : (is_code8(kv_dtype) ? 1 : 2);
   const size_t block_bytes = (size_t)num_kv_heads * kBlockSize * head_dim * eb;
   const bool q = is_quantised(kv_dtype);
   hipLaunchKernelGGL(kv_swap_kernel, dim3(num_pairs), dim3(256), 0, st, reinterpret_cast<uint8_t*>(k_pool),

@@ -4,11 +4,11 @@
 // Page "KV Cache 与 PagedAttention：显存复用与长上下文推理" (plumephp.com/ai-kv-cache-paged-attention):
 //   "PagedAttention 的设计" -- a token lives in the physical block its sequence's
 //     block table names for logical block p / 16, at offset p % 16;
-//   "量化原理" -- FP8 (E4M3) or INT8 storage with per-token scales;
+//   "量化原理" -- FP8 (E4M3) or INT8 storage with per-token or per-channel scales;
 //   "三大运行时组件" and copy_on_write -- a shared block is copied before a write.
 // Pool layout: K [NB][Hkv][D/X][16][X] (16-byte chunks of X elements),
-// V [NB][Hkv][D/(16Y)][16][4][Y][4] (16-byte chunks of 4 tokens x Y dims), FP8 scales
-// [NB][Hkv][16].
+// V [NB][Hkv][D/(16Y)][16][4][Y][4] (16-byte chunks of 4 tokens x Y dims), per-token
+// scales [NB][Hkv][16], per-channel scales [Hkv][D] (static, given by the caller).
 #include "device_common.hpp"
 #include "fp8_e4m3.hpp"
 #include "launch.hpp"
@@ -49,7 +49,7 @@ __device__ __forceinline__ float src_to_f32(const void* p, size_t i) {
 // saturated to +-127, two's complement).
 template <int KVT>
 __device__ __forceinline__ uint32_t encode8(float q) {
-  if constexpr (KVT == DT_INT8) {
+  if constexpr (code_set(KVT) == DT_INT8) {
     const float r = fminf(fmaxf(__builtin_rintf(q), -127.f), 127.f);
     return (uint32_t)(int32_t)r & 0xffu;
   } else {
@@ -125,6 +125,20 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
       k_scale[tile * kBlockSize + o] = ks;
       v_scale[tile * kBlockSize + o] = vs;
     }
+  } else if constexpr (is_channel_scaled(KVT)) {
+    // Static scales [Hkv][D]: the code of x / scale[h][d] (fp32 division).
+    uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool);
+    uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = e * 64 + lane;
+      const float kx = src_to_f32<SRC>(k_new, src + d);
+      const float vx = src_to_f32<SRC>(v_new, src + d);
+      const uint32_t kc = encode8<KVT>(__fdiv_rn(kx, k_scale[(size_t)h * D + d]));
+      const uint32_t vc = encode8<KVT>(__fdiv_rn(vx, v_scale[(size_t)h * D + d]));
+      kp[tile * kBlockSize * D + k_chunk_offset<1>(o, d)] = (uint8_t)kc;
+      vp[tile * kBlockSize * D + v_chunk_offset<1>(o, d)] = (uint8_t)vc;
+    }
   } else {
     using T = typename std::conditional<KVT == DT_F32, uint32_t, uint16_t>::type;
     const T* ks = reinterpret_cast<const T*>(k_new);
@@ -140,7 +154,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
   }
 }
 
-// Copy whole blocks src -> dst: K tile, V tile and (FP8) both scale rows, all KV heads.
+// Copy whole blocks src -> dst: K tile, V tile and (per-token FP8/INT8) both scale rows, all KV heads.
 __global__ void __launch_bounds__(256) block_copy_kernel(uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale,
                                                        const int32_t* pairs, int num_blocks, size_t block_bytes,
                                                        int scale_floats) {
@@ -197,6 +211,16 @@ hipError_t write_any(const void* k_new, const void* v_new, int src_dtype, void* 
     if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_INT8);
     return PKV_WRITE(DT_F16, DT_INT8);
   }
+  if (kv_dtype == DT_FP8_CH) {
+    if (src_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_FP8_CH);
+    if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_FP8_CH);
+    return PKV_WRITE(DT_F16, DT_FP8_CH);
+  }
+  if (kv_dtype == DT_INT8_CH) {
+    if (src_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_INT8_CH);
+    if (src_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_INT8_CH);
+    return PKV_WRITE(DT_F16, DT_INT8_CH);
+  }
   if (kv_dtype == DT_F32) return PKV_WRITE(DT_F32, DT_F32);
   if (kv_dtype == DT_BF16) return PKV_WRITE(DT_BF16, DT_BF16);
   return PKV_WRITE(DT_F16, DT_F16);
@@ -243,7 +267,7 @@ hipError_t launch_block_copy(void* k_pool, void* v_pool, float* k_scale, float* 
                              const int32_t* pairs, int num_pairs, int num_blocks, int num_kv_heads, int head_dim,
                              hipStream_t st) {
   if (num_pairs == 0) return hipSuccess;
-  const int eb = kv_dtype == DT_F32 ? 4 : (is_quantised(kv_dtype) ? 1 : 2);
+  const int eb = kv_dtype == DT_F32 ? 4 : (is_code8(kv_dtype) ? 1 : 2);
   const size_t block_bytes = (size_t)num_kv_heads * kBlockSize * head_dim * eb;
   const int scale_floats = num_kv_heads * kBlockSize;
   const unsigned chunks = (unsigned)((block_bytes / 16 + 255) / 256);

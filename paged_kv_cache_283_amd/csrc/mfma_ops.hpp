@@ -11,7 +11,7 @@ namespace pkv {
 
 template <int KVT>
 struct KvType {
-  static constexpr int kBytes = KVT == DT_F32 ? 4 : (is_quantised(KVT) ? 1 : 2);
+  static constexpr int kBytes = KVT == DT_F32 ? 4 : (is_code8(KVT) ? 1 : 2);
   static constexpr bool kOp32 = KVT == DT_F32;   // fp32 MFMA operands
   static constexpr bool kOpF16 = KVT == DT_F16;  // f16 MFMA operands (bf16 otherwise)
 };
@@ -66,7 +66,7 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
 // X elements, load u of row group j is chunk 4u + j.
 template <int KVT>
 __device__ __forceinline__ int qk_dim16(int st, int j) {
-  if constexpr (is_quantised(KVT)) return (4 * (st / 2) + j) * 16 + 8 * (st % 2);   // X = 16: two steps per chunk
+  if constexpr (is_code8(KVT)) return (4 * (st / 2) + j) * 16 + 8 * (st % 2);       // X = 16: two steps per chunk
   else return (4 * st + j) * 8;                                               // X = 8: one step per chunk
 }
 // Head-dim row group j contributes to step st of the fp32 16x16x4 MFMA (X = 4).

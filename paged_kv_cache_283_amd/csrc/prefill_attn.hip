@@ -58,7 +58,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   constexpr int KW = DPL * EB / 4;
   constexpr int NT = D / 16;
   constexpr int VW = EB;
-  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16));
+  constexpr bool CH = is_channel_scaled(KVT);   // static per-channel scales, folded into q and the output
+  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16)) && !CH;
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;
   __shared__ int s_tab_all[kPfWaves][kPfTab];
@@ -126,8 +127,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const int d0 = qk_dim16<KVT>(st, j) + 2 * w;
-          const float f0 = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
-          const float f1 = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+          float f0 = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + d0) : 0.f;
+          float f1 = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + d0 + 1) : 0.f;
+          if constexpr (CH) {   // q . (code * s) = (q * s) . code, with q * s carried as hi + lo
+            f0 *= a.k_scale[(size_t)kvh * D + d0];
+            f1 *= a.k_scale[(size_t)kvh * D + d0 + 1];
+          }
           const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
           const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
           const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
@@ -206,7 +211,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
-        if constexpr (is_quantised(KVT)) {
+        if constexpr (is_code8(KVT)) {
           code8x4_to_bf16x4<KVT>(r.k[2 * st], av[0], av[1]);
           code8x4_to_bf16x4<KVT>(r.k[2 * st + 1], av[2], av[3]);
         } else {
@@ -307,7 +312,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint32_t v0, v1;
-        if constexpr (is_quantised(KVT)) {
+        if constexpr (is_code8(KVT)) {
           code8x4_to_bf16x4<KVT>(r.v[t][0], v0, v1);
         } else {
           v0 = r.v[t][0];
@@ -373,8 +378,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     const float inv = 1.f / l;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      f32x4 o = acc[cs][t];
+      if constexpr (CH) o *= *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)kvh * D + 16 * t + 4 * j);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, acc[cs][t][e] * inv);
+      for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, o[e] * inv);
     }
   }
 }
@@ -419,7 +426,9 @@ hipError_t launch_prefill_attn(const PrefillArgs& a, int kv_dtype, int q_dtype, 
     case DT_BF16: return prefill_q<DT_BF16>(a, q_dtype, head_dim, max_query_len, st);
     case DT_F16: return prefill_q<DT_F16>(a, q_dtype, head_dim, max_query_len, st);
     case DT_FP8: return prefill_q<DT_FP8>(a, q_dtype, head_dim, max_query_len, st);
-    default: return prefill_q<DT_INT8>(a, q_dtype, head_dim, max_query_len, st);
+    case DT_INT8: return prefill_q<DT_INT8>(a, q_dtype, head_dim, max_query_len, st);
+    case DT_FP8_CH: return prefill_q<DT_FP8_CH>(a, q_dtype, head_dim, max_query_len, st);
+    default: return prefill_q<DT_INT8_CH>(a, q_dtype, head_dim, max_query_len, st);
   }
 }
 

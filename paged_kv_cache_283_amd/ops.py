@@ -6,8 +6,10 @@ include/pagedkv.h; shapes are read off the tensors.
 
 Storage dtypes: torch.float32 / bfloat16 / float16 pools hold those values;
 torch.uint8 or torch.float8_e4m3fn pools hold OCP E4M3FN codes and torch.int8
-pools hold INT8 codes, both with float32 scale tensors
-[num_blocks][num_kv_heads][16].  Pool shapes:
+pools hold INT8 codes.  8-bit pools come with float32 scale tensors: per-token
+scales [num_blocks][num_kv_heads][16] (written by the library), or static
+per-channel scales [num_kv_heads][head_dim] (given by the caller) -- the scale
+tensors' rank tells the two apart.  Pool shapes:
 K [num_blocks][num_kv_heads][head_dim/X][16][X] (X = 16 bytes of elements),
 V [num_blocks][num_kv_heads][head_dim/(16Y)][16][4][Y][4] (Y = 4 / element bytes);
 allocate_pools builds both.
@@ -49,8 +51,33 @@ def kv_code(dtype: torch.dtype) -> int:
 
 
 def quantised(dtype: torch.dtype) -> bool:
-    """Pools of 8-bit codes carry one float32 scale per (token, KV head)."""
+    """Pools of 8-bit codes (which carry float32 scales)."""
     return kv_code(dtype) in (_lib.FP8_E4M3, _lib.INT8)
+
+
+_CHANNEL_CODES = {_lib.FP8_E4M3: _lib.FP8_E4M3_CHANNEL, _lib.INT8: _lib.INT8_CHANNEL}
+
+
+def pool_code(k_pool, k_scale=None, v_scale=None):
+    """Storage code of a pool with its scale tensors: an 8-bit pool whose scales are
+    [num_kv_heads][head_dim] uses the per-channel format, one with [num_blocks][num_kv_heads][16]
+    (or no scales, for calls that take none) the per-token one.  Shapes are checked here since the
+    library cannot see array sizes."""
+    code = kv_code(k_pool.dtype)
+    if code not in _CHANNEL_CODES or k_scale is None:
+        return code
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    d = k_pool.shape[2] * k_pool.shape[4]
+    if v_scale is None or v_scale.shape != k_scale.shape:
+        raise ValueError("k_scale and v_scale must have the same shape")
+    _need(k_scale, torch.float32, "k_scale")
+    _need(v_scale, torch.float32, "v_scale")
+    if tuple(k_scale.shape) == (hkv, d):
+        return _CHANNEL_CODES[code]
+    if tuple(k_scale.shape) == (nb, hkv, BLOCK_SIZE):
+        return code
+    raise ValueError(f"scales must be [{nb}][{hkv}][{BLOCK_SIZE}] (per token) or [{hkv}][{d}] (per channel), "
+                     f"got {tuple(k_scale.shape)}")
 
 
 def _ptr(t):
@@ -149,7 +176,8 @@ def paged_token_slots(block_tables, seq_ids, positions, num_blocks, slot_mapping
 
 def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_scale=None, stream=None,
                    prepare=False):
-    """Store [T][Hkv][D] new K/V rows at their slots (FP8 pools quantise per row)."""
+    """Store [T][Hkv][D] new K/V rows at their slots (8-bit pools quantise per row, or per channel
+    with the given static scales)."""
     _need(slot_mapping, torch.int64, "slot_mapping")
     t, hkv, d = k_new.shape
     if v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
@@ -162,7 +190,7 @@ def paged_kv_write(k_new, v_new, k_pool, v_pool, slot_mapping, k_scale=None, v_s
     if slot_mapping.shape[0] != t:
         raise ValueError("slot_mapping must have one entry per token")
     return _issue("paged_kv_write", (_ptr(k_new), _ptr(v_new), float_code(k_new.dtype), _ptr(k_pool),
-                                     _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
+                                     _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale),
                                      _ptr(slot_mapping), t, nb, hkv, d, BLOCK_SIZE, _stream(stream)), prepare)
 
 
@@ -181,22 +209,31 @@ def paged_kv_append(k_new, v_new, k_pool, v_pool, block_tables, context_lens, k_
     if context_lens.shape[0] != b or block_tables.shape[0] != b:
         raise ValueError("one table row and one length per sequence")
     return _issue("paged_kv_append", (_ptr(k_new), _ptr(v_new), float_code(k_new.dtype), _ptr(k_pool), _ptr(v_pool),
-                                      _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype), _ptr(block_tables),
+                                      _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale), _ptr(block_tables),
                                       block_tables.shape[1], _ptr(context_lens), b, nb, hkv, d, BLOCK_SIZE,
                                       _stream(stream)), prepare)
 
 
-def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, device="cuda", fill_byte=None):
-    """(k_pool, v_pool, k_scale, v_scale) in the library's layout; scales are None unless kv_dtype is FP8
-    (torch.uint8 or torch.float8_e4m3fn).  fill_byte sets every byte (0xFF = NaN everywhere)."""
+def allocate_pools(num_blocks, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, device="cuda", fill_byte=None,
+                   channel_scales=None):
+    """(k_pool, v_pool, k_scale, v_scale) in the library's layout.  Scales are None for float pools;
+    for 8-bit pools (torch.uint8 / float8_e4m3fn / int8) they are per-token scale tensors, or, when
+    channel_scales = (k_channel, v_channel) is given, those [num_kv_heads][head_dim] float32 tensors
+    (copied to the device).  fill_byte sets every pool and per-token scale byte (0xFF = NaN everywhere)."""
     k = torch.empty(k_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
     v = torch.empty(v_pool_shape(num_blocks, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, device=device)
     ks = vs = None
-    if quantised(kv_dtype):
+    if channel_scales is not None:
+        if not quantised(kv_dtype):
+            raise ValueError("per-channel scales need an 8-bit pool dtype")
+        ks, vs = (torch.as_tensor(c, dtype=torch.float32).to(device).contiguous() for c in channel_scales)
+        if tuple(ks.shape) != (num_kv_heads, head_dim) or tuple(vs.shape) != (num_kv_heads, head_dim):
+            raise ValueError(f"channel scales must be [{num_kv_heads}][{head_dim}]")
+    elif quantised(kv_dtype):
         ks = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)
         vs = torch.empty((num_blocks, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, device=device)
     if fill_byte is not None:
-        for t in (k, v, ks, vs):
+        for t in (k, v) if channel_scales is not None else (k, v, ks, vs):
             if t is not None:
                 t.view(torch.uint8).fill_(fill_byte)
     return k, v, ks, vs
@@ -245,7 +282,7 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     if workspace is None:
         workspace = alloc_workspace(b, hq, d, max_context_len, num_sinks, window, attn_mass is not None, q.device)
     args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
-            _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype), _ptr(block_tables), block_tables.shape[1],
+            _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale), _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), int(max_context_len), b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), int(num_sinks),
             int(window), _ptr(attn_mass), mass_stride, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
@@ -268,7 +305,7 @@ def paged_prefill_attn(out, q, k_pool, v_pool, block_tables, context_lens, query
         raise ValueError("query_start needs num_seqs + 1 entries and block_tables one row per sequence")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
-            _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype), _ptr(block_tables), block_tables.shape[1],
+            _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale), _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), _ptr(query_start), t, int(max_context_len), int(max_query_len), b, nb, hq, hkv, d,
             BLOCK_SIZE, float(scale), _stream(stream))
     return _issue("paged_prefill_attn", args, prepare)
@@ -282,12 +319,13 @@ def _host_ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def allocate_host_arena(num_slots, num_kv_heads, head_dim, kv_dtype=torch.bfloat16):
-    """Pinned host (k, v, k_scale, v_scale) mirroring the pool layout with num_slots blocks."""
+def allocate_host_arena(num_slots, num_kv_heads, head_dim, kv_dtype=torch.bfloat16, per_token_scales=True):
+    """Pinned host (k, v, k_scale, v_scale) mirroring the pool layout with num_slots blocks (scale rows
+    only for 8-bit pools with per-token scales; per-channel scales stay on the device)."""
     k = torch.empty(k_pool_shape(num_slots, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, pin_memory=True)
     v = torch.empty(v_pool_shape(num_slots, num_kv_heads, head_dim, kv_dtype), dtype=kv_dtype, pin_memory=True)
     ks = vs = None
-    if quantised(kv_dtype):
+    if quantised(kv_dtype) and per_token_scales:
         ks = torch.empty((num_slots, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, pin_memory=True)
         vs = torch.empty((num_slots, num_kv_heads, BLOCK_SIZE), dtype=torch.float32, pin_memory=True)
     return k, v, ks, vs
@@ -302,7 +340,7 @@ def kv_swap(pools, arena, block_slot_pairs, to_host, stream=None, prepare=False)
         raise ValueError("the host arena must mirror the pool layout")
     nb, hkv = k.shape[0], k.shape[1]
     d = k.shape[2] * k.shape[4]
-    args = (_ptr(k), _ptr(v), _ptr(ks), _ptr(vs), kv_code(k.dtype), _host_ptr(hk), _host_ptr(hv), _host_ptr(hks),
+    args = (_ptr(k), _ptr(v), _ptr(ks), _ptr(vs), pool_code(k, ks, vs), _host_ptr(hk), _host_ptr(hv), _host_ptr(hks),
             _host_ptr(hvs), _ptr(block_slot_pairs), block_slot_pairs.shape[0], nb, hk.shape[0], hkv, d, BLOCK_SIZE,
             1 if to_host else 0, _stream(stream))
     return _issue("kv_swap", args, prepare)
@@ -313,7 +351,7 @@ def kv_block_copy(k_pool, v_pool, block_pairs, k_scale=None, v_scale=None, strea
     _need(block_pairs, torch.int32, "block_pairs")
     nb, hkv = k_pool.shape[0], k_pool.shape[1]
     d = k_pool.shape[2] * k_pool.shape[4]
-    _lib.call("kv_block_copy", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
+    _lib.call("kv_block_copy", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale),
               _ptr(block_pairs), block_pairs.shape[0], nb, hkv, d, BLOCK_SIZE, _stream(stream))
 
 
@@ -365,7 +403,7 @@ def kv_compact(k_pool, v_pool, src_tables, dst_tables, keep_idx, keep_count, k_s
     b = keep_count.shape[0]
     if src_tables.shape[0] != b or dst_tables.shape[0] != b or keep_idx.shape[0] != b:
         raise ValueError("tables, keep_idx and keep_count must have one row per sequence")
-    _lib.call("kv_compact", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), kv_code(k_pool.dtype),
+    _lib.call("kv_compact", _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale),
               _ptr(src_tables), src_tables.shape[1], _ptr(dst_tables), dst_tables.shape[1], _ptr(keep_idx),
               keep_idx.shape[1], _ptr(keep_count), b, nb, hkv, d, BLOCK_SIZE, _stream(stream))
 

@@ -36,13 +36,23 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def stored_values(kv_dtype, rows):
-    """float64 values a pool of kv_dtype holds for source rows [n][Hkv][D] (the oracle's own codec)."""
+def stored_values(kv_dtype, rows, channel=None):
+    """float64 values a pool of kv_dtype holds for source rows [n][Hkv][D] (the oracle's own codec);
+    channel: the static [Hkv][D] scales of a per-channel format."""
     if kv_dtype in ("fp8", "int8"):
         codec = fp8 if kv_dtype == "fp8" else int8
         c, sc = codec.quantize_per_token(np.asarray(rows).astype(np.float32))
         return codec.dequantize_per_token(c, sc)
+    if kv_dtype in ("fp8_ch", "int8_ch"):
+        codec = fp8 if kv_dtype == "fp8_ch" else int8
+        c = codec.quantize_per_channel(np.asarray(rows).astype(np.float32), channel)
+        return codec.decode(c) * channel.astype(np.float64)
     return rows
+
+
+def channel_pair(w, layer=0):
+    """(k, v) static channel scales of a per-channel workload, else (None, None)."""
+    return W.channel_scales(w, layer) if w.kv_dtype in W.CHANNEL_CODE_MAX else (None, None)
 
 
 def oracle_seq(w, lay, s, q_s, k_rows, v_rows, scale=None, num_sinks=0, window=0):
@@ -53,7 +63,8 @@ def oracle_seq(w, lay, s, q_s, k_rows, v_rows, scale=None, num_sinks=0, window=0
     """
     L = int(lay.lens[s])
     keep = policies.streaming_keep(L, num_sinks, window)
-    k_rows, v_rows = stored_values(w.kv_dtype, k_rows), stored_values(w.kv_dtype, v_rows)
+    kc, vc = channel_pair(w)
+    k_rows, v_rows = stored_values(w.kv_dtype, k_rows, kc), stored_values(w.kv_dtype, v_rows, vc)
     scale = 1.0 / math.sqrt(w.head_dim) if scale is None else scale
     out, p_kept = attention.decode_attention(q_s, k_rows, v_rows, scale)
     probs = np.zeros((q_s.shape[0], L))

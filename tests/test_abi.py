@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from paged_kv_cache_283_amd import _lib
 
@@ -62,6 +63,7 @@ def attn_args(**kw):
     (dict(nb=0), _lib.EINVAL),
     (dict(q=None), _lib.EINVAL),
     (dict(kv_dtype=3), _lib.EINVAL),                     # FP8 without scales
+    (dict(kv_dtype=6), _lib.EINVAL),                     # per-channel INT8 without scales
     (dict(mass=FAKE, mass_stride=100), _lib.EINVAL),
     (dict(ws_bytes=10), _lib.EWORKSPACE),
     (dict(ws=ctypes.c_void_p(0x100010)), _lib.EINVAL),   # not 256-byte aligned
@@ -100,6 +102,8 @@ def test_write_validation():
     assert w(*base[:13], 32, base[14]) == _lib.EUNSUPPORTED
     assert w(*base[:2], 0, *base[3:]) == _lib.EUNSUPPORTED          # f32 source into a bf16 pool
     assert w(*base[:7], 3, *base[8:]) == _lib.EINVAL                # FP8 without scales
+    assert w(*base[:7], 5, *base[8:]) == _lib.EINVAL                # per-channel FP8 without scales
+    assert w(*base[:7], 7, *base[8:]) == _lib.EINVAL                # no such format
     assert w(*base[:9], -1, *base[10:]) == _lib.EINVAL
     assert w(None, *base[1:]) == _lib.EINVAL
     assert w(*base[:9], 0, *base[10:]) == _lib.OK                   # nothing to write
@@ -170,3 +174,24 @@ def test_swap_validation():
     assert sw(FAKE, FAKE, None, None, 1, FAKE, FAKE, None, None, FAKE, 4, 64, 0, 8, 128, 16, 1, None) == _lib.EINVAL
     assert sw(FAKE, FAKE, None, None, 1, FAKE, FAKE, None, None, FAKE, 0, 64, 8, 8, 128, 16, 1, None) == _lib.OK
     assert sw(FAKE, FAKE, None, None, 1, None, FAKE, None, None, FAKE, 4, 64, 8, 8, 128, 16, 0, None) == _lib.EINVAL
+
+
+def test_pool_code_reads_the_scale_layout():
+    """The binding picks the per-channel format from [Hkv][D] scales and the per-token one from
+    [NB][Hkv][16] scales (shapes only: no device needed)."""
+    from paged_kv_cache_283_amd import ops
+    for dt, tok, ch in ((torch.uint8, _lib.FP8_E4M3, _lib.FP8_E4M3_CHANNEL), (torch.int8, _lib.INT8, _lib.INT8_CHANNEL)):
+        k = torch.empty(ops.k_pool_shape(10, 2, 64, dt), dtype=dt)
+        assert ops.pool_code(k) == tok
+        per_tok = torch.empty((10, 2, 16))
+        assert ops.pool_code(k, per_tok, per_tok) == tok
+        per_ch = torch.empty((2, 64))
+        assert ops.pool_code(k, per_ch, per_ch) == ch
+        with pytest.raises(ValueError):
+            ops.pool_code(k, torch.empty((2, 32)), torch.empty((2, 32)))
+        with pytest.raises(ValueError):
+            ops.pool_code(k, per_ch, per_tok)
+        with pytest.raises(TypeError):
+            ops.pool_code(k, per_ch.double(), per_ch.double())
+    kb = torch.empty(ops.k_pool_shape(10, 2, 64, torch.bfloat16), dtype=torch.bfloat16)
+    assert ops.pool_code(kb, torch.empty((2, 64)), torch.empty((2, 64))) == _lib.BF16

@@ -20,11 +20,12 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     from tests import _harness as H
 
-TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "fp8": 1e-2, "int8": 1e-2}
+TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "fp8": 1e-2, "int8": 1e-2, "fp8_ch": 1e-2, "int8_ch": 1e-2}
+CODE8 = ("fp8", "int8", "fp8_ch", "int8_ch")
 
 
 def _case_workload(kv, q, d, hq, hkv, seed, lens=(35, 70), **kw):
-    src = "bf16" if kv in ("fp8", "int8") else kv
+    src = "bf16" if kv in CODE8 else kv
     return dataclasses.replace(W.WORKLOADS["tiny"], name=f"t-{kv}-{q}-{d}", kv_dtype=kv, src_dtype=src, q_dtype=q,
                                head_dim=d, num_q_heads=hq, num_kv_heads=hkv, seed=seed, pool_blocks=None,
                                extra_blocks=3, lens=tuple(lens), num_seqs=len(lens), **kw)
@@ -73,15 +74,18 @@ def test_decode_and_token_slots_match_oracle():
 
 @pytest.mark.parametrize("kv,src,d", [("f32", "f32", 64), ("bf16", "bf16", 128), ("f16", "f16", 128),
                                       ("fp8", "bf16", 128), ("fp8", "f32", 64), ("fp8", "f16", 128),
-                                      ("int8", "bf16", 128), ("int8", "f32", 64), ("int8", "f16", 128)])
+                                      ("int8", "bf16", 128), ("int8", "f32", 64), ("int8", "f16", 128),
+                                      ("fp8_ch", "bf16", 128), ("fp8_ch", "f32", 64), ("int8_ch", "bf16", 128),
+                                      ("int8_ch", "f16", 64)])
 def test_write_pool_bytes_bit_exact(kv, src, d):
     w = dataclasses.replace(_case_workload(kv, "bf16", d, 8, 2, 91, lens=(35, 70, 16, 1)), src_dtype=src)
     case = H.Case(w)
     lay = case.lay
     # oracle pools: all bytes 0xFF, then the same tokens written by the oracle's own slot arithmetic
-    ref = list(paging.new_pools(lay.num_blocks, 2, d, kv))
+    kc, vc = H.channel_pair(w)
+    ref = list(paging.new_pools(lay.num_blocks, 2, d, kv, k_channel=kc, v_channel=vc))
     for a in ref:
-        if a is not None:
+        if a is not None and a.ndim > 2:          # static channel scales keep their values
             a.view(np.uint8)[...] = 0xFF
     seq, pos, rows = lay.fill_tokens()
     ks = case.ksrc.cpu()[torch.from_numpy(rows)]
@@ -160,6 +164,10 @@ GRID = [
     ("fp8", "f16", 128, 16, 2),
     ("int8", "bf16", 128, 32, 8),
     ("int8", "f32", 64, 8, 2),
+    ("fp8_ch", "bf16", 128, 32, 8),
+    ("fp8_ch", "f32", 64, 8, 2),
+    ("int8_ch", "bf16", 128, 16, 2),
+    ("int8_ch", "f16", 64, 8, 8),
 ]
 LENS = (1, 15, 16, 17, 35, 70, 511, 512, 513, 1100, 2049)
 
@@ -274,7 +282,7 @@ def test_invalid_device_values_poison_only_their_sequence():
 
 # ---------------------------------------------------------------------------- copy-on-write
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8", "int8_ch"])
 def test_copy_on_write(kv):
     """Four sequences share four blocks; seq 3 gets a private copy of its last block (a COW)."""
     w = dataclasses.replace(_case_workload(kv, "bf16", 128, 32, 8, 21, lens=(64,) * 4), shared_prefix=(4, 4),
@@ -285,10 +293,13 @@ def test_copy_on_write(kv):
     dst = int(case.lay.unused_blocks[0])
     assert (case.lay.tables[:, 3] == src).all()
     k, v, ks, vs = case.pools
+    ch_before = [None if t is None else t.clone() for t in (ks, vs)]
     ops.kv_block_copy(k, v, torch.tensor([[src, dst]], dtype=torch.int32).cuda(), ks, vs)
     for p in case.pools:
-        if p is not None:
+        if p is not None and p.dim() > 2:
             assert torch.equal(p[dst].view(torch.uint8), p[src].view(torch.uint8))
+    if kv.endswith("_ch"):                           # static channel scales are not per block: untouched
+        assert torch.equal(ks, ch_before[0]) and torch.equal(vs, ch_before[1])
     tables = case.tables.clone()
     tables[3, 3] = dst
     after = torch.empty_like(before)
@@ -422,7 +433,8 @@ def _host_pools(pools, kv):
         _NP[t.dtype]).reshape(t.shape) for t in pools]
 
 
-@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("fp8", 128), ("fp8", 64), ("int8", 128)])
+@pytest.mark.parametrize("kv,d", [("f32", 64), ("bf16", 128), ("f16", 64), ("fp8", 128), ("fp8", 64), ("int8", 128),
+                                  ("fp8_ch", 128), ("int8_ch", 64)])
 def test_compact_pool_bytes_bit_exact(kv, d):
     """kv_compact moves kept tokens exactly as the oracle's compact does; no other byte changes."""
     lens = (35, 70, 300, 1, 129)
@@ -521,7 +533,7 @@ def test_eviction_end_to_end_mass_select_compact_attend():
     assert worst <= 2e-3
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "f32", "int8", "fp8_ch"])
 def test_append_equals_slots_then_write(kv):
     """paged_kv_append stores exactly what paged_decode_slots + paged_kv_write store, and skips the
     sequences whose decode slot is -1."""
@@ -564,7 +576,8 @@ def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):
 def _prefill_oracle(w, case, qt, qs, s):
     L = int(case.lay.lens[s])
     kr, vr = H.kept_source(w, case.lay, s, case.ksrc, case.vsrc)
-    kr, vr = H.stored_values(w.kv_dtype, kr), H.stored_values(w.kv_dtype, vr)
+    kc, vc = H.channel_pair(w)
+    kr, vr = H.stored_values(w.kv_dtype, kr, kc), H.stored_values(w.kv_dtype, vr, vc)
     a, b = int(qs[s]), int(qs[s + 1])
     return attention.prefill_attention(H.to_f64(qt[a:b]), kr, vr, 1 / math.sqrt(w.head_dim))
 
@@ -574,6 +587,8 @@ PREFILL_GRID = [
     ("bf16", "bf16", 128, 32, 8),     # G = 4: 4 query tokens per wave
     ("fp8", "bf16", 128, 32, 8),
     ("int8", "bf16", 128, 32, 8),
+    ("fp8_ch", "bf16", 128, 32, 8),
+    ("int8_ch", "f16", 64, 16, 2),
     ("f32", "f32", 64, 8, 2),
     ("f16", "f16", 128, 16, 16),      # G = 1: 16 query tokens per wave
     ("bf16", "f32", 64, 16, 2),       # G = 8, split query operand
@@ -680,7 +695,7 @@ def test_prefix_cache_hit_prefills_only_the_suffix():
 
 # ---------------------------------------------------------------------------- swap to host
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8", "fp8_ch"])
 def test_swap_out_and_back_into_other_blocks(kv):
     """A sequence's blocks go to pinned host slots byte for byte, its pool blocks are overwritten,
     and after swapping back into different blocks its attention is bit-identical."""
@@ -689,18 +704,18 @@ def test_swap_out_and_back_into_other_blocks(kv):
     lay = case.lay
     before = case.attend()
     pools = case.pools
-    arena = ops.allocate_host_arena(32, 8, 128, pools[0].dtype)
+    arena = ops.allocate_host_arena(32, 8, 128, pools[0].dtype, per_token_scales=not kv.endswith("_ch"))
     nblk = -(-300 // 16)
     src = lay.tables[1, :nblk].astype(np.int32)
     slots = np.arange(5, 5 + nblk, dtype=np.int32)[::-1].copy()
     ops.kv_swap(pools, arena, torch.from_numpy(np.stack([src, slots], 1)).cuda(), to_host=True)
     torch.cuda.synchronize()
     for p, a in zip(pools, arena):
-        if p is not None:
+        if a is not None:
             assert torch.equal(a[torch.from_numpy(slots).long()].view(torch.uint8),
                                p[torch.from_numpy(src).long()].cpu().view(torch.uint8))
     for p in pools:                                   # the pool blocks are reused by someone else
-        if p is not None:
+        if p is not None and p.dim() > 2:
             p.view(torch.uint8)[torch.from_numpy(src).long()] = 0xFF
     dst = np.asarray(lay.unused_blocks[:nblk], dtype=np.int32)
     ops.kv_swap(pools, arena, torch.from_numpy(np.stack([dst, slots], 1)).cuda(), to_host=False)

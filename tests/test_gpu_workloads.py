@@ -127,3 +127,49 @@ def test_llama2_stack_80_layers_sampled():
         del ksrc, vsrc
     print(f"llama2: 8 layers x 8 sequences, max abs err {worst:.3e}")
     assert worst <= 2e-3
+
+
+@pytest.mark.parametrize("name", ["int8long", "fp8chlong"])
+def test_8bit_codec_long_contexts_sampled(name):
+    """16 x 32768 tokens in INT8 (per-token scales) or FP8 with static per-channel scales; the oracle
+    checks four sequences spread over the batch."""
+    w = W.WORKLOADS[name]
+    case = H.Case(w, hold_last=True)
+    case.decode_write()
+    out = _check(case, [0, 5, 10, 15], 1e-2)
+    assert torch.isfinite(out).all()
+
+
+def test_prefill_chunk_full_size_sampled_rows():
+    """4 sequences of 8192 tokens, each prefilling its last 2048 as one chunk, launched as the
+    multi-query benchmark launches it (bf16 output).  Each sampled query row is checked against the
+    oracle's decode attention over the context cut after that row's position."""
+    from oracle import attention
+    w = W.WORKLOADS["prefill"]
+    lay = W.make_layout(w)
+    tables = torch.from_numpy(lay.tables).cuda()
+    lens = torch.from_numpy(lay.lens).cuda()
+    pools = H.make_pools(w, lay.num_blocks)
+    ksrc, vsrc = W.kv_source(w, lay, device="cuda")
+    H.fill(w, lay, pools, ksrc, vsrc, tables)
+    k, v, ks, vs = pools
+    q, start = W.chunk_queries(w, device="cuda")
+    qs = torch.from_numpy(start).cuda()
+    out = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    ops.paged_prefill_attn(out, q, k, v, tables, lens, qs, lay.max_len, w.chunk, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    worst = 0.0
+    for s in range(w.num_seqs):
+        L = int(lay.lens[s])
+        rows = sorted({0, 1, 15, 16, 17, 1023, w.chunk - 1, *rng.integers(0, w.chunk, 4).tolist()})
+        kr, vr = H.kept_source(w, lay, s, ksrc, vsrc)
+        for i in rows:
+            p = L - w.chunk + i                                   # the row's position: keys 0..p
+            ref, _ = attention.decode_attention(H.to_f64(q[int(start[s]) + i]), kr[: p + 1], vr[: p + 1], scale)
+            got = H.to_f64(out[int(start[s]) + i])
+            # fp32 result within 2e-3, then one bf16 rounding on store (relative 2^-9)
+            assert np.all(np.abs(got - ref) <= 2e-3 + np.abs(ref) * 2.0 ** -8), (s, i)
+            worst = max(worst, float(np.max(np.abs(got - ref))))
+    print(f"prefill 4x2048 after 6144: {w.num_seqs} x {len(rows)} rows checked, max abs err {worst:.3e}")

@@ -32,7 +32,7 @@ class Workload:
     num_q_heads: int
     num_kv_heads: int
     head_dim: int
-    kv_dtype: str                  # "f32" | "bf16" | "f16" | "fp8" | "int8"
+    kv_dtype: str                  # "f32" | "bf16" | "f16" | "fp8" | "int8" | "fp8_ch" | "int8_ch"
     src_dtype: str                 # dtype of the new K/V rows written into the cache
     q_dtype: str
     seed: int
@@ -59,6 +59,7 @@ WORKLOADS = {
     "fp8long": Workload("fp8long", 16, 32, 8, 128, "fp8", "bf16", "bf16", 2833, lens=(32768,) * 16,
                         shared_prefix=(4, 128)),
     "int8long": Workload("int8long", 16, 32, 8, 128, "int8", "bf16", "bf16", 2837, lens=(32768,) * 16),
+    "fp8chlong": Workload("fp8chlong", 16, 32, 8, 128, "fp8_ch", "bf16", "bf16", 2838, lens=(32768,) * 16),
     "streaming": Workload("streaming", 32, 32, 8, 128, "bf16", "bf16", "bf16", 2834, lens=(131072,) * 32,
                           num_sinks=4, window=4096, table_width=8192,
                           mapped_ranges=((0, 1), (7936, 8192)), extra_blocks=0),
@@ -206,4 +207,20 @@ def chunk_queries(w: Workload, device="cpu"):
 def storage_dtype(kv_dtype: str):
     torch = _torch()
     return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "fp8": torch.uint8,
-            "int8": torch.int8}[kv_dtype]
+            "int8": torch.int8, "fp8_ch": torch.uint8, "int8_ch": torch.int8}[kv_dtype]
+
+
+CHANNEL_CODE_MAX = {"fp8_ch": 448.0, "int8_ch": 127.0}
+
+
+def channel_scales(w: Workload, layer: int = 0):
+    """Static per-channel scales (k, v), float32 numpy [Hkv][D], for the per-channel storage formats:
+    each channel is given a calibrated range of 4 * 2^u, u ~ U(-1, 1) (the unit-variance source rows
+    reach beyond it now and then, and saturate), and scale = range / largest code."""
+    import numpy as np
+    cmax = CHANNEL_CODE_MAX[w.kv_dtype]
+    rng = np.random.default_rng(w.seed * 100 + layer + 51)
+    shape = (w.num_kv_heads, w.head_dim)
+    k = (4.0 * 2.0 ** rng.uniform(-1, 1, shape) / cmax).astype(np.float32)
+    v = (4.0 * 2.0 ** rng.uniform(-1, 1, shape) / cmax).astype(np.float32)
+    return k, v

@@ -9,12 +9,15 @@ import torch
 
 from paged_kv_cache_283_amd import ops
 
-from . import storage_dtype
+from . import CHANNEL_CODE_MAX, channel_scales, storage_dtype
 
 
-def make_pools(w, num_blocks, device="cuda"):
-    """Pools of the workload's shape, every byte 0xFF (NaN) so unwritten slots poison any read."""
-    return ops.allocate_pools(num_blocks, w.num_kv_heads, w.head_dim, storage_dtype(w.kv_dtype), device, 0xFF)
+def make_pools(w, num_blocks, device="cuda", layer=0):
+    """Pools of the workload's shape, every pool byte 0xFF (NaN) so unwritten slots poison any read;
+    per-channel formats get the workload's static channel scales."""
+    ch = channel_scales(w, layer) if w.kv_dtype in CHANNEL_CODE_MAX else None
+    return ops.allocate_pools(num_blocks, w.num_kv_heads, w.head_dim, storage_dtype(w.kv_dtype), device, 0xFF,
+                              channel_scales=ch)
 
 
 def fill(w, lay, pools, ksrc, vsrc, tables_dev, chunk=1 << 18, hold_last=False):
