@@ -108,6 +108,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   constexpr int NT = D / 16;              // 16-dim output tiles
   constexpr int VW = EB;                  // V words per lane per tile (4 tokens)
   constexpr bool CH = is_channel_scaled(KVT);   // static per-channel scales, folded into q and the output
+  constexpr bool BIAS = code_biased<KVT>();      // INT8 operands are code + kInt8Bias
   constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16)) && !CH;
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
@@ -164,9 +165,21 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
       }
     }
   }
+  // Biased K operands add kInt8Bias * (sum of head c's q operand values) to every logit.
+  float qbias = 0.f;
+  if constexpr (BIAS) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < QW; ++w) {
+      sum += from_op16<F16>(qhi[w] & 0xffffu) + from_op16<F16>(qhi[w] >> 16);
+      if constexpr (QSPLIT) sum += from_op16<F16>(qlo[w] & 0xffffu) + from_op16<F16>(qlo[w] >> 16);
+    }
+    qbias = kInt8Bias * row_sum4(sum);
+  }
 
   float m_run = -INFINITY;   // reference max of this head's base-2 logits (same in all 4 rows)
   float l_run = 0.f;         // this lane's share of the exp-sum
+  float p_run = 0.f;         // biased V operands: this lane's share of the sum of P operand values
   f32x4 acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -247,7 +260,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     bool valid[4] = {true, true, true, true};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = sacc[e] * a.scale_log2;
+      x[e] = (BIAS ? sacc[e] - qbias : sacc[e]) * a.scale_log2;
       if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
     }
     if (!full) {
@@ -284,6 +297,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
       const float m_new = need ? mb : m_run;
       const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);   // 0 on the first block
       l_run *= alpha;
+      if constexpr (BIAS) p_run *= alpha;
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] *= alpha;
       m_run = m_new;
@@ -330,6 +344,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
           h1 = __float_as_uint(f1) >> 16;
           l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
           l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
+          if constexpr (BIAS) p_run += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
         }
         ph[w] = h0 | (h1 << 16);
         pl[w] = l0 | (l1 << 16);
@@ -398,6 +413,11 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 
   l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
   if (bad) l_run = __builtin_nanf("");
+  if constexpr (BIAS) {      // biased V operands added kInt8Bias * sum_p P_p to every output dim
+    const float vbias = kInt8Bias * row_sum4(p_run);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] -= vbias;
+  }
   if (!head_ok) return;
   if constexpr (CH) {   // V's channel scales: sum_p P_p (code_p * s) = s * sum_p P_p code_p
 #pragma unroll

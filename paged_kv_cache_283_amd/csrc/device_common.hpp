@@ -63,24 +63,32 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32
   hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
-// Four int8 codes (one word, two's complement) -> four bf16 values (two words;
-// byte 0 in the low half of lo), exactly: |code| <= 128 needs 8 significant
-// bits.  XOR 0x80 turns each code into code + 128 as an unsigned byte, which
-// v_cvt_f32_ubyte* converts; subtracting 128 is exact.
-__device__ __forceinline__ void int8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+// Four int8 codes (one word, two's complement) -> four bf16 values code + 128
+// (two words; byte 0 in the low half of lo), exactly: 0..255 needs 8
+// significant bits.  XOR 0x80 turns each code into the unsigned byte
+// code + 128, v_cvt_f32_ubyte* converts it, and one v_perm_b32 per pair keeps
+// the two high halves.  The attention kernels take the bias out of their sums
+// (q . (c + 128) = q . c + 128 sum q; sum_p P_p (c_p + 128) = sum_p P_p c_p +
+// 128 sum_p P_p), so no per-code subtraction is needed.
+constexpr float kInt8Bias = 128.f;
+__device__ __forceinline__ void int8x4_to_bf16x4_biased(uint32_t w, uint32_t& lo, uint32_t& hi) {
   const uint32_t b = w ^ 0x80808080u;
-  const float f0 = (float)(b & 0xffu) - 128.f;
-  const float f1 = (float)((b >> 8) & 0xffu) - 128.f;
-  const float f2 = (float)((b >> 16) & 0xffu) - 128.f;
-  const float f3 = (float)(b >> 24) - 128.f;
-  lo = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  hi = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xffff0000u);
+  const float f0 = (float)(b & 0xffu);
+  const float f1 = (float)((b >> 8) & 0xffu);
+  const float f2 = (float)((b >> 16) & 0xffu);
+  const float f3 = (float)(b >> 24);
+  // bytes 2, 3 of src1 then bytes 2, 3 of src0 (src1 is bytes 0-3 of the pair)
+  lo = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
 
-// 8-bit codes of storage format KV -> bf16 operands.
+// 8-bit codes of storage format KV -> bf16 MFMA operands: E4M3 values exactly,
+// INT8 codes biased by kInt8Bias (code_biased<KV>).
+template <int KV>
+__host__ __device__ constexpr bool code_biased() { return code_set(KV) == DT_INT8; }
 template <int KV>
 __device__ __forceinline__ void code8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  if constexpr (code_set(KV) == DT_INT8) int8x4_to_bf16x4(w, lo, hi);
+  if constexpr (code_biased<KV>()) int8x4_to_bf16x4_biased(w, lo, hi);
   else fp8x4_to_bf16x4(w, lo, hi);
 }
 

@@ -59,6 +59,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   constexpr int NT = D / 16;
   constexpr int VW = EB;
   constexpr bool CH = is_channel_scaled(KVT);   // static per-channel scales, folded into q and the output
+  constexpr bool BIAS = code_biased<KVT>();      // INT8 operands are code + kInt8Bias
   constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16)) && !CH;
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;
@@ -143,10 +144,28 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     }
   }
 
+  // Biased K operands add kInt8Bias * (sum of the column's q operand values) to every logit.
+  float qbias[CS];
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) {
+    qbias[cs] = 0.f;
+    if constexpr (BIAS) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < QW; ++w) {
+        sum += from_op16<F16>(qhi[cs][w] & 0xffffu) + from_op16<F16>(qhi[cs][w] >> 16);
+        if constexpr (QSPLIT) sum += from_op16<F16>(qlo[cs][w] & 0xffffu) + from_op16<F16>(qlo[cs][w] >> 16);
+      }
+      qbias[cs] = kInt8Bias * row_sum4(sum);
+    }
+  }
+
   float m_run[CS], l_run[CS];
+  float p_run[CS];   // biased V operands: this lane's share of the sum of P operand values
   f32x4 acc[CS][NT];
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) {
+    p_run[cs] = 0.f;
     m_run[cs] = -INFINITY;
     l_run[cs] = 0.f;
 #pragma unroll
@@ -253,7 +272,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       float x[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[e] = sacc[cs][e] * a.scale_log2;
+        x[e] = (BIAS ? sacc[cs][e] - qbias[cs] : sacc[cs][e]) * a.scale_log2;
         if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
         if (!full) x[e] = blk0 + 4 * j + e <= pos[cs] ? x[e] : -INFINITY;
       }
@@ -263,6 +282,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         const float m_new = need ? mb : m_run[cs];
         const float alpha = m_new == m_run[cs] ? 1.f : fast_exp2(m_run[cs] - m_new);
         l_run[cs] *= alpha;
+        if constexpr (BIAS) p_run[cs] *= alpha;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[cs][t] *= alpha;
         m_run[cs] = m_new;
@@ -292,6 +312,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
             h1 = __float_as_uint(f1) >> 16;
             l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
             l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
+            if constexpr (BIAS)
+              p_run[cs] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
           }
           ph[cs][w] = h0 | (h1 << 16);
           pl[cs][w] = l0 | (l1 << 16);
@@ -373,12 +395,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   for (int cs = 0; cs < CS; ++cs) {
     float l = row_sum4(l_run[cs]);
     if (bad) l = __builtin_nanf("");
+    const float vbias = BIAS ? kInt8Bias * row_sum4(p_run[cs]) : 0.f;   // biased V operands
     if (!col_ok[cs]) continue;
     const size_t orow = ((size_t)(q0 + tok[cs]) * hq + head) * D;
     const float inv = 1.f / l;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f32x4 o = acc[cs][t];
+      if constexpr (BIAS) o -= vbias;
       if constexpr (CH) o *= *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)kvh * D + 16 * t + 4 * j);
 #pragma unroll
       for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, o[e] * inv);
