@@ -23,6 +23,8 @@
 // the tiles come from HBM once and from the caches for the other waves.  Work
 // is split by query token only: every wave covers the whole causal range of
 // its tokens.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_ops.hpp"
@@ -40,9 +42,7 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #ifndef PKV_PREFILL_SETS
 #define PKV_PREFILL_SETS 2                // 16-column query sets per wave for long chunks
 #endif
-#ifndef PKV_PREFILL_PIPE
-#define PKV_PREFILL_PIPE 2                // K/V register buffers per wave (2 or 3); 2 keeps two waves per SIMD
-#endif
+
 
 namespace {
 
@@ -184,57 +184,70 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   int c0 = 0;
 
   struct Regs {
-    uint32_t k[KW];
-    uint32_t v[NT][VW];
+    // Held as the loaded 16-byte vectors: operands are then built by element
+    // selects, never through a word array the compiler could widen into
+    // memory accesses.
+    u32x4 kq[KW / 4];
+    u32x4 vq[NT * VW / 4];
+    __device__ uint32_t k(int w) const { return kq[w / 4][w % 4]; }
+    __device__ uint32_t v(int t, int e) const { return vq[(t * VW + e) / 4][(t * VW + e) % 4]; }
+    __device__ void set_v(int t, int e, uint32_t x) { vq[(t * VW + e) / 4][(t * VW + e) % 4] = x; }
     f32x4 ks, vs;
     bool ok;
   };
 
-  auto load = [&](Regs& r, int i) {
+  // Loads of block i's tiles into r (K and V halves separately, so a step can
+  // refill K while it still uses V).  An entry outside the pool reads block 0
+  // instead (in bounds) and marks r bad.
+  auto tile_of = [&](Regs& r, int i) {
     const int phys = __builtin_amdgcn_readfirstlane(s_tab[i]);
     r.ok = phys >= 0 && phys < a.num_blocks;
-    const size_t tile_i = (size_t)(r.ok ? phys : 0) * hkv + kvh;   // block 0 stands in for a bad entry
+    return (size_t)(r.ok ? phys : 0) * hkv + kvh;
+  };
+  auto load_k = [&](Regs& r, int i) {
+    const size_t tile_i = tile_of(r, i);
     const uint8_t* kt = kbase + tile_i * (size_t)(kBlockSize * D * EB);
 #pragma unroll
     for (int w = 0; w < KW / 4; ++w) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(kt + ((size_t)(4 * w + j) * kBlockSize + c) * 16);
-      r.k[4 * w + 0] = v[0]; r.k[4 * w + 1] = v[1]; r.k[4 * w + 2] = v[2]; r.k[4 * w + 3] = v[3];
+      r.kq[w] = v;
     }
+    if constexpr (is_quantised(KVT)) r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile_i * kBlockSize + 4 * j);
+  };
+  auto load_v = [&](Regs& r, int i) {
+    const size_t tile_i = tile_of(r, i);
     const uint8_t* vt = vbase + tile_i * (size_t)(kBlockSize * D * EB);
-    uint32_t* vw = &r.v[0][0];
 #pragma unroll
     for (int g = 0; g < NT * VW / 4; ++g) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(vt + ((size_t)(g * 16 + c) * 4 + j) * 16);
-      vw[4 * g + 0] = v[0]; vw[4 * g + 1] = v[1]; vw[4 * g + 2] = v[2]; vw[4 * g + 3] = v[3];
+      r.vq[g] = v;
     }
-    if constexpr (is_quantised(KVT)) {
-      r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile_i * kBlockSize + 4 * j);
-      r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile_i * kBlockSize + 4 * j);
-    }
+    if constexpr (is_quantised(KVT)) r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile_i * kBlockSize + 4 * j);
+  };
+  auto load = [&](Regs& r, int i) {
+    load_k(r, i);
+    load_v(r, i);
   };
 
-  auto compute = [&](Regs& r, int i) {
-    bad |= !r.ok;
-    const int blk0 = (c0 + i) * kBlockSize;
-    // ---- S = K q^T for every column set, sharing the converted K operand
-    f32x4 sacc[CS];
+  // S = K q^T of one block for every column set, sharing the converted K operand.
+  auto qk = [&](const Regs& r, f32x4* sacc) {
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) sacc[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (OP32) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) sacc[cs] = mfma_f32_k4(__uint_as_float(r.k[e]), qf[cs][e], sacc[cs]);
+        for (int cs = 0; cs < CS; ++cs) sacc[cs] = mfma_f32_k4(__uint_as_float(r.k(e)), qf[cs][e], sacc[cs]);
       }
     } else {
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
         if constexpr (is_code8(KVT)) {
-          code8x4_to_bf16x4<KVT>(r.k[2 * st], av[0], av[1]);
-          code8x4_to_bf16x4<KVT>(r.k[2 * st + 1], av[2], av[3]);
+          code8x4_to_bf16x4<KVT>(r.k(2 * st), av[0], av[1]);
+          code8x4_to_bf16x4<KVT>(r.k(2 * st + 1), av[2], av[3]);
         } else {
-          av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
+          av[0] = r.k(4 * st); av[1] = r.k(4 * st + 1); av[2] = r.k(4 * st + 2); av[3] = r.k(4 * st + 3);
         }
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs) {
@@ -243,40 +256,96 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         }
       }
     }
-    // ---- keys past the context (the unused tail of the last block): V zeroed
-    const bool full = blk0 + kBlockSize <= all_visible;
-    bool in_ctx[4] = {true, true, true, true};
-    if (!full) {
+  };
+
+  // Keys past the context (the unused tail of the last block): V zeroed.
+  auto mask_tail = [&](Regs& r, int blk0, bool* in_ctx) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) in_ctx[e] = blk0 + 4 * j + e < L;
+    for (int e = 0; e < 4; ++e) in_ctx[e] = blk0 + 4 * j + e < L;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if constexpr (VW == 1) {
-          const uint32_t msk = (in_ctx[0] ? 0xffu : 0u) | (in_ctx[1] ? 0xff00u : 0u) |
-                               (in_ctx[2] ? 0xff0000u : 0u) | (in_ctx[3] ? 0xff000000u : 0u);
-          r.v[t][0] &= msk;
-        } else if constexpr (VW == 2) {
-          r.v[t][0] &= (in_ctx[0] ? 0xffffu : 0u) | (in_ctx[1] ? 0xffff0000u : 0u);
-          r.v[t][1] &= (in_ctx[2] ? 0xffffu : 0u) | (in_ctx[3] ? 0xffff0000u : 0u);
-        } else {
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (VW == 1) {
+        const uint32_t msk = (in_ctx[0] ? 0xffu : 0u) | (in_ctx[1] ? 0xff00u : 0u) |
+                             (in_ctx[2] ? 0xff0000u : 0u) | (in_ctx[3] ? 0xff000000u : 0u);
+        r.set_v(t, 0, r.v(t, 0) & msk);
+      } else if constexpr (VW == 2) {
+        r.set_v(t, 0, r.v(t, 0) & ((in_ctx[0] ? 0xffffu : 0u) | (in_ctx[1] ? 0xffff0000u : 0u)));
+        r.set_v(t, 1, r.v(t, 1) & ((in_ctx[2] ? 0xffffu : 0u) | (in_ctx[3] ? 0xffff0000u : 0u)));
+      } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) r.v[t][e] = in_ctx[e] ? r.v[t][e] : 0u;
-        }
+        for (int e = 0; e < 4; ++e) r.set_v(t, e, in_ctx[e] ? r.v(t, e) : 0u);
       }
     }
+  };
+
+  // V tile t of one block as the 16-bit PV A operand (two words: tokens 4j..4j+3 of dim 16t + c).
+  auto v_operand = [&](const Regs& r, int t, uint32_t& v0, uint32_t& v1) {
+    if constexpr (is_code8(KVT)) {
+      code8x4_to_bf16x4<KVT>(r.v(t, 0), v0, v1);
+    } else {
+      v0 = r.v(t, 0);
+      v1 = r.v(t, 1);
+    }
+  };
+
+  // One step over the blocks i (ra) and i + 1 (rb, only if has_b): QK, the
+  // online softmax over the step's keys, PV.  Each PV MFMA is a 16x16x32 whose
+  // 32 keys are both blocks' 16: lane (c, j) holds tokens 4j..4j+3 of block i,
+  // then of block i + 1, in the V operand and the probability operand alike,
+  // so the contraction pairs them correctly and one instruction does the work
+  // of two 16x16x16 ones (which run at half the rate per flop on gfx950).
+  // Without a second block its logits are -inf and its V operand zero.
+  // With refill, the next pair's K loads (blocks i + 2, i + 3) are issued as
+  // soon as this step's QK MFMAs have consumed K.
+  constexpr int NB = 2;
+  auto compute = [&](Regs& ra, Regs& rb, int i, bool has_b, bool refill) {
+    // (ra and rb are named explicitly, never selected by index: a reference
+    // chosen at run time would keep the register buffers in memory.)
+    f32x4 sacc[NB][CS];
+    bool full[NB];
+    bool in_ctx[NB][4];
+    int blk0[NB];
+    float ksc[NB][4], vsc[NB][4];
+    bad |= !ra.ok || (has_b && !rb.ok);
+    blk0[0] = (c0 + i) * kBlockSize;
+    blk0[1] = blk0[0] + kBlockSize;
+    qk(ra, sacc[0]);
+    qk(rb, sacc[1]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ksc[0][e] = is_quantised(KVT) ? ra.ks[e] : 1.f;
+      ksc[1][e] = is_quantised(KVT) ? rb.ks[e] : 1.f;
+      vsc[0][e] = is_quantised(KVT) ? ra.vs[e] : 1.f;
+      vsc[1][e] = is_quantised(KVT) ? rb.vs[e] : 1.f;
+      in_ctx[0][e] = in_ctx[1][e] = true;
+    }
+    if (refill) {
+      load_k(ra, i + 2);
+      load_k(rb, i + 3);
+    }
+    full[0] = blk0[0] + kBlockSize <= all_visible;
+    full[1] = blk0[1] + kBlockSize <= all_visible && has_b;
+    if (!full[0]) mask_tail(ra, blk0[0], in_ctx[0]);
+    if (!full[1]) mask_tail(rb, has_b ? blk0[1] : L, in_ctx[1]);   // an absent block lies wholly past L
     // ---- per column set: causal mask, online softmax, probabilities as PV operands
-    uint32_t ph[CS][2], pl[CS][2];
-    float pvv[CS][4];
+    uint32_t ph[CS][2 * NB], pl[CS][2 * NB];
+    float pvv[CS][NB][4];
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
-      float x[4];
+      float x[NB][4];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = (BIAS ? sacc[cs][e] - qbias[cs] : sacc[cs][e]) * a.scale_log2;
-        if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
-        if (!full) x[e] = blk0 + 4 * j + e <= pos[cs] ? x[e] : -INFINITY;
+      for (int b = 0; b < NB; ++b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = (BIAS ? sacc[b][cs][e] - qbias[cs] : sacc[b][cs][e]) * a.scale_log2;
+          if constexpr (is_quantised(KVT)) v *= ksc[b][e];
+          if (!full[b]) v = in_ctx[b][e] && blk0[b] + 4 * j + e <= pos[cs] ? v : -INFINITY;
+          x[b][e] = v;
+        }
+        mx = fmaxf(mx, fmaxf(fmaxf(x[b][0], x[b][1]), fmaxf(x[b][2], x[b][3])));
       }
-      const float mb = row_max4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      const float mb = row_max4(mx);
       const bool need = mb > m_run[cs] + kPfRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
         const float m_new = need ? mb : m_run[cs];
@@ -288,35 +357,38 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         m_run[cs] = m_new;
       }
       const float mref = m_run[cs] == -INFINITY ? 0.f : m_run[cs];
-      float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[e] - mref);
-      l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      for (int b = 0; b < NB; ++b) {
+        float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (is_quantised(KVT)) pvv[cs][e] = in_ctx[e] ? pr[e] * r.vs[e] : 0.f;
-        else pvv[cs][e] = pr[e];
-      }
-      if constexpr (!OP32) {
+        for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[b][e] - mref);
+        l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const float f0 = pvv[cs][2 * w], f1 = pvv[cs][2 * w + 1];
-          uint32_t h0, h1, l0, l1;
-          if constexpr (F16) {
-            h0 = f32_to_f16_bits(f0);
-            h1 = f32_to_f16_bits(f1);
-            l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
-            l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
-          } else {
-            h0 = __float_as_uint(f0) >> 16;
-            h1 = __float_as_uint(f1) >> 16;
-            l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
-            l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
-            if constexpr (BIAS)
-              p_run[cs] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (is_quantised(KVT)) pvv[cs][b][e] = in_ctx[b][e] ? pr[e] * vsc[b][e] : 0.f;
+          else pvv[cs][b][e] = pr[e];
+        }
+        if constexpr (!OP32) {
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const float f0 = pvv[cs][b][2 * w], f1 = pvv[cs][b][2 * w + 1];
+            uint32_t h0, h1, l0, l1;
+            if constexpr (F16) {
+              h0 = f32_to_f16_bits(f0);
+              h1 = f32_to_f16_bits(f1);
+              l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
+              l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
+            } else {
+              h0 = __float_as_uint(f0) >> 16;
+              h1 = __float_as_uint(f1) >> 16;
+              l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
+              l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
+              if constexpr (BIAS)
+                p_run[cs] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+            }
+            ph[cs][2 * b + w] = h0 | (h1 << 16);
+            pl[cs][2 * b + w] = l0 | (l1 << 16);
           }
-          ph[cs][w] = h0 | (h1 << 16);
-          pl[cs][w] = l0 | (l1 << 16);
         }
       }
     }
@@ -327,26 +399,34 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
-          for (int cs = 0; cs < CS; ++cs) acc[cs][t] = mfma_f32_k4(__uint_as_float(r.v[t][e]), pvv[cs][e], acc[cs][t]);
+          for (int cs = 0; cs < CS; ++cs) {
+            acc[cs][t] = mfma_f32_k4(__uint_as_float(ra.v(t, e)), pvv[cs][0][e], acc[cs][t]);
+            acc[cs][t] = mfma_f32_k4(__uint_as_float(rb.v(t, e)), pvv[cs][1][e], acc[cs][t]);
+          }
         }
       }
     } else {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        uint32_t v0, v1;
-        if constexpr (is_code8(KVT)) {
-          code8x4_to_bf16x4<KVT>(r.v[t][0], v0, v1);
-        } else {
-          v0 = r.v[t][0];
-          v1 = r.v[t][1];
-        }
+        uint32_t av[4];
+        v_operand(ra, t, av[0], av[1]);
+        v_operand(rb, t, av[2], av[3]);
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs) {
-          acc[cs][t] = mfma_k16<F16>(v0, v1, ph[cs][0], ph[cs][1], acc[cs][t]);
-          acc[cs][t] = mfma_k16<F16>(v0, v1, pl[cs][0], pl[cs][1], acc[cs][t]);
+          acc[cs][t] = mfma_k32<F16>(av, ph[cs], acc[cs][t]);
+          acc[cs][t] = mfma_k32<F16>(av, pl[cs], acc[cs][t]);
         }
       }
     }
+  };
+  // An absent second block: defined (zero) operands; its keys are masked.
+  auto clear = [&](Regs& r) {
+#pragma unroll
+    for (int w = 0; w < KW / 4; ++w) r.kq[w] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < NT * VW / 4; ++g) r.vq[g] = u32x4{0u, 0u, 0u, 0u};
+    r.ks = r.vs = f32x4{0.f, 0.f, 0.f, 0.f};
+    r.ok = true;
   };
 
   for (; c0 < n_blocks; c0 += kPfTab) {
@@ -355,39 +435,25 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#if PKV_PREFILL_PIPE == 2
-    Regs ra, rb;
-    int i = 0;
-    if (n > 0) load(ra, 0);
-    for (; i + 2 < n; i += 2) {
-      load(rb, i + 1);
-      compute(ra, i);
-      load(ra, i + 2);
-      compute(rb, i + 1);
-    }
-    if (i + 1 < n) load(rb, i + 1);
-    if (i < n) compute(ra, i);
-    if (i + 1 < n) compute(rb, i + 1);
-#else
-    Regs r0, r1, r2;
+    // Pairs of blocks in two buffers: the next pair's K loads are issued as
+    // soon as the QK MFMAs have consumed K, its V loads once PV has consumed V.
+    Regs r0, r1;
     int i = 0;
     if (n > 0) load(r0, 0);
     if (n > 1) load(r1, 1);
-    for (; i + 4 < n; i += 3) {
-      load(r2, i + 2);
-      compute(r0, i);
-      load(r0, i + 3);
-      compute(r1, i + 1);
-      load(r1, i + 4);
-      compute(r2, i + 2);
+    for (; i + 3 < n; i += 2) {   // steady state: the next pair exists, loads unconditional
+      compute(r0, r1, i, true, true);
+      load_v(r0, i + 2);
+      load_v(r1, i + 3);
     }
-    if (i + 2 < n) load(r2, i + 2);
-    if (i < n) compute(r0, i);
-    if (i + 3 < n) load(r0, i + 3);
-    if (i + 1 < n) compute(r1, i + 1);
-    if (i + 2 < n) compute(r2, i + 2);
-    if (i + 3 < n) compute(r0, i + 3);
-#endif
+    const int rem = n - i;        // 0..3 blocks left; r0, r1 hold blocks i, i + 1 where they exist
+    if (rem >= 2) compute(r0, r1, i, true, false);
+    if (rem % 2) {                // one block left over: paired with an absent one
+      Regs rz;
+      clear(rz);
+      if (rem == 3) load(r0, i + 2);
+      compute(r0, rz, rem == 3 ? i + 2 : i, false, false);
+    }
     __builtin_amdgcn_wave_barrier();   // the next chunk rewrites this wave's s_tab
   }
 
