@@ -95,9 +95,12 @@ def cpu_baseline(w, lay, ksrc, vsrc, q, seconds):
     import torch
 
     from oracle import attention, policies
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas")
     except Exception:  # noqa: BLE001
         threads = len(os.sched_getaffinity(0))
     per_tok = kv_bytes_per_token(w)
@@ -127,7 +130,7 @@ def cpu_baseline(w, lay, ksrc, vsrc, q, seconds):
             if time.perf_counter() - t0 >= seconds:
                 break
     dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle", "blas": blas,
             "sample": f"{n_seq} sequence-decodes of the {w.name} workload ({len(sample)} distinct sequences, "
                       f"{done_bytes / 1e9:.2f} GB of KV) in {dt:.1f} s, numpy float64, bf16->f64 decode included",
             "seconds": round(dt, 2)}

@@ -360,6 +360,34 @@ def test_h2o_mass_with_streaming_keep_set():
         assert np.max(np.abs(got[keep] - exp[keep]) / exp[keep]) <= 1e-4
 
 
+def test_tiny_h2o_sub_case_budget_24_recent_8():
+    """The tiny workload's H2O sub-case: four decode steps accumulate the mass on the GPU, then the
+    GPU keep-set (budget 24, recent 8) equals the oracle's selection on the oracle's own mass, taken
+    in fp32 like the kernel's.  Where two candidates are closer than the mass tolerance the order
+    may legitimately differ; the test asserts there is no such near-tie at the cut here."""
+    w = W.WORKLOADS["tiny"]
+    case = H.Case(w)
+    maxl = case.lay.max_len
+    scores = torch.zeros((2, maxl), dtype=torch.float32, device="cuda")
+    acc = np.zeros((2, maxl))
+    for step in range(4):
+        q = W.queries(w, step=step, device="cuda")
+        case.attend(q=q, attn_mass=scores)
+        for s in range(2):
+            _, probs = case.oracle(s, q=q)
+            acc[s, : probs.shape[1]] += attention.head_mean_mass(probs)
+    idx, cnt = ops.h2o_select(scores, case.lens, maxl, 24, 8)
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for s in range(2):
+        L = int(case.lay.lens[s])
+        ref = policies.h2o_select(acc[s].astype(np.float32), L, 24, 8)
+        assert cnt[s] == ref.size and idx[s, : ref.size].tolist() == ref.tolist(), s
+        if L > 24:                                    # the cut among candidates is not a near-tie
+            cand = np.sort(acc[s, : L - 8])[::-1]
+            assert cand[15] - cand[16] > 1e-4 * cand[15]
+    assert cnt.tolist() == [24, 24]
+
+
 def test_h2o_select_bit_exact():
     rng = np.random.default_rng(5)
     B, maxl = 24, 3000
