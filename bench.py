@@ -270,6 +270,59 @@ def bench_prefill(args, dev, stream):
         "tokens_per_s": round(w.num_seqs * w.chunk / (t * 1e-3), 1)}), flush=True)
 
 
+def bench_fill(args, dev, stream, copy_gbs):
+    """Bulk cache write (a prefill's or a whole prompt's K/V): every position of the workload's layout
+    in one paged_kv_write call with precomputed slots.  Algorithmic bytes per token: the source rows
+    read plus the stored rows (and per-token scales) written, K and V."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from workloads import device as H
+    from paged_kv_cache_283_amd import ops
+
+    w = W.WORKLOADS[args.workload]
+    lay = W.make_layout(w)
+    tables = torch.from_numpy(lay.tables).to(dev)
+    pools = H.make_pools(w, lay.num_blocks)
+    ksrc, vsrc = W.kv_source(w, lay, device=dev)
+    seq, pos, rows = lay.fill_tokens()
+    r = torch.from_numpy(rows).to(dev)
+    k_rows, v_rows = ksrc.index_select(0, r).contiguous(), vsrc.index_select(0, r).contiguous()
+    del ksrc, vsrc
+    slots = ops.paged_token_slots(tables, torch.from_numpy(seq).to(dev), torch.from_numpy(pos).to(dev),
+                                  lay.num_blocks)
+    k, v, ks, vs = pools
+    call = ops.paged_kv_write(k_rows, v_rows, k, v, slots, ks, vs, stream=stream, prepare=True)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for ev in evs:
+        ev[0].record(stream)
+        call()
+        ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([ev[0].elapsed_time(ev[1]) for ev in evs])
+    t = float(np.median(ms))
+    n_tok = int(seq.size)
+    src_eb = k_rows.element_size()
+    per_tok = w.num_kv_heads * w.head_dim * 2 * src_eb + kv_bytes_per_token(w)
+    gbs = n_tok * per_tok / (t * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "bulk paged KV write (slot mapping precomputed): GB/s of source read + cache written",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": f"fill-{WORKLOAD_NAMES[args.workload]}", "tokens": n_tok,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "src_dtype": w.src_dtype,
+                   "kv_dtype": w.kv_dtype},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "bytes_per_token": per_tok, "write_kernel_avg_us": round(1e3 * float(np.mean(ms)), 2),
+        "probe_copy_gbs": round(copy_gbs, 1), "frac_of_probe_copy": round(gbs / copy_gbs, 4)}), flush=True)
+
+
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
 
 
@@ -330,10 +383,10 @@ def main():
     ap.add_argument("--probe-only", action="store_true", help="run only the HBM read/copy probes")
     ap.add_argument("--contiguous-blocks", action="store_true", help="hand out physical blocks in order "
                     "instead of the shuffled placement (comparison only)")
-    ap.add_argument("--op", default="decode", choices=("decode", "evict", "prefill", "swap"),
+    ap.add_argument("--op", default="decode", choices=("decode", "evict", "prefill", "swap", "fill"),
                     help="decode: the decode step (default); evict: H2O keep-set + compaction on the h2o "
                          "workload; prefill: causal multi-query attention on the prefill workload; swap: "
-                         "4096 blocks to pinned host memory and back")
+                         "4096 blocks to pinned host memory and back; fill: bulk cache write of --workload")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -389,6 +442,9 @@ def main():
         return
     if args.op == "swap":
         bench_swap(args, dev, stream)
+        return
+    if args.op == "fill":
+        bench_fill(args, dev, stream, copy_gbs)
         return
 
     # ---- workload: pools filled through the library's own write path (untimed prefill)

@@ -126,7 +126,8 @@ int paged_token_slots(const int32_t* block_tables, int block_table_stride, int n
  * and the scale is stored beside the codes.  The _CHANNEL formats store
  *     code  = E4M3FN(x / scale[h][d])  or  clamp(rint(x / scale[h][d]), -127, 127)
  *                                 (fp32 division) and leave the scales alone.
- *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of src_dtype
+ *   k_new, v_new   [num_tokens][num_kv_heads][head_dim] of src_dtype; these and the
+ *                  pools 16-byte aligned (PKV_EINVAL otherwise)
  *   kv_dtype       PKV_F32/BF16/F16 require src_dtype == kv_dtype (bytes are copied);
  *                  the 8-bit formats take src_dtype F32, BF16 or F16 (finite values)
  *   k_scale, v_scale   required for the 8-bit formats (written for per-token
@@ -144,7 +145,7 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype,
  * sequence s, the new token (k_new[s], v_new[s]) goes to logical position
  * context_lens[s] - 1 through block_tables[s] ([PA] "PagedAttention 的设计": the
  * token lands in block table[p / 16] at offset p % 16).  Same stores, FP8
- * quantisation and dtype rules as paged_kv_write with the slots that
+ * quantisation, dtype and alignment rules as paged_kv_write with the slots that
  * paged_decode_slots computes; a sequence whose slot would be -1 there (length
  * outside [1, 16 * stride], table entry outside [0, num_blocks)) is skipped.
  *   k_new, v_new   [num_seqs][num_kv_heads][head_dim] of src_dtype

@@ -120,12 +120,14 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_
   if (!code8_kv(kv_dtype) && src_dtype != kv_dtype)
     return fail(PKV_EUNSUPPORTED, "a non-quantised pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
   if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
-  if (num_kv_heads < 1) return fail(PKV_EINVAL, "num_kv_heads %d < 1", num_kv_heads);
+  if (num_kv_heads < 1 || num_kv_heads > 65535) return fail(PKV_EINVAL, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
   if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
   if ((long long)num_tokens * num_kv_heads > (1LL << 32))
     return fail(PKV_EINVAL, "num_tokens * num_kv_heads too large");
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return fail(PKV_EINVAL, "NULL array argument");
+  if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16)
+    return fail(PKV_EINVAL, "k_new, v_new and the pools must be 16-byte aligned");
   if (code8_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
   return device_status(pkv::launch_kv_write(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                             slot_mapping, num_tokens, num_blocks, num_kv_heads, head_dim,
@@ -144,7 +146,7 @@ int paged_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k
   if (!code8_kv(kv_dtype) && src_dtype != kv_dtype)
     return fail(PKV_EUNSUPPORTED, "a non-quantised pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
   if (num_seqs < 0) return fail(PKV_EINVAL, "num_seqs %d < 0", num_seqs);
-  if (num_kv_heads < 1) return fail(PKV_EINVAL, "num_kv_heads %d < 1", num_kv_heads);
+  if (num_kv_heads < 1 || num_kv_heads > 65535) return fail(PKV_EINVAL, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
   if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
   if (block_table_stride < 1 || block_table_stride > (1 << 26))
     return fail(PKV_EINVAL, "block_table_stride %d outside [1, 2^26]", block_table_stride);
@@ -152,6 +154,8 @@ int paged_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k
   if (num_seqs == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "NULL array argument");
+  if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16)
+    return fail(PKV_EINVAL, "k_new, v_new and the pools must be 16-byte aligned");
   if (code8_kv(kv_dtype) && (!k_scale || !v_scale)) return fail(PKV_EINVAL, "FP8/INT8 pools need k_scale and v_scale");
   return device_status(pkv::launch_kv_append(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                              block_tables, block_table_stride, context_lens, num_seqs, num_blocks,

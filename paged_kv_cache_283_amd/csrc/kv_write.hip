@@ -37,13 +37,6 @@ __global__ void __launch_bounds__(256) token_slots_kernel(const int32_t* tables,
   slots[t] = (b < 0 || b >= num_blocks) ? (int64_t)-1 : (int64_t)b * kBlockSize + p % kBlockSize;
 }
 
-template <int SRC>
-__device__ __forceinline__ float src_to_f32(const void* p, size_t i) {
-  if constexpr (SRC == DT_F32) return reinterpret_cast<const float*>(p)[i];
-  else if constexpr (SRC == DT_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-  else return f16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
-}
-
 // One 8-bit code of the quotient x / scale: E4M3FN (round to nearest even,
 // saturating to +-448) or INT8 (nearest integer, ties to even -- v_rndne_f32 --
 // saturated to +-127, two's complement).
@@ -55,12 +48,6 @@ __device__ __forceinline__ uint32_t encode8(float q) {
   } else {
     return e4m3fn_encode(q);
   }
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
 }
 
 // Where token t goes: slots[t], or -- for the decode append -- position
@@ -80,77 +67,165 @@ __device__ __forceinline__ int64_t token_slot(const SlotSource& ss, int t, int n
   return (b < 0 || b >= num_blocks) ? (int64_t)-1 : (int64_t)b * kBlockSize + (L - 1) % kBlockSize;
 }
 
-// One wave per (token, KV head) row; K and V of the row handled together.
+// Value of a raw source element (16 or 32 bits, zero-extended).
+template <int SRC>
+__device__ __forceinline__ float raw_to_f32(uint32_t r) {
+  if constexpr (SRC == DT_F32) return __uint_as_float(r);
+  else if constexpr (SRC == DT_BF16) return bf16_to_f32(r);
+  else return f16_to_f32(r);
+}
+
+// Tokens staged per workgroup.
+constexpr int kWriteGroup = 16;
+
+// One workgroup per 16 consecutive tokens and one KV head.  The tokens' K and
+// V rows are staged in LDS, so the pool is written in whole 16-byte
+// chunks wherever the layout allows: a K chunk holds X dims of one token, so
+// every token's K goes out as D/X chunks whatever its slot; a V chunk holds 4
+// consecutive rows of a block, so the 4 tokens of such a quad go out as whole
+// chunks when all 4 are in this workgroup with consecutive slots (any
+// prefill or bulk fill), and element by element otherwise (a decode step:
+// one token per sequence).  8-bit formats quantise each row with its own
+// scale (absmax / largest code) or by the static channel scales.
 template <int SRC, int KVT, int D>
 __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                                                      float* k_scale, float* v_scale, const SlotSource ss,
                                                      int num_tokens, int num_blocks, int num_kv_heads) {
-  const int lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (long)num_tokens * num_kv_heads) return;
-  const int t = (int)(row / num_kv_heads);
-  const int h = (int)(row % num_kv_heads);
-  const int64_t slot = token_slot(ss, t, num_blocks);
-  if (slot < 0 || slot >= (int64_t)num_blocks * kBlockSize) return;
-  const size_t tile = (size_t)(slot / kBlockSize) * num_kv_heads + h;
-  const int o = (int)(slot % kBlockSize);
-  const size_t src = (size_t)row * D;
-  constexpr int PER = D / 64;
+  constexpr int EB = KVT == DT_F32 ? 4 : (is_code8(KVT) ? 1 : 2);   // bytes per stored element
+  constexpr int X = 16 / EB;                                       // elements per K chunk
+  constexpr int Y = 4 / EB;                                        // dims per V chunk
+  constexpr int kThreads = 256;
+  constexpr float kMaxCode = code_set(KVT) == DT_INT8 ? 127.f : 448.f;
+  // Raw source bits of K and V, one word per element; rows padded by one word
+  // so that threads reading the same dim of consecutive rows hit different
+  // LDS banks.
+  constexpr int kRow = D + 1;
+  __shared__ uint32_t s_src[2][kWriteGroup][kRow];   // [K, V][token][dim]
+  __shared__ int64_t s_slot[kWriteGroup];      // -1: token skipped
+  __shared__ float s_scale[2][kWriteGroup];
+  __shared__ int s_lead[kWriteGroup];          // V: 1 leads a complete quad, 2 is covered by one, 0 neither
+
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int t_base = blockIdx.x * kWriteGroup;
+  if (tid < kWriteGroup) {
+    const int t = t_base + tid;
+    int64_t sl = t < num_tokens ? token_slot(ss, t, num_blocks) : -1;
+    if (sl >= (int64_t)num_blocks * kBlockSize) sl = -1;
+    s_slot[tid] = sl < 0 ? -1 : sl;
+  }
+  __syncthreads();
+  if (tid < kWriteGroup) {
+    // Quad of rows 4k..4k+3 of one block held by tokens o..o+3 in slot order.
+    const int64_t sl = s_slot[tid];
+    bool lead = sl >= 0 && sl % 4 == 0 && tid + 3 < kWriteGroup;
+    for (int e = 1; lead && e < 4; ++e) lead = s_slot[tid + e] == sl + e;
+    s_lead[tid] = lead ? 1 : 0;
+  }
+  // Both rows of every token, with 16-byte loads: K and V, row o, elements
+  // [8 p, 8 p + 8) (16-bit source) or [4 p, 4 p + 4) (f32).
+  constexpr int kPer = 16 / (SRC == DT_F32 ? 4 : 2);
+  for (int e = tid; e < 2 * kWriteGroup * D / kPer; e += kThreads) {
+    const int kv = e / (kWriteGroup * D / kPer), r = e % (kWriteGroup * D / kPer);
+    const int o = r / (D / kPer), d0 = (r % (D / kPer)) * kPer;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (s_slot[o] >= 0)
+      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(kv == 0 ? k_new : v_new) +
+                                          (((size_t)(t_base + o) * num_kv_heads + h) * D + d0) * (16 / kPer));
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if constexpr (SRC == DT_F32) s_src[kv][o][d0 + i] = w[i];
+      else s_src[kv][o][d0 + i] = (w[i / 2] >> (16 * (i % 2))) & 0xffffu;
+    }
+  }
+  __syncthreads();
+  if (tid < kWriteGroup && s_lead[tid] == 0) {
+    for (int e = 1; e < 4 && tid - e >= 0; ++e)
+      if (s_lead[tid - e] == 1 && s_slot[tid - e] + e == s_slot[tid]) s_lead[tid] = 2;
+  }
   if constexpr (is_quantised(KVT)) {
-    constexpr float kMaxCode = KVT == DT_INT8 ? 127.f : 448.f;
-    float kx[PER], vx[PER];
-    float kmax = 0.f, vmax = 0.f;
+    // 8 threads per (K or V, row): absmax, then the row's scale
+    const int kv = tid / 128, o = (tid / 8) % kWriteGroup, l = tid % 8;
+    float m = 0.f;
+    for (int d = l; d < D; d += 8) m = fmaxf(m, fabsf(raw_to_f32<SRC>(s_src[kv][o][d])));
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      kx[e] = src_to_f32<SRC>(k_new, src + e * 64 + lane);
-      vx[e] = src_to_f32<SRC>(v_new, src + e * 64 + lane);
-      kmax = fmaxf(kmax, fabsf(kx[e]));
-      vmax = fmaxf(vmax, fabsf(vx[e]));
+    for (int off = 4; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
+    const float sc = __fdiv_rn(m, kMaxCode);
+    if (l == 0) {
+      s_scale[kv][o] = sc;
+      const int64_t sl = s_slot[o];
+      if (sl >= 0)
+        (kv == 0 ? k_scale : v_scale)[((size_t)(sl / kBlockSize) * num_kv_heads + h) * kBlockSize + sl % kBlockSize] = sc;
     }
-    kmax = wave_max(kmax);
-    vmax = wave_max(vmax);
-    const float ks = __fdiv_rn(kmax, kMaxCode);
-    const float vs = __fdiv_rn(vmax, kMaxCode);
-    uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool);
-    uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool);
+  }
+  __syncthreads();
+
+  // Stored bits of element (token o, dim d) of K (kv 0) or V (kv 1).
+  auto code_of = [&](int kv, int o, int d) -> uint32_t {
+    const uint32_t r = s_src[kv][o][d];
+    if constexpr (is_quantised(KVT)) {
+      const float sc = s_scale[kv][o];
+      return sc == 0.f ? 0u : encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(r), sc));
+    } else if constexpr (is_channel_scaled(KVT)) {
+      return encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(r), (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d]));
+    } else {
+      return r;   // same dtype as the source: the bits unchanged
+    }
+  };
+  // 16 bytes from 16 / EB element codes.
+  auto pack = [&](const uint32_t* el) {
+    u32x4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = e * 64 + lane;
-      const uint32_t kc = ks == 0.f ? 0u : encode8<KVT>(__fdiv_rn(kx[e], ks));
-      const uint32_t vc = vs == 0.f ? 0u : encode8<KVT>(__fdiv_rn(vx[e], vs));
-      kp[tile * kBlockSize * D + k_chunk_offset<1>(o, d)] = (uint8_t)kc;
-      vp[tile * kBlockSize * D + v_chunk_offset<1>(o, d)] = (uint8_t)vc;
+    for (int i = 0; i < 16 / EB; ++i) {
+      if constexpr (EB == 4) w[i] = el[i];
+      else w[i * EB / 4] |= (el[i] & ((1u << (EB * 8)) - 1u)) << ((i * EB * 8) % 32);
     }
-    if (lane == 0) {
-      k_scale[tile * kBlockSize + o] = ks;
-      v_scale[tile * kBlockSize + o] = vs;
-    }
-  } else if constexpr (is_channel_scaled(KVT)) {
-    // Static scales [Hkv][D]: the code of x / scale[h][d] (fp32 division).
-    uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool);
-    uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool);
+    return w;
+  };
+  uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool);
+  uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool);
+
+  // K: chunk c of token o = dims c X .. c X + X - 1 at [c][row][*] of its tile
+  for (int q = tid; q < kWriteGroup * (D / X); q += kThreads) {
+    const int o = q % kWriteGroup, c = q / kWriteGroup;
+    const int64_t sl = s_slot[o];
+    if (sl < 0) continue;
+    uint32_t el[16 / EB];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = e * 64 + lane;
-      const float kx = src_to_f32<SRC>(k_new, src + d);
-      const float vx = src_to_f32<SRC>(v_new, src + d);
-      const uint32_t kc = encode8<KVT>(__fdiv_rn(kx, k_scale[(size_t)h * D + d]));
-      const uint32_t vc = encode8<KVT>(__fdiv_rn(vx, v_scale[(size_t)h * D + d]));
-      kp[tile * kBlockSize * D + k_chunk_offset<1>(o, d)] = (uint8_t)kc;
-      vp[tile * kBlockSize * D + v_chunk_offset<1>(o, d)] = (uint8_t)vc;
-    }
-  } else {
-    using T = typename std::conditional<KVT == DT_F32, uint32_t, uint16_t>::type;
-    const T* ks = reinterpret_cast<const T*>(k_new);
-    const T* vs = reinterpret_cast<const T*>(v_new);
-    T* kp = reinterpret_cast<T*>(k_pool);
-    T* vp = reinterpret_cast<T*>(v_pool);
+    for (int i = 0; i < X; ++i) el[i] = code_of(0, o, c * X + i);
+    const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
+    *reinterpret_cast<u32x4*>(kp + tile * kBlockSize * D * EB + ((size_t)c * kBlockSize + sl % kBlockSize) * 16) =
+        pack(el);
+  }
+  // V, complete quads: chunk (g, c) of the quad led by token o holds dims
+  // 16 (g Y + u) + c, u < Y, of its 4 rows, element order [u][row]
+  for (int q = tid; q < kWriteGroup * (D / Y); q += kThreads) {
+    const int o = q / (D / Y), gc = q % (D / Y);
+    if (s_lead[o] != 1) continue;
+    const int64_t sl = s_slot[o];
+    const int g = gc / kBlockSize, c = gc % kBlockSize;
+    uint32_t el[16 / EB];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int d = e * 64 + lane;
-      kp[tile * kBlockSize * D + k_chunk_offset<sizeof(T)>(o, d)] = ks[src + d];
-      vp[tile * kBlockSize * D + v_chunk_offset<sizeof(T)>(o, d)] = vs[src + d];
+    for (int u = 0; u < Y; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) el[u * 4 + e] = code_of(1, o + e, kBlockSize * (g * Y + u) + c);
     }
+    const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
+    const int jq = (int)(sl % kBlockSize) / 4;
+    *reinterpret_cast<u32x4*>(vp + tile * kBlockSize * D * EB + (((size_t)g * kBlockSize + c) * 4 + jq) * 16) =
+        pack(el);
+  }
+  // V, other tokens: element by element
+  for (int q = tid; q < kWriteGroup * D; q += kThreads) {
+    const int o = q / D, d = q % D;
+    const int64_t sl = s_slot[o];
+    if (sl < 0 || s_lead[o] != 0) continue;
+    const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
+    uint8_t* dst = vp + (tile * kBlockSize * D + v_chunk_offset<EB>((int)(sl % kBlockSize), d)) * EB;
+    const uint32_t v = code_of(1, o, d);
+    if constexpr (EB == 1) *dst = (uint8_t)v;
+    else if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
+    else *reinterpret_cast<uint32_t*>(dst) = v;
   }
 }
 
@@ -184,8 +259,7 @@ template <int SRC, int KVT>
 hipError_t write_d(const void* k_new, const void* v_new, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                    const SlotSource& ss, int num_tokens, int num_blocks, int num_kv_heads, int head_dim,
                    hipStream_t st) {
-  const long rows = (long)num_tokens * num_kv_heads;
-  dim3 grid((unsigned)((rows + 3) / 4));
+  dim3 grid((unsigned)((num_tokens + kWriteGroup - 1) / kWriteGroup), (unsigned)num_kv_heads);
   if (head_dim == 64)
     hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, 64>), grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool, k_scale,
                        v_scale, ss, num_tokens, num_blocks, num_kv_heads);
