@@ -107,6 +107,9 @@ def test_write_validation():
     assert w(*base[:9], -1, *base[10:]) == _lib.EINVAL
     assert w(None, *base[1:]) == _lib.EINVAL
     assert w(*base[:9], 0, *base[10:]) == _lib.OK                   # nothing to write
+    odd = ctypes.c_void_p(0x100008)
+    assert w(odd, *base[1:]) == _lib.EINVAL                          # source not 16-byte aligned
+    assert w(*base[:11], 70000, *base[12:]) == _lib.EINVAL           # more KV heads than the grid takes
 
 
 def test_copy_select_slots_probe_validation():
