@@ -75,8 +75,91 @@ __device__ __forceinline__ float raw_to_f32(uint32_t r) {
   else return f16_to_f32(r);
 }
 
-// Tokens staged per workgroup.
+// Stored bits of one element from its raw source bits: the bits themselves
+// (pool dtype = source dtype), or the 8-bit code of value / scale, where the
+// scale is the row's (per-token formats; 0 gives code 0) or the channel's.
+template <int SRC, int KVT>
+__device__ __forceinline__ uint32_t stored_code(uint32_t raw, float scale) {
+  if constexpr (is_quantised(KVT)) return scale == 0.f ? 0u : encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(raw), scale));
+  else if constexpr (is_channel_scaled(KVT)) return encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(raw), scale));
+  else return raw;
+}
+
+template <int SRC>
+__device__ __forceinline__ uint32_t load_raw(const void* p, size_t i) {
+  if constexpr (SRC == DT_F32) return reinterpret_cast<const uint32_t*>(p)[i];
+  else return reinterpret_cast<const uint16_t*>(p)[i];
+}
+
+template <int EB>
+__device__ __forceinline__ void store_elem(uint8_t* dst, uint32_t v) {
+  if constexpr (EB == 1) *dst = (uint8_t)v;
+  else if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
+  else *reinterpret_cast<uint32_t*>(dst) = v;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+  return x;
+}
+
+// One wave per (token, KV head) row, K and V together: the decode append,
+// whose tokens are one per sequence (no chunk of the layout holds two of
+// them), where latency is all that counts.  The source loads go out before the
+// slot lookup they do not depend on.
+template <int SRC, int KVT, int D>
+__global__ void __launch_bounds__(256) kv_row_kernel(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                                                   float* k_scale, float* v_scale, const SlotSource ss,
+                                                   int num_tokens, int num_blocks, int num_kv_heads) {
+  constexpr int EB = KVT == DT_F32 ? 4 : (is_code8(KVT) ? 1 : 2);
+  constexpr int PER = D / kWave;
+  constexpr float kMaxCode = code_set(KVT) == DT_INT8 ? 127.f : 448.f;
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long)num_tokens * num_kv_heads) return;
+  const int t = (int)(row / num_kv_heads), h = (int)(row % num_kv_heads);
+  uint32_t kr[PER], vr[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    kr[e] = load_raw<SRC>(k_new, (size_t)row * D + e * kWave + lane);
+    vr[e] = load_raw<SRC>(v_new, (size_t)row * D + e * kWave + lane);
+  }
+  const int64_t slot = token_slot(ss, t, num_blocks);
+  if (slot < 0 || slot >= (int64_t)num_blocks * kBlockSize) return;
+  const size_t tile = (size_t)(slot / kBlockSize) * num_kv_heads + h;
+  const int o = (int)(slot % kBlockSize);
+  float ks = 0.f, vs = 0.f;
+  if constexpr (is_quantised(KVT)) {
+    float km = 0.f, vm = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      km = fmaxf(km, fabsf(raw_to_f32<SRC>(kr[e])));
+      vm = fmaxf(vm, fabsf(raw_to_f32<SRC>(vr[e])));
+    }
+    ks = __fdiv_rn(wave_max(km), kMaxCode);
+    vs = __fdiv_rn(wave_max(vm), kMaxCode);
+    if (lane == 0) {
+      k_scale[tile * kBlockSize + o] = ks;
+      v_scale[tile * kBlockSize + o] = vs;
+    }
+  }
+  uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool) + tile * kBlockSize * D * EB;
+  uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool) + tile * kBlockSize * D * EB;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = e * kWave + lane;
+    const float kc = is_channel_scaled(KVT) ? k_scale[(size_t)h * D + d] : ks;
+    const float vc = is_channel_scaled(KVT) ? v_scale[(size_t)h * D + d] : vs;
+    store_elem<EB>(kp + (size_t)k_chunk_offset<EB>(o, d) * EB, stored_code<SRC, KVT>(kr[e], kc));
+    store_elem<EB>(vp + (size_t)v_chunk_offset<EB>(o, d) * EB, stored_code<SRC, KVT>(vr[e], vc));
+  }
+}
+
+// Tokens staged per workgroup of the slot-list write, and its threads (8 per
+// staged K or V row in the scale pass).
 constexpr int kWriteGroup = 16;
+constexpr int kWriteThreads = 16 * kWriteGroup;
 
 // One workgroup per 16 consecutive tokens and one KV head.  The tokens' K and
 // V rows are staged in LDS, so the pool is written in whole 16-byte
@@ -88,13 +171,13 @@ constexpr int kWriteGroup = 16;
 // one token per sequence).  8-bit formats quantise each row with its own
 // scale (absmax / largest code) or by the static channel scales.
 template <int SRC, int KVT, int D>
-__global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+__global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                                                      float* k_scale, float* v_scale, const SlotSource ss,
                                                      int num_tokens, int num_blocks, int num_kv_heads) {
   constexpr int EB = KVT == DT_F32 ? 4 : (is_code8(KVT) ? 1 : 2);   // bytes per stored element
   constexpr int X = 16 / EB;                                       // elements per K chunk
   constexpr int Y = 4 / EB;                                        // dims per V chunk
-  constexpr int kThreads = 256;
+  constexpr int kThreads = kWriteThreads;
   constexpr float kMaxCode = code_set(KVT) == DT_INT8 ? 127.f : 448.f;
   // Raw source bits of K and V, one word per element; rows padded by one word
   // so that threads reading the same dim of consecutive rows hit different
@@ -114,22 +197,15 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
     if (sl >= (int64_t)num_blocks * kBlockSize) sl = -1;
     s_slot[tid] = sl < 0 ? -1 : sl;
   }
-  __syncthreads();
-  if (tid < kWriteGroup) {
-    // Quad of rows 4k..4k+3 of one block held by tokens o..o+3 in slot order.
-    const int64_t sl = s_slot[tid];
-    bool lead = sl >= 0 && sl % 4 == 0 && tid + 3 < kWriteGroup;
-    for (int e = 1; lead && e < 4; ++e) lead = s_slot[tid + e] == sl + e;
-    s_lead[tid] = lead ? 1 : 0;
-  }
   // Both rows of every token, with 16-byte loads: K and V, row o, elements
-  // [8 p, 8 p + 8) (16-bit source) or [4 p, 4 p + 4) (f32).
+  // [8 p, 8 p + 8) (16-bit source) or [4 p, 4 p + 4) (f32).  They do not wait
+  // for the slot lookup above; rows of skipped tokens are simply not stored.
   constexpr int kPer = 16 / (SRC == DT_F32 ? 4 : 2);
   for (int e = tid; e < 2 * kWriteGroup * D / kPer; e += kThreads) {
     const int kv = e / (kWriteGroup * D / kPer), r = e % (kWriteGroup * D / kPer);
     const int o = r / (D / kPer), d0 = (r % (D / kPer)) * kPer;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (s_slot[o] >= 0)
+    if (t_base + o < num_tokens)
       w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(kv == 0 ? k_new : v_new) +
                                           (((size_t)(t_base + o) * num_kv_heads + h) * D + d0) * (16 / kPer));
 #pragma unroll
@@ -139,13 +215,23 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
     }
   }
   __syncthreads();
-  if (tid < kWriteGroup && s_lead[tid] == 0) {
-    for (int e = 1; e < 4 && tid - e >= 0; ++e)
-      if (s_lead[tid - e] == 1 && s_slot[tid - e] + e == s_slot[tid]) s_lead[tid] = 2;
+  if (tid == 0) {
+    // V quads: token o leads one when it and the next 3 tokens hold rows
+    // 4k..4k+3 of one block in slot order (1); the 3 others are covered (2).
+    for (int o = 0; o < kWriteGroup; ++o) s_lead[o] = 0;
+    for (int o = 0; o + 3 < kWriteGroup; ++o) {
+      const int64_t sl = s_slot[o];
+      bool lead = sl >= 0 && sl % 4 == 0 && s_lead[o] == 0;
+      for (int e = 1; lead && e < 4; ++e) lead = s_slot[o + e] == sl + e;
+      if (lead) {
+        s_lead[o] = 1;
+        s_lead[o + 1] = s_lead[o + 2] = s_lead[o + 3] = 2;
+      }
+    }
   }
   if constexpr (is_quantised(KVT)) {
     // 8 threads per (K or V, row): absmax, then the row's scale
-    const int kv = tid / 128, o = (tid / 8) % kWriteGroup, l = tid % 8;
+    const int kv = tid / (8 * kWriteGroup), o = (tid / 8) % kWriteGroup, l = tid % 8;
     float m = 0.f;
     for (int d = l; d < D; d += 8) m = fmaxf(m, fabsf(raw_to_f32<SRC>(s_src[kv][o][d])));
 #pragma unroll
@@ -162,15 +248,10 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
 
   // Stored bits of element (token o, dim d) of K (kv 0) or V (kv 1).
   auto code_of = [&](int kv, int o, int d) -> uint32_t {
-    const uint32_t r = s_src[kv][o][d];
-    if constexpr (is_quantised(KVT)) {
-      const float sc = s_scale[kv][o];
-      return sc == 0.f ? 0u : encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(r), sc));
-    } else if constexpr (is_channel_scaled(KVT)) {
-      return encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(r), (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d]));
-    } else {
-      return r;   // same dtype as the source: the bits unchanged
-    }
+    float sc = 0.f;
+    if constexpr (is_quantised(KVT)) sc = s_scale[kv][o];
+    if constexpr (is_channel_scaled(KVT)) sc = (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d];
+    return stored_code<SRC, KVT>(s_src[kv][o][d], sc);
   };
   // 16 bytes from 16 / EB element codes.
   auto pack = [&](const uint32_t* el) {
@@ -222,10 +303,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const void* k_new, const 
     if (sl < 0 || s_lead[o] != 0) continue;
     const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
     uint8_t* dst = vp + (tile * kBlockSize * D + v_chunk_offset<EB>((int)(sl % kBlockSize), d)) * EB;
-    const uint32_t v = code_of(1, o, d);
-    if constexpr (EB == 1) *dst = (uint8_t)v;
-    else if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
-    else *reinterpret_cast<uint32_t*>(dst) = v;
+    store_elem<EB>(dst, code_of(1, o, d));
   }
 }
 
@@ -255,17 +333,30 @@ __global__ void __launch_bounds__(256) block_copy_kernel(uint8_t* k_pool, uint8_
 
 namespace {
 
+template <int SRC, int KVT, int D>
+void launch_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                  const SlotSource& ss, int num_tokens, int num_blocks, int num_kv_heads, hipStream_t st) {
+  if (ss.slots != nullptr) {
+    dim3 grid((unsigned)((num_tokens + kWriteGroup - 1) / kWriteGroup), (unsigned)num_kv_heads);
+    hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, D>), grid, dim3(kWriteThreads), 0, st, k_new, v_new, k_pool, v_pool,
+                       k_scale, v_scale, ss, num_tokens, num_blocks, num_kv_heads);
+  } else {
+    const long rows = (long)num_tokens * num_kv_heads;
+    hipLaunchKernelGGL((kv_row_kernel<SRC, KVT, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, k_new, v_new,
+                       k_pool, v_pool, k_scale, v_scale, ss, num_tokens, num_blocks, num_kv_heads);
+  }
+}
+
 template <int SRC, int KVT>
 hipError_t write_d(const void* k_new, const void* v_new, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                    const SlotSource& ss, int num_tokens, int num_blocks, int num_kv_heads, int head_dim,
                    hipStream_t st) {
-  dim3 grid((unsigned)((num_tokens + kWriteGroup - 1) / kWriteGroup), (unsigned)num_kv_heads);
   if (head_dim == 64)
-    hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, 64>), grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool, k_scale,
-                       v_scale, ss, num_tokens, num_blocks, num_kv_heads);
+    launch_write<SRC, KVT, 64>(k_new, v_new, k_pool, v_pool, k_scale, v_scale, ss, num_tokens, num_blocks,
+                               num_kv_heads, st);
   else
-    hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, 128>), grid, dim3(256), 0, st, k_new, v_new, k_pool, v_pool,
-                       k_scale, v_scale, ss, num_tokens, num_blocks, num_kv_heads);
+    launch_write<SRC, KVT, 128>(k_new, v_new, k_pool, v_pool, k_scale, v_scale, ss, num_tokens, num_blocks,
+                                num_kv_heads, st);
   return hipGetLastError();
 }
 
