@@ -32,9 +32,11 @@
 //    output accumulator again puts head c in lane column c, next to its
 //    running max and sum, so the online-softmax rescale is lane-local.
 //  * Probabilities are split into a high and a low 16-bit part and fed as two
-//    MFMAs, keeping ~16 mantissa bits; FP8 codes convert to bf16 exactly with
-//    the hardware converter, K's per-token scale multiplies the logit and V's
-//    multiplies the probability.
+//    MFMAs, keeping ~16 mantissa bits.  8-bit codes convert to bf16 operands
+//    exactly: E4M3 with the hardware converter, INT8 as code + 128 (the bias
+//    is taken out of the sums).  Per-token scales multiply the logit (K) and
+//    the probability (V); static per-channel scales multiply q once per
+//    segment (K) and the output once at the end (V).
 //  * Logits are kept in base 2 (scale * log2 e folded in) and exponentiated
 //    with v_exp_f32.
 #include <map>
@@ -313,7 +315,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
       *reinterpret_cast<f32x4*>(a.stash + ((size_t)s * hq + head) * a.nv_pad + (size_t)vb * kBlockSize + 4 * j) = xv;
     }
 
-    // ---- probabilities as the PV B operand (V's FP8 scale folded in)
+    // ---- probabilities as the PV B operand (V's per-token scale folded in)
     float pv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

@@ -1,5 +1,5 @@
 // KV-cache maintenance kernels for gfx950: decode slot lookup, token write
-// (with FP8 quantisation) and whole-block copy for copy-on-write.
+// (with 8-bit quantisation) and whole-block copy for copy-on-write.
 //
 // Page "KV Cache 与 PagedAttention：显存复用与长上下文推理" (plumephp.com/ai-kv-cache-paged-attention):
 //   "PagedAttention 的设计" -- a token lives in the physical block its sequence's

@@ -62,7 +62,7 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
 }
 
 // First head-dim of the 8 consecutive dims row group j contributes to QK step
-// st (16-bit and FP8 K: one 16x16x32 MFMA per step).  With 16-byte K chunks of
+// st (16-bit and 8-bit K: one 16x16x32 MFMA per step).  With 16-byte K chunks of
 // X elements, load u of row group j is chunk 4u + j.
 template <int KVT>
 __device__ __forceinline__ int qk_dim16(int st, int j) {

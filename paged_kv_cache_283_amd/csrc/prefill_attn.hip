@@ -22,7 +22,8 @@
 // query tokens of one (sequence, KV head); its waves walk the same blocks, so
 // the tiles come from HBM once and from the caches for the other waves.  Work
 // is split by query token only: every wave covers the whole causal range of
-// its tokens.
+// its tokens, two blocks per step so that PV runs as 16x16x32 MFMAs over both
+// blocks' 32 keys.
 #include <type_traits>
 
 #include "device_common.hpp"
