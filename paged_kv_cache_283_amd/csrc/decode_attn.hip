@@ -67,7 +67,13 @@ constexpr float kRescaleSlack = 8.f;
 #define PKV_ATTN_WAVES_PER_CU_FP8 8  // the same for 8-bit (FP8, INT8) pools (two per SIMD)
 #endif
 #ifndef PKV_ATTN_HEAD_FAST
-#define PKV_ATTN_HEAD_FAST 1         // 1: workgroup id = range * KV heads + head; 0: head-major
+#define PKV_ATTN_HEAD_FAST 0         // 16-bit and f32 pools -- 1: workgroup id = range * KV heads + head; 0: head-major
+#endif
+#ifndef PKV_ATTN_HEAD_FAST_8BIT
+#define PKV_ATTN_HEAD_FAST_8BIT 1    // the same for 8-bit pools
+#endif
+#ifndef PKV_ATTN_ODD_SHARE
+#define PKV_ATTN_ODD_SHARE 880       // per mille: odd-numbered range length relative to even (head-major only)
 #endif
 
 template <typename T>
@@ -467,14 +473,17 @@ __device__ __forceinline__ int wave_scan(int v) {
 // holds at once.
 //
 // The attended blocks of all sequences form one sequence-major list, cut into
-// n_ranges ranges of R blocks (R >= kPartBlocks).  Workgroup w takes one range
-// for one KV head; with the head-fastest order the KV heads of a range -- whose
-// tiles sit side by side in the pool -- are read at the same time, and since
-// workgroup ids go to the 8 XCDs in turn every XCD gets the same share.  A
-// range is cut at sequence boundaries into segments: a segment that is a whole
-// sequence writes the output directly, the others write partials that
-// attn_reduce_kernel merges.  Cuts inside a sequence are multiples of R, so
-// partial slots (partial_slot) are distinct.
+// n_ranges ranges whose lengths alternate between pa and pb (>= kPartBlocks).
+// Workgroup w takes one range for one KV head.  Workgroup ids go to the 8
+// XCDs in turn: with the head-fastest order (8-bit pools) the KV heads of a
+// range -- whose tiles sit side by side in the pool -- are read at the same
+// time and every XCD gets the same share; with the head-major order (16-bit
+// and f32 pools) range r runs on XCD r % 8 and pb < pa evens out the slower
+// odd XCDs.  A range is cut at sequence boundaries into segments: a segment
+// that is a whole sequence writes the output directly, the others write
+// partials that attn_reduce_kernel merges.  Cuts inside a sequence are range
+// starts, at least kPartBlocks apart, so partial slots (partial_slot) are
+// distinct.
 template <int KVT, int QT, int D>
 __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   __shared__ int s_tab[kTabBlocks];
@@ -482,13 +491,9 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   const int B = a.num_seqs;
   const int lane = threadIdx.x;
   const int n_ranges = gridDim.x / hkv;
-#if PKV_ATTN_HEAD_FAST
-  const int r = blockIdx.x / hkv;
-  const int kvh = blockIdx.x % hkv;
-#else
-  const int r = blockIdx.x % n_ranges;
-  const int kvh = blockIdx.x / n_ranges;
-#endif
+  constexpr bool kHeadFast = is_code8(KVT) ? PKV_ATTN_HEAD_FAST_8BIT : PKV_ATTN_HEAD_FAST;
+  const int r = kHeadFast ? blockIdx.x / hkv : blockIdx.x % n_ranges;
+  const int kvh = kHeadFast ? blockIdx.x % hkv : blockIdx.x / n_ranges;
 
   // Pass 1: total attended blocks; workgroup 0 records the per-sequence prefix
   // and R for the merge kernel; NaN outputs for unusable lengths.
@@ -504,15 +509,29 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     }
     total += __shfl(incl, kWave - 1, kWave);
   }
-  int per = (int)(((long long)total + n_ranges - 1) / n_ranges);
-  if (per < kPartBlocks) per = kPartBlocks;
+  // Ranges alternate between two lengths, pa (even r) and pb (odd r).  With
+  // the head-major order and a range count divisible by 8, range r runs on
+  // XCD r % 8 (workgroup ids are dealt to the 8 XCDs in turn), so pb < pa
+  // gives the odd XCDs less work: on MI355X they stream the same blocks about
+  // 8% slower than the even ones (measured per XCD with the wall clock).
+  int pa, pb;
+  if (!kHeadFast && PKV_ATTN_ODD_SHARE != 1000 && n_ranges % 8 == 0) {
+    const long long pair = (2LL * total + n_ranges - 1) / n_ranges;     // pa + pb
+    pa = (int)(pair * 1000 / (1000 + PKV_ATTN_ODD_SHARE));
+    pb = (int)(pair - pa);
+  } else {
+    pa = pb = (int)(((long long)total + n_ranges - 1) / n_ranges);
+  }
+  if (pa < kPartBlocks) pa = kPartBlocks;
+  if (pb < kPartBlocks) pb = kPartBlocks;
   if (blockIdx.x == 0 && lane == 0) {
     a.seq_prefix[B] = total;
-    a.hdr->per = per;
+    a.hdr->per = pa;
+    a.hdr->per_odd = pb;
   }
-  const long long u0 = (long long)r * per;
+  const long long u0 = (long long)(r / 2) * (pa + pb) + (r % 2) * pa;
   if (u0 >= total) return;
-  const long long u1 = min(u0 + per, (long long)total);
+  const long long u1 = min(u0 + (r % 2 ? pb : pa), (long long)total);
 
   // Pass 2: the sequence holding block u0, and its prefix.
   int sq = -1, prefix = 0, run = 0;
@@ -563,13 +582,20 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
   if (h >= a.num_q_heads) return;
   const int nva = attended_blocks(a, a.context_lens[s]);
   if (nva == 0) return;                             // NaN already written
-  const int per = a.hdr->per;
+  // Range cuts: cut k is (k / 2) P + (k odd ? pa : 0), P = pa + pb.
+  const int pa = a.hdr->per, pb = a.hdr->per_odd, P = pa + pb;
   const int base = a.seq_prefix[s];
   const int end = base + nva;
-  const int c0 = (base / per + 1) * per;            // first cut after the sequence start
-  if (c0 >= end) return;                            // one segment: written directly
-  const int n = 1 + (end - c0 + per - 1) / per;     // segments of this sequence
-  auto seg_slot = [&](int i) { return i == 0 ? 0 : partial_slot(c0 + (i - 1) * per - base); };
+  auto cut = [&](long long k) { return (k / 2) * P + (k % 2 ? pa : 0); };
+  const long long k0 = 2LL * (base / P) + (base % P < pa ? 1 : 2);   // first cut after the sequence start
+  if (cut(k0) >= end) return;                       // one segment: written directly
+  int n = 1;                                        // segments of this sequence
+  {
+    const long long e = end - 1;                    // last cut before end: index of the range holding e
+    const long long k_last = 2LL * (e / P) + (e % P < pa ? 0 : 1);
+    n = (int)(k_last - k0 + 2);
+  }
+  auto seg_slot = [&](int i) { return i == 0 ? 0 : partial_slot((int)(cut(k0 + i - 1) - base)); };
   const size_t hs = (size_t)s * a.num_q_heads + h;
   const float* ml = a.part_ml + hs * a.p_max * 2;
   const float* pacc = a.part_acc + hs * a.p_max * D;

@@ -10,8 +10,9 @@ namespace pkv {
 
 // Per-call schedule the attention kernel hands to the merge kernel (workspace).
 struct StreamHdr {
-  int per;               // attended blocks per range (R)
-  int pad[3];
+  int per;               // attended blocks of an even-numbered range
+  int per_odd;           // attended blocks of an odd-numbered range (ranges alternate)
+  int pad[2];
 };
 
 struct AttnArgs {
