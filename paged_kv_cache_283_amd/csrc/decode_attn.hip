@@ -116,8 +116,12 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   constexpr int NT = D / 16;              // 16-dim output tiles
   constexpr int VW = EB;                  // V words per lane per tile (4 tokens)
   constexpr bool CH = is_channel_scaled(KVT);   // static per-channel scales, folded into q and the output
-  constexpr bool BIAS = code_biased<KVT>();      // INT8 operands are code + kInt8Bias
-  constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16)) && !CH;
+  constexpr bool BIAS = code_biased<KVT>();      // INT8 operands are biased codes
+  // INT8 K enters QK as f16 code + 1152 (one v_perm_b32 per two codes), so the
+  // QK operands are f16; q is prescaled by 2^e into f16's range.
+  constexpr bool KF16 = code_set(KVT) == DT_INT8 && is_code8(KVT);
+  constexpr bool QF16 = F16 || KF16;            // QK operand type
+  constexpr bool QSAME = (!OP32) && (QT == (QF16 ? DT_F16 : DT_BF16)) && !CH;
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
 
@@ -137,6 +141,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   uint32_t qhi[QW];
   uint32_t qlo[QSPLIT ? QW : 1];
   float qf[OP32 ? DPL : 1];
+  int q_exp = 0;                          // q operands carry q * 2^q_exp (INT8 K only)
   {
     // Lane (c, j) holds, for QK step st, the same head-dims the K chunks of row
     // group j carry in that step (qk_dim), so A and B agree on the contraction.
@@ -153,6 +158,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
         qhi[4 * st + 0] = v[0]; qhi[4 * st + 1] = v[1]; qhi[4 * st + 2] = v[2]; qhi[4 * st + 3] = v[3];
       }
     } else {
+      float qv[2 * QW];
 #pragma unroll
       for (int st = 0; st < QW / 4; ++st) {
 #pragma unroll
@@ -164,25 +170,46 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
             f0 *= a.k_scale[(size_t)kvh * D + d0];
             f1 *= a.k_scale[(size_t)kvh * D + d0 + 1];
           }
-          const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
-          const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
-          const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
-          qhi[4 * st + w] = h0 | (h1 << 16);
-          qlo[4 * st + w] = l0 | (l1 << 16);
+          qv[2 * (4 * st + w)] = f0;
+          qv[2 * (4 * st + w) + 1] = f1;
         }
+      }
+      if constexpr (KF16) {
+        // 2^e with the head's largest |q| in [2^14, 2^15): exact, inside f16's range
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2 * QW; ++i) m = fmaxf(m, fabsf(qv[i]));
+        m = row_max4(m);
+        if (m > 0.f && m < INFINITY) {
+          const int ex = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+          q_exp = min(max(14 - ex, -60), 60);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * QW; ++i) qv[i] = ldexpf(qv[i], q_exp);
+      }
+#pragma unroll
+      for (int w = 0; w < QW; ++w) {
+        const float f0 = qv[2 * w], f1 = qv[2 * w + 1];
+        const uint32_t h0 = to_op16<QF16>(f0), h1 = to_op16<QF16>(f1);
+        const uint32_t l0 = to_op16<QF16>(f0 - from_op16<QF16>(h0));
+        const uint32_t l1 = to_op16<QF16>(f1 - from_op16<QF16>(h1));
+        qhi[w] = h0 | (h1 << 16);
+        qlo[w] = l0 | (l1 << 16);
       }
     }
   }
-  // Biased K operands add kInt8Bias * (sum of head c's q operand values) to every logit.
+  // Logit factor: the softmax scale in base 2, times 2^-e for prescaled q.
+  const float lscale = a.scale_log2 * ldexpf(1.f, -q_exp);
+  // Biased K operands add bias * (sum of head c's q operand values) to every logit.
   float qbias = 0.f;
   if constexpr (BIAS) {
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < QW; ++w) {
-      sum += from_op16<F16>(qhi[w] & 0xffffu) + from_op16<F16>(qhi[w] >> 16);
-      if constexpr (QSPLIT) sum += from_op16<F16>(qlo[w] & 0xffffu) + from_op16<F16>(qlo[w] >> 16);
+      sum += from_op16<QF16>(qhi[w] & 0xffffu) + from_op16<QF16>(qhi[w] >> 16);
+      if constexpr (QSPLIT) sum += from_op16<QF16>(qlo[w] & 0xffffu) + from_op16<QF16>(qlo[w] >> 16);
     }
-    qbias = kInt8Bias * row_sum4(sum);
+    qbias = (KF16 ? kInt8BiasF16 : kInt8Bias) * row_sum4(sum);
   }
 
   float m_run = -INFINITY;   // reference max of this head's base-2 logits (same in all 4 rows)
@@ -250,14 +277,17 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
-        if constexpr (is_code8(KVT)) {
+        if constexpr (KF16) {
+          int8x4_to_f16x4_biased(r.k[2 * st], av[0], av[1]);
+          int8x4_to_f16x4_biased(r.k[2 * st + 1], av[2], av[3]);
+        } else if constexpr (is_code8(KVT)) {
           code8x4_to_bf16x4<KVT>(r.k[2 * st], av[0], av[1]);
           code8x4_to_bf16x4<KVT>(r.k[2 * st + 1], av[2], av[3]);
         } else {
           av[0] = r.k[4 * st]; av[1] = r.k[4 * st + 1]; av[2] = r.k[4 * st + 2]; av[3] = r.k[4 * st + 3];
         }
-        sacc = mfma_k32<F16>(av, &qhi[4 * st], sacc);
-        if constexpr (QSPLIT) sacc = mfma_k32<F16>(av, &qlo[4 * st], sacc);
+        sacc = mfma_k32<QF16>(av, &qhi[4 * st], sacc);
+        if constexpr (QSPLIT) sacc = mfma_k32<QF16>(av, &qlo[4 * st], sacc);
       }
     }
 
@@ -268,7 +298,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     bool valid[4] = {true, true, true, true};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[e] = (BIAS ? sacc[e] - qbias : sacc[e]) * a.scale_log2;
+      x[e] = (BIAS ? sacc[e] - qbias : sacc[e]) * lscale;
       if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
     }
     if (!full) {

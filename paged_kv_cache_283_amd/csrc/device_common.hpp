@@ -82,6 +82,17 @@ __device__ __forceinline__ void int8x4_to_bf16x4_biased(uint32_t w, uint32_t& lo
   hi = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
 }
 
+// Four int8 codes -> four f16 values code + 1152 (two words), exactly: XOR
+// 0x80 gives the unsigned byte b = code + 128, and f16 bits 0x6400 | b are
+// 1024 + b (exponent 10, b in the low mantissa bits); one v_perm_b32 per pair
+// interleaves the bytes with 0x64.
+constexpr float kInt8BiasF16 = 1152.f;
+__device__ __forceinline__ void int8x4_to_f16x4_biased(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  const uint32_t b = w ^ 0x80808080u;
+  lo = __builtin_amdgcn_perm(0x64646464u, b, 0x04010400u);
+  hi = __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u);
+}
+
 // 8-bit codes of storage format KV -> bf16 MFMA operands: E4M3 values exactly,
 // INT8 codes biased by kInt8Bias (code_biased<KV>).
 template <int KV>
