@@ -10,7 +10,7 @@
 // V [NB][Hkv][D/(16Y)][16][4][Y][4] (16-byte chunks of 4 tokens x Y dims), per-token
 // scales [NB][Hkv][16], per-channel scales [Hkv][D] (static, given by the caller).
 #include "device_common.hpp"
-#include "fp8_e4m3.hpp"
+#include "kv_codec.hpp"
 #include "launch.hpp"
 
 namespace pkv {
@@ -35,19 +35,6 @@ __global__ void __launch_bounds__(256) token_slots_kernel(const int32_t* tables,
   if (s < 0 || s >= num_seqs || p < 0 || p >= stride * kBlockSize) { slots[t] = -1; return; }
   const int b = tables[(size_t)s * stride + p / kBlockSize];
   slots[t] = (b < 0 || b >= num_blocks) ? (int64_t)-1 : (int64_t)b * kBlockSize + p % kBlockSize;
-}
-
-// One 8-bit code of the quotient x / scale: E4M3FN (round to nearest even,
-// saturating to +-448) or INT8 (nearest integer, ties to even -- v_rndne_f32 --
-// saturated to +-127, two's complement).
-template <int KVT>
-__device__ __forceinline__ uint32_t encode8(float q) {
-  if constexpr (code_set(KVT) == DT_INT8) {
-    const float r = fminf(fmaxf(__builtin_rintf(q), -127.f), 127.f);
-    return (uint32_t)(int32_t)r & 0xffu;
-  } else {
-    return e4m3fn_encode(q);
-  }
 }
 
 // Where token t goes: slots[t], or -- for the decode append -- position
@@ -89,13 +76,6 @@ template <int SRC>
 __device__ __forceinline__ uint32_t load_raw(const void* p, size_t i) {
   if constexpr (SRC == DT_F32) return reinterpret_cast<const uint32_t*>(p)[i];
   else return reinterpret_cast<const uint16_t*>(p)[i];
-}
-
-template <int EB>
-__device__ __forceinline__ void store_elem(uint8_t* dst, uint32_t v) {
-  if constexpr (EB == 1) *dst = (uint8_t)v;
-  else if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
-  else *reinterpret_cast<uint32_t*>(dst) = v;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
