@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import policies
+from oracle import fp8, policies
 from paged_kv_cache_283_amd import ops
 
 pytestmark = pytest.mark.gpu
@@ -173,3 +173,55 @@ def test_prefill_chunk_full_size_sampled_rows():
             assert np.all(np.abs(got - ref) <= 2e-3 + np.abs(ref) * 2.0 ** -8), (s, i)
             worst = max(worst, float(np.max(np.abs(got - ref))))
     print(f"prefill 4x2048 after 6144: {w.num_seqs} x {len(rows)} rows checked, max abs err {worst:.3e}")
+
+
+@pytest.mark.parametrize("name", ["llama3", "fp8long"])
+def test_bulk_fill_full_size_sampled_bytes(name):
+    """The bulk write as the fill benchmark launches it (every position of the workload in one
+    paged_kv_write call): the stored bytes of 2000 sampled tokens, K and V, every KV head, equal what
+    the oracle's own write stores for those tokens (raw bf16 bits, or FP8 codes and scales)."""
+    from oracle import paging
+    w = W.WORKLOADS[name]
+    lay = W.make_layout(w)
+    tables = torch.from_numpy(lay.tables).cuda()
+    pools = H.make_pools(w, lay.num_blocks)
+    ksrc, vsrc = W.kv_source(w, lay, device="cuda")
+    seq, pos, rows = lay.fill_tokens()
+    r = torch.from_numpy(rows).cuda()
+    k_rows, v_rows = ksrc.index_select(0, r).contiguous(), vsrc.index_select(0, r).contiguous()
+    slots = ops.paged_token_slots(tables, torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), lay.num_blocks)
+    k, v, ks, vs = pools
+    ops.paged_kv_write(k_rows, v_rows, k, v, slots, ks, vs)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    pick = np.sort(rng.choice(seq.size, 2000, replace=False))
+    slot = slots.cpu().numpy()[pick]
+    blk, off = slot // 16, slot % 16
+    krows = H.k_token_rows(k).view(lay.num_blocks * 16, w.num_kv_heads, w.head_dim)
+    vrows = H.v_token_rows(v).view(lay.num_blocks * 16, w.num_kv_heads, w.head_dim)
+    got_k = krows[torch.from_numpy(slot).cuda()].cpu()
+    got_v = vrows[torch.from_numpy(slot).cuda()].cpu()
+    src_k = k_rows[torch.from_numpy(pick).cuda()].cpu()
+    src_v = v_rows[torch.from_numpy(pick).cuda()].cpu()
+    if w.kv_dtype == "bf16":
+        assert torch.equal(got_k.view(torch.int16), src_k.view(torch.int16))
+        assert torch.equal(got_v.view(torch.int16), src_v.view(torch.int16))
+    else:
+        # the oracle's write of the same rows into a one-block pool per token
+        bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+        ref = list(paging.new_pools(1, w.num_kv_heads, w.head_dim, w.kv_dtype))
+        for i in range(0, pick.size, 16):
+            n = min(16, pick.size - i)
+            paging.write_tokens(ref, w.kv_dtype, bits(src_k[i:i + n]), bits(src_v[i:i + n]), w.src_dtype,
+                                [[0]], [0] * n, list(range(n)))
+            rk = ref[0][0].transpose(2, 0, 1, 3).reshape(16, w.num_kv_heads, w.head_dim)[:n]
+            assert np.array_equal(got_k[i:i + n].numpy(), rk)
+            kscale = ks[torch.from_numpy(blk[i:i + n]).cuda(), :, torch.from_numpy(off[i:i + n]).cuda()].cpu().numpy()
+            assert np.array_equal(kscale, ref[2][0].T[:n])
+            vscale = vs[torch.from_numpy(blk[i:i + n]).cuda(), :, torch.from_numpy(off[i:i + n]).cuda()].cpu().numpy()
+            assert np.array_equal(vscale, ref[3][0].T[:n])
+            got_vn = got_v[i:i + n].numpy()
+            ref_v = np.stack([paging.gather_logical(ref, w.kv_dtype, [0], [o])[1][0] for o in range(n)])
+            deq = fp8.decode(got_vn) * vscale[:, :, None]
+            assert np.array_equal(deq, ref_v)
+    print(f"{name}: {pick.size} sampled tokens of {seq.size} match")
