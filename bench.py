@@ -2,9 +2,11 @@
 """Paged decode attention benchmark on one MI355X.
 
 A step is one decode step of one layer over the whole batch, every kernel of
-the path on the GPU with all inputs resident in HBM:
-  paged_kv_append (the new token of every sequence, slot from its table)
-  -> paged_decode_attn (persistent attention kernel + log-sum-exp merge).
+the path on the GPU with all inputs resident in HBM: paged_decode_append_attn,
+i.e. the new token of every sequence written to its slot (found through its
+block table) and attention over the cache that holds it -- for 16-bit pools one
+persistent attention kernel that also stores the token, then the log-sum-exp
+merge; for 8-bit pools the quantising append kernel first.
 Default workload: the Llama-3-8B-shaped layer (64 sequences, lengths U{512..8192},
 32 q / 8 KV heads, head_dim 128, bf16 KV, shuffled 16-token blocks).
 
@@ -476,10 +478,9 @@ def main():
     for p in pools:
         k, v, ks, vs = p
         launches.append((
-            ops.paged_kv_append(k_new, v_new, k, v, tables, lens, ks, vs, stream=stream, prepare=True),
-            ops.paged_decode_attn(out, q, k, v, tables, lens, lay.max_len, k_scale=ks, v_scale=vs,
-                                  num_sinks=w.num_sinks, window=w.window, workspace=ws, stream=stream,
-                                  prepare=True)))
+            ops.paged_decode_append_attn(out, q, k_new, v_new, k, v, tables, lens, lay.max_len, k_scale=ks,
+                                         v_scale=vs, num_sinks=w.num_sinks, window=w.window, workspace=ws,
+                                         stream=stream, prepare=True),))
 
     def step(i):
         if layers > 1:

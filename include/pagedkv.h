@@ -215,6 +215,36 @@ int paged_decode_attn(void* out, int out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_decode_append_attn -- one decode step of one layer: paged_kv_append of
+ * the new token of every sequence, then paged_decode_attn over the cache that
+ * now holds it ([LC] StreamingKVCache: append, then attend; [PA]
+ * "PagedAttention 的设计": the token lands in block table[p / 16] at offset
+ * p % 16, p = context_lens[s] - 1).  The pools and the outputs end up exactly
+ * as after those two calls with the same arguments, and every argument follows
+ * their rules (k_new, v_new [num_seqs][num_kv_heads][head_dim] of src_dtype,
+ * 16-byte aligned; the workspace is paged_decode_attn's).
+ *   F32/BF16/F16 pools: one attention launch.  The wave that attends a
+ *     sequence's last block takes the new K/V row from k_new/v_new into that
+ *     block's operands and stores it into the pool slot, so attention does not
+ *     wait for the store.  A sequence whose last table entry lies outside
+ *     [0, num_blocks) gets NaN outputs and no store.
+ *   8-bit pools: the append kernel (which quantises the row) and then the
+ *     attention kernel, on the stream.
+ * Validation of every argument happens before anything is enqueued.
+ */
+int paged_decode_append_attn(void* out, int out_dtype,
+                             const void* q, int q_dtype,
+                             const void* k_new, const void* v_new, int src_dtype,
+                             void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
+                             const int32_t* block_tables, int block_table_stride,
+                             const int32_t* context_lens, int max_context_len,
+                             int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
+                             int head_dim, int block_size, float scale,
+                             int num_sinks, int window,
+                             float* attn_mass, int attn_mass_stride,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_prefill_attn -- causal multi-query attention over the paged cache: the
  * chunked prefill of a long prompt ([SO] 4.5 "Chunked Prefill") or the
  * continuation of a request whose prefix came from the prefix cache ([PA]
@@ -367,8 +397,9 @@ int kv_compact(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int k
 
 /*
  * Kernel timing for benchmarks.  Between pkv_timing_begin(capacity) and
- * pkv_timing_end(), each paged_decode_attn call records a HIP event pair on
- * its stream around its main attention kernel, up to `capacity` calls.
+ * pkv_timing_end(), each paged_decode_attn call has its main attention
+ * kernel's dispatch stamp a HIP event pair with that kernel's own start and
+ * end (no separate event packets on the stream), up to `capacity` calls.
  * pkv_timing_end waits for the last event, writes the elapsed milliseconds of
  * each recorded launch to ms_out (host, capacity floats), returns the count
  * (or -1 on error).  Not thread-safe: one timing session per process.

@@ -173,12 +173,16 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
       .total;
 }
 
-int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
-                      const float* k_scale, const float* v_scale, int kv_dtype, const int32_t* block_tables,
-                      int block_table_stride, const int32_t* context_lens, int max_context_len, int num_seqs,
-                      int num_blocks, int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale,
-                      int num_sinks, int window, float* attn_mass, int attn_mass_stride, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+// Validates the arguments of a decode-attention call and fills `a`; no HIP
+// call.  num_seqs == 0 leaves a.num_seqs = 0 (nothing to launch).
+static int prepare_decode_attn(pkv::AttnArgs& a, void* out, int out_dtype, const void* q, int q_dtype,
+                               const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
+                               int kv_dtype, const int32_t* block_tables, int block_table_stride,
+                               const int32_t* context_lens, int max_context_len, int num_seqs, int num_blocks,
+                               int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale,
+                               int num_sinks, int window, float* attn_mass, int attn_mass_stride, void* workspace,
+                               size_t workspace_bytes) {
+  a = pkv::AttnArgs{};
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
   int st = check_attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, num_sinks);
   if (st != PKV_OK) return st;
@@ -213,7 +217,6 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
       (k_scale && (uintptr_t)k_scale % 16) || (v_scale && (uintptr_t)v_scale % 16))
     return fail(PKV_EINVAL, "q, pools and scales must be 16-byte aligned");
 
-  pkv::AttnArgs a{};
   a.out = out;
   a.out_dtype = out_dtype;
   a.q = q;
@@ -244,14 +247,71 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
   a.p_max = lay.p_max;
   a.nv_pad = lay.nv_pad;
 
+  return ok();
+}
+
+static int launch_prepared_attn(const pkv::AttnArgs& a, int kv_dtype, int q_dtype, int head_dim, void* stream,
+                                const char* what) {
+  if (a.num_seqs == 0) return ok();
   hipEvent_t eb = nullptr, ee = nullptr;
   if (g_timing.active && g_timing.used < (int)g_timing.ev.size()) {
     eb = g_timing.ev[g_timing.used].first;
     ee = g_timing.ev[g_timing.used].second;
     ++g_timing.used;
   }
-  return device_status(pkv::launch_decode_attn(a, kv_dtype, q_dtype, head_dim, (hipStream_t)stream, eb, ee),
-                       "paged_decode_attn");
+  return device_status(pkv::launch_decode_attn(a, kv_dtype, q_dtype, head_dim, (hipStream_t)stream, eb, ee), what);
+}
+
+int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,
+                      const float* k_scale, const float* v_scale, int kv_dtype, const int32_t* block_tables,
+                      int block_table_stride, const int32_t* context_lens, int max_context_len, int num_seqs,
+                      int num_blocks, int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale,
+                      int num_sinks, int window, float* attn_mass, int attn_mass_stride, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  pkv::AttnArgs a;
+  const int st = prepare_decode_attn(a, out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
+                                     block_tables, block_table_stride, context_lens, max_context_len, num_seqs,
+                                     num_blocks, num_q_heads, num_kv_heads, head_dim, block_size, scale, num_sinks,
+                                     window, attn_mass, attn_mass_stride, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  return launch_prepared_attn(a, kv_dtype, q_dtype, head_dim, stream, "paged_decode_attn");
+}
+
+int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_new,
+                             const void* v_new, int src_dtype, void* k_pool, void* v_pool, float* k_scale,
+                             float* v_scale, int kv_dtype, const int32_t* block_tables, int block_table_stride,
+                             const int32_t* context_lens, int max_context_len, int num_seqs, int num_blocks,
+                             int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale,
+                             int num_sinks, int window, float* attn_mass, int attn_mass_stride, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  pkv::AttnArgs a;
+  int st = prepare_decode_attn(a, out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
+                               block_tables, block_table_stride, context_lens, max_context_len, num_seqs, num_blocks,
+                               num_q_heads, num_kv_heads, head_dim, block_size, scale, num_sinks, window, attn_mass,
+                               attn_mass_stride, workspace, workspace_bytes);
+  if (st != PKV_OK) return st;
+  if (!valid_float_dtype(src_dtype)) return fail(PKV_EINVAL, "src_dtype %d", src_dtype);
+  if (!code8_kv(kv_dtype) && src_dtype != kv_dtype)
+    return fail(PKV_EUNSUPPORTED, "a non-quantised pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
+  if (num_seqs == 0) return ok();
+  if (!k_new || !v_new) return fail(PKV_EINVAL, "NULL array argument");
+  if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)
+    return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
+  if (code8_kv(kv_dtype)) {
+    // 8-bit pools: the token is quantised by the append kernel first; the
+    // attention kernel then reads it from the pool like any other.
+    st = device_status(pkv::launch_kv_append(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
+                                             block_tables, block_table_stride, context_lens, num_seqs, num_blocks,
+                                             num_kv_heads, head_dim, (hipStream_t)stream),
+                       "paged_decode_append_attn");
+    if (st != PKV_OK) return st;
+  } else {
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_store = k_pool;
+    a.v_store = v_pool;
+  }
+  return launch_prepared_attn(a, kv_dtype, q_dtype, head_dim, stream, "paged_decode_append_attn");
 }
 
 int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool, const void* v_pool,

@@ -39,8 +39,11 @@
 //    segment (K) and the output once at the end (V).
 //  * Logits are kept in base 2 (scale * log2 e folded in) and exponentiated
 //    with v_exp_f32.
+#include <hip/hip_ext.h>
+
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 
 #include "device_common.hpp"
@@ -85,6 +88,14 @@ __device__ __forceinline__ T load_stream(const T* p) {
 #endif
 }
 
+// The workgroup is one wave: LDS written by some lanes is read by others after
+// this (LDS-only fences, so outstanding global stores are not waited for).
+__device__ __forceinline__ void lds_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Table entries staged in LDS per chunk of a segment.
 constexpr int kTabBlocks = 1024;
 
@@ -105,8 +116,8 @@ __device__ __forceinline__ int attended_blocks(const AttnArgs& a, int L) {
 // whole sequence) or a partial (running max, exp-sum, unnormalised output) in
 // slot partial_slot(seg_vb0).
 template <int KVT, int QT, int D>
-__device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int s, int kvh, int L, int seg_vb0,
-                                             int seg_vb1) {
+__device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint32_t* s_new, int s, int kvh, int L,
+                                             int seg_vb0, int seg_vb1) {
   using KT = KvType<KVT>;
   constexpr int EB = KT::kBytes;
   constexpr bool OP32 = KT::kOp32;
@@ -224,6 +235,48 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
   const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
 
+  // ---- decode append fused in (16-bit and f32 pools): the segment that ends
+  // the sequence loads the new token's K and V rows (position L - 1, offset
+  // o_new of the last attended block) together with its first table chunk and
+  // copies them to LDS next to the staged entries; the last block's operands
+  // get them patched in, so the products see exactly the bits the pool will
+  // hold.  The rows are stored into their slot when the wave has finished all
+  // its segments (append_stores): stores share the load counter, so a store
+  // issued here would hold up the wave's next tile waits until it completes.
+  constexpr bool kFusable = !is_code8(KVT);
+  constexpr int NW = D * EB / 4;          // words of one K or V row
+  constexpr int NWL = (NW + kWave - 1) / kWave;
+  const bool fuse = kFusable && a.k_new != nullptr && seg_vb1 == geo.n_virtual;
+  const int o_new = (L - 1) & (kBlockSize - 1);
+  const int vb_new = geo.n_virtual - 1;
+  uint32_t rk[kFusable ? NWL : 1], rv[kFusable ? NWL : 1];
+  auto fused_load = [&]() {
+    if constexpr (kFusable) {
+      const size_t row = ((size_t)s * a.num_kv_heads + kvh) * NW;
+      const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_new) + row;
+      const uint32_t* vr = reinterpret_cast<const uint32_t*>(a.v_new) + row;
+#pragma unroll
+      for (int u = 0; u < NWL; ++u) {
+        const int k = min(lane + kWave * u, NW - 1);
+        rk[u] = kr[k];
+        rv[u] = vr[k];
+      }
+    }
+  };
+  // The rows go to LDS for the patch once the first chunk's entries are
+  // staged (the same wait covers their loads).
+  auto fused_stage = [&]() {
+    if constexpr (kFusable) {
+#pragma unroll
+      for (int u = 0; u < NWL; ++u) {
+        const int k = lane + kWave * u;
+        if (k < NW) {
+          s_new[k] = rk[u];
+          s_new[NW + k] = rv[u];
+        }
+      }
+    }
+  };
   struct Regs {
     uint32_t k[KW];
     uint32_t v[NT][VW];
@@ -263,10 +316,49 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     }
   };
 
-  auto compute = [&](Regs& r, int i) {
+  // tail: a call that may compute the segment's last block (the pipeline's
+  // steady state never does), the only place the new token is patched in.
+  auto compute = [&](Regs& r, int i, auto tail) {
     bad |= !r.ok;   // outputs become NaN; the block is still computed
     const int vb = c0 + i;
     const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
+
+    if constexpr (kFusable && decltype(tail)::value) {
+      if (fuse && vb == vb_new) {
+        // K: token row o_new is lane column c == o_new, which takes chunks
+        // 4w + j of the row.  V: tokens 4j..4j+3 sit in lane row j, so o_new is
+        // element o_new % 4 of every tile's word pair (16-bit) or quad (f32) in
+        // lanes j == o_new / 4, which take dims 16 t + c.
+        const bool krow = c == o_new;
+        const bool vrow = j == (o_new >> 2);
+        const int e = o_new & 3;
+        uint32_t kn[KW], vn[NT];
+#pragma unroll
+        for (int w = 0; w < KW / 4; ++w) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(&s_new[(4 * w + j) * 4]);
+          kn[4 * w + 0] = v[0]; kn[4 * w + 1] = v[1]; kn[4 * w + 2] = v[2]; kn[4 * w + 3] = v[3];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (EB == 2) vn[t] = reinterpret_cast<const uint16_t*>(s_new + NW)[16 * t + c];
+          else vn[t] = s_new[NW + 16 * t + c];
+        }
+#pragma unroll
+        for (int w = 0; w < KW; ++w) r.k[w] = krow ? kn[w] : r.k[w];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (EB == 2) {
+            const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            const uint32_t put = (e & 1) ? (vn[t] << 16) : vn[t];
+            r.v[t][0] = (vrow && e < 2) ? ((r.v[t][0] & keep) | put) : r.v[t][0];
+            r.v[t][1] = (vrow && e >= 2) ? ((r.v[t][1] & keep) | put) : r.v[t][1];
+          } else {
+#pragma unroll
+            for (int ee = 0; ee < 4; ++ee) r.v[t][ee] = (vrow && ee == e) ? vn[t] : r.v[t][ee];
+          }
+        }
+      }
+    }
 
     // ---- S = K q^T: lane (c, j) receives head c's logits of tokens 4j..4j+3
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -402,13 +494,32 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     }
   };
 
+  constexpr std::false_type kMid{};
+  constexpr std::true_type kTail{};
   for (; c0 < seg_vb1; c0 += kTabBlocks) {
     // The chunk's table entries go to LDS first: the loop reads them with LDS
     // loads, whose wait counter is separate from the K/V loads', so the
     // compiler can wait for exactly the block about to be computed.
     const int n = min(kTabBlocks, seg_vb1 - c0);
-    for (int k = lane; k < n; k += kWave) s_tab[k] = trow[logical_block(c0 + k, geo.n_sink_blocks, geo.win_start)];
-    __syncthreads();
+    const bool first = fuse && c0 == seg_vb0;
+    {
+      // Every entry load goes out before the first is waited for (indices
+      // past the chunk reload its last entry, so no load is conditional); the
+      // fused append's row loads join them.
+      constexpr int TU = kTabBlocks / kWave;
+      int ent[TU];
+#pragma unroll
+      for (int u = 0; u < TU; ++u)
+        ent[u] = trow[logical_block(c0 + min(lane + kWave * u, n - 1), geo.n_sink_blocks, geo.win_start)];
+      if (first) fused_load();
+#pragma unroll
+      for (int u = 0; u < TU; ++u) {
+        const int k = lane + kWave * u;
+        if (k < n) s_tab[k] = ent[u];
+      }
+      if (first) fused_stage();
+    }
+    lds_wave_sync();
 #if PKV_ATTN_PIPE == 2
     // Software pipeline: block i+1's loads are in flight while block i computes.
     Regs ra, rb;
@@ -416,14 +527,14 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     if (n > 0) load(ra, 0);
     for (; i + 2 < n; i += 2) {   // steady state: every load unconditional
       load(rb, i + 1);
-      compute(ra, i);
+      compute(ra, i, kMid);
       load(ra, i + 2);
-      compute(rb, i + 1);
+      compute(rb, i + 1, kMid);
     }
     // at most 2 blocks left; ra holds block i
     if (i + 1 < n) load(rb, i + 1);
-    if (i < n) compute(ra, i);
-    if (i + 1 < n) compute(rb, i + 1);
+    if (i < n) compute(ra, i, kTail);
+    if (i + 1 < n) compute(rb, i + 1, kTail);
 #else
     // Software pipeline: blocks i+1 and i+2 are in flight while block i computes.
     Regs r0, r1, r2;
@@ -432,21 +543,21 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
     if (n > 1) load(r1, 1);
     for (; i + 4 < n; i += 3) {   // steady state: every load unconditional
       load(r2, i + 2);
-      compute(r0, i);
+      compute(r0, i, kMid);
       load(r0, i + 3);
-      compute(r1, i + 1);
+      compute(r1, i + 1, kMid);
       load(r1, i + 4);
-      compute(r2, i + 2);
+      compute(r2, i + 2, kMid);
     }
     // at most 4 blocks left; r0, r1 hold blocks i, i+1 where they exist
     if (i + 2 < n) load(r2, i + 2);
-    if (i < n) compute(r0, i);
+    if (i < n) compute(r0, i, kTail);
     if (i + 3 < n) load(r0, i + 3);
-    if (i + 1 < n) compute(r1, i + 1);
-    if (i + 2 < n) compute(r2, i + 2);
-    if (i + 3 < n) compute(r0, i + 3);
+    if (i + 1 < n) compute(r1, i + 1, kTail);
+    if (i + 2 < n) compute(r2, i + 2, kTail);
+    if (i + 3 < n) compute(r0, i + 3, kTail);
 #endif
-    __syncthreads();   // s_tab is rewritten by the next chunk
+    lds_wave_sync();   // s_tab is rewritten by the next chunk
   }
 
   l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
@@ -488,6 +599,55 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, int 
   }
 }
 
+// Word k of the fused decode append's K and V rows of (sequence sq, KV head h)
+// stored at offset (L - 1) % 16 of pool block blk.
+template <int KVT, int D>
+__device__ __forceinline__ void append_word(const AttnArgs& a, int sq, int h, int L, int blk, int k) {
+  constexpr int EB = KvType<KVT>::kBytes;
+  constexpr int NW = D * EB / 4;
+  const int o = (L - 1) & (kBlockSize - 1);
+  const size_t row = ((size_t)sq * a.num_kv_heads + h) * NW;
+  const size_t tile = (size_t)blk * a.num_kv_heads + h;
+  uint8_t* kt = reinterpret_cast<uint8_t*>(a.k_store) + tile * (size_t)(kBlockSize * D * EB);
+  uint8_t* vt = reinterpret_cast<uint8_t*>(a.v_store) + tile * (size_t)(kBlockSize * D * EB);
+  const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k_new)[row + k];   // bytes 4k..4k+3 of the row
+  const uint32_t vw = reinterpret_cast<const uint32_t*>(a.v_new)[row + k];
+  *reinterpret_cast<uint32_t*>(kt + ((size_t)(k / 4) * kBlockSize + o) * 16 + (k % 4) * 4) = kw;
+  if constexpr (EB == 2) {
+    *reinterpret_cast<uint16_t*>(vt + (size_t)v_chunk_offset<2>(o, 2 * k) * 2) = (uint16_t)vw;
+    *reinterpret_cast<uint16_t*>(vt + (size_t)v_chunk_offset<2>(o, 2 * k + 1) * 2) = (uint16_t)(vw >> 16);
+  } else {
+    *reinterpret_cast<uint32_t*>(vt + (size_t)v_chunk_offset<4>(o, k) * 4) = vw;
+  }
+}
+
+// Pool block that takes the fused append of a sequence of length L (the
+// decode append's rule: L in [1, 16 * stride] and a table entry in the pool),
+// or -1.
+__device__ __forceinline__ int append_block(const AttnArgs& a, int sq, int L) {
+  if (L < 1 || L > a.table_stride * kBlockSize) return -1;
+  const int blk = a.block_tables[(size_t)sq * a.table_stride + (L - 1) / kBlockSize];
+  return (blk < 0 || blk >= a.num_blocks) ? -1 : blk;
+}
+
+// The fused decode append's stores, issued when the wave has attended all its
+// segments (nothing waits for them then): the rows of KV head kvh of every
+// sequence in [end_lo, end_hi] with attended blocks -- the sequences whose
+// last block this wave attended.
+template <int KVT, int D>
+__device__ __forceinline__ void append_stores(const AttnArgs& a, int kvh, int end_lo, int end_hi) {
+  constexpr int NW = D * KvType<KVT>::kBytes / 4;
+  const int lane = threadIdx.x & 63;
+  for (int sq = end_lo; sq <= end_hi; ++sq) {
+    const int L = a.context_lens[sq];
+    if (attended_blocks(a, L) == 0) continue;   // stored in pass 1 of the kernel, if at all
+    const int blk = append_block(a, sq, L);
+    if (blk < 0) continue;
+#pragma unroll
+    for (int k = lane; k < NW; k += kWave) append_word<KVT, D>(a, sq, kvh, L, blk, k);
+  }
+}
+
 // Inclusive prefix sum over the wave's 64 lanes.
 __device__ __forceinline__ int wave_scan(int v) {
   const int lane = threadIdx.x & 63;
@@ -517,6 +677,8 @@ __device__ __forceinline__ int wave_scan(int v) {
 template <int KVT, int QT, int D>
 __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   __shared__ int s_tab[kTabBlocks];
+  // the new token's K and V rows when the decode append is fused in (16-bit and f32 pools)
+  __shared__ uint32_t s_new[is_code8(KVT) ? 1 : 2 * D * KvType<KVT>::kBytes / 4];
   const int hkv = a.num_kv_heads;
   const int B = a.num_seqs;
   const int lane = threadIdx.x;
@@ -536,6 +698,16 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     if (sq < B && nva == 0 && sq % (int)gridDim.x == (int)blockIdx.x) {
       for (int idx = 0; idx < a.num_q_heads * D; ++idx)
         store_out(a.out, (size_t)sq * a.num_q_heads * D + idx, a.out_dtype, __builtin_nanf(""));
+      if constexpr (!is_code8(KVT)) {
+        // no wave attends this sequence; its token is still stored where the
+        // decode append would store it (a length beyond max_context_len)
+        const int L = a.context_lens[sq];
+        const int blk = a.k_new != nullptr ? append_block(a, sq, L) : -1;
+        if (blk >= 0) {
+          for (int h = 0; h < hkv; ++h)
+            for (int k = 0; k < D * KvType<KVT>::kBytes / 4; ++k) append_word<KVT, D>(a, sq, h, L, blk, k);
+        }
+      }
     }
     total += __shfl(incl, kWave - 1, kWave);
   }
@@ -582,12 +754,17 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   prefix = __builtin_amdgcn_readfirstlane(prefix);
 
   long long u = u0;
+  int end_lo = B, end_hi = -1;   // sequences whose last block this wave attends
   while (u < u1) {
     const int L = a.context_lens[sq];
     const int nva = attended_blocks(a, L);
     const int vb = (int)(u - prefix);
     const int cnt = (int)min((long long)(nva - vb), u1 - u);
-    wave_segment<KVT, QT, D>(a, s_tab, sq, kvh, L, vb, vb + cnt);
+    wave_segment<KVT, QT, D>(a, s_tab, s_new, sq, kvh, L, vb, vb + cnt);
+    if (vb + cnt == nva) {
+      end_lo = min(end_lo, sq);
+      end_hi = sq;
+    }
     u += cnt;
     if (u < u1) {
       // next sequence with attended blocks (one exists: u < total)
@@ -595,6 +772,9 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
       ++sq;
       while (attended_blocks(a, a.context_lens[sq]) == 0) ++sq;
     }
+  }
+  if constexpr (!is_code8(KVT)) {
+    if (a.k_new != nullptr) append_stores<KVT, D>(a, kvh, end_lo, end_hi);
   }
 }
 
@@ -718,13 +898,14 @@ hipError_t launch_partition(const AttnArgs& a, hipStream_t st, hipEvent_t ev_beg
   const int waves = resident_waves<KVT, QT, D>();
   if (waves <= 0) return hipErrorInvalidDevice;
   const int n_ranges = waves / a.num_kv_heads > 0 ? waves / a.num_kv_heads : 1;
-  hipError_t err = hipSuccess;
-  if (ev_begin) err = hipEventRecord(ev_begin, st);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((attn_wave_kernel<KVT, QT, D>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st, a);
-  err = hipGetLastError();
-  if (err == hipSuccess && ev_end) err = hipEventRecord(ev_end, st);
-  return err;
+  // With timing events the dispatch stamps them itself (start and end of this
+  // kernel), so no marker packets enter the stream between launches.
+  if (ev_begin && ev_end)
+    hipExtLaunchKernelGGL((attn_wave_kernel<KVT, QT, D>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st,
+                          ev_begin, ev_end, 0, a);
+  else
+    hipLaunchKernelGGL((attn_wave_kernel<KVT, QT, D>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int KVT, int QT>

@@ -41,6 +41,14 @@ struct AttnArgs {
   int* seq_prefix;      // [B + 1]  attended-block prefix per sequence, then the total
   int p_max;
   int nv_pad;
+  // Decode append fused in (16-bit and f32 pools): the new token of every
+  // sequence (position context_lens[s] - 1), [B][Hkv][D] in the pool's dtype,
+  // enters the last block's operands from here and is stored into the pools.
+  // Null: the pools already hold it.
+  const void* k_new;
+  const void* v_new;
+  void* k_store;        // the K and V pools, writable (fused append only)
+  void* v_store;
 };
 
 // Causal multi-query attention over the paged cache (chunked prefill).

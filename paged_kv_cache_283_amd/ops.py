@@ -290,6 +290,43 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     return p if prepare else out
 
 
+def paged_decode_append_attn(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                             scale=None, k_scale=None, v_scale=None, num_sinks=0, window=0, attn_mass=None,
+                             workspace=None, stream=None, prepare=False):
+    """One decode step: the new token k_new/v_new [B][Hkv][D] goes to position context_lens[s] - 1 of
+    sequence s, then q [B][Hq][D] attends over the paged pools into out (paged_kv_append followed by
+    paged_decode_attn, in one attention launch for 16-bit and f32 pools)."""
+    b, hq, d = q.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    if tuple(out.shape) != (b, hq, d):
+        raise ValueError("out must have q's shape")
+    if tuple(k_new.shape) != (b, hkv, d) or v_new.shape != k_new.shape or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim] of one dtype")
+    if (tuple(k_pool.shape) != k_pool_shape(nb, hkv, d, k_pool.dtype)
+            or tuple(v_pool.shape) != v_pool_shape(nb, hkv, d, v_pool.dtype)):
+        raise ValueError("pool shapes do not match k_new")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if context_lens.shape[0] != b or block_tables.shape[0] != b:
+        raise ValueError("one table row and one length per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mass_stride = 0
+    if attn_mass is not None:
+        _need(attn_mass, torch.float32, "attn_mass")
+        mass_stride = attn_mass.shape[1]
+    if workspace is None:
+        workspace = alloc_workspace(b, hq, d, max_context_len, num_sinks, window, attn_mass is not None, q.device)
+    args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_new), _ptr(v_new),
+            float_code(k_new.dtype), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+            pool_code(k_pool, k_scale, v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+            int(max_context_len), b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), int(num_sinks), int(window),
+            _ptr(attn_mass), mass_stride, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    p = _issue("paged_decode_append_attn", args, prepare)
+    return p if prepare else out
+
+
 def paged_prefill_attn(out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_context_len,
                        max_query_len, scale=None, k_scale=None, v_scale=None, stream=None, prepare=False):
     """Causal multi-query attention: q/out [T][Hq][D]; sequence s owns rows

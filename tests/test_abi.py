@@ -82,6 +82,34 @@ def test_attn_zero_sequences_is_a_no_op():
     assert lib.pkv_last_error() == b""
 
 
+def append_attn_args(k_new=FAKE, v_new=FAKE, src_dtype=1, **kw):
+    """paged_decode_append_attn's arguments: paged_decode_attn's with the new rows after q_dtype."""
+    a = attn_args(**kw)
+    return a[:4] + [k_new, v_new, src_dtype] + a[4:]
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(bs=8), _lib.EUNSUPPORTED),
+    (dict(hq=30), _lib.EINVAL),
+    (dict(stride=100), _lib.EINVAL),
+    (dict(kv_dtype=3), _lib.EINVAL),                     # FP8 without scales
+    (dict(ws_bytes=10), _lib.EWORKSPACE),
+    (dict(src_dtype=0), _lib.EUNSUPPORTED),              # f32 rows into a bf16 pool
+    (dict(src_dtype=5), _lib.EINVAL),
+    (dict(k_new=None), _lib.EINVAL),
+    (dict(v_new=ctypes.c_void_p(0x100008)), _lib.EINVAL),   # not 16-byte aligned
+])
+def test_append_attn_validation(change, status):
+    lib = _lib.load()
+    assert lib.paged_decode_append_attn(*append_attn_args(**change)) == status
+    assert lib.pkv_last_error() != b""
+
+
+def test_append_attn_zero_sequences_is_a_no_op():
+    lib = _lib.load()
+    assert lib.paged_decode_append_attn(*append_attn_args(b=0, out=None, q=None, k_new=None, v_new=None)) == _lib.OK
+
+
 def test_workspace_size():
     lib = _lib.load()
     f = lib.paged_decode_attn_workspace_size

@@ -604,6 +604,71 @@ def test_append_equals_slots_then_write(kv):
         assert np.max(np.abs(H.to_f64(out[s]) - ref)) <= TOL[kv]
 
 
+APPEND_ATTN_GRID = [
+    # kv, q, d, hq, hkv, num_sinks, window, mass
+    ("bf16", "bf16", 128, 32, 8, 0, 0, False),
+    ("bf16", "f32", 64, 16, 2, 0, 0, True),
+    ("bf16", "bf16", 128, 16, 1, 0, 0, False),
+    ("f16", "f16", 128, 16, 16, 4, 40, False),
+    ("f16", "bf16", 64, 8, 4, 0, 0, True),
+    ("f32", "f32", 64, 8, 2, 0, 0, False),
+    ("f32", "f32", 128, 16, 1, 2, 100, True),
+    ("fp8", "bf16", 128, 32, 8, 0, 0, False),
+    ("int8", "bf16", 128, 32, 8, 4, 64, True),
+    ("fp8_ch", "bf16", 64, 8, 2, 0, 0, False),
+]
+APPEND_LENS = (1, 15, 16, 17, 35, 70, 511, 512, 513, 1100, 2049, 300, 64)
+
+
+@pytest.mark.parametrize("kv,q,d,hq,hkv,sinks,window,mass", APPEND_ATTN_GRID)
+def test_append_attn_equals_append_then_attend(kv, q, d, hq, hkv, sinks, window, mass):
+    """paged_decode_append_attn (the new token enters the attention kernel's operands, and the kernel
+    stores it, for 16-bit and f32 pools) leaves the output, the pools and the H2O mass bit-identical to
+    paged_kv_append followed by paged_decode_attn, and matches the oracle.  Both calls get
+    max_context_len = 2048, so sequence 10 (2049 tokens) is unusable for attention (NaN) while its
+    token is still appended; sequence 11 has an unusable length and sequence 12 a last table entry
+    outside the pool (NaN outputs, nothing stored)."""
+    w = dataclasses.replace(_case_workload(kv, q, d, hq, hkv, seed=hq * 7 + d + hkv + window, lens=APPEND_LENS),
+                            num_sinks=sinks, window=window, extra_blocks=4)
+    a, b = H.Case(w, hold_last=True), H.Case(w, hold_last=True)
+    assert int(a.lay.lens[10]) == 2049 and a.lay.max_len == 2049
+    for c in (a, b):
+        c.lens[11] = 0
+        c.tables[12, (int(c.lay.lens[12]) - 1) // 16] = c.lay.num_blocks + 5
+    k_new, v_new = a.newest_rows()
+    ka, va, ksa, vsa = a.pools
+    kb, vb, ksb, vsb = b.pools
+    L = 2048
+    n = len(APPEND_LENS)
+    mass_a = torch.zeros((n, L), dtype=torch.float32, device="cuda") if mass else None
+    mass_b = mass_a.clone() if mass else None
+    out_a = torch.empty((n, hq, d), dtype=torch.float32, device="cuda")
+    out_b = torch.empty_like(out_a)
+    ops.paged_kv_append(k_new, v_new, ka, va, a.tables, a.lens, ksa, vsa)
+    ops.paged_decode_attn(out_a, a.q, ka, va, a.tables, a.lens, L, k_scale=ksa, v_scale=vsa, num_sinks=sinks,
+                          window=window, attn_mass=mass_a)
+    ops.paged_decode_append_attn(out_b, b.q, k_new, v_new, kb, vb, b.tables, b.lens, L, k_scale=ksb, v_scale=vsb,
+                                 num_sinks=sinks, window=window, attn_mass=mass_b)
+    torch.cuda.synchronize()
+    for x, y in zip(a.pools, b.pools):
+        if x is not None:
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    valid = [s for s in range(n) if s not in (10, 11, 12)]
+    assert torch.equal(out_a[valid], out_b[valid])
+    for s in (10, 11, 12):
+        assert torch.isnan(out_b[s]).all()
+    if mass:
+        assert torch.equal(mass_a[valid], mass_b[valid])
+        assert torch.equal(mass_b[10:12], torch.zeros_like(mass_b[10:12]))
+    err = max(float(np.max(np.abs(H.to_f64(out_b[s]) - b.oracle(s)[0]))) for s in valid)
+    print(f"append+attend {kv}/{q} D={d} G={hq // hkv} sinks={sinks} window={window}: max abs err {err:.3e}")
+    assert err <= TOL[kv]
+    if kv not in CODE8:   # sequence 10's token was stored, not skipped by both paths
+        slot = int(a.lay.tables[10][2048 // 16]) * 16 + 2048 % 16
+        assert torch.equal(H.k_token_rows(kb)[slot].contiguous().view(torch.uint8), k_new[10].view(torch.uint8))
+        assert torch.equal(H.v_token_rows(vb)[slot].contiguous().view(torch.uint8), v_new[10].view(torch.uint8))
+
+
 # ---------------------------------------------------------------------------- multi-query (chunked prefill)
 
 def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):
