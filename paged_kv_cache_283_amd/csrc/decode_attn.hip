@@ -781,11 +781,16 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
 // Log-sum-exp merge of one (sequence, query head) per wave: the partials of the
 // segments the sequence was cut into (block 0 and every multiple of R inside
 // the sequence's span of the block list).  A sequence that was one segment
-// already has its output.  Lane i takes segment i (64 at a time): wave max of
-// the segment maxima, weights exp2(m_i - M), then every lane sums its output
-// dims over the segments with the weights broadcast.
+// already has its output.  Segments go 16 at a time: every lane loads its
+// D / 64 output dims of all 16 partials and lane k the (max, sum) of segment
+// k, all before the first wait (the merge is latency-bound); then the wave
+// max, the weights exp2(m_k - M), and the weighted sums, with a running
+// rescale when a sequence has more than 16 segments.
 template <int D>
 __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
+  constexpr int kChunk = 16;
+  constexpr int DL = D / 64;                      // output dims per lane
+  using VT = typename std::conditional<DL == 2, float2, float>::type;
   const int s = blockIdx.y;
   const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -809,41 +814,53 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
   const size_t hs = (size_t)s * a.num_q_heads + h;
   const float* ml = a.part_ml + hs * a.p_max * 2;
   const float* pacc = a.part_acc + hs * a.p_max * D;
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += kWave) M = fmaxf(M, ml[2 * seg_slot(i)]);
+  float M = -INFINITY, lsum = 0.f;
+  float o[DL];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-  constexpr int DL = D / 64;
-  float o_acc[DL];
+  for (int e = 0; e < DL; ++e) o[e] = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kChunk) {
+    const int cnt = min(kChunk, n - i0);
+    VT v[kChunk];
 #pragma unroll
-  for (int e = 0; e < DL; ++e) o_acc[e] = 0.f;
-  float lpart = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kWave) {
-    const int i = i0 + lane;
-    int sl = 0;
-    float f = 0.f;
-    if (i < n) {
-      sl = seg_slot(i);
-      const float mi = ml[2 * sl];
-      f = mi == -INFINITY ? 0.f : fast_exp2(mi - M);
-      lpart += f * ml[2 * sl + 1];
+    for (int k = 0; k < kChunk; ++k)   // past cnt: the last segment again (weight 0, skipped)
+      v[k] = *reinterpret_cast<const VT*>(pacc + (size_t)seg_slot(i0 + min(k, cnt - 1)) * D + DL * lane);
+    float mi = -INFINITY, li = 0.f;
+    if (lane < cnt) {
+      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * seg_slot(i0 + lane));
+      mi = x.x;
+      li = x.y;
     }
-    const int cnt = min(kWave, n - i0);
-#pragma unroll 4
-    for (int k = 0; k < cnt; ++k) {
-      const float fk = __shfl(f, k, kWave);
-      const int sk = __shfl(sl, k, kWave);
+    float Mc = mi;
 #pragma unroll
-      for (int e = 0; e < DL; ++e) o_acc[e] += fk * pacc[(size_t)sk * D + e * 64 + lane];
+    for (int off = 32; off >= 1; off >>= 1) Mc = fmaxf(Mc, __shfl_xor(Mc, off, kWave));
+    const float Mn = fmaxf(M, Mc);
+    const float keep = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    const float f = mi == -INFINITY ? 0.f : fast_exp2(mi - Mn);
+    float lc = f * li;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lc += __shfl_xor(lc, off, kWave);
+    lsum = lsum * keep + lc;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) o[e] *= keep;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      if (k < cnt) {
+        const float fk = __shfl(f, k, kWave);
+        if constexpr (DL == 2) {
+          o[0] += fk * v[k].x;
+          o[1] += fk * v[k].y;
+        } else {
+          o[0] += fk * v[k];
+        }
+      }
     }
+    M = Mn;
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lpart += __shfl_xor(lpart, o, kWave);
-#pragma unroll
-  for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + e * 64 + lane, a.out_dtype, o_acc[e] / lpart);
+  for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + DL * lane + e, a.out_dtype, o[e] / lsum);
   if (a.fin_ml != nullptr && lane == 0) {
     a.fin_ml[hs * 2 + 0] = M;
-    a.fin_ml[hs * 2 + 1] = lpart;
+    a.fin_ml[hs * 2 + 1] = lsum;
   }
 }
 
