@@ -297,9 +297,9 @@ int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtyp
   if (!k_new || !v_new) return fail(PKV_EINVAL, "NULL array argument");
   if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)
     return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
-  if (code8_kv(kv_dtype)) {
-    // 8-bit pools: the token is quantised by the append kernel first; the
-    // attention kernel then reads it from the pool like any other.
+  if (code8_kv(kv_dtype) && src_dtype != q_dtype) {
+    // 8-bit pools fed from a dtype other than q's: the append kernel quantises
+    // the token first; the attention kernel then reads it from the pool.
     st = device_status(pkv::launch_kv_append(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                              block_tables, block_table_stride, context_lens, num_seqs, num_blocks,
                                              num_kv_heads, head_dim, (hipStream_t)stream),
@@ -310,6 +310,8 @@ int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtyp
     a.v_new = v_new;
     a.k_store = k_pool;
     a.v_store = v_pool;
+    a.k_scale_store = k_scale;
+    a.v_scale_store = v_scale;
   }
   return launch_prepared_attn(a, kv_dtype, q_dtype, head_dim, stream, "paged_decode_append_attn");
 }

@@ -48,6 +48,7 @@
 
 #include "device_common.hpp"
 #include "geometry.hpp"
+#include "kv_codec.hpp"
 #include "launch.hpp"
 #include "mfma_ops.hpp"
 
@@ -235,44 +236,80 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_pool);
   const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
 
-  // ---- decode append fused in (16-bit and f32 pools): the segment that ends
-  // the sequence loads the new token's K and V rows (position L - 1, offset
-  // o_new of the last attended block) together with its first table chunk and
-  // copies them to LDS next to the staged entries; the last block's operands
-  // get them patched in, so the products see exactly the bits the pool will
-  // hold.  The rows are stored into their slot when the wave has finished all
-  // its segments (append_stores): stores share the load counter, so a store
-  // issued here would hold up the wave's next tile waits until it completes.
-  constexpr bool kFusable = !is_code8(KVT);
-  constexpr int NW = D * EB / 4;          // words of one K or V row
-  constexpr int NWL = (NW + kWave - 1) / kWave;
-  const bool fuse = kFusable && a.k_new != nullptr && seg_vb1 == geo.n_virtual;
+  // ---- decode append fused in: the segment that ends the sequence loads the
+  // new token's K and V source rows (position L - 1, offset o_new of the last
+  // attended block) together with its first table chunk and puts the stored
+  // form in LDS next to the staged entries -- the rows themselves for 16-bit
+  // and f32 pools, the 8-bit codes (and the per-token scales in registers) for
+  // 8-bit pools, quantised exactly as the write kernels do; the last block's
+  // operands get them patched in, so the products see exactly the bits the
+  // pool will hold.  The rows are stored into their slot when the wave has
+  // finished all its segments (append_stores): stores share the load counter,
+  // so a store issued here would hold up the wave's next tile waits until it
+  // completes.  8-bit pools take the source in q's dtype.
+  constexpr bool C8 = is_code8(KVT);
+  constexpr int SEB = C8 ? (QT == DT_F32 ? 4 : 2) : EB;   // source element bytes
+  constexpr int NWS = D * SEB / 4;        // words of one source row
+  constexpr int NWL = (NWS + kWave - 1) / kWave;
+  constexpr int NW = D * EB / 4;          // words of one stored row in LDS
+  const bool fuse = a.k_new != nullptr && seg_vb1 == geo.n_virtual;
   const int o_new = (L - 1) & (kBlockSize - 1);
   const int vb_new = geo.n_virtual - 1;
-  uint32_t rk[kFusable ? NWL : 1], rv[kFusable ? NWL : 1];
+  uint32_t rk[NWL], rv[NWL];
+  float ks_new = 0.f, vs_new = 0.f;       // the new token's per-token scales (per-token 8-bit formats)
   auto fused_load = [&]() {
-    if constexpr (kFusable) {
-      const size_t row = ((size_t)s * a.num_kv_heads + kvh) * NW;
-      const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_new) + row;
-      const uint32_t* vr = reinterpret_cast<const uint32_t*>(a.v_new) + row;
+    const size_t row = ((size_t)s * a.num_kv_heads + kvh) * NWS;
+    const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_new) + row;
+    const uint32_t* vr = reinterpret_cast<const uint32_t*>(a.v_new) + row;
 #pragma unroll
-      for (int u = 0; u < NWL; ++u) {
-        const int k = min(lane + kWave * u, NW - 1);
-        rk[u] = kr[k];
-        rv[u] = vr[k];
-      }
+    for (int u = 0; u < NWL; ++u) {
+      const int k = min(lane + kWave * u, NWS - 1);
+      rk[u] = kr[k];
+      rv[u] = vr[k];
     }
   };
-  // The rows go to LDS for the patch once the first chunk's entries are
-  // staged (the same wait covers their loads).
+  // Once the first chunk's entries are staged (the same wait covers these loads).
   auto fused_stage = [&]() {
-    if constexpr (kFusable) {
+    if constexpr (!C8) {
 #pragma unroll
       for (int u = 0; u < NWL; ++u) {
         const int k = lane + kWave * u;
         if (k < NW) {
           s_new[k] = rk[u];
           s_new[NW + k] = rv[u];
+        }
+      }
+    } else {
+      constexpr int EPW = 4 / SEB;        // source elements per word
+      auto elem = [](uint32_t w, int i) { return SEB == 4 ? w : (w >> (16 * i)) & 0xffffu; };
+      if constexpr (is_quantised(KVT)) {
+        float km = 0.f, vm = 0.f;
+#pragma unroll
+        for (int u = 0; u < NWL; ++u) {
+          if (lane + kWave * u < NWS) {
+#pragma unroll
+            for (int i = 0; i < EPW; ++i) {
+              km = fmaxf(km, fabsf(raw_to_f32<QT>(elem(rk[u], i))));
+              vm = fmaxf(vm, fabsf(raw_to_f32<QT>(elem(rv[u], i))));
+            }
+          }
+        }
+        ks_new = __fdiv_rn(wave_max(km), max_code8<KVT>());
+        vs_new = __fdiv_rn(wave_max(vm), max_code8<KVT>());
+      }
+      uint8_t* sb = reinterpret_cast<uint8_t*>(s_new);
+#pragma unroll
+      for (int u = 0; u < NWL; ++u) {
+        const int k = lane + kWave * u;
+        if (k < NWS) {
+#pragma unroll
+          for (int i = 0; i < EPW; ++i) {
+            const int d = k * EPW + i;
+            const float kc = CH ? a.k_scale[(size_t)kvh * D + d] : ks_new;
+            const float vc = CH ? a.v_scale[(size_t)kvh * D + d] : vs_new;
+            sb[d] = (uint8_t)stored_code<QT, KVT>(elem(rk[u], i), kc);
+            sb[D + d] = (uint8_t)stored_code<QT, KVT>(elem(rv[u], i), vc);
+          }
         }
       }
     }
@@ -323,7 +360,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     const int vb = c0 + i;
     const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
 
-    if constexpr (kFusable && decltype(tail)::value) {
+    if constexpr (decltype(tail)::value) {
       if (fuse && vb == vb_new) {
         // K: token row o_new is lane column c == o_new, which takes chunks
         // 4w + j of the row.  V: tokens 4j..4j+3 sit in lane row j, so o_new is
@@ -340,14 +377,17 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if constexpr (EB == 2) vn[t] = reinterpret_cast<const uint16_t*>(s_new + NW)[16 * t + c];
+          if constexpr (EB == 1) vn[t] = reinterpret_cast<const uint8_t*>(s_new + NW)[16 * t + c];
+          else if constexpr (EB == 2) vn[t] = reinterpret_cast<const uint16_t*>(s_new + NW)[16 * t + c];
           else vn[t] = s_new[NW + 16 * t + c];
         }
 #pragma unroll
         for (int w = 0; w < KW; ++w) r.k[w] = krow ? kn[w] : r.k[w];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-          if constexpr (EB == 2) {
+          if constexpr (EB == 1) {
+            r.v[t][0] = vrow ? ((r.v[t][0] & ~(0xffu << (8 * e))) | (vn[t] << (8 * e))) : r.v[t][0];
+          } else if constexpr (EB == 2) {
             const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
             const uint32_t put = (e & 1) ? (vn[t] << 16) : vn[t];
             r.v[t][0] = (vrow && e < 2) ? ((r.v[t][0] & keep) | put) : r.v[t][0];
@@ -355,6 +395,13 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
           } else {
 #pragma unroll
             for (int ee = 0; ee < 4; ++ee) r.v[t][ee] = (vrow && ee == e) ? vn[t] : r.v[t][ee];
+          }
+        }
+        if constexpr (is_quantised(KVT)) {   // lane row j holds the scales of tokens 4j..4j+3
+#pragma unroll
+          for (int ee = 0; ee < 4; ++ee) {
+            r.ks[ee] = (vrow && ee == e) ? ks_new : r.ks[ee];
+            r.vs[ee] = (vrow && ee == e) ? vs_new : r.vs[ee];
           }
         }
       }
@@ -599,25 +646,73 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   }
 }
 
-// Word k of the fused decode append's K and V rows of (sequence sq, KV head h)
-// stored at offset (L - 1) % 16 of pool block blk.
-template <int KVT, int D>
-__device__ __forceinline__ void append_word(const AttnArgs& a, int sq, int h, int L, int blk, int k) {
+// The fused decode append's stores of (sequence sq, KV head h) at offset
+// (L - 1) % 16 of pool block blk: the source rows' bits (16-bit and f32
+// pools) or their 8-bit codes with the per-token scales, quantised exactly as
+// the write kernels do.  kWaveWide: the wave's 64 lanes share the row; else
+// the calling lane does it all.
+template <int KVT, int QT, int D, bool kWaveWide>
+__device__ __forceinline__ void append_row(const AttnArgs& a, int sq, int h, int L, int blk) {
   constexpr int EB = KvType<KVT>::kBytes;
-  constexpr int NW = D * EB / 4;
+  constexpr bool C8 = is_code8(KVT);
+  constexpr int SEB = C8 ? (QT == DT_F32 ? 4 : 2) : EB;   // source element bytes
+  constexpr int NWS = D * SEB / 4;
+  constexpr int EPW = 4 / SEB;
+  const int ln = kWaveWide ? (int)(threadIdx.x & 63) : 0;
+  constexpr int step = kWaveWide ? kWave : 1;
   const int o = (L - 1) & (kBlockSize - 1);
-  const size_t row = ((size_t)sq * a.num_kv_heads + h) * NW;
+  const size_t row = ((size_t)sq * a.num_kv_heads + h) * NWS;
+  const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_new) + row;
+  const uint32_t* vr = reinterpret_cast<const uint32_t*>(a.v_new) + row;
   const size_t tile = (size_t)blk * a.num_kv_heads + h;
   uint8_t* kt = reinterpret_cast<uint8_t*>(a.k_store) + tile * (size_t)(kBlockSize * D * EB);
   uint8_t* vt = reinterpret_cast<uint8_t*>(a.v_store) + tile * (size_t)(kBlockSize * D * EB);
-  const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k_new)[row + k];   // bytes 4k..4k+3 of the row
-  const uint32_t vw = reinterpret_cast<const uint32_t*>(a.v_new)[row + k];
-  *reinterpret_cast<uint32_t*>(kt + ((size_t)(k / 4) * kBlockSize + o) * 16 + (k % 4) * 4) = kw;
-  if constexpr (EB == 2) {
-    *reinterpret_cast<uint16_t*>(vt + (size_t)v_chunk_offset<2>(o, 2 * k) * 2) = (uint16_t)vw;
-    *reinterpret_cast<uint16_t*>(vt + (size_t)v_chunk_offset<2>(o, 2 * k + 1) * 2) = (uint16_t)(vw >> 16);
+  if constexpr (!C8) {
+    for (int k = ln; k < NWS; k += step) {   // bytes 4k..4k+3 of the row
+      const uint32_t kw = kr[k], vw = vr[k];
+      *reinterpret_cast<uint32_t*>(kt + ((size_t)(k / 4) * kBlockSize + o) * 16 + (k % 4) * 4) = kw;
+      if constexpr (EB == 2) {
+        *reinterpret_cast<uint16_t*>(vt + (size_t)v_chunk_offset<2>(o, 2 * k) * 2) = (uint16_t)vw;
+        *reinterpret_cast<uint16_t*>(vt + (size_t)v_chunk_offset<2>(o, 2 * k + 1) * 2) = (uint16_t)(vw >> 16);
+      } else {
+        *reinterpret_cast<uint32_t*>(vt + (size_t)v_chunk_offset<4>(o, k) * 4) = vw;
+      }
+    }
   } else {
-    *reinterpret_cast<uint32_t*>(vt + (size_t)v_chunk_offset<4>(o, k) * 4) = vw;
+    auto elem = [](uint32_t w, int i) { return SEB == 4 ? w : (w >> (16 * i)) & 0xffffu; };
+    float ks = 0.f, vs = 0.f;
+    if constexpr (is_quantised(KVT)) {
+      float km = 0.f, vm = 0.f;
+      for (int k = ln; k < NWS; k += step) {
+        const uint32_t kw = kr[k], vw = vr[k];
+#pragma unroll
+        for (int i = 0; i < EPW; ++i) {
+          km = fmaxf(km, fabsf(raw_to_f32<QT>(elem(kw, i))));
+          vm = fmaxf(vm, fabsf(raw_to_f32<QT>(elem(vw, i))));
+        }
+      }
+      if constexpr (kWaveWide) {
+        km = wave_max(km);
+        vm = wave_max(vm);
+      }
+      ks = __fdiv_rn(km, max_code8<KVT>());
+      vs = __fdiv_rn(vm, max_code8<KVT>());
+      if (ln == 0) {
+        a.k_scale_store[tile * kBlockSize + o] = ks;
+        a.v_scale_store[tile * kBlockSize + o] = vs;
+      }
+    }
+    for (int k = ln; k < NWS; k += step) {
+      const uint32_t kw = kr[k], vw = vr[k];
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) {
+        const int d = k * EPW + i;
+        const float kc = is_channel_scaled(KVT) ? a.k_scale[(size_t)h * D + d] : ks;
+        const float vc = is_channel_scaled(KVT) ? a.v_scale[(size_t)h * D + d] : vs;
+        store_elem<1>(kt + k_chunk_offset<1>(o, d), stored_code<QT, KVT>(elem(kw, i), kc));
+        store_elem<1>(vt + v_chunk_offset<1>(o, d), stored_code<QT, KVT>(elem(vw, i), vc));
+      }
+    }
   }
 }
 
@@ -634,17 +729,13 @@ __device__ __forceinline__ int append_block(const AttnArgs& a, int sq, int L) {
 // segments (nothing waits for them then): the rows of KV head kvh of every
 // sequence in [end_lo, end_hi] with attended blocks -- the sequences whose
 // last block this wave attended.
-template <int KVT, int D>
+template <int KVT, int QT, int D>
 __device__ __forceinline__ void append_stores(const AttnArgs& a, int kvh, int end_lo, int end_hi) {
-  constexpr int NW = D * KvType<KVT>::kBytes / 4;
-  const int lane = threadIdx.x & 63;
   for (int sq = end_lo; sq <= end_hi; ++sq) {
     const int L = a.context_lens[sq];
     if (attended_blocks(a, L) == 0) continue;   // stored in pass 1 of the kernel, if at all
     const int blk = append_block(a, sq, L);
-    if (blk < 0) continue;
-#pragma unroll
-    for (int k = lane; k < NW; k += kWave) append_word<KVT, D>(a, sq, kvh, L, blk, k);
+    if (blk >= 0) append_row<KVT, QT, D, true>(a, sq, kvh, L, blk);
   }
 }
 
@@ -677,8 +768,8 @@ __device__ __forceinline__ int wave_scan(int v) {
 template <int KVT, int QT, int D>
 __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   __shared__ int s_tab[kTabBlocks];
-  // the new token's K and V rows when the decode append is fused in (16-bit and f32 pools)
-  __shared__ uint32_t s_new[is_code8(KVT) ? 1 : 2 * D * KvType<KVT>::kBytes / 4];
+  // the new token's stored K and V rows when the decode append is fused in
+  __shared__ uint32_t s_new[2 * D * KvType<KVT>::kBytes / 4];
   const int hkv = a.num_kv_heads;
   const int B = a.num_seqs;
   const int lane = threadIdx.x;
@@ -698,15 +789,12 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     if (sq < B && nva == 0 && sq % (int)gridDim.x == (int)blockIdx.x) {
       for (int idx = 0; idx < a.num_q_heads * D; ++idx)
         store_out(a.out, (size_t)sq * a.num_q_heads * D + idx, a.out_dtype, __builtin_nanf(""));
-      if constexpr (!is_code8(KVT)) {
-        // no wave attends this sequence; its token is still stored where the
-        // decode append would store it (a length beyond max_context_len)
-        const int L = a.context_lens[sq];
-        const int blk = a.k_new != nullptr ? append_block(a, sq, L) : -1;
-        if (blk >= 0) {
-          for (int h = 0; h < hkv; ++h)
-            for (int k = 0; k < D * KvType<KVT>::kBytes / 4; ++k) append_word<KVT, D>(a, sq, h, L, blk, k);
-        }
+      // no wave attends this sequence; its token is still stored where the
+      // decode append would store it (a length beyond max_context_len)
+      const int L = a.context_lens[sq];
+      const int blk = a.k_new != nullptr ? append_block(a, sq, L) : -1;
+      if (blk >= 0) {
+        for (int h = 0; h < hkv; ++h) append_row<KVT, QT, D, false>(a, sq, h, L, blk);
       }
     }
     total += __shfl(incl, kWave - 1, kWave);
@@ -773,9 +861,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
       while (attended_blocks(a, a.context_lens[sq]) == 0) ++sq;
     }
   }
-  if constexpr (!is_code8(KVT)) {
-    if (a.k_new != nullptr) append_stores<KVT, D>(a, kvh, end_lo, end_hi);
-  }
+  if (a.k_new != nullptr) append_stores<KVT, QT, D>(a, kvh, end_lo, end_hi);
 }
 
 // Log-sum-exp merge of one (sequence, query head) per wave: the partials of the

@@ -54,36 +54,6 @@ __device__ __forceinline__ int64_t token_slot(const SlotSource& ss, int t, int n
   return (b < 0 || b >= num_blocks) ? (int64_t)-1 : (int64_t)b * kBlockSize + (L - 1) % kBlockSize;
 }
 
-// Value of a raw source element (16 or 32 bits, zero-extended).
-template <int SRC>
-__device__ __forceinline__ float raw_to_f32(uint32_t r) {
-  if constexpr (SRC == DT_F32) return __uint_as_float(r);
-  else if constexpr (SRC == DT_BF16) return bf16_to_f32(r);
-  else return f16_to_f32(r);
-}
-
-// Stored bits of one element from its raw source bits: the bits themselves
-// (pool dtype = source dtype), or the 8-bit code of value / scale, where the
-// scale is the row's (per-token formats; 0 gives code 0) or the channel's.
-template <int SRC, int KVT>
-__device__ __forceinline__ uint32_t stored_code(uint32_t raw, float scale) {
-  if constexpr (is_quantised(KVT)) return scale == 0.f ? 0u : encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(raw), scale));
-  else if constexpr (is_channel_scaled(KVT)) return encode8<KVT>(__fdiv_rn(raw_to_f32<SRC>(raw), scale));
-  else return raw;
-}
-
-template <int SRC>
-__device__ __forceinline__ uint32_t load_raw(const void* p, size_t i) {
-  if constexpr (SRC == DT_F32) return reinterpret_cast<const uint32_t*>(p)[i];
-  else return reinterpret_cast<const uint16_t*>(p)[i];
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
-}
-
 // One wave per (token, KV head) row, K and V together: the decode append,
 // whose tokens are one per sequence (no chunk of the layout holds two of
 // them), where latency is all that counts.  The source loads go out before the

@@ -41,14 +41,16 @@ struct AttnArgs {
   int* seq_prefix;      // [B + 1]  attended-block prefix per sequence, then the total
   int p_max;
   int nv_pad;
-  // Decode append fused in (16-bit and f32 pools): the new token of every
-  // sequence (position context_lens[s] - 1), [B][Hkv][D] in the pool's dtype,
-  // enters the last block's operands from here and is stored into the pools.
-  // Null: the pools already hold it.
+  // Decode append fused in: the new token of every sequence (position
+  // context_lens[s] - 1), [B][Hkv][D] in the pool's dtype (16-bit and f32
+  // pools) or q's dtype (8-bit pools), enters the last block's operands from
+  // here and is stored into the pools.  Null: the pools already hold it.
   const void* k_new;
   const void* v_new;
   void* k_store;        // the K and V pools, writable (fused append only)
   void* v_store;
+  float* k_scale_store; // per-token scale arrays, writable (fused append, per-token 8-bit formats)
+  float* v_scale_store;
 };
 
 // Causal multi-query attention over the paged cache (chunked prefill).

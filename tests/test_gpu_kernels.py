@@ -605,31 +605,38 @@ def test_append_equals_slots_then_write(kv):
 
 
 APPEND_ATTN_GRID = [
-    # kv, q, d, hq, hkv, num_sinks, window, mass
-    ("bf16", "bf16", 128, 32, 8, 0, 0, False),
-    ("bf16", "f32", 64, 16, 2, 0, 0, True),
-    ("bf16", "bf16", 128, 16, 1, 0, 0, False),
-    ("f16", "f16", 128, 16, 16, 4, 40, False),
-    ("f16", "bf16", 64, 8, 4, 0, 0, True),
-    ("f32", "f32", 64, 8, 2, 0, 0, False),
-    ("f32", "f32", 128, 16, 1, 2, 100, True),
-    ("fp8", "bf16", 128, 32, 8, 0, 0, False),
-    ("int8", "bf16", 128, 32, 8, 4, 64, True),
-    ("fp8_ch", "bf16", 64, 8, 2, 0, 0, False),
+    # kv, src, q, d, hq, hkv, num_sinks, window, mass   (8-bit pools: fused when src == q, else two launches)
+    ("bf16", "bf16", "bf16", 128, 32, 8, 0, 0, False),
+    ("bf16", "bf16", "f32", 64, 16, 2, 0, 0, True),
+    ("bf16", "bf16", "bf16", 128, 16, 1, 0, 0, False),
+    ("f16", "f16", "f16", 128, 16, 16, 4, 40, False),
+    ("f16", "f16", "bf16", 64, 8, 4, 0, 0, True),
+    ("f32", "f32", "f32", 64, 8, 2, 0, 0, False),
+    ("f32", "f32", "f32", 128, 16, 1, 2, 100, True),
+    ("fp8", "bf16", "bf16", 128, 32, 8, 0, 0, False),
+    ("fp8", "f32", "f32", 64, 8, 2, 4, 40, True),
+    ("fp8", "bf16", "f16", 128, 16, 2, 0, 0, False),
+    ("int8", "bf16", "bf16", 128, 32, 8, 4, 64, True),
+    ("int8", "f16", "f16", 64, 16, 16, 0, 0, False),
+    ("int8", "bf16", "f32", 128, 8, 8, 0, 0, False),
+    ("fp8_ch", "bf16", "bf16", 64, 8, 2, 0, 0, False),
+    ("fp8_ch", "bf16", "bf16", 128, 32, 8, 0, 0, True),
+    ("int8_ch", "bf16", "bf16", 128, 16, 2, 0, 0, False),
+    ("int8_ch", "f32", "f32", 64, 8, 4, 0, 0, False),
 ]
 APPEND_LENS = (1, 15, 16, 17, 35, 70, 511, 512, 513, 1100, 2049, 300, 64)
 
 
-@pytest.mark.parametrize("kv,q,d,hq,hkv,sinks,window,mass", APPEND_ATTN_GRID)
-def test_append_attn_equals_append_then_attend(kv, q, d, hq, hkv, sinks, window, mass):
-    """paged_decode_append_attn (the new token enters the attention kernel's operands, and the kernel
-    stores it, for 16-bit and f32 pools) leaves the output, the pools and the H2O mass bit-identical to
-    paged_kv_append followed by paged_decode_attn, and matches the oracle.  Both calls get
+@pytest.mark.parametrize("kv,src,q,d,hq,hkv,sinks,window,mass", APPEND_ATTN_GRID)
+def test_append_attn_equals_append_then_attend(kv, src, q, d, hq, hkv, sinks, window, mass):
+    """paged_decode_append_attn (the new token -- quantised in the kernel for 8-bit pools -- enters the
+    attention kernel's operands, and the kernel stores it) leaves the output, the pools and the H2O
+    mass bit-identical to paged_kv_append followed by paged_decode_attn, and matches the oracle.  Both calls get
     max_context_len = 2048, so sequence 10 (2049 tokens) is unusable for attention (NaN) while its
     token is still appended; sequence 11 has an unusable length and sequence 12 a last table entry
     outside the pool (NaN outputs, nothing stored)."""
     w = dataclasses.replace(_case_workload(kv, q, d, hq, hkv, seed=hq * 7 + d + hkv + window, lens=APPEND_LENS),
-                            num_sinks=sinks, window=window, extra_blocks=4)
+                            src_dtype=src, num_sinks=sinks, window=window, extra_blocks=4)
     a, b = H.Case(w, hold_last=True), H.Case(w, hold_last=True)
     assert int(a.lay.lens[10]) == 2049 and a.lay.max_len == 2049
     for c in (a, b):
@@ -661,7 +668,7 @@ def test_append_attn_equals_append_then_attend(kv, q, d, hq, hkv, sinks, window,
         assert torch.equal(mass_a[valid], mass_b[valid])
         assert torch.equal(mass_b[10:12], torch.zeros_like(mass_b[10:12]))
     err = max(float(np.max(np.abs(H.to_f64(out_b[s]) - b.oracle(s)[0]))) for s in valid)
-    print(f"append+attend {kv}/{q} D={d} G={hq // hkv} sinks={sinks} window={window}: max abs err {err:.3e}")
+    print(f"append+attend {kv}<-{src}/{q} D={d} G={hq // hkv} sinks={sinks} window={window}: max abs err {err:.3e}")
     assert err <= TOL[kv]
     if kv not in CODE8:   # sequence 10's token was stored, not skipped by both paths
         slot = int(a.lay.tables[10][2048 // 16]) * 16 + 2048 % 16
