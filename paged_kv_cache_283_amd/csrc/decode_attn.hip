@@ -248,16 +248,18 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   // so a store issued here would hold up the wave's next tile waits until it
   // completes.  8-bit pools take the source in q's dtype.
   constexpr bool C8 = is_code8(KVT);
+  constexpr bool kFuse = fused_append_built(KVT);
   constexpr int SEB = C8 ? (QT == DT_F32 ? 4 : 2) : EB;   // source element bytes
   constexpr int NWS = D * SEB / 4;        // words of one source row
   constexpr int NWL = (NWS + kWave - 1) / kWave;
   constexpr int NW = D * EB / 4;          // words of one stored row in LDS
-  const bool fuse = a.k_new != nullptr && seg_vb1 == geo.n_virtual;
+  const bool fuse = kFuse && a.k_new != nullptr && seg_vb1 == geo.n_virtual;
   const int o_new = (L - 1) & (kBlockSize - 1);
   const int vb_new = geo.n_virtual - 1;
   uint32_t rk[NWL], rv[NWL];
   float ks_new = 0.f, vs_new = 0.f;       // the new token's per-token scales (per-token 8-bit formats)
   auto fused_load = [&]() {
+    if constexpr (!kFuse) return;
     const size_t row = ((size_t)s * a.num_kv_heads + kvh) * NWS;
     const uint32_t* kr = reinterpret_cast<const uint32_t*>(a.k_new) + row;
     const uint32_t* vr = reinterpret_cast<const uint32_t*>(a.v_new) + row;
@@ -270,7 +272,8 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   };
   // Once the first chunk's entries are staged (the same wait covers these loads).
   auto fused_stage = [&]() {
-    if constexpr (!C8) {
+    if constexpr (!kFuse) {
+    } else if constexpr (!C8) {
 #pragma unroll
       for (int u = 0; u < NWL; ++u) {
         const int k = lane + kWave * u;
@@ -360,7 +363,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     const int vb = c0 + i;
     const int lb = logical_block(vb, geo.n_sink_blocks, geo.win_start);
 
-    if constexpr (decltype(tail)::value) {
+    if constexpr (kFuse && decltype(tail)::value) {
       if (fuse && vb == vb_new) {
         // K: token row o_new is lane column c == o_new, which takes chunks
         // 4w + j of the row.  V: tokens 4j..4j+3 sit in lane row j, so o_new is
@@ -550,19 +553,22 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     const int n = min(kTabBlocks, seg_vb1 - c0);
     const bool first = fuse && c0 == seg_vb0;
     {
-      // Every entry load goes out before the first is waited for (indices
-      // past the chunk reload its last entry, so no load is conditional); the
-      // fused append's row loads join them.
-      constexpr int TU = kTabBlocks / kWave;
-      int ent[TU];
-#pragma unroll
-      for (int u = 0; u < TU; ++u)
-        ent[u] = trow[logical_block(c0 + min(lane + kWave * u, n - 1), geo.n_sink_blocks, geo.win_start)];
+      // 512 entries per memory latency: every lane issues 8 entry loads before
+      // the first is waited for (indices past the chunk reload its last entry,
+      // so no load is conditional); the fused append's row loads join the
+      // first round.  (16 loads per lane raised every instance by ~16 VGPRs.)
+      constexpr int TU = 8;
       if (first) fused_load();
+      for (int b0 = 0; b0 < n; b0 += kWave * TU) {
+        int ent[TU];
 #pragma unroll
-      for (int u = 0; u < TU; ++u) {
-        const int k = lane + kWave * u;
-        if (k < n) s_tab[k] = ent[u];
+        for (int u = 0; u < TU; ++u)
+          ent[u] = trow[logical_block(c0 + min(b0 + lane + kWave * u, n - 1), geo.n_sink_blocks, geo.win_start)];
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+          const int k = b0 + lane + kWave * u;
+          if (k < n) s_tab[k] = ent[u];
+        }
       }
       if (first) fused_stage();
     }
@@ -789,12 +795,14 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     if (sq < B && nva == 0 && sq % (int)gridDim.x == (int)blockIdx.x) {
       for (int idx = 0; idx < a.num_q_heads * D; ++idx)
         store_out(a.out, (size_t)sq * a.num_q_heads * D + idx, a.out_dtype, __builtin_nanf(""));
-      // no wave attends this sequence; its token is still stored where the
-      // decode append would store it (a length beyond max_context_len)
-      const int L = a.context_lens[sq];
-      const int blk = a.k_new != nullptr ? append_block(a, sq, L) : -1;
-      if (blk >= 0) {
-        for (int h = 0; h < hkv; ++h) append_row<KVT, QT, D, false>(a, sq, h, L, blk);
+      if constexpr (fused_append_built(KVT)) {
+        // no wave attends this sequence; its token is still stored where the
+        // decode append would store it (a length beyond max_context_len)
+        const int L = a.context_lens[sq];
+        const int blk = a.k_new != nullptr ? append_block(a, sq, L) : -1;
+        if (blk >= 0) {
+          for (int h = 0; h < hkv; ++h) append_row<KVT, QT, D, false>(a, sq, h, L, blk);
+        }
       }
     }
     total += __shfl(incl, kWave - 1, kWave);
@@ -861,7 +869,9 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
       while (attended_blocks(a, a.context_lens[sq]) == 0) ++sq;
     }
   }
-  if (a.k_new != nullptr) append_stores<KVT, QT, D>(a, kvh, end_lo, end_hi);
+  if constexpr (fused_append_built(KVT)) {
+    if (a.k_new != nullptr) append_stores<KVT, QT, D>(a, kvh, end_lo, end_hi);
+  }
 }
 
 // Log-sum-exp merge of one (sequence, query head) per wave: the partials of the

@@ -6,7 +6,17 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "pagedkv.h"
+
 namespace pkv {
+
+// Pool formats whose decode append the attention kernel takes in itself
+// (paged_decode_append_attn): all but the INT8 ones, whose attention kernel
+// already sits at the register limit of two waves per SIMD and measured 16%
+// slower with the append code compiled in.
+__host__ __device__ constexpr bool fused_append_built(int kv_dtype) {
+  return kv_dtype != PKV_INT8 && kv_dtype != PKV_INT8_CHANNEL;
+}
 
 // Per-call schedule the attention kernel hands to the merge kernel (workspace).
 struct StreamHdr {
