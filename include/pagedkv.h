@@ -133,6 +133,7 @@ int paged_token_slots(const int32_t* block_tables, int block_table_stride, int n
  *   k_scale, v_scale   required for the 8-bit formats (written for per-token
  *                  formats, read for _CHANNEL ones), ignored otherwise
  *   slot_mapping   int64 [num_tokens]; a slot < 0 or >= num_blocks*16 skips the token
+ * num_tokens * num_kv_heads must stay <= 2^28 (PKV_EINVAL otherwise).
  * Two tokens with the same slot race (one of them wins).
  */
 int paged_kv_write(const void* k_new, const void* v_new, int src_dtype,
@@ -150,6 +151,7 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype,
  * outside [1, 16 * stride], table entry outside [0, num_blocks)) is skipped.
  *   k_new, v_new   [num_seqs][num_kv_heads][head_dim] of src_dtype
  *   block_tables   int32 [num_seqs][block_table_stride]; context_lens int32 [num_seqs]
+ * num_seqs * num_kv_heads must stay <= 2^26 (PKV_EINVAL otherwise).
  */
 int paged_kv_append(const void* k_new, const void* v_new, int src_dtype,
                     void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,

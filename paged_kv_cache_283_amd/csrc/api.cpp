@@ -122,8 +122,8 @@ int paged_kv_write(const void* k_new, const void* v_new, int src_dtype, void* k_
   if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens %d < 0", num_tokens);
   if (num_kv_heads < 1 || num_kv_heads > 65535) return fail(PKV_EINVAL, "num_kv_heads %d outside [1, 65535]", num_kv_heads);
   if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
-  if ((long long)num_tokens * num_kv_heads > (1LL << 32))
-    return fail(PKV_EINVAL, "num_tokens * num_kv_heads too large");
+  if ((long long)num_tokens * num_kv_heads > (1LL << 28))   // 16 threads per row in one grid dimension
+    return fail(PKV_EINVAL, "num_tokens * num_kv_heads %lld > 2^28", (long long)num_tokens * num_kv_heads);
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return fail(PKV_EINVAL, "NULL array argument");
   if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16)
@@ -150,7 +150,8 @@ int paged_kv_append(const void* k_new, const void* v_new, int src_dtype, void* k
   if (num_blocks < 1) return fail(PKV_EINVAL, "num_blocks %d < 1", num_blocks);
   if (block_table_stride < 1 || block_table_stride > (1 << 26))
     return fail(PKV_EINVAL, "block_table_stride %d outside [1, 2^26]", block_table_stride);
-  if ((long long)num_seqs * num_kv_heads > (1LL << 32)) return fail(PKV_EINVAL, "num_seqs * num_kv_heads too large");
+  if ((long long)num_seqs * num_kv_heads > (1LL << 26))   // 64 threads per row in one grid dimension
+    return fail(PKV_EINVAL, "num_seqs * num_kv_heads %lld > 2^26", (long long)num_seqs * num_kv_heads);
   if (num_seqs == 0) return ok();
   if (!k_new || !v_new || !k_pool || !v_pool || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "NULL array argument");
@@ -293,6 +294,8 @@ int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtyp
   if (!valid_float_dtype(src_dtype)) return fail(PKV_EINVAL, "src_dtype %d", src_dtype);
   if (!code8_kv(kv_dtype) && src_dtype != kv_dtype)
     return fail(PKV_EUNSUPPORTED, "a non-quantised pool takes source of its own dtype (src %d, kv %d)", src_dtype, kv_dtype);
+  if ((long long)num_seqs * num_kv_heads > (1LL << 26))   // the append kernel's limit (INT8 pools)
+    return fail(PKV_EINVAL, "num_seqs * num_kv_heads %lld > 2^26", (long long)num_seqs * num_kv_heads);
   if (num_seqs == 0) return ok();
   if (!k_new || !v_new) return fail(PKV_EINVAL, "NULL array argument");
   if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)

@@ -139,13 +139,17 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   __shared__ int s_lead[kWriteGroup];          // V: 1 leads a complete quad, 2 is covered by one, 0 neither
 
   const int tid = threadIdx.x;
-  const int h = blockIdx.y;
-  const int t_base = blockIdx.x * kWriteGroup;
+  // KV head fastest: the heads of one token group read one contiguous stretch
+  // of the source and write side-by-side tiles of the pool.
+  const int h = (int)(blockIdx.x % (unsigned)num_kv_heads);
+  const int t_base = (int)(blockIdx.x / (unsigned)num_kv_heads) * kWriteGroup;
+  long long my_slot = -1;                      // lanes 0..15: token t_base + lane
   if (tid < kWriteGroup) {
     const int t = t_base + tid;
     int64_t sl = t < num_tokens ? token_slot(ss, t, num_blocks) : -1;
     if (sl >= (int64_t)num_blocks * kBlockSize) sl = -1;
-    s_slot[tid] = sl < 0 ? -1 : sl;
+    my_slot = sl < 0 ? -1 : sl;
+    s_slot[tid] = my_slot;
   }
   // Both rows of every token, with 16-byte loads: K and V, row o, elements
   // [8 p, 8 p + 8) (16-bit source) or [4 p, 4 p + 4) (f32).  They do not wait
@@ -165,19 +169,19 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    // V quads: token o leads one when it and the next 3 tokens hold rows
-    // 4k..4k+3 of one block in slot order (1); the 3 others are covered (2).
-    for (int o = 0; o < kWriteGroup; ++o) s_lead[o] = 0;
-    for (int o = 0; o + 3 < kWriteGroup; ++o) {
-      const int64_t sl = s_slot[o];
-      bool lead = sl >= 0 && sl % 4 == 0 && s_lead[o] == 0;
-      for (int e = 1; lead && e < 4; ++e) lead = s_slot[o + e] == sl + e;
-      if (lead) {
-        s_lead[o] = 1;
-        s_lead[o + 1] = s_lead[o + 2] = s_lead[o + 3] = 2;
-      }
-    }
+  if (tid < kWave) {
+    // V quads, in the first wave's registers: token o leads one when it and
+    // the next 3 tokens hold rows 4k..4k+3 of one block in slot order (1); the
+    // 3 others are covered (2).  A covered token's slot is not a multiple of
+    // 4, so no token both leads and is covered.
+    const long long n1 = __shfl_down(my_slot, 1, kWave), n2 = __shfl_down(my_slot, 2, kWave),
+                    n3 = __shfl_down(my_slot, 3, kWave);
+    const bool lead = tid + 3 < kWriteGroup && my_slot >= 0 && my_slot % 4 == 0 && n1 == my_slot + 1 &&
+                      n2 == my_slot + 2 && n3 == my_slot + 3;
+    const int l1 = __shfl_up((int)lead, 1, kWave), l2 = __shfl_up((int)lead, 2, kWave),
+              l3 = __shfl_up((int)lead, 3, kWave);
+    const bool covered = (tid >= 1 && l1) || (tid >= 2 && l2) || (tid >= 3 && l3);
+    if (tid < kWriteGroup) s_lead[tid] = lead ? 1 : (covered ? 2 : 0);
   }
   if constexpr (is_quantised(KVT)) {
     // 8 threads per (K or V, row): absmax, then the row's scale
@@ -287,7 +291,7 @@ template <int SRC, int KVT, int D>
 void launch_write(const void* k_new, const void* v_new, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                   const SlotSource& ss, int num_tokens, int num_blocks, int num_kv_heads, hipStream_t st) {
   if (ss.slots != nullptr) {
-    dim3 grid((unsigned)((num_tokens + kWriteGroup - 1) / kWriteGroup), (unsigned)num_kv_heads);
+    dim3 grid((unsigned)((num_tokens + kWriteGroup - 1) / kWriteGroup) * (unsigned)num_kv_heads);
     hipLaunchKernelGGL((kv_write_kernel<SRC, KVT, D>), grid, dim3(kWriteThreads), 0, st, k_new, v_new, k_pool, v_pool,
                        k_scale, v_scale, ss, num_tokens, num_blocks, num_kv_heads);
   } else {

@@ -138,6 +138,7 @@ def test_write_validation():
     odd = ctypes.c_void_p(0x100008)
     assert w(odd, *base[1:]) == _lib.EINVAL                          # source not 16-byte aligned
     assert w(*base[:11], 70000, *base[12:]) == _lib.EINVAL           # more KV heads than the grid takes
+    assert w(*base[:9], 1 << 26, 100, 8, *base[12:]) == _lib.EINVAL     # 2^29 rows: more than the grid takes
 
 
 def test_copy_select_slots_probe_validation():
