@@ -105,6 +105,18 @@ class Case:
         slots = ops.paged_decode_slots(self.tables, self.lens, self.lay.num_blocks)
         ops.paged_kv_write(k_new, v_new, k, v, slots, ks, vs)
 
+    def decode_step(self, out_dtype=torch.float32, attn_mass=None):
+        """The decode step bench.py times: paged_decode_append_attn writes every sequence's newest token
+        (held back by the fill) and attends over the cache that holds it."""
+        w = self.w
+        k_new, v_new = self.newest_rows()
+        out = torch.empty(self.q.shape, dtype=out_dtype, device=DEV)
+        k, v, ks, vs = self.pools
+        ops.paged_decode_append_attn(out, self.q, k_new, v_new, k, v, self.tables, self.lens, self.lay.max_len,
+                                     k_scale=ks, v_scale=vs, num_sinks=w.num_sinks, window=w.window,
+                                     attn_mass=attn_mass)
+        return out
+
     def attend(self, out_dtype=torch.float32, q=None, scale=None, attn_mass=None, num_sinks=None, window=None):
         w = self.w
         q = self.q if q is None else q

@@ -1,9 +1,10 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
-Each test builds the workload's pools through the HIP write path (the newest
-token of every sequence through the decode-step path), runs decode attention,
-and compares with the fp64 oracle on the seeded source rows: every sequence
-where the oracle is quick, a stated sample otherwise.
+Each test builds the workload's pools through the HIP write path, holding back
+the newest token of every sequence, then runs the decode step bench.py times
+(paged_decode_append_attn: the newest tokens written and attended in one
+call) and compares with the fp64 oracle on the seeded source rows: every
+sequence where the oracle is quick, a stated sample otherwise.
 """
 import math
 
@@ -22,7 +23,7 @@ if torch.cuda.is_available():
 
 
 def _check(case, seqs, tol, **kw):
-    out = case.attend(**kw)
+    out = case.decode_step(**kw)
     worst = 0.0
     for s in seqs:
         ref, _ = case.oracle(s)
@@ -35,15 +36,15 @@ def _check(case, seqs, tol, **kw):
 def test_llama3_layer_decode_step_all_sequences():
     w = W.WORKLOADS["llama3"]
     case = H.Case(w, hold_last=True)
-    case.decode_write()
     out = _check(case, range(w.num_seqs), 2e-3)
     assert torch.isfinite(out).all()
+    # bench.py's output dtype (bf16 for bf16 queries): the same result rounded once
+    assert torch.equal(case.decode_step(out_dtype=torch.bfloat16), out.to(torch.bfloat16))
 
 
 def test_fp8_long_shared_prefix_and_copy_on_write():
     w = W.WORKLOADS["fp8long"]
     case = H.Case(w, hold_last=True)
-    case.decode_write()
     lay = case.lay
     assert (lay.tables[:4, :128] == lay.tables[0, :128]).all()
     sample = [0, 3, 7, 15]                                  # two sharers, two private sequences
@@ -61,7 +62,6 @@ def test_fp8_long_shared_prefix_and_copy_on_write():
 def test_streaming_all_sequences():
     w = W.WORKLOADS["streaming"]
     case = H.Case(w, hold_last=True)
-    case.decode_write()
     assert (case.lay.tables == -1).sum() > 0.9 * case.lay.tables.size
     _check(case, range(w.num_seqs), 2e-3)
 
@@ -69,10 +69,9 @@ def test_streaming_all_sequences():
 def test_h2o_mass_and_keep_set_contract():
     w = W.WORKLOADS["h2o"]
     case = H.Case(w, hold_last=True)
-    case.decode_write()
     L = case.lay.max_len
     scores = torch.zeros((w.num_seqs, L), dtype=torch.float32, device="cuda")
-    out = case.attend(attn_mass=scores)
+    out = case.decode_step(attn_mass=scores)
     keep_idx, keep_cnt = ops.h2o_select(scores, case.lens, L, w.budget, w.recent)
     got_scores = scores.cpu().numpy().astype(np.float64)
     keep_idx = keep_idx.cpu().numpy()
@@ -96,16 +95,19 @@ def test_h2o_mass_and_keep_set_contract():
 
 
 def test_llama2_stack_80_layers_sampled():
-    """80 resident 1 GiB layer pools; the oracle checks all 8 sequences on 8 spread layers."""
+    """80 resident 1 GiB layer pools; the decode step (append + attend) on every layer; the oracle checks
+    all 8 sequences on 8 spread layers."""
     w = W.WORKLOADS["llama2"]
     lay = W.make_layout(w)
     tables = torch.from_numpy(lay.tables).cuda()
     lens = torch.from_numpy(lay.lens).cuda()
-    pools = []
+    newest = torch.from_numpy(H.newest_rows(lay)).cuda()
+    pools, new_rows = [], []
     for layer in range(w.num_layers):
         p = H.make_pools(w, lay.num_blocks)
         ksrc, vsrc = W.kv_source(w, lay, layer=layer, device="cuda")
-        H.fill(w, lay, p, ksrc, vsrc, tables)
+        H.fill(w, lay, p, ksrc, vsrc, tables, hold_last=True)
+        new_rows.append((ksrc.index_select(0, newest).contiguous(), vsrc.index_select(0, newest).contiguous()))
         del ksrc, vsrc
         pools.append(p)
     ws = ops.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, lay.max_len)
@@ -113,7 +115,8 @@ def test_llama2_stack_80_layers_sampled():
     for layer in range(w.num_layers):
         q = W.queries(w, layer=layer, device="cuda")
         o = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-        ops.paged_decode_attn(o, q, pools[layer][0], pools[layer][1], tables, lens, lay.max_len, workspace=ws)
+        ops.paged_decode_append_attn(o, q, *new_rows[layer], pools[layer][0], pools[layer][1], tables, lens,
+                                     lay.max_len, workspace=ws)
         outs.append(o)
     torch.cuda.synchronize()
     worst = 0.0
@@ -135,7 +138,6 @@ def test_8bit_codec_long_contexts_sampled(name):
     checks four sequences spread over the batch."""
     w = W.WORKLOADS[name]
     case = H.Case(w, hold_last=True)
-    case.decode_write()
     out = _check(case, [0, 5, 10, 15], 1e-2)
     assert torch.isfinite(out).all()
 
