@@ -382,7 +382,8 @@ int kv_keep_select(const float* scores, int scores_stride, const int32_t* kv_len
  * holds n tokens in ceil(n / 16) destination blocks; the host releases the
  * source blocks (BlockManager.compact).
  *   src_tables, dst_tables  int32 [num_seqs][src_stride], [num_seqs][dst_stride]
- *   keep_idx     int32 [num_seqs][keep_stride]; keep_count int32 [num_seqs]
+ *   keep_idx     int32 [num_seqs][keep_stride]; keep_count int32 [num_seqs];
+ *                ceil(keep_stride / 16) * num_kv_heads <= 2^24 (PKV_EINVAL otherwise)
  * Destination slots must not be source slots of a token copied in the same call
  * (use fresh blocks); otherwise the result is undefined.  Slots of the last
  * destination block beyond n are left as they were.  A sequence whose count is

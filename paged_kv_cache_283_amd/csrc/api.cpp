@@ -468,6 +468,8 @@ int kv_compact(void* k_pool, void* v_pool, float* k_scale, float* v_scale, int k
   if (src_stride < 1 || src_stride > (1 << 26) || dst_stride < 1 || dst_stride > (1 << 26))
     return fail(PKV_EINVAL, "table strides %d, %d outside [1, 2^26]", src_stride, dst_stride);
   if (keep_stride < 0 || keep_stride > (1 << 30)) return fail(PKV_EINVAL, "keep_stride %d outside [0, 2^30]", keep_stride);
+  if ((long long)((keep_stride + 15) / 16) * num_kv_heads > (1LL << 24))   // 256 threads each in one grid dimension
+    return fail(PKV_EINVAL, "ceil(keep_stride / 16) * num_kv_heads > 2^24");
   if (num_seqs == 0 || keep_stride == 0) return ok();
   if (!k_pool || !v_pool || !src_tables || !dst_tables || !keep_idx || !keep_count)
     return fail(PKV_EINVAL, "NULL array argument");

@@ -9,7 +9,7 @@
 // destination table, so the sequence occupies ceil(n / 16) blocks and the
 // source blocks can be released.
 //
-// One 256-thread workgroup per (destination block, KV head, sequence) writes
+// One 256-thread workgroup per (KV head, destination block, sequence) writes
 // whole 16-byte chunks of the destination tile: a K chunk is one token row's
 // 16 bytes (read as one chunk of the source token's tile); a V chunk holds 4
 // tokens x Y dims and is gathered element by element.  Chunks that hold both
@@ -39,7 +39,9 @@ __global__ void __launch_bounds__(256) kv_compact_kernel(uint8_t* k_pool, uint8_
   constexpr size_t kTile = (size_t)kBlockSize * D * EB;
   __shared__ int s_blk[kBlockSize];                 // source block of destination token o (-1: poison)
   __shared__ int s_off[kBlockSize];                 // its offset in that block
-  const int s = blockIdx.z, h = blockIdx.y, db = blockIdx.x;
+  // KV head fastest: the heads of one destination block write side-by-side
+  // tiles and read the same kept tokens from side-by-side source tiles.
+  const int s = blockIdx.z, h = (int)(blockIdx.x % (unsigned)num_kv_heads), db = (int)(blockIdx.x / (unsigned)num_kv_heads);
   const int tid = threadIdx.x;
   const int cnt = keep_count[s];
   if (cnt < 0 || cnt > keep_stride || cnt > dst_stride * kBlockSize) return;
@@ -116,7 +118,7 @@ hipError_t compact_d(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                      int src_stride, const int32_t* dst_tables, int dst_stride, const int32_t* keep_idx,
                      int keep_stride, const int32_t* keep_count, int num_seqs, int num_blocks, int num_kv_heads,
                      int head_dim, hipStream_t st) {
-  dim3 grid((keep_stride + kBlockSize - 1) / kBlockSize, num_kv_heads, num_seqs);
+  dim3 grid((unsigned)((keep_stride + kBlockSize - 1) / kBlockSize) * (unsigned)num_kv_heads, 1, num_seqs);
   if (head_dim == 64)
     hipLaunchKernelGGL((kv_compact_kernel<EB, 64>), grid, dim3(256), 0, st, reinterpret_cast<uint8_t*>(k_pool),
                        reinterpret_cast<uint8_t*>(v_pool), k_scale, v_scale, src_tables, src_stride, dst_tables,
