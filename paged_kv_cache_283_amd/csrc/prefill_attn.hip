@@ -432,7 +432,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 
   for (; c0 < n_blocks; c0 += kPfTab) {
     const int n = min(kPfTab, n_blocks - c0);
-    for (int k = lane; k < n; k += kWave) s_tab[k] = trow[c0 + k];
+    // 512 entries per memory latency: every lane issues 8 entry loads before
+    // the first is waited for (indices past the chunk reload its last entry)
+    for (int b0 = 0; b0 < n; b0 += kWave * 8) {
+      int ent[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ent[u] = trow[c0 + min(b0 + lane + kWave * u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = b0 + lane + kWave * u;
+        if (k < n) s_tab[k] = ent[u];
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
