@@ -134,7 +134,12 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   constexpr bool KF16 = code_set(KVT) == DT_INT8 && is_code8(KVT);
   constexpr bool QF16 = F16 || KF16;            // QK operand type
   constexpr bool QSAME = (!OP32) && (QT == (QF16 ? DT_F16 : DT_BF16)) && !CH;
-  constexpr bool QSPLIT = (!OP32) && !QSAME;
+  // bf16 queries against INT8's f16 K operands: after the power-of-two
+  // prescale every bf16 value of magnitude >= 2^-17 (8 significant bits) is an
+  // f16 value exactly, and smaller ones round at f16's subnormal spacing in the
+  // low half too, so the low half adds nothing and one MFMA per step does.
+  constexpr bool QEXACT = KF16 && QT == DT_BF16 && !CH;
+  constexpr bool QSPLIT = (!OP32) && !QSAME && !QEXACT;
   constexpr int QW = OP32 ? 1 : DPL / 2;  // 16-bit operand words of q per lane
 
   const int hq = a.num_q_heads;
@@ -206,7 +211,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
         const uint32_t l0 = to_op16<QF16>(f0 - from_op16<QF16>(h0));
         const uint32_t l1 = to_op16<QF16>(f1 - from_op16<QF16>(h1));
         qhi[w] = h0 | (h1 << 16);
-        qlo[w] = l0 | (l1 << 16);
+        if constexpr (QSPLIT) qlo[w] = l0 | (l1 << 16);
       }
     }
   }

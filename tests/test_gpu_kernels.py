@@ -182,15 +182,16 @@ def test_attention_matches_oracle(kv, q, d, hq, hkv):
     assert err <= TOL[kv]
 
 
-@pytest.mark.parametrize("kv", ["int8", "int8_ch"])
+@pytest.mark.parametrize("kv,qd", [("int8", "f32"), ("int8_ch", "f32"), ("int8", "bf16")])
 @pytest.mark.parametrize("factor", [2e4, 1e-6])
-def test_int8_queries_far_outside_f16_range(kv, factor):
+def test_int8_queries_far_outside_f16_range(kv, qd, factor):
     """INT8 K enters QK as f16, so q is rescaled by a power of two into f16's range first: queries
     whose magnitudes would overflow f16 (2e4 x N(0, 1) reaches 9e4) or fall into its subnormals
-    (1e-6) must still match the oracle (near one-hot and near uniform softmax respectively)."""
-    w = _case_workload(kv, "f32", 128, 32, 8, 61, lens=(700, 33, 1500))
+    (1e-6) must still match the oracle (near one-hot and near uniform softmax respectively).  bf16
+    queries take the path with one QK MFMA per step (no low half)."""
+    w = _case_workload(kv, qd, 128, 32, 8, 61, lens=(700, 33, 1500))
     case = H.Case(w)
-    q = (case.q.float() * factor).contiguous()
+    q = (case.q.float() * factor).to(case.q.dtype).contiguous()
     out = case.attend(q=q)
     err = max(float(np.max(np.abs(H.to_f64(out[s]) - case.oracle(s, q=q)[0]))) for s in range(3))
     print(f"{kv} q x {factor}: max abs err {err:.3e}")
