@@ -76,6 +76,9 @@ constexpr float kRescaleSlack = 8.f;
 #ifndef PKV_ATTN_HEAD_FAST_8BIT
 #define PKV_ATTN_HEAD_FAST_8BIT 1    // the same for 8-bit pools
 #endif
+#ifndef PKV_ATTN_PAIR_8BIT
+#define PKV_ATTN_PAIR_8BIT 1         // per-token 8-bit pools: KV head pairs of a range on one XCD
+#endif
 #ifndef PKV_ATTN_ODD_SHARE
 #define PKV_ATTN_ODD_SHARE 880       // per mille: odd-numbered range length relative to even (head-major only)
 #endif
@@ -786,8 +789,16 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   const int lane = threadIdx.x;
   const int n_ranges = gridDim.x / hkv;
   constexpr bool kHeadFast = is_code8(KVT) ? PKV_ATTN_HEAD_FAST_8BIT : PKV_ATTN_HEAD_FAST;
-  const int r = kHeadFast ? blockIdx.x / hkv : blockIdx.x % n_ranges;
-  const int kvh = kHeadFast ? blockIdx.x % hkv : blockIdx.x / n_ranges;
+  int r = kHeadFast ? blockIdx.x / hkv : blockIdx.x % n_ranges;
+  int kvh = kHeadFast ? blockIdx.x % hkv : blockIdx.x / n_ranges;
+  if (kHeadFast && is_quantised(KVT) && PKV_ATTN_PAIR_8BIT && hkv % 2 == 0 && gridDim.x % 16 == 0) {
+    // Heads 2i and 2i+1 of one range on one XCD, 8 ids apart (dispatched
+    // together): their per-token scale rows share 128-byte lines.
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+    const int v = (k / 2) * 8 + x;          // (range, head pair), head pair fastest
+    r = v / (hkv / 2);
+    kvh = 2 * (v % (hkv / 2)) + k % 2;
+  }
 
   // Pass 1: total attended blocks; workgroup 0 records the per-sequence prefix
   // and R for the merge kernel; NaN outputs for unusable lengths.
