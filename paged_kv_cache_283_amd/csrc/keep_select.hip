@@ -83,25 +83,61 @@ __global__ void __launch_bounds__(kSelThreads) keep_select_kernel(const float* s
   const bool take_all = k == n_cand;
 
   // Radix select of the k-th largest candidate key, most significant byte first.
+  // The first kKeyRegs * 1024 candidate keys stay in registers across the
+  // passes (loaded together, one memory latency); longer rows re-read the rest.
+  constexpr int kKeyRegs = 8;
+  uint32_t kc[kKeyRegs];
+  float kf[kKeyRegs];   // the final pass's scores of positions tid + 1024 i, loaded with them
+#pragma unroll
+  for (int i = 0; i < kKeyRegs; ++i) {
+    const int p = c_lo + tid + i * kSelThreads;
+    kc[i] = p < c_hi ? score_key(row[p]) : 0u;
+    const int q = tid + i * kSelThreads;
+    kf[i] = q < L ? row[q] : 0.f;
+  }
   uint32_t prefix = 0u, mask = 0u;
   int need = k;
   if (!take_all && k > 0) {
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
       __syncthreads();
-      for (int p = c_lo + tid; p < c_hi; p += kSelThreads) {
+#pragma unroll
+      for (int i = 0; i < kKeyRegs; ++i) {
+        if (c_lo + tid + i * kSelThreads < c_hi && (kc[i] & mask) == prefix)
+          atomicAdd(&hist[(kc[i] >> shift) & 255u], 1);
+      }
+      for (int p = c_lo + tid + kKeyRegs * kSelThreads; p < c_hi; p += kSelThreads) {
         const uint32_t key = score_key(row[p]);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int cum = 0, digit = 0;
-        for (int d = 255; d >= 0; --d) {
-          if (cum + hist[d] >= need) { digit = d; break; }
-          cum += hist[d];
+      if (tid < kWave) {
+        // The digit holding the need-th largest remaining key, by the first
+        // wave: lane l takes digits 255 - 4l .. 252 - 4l, a lane scan gives the
+        // count of keys above its digits, and the one (lane, digit) where the
+        // running count first reaches `need` records it.
+        int h[4], local = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = hist[255 - 4 * tid - e];
+          local += h[e];
         }
-        s_pick[0] = digit;
-        s_pick[1] = need - cum;
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+          const int t = __shfl_up(incl, off, kWave);
+          if (tid >= off) incl += t;
+        }
+        int cum = incl - local;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c2 = cum + h[e];
+          if (cum < need && c2 >= need) {
+            s_pick[0] = 255 - 4 * tid - e;
+            s_pick[1] = need - cum;
+          }
+          cum = c2;
+        }
       }
       __syncthreads();
       prefix |= (uint32_t)s_pick[0] << shift;
@@ -113,10 +149,11 @@ __global__ void __launch_bounds__(kSelThreads) keep_select_kernel(const float* s
   const uint32_t thresh = prefix;   // the k-th largest key; `need` keys equal to it are taken
 
   int eq_seen = 0, written = 0;
-  for (int base = 0; base < L; base += kSelThreads) {
-    const int p = base + tid;
+  // One position per thread and step, in position order (the steps are
+  // uniform, so the barriers inside are reached by every thread).
+  auto step = [&](int p, float score) {
     const bool in_c = p >= c_lo && p < c_hi;
-    const uint32_t key = in_c && !take_all && k > 0 ? score_key(row[p]) : 0u;
+    const uint32_t key = in_c && !take_all && k > 0 ? score_key(score) : 0u;
     const bool eq = in_c && !take_all && k > 0 && key == thresh;
     int eq_tot, sel_tot;
     const int eq_rank = eq_seen + block_prefix_count(eq, s_wave, &eq_tot);
@@ -126,6 +163,14 @@ __global__ void __launch_bounds__(kSelThreads) keep_select_kernel(const float* s
     if (sel && pos < keep_stride) out[pos] = p;
     eq_seen += eq_tot;
     written += sel_tot;
+  };
+#pragma unroll
+  for (int i = 0; i < kKeyRegs; ++i) {
+    if (i * kSelThreads < L) step(i * kSelThreads + tid, kf[i]);
+  }
+  for (int base = kKeyRegs * kSelThreads; base < L; base += kSelThreads) {
+    const int p = base + tid;
+    step(p, p < L ? row[p] : 0.f);
   }
   for (int i = written + tid; i < keep_stride; i += kSelThreads) out[i] = -1;
   if (tid == 0) keep_count[s] = written;
