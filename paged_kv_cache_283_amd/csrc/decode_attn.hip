@@ -248,13 +248,15 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   // new token's K and V source rows (position L - 1, offset o_new of the last
   // attended block) together with its first table chunk and puts the stored
   // form in LDS next to the staged entries -- the rows themselves for 16-bit
-  // and f32 pools, the 8-bit codes (and the per-token scales in registers) for
-  // 8-bit pools, quantised exactly as the write kernels do; the last block's
+  // and f32 pools, the codes (and the per-token scales in registers) for FP8
+  // pools, quantised exactly as the write kernels do; the last block's
   // operands get them patched in, so the products see exactly the bits the
   // pool will hold.  The rows are stored into their slot when the wave has
   // finished all its segments (append_stores): stores share the load counter,
   // so a store issued here would hold up the wave's next tile waits until it
-  // completes.  8-bit pools take the source in q's dtype.
+  // completes.  FP8 pools take the source in q's dtype; INT8 instances are
+  // built without this code (fused_append_built) and their pools already hold
+  // the token.
   constexpr bool C8 = is_code8(KVT);
   constexpr bool kFuse = fused_append_built(KVT);
   constexpr int SEB = C8 ? (QT == DT_F32 ? 4 : 2) : EB;   // source element bytes
