@@ -470,8 +470,10 @@ def main():
     k_new, v_new = ksrc.index_select(0, r).contiguous(), vsrc.index_select(0, r).contiguous()
     q = W.queries(w, device=dev)
     out = torch.empty(q.shape, dtype=torch.bfloat16 if w.q_dtype == "bf16" else torch.float32, device=dev)
+    # H2O workloads: the step also emits the per-position attention mass (accumulated into a score row)
+    scores = torch.zeros((w.num_seqs, lay.max_len), dtype=torch.float32, device=dev) if w.mass else None
     ws = ops.alloc_workspace(w.num_seqs, w.num_q_heads, w.head_dim, lay.max_len, w.num_sinks, w.window,
-                             False, dev)
+                             w.mass, dev)
     torch.cuda.synchronize()
 
     launches = []
@@ -479,8 +481,8 @@ def main():
         k, v, ks, vs = p
         launches.append((
             ops.paged_decode_append_attn(out, q, k_new, v_new, k, v, tables, lens, lay.max_len, k_scale=ks,
-                                         v_scale=vs, num_sinks=w.num_sinks, window=w.window, workspace=ws,
-                                         stream=stream, prepare=True),))
+                                         v_scale=vs, num_sinks=w.num_sinks, window=w.window, attn_mass=scores,
+                                         workspace=ws, stream=stream, prepare=True),))
 
     def step(i):
         if layers > 1:
@@ -537,6 +539,7 @@ def main():
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                    "kv_dtype": w.kv_dtype, "block_size": 16, "max_context_len": lay.max_len,
                    "attended_tokens_per_layer": n_tok, "num_sinks": w.num_sinks, "window": w.window,
+                   "h2o_mass": bool(w.mass),
                    "pool_replicas_rotated": replicas,
                    "block_placement": "contiguous" if args.contiguous_blocks else "shuffled"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -979,24 +979,36 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
 }
 
 // H2O mass: scores[s][p] += mean over query heads of exp2(x - M_h) / l_h, kept p only.
+// The heads' (M_h, l_h) are staged in LDS, 256 heads at a time, so the loop
+// over heads issues only the (coalesced) logit loads.
 __global__ void __launch_bounds__(256) attn_mass_kernel(const AttnArgs a) {
+  __shared__ float s_m[256], s_l[256];
   const int s = blockIdx.y;
   const int v = blockIdx.x * blockDim.x + threadIdx.x;   // attended (virtual) position
   const int L = a.context_lens[s];
   const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
-  if (L < 1 || L > len_cap) return;
+  if (L < 1 || L > len_cap) return;                      // the whole workgroup
   const KeepGeom geo = keep_geometry(L, a.num_sinks, a.window);
-  if (v >= geo.n_virtual * kBlockSize) return;
   const int p = logical_block(v / kBlockSize, geo.n_sink_blocks, geo.win_start) * kBlockSize + v % kBlockSize;
-  if (!is_kept(p, L, a.num_sinks, a.window)) return;
+  const bool active = v < geo.n_virtual * kBlockSize && is_kept(p, L, a.num_sinks, a.window);
   const int hq = a.num_q_heads;
   float sum = 0.f;
-  for (int h = 0; h < hq; ++h) {
-    const size_t hs = (size_t)s * hq + h;
-    const float x = a.stash[hs * a.nv_pad + v];
-    sum += fast_exp2(x - a.fin_ml[hs * 2]) / a.fin_ml[hs * 2 + 1];
+  for (int h0 = 0; h0 < hq; h0 += 256) {
+    const int hn = min(256, hq - h0);
+    __syncthreads();                                      // the previous heads are read
+    if ((int)threadIdx.x < hn) {
+      const size_t hs = (size_t)s * hq + h0 + threadIdx.x;
+      s_m[threadIdx.x] = a.fin_ml[hs * 2];
+      s_l[threadIdx.x] = a.fin_ml[hs * 2 + 1];
+    }
+    __syncthreads();
+    if (active) {
+      const float* x = a.stash + ((size_t)s * hq + h0) * a.nv_pad + v;
+#pragma unroll 8
+      for (int h = 0; h < hn; ++h) sum += fast_exp2(x[(size_t)h * a.nv_pad] - s_m[h]) / s_l[h];
+    }
   }
-  a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
+  if (active) a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
 }
 
 namespace {
