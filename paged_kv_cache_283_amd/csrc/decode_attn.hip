@@ -100,6 +100,10 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Floats of the per-wave LDS window for H2O logits: 16 KiB with one wave per
+// SIMD (16-bit and f32 pools), 8 KiB with two (8-bit pools).
+__host__ __device__ constexpr int stash_floats(int kvt) { return is_code8(kvt) ? 2048 : 4096; }
+
 // Table entries staged in LDS per chunk of a segment.
 constexpr int kTabBlocks = 1024;
 
@@ -120,8 +124,8 @@ __device__ __forceinline__ int attended_blocks(const AttnArgs& a, int L) {
 // whole sequence) or a partial (running max, exp-sum, unnormalised output) in
 // slot partial_slot(seg_vb0).
 template <int KVT, int QT, int D>
-__device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint32_t* s_new, int s, int kvh, int L,
-                                             int seg_vb0, int seg_vb1) {
+__device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint32_t* s_new, float* s_stash, int s,
+                                             int kvh, int L, int seg_vb0, int seg_vb1) {
   using KT = KvType<KVT>;
   constexpr int EB = KT::kBytes;
   constexpr bool OP32 = KT::kOp32;
@@ -366,6 +370,22 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     }
   };
 
+  // H2O logits go to an LDS window of st_blocks blocks per head of the group
+  // (the table chunks are cut to that length) and out to the stash in
+  // coalesced 16-byte stores after each chunk: a store in every block's step
+  // would make the tile waits two blocks later wait for it too (stores share
+  // the load counter).
+  const int st_blocks = stash_floats(KVT) / (group * kBlockSize);
+  auto stash_flush = [&](int vb0, int nb) {
+    lds_wave_sync();
+    const int n4 = nb * kBlockSize / 4;       // 16-byte pieces per head
+    for (int idx = lane; idx < group * n4; idx += kWave) {
+      const int g = idx / n4, k = idx % n4;
+      *reinterpret_cast<f32x4*>(a.stash + ((size_t)s * hq + kvh * group + g) * a.nv_pad + (size_t)vb0 * kBlockSize +
+                                4 * k) = *reinterpret_cast<const f32x4*>(&s_stash[g * st_blocks * kBlockSize + 4 * k]);
+    }
+  };
+
   // tail: a call that may compute the segment's last block (the pipeline's
   // steady state never does), the only place the new token is patched in.
   auto compute = [&](Regs& r, int i, auto tail) {
@@ -498,10 +518,8 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[e] - mref);
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-    if (a.stash != nullptr && head_ok) {
-      const f32x4 xv = {x[0], x[1], x[2], x[3]};
-      *reinterpret_cast<f32x4*>(a.stash + ((size_t)s * hq + head) * a.nv_pad + (size_t)vb * kBlockSize + 4 * j) = xv;
-    }
+    if (a.stash != nullptr && head_ok)       // block i of the chunk in the LDS window
+      *reinterpret_cast<f32x4*>(&s_stash[(c * st_blocks + i) * kBlockSize + 4 * j]) = f32x4{x[0], x[1], x[2], x[3]};
 
     // ---- probabilities as the PV B operand (V's per-token scale folded in)
     float pv[4];
@@ -556,11 +574,12 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
 
   constexpr std::false_type kMid{};
   constexpr std::true_type kTail{};
-  for (; c0 < seg_vb1; c0 += kTabBlocks) {
+  const int chunk_cap = a.stash != nullptr ? st_blocks : kTabBlocks;
+  for (; c0 < seg_vb1; c0 += chunk_cap) {
     // The chunk's table entries go to LDS first: the loop reads them with LDS
     // loads, whose wait counter is separate from the K/V loads', so the
     // compiler can wait for exactly the block about to be computed.
-    const int n = min(kTabBlocks, seg_vb1 - c0);
+    const int n = min(chunk_cap, seg_vb1 - c0);
     const bool first = fuse && c0 == seg_vb0;
     {
       // 512 entries per memory latency: every lane issues 8 entry loads before
@@ -620,7 +639,8 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     if (i + 2 < n) compute(r2, i + 2, kTail);
     if (i + 3 < n) compute(r0, i + 3, kTail);
 #endif
-    lds_wave_sync();   // s_tab is rewritten by the next chunk
+    if (a.stash != nullptr) stash_flush(c0, n);
+    lds_wave_sync();   // s_tab (and the logit window) are rewritten by the next chunk
   }
 
   l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
@@ -786,6 +806,8 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   __shared__ int s_tab[kTabBlocks];
   // the new token's stored K and V rows when the decode append is fused in
   __shared__ uint32_t s_new[2 * D * KvType<KVT>::kBytes / 4];
+  // the H2O logit window (used only when attn_mass is requested)
+  __shared__ __attribute__((aligned(16))) float s_stash[stash_floats(KVT)];
   const int hkv = a.num_kv_heads;
   const int B = a.num_seqs;
   const int lane = threadIdx.x;
@@ -874,7 +896,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     const int nva = attended_blocks(a, L);
     const int vb = (int)(u - prefix);
     const int cnt = (int)min((long long)(nva - vb), u1 - u);
-    wave_segment<KVT, QT, D>(a, s_tab, s_new, sq, kvh, L, vb, vb + cnt);
+    wave_segment<KVT, QT, D>(a, s_tab, s_new, s_stash, sq, kvh, L, vb, vb + cnt);
     if (vb + cnt == nva) {
       end_lo = min(end_lo, sq);
       end_hi = sq;
