@@ -100,9 +100,10 @@ __device__ __forceinline__ void lds_wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Floats of the per-wave LDS window for H2O logits: 16 KiB with one wave per
-// SIMD (16-bit and f32 pools), 8 KiB with two (8-bit pools).
-__host__ __device__ constexpr int stash_floats(int kvt) { return is_code8(kvt) ? 2048 : 4096; }
+// Floats of the per-wave LDS window for H2O logits: 32 KiB with one wave per
+// SIMD (16-bit and f32 pools; a typical range fits, so chunks rarely drain),
+// 8 KiB with two (8-bit pools).
+__host__ __device__ constexpr int stash_floats(int kvt) { return is_code8(kvt) ? 2048 : 8192; }
 
 // Table entries staged in LDS per chunk of a segment.
 constexpr int kTabBlocks = 1024;
