@@ -828,10 +828,15 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   // Pass 1: total attended blocks; workgroup 0 records the per-sequence prefix
   // and R for the merge kernel; NaN outputs for unusable lengths.
   int total = 0;
+  int nva0 = 0, incl0 = 0;     // the first 64 sequences' counts, kept for pass 2
   for (int base = 0; base < B; base += kWave) {
     const int sq = base + lane;
     const int nva = sq < B ? attended_blocks(a, a.context_lens[sq]) : 0;
     const int incl = wave_scan(nva);
+    if (base == 0) {
+      nva0 = nva;
+      incl0 = incl;
+    }
     if (blockIdx.x == 0 && sq < B) a.seq_prefix[sq] = total + incl - nva;
     if (sq < B && nva == 0 && sq % (int)gridDim.x == (int)blockIdx.x) {
       for (int idx = 0; idx < a.num_q_heads * D; ++idx)
@@ -876,8 +881,9 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   int sq = -1, prefix = 0, run = 0;
   for (int base = 0; base < B && sq < 0; base += kWave) {
     const int q = base + lane;
-    const int nva = q < B ? attended_blocks(a, a.context_lens[q]) : 0;
-    const int incl = wave_scan(nva);
+    // (the first 64 come from pass 1's registers: no second load of the lengths)
+    const int nva = base == 0 ? nva0 : (q < B ? attended_blocks(a, a.context_lens[q]) : 0);
+    const int incl = base == 0 ? incl0 : wave_scan(nva);
     const int excl = run + incl - nva;
     const unsigned long long hit = __ballot(nva > 0 && excl <= u0 && u0 < excl + nva);
     if (hit != 0ull) {
