@@ -548,6 +548,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kv_bytes_per_step": kv_bytes_step,
         "attn_kernel_avg_us": round(1e3 * k_avg_ms, 2),
+        "attn_kernel_median_us": round(1e3 * float(np.median(kernel_ms)), 2),
         "attn_kernel_min_us": round(1e3 * float(np.min(kernel_ms)), 2),
         "attn_kernel_timed_launches": len(kernel_ms),
         "probe_read_gbs": round(read_gbs, 1),
