@@ -677,6 +677,30 @@ def test_append_attn_equals_append_then_attend(kv, src, q, d, hq, hkv, sinks, wi
         assert torch.equal(H.v_token_rows(vb)[slot].contiguous().view(torch.uint8), v_new[10].view(torch.uint8))
 
 
+@pytest.mark.parametrize("kv,d,hq,hkv", [("bf16", 128, 32, 8), ("fp8", 128, 32, 8), ("f32", 64, 16, 1)])
+def test_append_attn_repeated_step_is_idempotent(kv, d, hq, hkv):
+    """bench.py repeats the decode step on the same pools: the second call finds the token already in
+    its slot (stored after the first call's waves finished) and must give the same output, pools and
+    H2O mass; the mass window cuts the longer sequences into several chunks."""
+    w = _case_workload(kv, "bf16" if kv != "f32" else "f32", d, hq, hkv, seed=77, lens=APPEND_LENS[:11])
+    c = H.Case(w, hold_last=True)
+    L = c.lay.max_len
+    mass1 = torch.zeros((11, L), dtype=torch.float32, device="cuda")
+    mass2 = torch.zeros_like(mass1)
+    out1 = c.decode_step(attn_mass=mass1)
+    torch.cuda.synchronize()
+    pools1 = [x.clone() if x is not None else None for x in c.pools]
+    out2 = c.decode_step(attn_mass=mass2)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2)
+    assert torch.equal(mass1, mass2)
+    for x, y in zip(pools1, c.pools):
+        if x is not None:
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    err = max(float(np.max(np.abs(H.to_f64(out2[s]) - c.oracle(s)[0]))) for s in range(11))
+    assert err <= TOL[kv]
+
+
 # ---------------------------------------------------------------------------- multi-query (chunked prefill)
 
 def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):
