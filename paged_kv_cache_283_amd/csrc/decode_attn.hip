@@ -921,39 +921,49 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   }
 }
 
+// The segments a sequence was cut into: block 0 and every range cut inside the
+// sequence's span of the block list.  Cut k is (k / 2) P + (k odd ? pa : 0),
+// P = pa + pb; n == 1 means one segment, whose wave wrote the output itself.
+struct SeqCuts {
+  long long k0;   // first cut after the sequence start
+  int base, n, pa, P;
+  __device__ long long cut(long long k) const { return (k / 2) * P + (k % 2 ? pa : 0); }
+  __device__ int slot(int i) const { return i == 0 ? 0 : partial_slot((int)(cut(k0 + i - 1) - base)); }
+};
+
+__device__ __forceinline__ SeqCuts seq_cuts(const AttnArgs& a, int s, int nva) {
+  SeqCuts c;
+  c.pa = a.hdr->per;
+  c.P = c.pa + a.hdr->per_odd;
+  c.base = a.seq_prefix[s];
+  c.k0 = 2LL * (c.base / c.P) + (c.base % c.P < c.pa ? 1 : 2);
+  const int end = c.base + nva;
+  c.n = 1;
+  if (c.cut(c.k0) < end) {
+    const long long e = end - 1;                    // index of the last cut before end: the range holding e
+    const long long k_last = 2LL * (e / c.P) + (e % c.P < c.pa ? 0 : 1);
+    c.n = (int)(k_last - c.k0 + 2);
+  }
+  return c;
+}
+
 // Log-sum-exp merge of one (sequence, query head) per wave: the partials of the
-// segments the sequence was cut into (block 0 and every multiple of R inside
-// the sequence's span of the block list).  A sequence that was one segment
+// segments the sequence was cut into.  A sequence that was one segment
 // already has its output.  Segments go 16 at a time: every lane loads its
 // D / 64 output dims of all 16 partials and lane k the (max, sum) of segment
 // k, all before the first wait (the merge is latency-bound); then the wave
 // max, the weights exp2(m_k - M), and the weighted sums, with a running
 // rescale when a sequence has more than 16 segments.
 template <int D>
-__global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
+__device__ __forceinline__ void merge_head(const AttnArgs& a, int s, int h, int lane) {
   constexpr int kChunk = 16;
   constexpr int DL = D / 64;                      // output dims per lane
   using VT = typename std::conditional<DL == 2, float2, float>::type;
-  const int s = blockIdx.y;
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (h >= a.num_q_heads) return;
   const int nva = attended_blocks(a, a.context_lens[s]);
   if (nva == 0) return;                             // NaN already written
-  // Range cuts: cut k is (k / 2) P + (k odd ? pa : 0), P = pa + pb.
-  const int pa = a.hdr->per, pb = a.hdr->per_odd, P = pa + pb;
-  const int base = a.seq_prefix[s];
-  const int end = base + nva;
-  auto cut = [&](long long k) { return (k / 2) * P + (k % 2 ? pa : 0); };
-  const long long k0 = 2LL * (base / P) + (base % P < pa ? 1 : 2);   // first cut after the sequence start
-  if (cut(k0) >= end) return;                       // one segment: written directly
-  int n = 1;                                        // segments of this sequence
-  {
-    const long long e = end - 1;                    // last cut before end: index of the range holding e
-    const long long k_last = 2LL * (e / P) + (e % P < pa ? 0 : 1);
-    n = (int)(k_last - k0 + 2);
-  }
-  auto seg_slot = [&](int i) { return i == 0 ? 0 : partial_slot((int)(cut(k0 + i - 1) - base)); };
+  const SeqCuts c = seq_cuts(a, s, nva);
+  if (c.n == 1) return;                             // one segment: written directly
+  const int n = c.n;
   const size_t hs = (size_t)s * a.num_q_heads + h;
   const float* ml = a.part_ml + hs * a.p_max * 2;
   const float* pacc = a.part_acc + hs * a.p_max * D;
@@ -966,10 +976,10 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
     VT v[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k)   // past cnt: the last segment again (weight 0, skipped)
-      v[k] = *reinterpret_cast<const VT*>(pacc + (size_t)seg_slot(i0 + min(k, cnt - 1)) * D + DL * lane);
+      v[k] = *reinterpret_cast<const VT*>(pacc + (size_t)c.slot(i0 + min(k, cnt - 1)) * D + DL * lane);
     float mi = -INFINITY, li = 0.f;
     if (lane < cnt) {
-      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * seg_slot(i0 + lane));
+      const float2 x = *reinterpret_cast<const float2*>(ml + 2 * c.slot(i0 + lane));
       mi = x.x;
       li = x.y;
     }
@@ -1001,19 +1011,25 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
   }
 #pragma unroll
   for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + DL * lane + e, a.out_dtype, o[e] / lsum);
-  if (a.fin_ml != nullptr && lane == 0) {
-    a.fin_ml[hs * 2 + 0] = M;
-    a.fin_ml[hs * 2 + 1] = lsum;
-  }
 }
 
-// H2O mass: scores[s][p] += mean over query heads of exp2(x - M_h) / l_h, kept p only.
-// The heads' (M_h, l_h) are staged in LDS, 256 heads at a time, so the loop
-// over heads issues only the (coalesced) logit loads.
-__global__ void __launch_bounds__(256) attn_mass_kernel(const AttnArgs a) {
+template <int D>
+__global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
+  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (h >= a.num_q_heads) return;
+  merge_head<D>(a, blockIdx.y, h, threadIdx.x & 63);
+}
+
+// H2O mass of 256 attended positions of sequence s (workgroup-uniform s):
+// scores[s][p] += mean over query heads of exp2(x - M_h) / l_h, kept p only.
+// The heads' global (M_h, l_h) are staged in LDS, 256 heads at a time, so the
+// loop over heads issues only the (coalesced) logit loads.  A head of a
+// sequence that was one segment has them from its wave; otherwise the thread
+// of head h merges the segments' (max, exp-sum) pairs itself, 8 loads in
+// flight at a time, so that the mass does not wait for the output merge.
+__device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
   __shared__ float s_m[256], s_l[256];
-  const int s = blockIdx.y;
-  const int v = blockIdx.x * blockDim.x + threadIdx.x;   // attended (virtual) position
+  const int v = bx * 256 + threadIdx.x;                  // attended (virtual) position
   const int L = a.context_lens[s];
   const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
   if (L < 1 || L > len_cap) return;                      // the whole workgroup
@@ -1021,14 +1037,39 @@ __global__ void __launch_bounds__(256) attn_mass_kernel(const AttnArgs a) {
   const int p = logical_block(v / kBlockSize, geo.n_sink_blocks, geo.win_start) * kBlockSize + v % kBlockSize;
   const bool active = v < geo.n_virtual * kBlockSize && is_kept(p, L, a.num_sinks, a.window);
   const int hq = a.num_q_heads;
+  const SeqCuts c = seq_cuts(a, s, geo.n_virtual);
   float sum = 0.f;
   for (int h0 = 0; h0 < hq; h0 += 256) {
     const int hn = min(256, hq - h0);
     __syncthreads();                                      // the previous heads are read
     if ((int)threadIdx.x < hn) {
       const size_t hs = (size_t)s * hq + h0 + threadIdx.x;
-      s_m[threadIdx.x] = a.fin_ml[hs * 2];
-      s_l[threadIdx.x] = a.fin_ml[hs * 2 + 1];
+      float M = -INFINITY, l = 0.f;
+      if (c.n == 1) {
+        M = a.fin_ml[hs * 2];
+        l = a.fin_ml[hs * 2 + 1];
+      } else {
+        const float* ml = a.part_ml + hs * a.p_max * 2;
+        for (int i0 = 0; i0 < c.n; i0 += 8) {
+          const int cnt = min(8, c.n - i0);
+          float2 x[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = *reinterpret_cast<const float2*>(ml + 2 * c.slot(i0 + min(k, cnt - 1)));
+          float Mc = -INFINITY;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k < cnt) Mc = fmaxf(Mc, x[k].x);
+          const float Mn = fmaxf(M, Mc);
+          float lc = 0.f;
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if (k < cnt && x[k].x != -INFINITY) lc += fast_exp2(x[k].x - Mn) * x[k].y;
+          l = (M == -INFINITY ? 0.f : l * fast_exp2(M - Mn)) + lc;
+          M = Mn;
+        }
+      }
+      s_m[threadIdx.x] = M;
+      s_l[threadIdx.x] = l;
     }
     __syncthreads();
     if (active) {
@@ -1038,6 +1079,20 @@ __global__ void __launch_bounds__(256) attn_mass_kernel(const AttnArgs a) {
     }
   }
   if (active) a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
+}
+
+// The H2O step's tail in one launch: workgroups x < ceil(Hq / 4) of row s
+// merge the output of four query heads each; the rest add the mass of 256
+// positions each.  Neither reads what the other writes.
+template <int D>
+__global__ void __launch_bounds__(256) attn_merge_mass_kernel(const AttnArgs a) {
+  const int rx = (a.num_q_heads + 3) / 4;
+  if ((int)blockIdx.x < rx) {
+    const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (h < a.num_q_heads) merge_head<D>(a, blockIdx.y, h, threadIdx.x & 63);
+  } else {
+    mass_block(a, blockIdx.y, blockIdx.x - rx);
+  }
 }
 
 namespace {
@@ -1138,19 +1193,17 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
     default: err = dispatch_q<DT_INT8_CH>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
   }
   if (err != hipSuccess) return err;
-  {
-    dim3 grid((a.num_q_heads + 3) / 4, a.num_seqs);
+  const int rx = (a.num_q_heads + 3) / 4;
+  if (a.attn_mass != nullptr) {
+    dim3 grid(rx + (a.nv_pad + 255) / 256, a.num_seqs);
+    if (head_dim == 64) hipLaunchKernelGGL((attn_merge_mass_kernel<64>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn_merge_mass_kernel<128>), grid, dim3(256), 0, st, a);
+  } else {
+    dim3 grid(rx, a.num_seqs);
     if (head_dim == 64) hipLaunchKernelGGL((attn_reduce_kernel<64>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((attn_reduce_kernel<128>), grid, dim3(256), 0, st, a);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
   }
-  if (a.attn_mass != nullptr) {
-    dim3 grid((a.nv_pad + 255) / 256, a.num_seqs);
-    hipLaunchKernelGGL(attn_mass_kernel, grid, dim3(256), 0, st, a);
-    err = hipGetLastError();
-  }
-  return err;
+  return hipGetLastError();
 }
 
 }  // namespace pkv

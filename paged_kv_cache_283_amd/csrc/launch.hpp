@@ -46,7 +46,7 @@ struct AttnArgs {
   float* part_acc;      // [B][Hq][p_max][D]   unnormalised partial outputs
   float* part_ml;       // [B][Hq][p_max][2]   partition max (base-2) and exp-sum
   float* stash;         // [B][Hq][nv_pad]     base-2 logits per attended position (mass only)
-  float* fin_ml;        // [B][Hq][2]          global max and exp-sum (mass only)
+  float* fin_ml;        // [B][Hq][2]          max and exp-sum of one-segment sequences (mass only)
   StreamHdr* hdr;       // schedule of this call
   int* seq_prefix;      // [B + 1]  attended-block prefix per sequence, then the total
   int p_max;
