@@ -376,6 +376,25 @@ def test_h2o_mass_with_streaming_keep_set():
         assert np.max(np.abs(got[keep] - exp[keep]) / exp[keep]) <= 1e-4
 
 
+@pytest.mark.parametrize("kv,d,hq,hkv", [("bf16", 64, 512, 64), ("fp8", 128, 288, 36)])
+def test_h2o_mass_more_than_256_query_heads(kv, d, hq, hkv):
+    """The mass stages the heads' (max, exp-sum) in LDS 256 heads at a time: 512 heads take two full
+    chunks, 288 a full and a ragged one.  The 5000-token sequence is cut into several segments, so
+    the mass workgroups merge its heads' segment pairs themselves."""
+    w = _case_workload(kv, "bf16", d, hq, hkv, 43, lens=(5000, 300, 17))
+    case = H.Case(w)
+    maxl = case.lay.max_len
+    scores = torch.zeros((3, maxl + 5), dtype=torch.float32, device="cuda")
+    out = case.attend(attn_mass=scores)
+    got = scores.cpu().numpy().astype(np.float64)
+    for s in range(3):
+        ref, probs = case.oracle(s)
+        assert np.max(np.abs(H.to_f64(out[s]) - ref)) <= TOL[kv]
+        exp = probs.mean(axis=0)
+        assert np.max(np.abs(got[s, : exp.size] - exp) / exp) <= 1e-4
+        assert np.all(got[s, exp.size:] == 0)
+
+
 def test_tiny_h2o_sub_case_budget_24_recent_8():
     """The tiny workload's H2O sub-case: four decode steps accumulate the mass on the GPU, then the
     GPU keep-set (budget 24, recent 8) equals the oracle's selection on the oracle's own mass, taken
