@@ -1025,9 +1025,11 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
 // The heads' global (M_h, l_h) are staged in LDS, 256 heads at a time, so the
 // loop over heads issues only the (coalesced) logit loads.  A head of a
 // sequence that was one segment has them from its wave; otherwise the thread
-// of head h merges the segments' (max, exp-sum) pairs itself, 8 loads in
-// flight at a time, so that the mass does not wait for the output merge.
+// of head h merges the segments' (max, exp-sum) pairs itself, 16 loads in
+// flight at a time (as many round trips as the output merge's 16 segments per
+// wave), so that the mass does not wait for the output merge.
 __device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
+  constexpr int kPairs = 16;
   __shared__ float s_m[256], s_l[256];
   const int v = bx * 256 + threadIdx.x;                  // attended (virtual) position
   const int L = a.context_lens[s];
@@ -1050,19 +1052,20 @@ __device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
         l = a.fin_ml[hs * 2 + 1];
       } else {
         const float* ml = a.part_ml + hs * a.p_max * 2;
-        for (int i0 = 0; i0 < c.n; i0 += 8) {
-          const int cnt = min(8, c.n - i0);
-          float2 x[8];
+        for (int i0 = 0; i0 < c.n; i0 += kPairs) {
+          const int cnt = min(kPairs, c.n - i0);
+          float2 x[kPairs];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) x[k] = *reinterpret_cast<const float2*>(ml + 2 * c.slot(i0 + min(k, cnt - 1)));
+          for (int k = 0; k < kPairs; ++k)
+            x[k] = *reinterpret_cast<const float2*>(ml + 2 * c.slot(i0 + min(k, cnt - 1)));
           float Mc = -INFINITY;
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
+          for (int k = 0; k < kPairs; ++k)
             if (k < cnt) Mc = fmaxf(Mc, x[k].x);
           const float Mn = fmaxf(M, Mc);
           float lc = 0.f;
 #pragma unroll
-          for (int k = 0; k < 8; ++k)
+          for (int k = 0; k < kPairs; ++k)
             if (k < cnt && x[k].x != -INFINITY) lc += fast_exp2(x[k].x - Mn) * x[k].y;
           l = (M == -INFINITY ? 0.f : l * fast_exp2(M - Mn)) + lc;
           M = Mn;
