@@ -947,23 +947,32 @@ __device__ __forceinline__ SeqCuts seq_cuts(const AttnArgs& a, int s, int nva) {
   return c;
 }
 
-// Log-sum-exp merge of one (sequence, query head) per wave: the partials of the
+// Log-sum-exp merge of one (sequence, query head): the partials of the
 // segments the sequence was cut into.  A sequence that was one segment
-// already has its output.  Segments go 16 at a time: every lane loads its
-// D / 64 output dims of all 16 partials and lane k the (max, sum) of segment
-// k, all before the first wait (the merge is latency-bound); then the wave
-// max, the weights exp2(m_k - M), and the weighted sums, with a running
-// rescale when a sequence has more than 16 segments.
+// already has its output.  With parts == 1 one wave merges the head; with
+// parts == 4 the head has a 4-wave workgroup and wave w takes segment chunks
+// w, w + 4, ... (few sequences: each is cut into many segments).  Per chunk
+// of 16 every lane loads its D / 64 output dims of all 16 partials and lane k
+// the (max, sum) of segment k, all before the first wait (the merge is
+// latency-bound); then the wave max, the weights exp2(m_k - M), and the
+// weighted sums, with a running rescale past one chunk.  Up to 16 segments
+// wave 0 stores the output itself; past that the four waves' (M, l, o) are
+// combined through LDS, so n segments cost ceil(n / 64) round trips, not
+// ceil(n / 16).
 template <int D>
-__device__ __forceinline__ void merge_head(const AttnArgs& a, int s, int h, int lane) {
-  constexpr int kChunk = 16;
+__device__ __forceinline__ void merge_head(const AttnArgs& a, int s, int h, int w, int lane, int parts) {
+  constexpr int kChunk = 16, kParts = 4;
   constexpr int DL = D / 64;                      // output dims per lane
   using VT = typename std::conditional<DL == 2, float2, float>::type;
+  __shared__ float s_o[kParts][D];
+  __shared__ float s_ml[kParts][2];
   const int nva = attended_blocks(a, a.context_lens[s]);
   if (nva == 0) return;                             // NaN already written
   const SeqCuts c = seq_cuts(a, s, nva);
   if (c.n == 1) return;                             // one segment: written directly
   const int n = c.n;
+  if (parts > 1 && n <= kChunk && w != 0) return;   // the whole workgroup agrees on n
+  const int part = parts > 1 ? w : 0;
   const size_t hs = (size_t)s * a.num_q_heads + h;
   const float* ml = a.part_ml + hs * a.p_max * 2;
   const float* pacc = a.part_acc + hs * a.p_max * D;
@@ -971,7 +980,7 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int s, int h, int 
   float o[DL];
 #pragma unroll
   for (int e = 0; e < DL; ++e) o[e] = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kChunk) {
+  for (int i0 = part * kChunk; i0 < n; i0 += parts * kChunk) {
     const int cnt = min(kChunk, n - i0);
     VT v[kChunk];
 #pragma unroll
@@ -1009,15 +1018,41 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int s, int h, int 
     }
     M = Mn;
   }
+  if (parts > 1 && n > kChunk) {   // combine the four waves' states (one without chunks: M = -inf, weight 0)
+#pragma unroll
+    for (int e = 0; e < DL; ++e) s_o[w][DL * lane + e] = o[e];
+    if (lane == 0) {
+      s_ml[w][0] = M;
+      s_ml[w][1] = lsum;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kParts; ++p) Mt = fmaxf(Mt, s_ml[p][0]);
+    lsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < kParts; ++p) {
+      const float mp = s_ml[p][0];
+      const float f = mp == -INFINITY ? 0.f : fast_exp2(mp - Mt);
+      lsum += f * s_ml[p][1];
+#pragma unroll
+      for (int e = 0; e < DL; ++e) o[e] += f * s_o[p][DL * lane + e];
+    }
+  }
 #pragma unroll
   for (int e = 0; e < DL; ++e) store_out(a.out, hs * D + DL * lane + e, a.out_dtype, o[e] / lsum);
 }
 
+// split: one query head per workgroup (grid.x = Hq), else four (one per wave).
 template <int D>
-__global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a) {
-  const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (h >= a.num_q_heads) return;
-  merge_head<D>(a, blockIdx.y, h, threadIdx.x & 63);
+__global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a, int split) {
+  const int w = threadIdx.x >> 6;
+  const int h = split ? (int)blockIdx.x : (int)blockIdx.x * 4 + w;
+  if (h >= a.num_q_heads) return;   // 4-head workgroups only: no barrier there
+  merge_head<D>(a, blockIdx.y, h, w, threadIdx.x & 63, split ? 4 : 1);
 }
 
 // H2O mass of 256 attended positions of sequence s (workgroup-uniform s):
@@ -1084,15 +1119,16 @@ __device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
   if (active) a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
 }
 
-// The H2O step's tail in one launch: workgroups x < ceil(Hq / 4) of row s
-// merge the output of four query heads each; the rest add the mass of 256
+// The H2O step's tail in one launch: the first rx workgroups of row s merge
+// the output as attn_reduce_kernel does; the rest add the mass of 256
 // positions each.  Neither reads what the other writes.
 template <int D>
-__global__ void __launch_bounds__(256) attn_merge_mass_kernel(const AttnArgs a) {
-  const int rx = (a.num_q_heads + 3) / 4;
+__global__ void __launch_bounds__(256) attn_merge_mass_kernel(const AttnArgs a, int split) {
+  const int rx = split ? a.num_q_heads : (a.num_q_heads + 3) / 4;
   if ((int)blockIdx.x < rx) {
-    const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (h < a.num_q_heads) merge_head<D>(a, blockIdx.y, h, threadIdx.x & 63);
+    const int w = threadIdx.x >> 6;
+    const int h = split ? (int)blockIdx.x : (int)blockIdx.x * 4 + w;
+    if (h < a.num_q_heads) merge_head<D>(a, blockIdx.y, h, w, threadIdx.x & 63, split ? 4 : 1);
   } else {
     mass_block(a, blockIdx.y, blockIdx.x - rx);
   }
@@ -1196,15 +1232,19 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
     default: err = dispatch_q<DT_INT8_CH>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
   }
   if (err != hipSuccess) return err;
-  const int rx = (a.num_q_heads + 3) / 4;
+  // Few sequences share the ranges: each is cut into many segments, and a
+  // head's merge gets four waves.  Otherwise four heads share a workgroup
+  // (measured: one head per workgroup costs ~1.5 us more at 64 sequences).
+  const int split = a.num_seqs <= 8;
+  const int rx = split ? a.num_q_heads : (a.num_q_heads + 3) / 4;
   if (a.attn_mass != nullptr) {
     dim3 grid(rx + (a.nv_pad + 255) / 256, a.num_seqs);
-    if (head_dim == 64) hipLaunchKernelGGL((attn_merge_mass_kernel<64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_merge_mass_kernel<128>), grid, dim3(256), 0, st, a);
+    if (head_dim == 64) hipLaunchKernelGGL((attn_merge_mass_kernel<64>), grid, dim3(256), 0, st, a, split);
+    else hipLaunchKernelGGL((attn_merge_mass_kernel<128>), grid, dim3(256), 0, st, a, split);
   } else {
     dim3 grid(rx, a.num_seqs);
-    if (head_dim == 64) hipLaunchKernelGGL((attn_reduce_kernel<64>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn_reduce_kernel<128>), grid, dim3(256), 0, st, a);
+    if (head_dim == 64) hipLaunchKernelGGL((attn_reduce_kernel<64>), grid, dim3(256), 0, st, a, split);
+    else hipLaunchKernelGGL((attn_reduce_kernel<128>), grid, dim3(256), 0, st, a, split);
   }
   return hipGetLastError();
 }
