@@ -514,6 +514,17 @@ def main():
     kernel_ms = ops.timing_end(n_attn)
     step_ms = t_start.elapsed_time(t_end) / args.steps
 
+    # Per-iteration step times (an event pair around each step, in a pass of its own after the
+    # back-to-back timed steps above, which give ms_per_step).
+    it_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for i, (a, b) in enumerate(it_evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    it_ms = np.array([a.elapsed_time(b) for a, b in it_evs])
+
     n_tok = attended_tokens(w, lay)
     per_tok = kv_bytes_per_token(w)
     kv_bytes_layer = n_tok * per_tok
@@ -551,6 +562,11 @@ def main():
         "attn_kernel_median_us": round(1e3 * float(np.median(kernel_ms)), 2),
         "attn_kernel_min_us": round(1e3 * float(np.min(kernel_ms)), 2),
         "attn_kernel_timed_launches": len(kernel_ms),
+        "step_ms_median": round(float(np.median(it_ms)), 4),
+        "step_ms_min": round(float(np.min(it_ms)), 4),
+        "traffic_source": (f"profiles/attn_wave_{args.workload}_traffic.txt: rocprofv3 --pmc FETCH_SIZE and "
+                           "WRITE_SIZE of this kernel build (kernel_hash matches), scaled by the copy-probe "
+                           "calibration" if traffic is not None else None),
         "probe_read_gbs": round(read_gbs, 1),
         "probe_copy_gbs": round(copy_gbs, 1),
         "frac_of_probe_read": round(achieved / read_gbs, 4),

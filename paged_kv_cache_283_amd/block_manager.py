@@ -66,6 +66,7 @@ class BlockManager:
         self.lens = {}            # seq id -> tokens held
         self.swapped = {}         # seq id -> (host slots, tokens held) while swapped out
         self.cow_copies = 0
+        self._pending = []        # source blocks of compactions not yet released
 
     # ---- pool ---------------------------------------------------------------
     def _alloc(self) -> int:
@@ -149,10 +150,14 @@ class BlockManager:
         """Give seq fresh blocks for a dense prefix of num_kept tokens (eviction).
 
         Returns (old_table, new_table): the caller enqueues kv_compact from
-        old_table to new_table with the keep-set.  The old blocks are released
-        here (shared ones only lose this reference), so a later allocation may
-        hand them out again: device work that writes them must be enqueued
-        after the kv_compact call on the same stream.
+        old_table to new_table with the keep-set.  The old blocks are not
+        released yet: they stay referenced until release_compacted(), so the
+        fresh blocks of another sequence compacted before that call are never
+        one of them, and one batched kv_compact over every sequence compacted
+        so far has no destination slot that is also a source slot.  Call
+        release_compacted() once those kv_compact calls are enqueued; device
+        work that writes the released blocks must come after them on the same
+        stream.
         """
         if num_kept < 0 or num_kept > self.lens[seq]:
             raise ValueError(f"num_kept {num_kept} outside [0, {self.lens[seq]}]")
@@ -161,11 +166,19 @@ class BlockManager:
             raise OutOfBlocks(f"compaction to {num_kept} tokens needs {need} blocks, {self.num_free} free")
         old = self.tables[seq]
         new = [self._alloc() for _ in range(need)]
-        for b in old:
-            self._release(b)
+        self._pending.extend(old)
         self.tables[seq] = new
         self.lens[seq] = num_kept
         return list(old), list(new)
+
+    def release_compacted(self) -> int:
+        """Release the source blocks of every compact() since the last call (shared ones only lose
+        that sequence's reference); returns how many references were dropped."""
+        n = len(self._pending)
+        for b in self._pending:
+            self._release(b)
+        self._pending = []
+        return n
 
     def swap_out(self, seq, store: HostBlockStore):
         """Move seq out of the pool ([PA] 三大运行时组件: blocks can be swapped out to CPU RAM).
@@ -241,13 +254,13 @@ class BlockManager:
 class PrefixCachingBlockManager(BlockManager):
     """BlockManager whose full blocks are also found by the token prefix they complete.
 
-    Page "KV Cache 与 PagedAttention：显存复用与长上下文推理", "共享场景的价值": requests that
-    share a system prompt, a RAG document or a conversation history can share
-    its KV; with vLLM-style prefix caching a request that arrives is matched
-    block by block against cached prefixes, and a hit skips the prefill of the
-    shared part ("按 token 前缀匹配缓存块，命中则跳过 prefill"); cached blocks are shared
-    physically, with reference counts and copy-on-write.  The page also advises
-    putting reused text first, since matching is by prefix.
+    Page "KV Cache 与 PagedAttention：显存复用与长上下文推理", section "共享场景的价值": requests
+    that share a system prompt, a RAG document or a conversation history can
+    share its KV; with vLLM-style prefix caching a new request is compared,
+    block by block, with the prefixes already cached, and the part that
+    matches needs no prefill; cached blocks are shared physically, with
+    reference counts and copy-on-write.  Since matching goes by prefix, the
+    page recommends placing reused text at the start of the prompt.
 
     Design: each full block is keyed by a chained digest, hash(parent key,
     its 16 token ids), so a key names the whole prefix up to the end of that
@@ -257,6 +270,13 @@ class PrefixCachingBlockManager(BlockManager):
     then evicts the least recently freed cached block.  Only full blocks are
     shared, and writes only ever go to a sequence's partial last block, so a
     shared block is never written.
+
+    A sequence's blocks are keyed only while the token id of every position
+    it holds is known.  One that loses that (added with tokens but no ids,
+    extended without ids, or compacted by eviction, after which its
+    positions are no longer a prefix of any prompt) becomes uncacheable:
+    commit() registers nothing more for it, and its blocks registered before
+    keep their (correct) keys.
     """
 
     def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
@@ -264,7 +284,7 @@ class PrefixCachingBlockManager(BlockManager):
         self._by_key = {}               # prefix key -> block
         self._key_of = {}               # block -> prefix key
         self._evictable = OrderedDict()  # cached blocks with refcount 0, least recently freed first
-        self.tokens = {}                # seq -> token ids held
+        self.tokens = {}                # seq -> token ids held, None once unknown (uncacheable)
         self.hits = 0                   # blocks reused from the cache
         self.evictions = 0
 
@@ -349,10 +369,19 @@ class PrefixCachingBlockManager(BlockManager):
         self.hits += len(hits)
         return list(self.tables[seq]), len(hits) * self.block_size
 
+    def add_sequence(self, seq, num_tokens: int = 0):
+        table = super().add_sequence(seq, num_tokens)
+        self.tokens[seq] = [] if num_tokens == 0 else None    # ids of a non-empty start are unknown
+        return table
+
     def commit(self, seq):
-        """Make seq's full blocks findable (call once their KV has been written)."""
+        """Make seq's full blocks findable (call once their KV has been written).  Does nothing for a
+        sequence whose token ids are not all known."""
         table = self.tables[seq]
-        for i, k in enumerate(self._keys(self.tokens[seq][: self.lens[seq]])):
+        tokens = self.tokens.get(seq)
+        if tokens is None or len(tokens) != self.lens[seq]:
+            return
+        for i, k in enumerate(self._keys(tokens)):
             b = table[i]
             if k in self._by_key or b in self._key_of:
                 continue                     # already cached (shared) or registered under its key
@@ -360,21 +389,26 @@ class PrefixCachingBlockManager(BlockManager):
             self._key_of[b] = k
 
     def append_tokens(self, seq, n: int = 1, token_ids=None):
-        if token_ids is not None:
-            if len(token_ids) != n:
-                raise ValueError("one token id per appended token")
-            self.tokens.setdefault(seq, []).extend(int(t) for t in token_ids)
-        return super().append_tokens(seq, n)
+        if token_ids is not None and len(token_ids) != n:
+            raise ValueError("one token id per appended token")
+        out = super().append_tokens(seq, n)
+        known = self.tokens.get(seq)
+        if known is not None:
+            # without ids the positions from here on are unknown: the sequence stops being cacheable
+            self.tokens[seq] = known + [int(t) for t in token_ids] if token_ids is not None else None
+        return out
 
     def fork(self, parent, child):
         table = super().fork(parent, child)
-        self.tokens[child] = list(self.tokens.get(parent, []))
+        known = self.tokens.get(parent)
+        self.tokens[child] = None if known is None else list(known)
         return table
 
     def compact(self, seq, num_kept: int):
-        # kept tokens are a new sequence of positions: the prefix keys no longer describe them
-        self.tokens.pop(seq, None)
-        return super().compact(seq, num_kept)
+        # kept tokens are no longer the prefix of a prompt: the sequence becomes uncacheable
+        out = super().compact(seq, num_kept)
+        self.tokens[seq] = None
+        return out
 
     def free(self, seq) -> None:
         super().free(seq)

@@ -98,14 +98,17 @@ def _stream(stream):
 
 class Prepared:
     """A library call with every argument already marshalled: calling it re-issues the same
-    launch on the same stream (for benchmark and serving loops that repeat a step)."""
+    launch on the same stream (for benchmark and serving loops that repeat a step).  It holds a
+    reference to every buffer the binding allocated for the call (a workspace, a slot mapping), so
+    their memory stays with this launch for as long as the object lives."""
 
-    __slots__ = ("name", "fn", "args")
+    __slots__ = ("name", "fn", "args", "keep")
 
-    def __init__(self, name, args):
+    def __init__(self, name, args, keep=()):
         self.name = name
         self.fn = getattr(_lib.load(), name)
         self.args = tuple(args)
+        self.keep = tuple(keep)
 
     def __call__(self):
         status = self.fn(*self.args)
@@ -113,10 +116,16 @@ class Prepared:
             _lib.check(self.name, status)
 
 
-def _issue(name, args, prepare):
+def _issue(name, args, prepare, stream=None, scratch=()):
+    """Run (or prepare) a call.  scratch: tensors this binding allocated for the call; a prepared
+    call keeps them, and on a stream other than the current one they are recorded on it, so the
+    caching allocator does not hand their memory out again before the call has run."""
     if prepare:
-        return Prepared(name, args)
+        return Prepared(name, args, scratch)
     _lib.call(name, *args)
+    if stream is not None and scratch and stream != torch.cuda.current_stream(stream.device):
+        for t in scratch:
+            t.record_stream(stream)
     return None
 
 
@@ -152,10 +161,13 @@ def paged_decode_slots(block_tables, context_lens, num_blocks, slot_mapping=None
     _need(block_tables, torch.int32, "block_tables")
     _need(context_lens, torch.int32, "context_lens")
     b = context_lens.shape[0]
+    made = ()
     if slot_mapping is None:
         slot_mapping = torch.empty(b, dtype=torch.int64, device=context_lens.device)
+        made = (slot_mapping,)
     p = _issue("paged_decode_slots", (_ptr(block_tables), block_tables.shape[1], _ptr(context_lens), b,
-                                      int(num_blocks), BLOCK_SIZE, _ptr(slot_mapping), _stream(stream)), prepare)
+                                      int(num_blocks), BLOCK_SIZE, _ptr(slot_mapping), _stream(stream)), prepare,
+               scratch=made)
     return p if prepare else slot_mapping
 
 
@@ -279,14 +291,16 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     if attn_mass is not None:
         _need(attn_mass, torch.float32, "attn_mass")
         mass_stride = attn_mass.shape[1]
+    made = ()
     if workspace is None:
         workspace = alloc_workspace(b, hq, d, max_context_len, num_sinks, window, attn_mass is not None, q.device)
+        made = (workspace,)
     args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
             _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale), _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), int(max_context_len), b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), int(num_sinks),
             int(window), _ptr(attn_mass), mass_stride, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
-    p = _issue("paged_decode_attn", args, prepare)
+    p = _issue("paged_decode_attn", args, prepare, stream, made)
     return p if prepare else out
 
 
@@ -315,15 +329,17 @@ def paged_decode_append_attn(out, q, k_new, v_new, k_pool, v_pool, block_tables,
     if attn_mass is not None:
         _need(attn_mass, torch.float32, "attn_mass")
         mass_stride = attn_mass.shape[1]
+    made = ()
     if workspace is None:
         workspace = alloc_workspace(b, hq, d, max_context_len, num_sinks, window, attn_mass is not None, q.device)
+        made = (workspace,)
     args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_new), _ptr(v_new),
             float_code(k_new.dtype), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
             pool_code(k_pool, k_scale, v_scale), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
             int(max_context_len), b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), int(num_sinks), int(window),
             _ptr(attn_mass), mass_stride, _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream(stream))
-    p = _issue("paged_decode_append_attn", args, prepare)
+    p = _issue("paged_decode_append_attn", args, prepare, stream, made)
     return p if prepare else out
 
 

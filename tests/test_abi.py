@@ -227,3 +227,35 @@ def test_pool_code_reads_the_scale_layout():
             ops.pool_code(k, per_ch.double(), per_ch.double())
     kb = torch.empty(ops.k_pool_shape(10, 2, 64, torch.bfloat16), dtype=torch.bfloat16)
     assert ops.pool_code(kb, torch.empty((2, 64)), torch.empty((2, 64))) == _lib.BF16
+
+
+def test_prepared_call_holds_the_buffers_the_binding_allocated(monkeypatch):
+    """A prepared decode call whose workspace (or slot mapping) the binding allocated keeps that
+    tensor, so re-issuing the launch never writes into memory the allocator gave to someone else.
+    CPU tensors stand in for device ones: the call is only marshalled, never run."""
+    from paged_kv_cache_283_amd import ops
+    monkeypatch.setattr(ops, "_ptr", lambda t: None if t is None else ctypes.c_void_p(t.data_ptr()))
+    monkeypatch.setattr(ops, "_stream", lambda s: ctypes.c_void_p(0))
+    made = []
+
+    def fake_workspace(*a, **k):
+        made.append(torch.empty(4096, dtype=torch.uint8))
+        return made[-1]
+
+    monkeypatch.setattr(ops, "alloc_workspace", fake_workspace)
+    b, hq, hkv, d, nb = 2, 8, 2, 64, 4
+    q = torch.zeros((b, hq, d), dtype=torch.bfloat16)
+    out = torch.empty_like(q)
+    k, v, _, _ = ops.allocate_pools(nb, hkv, d, torch.bfloat16, device="cpu")
+    tables = torch.zeros((b, 1), dtype=torch.int32)
+    lens = torch.ones(b, dtype=torch.int32)
+    p = ops.paged_decode_attn(out, q, k, v, tables, lens, 16, prepare=True)
+    assert isinstance(p, ops.Prepared) and p.keep == (made[0],)
+    assert made[0].data_ptr() in [a.value for a in p.args if isinstance(a, ctypes.c_void_p)]
+    kn = torch.zeros((b, hkv, d), dtype=torch.bfloat16)
+    p2 = ops.paged_decode_append_attn(out, q, kn, kn, k, v, tables, lens, 16, prepare=True)
+    assert p2.keep == (made[1],)
+    ws = torch.empty(4096, dtype=torch.uint8)
+    assert ops.paged_decode_attn(out, q, k, v, tables, lens, 16, workspace=ws, prepare=True).keep == ()
+    p3 = ops.paged_decode_slots(tables, lens, nb, prepare=True)
+    assert len(p3.keep) == 1 and p3.keep[0].dtype == torch.int64

@@ -114,17 +114,42 @@ def test_compact_swaps_in_fresh_blocks_and_releases_the_old():
     old, new = bm.compact("a", 20)            # keep 20 tokens -> 2 fresh blocks
     assert len(old) == 5 and len(new) == 2 and not set(old) & set(new)
     assert bm.tables["a"] == new and bm.lens["a"] == 20
+    assert all(bm.refcount[x] == 2 for x in old)          # still referenced until the release
+    assert bm.release_compacted() == 5 and bm.release_compacted() == 0
     assert bm.num_free == free_before - 2     # old blocks still held by "b"
     assert all(bm.refcount[x] == 1 for x in old) and all(bm.refcount[x] == 1 for x in new)
     bm.free("b")
     assert bm.num_free == 12 - 2
     _, new2 = bm.compact("a", 0)              # evict everything
+    bm.release_compacted()
     assert new2 == [] and bm.num_free == 12
     with pytest.raises(ValueError):
         bm.compact("a", 1)
     bm.add_sequence("c", 16 * 12)
     with pytest.raises(OutOfBlocks):
         bm.compact("c", 16)                   # no free block left for the copy
+
+
+def test_batched_compaction_never_writes_a_pending_source():
+    """Two sequences compacted before one batched kv_compact: the second one's fresh blocks are
+    never the first one's source blocks (kv_compact's rule: no destination slot may be a source
+    slot of the same call).  With the release at compact() time, b's fresh block would be a's."""
+    bm = BlockManager(5)
+    bm.add_sequence("a", 32)                  # blocks 0, 1
+    bm.add_sequence("b", 32)                  # blocks 2, 3
+    old_a, new_a = bm.compact("a", 16)        # block 4
+    with pytest.raises(OutOfBlocks):
+        bm.compact("b", 16)                   # a's sources are still pending: nothing free
+    bm.release_compacted()
+    old_b, new_b = bm.compact("b", 16)
+    assert not set(new_b) & set(old_b) and new_b[0] in old_a     # a's copy is enqueued by now
+    bm2 = BlockManager(6)
+    bm2.add_sequence("a", 32)
+    bm2.add_sequence("b", 32)
+    old_a, new_a = bm2.compact("a", 16)
+    old_b, new_b = bm2.compact("b", 16)
+    assert not (set(new_a) | set(new_b)) & (set(old_a) | set(old_b))
+    assert bm2.release_compacted() == 4 and bm2.num_free == 4
 
 
 # ---------------------------------------------------------------------------- prefix caching
@@ -180,6 +205,43 @@ def test_decode_tokens_extend_the_cacheable_prefix():
     assert cached == 32 and tab[:2] == bm.tables["a"][:2]
     with pytest.raises(ValueError):
         bm.append_tokens("a", 2, token_ids=[1])
+
+
+def test_compacted_sequence_is_never_cached_under_new_ids():
+    """After eviction a sequence's positions are no longer a prompt prefix: token ids appended
+    afterwards must not key its blocks, or a later request starting with those ids would read the
+    compacted sequence's KV as its own prefix."""
+    bm = PrefixCachingBlockManager(32)
+    bm.add_cached_sequence("a", list(range(40)))
+    bm.commit("a")
+    cached = bm.num_cached
+    bm.compact("a", 20)
+    bm.release_compacted()
+    bm.append_tokens("a", 16, token_ids=list(range(500, 516)))
+    bm.commit("a")
+    assert bm.num_cached == cached
+    _, hit = bm.add_cached_sequence("b", list(range(500, 516)) + [1, 2])
+    assert hit == 0
+
+
+def test_sequences_with_unknown_token_ids_are_not_cached():
+    bm = PrefixCachingBlockManager(32)
+    bm.add_sequence("a", 40)                             # no ids for its first 40 tokens
+    bm.append_tokens("a", 24, token_ids=list(range(24)))
+    bm.commit("a")
+    assert bm.num_cached == 0
+    bm.add_cached_sequence("b", list(range(16)) + [3])
+    bm.append_tokens("b", 1)                             # an appended token without its id
+    bm.append_tokens("b", 30, token_ids=list(range(30)))
+    bm.commit("b")
+    assert bm.num_cached == 0                            # only 17 known ids: block 1 is not known
+    bm.add_sequence("c", 0)                              # empty start: ids tracked from here
+    bm.append_tokens("c", 32, token_ids=list(range(32)))
+    bm.commit("c")
+    assert bm.num_cached == 2
+    bm.fork("b", "d")
+    bm.commit("d")
+    assert bm.num_cached == 2
 
 
 def test_prefix_cache_exhaustion_leaves_state_unchanged():
