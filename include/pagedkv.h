@@ -15,6 +15,8 @@
  *    unless its comment says "host".  Arrays are dense and row-major.
  *  - The caller owns all memory.  The library never allocates or frees device
  *    memory; scratch space is a caller-provided workspace sized by a query call.
+ *    The one exception is paged_decode_attn_noalloc, whose workspace is a fixed
+ *    device array of the library (64 MiB per GPU, held until the process ends).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *    call only enqueues work and returns; nothing synchronises implicitly.
  *  - Return value: a pkv_status.  Scalar arguments and pointer presence are
@@ -215,6 +217,37 @@ int paged_decode_attn(void* out, int out_dtype,
                       int num_sinks, int window,
                       float* attn_mass, int attn_mass_stride,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_decode_attn_noalloc -- paged_decode_attn without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it.  The call allocates nothing; its workspace is a fixed array of 64 MiB
+ * in device memory that the library holds on every GPU it runs on until the
+ * process ends (its address is looked up once per device, at the first call
+ * with that device current).
+ *   Arguments, results and error behaviour: those of paged_decode_attn, minus
+ *   workspace and workspace_bytes.  A call whose paged_decode_attn workspace
+ *   (paged_decode_attn_workspace_size with the same arguments) exceeds 64 MiB
+ *   returns PKV_EWORKSPACE before anything is enqueued; e.g. without
+ *   attn_mass 64 sequences x 32 query heads x head_dim 128 fit up to
+ *   max_context_len 15872, and one sequence of 32 heads up to 10^6 tokens.
+ *   All calls on one GPU share that GPU's array: two calls that overlap in
+ *   time on one GPU (other streams, other host threads) race and give
+ *   undefined results; calls ordered on one stream are safe.  Nothing in the
+ *   array needs to start at zero, so what an earlier call left there is never
+ *   read.
+ */
+int paged_decode_attn_noalloc(void* out, int out_dtype,
+                              const void* q, int q_dtype,
+                              const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale, int kv_dtype,
+                              const int32_t* block_tables, int block_table_stride,
+                              const int32_t* context_lens, int max_context_len,
+                              int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
+                              int head_dim, int block_size, float scale,
+                              int num_sinks, int window,
+                              float* attn_mass, int attn_mass_stride, void* stream);
 
 /*
  * paged_decode_append_attn -- one decode step of one layer: paged_kv_append of

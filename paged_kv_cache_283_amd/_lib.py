@@ -32,6 +32,8 @@ SIGNATURES = {
     "paged_decode_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "paged_decode_attn": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                _F, _I, _I, _P, _I, _P, _Z, _P]),
+    "paged_decode_attn_noalloc": (_I, [_P, _I, _P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                       _F, _I, _I, _P, _I, _P]),
     "paged_decode_append_attn": (_I, [_P, _I, _P, _I, _P, _P, _I, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I,
                                       _I, _I, _I, _F, _I, _I, _P, _I, _P, _Z, _P]),
     "kv_block_copy": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P]),

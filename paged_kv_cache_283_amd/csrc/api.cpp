@@ -174,15 +174,29 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
       .total;
 }
 
+// Points a call's workspace views into `workspace`, laid out as `lay`.
+static void bind_workspace(pkv::AttnArgs& a, const pkv::WorkspaceLayout& lay, void* workspace) {
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
+  a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.hdr = reinterpret_cast<pkv::StreamHdr*>(ws + lay.hdr_off);
+  a.seq_prefix = reinterpret_cast<int*>(ws + lay.prefix_off);
+  a.stash = a.attn_mass ? reinterpret_cast<float*>(ws + lay.stash_off) : nullptr;
+  a.fin_ml = a.attn_mass ? reinterpret_cast<float*>(ws + lay.fin_off) : nullptr;
+}
+
 // Validates the arguments of a decode-attention call and fills `a`; no HIP
 // call.  num_seqs == 0 leaves a.num_seqs = 0 (nothing to launch).
+// static_workspace: the workspace is the library's fixed one of workspace_bytes
+// (bound later by the caller); only its size is checked here.
 static int prepare_decode_attn(pkv::AttnArgs& a, void* out, int out_dtype, const void* q, int q_dtype,
                                const void* k_pool, const void* v_pool, const float* k_scale, const float* v_scale,
                                int kv_dtype, const int32_t* block_tables, int block_table_stride,
                                const int32_t* context_lens, int max_context_len, int num_seqs, int num_blocks,
                                int num_q_heads, int num_kv_heads, int head_dim, int block_size, float scale,
                                int num_sinks, int window, float* attn_mass, int attn_mass_stride, void* workspace,
-                               size_t workspace_bytes) {
+                               size_t workspace_bytes, bool static_workspace = false,
+                               pkv::WorkspaceLayout* layout = nullptr) {
   a = pkv::AttnArgs{};
   if (block_size != pkv::kBlockSize) return fail(PKV_EUNSUPPORTED, "block_size %d (built: 16)", block_size);
   int st = check_attn_shape(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, num_sinks);
@@ -210,10 +224,17 @@ static int prepare_decode_attn(pkv::AttnArgs& a, void* out, int out_dtype, const
                                                               num_sinks, window, attn_mass != nullptr);
   if (lay.p_max > 65535)
     return fail(PKV_EUNSUPPORTED, "max_context_len %d needs %d partial slots (> 65535)", max_context_len, lay.p_max);
-  if (workspace_bytes < lay.total)
-    return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
-  if (lay.total > 0 && !workspace) return fail(PKV_EINVAL, "NULL workspace");
-  if (((uintptr_t)workspace & 255u) != 0) return fail(PKV_EINVAL, "workspace is not 256-byte aligned");
+  if (static_workspace) {
+    if (lay.total > workspace_bytes)
+      return fail(PKV_EWORKSPACE, "this call needs %zu bytes of workspace; the fixed workspace of "
+                  "paged_decode_attn_noalloc holds %zu (use paged_decode_attn with a caller workspace)",
+                  lay.total, workspace_bytes);
+  } else {
+    if (workspace_bytes < lay.total)
+      return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, lay.total);
+    if (lay.total > 0 && !workspace) return fail(PKV_EINVAL, "NULL workspace");
+    if (((uintptr_t)workspace & 255u) != 0) return fail(PKV_EINVAL, "workspace is not 256-byte aligned");
+  }
   if ((uintptr_t)q % 16 || (uintptr_t)k_pool % 16 || (uintptr_t)v_pool % 16 ||
       (k_scale && (uintptr_t)k_scale % 16) || (v_scale && (uintptr_t)v_scale % 16))
     return fail(PKV_EINVAL, "q, pools and scales must be 16-byte aligned");
@@ -238,16 +259,10 @@ static int prepare_decode_attn(pkv::AttnArgs& a, void* out, int out_dtype, const
   a.window = window;
   a.attn_mass = attn_mass;
   a.mass_stride = attn_mass_stride;
-  char* ws = reinterpret_cast<char*>(workspace);
-  a.part_acc = reinterpret_cast<float*>(ws + lay.acc_off);
-  a.part_ml = reinterpret_cast<float*>(ws + lay.ml_off);
-  a.hdr = reinterpret_cast<pkv::StreamHdr*>(ws + lay.hdr_off);
-  a.seq_prefix = reinterpret_cast<int*>(ws + lay.prefix_off);
-  a.stash = attn_mass ? reinterpret_cast<float*>(ws + lay.stash_off) : nullptr;
-  a.fin_ml = attn_mass ? reinterpret_cast<float*>(ws + lay.fin_off) : nullptr;
   a.p_max = lay.p_max;
   a.nv_pad = lay.nv_pad;
-
+  if (layout) *layout = lay;
+  if (!static_workspace) bind_workspace(a, lay, workspace);
   return ok();
 }
 
@@ -276,6 +291,30 @@ int paged_decode_attn(void* out, int out_dtype, const void* q, int q_dtype, cons
                                      window, attn_mass, attn_mass_stride, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   return launch_prepared_attn(a, kv_dtype, q_dtype, head_dim, stream, "paged_decode_attn");
+}
+
+int paged_decode_attn_noalloc(void* out, int out_dtype, const void* q, int q_dtype, const void* k_pool,
+                              const void* v_pool, const float* k_scale, const float* v_scale, int kv_dtype,
+                              const int32_t* block_tables, int block_table_stride, const int32_t* context_lens,
+                              int max_context_len, int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
+                              int head_dim, int block_size, float scale, int num_sinks, int window, float* attn_mass,
+                              int attn_mass_stride, void* stream) {
+  // Every argument is checked against a workspace of the fixed size first
+  // (the size limit included), before any HIP call.
+  pkv::AttnArgs a;
+  pkv::WorkspaceLayout lay{};
+  const int st = prepare_decode_attn(a, out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
+                                     block_tables, block_table_stride, context_lens, max_context_len, num_seqs,
+                                     num_blocks, num_q_heads, num_kv_heads, head_dim, block_size, scale, num_sinks,
+                                     window, attn_mass, attn_mass_stride, nullptr, pkv::kStaticScratchBytes,
+                                     /*static_workspace=*/true, &lay);
+  if (st != PKV_OK) return st;
+  if (a.num_seqs == 0) return ok();
+  void* ws = nullptr;
+  const int dst = device_status(pkv::static_scratch(&ws), "paged_decode_attn_noalloc: scratch lookup");
+  if (dst != PKV_OK) return dst;
+  bind_workspace(a, lay, ws);
+  return launch_prepared_attn(a, kv_dtype, q_dtype, head_dim, stream, "paged_decode_attn_noalloc");
 }
 
 int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtype, const void* k_new,

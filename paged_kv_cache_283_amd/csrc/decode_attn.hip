@@ -1192,6 +1192,33 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Workspace of paged_decode_attn_noalloc: a fixed device array instead of a
+// caller buffer, for callers that cannot allocate.  Each GPU the library runs
+// on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current, and that pointer is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> by_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it == by_device.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+    it = by_device.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
+
 WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
                                       int num_sinks, int window, bool want_mass) {
   WorkspaceLayout w{};

@@ -94,6 +94,13 @@ struct WorkspaceLayout {
 WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
                                       int num_sinks, int window, bool want_mass);
 
+// Size of the fixed per-device workspace behind paged_decode_attn_noalloc.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+
+// Device address of that workspace on the current device (looked up once per
+// device).
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int head_dim,
                               hipStream_t stream, hipEvent_t ev_main_begin, hipEvent_t ev_main_end);
 

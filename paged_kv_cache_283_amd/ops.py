@@ -304,6 +304,31 @@ def paged_decode_attn(out, q, k_pool, v_pool, block_tables, context_lens, max_co
     return p if prepare else out
 
 
+def paged_decode_attn_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, scale=None,
+                              k_scale=None, v_scale=None, num_sinks=0, window=0, attn_mass=None, stream=None,
+                              prepare=False):
+    """paged_decode_attn with the library's fixed per-device workspace: this call allocates nothing
+    (for graph capture and loops that must not allocate).  Calls that overlap on one GPU race."""
+    b, hq, d = q.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    if tuple(out.shape) != (b, hq, d):
+        raise ValueError("out must have q's shape")
+    _need(block_tables, torch.int32, "block_tables")
+    _need(context_lens, torch.int32, "context_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mass_stride = 0
+    if attn_mass is not None:
+        _need(attn_mass, torch.float32, "attn_mass")
+        mass_stride = attn_mass.shape[1]
+    args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_pool), _ptr(v_pool),
+            _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), int(max_context_len), b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), int(num_sinks),
+            int(window), _ptr(attn_mass), mass_stride, _stream(stream))
+    p = _issue("paged_decode_attn_noalloc", args, prepare)
+    return p if prepare else out
+
+
 def paged_decode_append_attn(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, max_context_len,
                              scale=None, k_scale=None, v_scale=None, num_sinks=0, window=0, attn_mass=None,
                              workspace=None, stream=None, prepare=False):

@@ -259,3 +259,32 @@ def test_prepared_call_holds_the_buffers_the_binding_allocated(monkeypatch):
     assert ops.paged_decode_attn(out, q, k, v, tables, lens, 16, workspace=ws, prepare=True).keep == ()
     p3 = ops.paged_decode_slots(tables, lens, nb, prepare=True)
     assert len(p3.keep) == 1 and p3.keep[0].dtype == torch.int64
+
+
+def noalloc_args(**kw):
+    """paged_decode_attn_noalloc's arguments: paged_decode_attn's without the workspace pair."""
+    a = attn_args(**kw)
+    return a[:-3] + a[-1:]
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(bs=8), _lib.EUNSUPPORTED),
+    (dict(hq=30), _lib.EINVAL),
+    (dict(stride=100), _lib.EINVAL),
+    (dict(kv_dtype=3), _lib.EINVAL),                                       # FP8 without scales
+    (dict(q=None), _lib.EINVAL),
+    (dict(b=64, max_len=16384, stride=1024), _lib.EWORKSPACE),             # needs more than 64 MiB
+    (dict(b=64, max_len=8192, mass=FAKE, mass_stride=8192), _lib.EWORKSPACE),
+])
+def test_noalloc_validation_before_any_hip_call(change, status):
+    lib = _lib.load()
+    assert lib.paged_decode_attn_noalloc(*noalloc_args(**change)) == status
+    msg = lib.pkv_last_error()
+    assert msg != b""
+    if status == _lib.EWORKSPACE:
+        assert b"paged_decode_attn_noalloc" in msg
+
+
+def test_noalloc_zero_sequences_is_a_no_op():
+    lib = _lib.load()
+    assert lib.paged_decode_attn_noalloc(*noalloc_args(b=0, out=None, q=None)) == _lib.OK
