@@ -30,19 +30,29 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: KV GB/s read (% of HBM peak) and decode tokens/s, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ("paged_kv_cache_283_amd/csrc/decode_attn.hip", "paged_kv_cache_283_amd/csrc/device_common.hpp",
-                  "paged_kv_cache_283_amd/csrc/geometry.hpp", "paged_kv_cache_283_amd/csrc/launch.hpp",
-                  "paged_kv_cache_283_amd/csrc/mfma_ops.hpp", "paged_kv_cache_283_amd/build.py")
+_CSRC = "paged_kv_cache_283_amd/csrc/"
+_COMMON = ("device_common.hpp", "geometry.hpp", "launch.hpp", "../build.py")
+# Sources each operation's kernels are built from: a profile summary carries the hash of its set,
+# so a summary taken before a kernel change is recognisably stale.
+OP_SOURCES = {
+    "decode": ("decode_attn.hip", "mfma_ops.hpp", "kv_codec.hpp", "fp8_e4m3.hpp"),
+    "prefill": ("prefill_attn.hip", "mfma_ops.hpp"),
+    "evict": ("keep_select.hip", "kv_compact.hip"),
+    "fill": ("kv_write.hip", "kv_codec.hpp", "fp8_e4m3.hpp"),
+    "swap": ("kv_swap.hip",),
+}
+KERNEL_SOURCES = tuple(_CSRC + f for f in OP_SOURCES["decode"] + _COMMON)
 WORKLOAD_NAMES = {"llama3": "llama3-8b-layer-decode", "fp8long": "fp8-kv-32k-shared-prefix",
                   "int8long": "int8-kv-32k", "fp8chlong": "fp8-per-channel-kv-32k",
                   "streaming": "streamingllm-131k-sinks4-window4096", "h2o": "h2o-8k-mass",
                   "llama2": "llama2-70b-80-layer-decode", "tiny": "tiny-paged-decode"}
 
 
-def kernel_hash() -> str:
+def kernel_hash(op: str = "decode") -> str:
+    """sha256 prefix of the sources (and build flags) the operation's kernels are built from."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+    for f in OP_SOURCES[op] + _COMMON:
+        h.update(open(os.path.join(ROOT, _CSRC + f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -208,7 +218,8 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "keep_select_us": round(1e3 * t_sel, 2), "keep_select_bytes": sel_bytes,
         "compact_us": round(1e3 * t_cmp, 2), "compact_bytes": moved,
-        "probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1)}), flush=True)
+        "probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1),
+        "kernel_hash": kernel_hash("evict")}), flush=True)
 
 
 MFMA_PEAK_BF16_TFLOPS = 2500.0
@@ -269,7 +280,8 @@ def bench_prefill(args, dev, stream):
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None},
         "flops_per_step": flops, "prefill_kernel_avg_us": round(1e3 * float(np.mean(ms)), 2),
         "prefill_kernel_min_us": round(1e3 * float(ms.min()), 2), "kv_bytes_in_context": kv_bytes,
-        "tokens_per_s": round(w.num_seqs * w.chunk / (t * 1e-3), 1)}), flush=True)
+        "tokens_per_s": round(w.num_seqs * w.chunk / (t * 1e-3), 1), "kernel_hash": kernel_hash("prefill")}),
+          flush=True)
 
 
 def bench_fill(args, dev, stream, copy_gbs):
@@ -322,7 +334,8 @@ def bench_fill(args, dev, stream, copy_gbs):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
         "bytes_per_token": per_tok, "write_kernel_avg_us": round(1e3 * float(np.mean(ms)), 2),
-        "probe_copy_gbs": round(copy_gbs, 1), "frac_of_probe_copy": round(gbs / copy_gbs, 4)}), flush=True)
+        "probe_copy_gbs": round(copy_gbs, 1), "frac_of_probe_copy": round(gbs / copy_gbs, 4),
+        "kernel_hash": kernel_hash("fill")}), flush=True)
 
 
 HOST_LINK_PEAK_GBS = 64.0   # PCIe 5.0 x16, one direction
@@ -369,7 +382,8 @@ def bench_swap(args, dev, stream):
         "roofline": {"bound": "link", "achieved": round(max(out_gbs, in_gbs), 2), "peak": HOST_LINK_PEAK_GBS,
                      "unit": "GB/s", "frac": round(max(out_gbs, in_gbs) / HOST_LINK_PEAK_GBS, 4), "traffic": None},
         "swap_out_gbs": round(out_gbs, 2), "swap_in_gbs": round(in_gbs, 2),
-        "swap_out_ms": round(t_out, 4), "swap_in_ms": round(t_in, 4)}), flush=True)
+        "swap_out_ms": round(t_out, 4), "swap_in_ms": round(t_in, 4), "kernel_hash": kernel_hash("swap")}),
+          flush=True)
 
 
 def main():

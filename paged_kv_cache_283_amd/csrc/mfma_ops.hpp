@@ -47,6 +47,26 @@ __device__ __forceinline__ f32x4 mfma_k32(const uint32_t* a, const uint32_t* b, 
 }
 
 template <bool F16>
+__device__ __forceinline__ f32x4 mfma_k32v(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (F16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Two floats as packed 16-bit MFMA operands: the bf16 high parts (the upper 16
+// bits, truncated) and the bf16 truncation of the residuals f - high, so that
+// high + low carries about 16 significant bits.  One v_perm_b32 packs each pair.
+__device__ __forceinline__ void split_bf16_pair(float f0, float f1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t u0 = __float_as_uint(f0), u1 = __float_as_uint(f1);
+  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+  const float r0 = f0 - __uint_as_float(u0 & 0xffff0000u);
+  const float r1 = f1 - __uint_as_float(u1 & 0xffff0000u);
+  lo = __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u);
+}
+
+template <bool F16>
 __device__ __forceinline__ f32x4 mfma_k16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
   u32x2 av = {a0, a1};
   u32x2 bv = {b0, b1};

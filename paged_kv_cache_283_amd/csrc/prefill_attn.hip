@@ -23,7 +23,10 @@
 // the tiles come from HBM once and from the caches for the other waves.  Work
 // is split by query token only: every wave covers the whole causal range of
 // its tokens, two blocks per step so that PV runs as 16x16x32 MFMAs over both
-// blocks' 32 keys.
+// blocks' 32 keys.  Steps whose keys every column of the wave sees (all but
+// the last one or two of a wave) take a path with no mask at all, where the
+// logit factor enters the exponent's fma; the factor's sign is folded into the
+// query operands so that the running max is taken on the raw products.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -43,11 +46,57 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #ifndef PKV_PREFILL_SETS
 #define PKV_PREFILL_SETS 2                // 16-column query sets per wave for long chunks
 #endif
+#ifndef PKV_PREFILL_STAGE
+#define PKV_PREFILL_STAGE 1               // 16-bit pools: K/V block pairs staged once per workgroup in LDS
+#endif
+#ifndef PKV_PREFILL_STAGES
+#define PKV_PREFILL_STAGES 4              // LDS ring slots (pairs in flight = slots - 1)
+#endif
+
 
 
 namespace {
 
 }  // namespace
+
+// One step of the LDS ring: the table entries of the step's block pair, this
+// lane's K and V operand chunks of the pair from the slot at rd, and the
+// direct-to-LDS copy of one tile of a later pair into the slot at wr (LPS rows
+// of 1 KiB: row k from src_tile + k * 1024 to row row0 + row_step * k).  Every
+// LDS access of the step goes through the restrict parameters, so once inlined
+// the compiler knows the copy writes none of what the step reads; otherwise
+// each LDS read waits for every copy in flight (vmcnt(0)) and the ring holds a
+// single pair.
+template <int TB, int LPS, int KW4, int VQ>
+__device__ __forceinline__ void ring_io(const int* __restrict__ tab, const uint8_t* __restrict__ rd,
+                                        uint8_t* __restrict__ wr, int i, bool has_b, int blk_next,
+                                        const uint8_t* kvbase, size_t tile_mul, size_t tile_add, int num_blocks,
+                                        int row0, int row_step, int c, int j, int lane, int src_off, u32x4* ka,
+                                        u32x4* kb, u32x4* va, u32x4* vb, bool& oka, bool& okb) {
+  const int ea = tab[i], eb = has_b ? tab[i + 1] : 0;
+  oka = ea >= 0 && ea < num_blocks;
+  okb = eb >= 0 && eb < num_blocks;
+  const int phys = __builtin_amdgcn_readfirstlane(tab[blk_next]);
+  const uint8_t* src = kvbase + ((size_t)(phys >= 0 && phys < num_blocks ? phys : 0) * tile_mul + tile_add) * TB +
+                       src_off;
+#pragma unroll
+  for (int w = 0; w < KW4; ++w) {
+    ka[w] = *reinterpret_cast<const u32x4*>(rd + ((4 * w + j) * kBlockSize + c) * 16);
+    kb[w] = *reinterpret_cast<const u32x4*>(rd + TB + ((4 * w + j) * kBlockSize + c) * 16);
+  }
+  // Both are in lane order: lane l's 16 bytes of row r at r * 1024 + l * 16
+  // (the copy of a V tile gathers each lane's chunk from where the pool keeps
+  // it, so that these reads are conflict-free).
+#pragma unroll
+  for (int g = 0; g < VQ; ++g) {
+    va[g] = *reinterpret_cast<const u32x4*>(rd + 2 * TB + (2 * g) * 1024 + lane * 16);
+    vb[g] = *reinterpret_cast<const u32x4*>(rd + 2 * TB + (2 * g + 1) * 1024 + lane * 16);
+  }
+#pragma unroll
+  for (int k = 0; k < LPS; ++k)
+    __builtin_amdgcn_global_load_lds(src + k * 1024, (__attribute__((address_space(3))) void*)(wr + (row0 + row_step * k) * 1024),
+                                     16, 0, 0);
+}
 
 template <int KVT, int QT, int D, int CS>
 __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
@@ -64,7 +113,19 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   constexpr bool QSAME = (!OP32) && (QT == (F16 ? DT_F16 : DT_BF16)) && !CH;
   constexpr bool QSPLIT = (!OP32) && !QSAME;
   constexpr int QW = OP32 ? 1 : DPL / 2;
-  __shared__ int s_tab_all[kPfWaves][kPfTab];
+  constexpr int VQ = NT * VW / 4;                // 16-byte V chunks per block
+  // 16-bit pools: the workgroup's 4 waves walk the same blocks, so each block
+  // pair is copied once into an LDS ring (direct global-to-LDS loads, one tile
+  // per wave) and every wave builds its operands from there: the L2-to-CU
+  // load instructions per MFMA drop by 4, and those are what bound the
+  // register path (each wave loading every tile itself).
+  constexpr bool STAGE = PKV_PREFILL_STAGE && EB == 2 && !OP32;
+  constexpr int TB = kBlockSize * D * EB;        // bytes of one (block, KV head) tile
+  constexpr int SB = 4 * TB;                     // one ring slot: K_a, K_b, then V_a / V_b by 1 KiB rows
+  constexpr int NS = PKV_PREFILL_STAGES;
+  constexpr int LPS = TB / 1024;                 // direct-to-LDS loads per wave and slot
+  __shared__ int s_tab_all[STAGE ? 1 : kPfWaves][kPfTab];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[STAGE ? NS * SB : 16];
 
   const int hq = a.num_q_heads;
   const int hkv = a.num_kv_heads;
@@ -74,7 +135,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   const int lane = threadIdx.x & 63;
   const int c = lane & 15;
   const int j = lane >> 4;
-  int* s_tab = s_tab_all[wave];
+  int* s_tab = s_tab_all[STAGE ? 0 : wave];
 
   // Workgroup -> (sequence, KV head, tile).  With a pair count divisible by 8,
   // all tiles of a (sequence, KV head) go to one XCD (ids are dealt to the 8
@@ -95,9 +156,21 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   const int n_q = a.query_start[s + 1] - q0;
   const int L = a.context_lens[s];
   const int t0 = (tile * kPfWaves + wave) * CS * tpw;   // first query token of this wave
-  if (q0 < 0 || n_q < 1 || n_q > a.num_tokens - q0 || t0 >= n_q) return;   // rows outside q/out: skip
+  const int t0_wg = tile * kPfWaves * CS * tpw;          // first query token of the workgroup
+  // Rows outside q/out: skip.  With the LDS ring the workgroup stays together
+  // (every wave takes part in the loads and barriers); a wave past the chunk
+  // computes but stores nothing.
+  if (q0 < 0 || n_q < 1 || n_q > a.num_tokens - q0 || (STAGE ? t0_wg : t0) >= n_q) return;
+  const bool wave_live = t0 < n_q;
   const int prefix = L - n_q;
   const bool seq_ok = L >= n_q && L <= a.max_context_len && L <= a.table_stride * kBlockSize;
+
+  // The logit factor's sign goes into q: q . k * scale = (-q) . k * |scale|, and
+  // negating the 16-bit (or f32) operands flips sign bits only, so it is exact.
+  // With a non-negative factor the largest logit is the largest raw product.
+  const bool neg = a.scale_log2 < 0.f;
+  const float sl2 = fabsf(a.scale_log2);
+  const uint32_t qflip = neg ? 0x80008000u : 0u;
 
   // ---- column c of set cs = (query token t0 + cs * tpw + c / G, head kvh * G + c % G)
   const int head = kvh * group + c % group;
@@ -114,14 +187,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     const size_t qrow = ((size_t)(q0 + (col_ok[cs] ? tok[cs] : 0)) * hq + head) * D;
     if constexpr (OP32) {
 #pragma unroll
-      for (int st = 0; st < DPL; ++st)
-        qf[cs][st] = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + qk_dim_f32(st, j)) : 0.f;
+      for (int st = 0; st < DPL; ++st) {
+        const float f = col_ok[cs] ? load_q_elem<QT>(a.q, qrow + qk_dim_f32(st, j)) : 0.f;
+        qf[cs][st] = neg ? -f : f;
+      }
     } else if constexpr (QSAME) {
       const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) + qrow;
 #pragma unroll
       for (int st = 0; st < QW / 4; ++st) {
         const u32x4 v = col_ok[cs] ? *reinterpret_cast<const u32x4*>(qh + qk_dim16<KVT>(st, j)) : u32x4{0, 0, 0, 0};
-        qhi[cs][4 * st + 0] = v[0]; qhi[cs][4 * st + 1] = v[1]; qhi[cs][4 * st + 2] = v[2]; qhi[cs][4 * st + 3] = v[3];
+        qhi[cs][4 * st + 0] = v[0] ^ qflip; qhi[cs][4 * st + 1] = v[1] ^ qflip;
+        qhi[cs][4 * st + 2] = v[2] ^ qflip; qhi[cs][4 * st + 3] = v[3] ^ qflip;
       }
     } else {
 #pragma unroll
@@ -138,8 +214,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           const uint32_t h0 = to_op16<F16>(f0), h1 = to_op16<F16>(f1);
           const uint32_t l0 = to_op16<F16>(f0 - from_op16<F16>(h0));
           const uint32_t l1 = to_op16<F16>(f1 - from_op16<F16>(h1));
-          qhi[cs][4 * st + w] = h0 | (h1 << 16);
-          qlo[cs][4 * st + w] = l0 | (l1 << 16);
+          qhi[cs][4 * st + w] = (h0 | (h1 << 16)) ^ qflip;
+          qlo[cs][4 * st + w] = (l0 | (l1 << 16)) ^ qflip;
         }
       }
     }
@@ -179,76 +255,102 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   const int32_t* trow = a.block_tables + (size_t)s * a.table_stride;
   // Keys the wave needs: 0 .. prefix + its last token; keys below prefix + t0
   // are visible to every column (no mask there).
-  const int t_last = min(t0 + CS * tpw, n_q) - 1;
+  // (with the ring: the last token of the workgroup, which all its waves walk to)
+  const int t_last = min((STAGE ? t0_wg + kPfWaves * CS * tpw : t0 + CS * tpw), n_q) - 1;
   const int n_blocks = seq_ok ? (prefix + t_last) / kBlockSize + 1 : 0;
   const int all_visible = prefix + t0;
   int c0 = 0;
 
-  struct Regs {
-    // Held as the loaded 16-byte vectors: operands are then built by element
-    // selects, never through a word array the compiler could widen into
-    // memory accesses.
-    u32x4 kq[KW / 4];
-    u32x4 vq[NT * VW / 4];
-    __device__ uint32_t k(int w) const { return kq[w / 4][w % 4]; }
-    __device__ uint32_t v(int t, int e) const { return vq[(t * VW + e) / 4][(t * VW + e) % 4]; }
-    __device__ void set_v(int t, int e, uint32_t x) { vq[(t * VW + e) / 4][(t * VW + e) % 4] = x; }
-    f32x4 ks, vs;
-    bool ok;
+  // The two blocks (a, b) of one step, held as the loaded 16-byte vectors:
+  // operands are built by element selects, never through a word array the
+  // compiler could widen into memory accesses.  (Loading 16-bit V as 8-byte
+  // pieces straight into each tile's operand quad saves the register moves that
+  // assemble it, but doubles the load instructions, and the L2-to-CU path they
+  // share is what bounds this kernel: measured 30% slower.)
+  struct Pair {
+    u32x4 ka[KW / 4], kb[KW / 4];
+    u32x4 va[VQ], vb[VQ];
+    f32x4 ksa, ksb, vsa, vsb;
+    bool oka, okb;
   };
+  // Word e of tile t of block a (B = false) or b (B = true).
+  auto vword = [](const Pair& P, auto bsel, int t, int e) -> uint32_t {
+    constexpr bool B = decltype(bsel)::value;
+    return B ? P.vb[(t * VW + e) / 4][(t * VW + e) % 4] : P.va[(t * VW + e) / 4][(t * VW + e) % 4];
+  };
+  auto set_vword = [](Pair& P, auto bsel, int t, int e, uint32_t x) {
+    constexpr bool B = decltype(bsel)::value;
+    if constexpr (B) P.vb[(t * VW + e) / 4][(t * VW + e) % 4] = x;
+    else P.va[(t * VW + e) / 4][(t * VW + e) % 4] = x;
+  };
+  constexpr std::false_type kA{};
+  constexpr std::true_type kB{};
 
-  // Loads of block i's tiles into r (K and V halves separately, so a step can
-  // refill K while it still uses V).  An entry outside the pool reads block 0
-  // instead (in bounds) and marks r bad.
-  auto tile_of = [&](Regs& r, int i) {
+  // Loads of block i's tiles into half a or b of P (K and V separately, so a
+  // step can refill K while it still uses V).  An entry outside the pool reads
+  // block 0 instead (in bounds) and marks that half bad.
+  auto tile_of = [&](int i, bool& ok) {
     const int phys = __builtin_amdgcn_readfirstlane(s_tab[i]);
-    r.ok = phys >= 0 && phys < a.num_blocks;
-    return (size_t)(r.ok ? phys : 0) * hkv + kvh;
+    ok = phys >= 0 && phys < a.num_blocks;
+    return (size_t)(ok ? phys : 0) * hkv + kvh;
   };
-  auto load_k = [&](Regs& r, int i) {
-    const size_t tile_i = tile_of(r, i);
+  auto load_k = [&](Pair& P, auto bsel, int i) {
+    constexpr bool B = decltype(bsel)::value;
+    bool ok;
+    const size_t tile_i = tile_of(i, ok);
     const uint8_t* kt = kbase + tile_i * (size_t)(kBlockSize * D * EB);
 #pragma unroll
     for (int w = 0; w < KW / 4; ++w) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(kt + ((size_t)(4 * w + j) * kBlockSize + c) * 16);
-      r.kq[w] = v;
+      if constexpr (B) P.kb[w] = v;
+      else P.ka[w] = v;
     }
-    if constexpr (is_quantised(KVT)) r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile_i * kBlockSize + 4 * j);
+    if constexpr (is_quantised(KVT)) {
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(a.k_scale + tile_i * kBlockSize + 4 * j);
+      if constexpr (B) P.ksb = sc;
+      else P.ksa = sc;
+    }
+    if constexpr (B) P.okb = ok;
+    else P.oka = ok;
   };
-  auto load_v = [&](Regs& r, int i) {
-    const size_t tile_i = tile_of(r, i);
+  auto load_v = [&](Pair& P, auto bsel, int i) {
+    constexpr bool B = decltype(bsel)::value;
+    bool ok;
+    const size_t tile_i = tile_of(i, ok);
     const uint8_t* vt = vbase + tile_i * (size_t)(kBlockSize * D * EB);
 #pragma unroll
-    for (int g = 0; g < NT * VW / 4; ++g) {
+    for (int g = 0; g < VQ; ++g) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(vt + ((size_t)(g * 16 + c) * 4 + j) * 16);
-      r.vq[g] = v;
+      if constexpr (B) P.vb[g] = v;
+      else P.va[g] = v;
     }
-    if constexpr (is_quantised(KVT)) r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile_i * kBlockSize + 4 * j);
-  };
-  auto load = [&](Regs& r, int i) {
-    load_k(r, i);
-    load_v(r, i);
+    if constexpr (is_quantised(KVT)) {
+      const f32x4 sc = *reinterpret_cast<const f32x4*>(a.v_scale + tile_i * kBlockSize + 4 * j);
+      if constexpr (B) P.vsb = sc;
+      else P.vsa = sc;
+    }
   };
 
   // S = K q^T of one block for every column set, sharing the converted K operand.
-  auto qk = [&](const Regs& r, f32x4* sacc) {
+  auto qk = [&](const u32x4* kq, f32x4* sacc) {
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) sacc[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (OP32) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) sacc[cs] = mfma_f32_k4(__uint_as_float(r.k(e)), qf[cs][e], sacc[cs]);
+        for (int cs = 0; cs < CS; ++cs)
+          sacc[cs] = mfma_f32_k4(__uint_as_float(kq[e / 4][e % 4]), qf[cs][e], sacc[cs]);
       }
     } else {
 #pragma unroll
       for (int st = 0; st < DPL / 8; ++st) {
         uint32_t av[4];
         if constexpr (is_code8(KVT)) {
-          code8x4_to_bf16x4<KVT>(r.k(2 * st), av[0], av[1]);
-          code8x4_to_bf16x4<KVT>(r.k(2 * st + 1), av[2], av[3]);
+          code8x4_to_bf16x4<KVT>(kq[st / 2][2 * (st % 2)], av[0], av[1]);
+          code8x4_to_bf16x4<KVT>(kq[st / 2][2 * (st % 2) + 1], av[2], av[3]);
         } else {
-          av[0] = r.k(4 * st); av[1] = r.k(4 * st + 1); av[2] = r.k(4 * st + 2); av[3] = r.k(4 * st + 3);
+          av[0] = kq[st][0]; av[1] = kq[st][1]; av[2] = kq[st][2]; av[3] = kq[st][3];
         }
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs) {
@@ -260,7 +362,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   };
 
   // Keys past the context (the unused tail of the last block): V zeroed.
-  auto mask_tail = [&](Regs& r, int blk0, bool* in_ctx) {
+  auto mask_tail = [&](Pair& P, auto bsel, int blk0, bool* in_ctx) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) in_ctx[e] = blk0 + 4 * j + e < L;
 #pragma unroll
@@ -268,69 +370,82 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       if constexpr (VW == 1) {
         const uint32_t msk = (in_ctx[0] ? 0xffu : 0u) | (in_ctx[1] ? 0xff00u : 0u) |
                              (in_ctx[2] ? 0xff0000u : 0u) | (in_ctx[3] ? 0xff000000u : 0u);
-        r.set_v(t, 0, r.v(t, 0) & msk);
+        set_vword(P, bsel, t, 0, vword(P, bsel, t, 0) & msk);
       } else if constexpr (VW == 2) {
-        r.set_v(t, 0, r.v(t, 0) & ((in_ctx[0] ? 0xffffu : 0u) | (in_ctx[1] ? 0xffff0000u : 0u)));
-        r.set_v(t, 1, r.v(t, 1) & ((in_ctx[2] ? 0xffffu : 0u) | (in_ctx[3] ? 0xffff0000u : 0u)));
+        set_vword(P, bsel, t, 0, vword(P, bsel, t, 0) & ((in_ctx[0] ? 0xffffu : 0u) | (in_ctx[1] ? 0xffff0000u : 0u)));
+        set_vword(P, bsel, t, 1, vword(P, bsel, t, 1) & ((in_ctx[2] ? 0xffffu : 0u) | (in_ctx[3] ? 0xffff0000u : 0u)));
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) r.set_v(t, e, in_ctx[e] ? r.v(t, e) : 0u);
+        for (int e = 0; e < 4; ++e) set_vword(P, bsel, t, e, in_ctx[e] ? vword(P, bsel, t, e) : 0u);
       }
     }
   };
 
-  // V tile t of one block as the 16-bit PV A operand (two words: tokens 4j..4j+3 of dim 16t + c).
-  auto v_operand = [&](const Regs& r, int t, uint32_t& v0, uint32_t& v1) {
-    if constexpr (is_code8(KVT)) {
-      code8x4_to_bf16x4<KVT>(r.v(t, 0), v0, v1);
-    } else {
-      v0 = r.v(t, 0);
-      v1 = r.v(t, 1);
+  // One step over the blocks i (half a) and i + 1 (half b, only if has_b): QK,
+  // the online softmax over the step's keys, PV.  Each PV MFMA is a 16x16x32
+  // whose 32 keys are both blocks' 16: lane (c, j) holds tokens 4j..4j+3 of
+  // block i, then of block i + 1, in the V operand and the probability operand
+  // alike, so the contraction pairs them correctly and one instruction does the
+  // work of two 16x16x16 ones (which run at half the rate per flop on gfx950).
+  // Without a second block its logits are -inf and its V operand zero.
+  //
+  // qk_step: S = K q^T for both blocks; with refill, the next pair's K loads
+  // (blocks i + 2, i + 3) are issued as soon as the QK MFMAs have consumed K.
+  constexpr int NB = 2;
+  // The step's K scales (per-token formats) are taken before the refill overwrites them.
+  auto qk_step = [&](Pair& P, f32x4 (&sacc)[NB][CS], f32x4 (&kscale)[NB], int i, bool has_b, bool refill) {
+    bad |= !P.oka || (has_b && !P.okb);
+    qk(P.ka, sacc[0]);
+    qk(P.kb, sacc[1]);
+    if constexpr (is_quantised(KVT)) {
+      kscale[0] = P.ksa;
+      kscale[1] = P.ksb;
+    }
+    if (refill) {
+      load_k(P, kA, i + 2);
+      load_k(P, kB, i + 3);
     }
   };
-
-  // One step over the blocks i (ra) and i + 1 (rb, only if has_b): QK, the
-  // online softmax over the step's keys, PV.  Each PV MFMA is a 16x16x32 whose
-  // 32 keys are both blocks' 16: lane (c, j) holds tokens 4j..4j+3 of block i,
-  // then of block i + 1, in the V operand and the probability operand alike,
-  // so the contraction pairs them correctly and one instruction does the work
-  // of two 16x16x16 ones (which run at half the rate per flop on gfx950).
-  // Without a second block its logits are -inf and its V operand zero.
-  // With refill, the next pair's K loads (blocks i + 2, i + 3) are issued as
-  // soon as this step's QK MFMAs have consumed K.
-  constexpr int NB = 2;
-  auto compute = [&](Regs& ra, Regs& rb, int i, bool has_b, bool refill) {
-    // (ra and rb are named explicitly, never selected by index: a reference
-    // chosen at run time would keep the register buffers in memory.)
-    f32x4 sacc[NB][CS];
-    bool full[NB];
+  // softmax_pv: the online softmax over the step's keys and PV.  Modes:
+  //  kFull   every key of both blocks is inside the context and visible to
+  //          every column: no mask is evaluated, and for formats without
+  //          per-key scales the logit factor is applied inside the exponent,
+  //          exp2(raw * |f| - (bias * |f| + m)), one fma per logit;
+  //  kCausal every key is inside the context (the steady-state loop never
+  //          reaches the sequence's last block), only the columns' causal
+  //          limits apply;
+  //  kAny    also keys past the context: their V values are zeroed.
+  // Only kAny changes P, so the branch between kFull and kCausal in the loop
+  // joins with the same operand registers.
+  auto softmax_pv = [&](Pair& P, f32x4 (&sacc)[NB][CS], const f32x4 (&kscale)[NB], int i, bool has_b, auto mode) {
+    constexpr int MODE = decltype(mode)::value;
+    constexpr bool FULL = MODE == 0;
+    constexpr bool TAIL = MODE == 2;
+    constexpr bool RAWMAX = FULL && !is_quantised(KVT);
+    bool full[NB] = {true, true};
     bool in_ctx[NB][4];
     int blk0[NB];
     float ksc[NB][4], vsc[NB][4];
-    bad |= !ra.ok || (has_b && !rb.ok);
     blk0[0] = (c0 + i) * kBlockSize;
     blk0[1] = blk0[0] + kBlockSize;
-    qk(ra, sacc[0]);
-    qk(rb, sacc[1]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ksc[0][e] = is_quantised(KVT) ? ra.ks[e] : 1.f;
-      ksc[1][e] = is_quantised(KVT) ? rb.ks[e] : 1.f;
-      vsc[0][e] = is_quantised(KVT) ? ra.vs[e] : 1.f;
-      vsc[1][e] = is_quantised(KVT) ? rb.vs[e] : 1.f;
+      ksc[0][e] = is_quantised(KVT) ? kscale[0][e] * sl2 : sl2;
+      ksc[1][e] = is_quantised(KVT) ? kscale[1][e] * sl2 : sl2;
+      vsc[0][e] = is_quantised(KVT) ? P.vsa[e] : 1.f;
+      vsc[1][e] = is_quantised(KVT) ? P.vsb[e] : 1.f;
       in_ctx[0][e] = in_ctx[1][e] = true;
     }
-    if (refill) {
-      load_k(ra, i + 2);
-      load_k(rb, i + 3);
+    if constexpr (!FULL) {
+      full[0] = blk0[0] + kBlockSize <= all_visible;
+      full[1] = blk0[1] + kBlockSize <= all_visible && has_b;
     }
-    full[0] = blk0[0] + kBlockSize <= all_visible;
-    full[1] = blk0[1] + kBlockSize <= all_visible && has_b;
-    if (!full[0]) mask_tail(ra, blk0[0], in_ctx[0]);
-    if (!full[1]) mask_tail(rb, has_b ? blk0[1] : L, in_ctx[1]);   // an absent block lies wholly past L
+    if constexpr (TAIL) {
+      if (!full[0]) mask_tail(P, kA, blk0[0], in_ctx[0]);
+      if (!full[1]) mask_tail(P, kB, has_b ? blk0[1] : L, in_ctx[1]);   // an absent block lies wholly past L
+    }
     // ---- per column set: causal mask, online softmax, probabilities as PV operands
     uint32_t ph[CS][2 * NB], pl[CS][2 * NB];
-    float pvv[CS][NB][4];
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
       float x[NB][4];
@@ -339,14 +454,19 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          float v = (BIAS ? sacc[b][cs][e] - qbias[cs] : sacc[b][cs][e]) * a.scale_log2;
-          if constexpr (is_quantised(KVT)) v *= ksc[b][e];
-          if (!full[b]) v = in_ctx[b][e] && blk0[b] + 4 * j + e <= pos[cs] ? v : -INFINITY;
+          float v;
+          if constexpr (RAWMAX) {
+            v = sacc[b][cs][e];
+          } else {
+            v = (BIAS ? sacc[b][cs][e] - qbias[cs] : sacc[b][cs][e]) * ksc[b][e];
+            if (!full[b]) v = in_ctx[b][e] && blk0[b] + 4 * j + e <= pos[cs] ? v : -INFINITY;
+          }
           x[b][e] = v;
         }
         mx = fmaxf(mx, fmaxf(fmaxf(x[b][0], x[b][1]), fmaxf(x[b][2], x[b][3])));
       }
-      const float mb = row_max4(mx);
+      // the step's largest (scaled) logit of this column
+      const float mb = RAWMAX ? (row_max4(mx) - qbias[cs]) * sl2 : row_max4(mx);
       const bool need = mb > m_run[cs] + kPfRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
         const float m_new = need ? mb : m_run[cs];
@@ -358,78 +478,163 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         m_run[cs] = m_new;
       }
       const float mref = m_run[cs] == -INFINITY ? 0.f : m_run[cs];
+      const float off = -(qbias[cs] * sl2) - mref;   // RAWMAX: exponent = raw * |f| + off
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        float pr[4];
+        float pr[4], pv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(x[b][e] - mref);
+        for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(RAWMAX ? __builtin_fmaf(x[b][e], sl2, off) : x[b][e] - mref);
         l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if constexpr (is_quantised(KVT)) pvv[cs][b][e] = in_ctx[b][e] ? pr[e] * vsc[b][e] : 0.f;
-          else pvv[cs][b][e] = pr[e];
+          if constexpr (is_quantised(KVT)) pv[e] = in_ctx[b][e] ? pr[e] * vsc[b][e] : 0.f;
+          else pv[e] = pr[e];
         }
         if constexpr (!OP32) {
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
-            const float f0 = pvv[cs][b][2 * w], f1 = pvv[cs][b][2 * w + 1];
-            uint32_t h0, h1, l0, l1;
+            const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
+            uint32_t hw, lw;
             if constexpr (F16) {
-              h0 = f32_to_f16_bits(f0);
-              h1 = f32_to_f16_bits(f1);
-              l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
-              l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
+              const uint32_t h0 = f32_to_f16_bits(f0), h1 = f32_to_f16_bits(f1);
+              const uint32_t l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
+              const uint32_t l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
+              hw = h0 | (h1 << 16);
+              lw = l0 | (l1 << 16);
             } else {
-              h0 = __float_as_uint(f0) >> 16;
-              h1 = __float_as_uint(f1) >> 16;
-              l0 = __float_as_uint(f0 - bf16_to_f32(h0)) >> 16;
-              l1 = __float_as_uint(f1 - bf16_to_f32(h1)) >> 16;
+              split_bf16_pair(f0, f1, hw, lw);
               if constexpr (BIAS)
-                p_run[cs] += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+                p_run[cs] += (bf16_to_f32(hw & 0xffffu) + bf16_to_f32(lw & 0xffffu)) +
+                             (bf16_to_f32(hw >> 16) + bf16_to_f32(lw >> 16));
             }
-            ph[cs][2 * b + w] = h0 | (h1 << 16);
-            pl[cs][2 * b + w] = l0 | (l1 << 16);
+            ph[cs][2 * b + w] = hw;
+            pl[cs][2 * b + w] = lw;
+          }
+        } else {
+          // f32 pools: PV with the 16x16x4 f32 MFMA, one key per step
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t vw = b ? vword(P, kB, t, e) : vword(P, kA, t, e);
+              acc[cs][t] = mfma_f32_k4(__uint_as_float(vw), pv[e], acc[cs][t]);
+            }
           }
         }
       }
     }
     // ---- O^T += V^T P^T per set, sharing the converted V operand
-    if constexpr (OP32) {
+    if constexpr (!OP32) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-#pragma unroll
-          for (int cs = 0; cs < CS; ++cs) {
-            acc[cs][t] = mfma_f32_k4(__uint_as_float(ra.v(t, e)), pvv[cs][0][e], acc[cs][t]);
-            acc[cs][t] = mfma_f32_k4(__uint_as_float(rb.v(t, e)), pvv[cs][1][e], acc[cs][t]);
-          }
+        u32x4 av;
+        if constexpr (EB == 2) {
+          av = u32x4{vword(P, kA, t, 0), vword(P, kA, t, 1), vword(P, kB, t, 0), vword(P, kB, t, 1)};
+        } else {
+          uint32_t v0, v1, v2, v3;
+          code8x4_to_bf16x4<KVT>(vword(P, kA, t, 0), v0, v1);
+          code8x4_to_bf16x4<KVT>(vword(P, kB, t, 0), v2, v3);
+          av = u32x4{v0, v1, v2, v3};
         }
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        uint32_t av[4];
-        v_operand(ra, t, av[0], av[1]);
-        v_operand(rb, t, av[2], av[3]);
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs) {
-          acc[cs][t] = mfma_k32<F16>(av, ph[cs], acc[cs][t]);
-          acc[cs][t] = mfma_k32<F16>(av, pl[cs], acc[cs][t]);
+          acc[cs][t] = mfma_k32v<F16>(av, u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, acc[cs][t]);
+          acc[cs][t] = mfma_k32v<F16>(av, u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t]);
         }
       }
     }
   };
   // An absent second block: defined (zero) operands; its keys are masked.
-  auto clear = [&](Regs& r) {
+  auto clear_b = [&](Pair& P) {
 #pragma unroll
-    for (int w = 0; w < KW / 4; ++w) r.kq[w] = u32x4{0u, 0u, 0u, 0u};
+    for (int w = 0; w < KW / 4; ++w) P.kb[w] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int g = 0; g < NT * VW / 4; ++g) r.vq[g] = u32x4{0u, 0u, 0u, 0u};
-    r.ks = r.vs = f32x4{0.f, 0.f, 0.f, 0.f};
-    r.ok = true;
+    for (int g = 0; g < VQ; ++g) P.vb[g] = u32x4{0u, 0u, 0u, 0u};
+    P.ksb = P.vsb = f32x4{0.f, 0.f, 0.f, 0.f};
+    P.okb = true;
   };
+  constexpr std::integral_constant<int, 0> kFull{};
+  constexpr std::integral_constant<int, 1> kCausal{};
+  constexpr std::integral_constant<int, 2> kAny{};
 
+  if constexpr (STAGE) {
+    for (; c0 < n_blocks; c0 += kPfTab) {
+      const int n = min(kPfTab, n_blocks - c0);
+      for (int k = threadIdx.x; k < n; k += 256) s_tab[k] = trow[c0 + k];
+      __syncthreads();                 // the ring is drained here: no copy in flight
+      const int npairs = (n + 1) / 2;
+      // Slot p % NS receives pair p (blocks 2p, 2p + 1): wave 0 copies K of
+      // block 2p, wave 1 K of 2p + 1, wave 2 V of 2p, wave 3 V of 2p + 1, each
+      // 1 KiB of the tile per instruction, byte for byte.  V's 1 KiB rows of
+      // the two blocks alternate, so a lane's chunk of V_a and of V_b are 1 KiB
+      // apart.  Pairs past the chunk reload its last pair (their slots are
+      // never read), so every wave issues the same count and the waits below
+      // are exact.  An entry outside the pool loads block 0 (in bounds); the
+      // pair's compute marks the result bad.
+      // This wave's tile of pair p (pairs past the chunk: its last pair again,
+      // so every wave issues the same count) and its place in slot p % NS.
+      auto tile_blk = [&](int p) { return min(2 * min(p, npairs - 1) + (wave & 1), n - 1); };
+      auto tile_dst = [&](int p) { return s_ring + (p % NS) * SB + (wave < 2 ? wave * TB : 2 * TB); };
+      const uint8_t* kvb = wave < 2 ? kbase : vbase;
+      // Lane l copies the 16 bytes the operand reads of lane l need: a K row
+      // holds them in lane order already; in a V row lane (c, j)'s chunk sits
+      // at (4 c + j) * 16 (read there in lane order, a 16-byte read at a 64-byte
+      // stride would hit each LDS bank four times).
+      const int src_off = (wave < 2 ? lane : 4 * c + j) * 16;
+      const int row0 = wave < 2 ? 0 : (wave & 1);   // K tiles: rows 0, 1, ..; V tiles interleaved
+      const int row_step = wave < 2 ? 1 : 2;
+#pragma unroll
+      for (int p = 0; p < NS - 1; ++p) {
+        const int phys = __builtin_amdgcn_readfirstlane(s_tab[tile_blk(p)]);
+        const uint8_t* src = kvb + ((size_t)(phys >= 0 && phys < a.num_blocks ? phys : 0) * hkv + kvh) * TB + src_off;
+        uint8_t* dst = tile_dst(p);
+#pragma unroll
+        for (int k = 0; k < LPS; ++k)
+          __builtin_amdgcn_global_load_lds(src + k * 1024,
+                                           (__attribute__((address_space(3))) void*)(dst + (row0 + row_step * k) * 1024),
+                                           16, 0, 0);
+      }
+      // The first copies are waited for here, in the compiler's view too:
+      // left in flight into the loop, they would make it wait for all copies
+      // at every step.
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      // One pair: wait for its copies, take the operands from its slot, send
+      // the copy of pair p + NS - 1 into the slot of pair p - 1, compute.
+      // Every wave runs npairs steps (one barrier each), first the pairs all
+      // its columns see whole, then the rest: two loops rather than a branch
+      // per step, which would hold both bodies' registers at once.
+      auto step = [&](int p, auto mode) {
+        // this wave's copies of pair p have landed; after the barrier so have
+        // everyone's, and every wave has finished pair p - 1, whose slot the
+        // next copy overwrites (s_waitcnt through the builtin, so that the
+        // compiler's own wait counting knows what is still in flight)
+        static_assert(LPS * (NS - 2) < 16, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 2)));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const int i = 2 * p;
+        const bool has_b = i + 1 < n;
+        Pair P;
+        ring_io<TB, LPS, KW / 4, VQ>(s_tab, s_ring + (p % NS) * SB, tile_dst(p + NS - 1), i, has_b,
+                                     tile_blk(p + NS - 1), kvb, hkv, kvh, a.num_blocks, row0, row_step, c, j, lane, src_off,
+                                     P.ka, P.kb, P.va, P.vb, P.oka, P.okb);
+        if (!has_b) clear_b(P);
+        f32x4 sacc[NB][CS];
+        f32x4 kscale[NB] = {};
+        qk_step(P, sacc, kscale, i, has_b, false);
+        softmax_pv(P, sacc, kscale, i, has_b, mode);
+      };
+      // pairs p with both blocks below the wave's causal limits: (c0 + 2p + 2) * 16 <= all_visible
+      const int p_full = min(npairs, max(0, (all_visible / kBlockSize - c0) / 2));
+      int p = 0;
+#pragma unroll 1
+      for (; p < p_full; ++p) step(p, kFull);
+#pragma unroll 1
+      for (; p < npairs; ++p) step(p, kAny);
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies too
+      __syncthreads();                 // s_tab and the ring are rewritten by the next chunk
+    }
+  } else {
   for (; c0 < n_blocks; c0 += kPfTab) {
     const int n = min(kPfTab, n_blocks - c0);
     // 512 entries per memory latency: every lane issues 8 entry loads before
@@ -447,26 +652,73 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // Pairs of blocks in two buffers: the next pair's K loads are issued as
-    // soon as the QK MFMAs have consumed K, its V loads once PV has consumed V.
-    Regs r0, r1;
+    // One pair of blocks in flight: the next pair's K loads are issued as soon
+    // as the QK MFMAs have consumed K, its V loads once PV has consumed V.
+    Pair P;
+    f32x4 sacc[NB][CS];
+    f32x4 kscale[NB] = {};
     int i = 0;
-    if (n > 0) load(r0, 0);
-    if (n > 1) load(r1, 1);
-    for (; i + 3 < n; i += 2) {   // steady state: the next pair exists, loads unconditional
-      compute(r0, r1, i, true, true);
-      load_v(r0, i + 2);
-      load_v(r1, i + 3);
+    if (n > 0) {
+      load_k(P, kA, 0);
+      load_v(P, kA, 0);
     }
-    const int rem = n - i;        // 0..3 blocks left; r0, r1 hold blocks i, i + 1 where they exist
-    if (rem >= 2) compute(r0, r1, i, true, false);
+    if (n > 1) {
+      load_k(P, kB, 1);
+      load_v(P, kB, 1);
+    }
+    // Steady state: the next pair exists, so loads are unconditional, and the
+    // step's blocks end at least 32 keys before the wave's last block: inside
+    // the context.  First the pairs below every column's causal limit, then
+    // (at most a few) pairs that cross some column's limit.
+    // The pairs every column sees whole are software-pipelined: the next
+    // pair's QK MFMAs are issued before this pair's softmax, so the matrix
+    // pipe has independent work while the VALU computes the exponentials.
+    if (i + 3 < n && (c0 + i + 2) * kBlockSize <= all_visible) {
+      qk_step(P, sacc, kscale, i, true, true);            // QK of pair i; K of pair i + 2 requested
+#pragma unroll 1
+      for (; i + 5 < n && (c0 + i + 4) * kBlockSize <= all_visible; i += 2) {
+        f32x4 s_next[NB][CS];
+        f32x4 k_next[NB] = {};
+        qk_step(P, s_next, k_next, i + 2, true, true);    // QK of pair i + 2; K of pair i + 4 requested
+        softmax_pv(P, sacc, kscale, i, true, kFull);      // pair i with its V
+        load_v(P, kA, i + 2);
+        load_v(P, kB, i + 3);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          kscale[b] = k_next[b];
+#pragma unroll
+          for (int cs = 0; cs < CS; ++cs) sacc[b][cs] = s_next[b][cs];
+        }
+      }
+      softmax_pv(P, sacc, kscale, i, true, kFull);
+      load_v(P, kA, i + 2);
+      load_v(P, kB, i + 3);
+      i += 2;
+    }
+#pragma unroll 1
+    for (; i + 3 < n; i += 2) {
+      qk_step(P, sacc, kscale, i, true, true);
+      softmax_pv(P, sacc, kscale, i, true, kCausal);
+      load_v(P, kA, i + 2);
+      load_v(P, kB, i + 3);
+    }
+    const int rem = n - i;        // 0..3 blocks left; P holds blocks i, i + 1 where they exist
+    if (rem >= 2) {
+      qk_step(P, sacc, kscale, i, true, false);
+      softmax_pv(P, sacc, kscale, i, true, kAny);
+    }
     if (rem % 2) {                // one block left over: paired with an absent one
-      Regs rz;
-      clear(rz);
-      if (rem == 3) load(r0, i + 2);
-      compute(r0, rz, rem == 3 ? i + 2 : i, false, false);
+      if (rem == 3) {
+        load_k(P, kA, i + 2);
+        load_v(P, kA, i + 2);
+      }
+      clear_b(P);
+      const int il = rem == 3 ? i + 2 : i;
+      qk_step(P, sacc, kscale, il, false, false);
+      softmax_pv(P, sacc, kscale, il, false, kAny);
     }
     __builtin_amdgcn_wave_barrier();   // the next chunk rewrites this wave's s_tab
+  }
   }
 
 #pragma unroll
@@ -474,7 +726,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     float l = row_sum4(l_run[cs]);
     if (bad) l = __builtin_nanf("");
     const float vbias = BIAS ? kInt8Bias * row_sum4(p_run[cs]) : 0.f;   // biased V operands
-    if (!col_ok[cs]) continue;
+    if (!wave_live || !col_ok[cs]) continue;
     const size_t orow = ((size_t)(q0 + tok[cs]) * hq + head) * D;
     const float inv = 1.f / l;
 #pragma unroll

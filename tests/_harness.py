@@ -36,6 +36,20 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+def max_err(got, ref) -> float:
+    """Largest |got - ref|, with NaN anywhere counted as infinite: Python's max() skips a NaN
+    (every comparison with it is false), so a running max over NaN errors would pass silently."""
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    return float("inf") if np.isnan(d).any() else (float(d.max()) if d.size else 0.0)
+
+
+def max_rel_err(got, ref) -> float:
+    """Largest |got - ref| / ref (ref > 0), NaN counted as infinite."""
+    ref = np.asarray(ref, dtype=np.float64)
+    d = np.abs(np.asarray(got, dtype=np.float64) - ref) / ref
+    return float("inf") if np.isnan(d).any() else (float(d.max()) if d.size else 0.0)
+
+
 def stored_values(kv_dtype, rows, channel=None):
     """float64 values a pool of kv_dtype holds for source rows [n][Hkv][D] (the oracle's own codec);
     channel: the static [Hkv][D] scales of a per-channel format."""

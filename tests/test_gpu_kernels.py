@@ -35,7 +35,7 @@ def _max_err(case, out, **kw):
     err = 0.0
     for s in range(case.lay.lens.shape[0]):
         ref, _ = case.oracle(s, **kw)
-        err = max(err, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
+        err = max(err, H.max_err(H.to_f64(out[s]), ref))
     return err
 
 
@@ -193,7 +193,7 @@ def test_int8_queries_far_outside_f16_range(kv, qd, factor):
     case = H.Case(w)
     q = (case.q.float() * factor).to(case.q.dtype).contiguous()
     out = case.attend(q=q)
-    err = max(float(np.max(np.abs(H.to_f64(out[s]) - case.oracle(s, q=q)[0]))) for s in range(3))
+    err = max(H.max_err(H.to_f64(out[s]), case.oracle(s, q=q)[0]) for s in range(3))
     print(f"{kv} q x {factor}: max abs err {err:.3e}")
     assert err <= TOL[kv]
 
@@ -591,7 +591,7 @@ def test_eviction_end_to_end_mass_select_compact_attend():
         rows = torch.from_numpy(H.logical_rows(lay, s, ref_keeps[s])).to(case.ksrc.device)
         kr, vr = H.to_f64(case.ksrc.index_select(0, rows)), H.to_f64(case.vsrc.index_select(0, rows))
         ref, _ = attention.decode_attention(H.to_f64(q[s]), kr, vr, 1 / math.sqrt(w.head_dim))
-        worst = max(worst, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
+        worst = max(worst, H.max_err(H.to_f64(out[s]), ref))
     print(f"eviction end to end: kept {cnt_h.tolist()}, max abs err {worst:.3e}")
     assert worst <= 2e-3
 
@@ -687,7 +687,7 @@ def test_append_attn_equals_append_then_attend(kv, src, q, d, hq, hkv, sinks, wi
     if mass:
         assert torch.equal(mass_a[valid], mass_b[valid])
         assert torch.equal(mass_b[10:12], torch.zeros_like(mass_b[10:12]))
-    err = max(float(np.max(np.abs(H.to_f64(out_b[s]) - b.oracle(s)[0]))) for s in valid)
+    err = max(H.max_err(H.to_f64(out_b[s]), b.oracle(s)[0]) for s in valid)
     print(f"append+attend {kv}<-{src}/{q} D={d} G={hq // hkv} sinks={sinks} window={window}: max abs err {err:.3e}")
     assert err <= TOL[kv]
     if kv not in CODE8:   # sequence 10's token was stored, not skipped by both paths
@@ -716,7 +716,7 @@ def test_append_attn_repeated_step_is_idempotent(kv, d, hq, hkv):
     for x, y in zip(pools1, c.pools):
         if x is not None:
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
-    err = max(float(np.max(np.abs(H.to_f64(out2[s]) - c.oracle(s)[0]))) for s in range(11))
+    err = max(H.max_err(H.to_f64(out2[s]), c.oracle(s)[0]) for s in range(11))
     assert err <= TOL[kv]
 
 
@@ -732,13 +732,14 @@ def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):
     return w, case, qt, qs
 
 
-def _prefill_oracle(w, case, qt, qs, s):
+def _prefill_oracle(w, case, qt, qs, s, scale=None):
     L = int(case.lay.lens[s])
     kr, vr = H.kept_source(w, case.lay, s, case.ksrc, case.vsrc)
     kc, vc = H.channel_pair(w)
     kr, vr = H.stored_values(w.kv_dtype, kr, kc), H.stored_values(w.kv_dtype, vr, vc)
     a, b = int(qs[s]), int(qs[s + 1])
-    return attention.prefill_attention(H.to_f64(qt[a:b]), kr, vr, 1 / math.sqrt(w.head_dim))
+    scale = 1 / math.sqrt(w.head_dim) if scale is None else scale
+    return attention.prefill_attention(H.to_f64(qt[a:b]), kr, vr, scale)
 
 
 PREFILL_GRID = [
@@ -757,8 +758,10 @@ PREFILL_GRID = [
 
 @pytest.mark.parametrize("kv,q,d,hq,hkv", PREFILL_GRID)
 def test_prefill_matches_oracle(kv, q, d, hq, hkv):
-    lens = (70, 300, 17, 129, 1)
-    n_qs = (70, 37, 1, 64, 1)          # whole prompt, chunk after a prefix, single token, ragged tails
+    # whole prompt, chunk after a prefix, single token, ragged tails, and a chunk after a longer
+    # prefix (many block pairs every column sees whole, then pairs across the causal limits)
+    lens = (70, 300, 17, 129, 1, 1000)
+    n_qs = (70, 37, 1, 64, 1, 150)
     w, case, qt, qs = _prefill_case(kv, q, d, hq, hkv, 101, lens, n_qs)
     out = torch.full(qt.shape, float("nan"), dtype=torch.float32, device="cuda")
     k, v, ks, vs = case.pools
@@ -768,9 +771,29 @@ def test_prefill_matches_oracle(kv, q, d, hq, hkv):
     for s in range(len(lens)):
         ref = _prefill_oracle(w, case, qt, qs, s)
         a, b = int(qs[s]), int(qs[s + 1])
-        worst = max(worst, float(np.max(np.abs(H.to_f64(out[a:b]) - ref))))
+        worst = max(worst, H.max_err(H.to_f64(out[a:b]), ref))
     print(f"prefill {kv}/{q} d{d} {hq}/{hkv}: max abs err {worst:.3e}")
     assert worst <= TOL[kv]
+
+
+@pytest.mark.parametrize("kv,q,d,hq,hkv", [("bf16", "bf16", 128, 32, 8), ("fp8", "bf16", 128, 32, 8),
+                                           ("int8_ch", "f16", 64, 16, 2), ("f32", "f32", 64, 8, 2)])
+def test_prefill_scale_sign_and_zero(kv, q, d, hq, hkv):
+    """The logit factor's sign is folded into the query operands (the largest logit is then the
+    largest raw product): negative and zero scales give the oracle's result."""
+    lens, n_qs = (300, 90, 1000), (37, 90, 100)
+    w, case, qt, qs = _prefill_case(kv, q, d, hq, hkv, 104, lens, n_qs)
+    k, v, ks, vs = case.pools
+    for sc in (-0.07, 0.0, 0.2):
+        out = torch.full(qt.shape, float("nan"), dtype=torch.float32, device="cuda")
+        ops.paged_prefill_attn(out, qt, k, v, case.tables, case.lens, qs, case.lay.max_len, max(n_qs),
+                               scale=sc, k_scale=ks, v_scale=vs)
+        worst = 0.0
+        for s in range(len(lens)):
+            ref = _prefill_oracle(w, case, qt, qs, s, scale=sc)
+            a, b = int(qs[s]), int(qs[s + 1])
+            worst = max(worst, H.max_err(H.to_f64(out[a:b]), ref))
+        assert worst <= TOL[kv], (sc, worst)
 
 
 def test_prefill_last_row_equals_decode():
@@ -847,7 +870,7 @@ def test_prefix_cache_hit_prefills_only_the_suffix():
     kb, vb = f64(torch.cat([rows["p"][0], rows["b"][0]])), f64(torch.cat([rows["p"][1], rows["b"][1]]))
     ref_a = attention.prefill_attention(H.to_f64(q[0:1]), ka, va, 1 / math.sqrt(d))
     ref_b = attention.prefill_attention(H.to_f64(q[1:301]), kb, vb, 1 / math.sqrt(d))
-    err = max(float(np.max(np.abs(H.to_f64(out[0:1]) - ref_a))), float(np.max(np.abs(H.to_f64(out[1:301]) - ref_b))))
+    err = max(H.max_err(H.to_f64(out[0:1]), ref_a), H.max_err(H.to_f64(out[1:301]), ref_b))
     print(f"prefix cache: b reused {cached_b} tokens, max abs err {err:.3e}")
     assert err <= 2e-3
 

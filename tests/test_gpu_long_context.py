@@ -46,10 +46,10 @@ def _check_out_and_mass(case, out, scores, seqs, tol):
     worst_out, worst_mass = 0.0, 0.0
     for s in seqs:
         ref, probs = case.oracle(s)
-        worst_out = max(worst_out, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
+        worst_out = max(worst_out, H.max_err(H.to_f64(out[s]), ref))
         mass = attention.head_mean_mass(probs)
         L = mass.size
-        worst_mass = max(worst_mass, float(np.max(np.abs(got[s, :L] - mass) / mass)))
+        worst_mass = max(worst_mass, H.max_rel_err(got[s, :L], mass))
         assert np.all(got[s, L:] == 0), s
     print(f"{case.w.name}: out err {worst_out:.3e}, mass rel err {worst_mass:.3e}")
     assert worst_out <= tol
@@ -95,7 +95,7 @@ def test_six_131072_token_fp8_sequences_sampled_heads():
             v = H.stored_values(w.kv_dtype, vr[:, g:g + 1, :])
             heads = slice(g * group, (g + 1) * group)
             ref, _ = attention.decode_attention(q_s[heads], k, v, scale)
-            worst = max(worst, float(np.max(np.abs(H.to_f64(out[s, heads]) - ref))))
+            worst = max(worst, H.max_err(H.to_f64(out[s, heads]), ref))
         del kr, vr
     print(f"fp8 6 x 131072: 12 (sequence, KV head) pairs, max abs err {worst:.3e}")
     assert worst <= 1e-2
@@ -177,9 +177,9 @@ def test_h2o_four_steps_full_size_accumulation_and_selection():
         acc = np.zeros(L)
         for t in range(steps):
             ref, probs = attention.decode_attention(H.to_f64(qs[t][s]), kr, vr, scale)
-            worst_out = max(worst_out, float(np.max(np.abs(H.to_f64(outs[t][s]) - ref))))
+            worst_out = max(worst_out, H.max_err(H.to_f64(outs[t][s]), ref))
             acc = policies.h2o_accumulate(acc, attention.head_mean_mass(probs))
-        worst_mass = max(worst_mass, float(np.max(np.abs(got[s].astype(np.float64) - acc) / acc)))
+        worst_mass = max(worst_mass, H.max_rel_err(got[s], acc))
         # identical scores: bit-exact
         direct = policies.h2o_select(got[s], L, w.budget, w.recent)
         assert int(keep_cnt[s]) == w.budget == direct.size

@@ -27,7 +27,7 @@ def _check(case, seqs, tol, **kw):
     worst = 0.0
     for s in seqs:
         ref, _ = case.oracle(s)
-        worst = max(worst, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
+        worst = max(worst, H.max_err(H.to_f64(out[s]), ref))
     print(f"{case.w.name}: {len(seqs)} sequences checked, max abs err {worst:.3e}")
     assert worst <= tol
     return out
@@ -78,9 +78,9 @@ def test_h2o_mass_and_keep_set_contract():
     worst_out, worst_mass, flips = 0.0, 0.0, 0
     for s in range(w.num_seqs):
         ref, probs = case.oracle(s)
-        worst_out = max(worst_out, float(np.max(np.abs(H.to_f64(out[s]) - ref))))
+        worst_out = max(worst_out, H.max_err(H.to_f64(out[s]), ref))
         mass = probs.mean(axis=0)
-        worst_mass = max(worst_mass, float(np.max(np.abs(got_scores[s] - mass) / mass)))
+        worst_mass = max(worst_mass, H.max_rel_err(got_scores[s], mass))
         ref_keep = policies.h2o_select(mass, L, w.budget, w.recent)
         assert int(keep_cnt[s]) == w.budget
         diff = np.setxor1d(ref_keep, keep_idx[s])
@@ -126,7 +126,7 @@ def test_llama2_stack_80_layers_sampled():
         for s in range(w.num_seqs):
             kr, vr = H.kept_source(w, lay, s, ksrc, vsrc)
             ref, _ = H.oracle_seq(w, lay, s, H.to_f64(q[s]), kr, vr)
-            worst = max(worst, float(np.max(np.abs(H.to_f64(outs[layer][s]) - ref))))
+            worst = max(worst, H.max_err(H.to_f64(outs[layer][s]), ref))
         del ksrc, vsrc
     print(f"llama2: 8 layers x 8 sequences, max abs err {worst:.3e}")
     assert worst <= 2e-3
@@ -174,7 +174,7 @@ def test_prefill_chunk_full_size_sampled_rows():
             # fp32 result within 2e-3, then one bf16 rounding on store: half an ulp of 8 significant
             # bits, at most 2^-8 of the value
             assert np.all(np.abs(got - ref) <= 2e-3 + np.abs(ref) * 2.0 ** -8), (s, i)
-            worst = max(worst, float(np.max(np.abs(got - ref))))
+            worst = max(worst, H.max_err(got, ref))
     print(f"prefill 4x2048 after 6144: {w.num_seqs} x {len(rows)} rows checked, max abs err {worst:.3e}")
 
 

@@ -47,7 +47,7 @@ def test_noalloc_equals_workspace_call_two_calls_second_smaller():
     worst = 0.0
     for s in (0, 21, 42, 63):
         ref, _ = big.oracle(s)
-        worst = max(worst, float(np.max(np.abs(H.to_f64(a[s]) - ref))))
+        worst = max(worst, H.max_err(H.to_f64(a[s]), ref))
     assert worst <= 2e-3
     # call 2: fewer, shorter sequences, with the H2O mass (a different layout of the array)
     small = dataclasses.replace(W.WORKLOADS["llama3"], name="noalloc-small", num_seqs=5, len_range=(20, 3000),
