@@ -196,7 +196,9 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
  *                  for every kept position, += the H2O mass of this step
  *                  ([LC] H2OEviction.update_scores): the attention probability
  *                  averaged over all num_q_heads heads.  Other entries are untouched.
- *   workspace      >= paged_decode_attn_workspace_size(...) bytes, 256-byte aligned
+ *   workspace      >= paged_decode_attn_workspace_size(...) bytes, 256-byte aligned; any
+ *                  contents (never zeroed by the caller); calls sharing one workspace
+ *                  must not overlap in time
  * num_seqs * (blocks one sequence of max_context_len attends) must stay <= 2^30
  * (PKV_EUNSUPPORTED otherwise).
  * Out-of-range device values never make the kernels touch memory outside the

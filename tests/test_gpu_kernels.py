@@ -720,6 +720,49 @@ def test_append_attn_repeated_step_is_idempotent(kv, d, hq, hkv):
     assert err <= TOL[kv]
 
 
+@pytest.mark.parametrize("lens", [(35, 70, 300, 1000, 17, 129, 64, 2000, 900, 33, 4096, 250),   # one wave per head merge
+                                  (700, 1500, 3000)])                                          # four-wave merge
+def test_decode_graph_replays_equal_eager(lens):
+    """Both decode entry points captured in a HIP graph replay to the eager result bit for bit, with
+    eager calls on other queries (same workspace) and synchronisations between the replays: nothing
+    a call leaves in the workspace changes a later call, and no captured node depends on a value the
+    host computed at capture time from device state."""
+    w = _case_workload("bf16", "bf16", 128, 32, 8, seed=9100, lens=lens)
+    case = H.Case(w)
+    k, v, ks, vs = case.pools
+    b, hq, d = case.q.shape
+    L = case.lay.max_len
+    ws = ops.alloc_workspace(b, hq, d, L, 0, 0, False, case.q.device)
+    q2 = case.q.flip(0).contiguous()
+
+    def call(out, q, noalloc):
+        if noalloc:
+            ops.paged_decode_attn_noalloc(out, q, k, v, case.tables, case.lens, L, k_scale=ks, v_scale=vs)
+        else:
+            ops.paged_decode_attn(out, q, k, v, case.tables, case.lens, L, k_scale=ks, v_scale=vs, workspace=ws)
+
+    for noalloc in (False, True):
+        ref, ref2 = torch.empty_like(case.q, dtype=torch.float32), torch.empty_like(case.q, dtype=torch.float32)
+        call(ref, case.q, noalloc)
+        call(ref2, q2, noalloc)
+        torch.cuda.synchronize()
+        out = torch.empty_like(ref)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(out, case.q, noalloc)
+        for _ in range(3):
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), noalloc
+            o2 = torch.full_like(ref, float("nan"))
+            call(o2, q2, noalloc)
+            torch.cuda.synchronize()
+            assert torch.equal(o2, ref2), noalloc
+    err = max(H.max_err(H.to_f64(ref[s]), case.oracle(s)[0]) for s in range(b))
+    assert err <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------- multi-query (chunked prefill)
 
 def _prefill_case(kv, q, d, hq, hkv, seed, lens, n_qs):

@@ -8,7 +8,8 @@
   rescales its running state between them before the LDS combine.
 * Nine sequences, one of 65536 tokens among eight of 512: more than 8 sequences,
   so a head is merged by one wave, and the long one's 100+ segments take that
-  wave through many chunks.
+  wave through many chunks (with the mass, and without it through the plain
+  merge kernel).
 * Six 131072-token sequences with FP8 KV (page "系统优化" section 5: about 8 GB of
   FP8 KV per 128K request, six requests per GPU), the decode step as the
   benchmark launches it.
@@ -74,6 +75,18 @@ def test_nine_sequences_one_65536_long_with_mass():
     scores = torch.zeros((9, 65536 + 7), dtype=torch.float32, device="cuda")
     out = case.decode_step(attn_mass=scores)
     _check_out_and_mass(case, out, scores, range(9), 2e-3)
+
+
+def test_nine_sequences_one_65536_long_without_mass():
+    """More than 8 sequences and no mass: the plain merge kernel (one wave per query head) over the
+    long sequence's 100+ segments, many chunks of 16 with a running rescale between them."""
+    lens = (512,) * 4 + (65536,) + (512,) * 4
+    w = dataclasses.replace(W.WORKLOADS["llama3"], name="nine_one_long", num_seqs=9, lens=lens, seed=2844)
+    case = H.Case(w, hold_last=True)
+    out = case.decode_step()
+    worst = max(H.max_err(H.to_f64(out[s]), case.oracle(s)[0]) for s in range(9))
+    print(f"nine sequences, one 65536 long, no mass: max abs err {worst:.3e}")
+    assert worst <= 2e-3
 
 
 def test_six_131072_token_fp8_sequences_sampled_heads():
