@@ -37,7 +37,7 @@ _COMMON = ("device_common.hpp", "geometry.hpp", "launch.hpp", "../build.py")
 OP_SOURCES = {
     "decode": ("decode_attn.hip", "mfma_ops.hpp", "kv_codec.hpp", "fp8_e4m3.hpp"),
     "prefill": ("prefill_attn.hip", "mfma_ops.hpp"),
-    "evict": ("keep_select.hip", "kv_compact.hip"),
+    "evict": ("keep_select.hip", "kv_compact.hip", "decode_attn.hip", "mfma_ops.hpp", "kv_codec.hpp", "fp8_e4m3.hpp"),
     "fill": ("kv_write.hip", "kv_codec.hpp", "fp8_e4m3.hpp"),
     "swap": ("kv_swap.hip",),
 }
@@ -152,7 +152,9 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
     """Eviction step on the h2o workload: kv_keep_select (H2OEviction.select: budget 2048, recent 512)
     then kv_compact of every sequence's kept tokens into fresh blocks.  The scores come from one
     untimed decode step with the H2O mass.  Bytes: compaction reads and writes each kept token's K and
-    V (all KV heads); the select reads the score rows and writes the keep lists."""
+    V (all KV heads); the select reads the score rows and writes the keep lists.  Also timed: the next
+    decode step applying the same keep-set itself (paged_decode_attn_compact) against a plain decode
+    step over the same cache; their difference is the eviction's cost when fused."""
     import dataclasses
 
     import numpy as np
@@ -201,6 +203,29 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
     torch.cuda.synchronize()
     sel_ms = [ev[0].elapsed_time(ev[1]) for ev in evs]
     cmp_ms = [ev[1].elapsed_time(ev[2]) for ev in evs]
+
+    # The same keep-set applied by the next decode step instead (paged_decode_attn_compact: attention
+    # over the kept tokens, which it also stores into the destination blocks), against a plain decode
+    # step over the same cache (paged_decode_attn, no mass): the difference is what eviction adds.
+    plain = ops.paged_decode_attn(out, q, k, v, tables, lens, L, workspace=ops.alloc_workspace(
+        w.num_seqs, w.num_q_heads, w.head_dim, L, device=dev), stream=stream, prepare=True)
+    fused = ops.paged_decode_attn_compact(out, q, k, v, tables, lens, L, keep_idx, keep_count, dst, stream=stream,
+                                          prepare=True)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        plain()
+        fused()
+    torch.cuda.synchronize()
+    ops.probe_read(torch.empty(1 << 30, dtype=torch.uint8, device=dev), torch.zeros(1024, device=dev))
+    for ev in pev:
+        ev[0].record(stream)
+        plain()
+        ev[1].record(stream)
+        fused()
+        ev[2].record(stream)
+    torch.cuda.synchronize()
+    t_plain = float(np.median([ev[0].elapsed_time(ev[1]) for ev in pev]))
+    t_fused = float(np.median([ev[1].elapsed_time(ev[2]) for ev in pev]))
     kept = int(keep_count.sum().item())
     tok_bytes = kv_bytes_per_token(w)
     moved = 2 * kept * tok_bytes                          # read + write of every kept token
@@ -218,6 +243,8 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "keep_select_us": round(1e3 * t_sel, 2), "keep_select_bytes": sel_bytes,
         "compact_us": round(1e3 * t_cmp, 2), "compact_bytes": moved,
+        "decode_step_us": round(1e3 * t_plain, 2), "compacting_decode_step_us": round(1e3 * t_fused, 2),
+        "eviction_added_to_decode_us": round(1e3 * (t_fused - t_plain), 2),
         "probe_read_gbs": round(read_gbs, 1), "probe_copy_gbs": round(copy_gbs, 1),
         "kernel_hash": kernel_hash("evict")}), flush=True)
 

@@ -284,6 +284,61 @@ int paged_decode_append_attn(void* out, int out_dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_decode_attn_compact -- a decode step that also applies an eviction
+ * keep-set: attention over the kept tokens only, and the kept tokens moved to
+ * fresh blocks in the same pass over the cache ([SO] 4.2 evict_tokens: the
+ * cache restricted to the kept indices; [LC] H2OEviction: select the heavy
+ * hitters, then decode on the reduced cache).  A separate kv_compact has to
+ * read nearly every source tile again (a token's K row is 16-byte pieces
+ * spread over its tile and its V elements are interleaved with those of its
+ * block's other tokens); this call stores the kept tokens from the operand
+ * registers of the attention that reads those tiles anyway.
+ *
+ * For sequence s with n = keep_count[s] and L = context_lens[s]:
+ *   k_new, v_new NULL: the step attends positions keep_idx[s][0..n) of
+ *     block_tables[s] (n >= 1; n == 0 gives NaN), and the token at
+ *     keep_idx[s][i] is copied (K and V, all KV heads) to logical position i
+ *     of dst_tables[s];
+ *   k_new, v_new given ([num_seqs][num_kv_heads][head_dim] in the pool's
+ *     dtype, 16-byte aligned): position L - 1 holds the step's new token,
+ *     stored there as paged_decode_append_attn stores it; the step attends the
+ *     listed positions (all < L - 1) and the new token, which is also copied,
+ *     to logical position n.
+ *   out = sum_t softmax_t(scale * q . K[t]) * V[t] over those tokens, t in
+ *   keep order; the sequence then holds n (+1) tokens in dst_tables[s], the
+ *   same bytes kv_compact (and the append) would give, and the host releases
+ *   its source blocks.
+ *   kv_dtype     BF16 or F16 (PKV_EUNSUPPORTED otherwise); q_dtype == kv_dtype
+ *   keep_idx     int32 [num_seqs][keep_stride], strictly ascending per
+ *                sequence; keep_count int32 [num_seqs]
+ *   dst_tables   int32 [num_seqs][dst_stride], fresh blocks (no slot written
+ *                here may be a source slot of this call); entries outside
+ *                [0, num_blocks) skip the tokens that fall in them
+ *   workspace    >= paged_decode_attn_compact_workspace_size(...) bytes,
+ *                256-byte aligned
+ * Other arguments: paged_decode_attn's (no sinks, window or H2O mass).  A
+ * sequence whose count is outside [0, min(keep_stride, L - (k_new ? 1 : 0))],
+ * or whose kept tokens do not fit dst_tables[s], gets NaN outputs and no
+ * copies (the new token is still stored at L - 1).  A keep list that is not
+ * ascending gives unspecified outputs and destination contents, written only
+ * to blocks listed in dst_tables[s].  Validation of every argument happens
+ * before anything is enqueued.
+ */
+size_t paged_decode_attn_compact_workspace_size(int num_seqs, int num_q_heads, int head_dim,
+                                                int max_context_len);
+int paged_decode_attn_compact(void* out, int out_dtype,
+                              const void* q, int q_dtype,
+                              const void* k_new, const void* v_new,
+                              void* k_pool, void* v_pool, int kv_dtype,
+                              const int32_t* block_tables, int block_table_stride,
+                              const int32_t* context_lens, int max_context_len,
+                              const int32_t* keep_idx, int keep_stride, const int32_t* keep_count,
+                              const int32_t* dst_tables, int dst_stride,
+                              int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
+                              int head_dim, int block_size, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * paged_prefill_attn -- causal multi-query attention over the paged cache: the
  * chunked prefill of a long prompt ([SO] 4.5 "Chunked Prefill") or the
  * continuation of a request whose prefix came from the prefix cache ([PA]

@@ -123,8 +123,11 @@ __device__ __forceinline__ int attended_blocks(const AttnArgs& a, int L) {
 // One wave attends the GQA group of KV head kvh of sequence s over attended
 // blocks [seg_vb0, seg_vb1) and writes the normalised output (the segment is the
 // whole sequence) or a partial (running max, exp-sum, unnormalised output) in
-// slot partial_slot(seg_vb0).
-template <int KVT, int QT, int D>
+// slot partial_slot(seg_vb0).  CMP (16-bit pools, no sinks or window): the
+// keep map masks the evicted tokens out and the kept ones are stored, from the
+// operand registers, into the destination blocks (the compaction the
+// eviction policy asks for, without a second read of the cache).
+template <int KVT, int QT, int D, bool CMP>
 __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint32_t* s_new, float* s_stash, int s,
                                              int kvh, int L, int seg_vb0, int seg_vb1) {
   using KT = KvType<KVT>;
@@ -332,11 +335,13 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
       }
     }
   };
+  static_assert(!CMP || EB == 2, "compaction is built for 16-bit pools");
   struct Regs {
     uint32_t k[KW];
     uint32_t v[NT][VW];
     f32x4 ks, vs;
     bool ok;
+    int km, kd0, kd1, krank;   // CMP: keep-map entry of the block
   };
 
   int c0 = seg_vb0;     // first block of the current table chunk (s_tab[i] = entry of block c0 + i)
@@ -368,6 +373,100 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     if constexpr (is_quantised(KVT)) {
       r.ks = *reinterpret_cast<const f32x4*>(a.k_scale + tile * kBlockSize + 4 * j);
       r.vs = *reinterpret_cast<const f32x4*>(a.v_scale + tile * kBlockSize + 4 * j);
+    }
+    if constexpr (CMP) {   // attended block == logical block (no sinks or window)
+      const KeepMapEntry m = a.keep_map[(size_t)s * a.map_stride + c0 + i];
+      r.km = m.w0;
+      r.kd0 = m.dst0;
+      r.kd1 = m.dst1;
+      r.krank = m.rank;
+    }
+  };
+
+  // CMP: the kept tokens pass through LDS images of their destination tiles
+  // (the logit window's space: compacting calls take no mass), destination
+  // tile T of the sequence in image T % 2, laid out as the pool's tile, and a
+  // tile goes out in whole 16-byte chunks once this wave has written its last
+  // slot.  The segment's first and last tiles may be shared with the waves of
+  // the neighbouring segments: of those only this wave's slots are stored (K
+  // pieces of 16 bytes, V elements of 2).
+  constexpr int kTileB = kBlockSize * D * EB;
+  static_assert(!CMP || 4 * kTileB <= 4 * stash_floats(KVT), "two K and V tile images fit the logit window");
+  uint8_t* cimg = reinterpret_cast<uint8_t*>(s_stash);
+  int c_first = -1;            // rank (destination position) of the segment's first kept token
+  int c_end = 0;               // one past the last rank written
+  int c_blk[2] = {-1, -1};     // destination block of the tile in each image
+  auto compact_flush = [&](int T, int lo, int hi) {
+    if constexpr (CMP) {
+      const int blk = c_blk[T & 1];
+      if (blk < 0) return;
+      lds_wave_sync();
+      const uint8_t* img = cimg + (T & 1) * 2 * kTileB;
+      uint8_t* kt = reinterpret_cast<uint8_t*>(a.k_store) + ((size_t)blk * a.num_kv_heads + kvh) * kTileB;
+      uint8_t* vt = reinterpret_cast<uint8_t*>(a.v_store) + ((size_t)blk * a.num_kv_heads + kvh) * kTileB;
+      if (lo == 0 && hi == kBlockSize) {
+#pragma unroll
+        for (int k = 0; k < kTileB / (kWave * 16); ++k) {
+          const int off = (k * kWave + lane) * 16;
+          *reinterpret_cast<u32x4*>(kt + off) = *reinterpret_cast<const u32x4*>(img + off);
+          *reinterpret_cast<u32x4*>(vt + off) = *reinterpret_cast<const u32x4*>(img + kTileB + off);
+        }
+      } else {
+        // K piece p is slot p % 16 of chunk p / 16
+#pragma unroll
+        for (int k = 0; k < kTileB / (kWave * 16); ++k) {
+          const int p = k * kWave + lane, sl = p & 15;
+          if (sl >= lo && sl < hi)
+            *reinterpret_cast<u32x4*>(kt + p * 16) = *reinterpret_cast<const u32x4*>(img + p * 16);
+        }
+        // V element x of chunk x / 8 belongs to slot 4 (chunk % 4) + x % 4
+        const uint16_t* iv = reinterpret_cast<const uint16_t*>(img + kTileB);
+        uint16_t* dv = reinterpret_cast<uint16_t*>(vt);
+#pragma unroll 4
+        for (int k = 0; k < kTileB / (kWave * 2); ++k) {
+          const int x = k * kWave + lane, sl = (((x >> 3) & 3) << 2) | (x & 3);
+          if (sl >= lo && sl < hi) dv[x] = iv[x];
+        }
+      }
+    }
+  };
+  // Lane (c, j) holds K chunks 4w + j of token row c and the V elements of
+  // tokens 4j..4j+3 for dims 16t + c; a kept token's rank is the block's first
+  // rank plus the kept tokens before it in the block.
+  auto compact_put = [&](const Regs& r) {
+    if constexpr (CMP) {
+      const uint32_t mask = (uint32_t)r.km & 0xffffu;
+      if (mask == 0u) return;
+      const int r0 = r.krank;
+      const int t0 = r0 >> 4;
+      const int cnt = __builtin_popcount(mask);
+      if (c_first < 0) c_first = r0;
+      c_blk[t0 & 1] = r.kd0;
+      if ((r0 & 15) + cnt > kBlockSize) c_blk[(t0 + 1) & 1] = r.kd1;
+      if ((mask >> c) & 1u) {
+        const int q = r0 + __builtin_popcount(mask & ((1u << c) - 1u));
+        uint8_t* img = cimg + ((q >> 4) & 1) * 2 * kTileB;
+#pragma unroll
+        for (int w = 0; w < KW / 4; ++w)
+          *reinterpret_cast<u32x4*>(img + ((4 * w + j) * kBlockSize + (q & 15)) * 16) =
+              u32x4{r.k[4 * w], r.k[4 * w + 1], r.k[4 * w + 2], r.k[4 * w + 3]};
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = 4 * j + e;
+        if ((mask >> tok) & 1u) {
+          const int q = r0 + __builtin_popcount(mask & ((1u << tok) - 1u));
+          uint16_t* iv = reinterpret_cast<uint16_t*>(cimg + ((q >> 4) & 1) * 2 * kTileB + kTileB);
+          const int s2 = q & 15;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)   // chunk ((t / 2) 16 + c) 4 + s2 / 4, element (t % 2) 4 + s2 % 4
+            iv[(((t >> 1) * kBlockSize + c) * 4 + (s2 >> 2)) * 8 + (t & 1) * 4 + (s2 & 3)] =
+                (uint16_t)(r.v[t][e >> 1] >> (16 * (e & 1)));
+        }
+      }
+      c_end = r0 + cnt;
+      if (c_end >= (t0 + 1) * kBlockSize)   // tile t0 has its last slot
+        compact_flush(t0, t0 == (c_first >> 4) ? (c_first & 15) : 0, kBlockSize);
     }
   };
 
@@ -441,6 +540,11 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
       }
     }
 
+    if constexpr (CMP) {
+      bad |= r.km < 0;                 // poisoned sequence
+      compact_put(r);                  // (an entry outside the pool read block 0: its bytes are copied)
+    }
+
     // ---- S = K q^T: lane (c, j) receives head c's logits of tokens 4j..4j+3
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (OP32) {
@@ -474,11 +578,19 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
       x[e] = (BIAS ? sacc[e] - qbias : sacc[e]) * lscale;
       if constexpr (is_quantised(KVT)) x[e] *= r.ks[e];
     }
-    if (!full) {
+    if constexpr (CMP) {   // evicted tokens (their V zeroed with the rest below)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        valid[e] = (r.km >> (4 * j + e)) & 1;
+        x[e] = valid[e] ? x[e] : -INFINITY;
+      }
+    }
+    if (CMP || !full) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int p = blk0 + 4 * j + e;
-        valid[e] = p < L && (p < sinks || p >= keep_lo);
+        if constexpr (CMP) valid[e] = valid[e] && p < L;   // (no sinks or window)
+        else valid[e] = p < L && (p < sinks || p >= keep_lo);
         x[e] = valid[e] ? x[e] : -INFINITY;
       }
       // Slots outside the keep-set may hold anything (NaN included): zero their V.
@@ -644,6 +756,13 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
     lds_wave_sync();   // s_tab (and the logit window) are rewritten by the next chunk
   }
 
+  if constexpr (CMP) {   // the open tile: this wave's slots of it
+    if (c_first >= 0 && (c_end & 15) != 0) {
+      const int T = (c_end - 1) >> 4;
+      compact_flush(T, T == (c_first >> 4) ? (c_first & 15) : 0, c_end & 15);
+    }
+  }
+
   l_run = row_sum4(l_run);   // head c's exp-sum, in all four lanes of column c
   if (bad) l_run = __builtin_nanf("");
   if constexpr (BIAS) {      // biased V operands added kInt8Bias * sum_p P_p to every output dim
@@ -802,7 +921,7 @@ __device__ __forceinline__ int wave_scan(int v) {
 // partials that attn_reduce_kernel merges.  Cuts inside a sequence are range
 // starts, at least kPartBlocks apart, so partial slots (partial_slot) are
 // distinct.
-template <int KVT, int QT, int D>
+template <int KVT, int QT, int D, bool CMP>
 __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   __shared__ int s_tab[kTabBlocks];
   // the new token's stored K and V rows when the decode append is fused in
@@ -903,7 +1022,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     const int nva = attended_blocks(a, L);
     const int vb = (int)(u - prefix);
     const int cnt = (int)min((long long)(nva - vb), u1 - u);
-    wave_segment<KVT, QT, D>(a, s_tab, s_new, s_stash, sq, kvh, L, vb, vb + cnt);
+    wave_segment<KVT, QT, D, CMP>(a, s_tab, s_new, s_stash, sq, kvh, L, vb, vb + cnt);
     if (vb + cnt == nva) {
       end_lo = min(end_lo, sq);
       end_hi = sq;
@@ -1138,7 +1257,7 @@ namespace {
 
 // Single-wave workgroups launched: per CU, as many as fit (or the build-time
 // count), times the CU count; cached per device.
-template <int KVT, int QT, int D>
+template <int KVT, int QT, int D, bool CMP>
 int resident_waves() {
   static std::mutex mu;
   static std::map<int, int> cache;
@@ -1149,7 +1268,7 @@ int resident_waves() {
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wave_kernel<KVT, QT, D>, kWave, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_wave_kernel<KVT, QT, D, CMP>, kWave, 0) != hipSuccess)
     return 0;
   if (per_cu < 1) per_cu = 1;
   const int want = is_code8(KVT) ? PKV_ATTN_WAVES_PER_CU_FP8 : PKV_ATTN_WAVES_PER_CU;
@@ -1159,24 +1278,31 @@ int resident_waves() {
   return n;
 }
 
-template <int KVT, int QT, int D>
+template <int KVT, int QT, int D, bool CMP = false>
 hipError_t launch_partition(const AttnArgs& a, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  const int waves = resident_waves<KVT, QT, D>();
+  const int waves = resident_waves<KVT, QT, D, CMP>();
   if (waves <= 0) return hipErrorInvalidDevice;
   const int n_ranges = waves / a.num_kv_heads > 0 ? waves / a.num_kv_heads : 1;
   // With timing events the dispatch stamps them itself (start and end of this
   // kernel), so no marker packets enter the stream between launches.
   if (ev_begin && ev_end)
-    hipExtLaunchKernelGGL((attn_wave_kernel<KVT, QT, D>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st,
+    hipExtLaunchKernelGGL((attn_wave_kernel<KVT, QT, D, CMP>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st,
                           ev_begin, ev_end, 0, a);
   else
-    hipLaunchKernelGGL((attn_wave_kernel<KVT, QT, D>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st, a);
+    hipLaunchKernelGGL((attn_wave_kernel<KVT, QT, D, CMP>), dim3(n_ranges * a.num_kv_heads), dim3(kWave), 0, st, a);
   return hipGetLastError();
 }
 
 template <int KVT, int QT>
 hipError_t dispatch_d(const AttnArgs& a, int d, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
   return d == 64 ? launch_partition<KVT, QT, 64>(a, st, eb, ee) : launch_partition<KVT, QT, 128>(a, st, eb, ee);
+}
+
+// Compacting calls: 16-bit pools with queries of the pool's dtype.
+template <int KVT>
+hipError_t dispatch_compact(const AttnArgs& a, int d, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
+  return d == 64 ? launch_partition<KVT, KVT, 64, true>(a, st, eb, ee)
+                 : launch_partition<KVT, KVT, 128, true>(a, st, eb, ee);
 }
 
 template <int KVT>
@@ -1249,7 +1375,10 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
                               hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (a.num_seqs == 0) return hipSuccess;
   hipError_t err;
-  switch (kv_dtype) {
+  if (a.keep_map != nullptr) {   // validated: BF16 or F16 pool, q of the same dtype
+    err = kv_dtype == DT_BF16 ? dispatch_compact<DT_BF16>(a, head_dim, st, ev_begin, ev_end)
+                              : dispatch_compact<DT_F16>(a, head_dim, st, ev_begin, ev_end);
+  } else switch (kv_dtype) {
     case DT_F32: err = dispatch_q<DT_F32>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_F16: err = dispatch_q<DT_F16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;

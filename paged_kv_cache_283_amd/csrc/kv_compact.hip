@@ -111,6 +111,60 @@ __global__ void __launch_bounds__(256) kv_compact_kernel(uint8_t* k_pool, uint8_
   }
 }
 
+// Keep map of a compacting attention call (paged_decode_attn_compact): thread
+// (s, b) describes block b of sequence s -- which of its 16 positions the keep
+// list holds (and the appended token at L - 1 when keep_last), the destination
+// slot of its first kept token and the destination blocks they fall in.  The
+// list is strictly ascending, so the first kept token of block b is entry
+// lower_bound(16 b) and its rank is that index.  A list that is not ascending
+// gives unspecified masks and slots, still inside the listed destination
+// blocks; a count outside [0, min(keep_stride, L - keep_last)], or that with
+// the appended token exceeds the destination table, poisons the sequence.
+__global__ void __launch_bounds__(256) keep_map_kernel(const int32_t* keep_idx, int keep_stride,
+                                                       const int32_t* keep_count, const int32_t* context_lens,
+                                                       int max_context_len, const int32_t* dst_tables, int dst_stride,
+                                                       int num_blocks, int map_stride, int keep_last,
+                                                       KeepMapEntry* map) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int s = blockIdx.y;
+  if (b >= map_stride) return;
+  const int L = context_lens[s];
+  const int n = keep_count[s];
+  const int old_len = L - keep_last;             // positions the list refers to
+  KeepMapEntry e{0, -1, -1, 0};
+  const bool ok = L >= 1 && L <= max_context_len && n >= 0 && n <= keep_stride && n <= old_len &&
+                  (long long)n + keep_last <= (long long)kBlockSize * dst_stride;
+  const int p0 = b * kBlockSize;
+  if (!ok) {
+    e.w0 = (int)0x80000000u;
+  } else if (p0 < L) {
+    const int32_t* ki = keep_idx + (size_t)s * keep_stride;
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ki[mid] < p0) lo = mid + 1;
+      else hi = mid;
+    }
+    uint32_t mask = 0;
+    for (int i = lo; i < n && i < lo + kBlockSize; ++i) {
+      const int p = ki[i];
+      if (p >= p0 + kBlockSize) break;
+      if (p >= p0 && p < old_len) mask |= 1u << (p - p0);
+    }
+    if (keep_last && L - 1 < p0 + kBlockSize) mask |= 1u << (L - 1 - p0);   // the appended token, rank n
+    const int q = lo / kBlockSize;                 // destination block of the first kept token
+    int d0 = q < dst_stride ? dst_tables[(size_t)s * dst_stride + q] : -1;
+    int d1 = q + 1 < dst_stride ? dst_tables[(size_t)s * dst_stride + q + 1] : -1;
+    if (d0 < 0 || d0 >= num_blocks) d0 = -1;
+    if (d1 < 0 || d1 >= num_blocks) d1 = -1;
+    e.w0 = (int)(mask | ((uint32_t)(lo % kBlockSize) << 16));
+    e.dst0 = d0;
+    e.dst1 = d1;
+    e.rank = lo;
+  }
+  map[(size_t)s * map_stride + b] = e;
+}
+
 namespace {
 
 template <int EB>
@@ -153,6 +207,17 @@ hipError_t launch_kv_compact(void* k_pool, void* v_pool, float* k_scale, float* 
       return compact_d<2>(k_pool, v_pool, ks, vs, src_tables, src_stride, dst_tables, dst_stride, keep_idx,
                           keep_stride, keep_count, num_seqs, num_blocks, num_kv_heads, head_dim, st);
   }
+}
+
+hipError_t launch_keep_map(const int32_t* keep_idx, int keep_stride, const int32_t* keep_count,
+                           const int32_t* context_lens, int max_context_len, const int32_t* dst_tables,
+                           int dst_stride, int num_blocks, int num_seqs, int map_stride, int keep_last,
+                           KeepMapEntry* map, hipStream_t st) {
+  if (num_seqs == 0 || map_stride == 0) return hipSuccess;
+  dim3 grid((unsigned)((map_stride + 255) / 256), (unsigned)num_seqs);
+  hipLaunchKernelGGL(keep_map_kernel, grid, dim3(256), 0, st, keep_idx, keep_stride, keep_count, context_lens,
+                     max_context_len, dst_tables, dst_stride, num_blocks, map_stride, keep_last, map);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -25,6 +25,17 @@ struct StreamHdr {
   int pad[2];
 };
 
+// Per attended block of a sequence, what the compacting attention call
+// (paged_decode_attn_compact) does with its 16 tokens: bit t of w0's low 16
+// bits keeps position 16 b + t (the rest are masked out of the attention);
+// the kept tokens go, in order, to slots (w0 >> 16) & 15, +1, ... of physical
+// block dst0, continuing at slot 0 of dst1 (-1: not stored); bit 31 of w0
+// poisons the sequence (NaN output, nothing stored).  rank: the first kept
+// token's destination position.
+struct __attribute__((aligned(16))) KeepMapEntry {
+  int w0, dst0, dst1, rank;
+};
+
 struct AttnArgs {
   void* out;
   int out_dtype;
@@ -61,6 +72,10 @@ struct AttnArgs {
   void* v_store;
   float* k_scale_store; // per-token scale arrays, writable (fused append, per-token 8-bit formats)
   float* v_scale_store;
+  // Compaction fused in (16-bit pools): keep_map [B][map_stride] (see
+  // KeepMapEntry); the kept tokens are stored through k_store / v_store.
+  const KeepMapEntry* keep_map;
+  int map_stride;
 };
 
 // Causal multi-query attention over the paged cache (chunked prefill).
@@ -93,6 +108,15 @@ struct WorkspaceLayout {
 
 WorkspaceLayout attn_workspace_layout(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
                                       int num_sinks, int window, bool want_mass);
+
+// Keep map of a compacting attention call: one entry per (sequence, block of
+// max_context_len) from the sorted keep lists and the destination tables;
+// keep_last adds position context_lens[s] - 1 (the appended token) after the
+// listed ones.
+hipError_t launch_keep_map(const int32_t* keep_idx, int keep_stride, const int32_t* keep_count,
+                           const int32_t* context_lens, int max_context_len, const int32_t* dst_tables,
+                           int dst_stride, int num_blocks, int num_seqs, int map_stride, int keep_last,
+                           KeepMapEntry* map, hipStream_t stream);
 
 // Size of the fixed per-device workspace behind paged_decode_attn_noalloc.
 constexpr size_t kStaticScratchBytes = size_t(64) << 20;

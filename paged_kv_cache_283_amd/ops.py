@@ -368,6 +368,49 @@ def paged_decode_append_attn(out, q, k_new, v_new, k_pool, v_pool, block_tables,
     return p if prepare else out
 
 
+def compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len):
+    return int(_lib.load().paged_decode_attn_compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
+
+
+def paged_decode_attn_compact(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, keep_idx,
+                              keep_count, dst_tables, k_new=None, v_new=None, scale=None, workspace=None,
+                              stream=None, prepare=False):
+    """A decode step that applies an eviction keep-set in the same pass: q [B][Hq][D] attends the kept
+    positions keep_idx[s][:keep_count[s]] of each sequence (plus, with k_new/v_new [B][Hkv][D], the new
+    token stored at position context_lens[s] - 1), and those tokens move, in order, to logical positions
+    0.. of dst_tables[s] (16-bit pools, q of the pool's dtype)."""
+    b, hq, d = q.shape
+    nb, hkv = k_pool.shape[0], k_pool.shape[1]
+    if tuple(out.shape) != (b, hq, d):
+        raise ValueError("out must have q's shape")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        if tuple(k_new.shape) != (b, hkv, d) or v_new.shape != k_new.shape or k_new.dtype != k_pool.dtype \
+                or v_new.dtype != k_pool.dtype:
+            raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim] of the pool's dtype")
+    for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (keep_idx, "keep_idx"),
+                    (keep_count, "keep_count"), (dst_tables, "dst_tables")):
+        _need(t, torch.int32, name)
+    if not (context_lens.shape[0] == block_tables.shape[0] == keep_idx.shape[0] == keep_count.shape[0]
+            == dst_tables.shape[0] == b):
+        raise ValueError("one table row, length, keep list and destination row per sequence")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    made = ()
+    if workspace is None:
+        n = compact_workspace_size(b, hq, d, max_context_len)
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+        made = (workspace,)
+    args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_new), _ptr(v_new),
+            _ptr(k_pool), _ptr(v_pool), pool_code(k_pool, None, None), _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), int(max_context_len), _ptr(keep_idx), keep_idx.shape[1], _ptr(keep_count),
+            _ptr(dst_tables), dst_tables.shape[1], b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    p = _issue("paged_decode_attn_compact", args, prepare, stream, made)
+    return p if prepare else out
+
+
 def paged_prefill_attn(out, q, k_pool, v_pool, block_tables, context_lens, query_start, max_context_len,
                        max_query_len, scale=None, k_scale=None, v_scale=None, stream=None, prepare=False):
     """Causal multi-query attention: q/out [T][Hq][D]; sequence s owns rows

@@ -32,6 +32,14 @@ def v_token_rows(v_pool):
     return v_pool.permute(0, 4, 6, 1, 2, 5, 3).reshape(nb * j * e, hkv, g * y * c)
 
 
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a float tensor in the oracle's storage dtype (bf16 as its uint16 bit patterns)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 

@@ -105,6 +105,45 @@ def test_append_attn_validation(change, status):
     assert lib.pkv_last_error() != b""
 
 
+def compact_args(**kw):
+    a = dict(out=FAKE, out_dtype=0, q=FAKE, q_dtype=1, k_new=FAKE, v_new=FAKE, k_pool=FAKE, v_pool=FAKE,
+             kv_dtype=1, tables=FAKE, stride=512, lens=FAKE, max_len=8192, keep_idx=FAKE, keep_stride=2048,
+             keep_count=FAKE, dst=FAKE, dst_stride=129, b=4, nb=100, hq=32, hkv=8, d=128, bs=16, scale=0.088,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(kv_dtype=3), _lib.EUNSUPPORTED),               # FP8 pool: compaction is built for 16-bit pools
+    (dict(kv_dtype=0, q_dtype=0), _lib.EUNSUPPORTED),    # f32 pool
+    (dict(q_dtype=2), _lib.EUNSUPPORTED),                # f16 queries on a bf16 pool
+    (dict(v_new=None), _lib.EINVAL),                     # one of the new rows only
+    (dict(keep_stride=-1), _lib.EINVAL),
+    (dict(dst_stride=0), _lib.EINVAL),
+    (dict(ws_bytes=10), _lib.EWORKSPACE),
+    (dict(stride=100), _lib.EINVAL),
+    (dict(bs=8), _lib.EUNSUPPORTED),
+    (dict(keep_idx=None), _lib.EINVAL),
+    (dict(dst=None), _lib.EINVAL),
+    (dict(k_new=ctypes.c_void_p(0x100008), v_new=ctypes.c_void_p(0x100008)), _lib.EINVAL),   # not 16-byte aligned
+])
+def test_compact_attn_validation(change, status):
+    lib = _lib.load()
+    assert lib.paged_decode_attn_compact(*compact_args(**change)) == status
+    assert lib.pkv_last_error() != b""
+
+
+def test_compact_attn_zero_sequences_and_workspace_size():
+    lib = _lib.load()
+    assert lib.paged_decode_attn_compact(*compact_args(b=0, out=None, q=None, keep_idx=None, dst=None)) == _lib.OK
+    f = lib.paged_decode_attn_compact_workspace_size
+    base = lib.paged_decode_attn_workspace_size(4, 32, 128, 8192, 0, 0, 0)
+    # the attention call's workspace, then 16 bytes per (sequence, block of max_context_len)
+    assert f(4, 32, 128, 8192) == -(-base // 256) * 256 + 4 * 512 * 16
+    assert f(4, 32, 96, 8192) == 0 and f(-1, 32, 128, 8192) == 0
+
+
 def test_append_attn_zero_sequences_is_a_no_op():
     lib = _lib.load()
     assert lib.paged_decode_append_attn(*append_attn_args(b=0, out=None, q=None, k_new=None, v_new=None)) == _lib.OK

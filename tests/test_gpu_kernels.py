@@ -596,6 +596,156 @@ def test_eviction_end_to_end_mass_select_compact_attend():
     assert worst <= 2e-3
 
 
+COMPACT_LENS = (35, 70, 300, 1000, 17, 1, 129, 2000, 640, 48)
+
+
+def _compact_keeps(lens, append, seed):
+    """Keep lists (ascending positions of the old tokens) of many shapes: sparse and dense random
+    subsets, keep-all, keep-none, a policy keep-set (sinks + recent window + heavy hitters), one half."""
+    rng = np.random.default_rng(seed)
+    keeps = []
+    for s, L in enumerate(lens):
+        old = L - 1 if append else L
+        kind = s % 6
+        if kind == 0:
+            k = np.flatnonzero(rng.random(old) < 0.25)
+        elif kind == 1:
+            k = np.arange(old)
+        elif kind == 2:
+            k = np.flatnonzero(rng.random(old) < 0.08)
+        elif kind == 3:
+            k = policies.keep_select(rng.random(old), old, 4, 16, max(1, old // 5), "all") if old else np.arange(0)
+        elif kind == 4:
+            k = np.arange(0)
+        else:
+            k = np.arange(old // 2)
+        keeps.append(np.asarray(k, dtype=np.int64))
+    return keeps
+
+
+COMPACT_GRID = [
+    # kv, d, hq, hkv, append
+    ("bf16", 128, 32, 8, True),
+    ("bf16", 128, 32, 8, False),
+    ("f16", 64, 16, 2, True),
+    ("bf16", 64, 8, 8, True),      # G = 1
+    ("f16", 128, 16, 1, False),    # G = 16
+]
+
+
+@pytest.mark.parametrize("kv,d,hq,hkv,append", COMPACT_GRID)
+def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
+    """paged_decode_attn_compact: the output equals the oracle's attention over the kept tokens (and
+    the new one), and the pools end up exactly as the oracle's append (new token at L - 1) followed by
+    its compaction of the kept positions (and L - 1) into the destination blocks; a decode over the
+    destination tables afterwards matches the oracle too.  Ten sequences (more than 8: the long ones are
+    cut at range boundaries, so several waves fill one sequence's destination blocks), with one
+    length-1 sequence and keep-none lists; keep-none without a new token attends nothing (NaN)."""
+    lens = COMPACT_LENS
+    w = dataclasses.replace(_case_workload(kv, kv, d, hq, hkv, seed=4100 + d + hq, lens=lens), extra_blocks=400)
+    case = H.Case(w, hold_last=append)
+    lay = case.lay
+    n_seq = len(lens)
+    keeps = _compact_keeps(lens, append, seed=d + hq)
+    stride = max(1, max(k.size for k in keeps))
+    keep_idx = np.full((n_seq, stride), -1, np.int32)
+    for s, k in enumerate(keeps):
+        keep_idx[s, : k.size] = k
+    counts = np.array([k.size for k in keeps], np.int32)
+    free = list(lay.unused_blocks)
+    dst_w = -(-(stride + 1) // 16)
+    dst = np.full((n_seq, dst_w), -1, np.int32)
+    for s, k in enumerate(keeps):
+        for jb in range(-(-(k.size + int(append)) // 16)):
+            dst[s, jb] = free.pop()
+    k_new, v_new = case.newest_rows() if append else (None, None)
+
+    # the oracle: append (new token at L - 1), then compaction of the kept positions (+ L - 1)
+    ref = _host_pools(case.pools, kv)
+    if append:
+        paging.write_tokens(ref, kv, H.to_host(k_new), H.to_host(v_new), kv, lay.tables, list(range(n_seq)),
+                            [L - 1 for L in lens])
+    moved = [np.concatenate([k, [L - 1]]) if append else k for k, L in zip(keeps, lens)]
+    for s in range(n_seq):
+        paging.compact(ref, kv, lay.tables[s], moved[s], dst[s], lay.num_blocks)
+
+    k, v, _, _ = case.pools
+    out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dst_t = torch.from_numpy(dst).cuda()
+    ops.paged_decode_attn_compact(out, case.q, k, v, case.tables, case.lens, lay.max_len,
+                                  torch.from_numpy(keep_idx).cuda(), torch.from_numpy(counts).cuda(), dst_t,
+                                  k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    for got, exp in zip(case.pools, ref):
+        if exp is not None:
+            assert np.array_equal(got.cpu().contiguous().view(torch.uint8).numpy().reshape(-1),
+                                  exp.view(np.uint8).reshape(-1))
+    scale = 1 / math.sqrt(d)
+    worst = 0.0
+    for s in range(n_seq):
+        if moved[s].size == 0:
+            assert torch.isnan(out[s]).all(), s
+            continue
+        rows = torch.from_numpy(H.logical_rows(lay, s, moved[s])).to(case.ksrc.device)
+        kr, vr = H.to_f64(case.ksrc.index_select(0, rows)), H.to_f64(case.vsrc.index_select(0, rows))
+        ref_out, _ = attention.decode_attention(H.to_f64(case.q[s]), kr, vr, scale)
+        worst = max(worst, H.max_err(H.to_f64(out[s]), ref_out))
+        if s == 7:
+            keep_rows, keep_v = kr, vr
+    # the next step over the destination tables
+    new_lens = torch.tensor([m.size for m in moved], dtype=torch.int32).cuda()
+    q2 = W.queries(w, step=1, device="cuda")
+    out2 = torch.empty(q2.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn(out2, q2, k, v, dst_t, new_lens, 16 * dst_w)
+    ref2, _ = attention.decode_attention(H.to_f64(q2[7]), keep_rows, keep_v, scale)
+    err2 = H.max_err(H.to_f64(out2[7]), ref2)
+    print(f"compacting decode {kv} D={d} G={hq // hkv} append={append}: kept {counts.tolist()}, "
+          f"max abs err {worst:.3e}, next step {err2:.3e}")
+    assert worst <= TOL[kv] and err2 <= TOL[kv]
+
+
+def test_decode_attn_compact_poisons_bad_counts_and_skips_bad_destinations():
+    """A count past the list or past the old tokens poisons its sequence (NaN output, nothing copied;
+    the new token is still stored at L - 1); a destination entry outside the pool skips just the
+    tokens that fall in it."""
+    lens = (200, 300, 150, 90)
+    w = dataclasses.replace(_case_workload("bf16", "bf16", 128, 16, 4, seed=4242, lens=lens), extra_blocks=80)
+    case = H.Case(w, hold_last=True)
+    lay = case.lay
+    keeps = [np.arange(0, 199, 3), np.arange(0, 299, 2), np.arange(0, 149, 7), np.arange(0, 89, 5)]
+    stride = max(kk.size for kk in keeps)
+    keep_idx = np.full((4, stride), -1, np.int32)
+    for s, kk in enumerate(keeps):
+        keep_idx[s, : kk.size] = kk
+    counts = np.array([kk.size for kk in keeps], np.int32)
+    counts[1] = stride + 1            # past the list
+    counts[2] = 150                   # past the 149 old tokens
+    free = list(lay.unused_blocks)
+    dst = np.full((4, 12), -1, np.int32)
+    for s, kk in enumerate(keeps):
+        for jb in range(-(-(kk.size + 1) // 16)):
+            dst[s, jb] = free.pop()
+    dst[3, 1] = lay.num_blocks + 7    # sequence 3 (19 tokens): tokens 16..18 fall in an entry outside the pool
+    k_new, v_new = case.newest_rows()
+    ref = _host_pools(case.pools, "bf16")
+    paging.write_tokens(ref, "bf16", H.to_host(k_new), H.to_host(v_new), "bf16", lay.tables, [0, 1, 2, 3],
+                        [L - 1 for L in lens])
+    paging.compact(ref, "bf16", lay.tables[0], np.concatenate([keeps[0], [lens[0] - 1]]), dst[0], lay.num_blocks)
+    paging.compact(ref, "bf16", lay.tables[3], keeps[3][:16], dst[3, :1], lay.num_blocks)
+    k, v, _, _ = case.pools
+    out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn_compact(out, case.q, k, v, case.tables, case.lens, lay.max_len,
+                                  torch.from_numpy(keep_idx).cuda(), torch.from_numpy(counts).cuda(),
+                                  torch.from_numpy(dst).cuda(), k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+    assert torch.isfinite(out[[0, 3]]).all()
+    for got, exp in zip(case.pools, ref):
+        if exp is not None:
+            assert np.array_equal(got.cpu().contiguous().view(torch.uint8).numpy().reshape(-1),
+                                  exp.view(np.uint8).reshape(-1))
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "f32", "int8", "fp8_ch"])
 def test_append_equals_slots_then_write(kv):
     """paged_kv_append stores exactly what paged_decode_slots + paged_kv_write store, and skips the
