@@ -260,15 +260,16 @@ int paged_decode_attn_noalloc(void* out, int out_dtype,
  * as after those two calls with the same arguments, and every argument follows
  * their rules (k_new, v_new [num_seqs][num_kv_heads][head_dim] of src_dtype,
  * 16-byte aligned; the workspace is paged_decode_attn's).
- *   F32/BF16/F16 pools, and FP8 pools whose src_dtype equals q_dtype: one
- *     attention launch.  The wave that attends a sequence's last block takes
+ *   F32/BF16/F16 pools, and 8-bit pools whose src_dtype equals q_dtype (for
+ *     INT8 pools a 16-bit q_dtype): one attention launch.  The wave that attends a sequence's last block takes
  *     the new K/V row from k_new/v_new (quantised there for 8-bit pools, with
  *     the write's arithmetic) into that block's operands and stores it into
  *     the pool slot after its last segment, so attention does not wait for
  *     the store.  A sequence whose last table entry lies outside
  *     [0, num_blocks) gets NaN outputs and no store.
- *   INT8 pools, and FP8 pools with another src_dtype: the append kernel
- *     (which quantises the row) and then the attention kernel, on the stream.
+ *   INT8 pools with f32 queries, and 8-bit pools with another src_dtype: the
+ *     append kernel (which quantises the row) and then the attention kernel,
+ *     on the stream.
  * Validation of every argument happens before anything is enqueued.
  */
 int paged_decode_append_attn(void* out, int out_dtype,

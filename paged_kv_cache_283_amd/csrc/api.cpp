@@ -355,10 +355,10 @@ int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtyp
   if (!k_new || !v_new) return fail(PKV_EINVAL, "NULL array argument");
   if ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16)
     return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
-  if (!pkv::fused_append_built(kv_dtype) || (code8_kv(kv_dtype) && src_dtype != q_dtype)) {
-    // INT8 pools, and 8-bit pools fed from a dtype other than q's: the append
-    // kernel quantises the token first; the attention kernel then reads it
-    // from the pool.
+  if (!pkv::fused_append_built(kv_dtype, q_dtype) || (code8_kv(kv_dtype) && src_dtype != q_dtype)) {
+    // INT8 pools with f32 queries, and 8-bit pools fed from a dtype other than
+    // q's: the append kernel quantises the token first; the attention kernel
+    // then reads it from the pool.
     st = device_status(pkv::launch_kv_append(k_new, v_new, src_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                              block_tables, block_table_stride, context_lens, num_seqs, num_blocks,
                                              num_kv_heads, head_dim, (hipStream_t)stream),

@@ -262,11 +262,11 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   // pool will hold.  The rows are stored into their slot when the wave has
   // finished all its segments (append_stores): stores share the load counter,
   // so a store issued here would hold up the wave's next tile waits until it
-  // completes.  FP8 pools take the source in q's dtype; INT8 instances are
-  // built without this code (fused_append_built) and their pools already hold
-  // the token.
+  // completes.  8-bit pools take the source in q's dtype; INT8 instances with
+  // f32 queries are built without this code (fused_append_built) and their
+  // pools already hold the token.
   constexpr bool C8 = is_code8(KVT);
-  constexpr bool kFuse = fused_append_built(KVT);
+  constexpr bool kFuse = fused_append_built(KVT, QT);
   constexpr int SEB = C8 ? (QT == DT_F32 ? 4 : 2) : EB;   // source element bytes
   constexpr int NWS = D * SEB / 4;        // words of one source row
   constexpr int NWL = (NWS + kWave - 1) / kWave;
@@ -960,7 +960,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
     if (sq < B && nva == 0 && sq % (int)gridDim.x == (int)blockIdx.x) {
       for (int idx = 0; idx < a.num_q_heads * D; ++idx)
         store_out(a.out, (size_t)sq * a.num_q_heads * D + idx, a.out_dtype, __builtin_nanf(""));
-      if constexpr (fused_append_built(KVT)) {
+      if constexpr (fused_append_built(KVT, QT)) {
         // no wave attends this sequence; its token is still stored where the
         // decode append would store it (a length beyond max_context_len)
         const int L = a.context_lens[sq];
@@ -1035,7 +1035,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
       while (attended_blocks(a, a.context_lens[sq]) == 0) ++sq;
     }
   }
-  if constexpr (fused_append_built(KVT)) {
+  if constexpr (fused_append_built(KVT, QT)) {
     if (a.k_new != nullptr) append_stores<KVT, QT, D>(a, kvh, end_lo, end_hi);
   }
 }

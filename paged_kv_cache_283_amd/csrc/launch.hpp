@@ -10,12 +10,13 @@
 
 namespace pkv {
 
-// Pool formats whose decode append the attention kernel takes in itself
-// (paged_decode_append_attn): all but the INT8 ones, whose attention kernel
-// already sits at the register limit of two waves per SIMD and measured 16%
-// slower with the append code compiled in.
-__host__ __device__ constexpr bool fused_append_built(int kv_dtype) {
-  return kv_dtype != PKV_INT8 && kv_dtype != PKV_INT8_CHANNEL;
+// (pool format, query dtype) pairs whose decode append the attention kernel
+// takes in itself (paged_decode_append_attn): all but INT8 pools with f32
+// queries, whose attention kernel would pass 256 VGPRs with the append code
+// (one wave per SIMD instead of two); with 16-bit queries the INT8 kernel
+// holds it at 250-252 and times the same as without it.
+__host__ __device__ constexpr bool fused_append_built(int kv_dtype, int q_dtype) {
+  return !((kv_dtype == PKV_INT8 || kv_dtype == PKV_INT8_CHANNEL) && q_dtype == PKV_F32);
 }
 
 // Per-call schedule the attention kernel hands to the merge kernel (workspace).
