@@ -538,10 +538,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # The attention kernel's dispatches of the first tenth of the timed steps
-    # (at least 5) stamp HIP events (its own start and end); each stamped
+    # The attention kernel's dispatches of the first fifth of the timed steps
+    # (at least 10) stamp HIP events (its own start and end); each stamped
     # dispatch costs its step a few us, so the rest run without them.
-    n_attn = min(args.steps * layers, max(5, (args.steps * layers) // 10))
+    n_attn = min(args.steps * layers, max(10, (args.steps * layers) // 5))
     ops.timing_begin(n_attn)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
