@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import workloads as W
-from oracle import fp8, policies
+from oracle import attention, fp8, policies
 from paged_kv_cache_283_amd import ops
 
 pytestmark = pytest.mark.gpu
@@ -92,6 +92,63 @@ def test_h2o_mass_and_keep_set_contract():
             flips += diff.size // 2
     print(f"h2o: out err {worst_out:.3e}, mass rel err {worst_mass:.3e}, keep-set flips {flips}")
     assert worst_out <= 2e-3 and worst_mass <= 1e-4
+
+
+def test_h2o_compacting_step_full_size():
+    """The eviction step bench.py times at full size (32 x 8192 bf16, H2OEviction.select with budget 2048
+    and recent 512 on the GPU's own mass): paged_decode_attn_compact attends the kept tokens and stores
+    them into fresh blocks.  Every kept token of every sequence is compared in the destination pool
+    (K and V rows, all KV heads) with its source row, bit for bit; the output of 8 sequences and the
+    next decode over the destination tables are compared with the oracle on the kept rows."""
+    import dataclasses
+
+    base = W.WORKLOADS["h2o"]
+    per_seq = -(-base.budget // 16)
+    w = dataclasses.replace(base, extra_blocks=base.num_seqs * per_seq)
+    case = H.Case(w)
+    lay, L, B = case.lay, case.lay.max_len, w.num_seqs
+    k, v, ks, vs = case.pools
+    scores = torch.zeros((B, L), dtype=torch.float32, device="cuda")
+    out0 = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn(out0, case.q, k, v, case.tables, case.lens, L, attn_mass=scores)
+    keep_idx, keep_cnt = ops.keep_select(scores, case.lens, L, 0, w.recent, w.budget - w.recent, "rest")
+    free = np.asarray(lay.unused_blocks, dtype=np.int32)[: B * per_seq]
+    dst = torch.from_numpy(free.reshape(B, per_seq).copy()).cuda()
+    q1 = W.queries(w, step=1, device="cuda")
+    out = torch.full(q1.shape, float("nan"), dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn_compact(out, q1, k, v, case.tables, case.lens, L, keep_idx, keep_cnt, dst)
+    torch.cuda.synchronize()
+    kept = keep_idx.cpu().numpy()
+    cnt = keep_cnt.cpu().numpy()
+    assert np.all(cnt == w.budget)
+    # every kept token's bytes in its destination slot
+    dst_h = dst.cpu().numpy()
+    slots, rows = [], []
+    for s in range(B):
+        i = np.arange(cnt[s])
+        slots.append(dst_h[s, i // 16].astype(np.int64) * 16 + i % 16)
+        rows.append(H.logical_rows(lay, s, kept[s, : cnt[s]]))
+    slots = torch.from_numpy(np.concatenate(slots)).cuda()
+    rows = torch.from_numpy(np.concatenate(rows)).to(case.ksrc.device)
+    assert torch.equal(H.k_token_rows(k).index_select(0, slots).view(torch.int16).cpu(),
+                       case.ksrc.index_select(0, rows).contiguous().view(torch.int16).cpu())
+    assert torch.equal(H.v_token_rows(v).index_select(0, slots).view(torch.int16).cpu(),
+                       case.vsrc.index_select(0, rows).contiguous().view(torch.int16).cpu())
+    # outputs, and the next step over the destination tables
+    q2 = W.queries(w, step=2, device="cuda")
+    out2 = torch.empty(q2.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn(out2, q2, k, v, dst, keep_cnt, 16 * per_seq)
+    scale = 1 / math.sqrt(w.head_dim)
+    worst = worst2 = 0.0
+    for s in range(0, B, 4):
+        r = torch.from_numpy(H.logical_rows(lay, s, kept[s, : cnt[s]])).to(case.ksrc.device)
+        kr, vr = H.to_f64(case.ksrc.index_select(0, r)), H.to_f64(case.vsrc.index_select(0, r))
+        ref, _ = attention.decode_attention(H.to_f64(q1[s]), kr, vr, scale)
+        worst = max(worst, H.max_err(H.to_f64(out[s]), ref))
+        ref2, _ = attention.decode_attention(H.to_f64(q2[s]), kr, vr, scale)
+        worst2 = max(worst2, H.max_err(H.to_f64(out2[s]), ref2))
+    print(f"h2o compacting step: {int(cnt.sum())} tokens moved, out err {worst:.3e}, next step {worst2:.3e}")
+    assert worst <= 2e-3 and worst2 <= 2e-3
 
 
 def test_llama2_stack_80_layers_sampled():
