@@ -150,7 +150,10 @@ class BlockManager:
         """Give seq fresh blocks for a dense prefix of num_kept tokens (eviction).
 
         Returns (old_table, new_table): the caller enqueues kv_compact from
-        old_table to new_table with the keep-set.  The old blocks are not
+        old_table to new_table with the keep-set, or lets the next decode step
+        move the tokens (paged_decode_attn_compact over old_table: append the
+        step's token first, then compact to the kept count + 1; the kept tokens
+        and the new one land in new_table).  The old blocks are not
         released yet: they stay referenced until release_compacted(), so the
         fresh blocks of another sequence compacted before that call are never
         one of them, and one batched kv_compact over every sequence compacted
