@@ -35,6 +35,21 @@
 
 namespace pkv {
 
+// Maximum for the softmax's running max: IEEE maximum (a NaN logit makes the
+// max NaN, and the output is NaN either way), which gfx950 has as
+// v_maximum3_f32; fmaxf's NaN-ignoring form needs every MFMA result
+// canonicalised first (one v_max_f32 x, x per logit).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// The same over the four 16-lane rows of an MFMA accumulator (lanes 16 and 32 apart).
+__device__ __forceinline__ float row_vmax4(float x) {
+  const uint32_t u = __float_as_uint(x);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 namespace {
 
 constexpr int kPfWaves = 4;
@@ -463,10 +478,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           }
           x[b][e] = v;
         }
-        mx = fmaxf(mx, fmaxf(fmaxf(x[b][0], x[b][1]), fmaxf(x[b][2], x[b][3])));
+        mx = vmax(mx, vmax(vmax(x[b][0], x[b][1]), vmax(x[b][2], x[b][3])));
       }
       // the step's largest (scaled) logit of this column
-      const float mb = RAWMAX ? (row_max4(mx) - qbias[cs]) * sl2 : row_max4(mx);
+      const float mb = RAWMAX ? (row_vmax4(mx) - qbias[cs]) * sl2 : row_vmax4(mx);
       const bool need = mb > m_run[cs] + kPfRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
         const float m_new = need ? mb : m_run[cs];
