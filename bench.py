@@ -153,8 +153,9 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
     then kv_compact of every sequence's kept tokens into fresh blocks.  The scores come from one
     untimed decode step with the H2O mass.  Bytes: compaction reads and writes each kept token's K and
     V (all KV heads); the select reads the score rows and writes the keep lists.  Also timed: the next
-    decode step applying the same keep-set itself (paged_decode_attn_compact) against a plain decode
-    step over the same cache; their difference is the eviction's cost when fused."""
+    decode step applying the same keep-set itself (paged_decode_attn_compact, with the H2O mass)
+    against the H2O decode step over the same cache; their difference is the eviction's cost when
+    fused."""
     import dataclasses
 
     import numpy as np
@@ -205,12 +206,14 @@ def bench_evict(args, dev, stream, read_gbs, copy_gbs):
     cmp_ms = [ev[1].elapsed_time(ev[2]) for ev in evs]
 
     # The same keep-set applied by the next decode step instead (paged_decode_attn_compact: attention
-    # over the kept tokens, which it also stores into the destination blocks), against a plain decode
-    # step over the same cache (paged_decode_attn, no mass): the difference is what eviction adds.
-    plain = ops.paged_decode_attn(out, q, k, v, tables, lens, L, workspace=ops.alloc_workspace(
-        w.num_seqs, w.num_q_heads, w.head_dim, L, device=dev), stream=stream, prepare=True)
-    fused = ops.paged_decode_attn_compact(out, q, k, v, tables, lens, L, keep_idx, keep_count, dst, stream=stream,
-                                          prepare=True)
+    # over the kept tokens, which it also stores into the destination blocks, and the H2O scores of the
+    # kept tokens moved to their new positions with this step's mass added), against the H2O decode step
+    # over the same cache (paged_decode_attn with the mass): the difference is what eviction adds.
+    scores2 = torch.zeros_like(scores)
+    plain = ops.paged_decode_attn(out, q, k, v, tables, lens, L, attn_mass=scores, workspace=ops.alloc_workspace(
+        w.num_seqs, w.num_q_heads, w.head_dim, L, want_mass=True, device=dev), stream=stream, prepare=True)
+    fused = ops.paged_decode_attn_compact(out, q, k, v, tables, lens, L, keep_idx, keep_count, dst,
+                                          attn_mass_src=scores, attn_mass=scores2, stream=stream, prepare=True)
     pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for _ in range(args.warmup):
         plain()

@@ -315,9 +315,17 @@ int paged_decode_append_attn(void* out, int out_dtype,
  *   dst_tables   int32 [num_seqs][dst_stride], fresh blocks (no slot written
  *                here may be a source slot of this call); entries outside
  *                [0, num_blocks) skip the tokens that fall in them
- *   workspace    >= paged_decode_attn_compact_workspace_size(...) bytes,
- *                256-byte aligned
- * Other arguments: paged_decode_attn's (no sinks, window or H2O mass).  A
+ *   attn_mass    NULL, or the H2O score rows after the step, float
+ *                [num_seqs][attn_mass_stride] (stride >= max_context_len): entry i
+ *                (i < n, and n for the new token) becomes attn_mass_src[s][p] + this
+ *                step's mass of p ([LC] H2OEviction.update_scores over the kept
+ *                tokens), p the source position of the token moved to i; other
+ *                entries are untouched.  attn_mass_src: the score rows before the
+ *                step, float [num_seqs][attn_mass_src_stride] (stride >=
+ *                max_context_len), a different array (PKV_EINVAL otherwise).
+ *   workspace    >= paged_decode_attn_compact_workspace_size(..., attn_mass != NULL)
+ *                bytes, 256-byte aligned
+ * Other arguments: paged_decode_attn's (no sinks or window).  A
  * sequence whose count is outside [0, min(keep_stride, L - (k_new ? 1 : 0))],
  * or whose kept tokens do not fit dst_tables[s], gets NaN outputs and no
  * copies (the new token is still stored at L - 1).  A keep list that is not
@@ -326,7 +334,7 @@ int paged_decode_append_attn(void* out, int out_dtype,
  * before anything is enqueued.
  */
 size_t paged_decode_attn_compact_workspace_size(int num_seqs, int num_q_heads, int head_dim,
-                                                int max_context_len);
+                                                int max_context_len, int want_mass);
 int paged_decode_attn_compact(void* out, int out_dtype,
                               const void* q, int q_dtype,
                               const void* k_new, const void* v_new,
@@ -337,6 +345,8 @@ int paged_decode_attn_compact(void* out, int out_dtype,
                               const int32_t* dst_tables, int dst_stride,
                               int num_seqs, int num_blocks, int num_q_heads, int num_kv_heads,
                               int head_dim, int block_size, float scale,
+                              const float* attn_mass_src, int attn_mass_src_stride,
+                              float* attn_mass, int attn_mass_stride,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*

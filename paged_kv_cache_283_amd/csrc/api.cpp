@@ -174,19 +174,20 @@ size_t paged_decode_attn_workspace_size(int num_seqs, int num_q_heads, int head_
       .total;
 }
 
-// Workspace of paged_decode_attn_compact: the attention call's (no sinks,
-// window or mass), then the keep map at the next 256-byte boundary.
-static size_t compact_map_offset(int num_seqs, int num_q_heads, int head_dim, int max_context_len) {
-  return (pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, 0, 0, false).total + 255) &
-         ~(size_t)255;
+// Workspace of paged_decode_attn_compact: the attention call's (no sinks or
+// window), then the keep map at the next 256-byte boundary.
+static size_t compact_map_offset(int num_seqs, int num_q_heads, int head_dim, int max_context_len, bool want_mass) {
+  return (pkv::attn_workspace_layout(num_seqs, num_q_heads, head_dim, max_context_len, 0, 0, want_mass).total +
+          255) & ~(size_t)255;
 }
 
-size_t paged_decode_attn_compact_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_context_len) {
+size_t paged_decode_attn_compact_workspace_size(int num_seqs, int num_q_heads, int head_dim, int max_context_len,
+                                                int want_mass) {
   if (num_seqs < 0 || num_q_heads < 1 || (head_dim != 64 && head_dim != 128) || max_context_len < 1 ||
       max_context_len > (1 << 30))
     return 0;
   const size_t map_stride = ((size_t)max_context_len + 15) / 16;
-  return compact_map_offset(num_seqs, num_q_heads, head_dim, max_context_len) +
+  return compact_map_offset(num_seqs, num_q_heads, head_dim, max_context_len, want_mass != 0) +
          (size_t)num_seqs * map_stride * sizeof(pkv::KeepMapEntry);
 }
 
@@ -381,28 +382,36 @@ int paged_decode_attn_compact(void* out, int out_dtype, const void* q, int q_dty
                               int max_context_len, const int32_t* keep_idx, int keep_stride,
                               const int32_t* keep_count, const int32_t* dst_tables, int dst_stride, int num_seqs,
                               int num_blocks, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
-                              float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                              float scale, const float* attn_mass_src, int attn_mass_src_stride, float* attn_mass,
+                              int attn_mass_stride, void* workspace, size_t workspace_bytes, void* stream) {
   if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16)
     return fail(PKV_EUNSUPPORTED, "kv_dtype %d (compaction is built for BF16 and F16 pools)", kv_dtype);
   if (q_dtype != kv_dtype) return fail(PKV_EUNSUPPORTED, "q_dtype %d must be the pool's dtype %d", q_dtype, kv_dtype);
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(PKV_EINVAL, "k_new and v_new must both be given or NULL");
   if (keep_stride < 0 || keep_stride > (1 << 30)) return fail(PKV_EINVAL, "keep_stride %d outside [0, 2^30]", keep_stride);
   if (dst_stride < 1 || dst_stride > (1 << 26)) return fail(PKV_EINVAL, "dst_stride %d outside [1, 2^26]", dst_stride);
-  const size_t need = paged_decode_attn_compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len);
+  const bool mass = attn_mass != nullptr;
+  if (mass) {
+    if (!attn_mass_src) return fail(PKV_EINVAL, "attn_mass needs attn_mass_src (the source score rows)");
+    if (attn_mass_src == attn_mass) return fail(PKV_EINVAL, "attn_mass_src and attn_mass must be different arrays");
+    if (attn_mass_src_stride < max_context_len)
+      return fail(PKV_EINVAL, "attn_mass_src_stride %d < max_context_len %d", attn_mass_src_stride, max_context_len);
+  }
+  const size_t need = paged_decode_attn_compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, mass);
   if (workspace_bytes < need) return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   pkv::AttnArgs a;
   int st = prepare_decode_attn(a, out, out_dtype, q, q_dtype, k_pool, v_pool, nullptr, nullptr, kv_dtype,
                                block_tables, block_table_stride, context_lens, max_context_len, num_seqs, num_blocks,
-                               num_q_heads, num_kv_heads, head_dim, block_size, scale, 0, 0, nullptr, 0, workspace,
-                               workspace_bytes);
+                               num_q_heads, num_kv_heads, head_dim, block_size, scale, 0, 0, attn_mass,
+                               attn_mass_stride, workspace, workspace_bytes);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return ok();
   if (!keep_idx || !keep_count || !dst_tables) return fail(PKV_EINVAL, "NULL array argument");
   if (k_new && ((uintptr_t)k_new % 16 || (uintptr_t)v_new % 16))
     return fail(PKV_EINVAL, "k_new and v_new must be 16-byte aligned");
   const int map_stride = (max_context_len + 15) / 16;
-  auto* map = reinterpret_cast<pkv::KeepMapEntry*>(reinterpret_cast<char*>(workspace) +
-                                                   compact_map_offset(num_seqs, num_q_heads, head_dim, max_context_len));
+  auto* map = reinterpret_cast<pkv::KeepMapEntry*>(
+      reinterpret_cast<char*>(workspace) + compact_map_offset(num_seqs, num_q_heads, head_dim, max_context_len, mass));
   st = device_status(pkv::launch_keep_map(keep_idx, keep_stride, keep_count, context_lens, max_context_len, dst_tables,
                                           dst_stride, num_blocks, num_seqs, map_stride, k_new != nullptr ? 1 : 0, map,
                                           (hipStream_t)stream),
@@ -414,6 +423,8 @@ int paged_decode_attn_compact(void* out, int out_dtype, const void* q, int q_dty
   a.v_store = v_pool;
   a.keep_map = map;
   a.map_stride = map_stride;
+  a.mass_src = attn_mass_src;
+  a.mass_src_stride = attn_mass_src_stride;
   return launch_prepared_attn(a, kv_dtype, q_dtype, head_dim, stream, "paged_decode_attn_compact");
 }
 

@@ -384,15 +384,18 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   };
 
   // CMP: the kept tokens pass through LDS images of their destination tiles
-  // (the logit window's space: compacting calls take no mass), destination
+  // (the end of the logit window's space), destination
   // tile T of the sequence in image T % 2, laid out as the pool's tile, and a
   // tile goes out in whole 16-byte chunks once this wave has written its last
   // slot.  The segment's first and last tiles may be shared with the waves of
   // the neighbouring segments: of those only this wave's slots are stored (K
   // pieces of 16 bytes, V elements of 2).
   constexpr int kTileB = kBlockSize * D * EB;
-  static_assert(!CMP || 4 * kTileB <= 4 * stash_floats(KVT), "two K and V tile images fit the logit window");
-  uint8_t* cimg = reinterpret_cast<uint8_t*>(s_stash);
+  // the images take the window's last 4 kTileB bytes (kTileB floats); the
+  // H2O logit window keeps the rest
+  constexpr int kImgFloats = CMP ? kTileB : 0;
+  static_assert(2 * kImgFloats <= stash_floats(KVT), "two K and V tile images fit the logit window");
+  uint8_t* cimg = reinterpret_cast<uint8_t*>(s_stash + (stash_floats(KVT) - kImgFloats));
   int c_first = -1;            // rank (destination position) of the segment's first kept token
   int c_end = 0;               // one past the last rank written
   int c_blk[2] = {-1, -1};     // destination block of the tile in each image
@@ -475,7 +478,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   // coalesced 16-byte stores after each chunk: a store in every block's step
   // would make the tile waits two blocks later wait for it too (stores share
   // the load counter).
-  const int st_blocks = stash_floats(KVT) / (group * kBlockSize);
+  const int st_blocks = (stash_floats(KVT) - kImgFloats) / (group * kBlockSize);
   auto stash_flush = [&](int vb0, int nb) {
     lds_wave_sync();
     const int n4 = nb * kBlockSize / 4;       // 16-byte pieces per head
@@ -1235,7 +1238,21 @@ __device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
       for (int h = 0; h < hn; ++h) sum += fast_exp2(x[(size_t)h * a.nv_pad] - s_m[h]) / s_l[h];
     }
   }
-  if (active) a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
+  if (!active) return;
+  if (a.keep_map == nullptr) {
+    a.attn_mass[(size_t)s * a.mass_stride + p] += sum / (float)hq;
+  } else {
+    // compacting call: a kept position's score moves to its rank in the
+    // compacted row, with this step's mass added; evicted ones are dropped
+    const KeepMapEntry m = a.keep_map[(size_t)s * a.map_stride + p / kBlockSize];
+    const uint32_t mask = (uint32_t)m.w0 & 0xffffu;
+    const int t = p % kBlockSize;
+    if (m.w0 >= 0 && ((mask >> t) & 1u)) {
+      const int rank = m.rank + __builtin_popcount(mask & ((1u << t) - 1u));
+      if (rank < a.mass_stride)
+        a.attn_mass[(size_t)s * a.mass_stride + rank] = a.mass_src[(size_t)s * a.mass_src_stride + p] + sum / (float)hq;
+    }
+  }
 }
 
 // The H2O step's tail in one launch: the first rx workgroups of row s merge

@@ -75,8 +75,13 @@ struct AttnArgs {
   float* v_scale_store;
   // Compaction fused in (16-bit pools): keep_map [B][map_stride] (see
   // KeepMapEntry); the kept tokens are stored through k_store / v_store.
+  // With the H2O mass, attn_mass is the compacted score rows: entry i of
+  // sequence s (the kept token of rank i) becomes mass_src[s][p] + this
+  // step's mass of p, p its source position.
   const KeepMapEntry* keep_map;
   int map_stride;
+  const float* mass_src;
+  int mass_src_stride;
 };
 
 // Causal multi-query attention over the paged cache (chunked prefill).

@@ -368,17 +368,20 @@ def paged_decode_append_attn(out, q, k_new, v_new, k_pool, v_pool, block_tables,
     return p if prepare else out
 
 
-def compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len):
-    return int(_lib.load().paged_decode_attn_compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len))
+def compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, want_mass=False):
+    return int(_lib.load().paged_decode_attn_compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                                     int(bool(want_mass))))
 
 
 def paged_decode_attn_compact(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, keep_idx,
-                              keep_count, dst_tables, k_new=None, v_new=None, scale=None, workspace=None,
-                              stream=None, prepare=False):
+                              keep_count, dst_tables, k_new=None, v_new=None, scale=None, attn_mass_src=None,
+                              attn_mass=None, workspace=None, stream=None, prepare=False):
     """A decode step that applies an eviction keep-set in the same pass: q [B][Hq][D] attends the kept
     positions keep_idx[s][:keep_count[s]] of each sequence (plus, with k_new/v_new [B][Hkv][D], the new
     token stored at position context_lens[s] - 1), and those tokens move, in order, to logical positions
-    0.. of dst_tables[s] (16-bit pools, q of the pool's dtype)."""
+    0.. of dst_tables[s] (16-bit pools, q of the pool's dtype).  With attn_mass (float32 [B][>= max_len],
+    the compacted H2O score rows) and attn_mass_src (the rows before the step): entry i gets the moved
+    token's source score plus this step's mass."""
     b, hq, d = q.shape
     nb, hkv = k_pool.shape[0], k_pool.shape[1]
     if tuple(out.shape) != (b, hq, d):
@@ -397,15 +400,23 @@ def paged_decode_attn_compact(out, q, k_pool, v_pool, block_tables, context_lens
         raise ValueError("one table row, length, keep list and destination row per sequence")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if (attn_mass is None) != (attn_mass_src is None):
+        raise ValueError("give both attn_mass and attn_mass_src, or neither")
+    src_stride = dst_stride = 0
+    if attn_mass is not None:
+        _need(attn_mass, torch.float32, "attn_mass")
+        _need(attn_mass_src, torch.float32, "attn_mass_src")
+        src_stride, dst_stride = attn_mass_src.shape[1], attn_mass.shape[1]
     made = ()
     if workspace is None:
-        n = compact_workspace_size(b, hq, d, max_context_len)
+        n = compact_workspace_size(b, hq, d, max_context_len, attn_mass is not None)
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
         made = (workspace,)
     args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_new), _ptr(v_new),
             _ptr(k_pool), _ptr(v_pool), pool_code(k_pool, None, None), _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), int(max_context_len), _ptr(keep_idx), keep_idx.shape[1], _ptr(keep_count),
-            _ptr(dst_tables), dst_tables.shape[1], b, nb, hq, hkv, d, BLOCK_SIZE, float(scale), _ptr(workspace),
+            _ptr(dst_tables), dst_tables.shape[1], b, nb, hq, hkv, d, BLOCK_SIZE, float(scale),
+            _ptr(attn_mass_src), src_stride, _ptr(attn_mass), dst_stride, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
     p = _issue("paged_decode_attn_compact", args, prepare, stream, made)
     return p if prepare else out

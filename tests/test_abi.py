@@ -109,7 +109,7 @@ def compact_args(**kw):
     a = dict(out=FAKE, out_dtype=0, q=FAKE, q_dtype=1, k_new=FAKE, v_new=FAKE, k_pool=FAKE, v_pool=FAKE,
              kv_dtype=1, tables=FAKE, stride=512, lens=FAKE, max_len=8192, keep_idx=FAKE, keep_stride=2048,
              keep_count=FAKE, dst=FAKE, dst_stride=129, b=4, nb=100, hq=32, hkv=8, d=128, bs=16, scale=0.088,
-             ws=FAKE, ws_bytes=1 << 40, stream=None)
+             mass_src=None, mass_src_stride=0, mass=None, mass_stride=0, ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return list(a.values())
 
@@ -127,6 +127,10 @@ def compact_args(**kw):
     (dict(keep_idx=None), _lib.EINVAL),
     (dict(dst=None), _lib.EINVAL),
     (dict(k_new=ctypes.c_void_p(0x100008), v_new=ctypes.c_void_p(0x100008)), _lib.EINVAL),   # not 16-byte aligned
+    (dict(mass=FAKE, mass_stride=8192), _lib.EINVAL),                                     # no source rows
+    (dict(mass=FAKE, mass_stride=8192, mass_src=FAKE, mass_src_stride=8192), _lib.EINVAL),   # the same array
+    (dict(mass=FAKE, mass_stride=8192, mass_src=ctypes.c_void_p(0x200000), mass_src_stride=100), _lib.EINVAL),
+    (dict(mass=FAKE, mass_stride=100, mass_src=ctypes.c_void_p(0x200000), mass_src_stride=8192), _lib.EINVAL),
 ])
 def test_compact_attn_validation(change, status):
     lib = _lib.load()
@@ -138,10 +142,11 @@ def test_compact_attn_zero_sequences_and_workspace_size():
     lib = _lib.load()
     assert lib.paged_decode_attn_compact(*compact_args(b=0, out=None, q=None, keep_idx=None, dst=None)) == _lib.OK
     f = lib.paged_decode_attn_compact_workspace_size
-    base = lib.paged_decode_attn_workspace_size(4, 32, 128, 8192, 0, 0, 0)
-    # the attention call's workspace, then 16 bytes per (sequence, block of max_context_len)
-    assert f(4, 32, 128, 8192) == -(-base // 256) * 256 + 4 * 512 * 16
-    assert f(4, 32, 96, 8192) == 0 and f(-1, 32, 128, 8192) == 0
+    for mass in (0, 1):
+        base = lib.paged_decode_attn_workspace_size(4, 32, 128, 8192, 0, 0, mass)
+        # the attention call's workspace, then 16 bytes per (sequence, block of max_context_len)
+        assert f(4, 32, 128, 8192, mass) == -(-base // 256) * 256 + 4 * 512 * 16
+    assert f(4, 32, 96, 8192, 0) == 0 and f(-1, 32, 128, 8192, 0) == 0
 
 
 def test_append_attn_zero_sequences_is_a_no_op():

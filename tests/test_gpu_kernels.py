@@ -781,6 +781,63 @@ def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
     assert worst <= TOL[kv] and err2 <= TOL[kv]
 
 
+@pytest.mark.parametrize("kv,d,hq,hkv,append", [("bf16", 128, 32, 8, True), ("f16", 64, 16, 2, False)])
+def test_decode_attn_compact_with_h2o_mass(kv, d, hq, hkv, append):
+    """The compacting step with the H2O mass: entry i of the compacted score row is the moved token's
+    source score plus this step's mass of it (the oracle's head-mean probabilities over the kept tokens
+    and the new one, 1e-4 relative, plus the fp32 rounding of the sum); entries past the moved tokens
+    keep their values; output and pools as without the mass."""
+    lens = COMPACT_LENS
+    w = dataclasses.replace(_case_workload(kv, kv, d, hq, hkv, seed=4300 + d, lens=lens), extra_blocks=400)
+    case = H.Case(w, hold_last=append)
+    lay = case.lay
+    n_seq, L = len(lens), lay.max_len
+    keeps = _compact_keeps(lens, append, seed=7 + d)
+    stride = max(1, max(k.size for k in keeps))
+    keep_idx = np.full((n_seq, stride), -1, np.int32)
+    for s_, k_ in enumerate(keeps):
+        keep_idx[s_, : k_.size] = k_
+    counts = np.array([k_.size for k_ in keeps], np.int32)
+    free = list(lay.unused_blocks)
+    dst_w = -(-(stride + 1) // 16)
+    dst = np.full((n_seq, dst_w), -1, np.int32)
+    for s_, k_ in enumerate(keeps):
+        for jb in range(-(-(k_.size + int(append)) // 16)):
+            dst[s_, jb] = free.pop()
+    rng = np.random.default_rng(99)
+    src_scores = rng.random((n_seq, L)).astype(np.float32)
+    src_t = torch.from_numpy(src_scores).cuda()
+    dst_t = torch.full((n_seq, L), -7.0, dtype=torch.float32, device="cuda")
+    k_new, v_new = case.newest_rows() if append else (None, None)
+    k, v, _, _ = case.pools
+    out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
+    ops.paged_decode_attn_compact(out, case.q, k, v, case.tables, case.lens, L, torch.from_numpy(keep_idx).cuda(),
+                                  torch.from_numpy(counts).cuda(), torch.from_numpy(dst).cuda(), k_new=k_new,
+                                  v_new=v_new, attn_mass_src=src_t, attn_mass=dst_t)
+    torch.cuda.synchronize()
+    got = dst_t.cpu().numpy().astype(np.float64)
+    assert torch.equal(src_t.cpu(), torch.from_numpy(src_scores))      # the source rows are only read
+    scale = 1 / math.sqrt(d)
+    worst_out, worst_mass = 0.0, 0.0
+    for s_, Ls in enumerate(lens):
+        moved = np.concatenate([keeps[s_], [Ls - 1]]) if append else keeps[s_]
+        if moved.size == 0:
+            assert np.all(got[s_] == -7.0)
+            continue
+        rows = torch.from_numpy(H.logical_rows(lay, s_, moved)).to(case.ksrc.device)
+        kr, vr = H.to_f64(case.ksrc.index_select(0, rows)), H.to_f64(case.vsrc.index_select(0, rows))
+        ref, probs = attention.decode_attention(H.to_f64(case.q[s_]), kr, vr, scale)
+        worst_out = max(worst_out, H.max_err(H.to_f64(out[s_]), ref))
+        mass = attention.head_mean_mass(probs)
+        exp = src_scores[s_, moved].astype(np.float64) + mass
+        err = np.abs(got[s_, : moved.size] - exp)
+        bound = 1e-4 * mass + 2.0 ** -22 * np.abs(exp)
+        worst_mass = max(worst_mass, float(np.max(err / bound)))
+        assert np.all(got[s_, moved.size:] == -7.0), s_
+    print(f"compacting step with mass {kv} D={d}: out err {worst_out:.3e}, mass err / bound {worst_mass:.3f}")
+    assert worst_out <= TOL[kv] and worst_mass <= 1.0
+
+
 def test_decode_attn_compact_poisons_bad_counts_and_skips_bad_destinations():
     """A count past the list or past the old tokens poisons its sequence (NaN output, nothing copied;
     the new token is still stored at L - 1); a destination entry outside the pool skips just the

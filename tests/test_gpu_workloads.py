@@ -96,10 +96,12 @@ def test_h2o_mass_and_keep_set_contract():
 
 def test_h2o_compacting_step_full_size():
     """The eviction step bench.py times at full size (32 x 8192 bf16, H2OEviction.select with budget 2048
-    and recent 512 on the GPU's own mass): paged_decode_attn_compact attends the kept tokens and stores
-    them into fresh blocks.  Every kept token of every sequence is compared in the destination pool
-    (K and V rows, all KV heads) with its source row, bit for bit; the output of 8 sequences and the
-    next decode over the destination tables are compared with the oracle on the kept rows."""
+    and recent 512 on the GPU's own mass): paged_decode_attn_compact attends the kept tokens, stores
+    them into fresh blocks and moves their scores with this step's mass added.  Every kept token of
+    every sequence is compared in the destination pool (K and V rows, all KV heads) with its source
+    row, bit for bit; the output, the compacted scores (source score + the oracle's mass, 1e-4
+    relative) of 8 sequences and the next decode over the destination tables are compared with the
+    oracle on the kept rows."""
     import dataclasses
 
     base = W.WORKLOADS["h2o"]
@@ -116,7 +118,9 @@ def test_h2o_compacting_step_full_size():
     dst = torch.from_numpy(free.reshape(B, per_seq).copy()).cuda()
     q1 = W.queries(w, step=1, device="cuda")
     out = torch.full(q1.shape, float("nan"), dtype=torch.float32, device="cuda")
-    ops.paged_decode_attn_compact(out, q1, k, v, case.tables, case.lens, L, keep_idx, keep_cnt, dst)
+    scores_dst = torch.full_like(scores, -7.0)
+    ops.paged_decode_attn_compact(out, q1, k, v, case.tables, case.lens, L, keep_idx, keep_cnt, dst,
+                                  attn_mass_src=scores, attn_mass=scores_dst)
     torch.cuda.synchronize()
     kept = keep_idx.cpu().numpy()
     cnt = keep_cnt.cpu().numpy()
@@ -139,16 +143,23 @@ def test_h2o_compacting_step_full_size():
     out2 = torch.empty(q2.shape, dtype=torch.float32, device="cuda")
     ops.paged_decode_attn(out2, q2, k, v, dst, keep_cnt, 16 * per_seq)
     scale = 1 / math.sqrt(w.head_dim)
-    worst = worst2 = 0.0
+    src_sc = scores.cpu().numpy().astype(np.float64)
+    dst_sc = scores_dst.cpu().numpy().astype(np.float64)
+    worst = worst2 = worst_mass = 0.0
     for s in range(0, B, 4):
         r = torch.from_numpy(H.logical_rows(lay, s, kept[s, : cnt[s]])).to(case.ksrc.device)
         kr, vr = H.to_f64(case.ksrc.index_select(0, r)), H.to_f64(case.vsrc.index_select(0, r))
-        ref, _ = attention.decode_attention(H.to_f64(q1[s]), kr, vr, scale)
+        ref, probs = attention.decode_attention(H.to_f64(q1[s]), kr, vr, scale)
         worst = max(worst, H.max_err(H.to_f64(out[s]), ref))
+        exp = src_sc[s, kept[s, : cnt[s]]] + attention.head_mean_mass(probs)
+        bound = 1e-4 * attention.head_mean_mass(probs) + 2.0 ** -22 * np.abs(exp)
+        worst_mass = max(worst_mass, float(np.max(np.abs(dst_sc[s, : cnt[s]] - exp) / bound)))
+        assert np.all(dst_sc[s, cnt[s]:] == -7.0)
         ref2, _ = attention.decode_attention(H.to_f64(q2[s]), kr, vr, scale)
         worst2 = max(worst2, H.max_err(H.to_f64(out2[s]), ref2))
-    print(f"h2o compacting step: {int(cnt.sum())} tokens moved, out err {worst:.3e}, next step {worst2:.3e}")
-    assert worst <= 2e-3 and worst2 <= 2e-3
+    print(f"h2o compacting step: {int(cnt.sum())} tokens moved, out err {worst:.3e}, next step {worst2:.3e}, "
+          f"score err / bound {worst_mass:.3f}")
+    assert worst <= 2e-3 and worst2 <= 2e-3 and worst_mass <= 1.0
 
 
 def test_llama2_stack_80_layers_sampled():
