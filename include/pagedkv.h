@@ -300,16 +300,19 @@ int paged_decode_append_attn(void* out, int out_dtype,
  *     block_tables[s] (n >= 1; n == 0 gives NaN), and the token at
  *     keep_idx[s][i] is copied (K and V, all KV heads) to logical position i
  *     of dst_tables[s];
- *   k_new, v_new given ([num_seqs][num_kv_heads][head_dim] in the pool's
- *     dtype, 16-byte aligned): position L - 1 holds the step's new token,
- *     stored there as paged_decode_append_attn stores it; the step attends the
+ *   k_new, v_new given ([num_seqs][num_kv_heads][head_dim] in q's dtype,
+ *     16-byte aligned): position L - 1 holds the step's new token, stored
+ *     there (quantised for 8-bit pools) as paged_decode_append_attn stores
+ *     it; the step attends the
  *     listed positions (all < L - 1) and the new token, which is also copied,
  *     to logical position n.
  *   out = sum_t softmax_t(scale * q . K[t]) * V[t] over those tokens, t in
  *   keep order; the sequence then holds n (+1) tokens in dst_tables[s], the
- *   same bytes kv_compact (and the append) would give, and the host releases
- *   its source blocks.
- *   kv_dtype     BF16 or F16 (PKV_EUNSUPPORTED otherwise); q_dtype == kv_dtype
+ *   same bytes (codes and per-token scales for 8-bit pools) kv_compact and
+ *   the append would give, and the host releases its source blocks.
+ *   kv_dtype     BF16 or F16 with q_dtype == kv_dtype, or an 8-bit format (per-token
+ *                or per-channel FP8 / INT8, k_scale / v_scale as for paged_decode_attn)
+ *                with q_dtype BF16 or F16; PKV_EUNSUPPORTED otherwise
  *   keep_idx     int32 [num_seqs][keep_stride], strictly ascending per
  *                sequence; keep_count int32 [num_seqs]
  *   dst_tables   int32 [num_seqs][dst_stride], fresh blocks (no slot written
@@ -338,7 +341,7 @@ size_t paged_decode_attn_compact_workspace_size(int num_seqs, int num_q_heads, i
 int paged_decode_attn_compact(void* out, int out_dtype,
                               const void* q, int q_dtype,
                               const void* k_new, const void* v_new,
-                              void* k_pool, void* v_pool, int kv_dtype,
+                              void* k_pool, void* v_pool, float* k_scale, float* v_scale, int kv_dtype,
                               const int32_t* block_tables, int block_table_stride,
                               const int32_t* context_lens, int max_context_len,
                               const int32_t* keep_idx, int keep_stride, const int32_t* keep_count,

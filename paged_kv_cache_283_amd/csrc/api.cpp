@@ -377,16 +377,19 @@ int paged_decode_append_attn(void* out, int out_dtype, const void* q, int q_dtyp
 }
 
 int paged_decode_attn_compact(void* out, int out_dtype, const void* q, int q_dtype, const void* k_new,
-                              const void* v_new, void* k_pool, void* v_pool, int kv_dtype,
+                              const void* v_new, void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                              int kv_dtype,
                               const int32_t* block_tables, int block_table_stride, const int32_t* context_lens,
                               int max_context_len, const int32_t* keep_idx, int keep_stride,
                               const int32_t* keep_count, const int32_t* dst_tables, int dst_stride, int num_seqs,
                               int num_blocks, int num_q_heads, int num_kv_heads, int head_dim, int block_size,
                               float scale, const float* attn_mass_src, int attn_mass_src_stride, float* attn_mass,
                               int attn_mass_stride, void* workspace, size_t workspace_bytes, void* stream) {
-  if (kv_dtype != PKV_BF16 && kv_dtype != PKV_F16)
-    return fail(PKV_EUNSUPPORTED, "kv_dtype %d (compaction is built for BF16 and F16 pools)", kv_dtype);
-  if (q_dtype != kv_dtype) return fail(PKV_EUNSUPPORTED, "q_dtype %d must be the pool's dtype %d", q_dtype, kv_dtype);
+  if (!valid_kv_dtype(kv_dtype) || kv_dtype == PKV_F32)
+    return fail(PKV_EUNSUPPORTED, "kv_dtype %d (compaction is built for 16-bit and 8-bit pools)", kv_dtype);
+  if (code8_kv(kv_dtype) ? (q_dtype != PKV_BF16 && q_dtype != PKV_F16) : q_dtype != kv_dtype)
+    return fail(PKV_EUNSUPPORTED, "q_dtype %d (built: the pool's dtype for 16-bit pools, bf16 or f16 for 8-bit)",
+                q_dtype);
   if ((k_new == nullptr) != (v_new == nullptr)) return fail(PKV_EINVAL, "k_new and v_new must both be given or NULL");
   if (keep_stride < 0 || keep_stride > (1 << 30)) return fail(PKV_EINVAL, "keep_stride %d outside [0, 2^30]", keep_stride);
   if (dst_stride < 1 || dst_stride > (1 << 26)) return fail(PKV_EINVAL, "dst_stride %d outside [1, 2^26]", dst_stride);
@@ -400,7 +403,7 @@ int paged_decode_attn_compact(void* out, int out_dtype, const void* q, int q_dty
   const size_t need = paged_decode_attn_compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, mass);
   if (workspace_bytes < need) return fail(PKV_EWORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
   pkv::AttnArgs a;
-  int st = prepare_decode_attn(a, out, out_dtype, q, q_dtype, k_pool, v_pool, nullptr, nullptr, kv_dtype,
+  int st = prepare_decode_attn(a, out, out_dtype, q, q_dtype, k_pool, v_pool, k_scale, v_scale, kv_dtype,
                                block_tables, block_table_stride, context_lens, max_context_len, num_seqs, num_blocks,
                                num_q_heads, num_kv_heads, head_dim, block_size, scale, 0, 0, attn_mass,
                                attn_mass_stride, workspace, workspace_bytes);
@@ -421,6 +424,8 @@ int paged_decode_attn_compact(void* out, int out_dtype, const void* q, int q_dty
   a.v_new = v_new;
   a.k_store = k_pool;
   a.v_store = v_pool;
+  a.k_scale_store = k_scale;
+  a.v_scale_store = v_scale;
   a.keep_map = map;
   a.map_stride = map_stride;
   a.mass_src = attn_mass_src;

@@ -102,8 +102,12 @@ __device__ __forceinline__ void lds_wave_sync() {
 
 // Floats of the per-wave LDS window for H2O logits: 32 KiB with one wave per
 // SIMD (16-bit and f32 pools; a typical range fits, so chunks rarely drain),
-// 8 KiB with two (8-bit pools).
-__host__ __device__ constexpr int stash_floats(int kvt) { return is_code8(kvt) ? 2048 : 8192; }
+// 8 KiB with two (8-bit pools).  Compacting instances keep 32 KiB for every
+// format (half of it holds the destination tile images), which leaves room
+// for one workgroup per SIMD.
+__host__ __device__ constexpr int stash_floats(int kvt, bool cmp = false) {
+  return is_code8(kvt) && !cmp ? 2048 : 8192;
+}
 
 // Table entries staged in LDS per chunk of a segment.
 constexpr int kTabBlocks = 1024;
@@ -335,7 +339,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
       }
     }
   };
-  static_assert(!CMP || EB == 2, "compaction is built for 16-bit pools");
+  static_assert(!CMP || EB <= 2, "compaction is built for 16-bit and 8-bit pools");
   struct Regs {
     uint32_t k[KW];
     uint32_t v[NT][VW];
@@ -384,18 +388,24 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   };
 
   // CMP: the kept tokens pass through LDS images of their destination tiles
-  // (the end of the logit window's space), destination
-  // tile T of the sequence in image T % 2, laid out as the pool's tile, and a
-  // tile goes out in whole 16-byte chunks once this wave has written its last
-  // slot.  The segment's first and last tiles may be shared with the waves of
-  // the neighbouring segments: of those only this wave's slots are stored (K
-  // pieces of 16 bytes, V elements of 2).
+  // (the end of the logit window's space), destination tile T of the
+  // sequence in image T % 2, laid out as the pool's tile (K, V, then for
+  // per-token 8-bit formats the tile's 16 K and 16 V scales), and a tile goes
+  // out in whole 16-byte chunks once this wave has written its last slot.
+  // The segment's first and last tiles may be shared with the waves of the
+  // neighbouring segments: of those only this wave's slots are stored (K
+  // pieces of 16 bytes, single V elements, single scales).
   constexpr int kTileB = kBlockSize * D * EB;
-  // the images take the window's last 4 kTileB bytes (kTileB floats); the
-  // H2O logit window keeps the rest
-  constexpr int kImgFloats = CMP ? kTileB : 0;
-  static_assert(2 * kImgFloats <= stash_floats(KVT), "two K and V tile images fit the logit window");
-  uint8_t* cimg = reinterpret_cast<uint8_t*>(s_stash + (stash_floats(KVT) - kImgFloats));
+  constexpr bool kScl = is_quantised(KVT);
+  constexpr int kImgB = 2 * kTileB + (kScl ? 2 * kBlockSize * 4 : 0);   // one image
+  constexpr int kVY = 4 / EB;                  // tiles (16 dims apart) per V chunk
+  constexpr int kVE = 16 / EB;                 // elements per V chunk
+  // the two images take the window's last 2 kImgB bytes; the H2O logit
+  // window keeps the rest
+  constexpr int kImgFloats = CMP ? 2 * kImgB / 4 : 0;
+  static_assert(2 * kImgFloats <= stash_floats(KVT, CMP), "the tile images leave half the logit window");
+  uint8_t* cimg = reinterpret_cast<uint8_t*>(s_stash + (stash_floats(KVT, CMP) - kImgFloats));
+  using VE = typename std::conditional<EB == 2, uint16_t, uint8_t>::type;
   int c_first = -1;            // rank (destination position) of the segment's first kept token
   int c_end = 0;               // one past the last rank written
   int c_blk[2] = {-1, -1};     // destination block of the tile in each image
@@ -404,9 +414,10 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
       const int blk = c_blk[T & 1];
       if (blk < 0) return;
       lds_wave_sync();
-      const uint8_t* img = cimg + (T & 1) * 2 * kTileB;
-      uint8_t* kt = reinterpret_cast<uint8_t*>(a.k_store) + ((size_t)blk * a.num_kv_heads + kvh) * kTileB;
-      uint8_t* vt = reinterpret_cast<uint8_t*>(a.v_store) + ((size_t)blk * a.num_kv_heads + kvh) * kTileB;
+      const uint8_t* img = cimg + (T & 1) * kImgB;
+      const size_t tile = (size_t)blk * a.num_kv_heads + kvh;
+      uint8_t* kt = reinterpret_cast<uint8_t*>(a.k_store) + tile * kTileB;
+      uint8_t* vt = reinterpret_cast<uint8_t*>(a.v_store) + tile * kTileB;
       if (lo == 0 && hi == kBlockSize) {
 #pragma unroll
         for (int k = 0; k < kTileB / (kWave * 16); ++k) {
@@ -422,20 +433,28 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
           if (sl >= lo && sl < hi)
             *reinterpret_cast<u32x4*>(kt + p * 16) = *reinterpret_cast<const u32x4*>(img + p * 16);
         }
-        // V element x of chunk x / 8 belongs to slot 4 (chunk % 4) + x % 4
-        const uint16_t* iv = reinterpret_cast<const uint16_t*>(img + kTileB);
-        uint16_t* dv = reinterpret_cast<uint16_t*>(vt);
+        // V element x of chunk x / kVE belongs to slot 4 (chunk % 4) + x % 4
+        const VE* iv = reinterpret_cast<const VE*>(img + kTileB);
+        VE* dv = reinterpret_cast<VE*>(vt);
 #pragma unroll 4
-        for (int k = 0; k < kTileB / (kWave * 2); ++k) {
-          const int x = k * kWave + lane, sl = (((x >> 3) & 3) << 2) | (x & 3);
+        for (int k = 0; k < kTileB / (kWave * EB); ++k) {
+          const int x = k * kWave + lane, sl = (((x / kVE) & 3) << 2) | (x & 3);
           if (sl >= lo && sl < hi) dv[x] = iv[x];
+        }
+      }
+      if constexpr (kScl) {   // lanes 0-15 the K scales, 16-31 the V scales of the tile's slots
+        const float* is = reinterpret_cast<const float*>(img + 2 * kTileB);
+        const int sl = lane & 15;
+        if (lane < 2 * kBlockSize && sl >= lo && sl < hi) {
+          float* ds = lane < kBlockSize ? a.k_scale_store : a.v_scale_store;
+          ds[tile * kBlockSize + sl] = is[lane];
         }
       }
     }
   };
   // Lane (c, j) holds K chunks 4w + j of token row c and the V elements of
-  // tokens 4j..4j+3 for dims 16t + c; a kept token's rank is the block's first
-  // rank plus the kept tokens before it in the block.
+  // tokens 4j..4j+3 for dims 16t + c (and their scales); a kept token's rank
+  // is the block's first rank plus the kept tokens before it in the block.
   auto compact_put = [&](const Regs& r) {
     if constexpr (CMP) {
       const uint32_t mask = (uint32_t)r.km & 0xffffu;
@@ -448,7 +467,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
       if ((r0 & 15) + cnt > kBlockSize) c_blk[(t0 + 1) & 1] = r.kd1;
       if ((mask >> c) & 1u) {
         const int q = r0 + __builtin_popcount(mask & ((1u << c) - 1u));
-        uint8_t* img = cimg + ((q >> 4) & 1) * 2 * kTileB;
+        uint8_t* img = cimg + ((q >> 4) & 1) * kImgB;
 #pragma unroll
         for (int w = 0; w < KW / 4; ++w)
           *reinterpret_cast<u32x4*>(img + ((4 * w + j) * kBlockSize + (q & 15)) * 16) =
@@ -459,12 +478,20 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
         const int tok = 4 * j + e;
         if ((mask >> tok) & 1u) {
           const int q = r0 + __builtin_popcount(mask & ((1u << tok) - 1u));
-          uint16_t* iv = reinterpret_cast<uint16_t*>(cimg + ((q >> 4) & 1) * 2 * kTileB + kTileB);
+          uint8_t* img = cimg + ((q >> 4) & 1) * kImgB;
+          VE* iv = reinterpret_cast<VE*>(img + kTileB);
           const int s2 = q & 15;
 #pragma unroll
-          for (int t = 0; t < NT; ++t)   // chunk ((t / 2) 16 + c) 4 + s2 / 4, element (t % 2) 4 + s2 % 4
-            iv[(((t >> 1) * kBlockSize + c) * 4 + (s2 >> 2)) * 8 + (t & 1) * 4 + (s2 & 3)] =
-                (uint16_t)(r.v[t][e >> 1] >> (16 * (e & 1)));
+          for (int t = 0; t < NT; ++t)   // chunk ((t / Y) 16 + c) 4 + s2 / 4, element (t % Y) 4 + s2 % 4
+            iv[(((t / kVY) * kBlockSize + c) * 4 + (s2 >> 2)) * kVE + (t % kVY) * 4 + (s2 & 3)] =
+                (VE)(r.v[t][(e * EB) / 4] >> (8 * ((e * EB) % 4)));
+          if constexpr (kScl) {
+            if (c == 0) {
+              float* is = reinterpret_cast<float*>(img + 2 * kTileB);
+              is[s2] = r.ks[e];
+              is[kBlockSize + s2] = r.vs[e];
+            }
+          }
         }
       }
       c_end = r0 + cnt;
@@ -478,7 +505,7 @@ __device__ __forceinline__ void wave_segment(const AttnArgs& a, int* s_tab, uint
   // coalesced 16-byte stores after each chunk: a store in every block's step
   // would make the tile waits two blocks later wait for it too (stores share
   // the load counter).
-  const int st_blocks = (stash_floats(KVT) - kImgFloats) / (group * kBlockSize);
+  const int st_blocks = (stash_floats(KVT, CMP) - kImgFloats) / (group * kBlockSize);
   auto stash_flush = [&](int vb0, int nb) {
     lds_wave_sync();
     const int n4 = nb * kBlockSize / 4;       // 16-byte pieces per head
@@ -930,7 +957,7 @@ __global__ void __launch_bounds__(64) attn_wave_kernel(const AttnArgs a) {
   // the new token's stored K and V rows when the decode append is fused in
   __shared__ uint32_t s_new[2 * D * KvType<KVT>::kBytes / 4];
   // the H2O logit window (used only when attn_mass is requested)
-  __shared__ __attribute__((aligned(16))) float s_stash[stash_floats(KVT)];
+  __shared__ __attribute__((aligned(16))) float s_stash[stash_floats(KVT, CMP)];
   const int hkv = a.num_kv_heads;
   const int B = a.num_seqs;
   const int lane = threadIdx.x;
@@ -1315,11 +1342,17 @@ hipError_t dispatch_d(const AttnArgs& a, int d, hipStream_t st, hipEvent_t eb, h
   return d == 64 ? launch_partition<KVT, QT, 64>(a, st, eb, ee) : launch_partition<KVT, QT, 128>(a, st, eb, ee);
 }
 
-// Compacting calls: 16-bit pools with queries of the pool's dtype.
-template <int KVT>
+// Compacting calls: 16-bit pools with queries of the pool's dtype, 8-bit
+// pools with bf16 or f16 queries.
+template <int KVT, int QT>
 hipError_t dispatch_compact(const AttnArgs& a, int d, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
-  return d == 64 ? launch_partition<KVT, KVT, 64, true>(a, st, eb, ee)
-                 : launch_partition<KVT, KVT, 128, true>(a, st, eb, ee);
+  return d == 64 ? launch_partition<KVT, QT, 64, true>(a, st, eb, ee)
+                 : launch_partition<KVT, QT, 128, true>(a, st, eb, ee);
+}
+template <int KVT>
+hipError_t dispatch_compact8(const AttnArgs& a, int q_dtype, int d, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
+  return q_dtype == DT_BF16 ? dispatch_compact<KVT, DT_BF16>(a, d, st, eb, ee)
+                            : dispatch_compact<KVT, DT_F16>(a, d, st, eb, ee);
 }
 
 template <int KVT>
@@ -1392,9 +1425,15 @@ hipError_t launch_decode_attn(const AttnArgs& a, int kv_dtype, int q_dtype, int 
                               hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
   if (a.num_seqs == 0) return hipSuccess;
   hipError_t err;
-  if (a.keep_map != nullptr) {   // validated: BF16 or F16 pool, q of the same dtype
-    err = kv_dtype == DT_BF16 ? dispatch_compact<DT_BF16>(a, head_dim, st, ev_begin, ev_end)
-                              : dispatch_compact<DT_F16>(a, head_dim, st, ev_begin, ev_end);
+  if (a.keep_map != nullptr) {   // validated: 16-bit pool with q of its dtype, or 8-bit pool with 16-bit q
+    switch (kv_dtype) {
+      case DT_BF16: err = dispatch_compact<DT_BF16, DT_BF16>(a, head_dim, st, ev_begin, ev_end); break;
+      case DT_F16: err = dispatch_compact<DT_F16, DT_F16>(a, head_dim, st, ev_begin, ev_end); break;
+      case DT_FP8: err = dispatch_compact8<DT_FP8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+      case DT_INT8: err = dispatch_compact8<DT_INT8>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+      case DT_FP8_CH: err = dispatch_compact8<DT_FP8_CH>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+      default: err = dispatch_compact8<DT_INT8_CH>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
+    }
   } else switch (kv_dtype) {
     case DT_F32: err = dispatch_q<DT_F32>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;
     case DT_BF16: err = dispatch_q<DT_BF16>(a, q_dtype, head_dim, st, ev_begin, ev_end); break;

@@ -374,12 +374,13 @@ def compact_workspace_size(num_seqs, num_q_heads, head_dim, max_context_len, wan
 
 
 def paged_decode_attn_compact(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len, keep_idx,
-                              keep_count, dst_tables, k_new=None, v_new=None, scale=None, attn_mass_src=None,
-                              attn_mass=None, workspace=None, stream=None, prepare=False):
+                              keep_count, dst_tables, k_new=None, v_new=None, scale=None, k_scale=None, v_scale=None,
+                              attn_mass_src=None, attn_mass=None, workspace=None, stream=None, prepare=False):
     """A decode step that applies an eviction keep-set in the same pass: q [B][Hq][D] attends the kept
     positions keep_idx[s][:keep_count[s]] of each sequence (plus, with k_new/v_new [B][Hkv][D], the new
     token stored at position context_lens[s] - 1), and those tokens move, in order, to logical positions
-    0.. of dst_tables[s] (16-bit pools, q of the pool's dtype).  With attn_mass (float32 [B][>= max_len],
+    0.. of dst_tables[s] (16-bit pools with q of the pool's dtype, or 8-bit pools with their scales and
+    bf16/f16 q; k_new/v_new in q's dtype).  With attn_mass (float32 [B][>= max_len],
     the compacted H2O score rows) and attn_mass_src (the rows before the step): entry i gets the moved
     token's source score plus this step's mass."""
     b, hq, d = q.shape
@@ -389,9 +390,9 @@ def paged_decode_attn_compact(out, q, k_pool, v_pool, block_tables, context_lens
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
     if k_new is not None:
-        if tuple(k_new.shape) != (b, hkv, d) or v_new.shape != k_new.shape or k_new.dtype != k_pool.dtype \
-                or v_new.dtype != k_pool.dtype:
-            raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim] of the pool's dtype")
+        if tuple(k_new.shape) != (b, hkv, d) or v_new.shape != k_new.shape or k_new.dtype != q.dtype \
+                or v_new.dtype != q.dtype:
+            raise ValueError("k_new and v_new must be [num_seqs][num_kv_heads][head_dim] of q's dtype")
     for t, name in ((block_tables, "block_tables"), (context_lens, "context_lens"), (keep_idx, "keep_idx"),
                     (keep_count, "keep_count"), (dst_tables, "dst_tables")):
         _need(t, torch.int32, name)
@@ -413,7 +414,8 @@ def paged_decode_attn_compact(out, q, k_pool, v_pool, block_tables, context_lens
         workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
         made = (workspace,)
     args = (_ptr(out), float_code(out.dtype), _ptr(q), float_code(q.dtype), _ptr(k_new), _ptr(v_new),
-            _ptr(k_pool), _ptr(v_pool), pool_code(k_pool, None, None), _ptr(block_tables), block_tables.shape[1],
+            _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), pool_code(k_pool, k_scale, v_scale),
+            _ptr(block_tables), block_tables.shape[1],
             _ptr(context_lens), int(max_context_len), _ptr(keep_idx), keep_idx.shape[1], _ptr(keep_count),
             _ptr(dst_tables), dst_tables.shape[1], b, nb, hq, hkv, d, BLOCK_SIZE, float(scale),
             _ptr(attn_mass_src), src_stride, _ptr(attn_mass), dst_stride, _ptr(workspace),

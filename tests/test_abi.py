@@ -107,7 +107,7 @@ def test_append_attn_validation(change, status):
 
 def compact_args(**kw):
     a = dict(out=FAKE, out_dtype=0, q=FAKE, q_dtype=1, k_new=FAKE, v_new=FAKE, k_pool=FAKE, v_pool=FAKE,
-             kv_dtype=1, tables=FAKE, stride=512, lens=FAKE, max_len=8192, keep_idx=FAKE, keep_stride=2048,
+             k_scale=None, v_scale=None, kv_dtype=1, tables=FAKE, stride=512, lens=FAKE, max_len=8192, keep_idx=FAKE, keep_stride=2048,
              keep_count=FAKE, dst=FAKE, dst_stride=129, b=4, nb=100, hq=32, hkv=8, d=128, bs=16, scale=0.088,
              mass_src=None, mass_src_stride=0, mass=None, mass_stride=0, ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
@@ -115,8 +115,10 @@ def compact_args(**kw):
 
 
 @pytest.mark.parametrize("change,status", [
-    (dict(kv_dtype=3), _lib.EUNSUPPORTED),               # FP8 pool: compaction is built for 16-bit pools
+    (dict(kv_dtype=3), _lib.EINVAL),                     # FP8 pool without scales
+    (dict(kv_dtype=3, q_dtype=0, k_scale=FAKE, v_scale=FAKE), _lib.EUNSUPPORTED),   # f32 queries on an 8-bit pool
     (dict(kv_dtype=0, q_dtype=0), _lib.EUNSUPPORTED),    # f32 pool
+    (dict(kv_dtype=9), _lib.EUNSUPPORTED),
     (dict(q_dtype=2), _lib.EUNSUPPORTED),                # f16 queries on a bf16 pool
     (dict(v_new=None), _lib.EINVAL),                     # one of the new rows only
     (dict(keep_stride=-1), _lib.EINVAL),

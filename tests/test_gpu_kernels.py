@@ -701,17 +701,30 @@ def _compact_keeps(lens, append, seed):
 
 
 COMPACT_GRID = [
-    # kv, d, hq, hkv, append
-    ("bf16", 128, 32, 8, True),
-    ("bf16", 128, 32, 8, False),
-    ("f16", 64, 16, 2, True),
-    ("bf16", 64, 8, 8, True),      # G = 1
-    ("f16", 128, 16, 1, False),    # G = 16
+    # kv, q, d, hq, hkv, append
+    ("bf16", "bf16", 128, 32, 8, True),
+    ("bf16", "bf16", 128, 32, 8, False),
+    ("f16", "f16", 64, 16, 2, True),
+    ("bf16", "bf16", 64, 8, 8, True),      # G = 1
+    ("f16", "f16", 128, 16, 1, False),     # G = 16
+    ("fp8", "bf16", 128, 32, 8, True),     # 8-bit pools: codes and per-token scales move
+    ("int8", "bf16", 64, 16, 2, True),
+    ("int8", "f16", 128, 32, 8, False),
+    ("fp8_ch", "bf16", 128, 32, 8, True),  # static per-channel scales stay
+    ("int8_ch", "bf16", 64, 8, 1, False),
 ]
 
 
-@pytest.mark.parametrize("kv,d,hq,hkv,append", COMPACT_GRID)
-def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
+def _stored_rows(w, case, s, positions):
+    """float64 values the pool holds for sequence s's given positions (the oracle's codec)."""
+    rows = torch.from_numpy(H.logical_rows(case.lay, s, positions)).to(case.ksrc.device)
+    kc, vc = H.channel_pair(w)
+    return (H.stored_values(w.kv_dtype, H.to_f64(case.ksrc.index_select(0, rows)), kc),
+            H.stored_values(w.kv_dtype, H.to_f64(case.vsrc.index_select(0, rows)), vc))
+
+
+@pytest.mark.parametrize("kv,q,d,hq,hkv,append", COMPACT_GRID)
+def test_decode_attn_compact_matches_oracle(kv, q, d, hq, hkv, append):
     """paged_decode_attn_compact: the output equals the oracle's attention over the kept tokens (and
     the new one), and the pools end up exactly as the oracle's append (new token at L - 1) followed by
     its compaction of the kept positions (and L - 1) into the destination blocks; a decode over the
@@ -719,7 +732,8 @@ def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
     cut at range boundaries, so several waves fill one sequence's destination blocks), with one
     length-1 sequence and keep-none lists; keep-none without a new token attends nothing (NaN)."""
     lens = COMPACT_LENS
-    w = dataclasses.replace(_case_workload(kv, kv, d, hq, hkv, seed=4100 + d + hq, lens=lens), extra_blocks=400)
+    w = dataclasses.replace(_case_workload(kv, q, d, hq, hkv, seed=4100 + d + hq, lens=lens), extra_blocks=400,
+                            src_dtype=q if kv in CODE8 else kv)
     case = H.Case(w, hold_last=append)
     lay = case.lay
     n_seq = len(lens)
@@ -740,18 +754,18 @@ def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
     # the oracle: append (new token at L - 1), then compaction of the kept positions (+ L - 1)
     ref = _host_pools(case.pools, kv)
     if append:
-        paging.write_tokens(ref, kv, H.to_host(k_new), H.to_host(v_new), kv, lay.tables, list(range(n_seq)),
-                            [L - 1 for L in lens])
+        paging.write_tokens(ref, kv, H.to_host(k_new), H.to_host(v_new), w.src_dtype, lay.tables,
+                            list(range(n_seq)), [L - 1 for L in lens])
     moved = [np.concatenate([k, [L - 1]]) if append else k for k, L in zip(keeps, lens)]
     for s in range(n_seq):
         paging.compact(ref, kv, lay.tables[s], moved[s], dst[s], lay.num_blocks)
 
-    k, v, _, _ = case.pools
+    k, v, ks, vs = case.pools
     out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device="cuda")
     dst_t = torch.from_numpy(dst).cuda()
     ops.paged_decode_attn_compact(out, case.q, k, v, case.tables, case.lens, lay.max_len,
                                   torch.from_numpy(keep_idx).cuda(), torch.from_numpy(counts).cuda(), dst_t,
-                                  k_new=k_new, v_new=v_new)
+                                  k_new=k_new, v_new=v_new, k_scale=ks, v_scale=vs)
     torch.cuda.synchronize()
     for got, exp in zip(case.pools, ref):
         if exp is not None:
@@ -763,8 +777,7 @@ def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
         if moved[s].size == 0:
             assert torch.isnan(out[s]).all(), s
             continue
-        rows = torch.from_numpy(H.logical_rows(lay, s, moved[s])).to(case.ksrc.device)
-        kr, vr = H.to_f64(case.ksrc.index_select(0, rows)), H.to_f64(case.vsrc.index_select(0, rows))
+        kr, vr = _stored_rows(w, case, s, moved[s])
         ref_out, _ = attention.decode_attention(H.to_f64(case.q[s]), kr, vr, scale)
         worst = max(worst, H.max_err(H.to_f64(out[s]), ref_out))
         if s == 7:
@@ -773,22 +786,24 @@ def test_decode_attn_compact_matches_oracle(kv, d, hq, hkv, append):
     new_lens = torch.tensor([m.size for m in moved], dtype=torch.int32).cuda()
     q2 = W.queries(w, step=1, device="cuda")
     out2 = torch.empty(q2.shape, dtype=torch.float32, device="cuda")
-    ops.paged_decode_attn(out2, q2, k, v, dst_t, new_lens, 16 * dst_w)
+    ops.paged_decode_attn(out2, q2, k, v, dst_t, new_lens, 16 * dst_w, k_scale=ks, v_scale=vs)
     ref2, _ = attention.decode_attention(H.to_f64(q2[7]), keep_rows, keep_v, scale)
     err2 = H.max_err(H.to_f64(out2[7]), ref2)
-    print(f"compacting decode {kv} D={d} G={hq // hkv} append={append}: kept {counts.tolist()}, "
+    print(f"compacting decode {kv}/{q} D={d} G={hq // hkv} append={append}: kept {counts.tolist()}, "
           f"max abs err {worst:.3e}, next step {err2:.3e}")
     assert worst <= TOL[kv] and err2 <= TOL[kv]
 
 
-@pytest.mark.parametrize("kv,d,hq,hkv,append", [("bf16", 128, 32, 8, True), ("f16", 64, 16, 2, False)])
-def test_decode_attn_compact_with_h2o_mass(kv, d, hq, hkv, append):
+@pytest.mark.parametrize("kv,q,d,hq,hkv,append", [("bf16", "bf16", 128, 32, 8, True), ("f16", "f16", 64, 16, 2, False),
+                                                  ("fp8", "bf16", 128, 32, 8, True)])
+def test_decode_attn_compact_with_h2o_mass(kv, q, d, hq, hkv, append):
     """The compacting step with the H2O mass: entry i of the compacted score row is the moved token's
     source score plus this step's mass of it (the oracle's head-mean probabilities over the kept tokens
     and the new one, 1e-4 relative, plus the fp32 rounding of the sum); entries past the moved tokens
     keep their values; output and pools as without the mass."""
     lens = COMPACT_LENS
-    w = dataclasses.replace(_case_workload(kv, kv, d, hq, hkv, seed=4300 + d, lens=lens), extra_blocks=400)
+    w = dataclasses.replace(_case_workload(kv, q, d, hq, hkv, seed=4300 + d, lens=lens), extra_blocks=400,
+                            src_dtype=q if kv in CODE8 else kv)
     case = H.Case(w, hold_last=append)
     lay = case.lay
     n_seq, L = len(lens), lay.max_len
@@ -809,11 +824,11 @@ def test_decode_attn_compact_with_h2o_mass(kv, d, hq, hkv, append):
     src_t = torch.from_numpy(src_scores).cuda()
     dst_t = torch.full((n_seq, L), -7.0, dtype=torch.float32, device="cuda")
     k_new, v_new = case.newest_rows() if append else (None, None)
-    k, v, _, _ = case.pools
+    k, v, ks, vs = case.pools
     out = torch.empty(case.q.shape, dtype=torch.float32, device="cuda")
     ops.paged_decode_attn_compact(out, case.q, k, v, case.tables, case.lens, L, torch.from_numpy(keep_idx).cuda(),
                                   torch.from_numpy(counts).cuda(), torch.from_numpy(dst).cuda(), k_new=k_new,
-                                  v_new=v_new, attn_mass_src=src_t, attn_mass=dst_t)
+                                  v_new=v_new, k_scale=ks, v_scale=vs, attn_mass_src=src_t, attn_mass=dst_t)
     torch.cuda.synchronize()
     got = dst_t.cpu().numpy().astype(np.float64)
     assert torch.equal(src_t.cpu(), torch.from_numpy(src_scores))      # the source rows are only read
@@ -824,8 +839,7 @@ def test_decode_attn_compact_with_h2o_mass(kv, d, hq, hkv, append):
         if moved.size == 0:
             assert np.all(got[s_] == -7.0)
             continue
-        rows = torch.from_numpy(H.logical_rows(lay, s_, moved)).to(case.ksrc.device)
-        kr, vr = H.to_f64(case.ksrc.index_select(0, rows)), H.to_f64(case.vsrc.index_select(0, rows))
+        kr, vr = _stored_rows(w, case, s_, moved)
         ref, probs = attention.decode_attention(H.to_f64(case.q[s_]), kr, vr, scale)
         worst_out = max(worst_out, H.max_err(H.to_f64(out[s_]), ref))
         mass = attention.head_mean_mass(probs)
@@ -834,7 +848,7 @@ def test_decode_attn_compact_with_h2o_mass(kv, d, hq, hkv, append):
         bound = 1e-4 * mass + 2.0 ** -22 * np.abs(exp)
         worst_mass = max(worst_mass, float(np.max(err / bound)))
         assert np.all(got[s_, moved.size:] == -7.0), s_
-    print(f"compacting step with mass {kv} D={d}: out err {worst_out:.3e}, mass err / bound {worst_mass:.3f}")
+    print(f"compacting step with mass {kv}/{q} D={d}: out err {worst_out:.3e}, mass err / bound {worst_mass:.3f}")
     assert worst_out <= TOL[kv] and worst_mass <= 1.0
 
 
