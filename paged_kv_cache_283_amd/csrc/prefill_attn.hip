@@ -35,6 +35,20 @@
 
 namespace pkv {
 
+#ifndef PKV_PREFILL_PRIO
+#define PKV_PREFILL_PRIO 1   // wave priority over a run of MFMAs (0: leave it)
+#endif
+
+// Two waves share each SIMD: a wave's block of MFMAs runs at raised priority,
+// so its next MFMA issues as soon as the matrix core takes it while the other
+// wave's softmax VALU work fills the cycles in between.
+__device__ __forceinline__ void mfma_phase(bool on) {
+  if constexpr (PKV_PREFILL_PRIO > 0) {
+    if (on) __builtin_amdgcn_s_setprio(PKV_PREFILL_PRIO);
+    else __builtin_amdgcn_s_setprio(0);
+  }
+}
+
 // Maximum for the softmax's running max: IEEE maximum (a NaN logit makes the
 // max NaN, and the output is NaN either way), which gfx950 has as
 // v_maximum3_f32; fmaxf's NaN-ignoring form needs every MFMA result
@@ -67,6 +81,15 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #ifndef PKV_PREFILL_STAGES
 #define PKV_PREFILL_STAGES 4              // LDS ring slots (pairs in flight = slots - 1)
 #endif
+#ifndef PKV_PREFILL_ILV_LEAD
+#define PKV_PREFILL_ILV_LEAD 8            // VALU instructions scheduled between the LDS reads and the first MFMA
+#endif
+#ifndef PKV_PREFILL_ILV_QK
+#define PKV_PREFILL_ILV_QK 4              // VALU instructions scheduled after each QK MFMA of the next pair
+#endif
+#ifndef PKV_PREFILL_ILV_PV
+#define PKV_PREFILL_ILV_PV 4              // ... after each PV MFMA of a column set but the last
+#endif
 
 
 
@@ -74,43 +97,52 @@ namespace {
 
 }  // namespace
 
-// One step of the LDS ring: the table entries of the step's block pair, this
-// lane's K and V operand chunks of the pair from the slot at rd, and the
-// direct-to-LDS copy of one tile of a later pair into the slot at wr (LPS rows
-// of 1 KiB: row k from src_tile + k * 1024 to row row0 + row_step * k).  Every
-// LDS access of the step goes through the restrict parameters, so once inlined
-// the compiler knows the copy writes none of what the step reads; otherwise
-// each LDS read waits for every copy in flight (vmcnt(0)) and the ring holds a
-// single pair.
-template <int TB, int LPS, int KW4, int VQ>
-__device__ __forceinline__ void ring_io(const int* __restrict__ tab, const uint8_t* __restrict__ rd,
-                                        uint8_t* __restrict__ wr, int i, bool has_b, int blk_next,
-                                        const uint8_t* kvbase, size_t tile_mul, size_t tile_add, int num_blocks,
-                                        int row0, int row_step, int c, int j, int lane, int src_off, u32x4* ka,
-                                        u32x4* kb, u32x4* va, u32x4* vb, bool& oka, bool& okb) {
-  const int ea = tab[i], eb = has_b ? tab[i + 1] : 0;
-  oka = ea >= 0 && ea < num_blocks;
-  okb = eb >= 0 && eb < num_blocks;
-  const int phys = __builtin_amdgcn_readfirstlane(tab[blk_next]);
-  const uint8_t* src = kvbase + ((size_t)(phys >= 0 && phys < num_blocks ? phys : 0) * tile_mul + tile_add) * TB +
-                       src_off;
+// One iteration of the LDS ring: this lane's K operand chunks of the next
+// pair (slot at rk), its V operand chunks of the current pair (V rows at rv),
+// the direct-to-LDS copy of one tile of a later pair into wr (LPS rows of
+// 1 KiB: row k from src + k * 1024 to row row0 + row_step * k), and the table
+// entry tab[next] (the tile the next iteration copies).  Every LDS access goes
+// through the restrict parameters, so once inlined the compiler knows the copy
+// writes none of what the reads return; otherwise each read waits for every
+// copy in flight (vmcnt(0)) and the ring holds a single pair.
+template <int TB, int LPS, int KW4, int VQ, bool READ_V = true>
+__device__ __forceinline__ int ring_io(const uint8_t* __restrict__ rk, const uint8_t* __restrict__ rv,
+                                       uint8_t* __restrict__ wr, const int* __restrict__ tab, int next,
+                                       const uint8_t* __restrict__ src, int row0, int row_step, int c, int j, int lane,
+                                       u32x4* ka, u32x4* kb, u32x4* va, u32x4* vb) {
 #pragma unroll
   for (int w = 0; w < KW4; ++w) {
-    ka[w] = *reinterpret_cast<const u32x4*>(rd + ((4 * w + j) * kBlockSize + c) * 16);
-    kb[w] = *reinterpret_cast<const u32x4*>(rd + TB + ((4 * w + j) * kBlockSize + c) * 16);
+    ka[w] = *reinterpret_cast<const u32x4*>(rk + ((4 * w + j) * kBlockSize + c) * 16);
+    kb[w] = *reinterpret_cast<const u32x4*>(rk + TB + ((4 * w + j) * kBlockSize + c) * 16);
   }
   // Both are in lane order: lane l's 16 bytes of row r at r * 1024 + l * 16
   // (the copy of a V tile gathers each lane's chunk from where the pool keeps
   // it, so that these reads are conflict-free).
+  if constexpr (READ_V) {
 #pragma unroll
-  for (int g = 0; g < VQ; ++g) {
-    va[g] = *reinterpret_cast<const u32x4*>(rd + 2 * TB + (2 * g) * 1024 + lane * 16);
-    vb[g] = *reinterpret_cast<const u32x4*>(rd + 2 * TB + (2 * g + 1) * 1024 + lane * 16);
+    for (int g = 0; g < VQ; ++g) {
+      va[g] = *reinterpret_cast<const u32x4*>(rv + (2 * g) * 1024 + lane * 16);
+      vb[g] = *reinterpret_cast<const u32x4*>(rv + (2 * g + 1) * 1024 + lane * 16);
+    }
   }
+  const int e = READ_V ? tab[next] : 0;
 #pragma unroll
   for (int k = 0; k < LPS; ++k)
     __builtin_amdgcn_global_load_lds(src + k * 1024, (__attribute__((address_space(3))) void*)(wr + (row0 + row_step * k) * 1024),
                                      16, 0, 0);
+  return e;
+}
+
+// Scheduling hint for the rest of the basic block: N MFMAs, each followed by
+// up to V other vector-ALU instructions, so that one wave keeps the matrix
+// core and the VALU busy together.
+template <int N, int V>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
 }
 
 template <int KVT, int QT, int D, int CS>
@@ -300,6 +332,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   };
   constexpr std::false_type kA{};
   constexpr std::true_type kB{};
+  // Two probabilities as packed 16-bit PV operands, high parts and residuals.
+  auto pack_p = [](float f0, float f1, uint32_t& hw, uint32_t& lw) {
+    if constexpr (F16) {
+      const uint32_t h0 = f32_to_f16_bits(f0), h1 = f32_to_f16_bits(f1);
+      const uint32_t l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
+      const uint32_t l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
+      hw = h0 | (h1 << 16);
+      lw = l0 | (l1 << 16);
+    } else {
+      split_bf16_pair(f0, f1, hw, lw);
+    }
+  };
 
   // Loads of block i's tiles into half a or b of P (K and V separately, so a
   // step can refill K while it still uses V).  An entry outside the pool reads
@@ -410,8 +454,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   // The step's K scales (per-token formats) are taken before the refill overwrites them.
   auto qk_step = [&](Pair& P, f32x4 (&sacc)[NB][CS], f32x4 (&kscale)[NB], int i, bool has_b, bool refill) {
     bad |= !P.oka || (has_b && !P.okb);
+    mfma_phase(true);
     qk(P.ka, sacc[0]);
     qk(P.kb, sacc[1]);
+    mfma_phase(false);
     if constexpr (is_quantised(KVT)) {
       kscale[0] = P.ksa;
       kscale[1] = P.ksb;
@@ -510,14 +556,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           for (int w = 0; w < 2; ++w) {
             const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
             uint32_t hw, lw;
-            if constexpr (F16) {
-              const uint32_t h0 = f32_to_f16_bits(f0), h1 = f32_to_f16_bits(f1);
-              const uint32_t l0 = f32_to_f16_bits(f0 - f16_to_f32(h0));
-              const uint32_t l1 = f32_to_f16_bits(f1 - f16_to_f32(h1));
-              hw = h0 | (h1 << 16);
-              lw = l0 | (l1 << 16);
-            } else {
-              split_bf16_pair(f0, f1, hw, lw);
+            pack_p(f0, f1, hw, lw);
+            if constexpr (!F16) {
               if constexpr (BIAS)
                 p_run[cs] += (bf16_to_f32(hw & 0xffffu) + bf16_to_f32(lw & 0xffffu)) +
                              (bf16_to_f32(hw >> 16) + bf16_to_f32(lw >> 16));
@@ -540,6 +580,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     }
     // ---- O^T += V^T P^T per set, sharing the converted V operand
     if constexpr (!OP32) {
+      mfma_phase(true);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         u32x4 av;
@@ -557,6 +598,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           acc[cs][t] = mfma_k32v<F16>(av, u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t]);
         }
       }
+      mfma_phase(false);
     }
   };
   // An absent second block: defined (zero) operands; its keys are masked.
@@ -573,79 +615,233 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   constexpr std::integral_constant<int, 2> kAny{};
 
   if constexpr (STAGE) {
+    // Pair q (blocks 2q, 2q + 1 of the chunk) has slot q % NS: K of its first
+    // block, K of its second, then both V tiles by interleaved 1 KiB rows.  K
+    // runs one pair ahead of V: iteration p reads V(p) and K(p + 1), so that
+    // the QK MFMAs of pair p + 1 run beside the softmax VALU of pair p.  Wave 0
+    // copies the first block's K tile, wave 1 the second's, waves 2 and 3 the
+    // V tiles, each 1 KiB per instruction, byte for byte; in iteration p a wave
+    // sends the copy of pair p + lead (K: NS ahead, V: NS - 1 ahead), before
+    // the loop those of pairs 0 .. lead - 1.  Then the pair an iteration needs
+    // was sent NS - 1 iterations earlier and its slot's previous pair was last
+    // read an iteration earlier (every read of an iteration is consumed by its
+    // MFMAs before the next barrier).  Pairs past the chunk reload its last
+    // pair (their slots are never read), so every wave issues the same count
+    // and the waits below are exact.
+    const int lead = wave < 2 ? NS : NS - 1;
+    const uint8_t* kvb = wave < 2 ? kbase : vbase;
+    // Lane l copies the 16 bytes the operand reads of lane l need: a K row
+    // holds them in lane order already; in a V row lane (c, j)'s chunk sits
+    // at (4 c + j) * 16 (read there in lane order, a 16-byte read at a 64-byte
+    // stride would hit each LDS bank four times).
+    const int src_off = (wave < 2 ? lane : 4 * c + j) * 16;
+    const int row0 = wave < 2 ? 0 : (wave & 1);   // K tiles: rows 0, 1, ..; V tiles interleaved
+    const int row_step = wave < 2 ? 1 : 2;
     for (; c0 < n_blocks; c0 += kPfTab) {
       const int n = min(kPfTab, n_blocks - c0);
       for (int k = threadIdx.x; k < n; k += 256) s_tab[k] = trow[c0 + k];
       __syncthreads();                 // the ring is drained here: no copy in flight
       const int npairs = (n + 1) / 2;
-      // Slot p % NS receives pair p (blocks 2p, 2p + 1): wave 0 copies K of
-      // block 2p, wave 1 K of 2p + 1, wave 2 V of 2p, wave 3 V of 2p + 1, each
-      // 1 KiB of the tile per instruction, byte for byte.  V's 1 KiB rows of
-      // the two blocks alternate, so a lane's chunk of V_a and of V_b are 1 KiB
-      // apart.  Pairs past the chunk reload its last pair (their slots are
-      // never read), so every wave issues the same count and the waits below
-      // are exact.  An entry outside the pool loads block 0 (in bounds); the
-      // pair's compute marks the result bad.
-      // This wave's tile of pair p (pairs past the chunk: its last pair again,
-      // so every wave issues the same count) and its place in slot p % NS.
-      auto tile_blk = [&](int p) { return min(2 * min(p, npairs - 1) + (wave & 1), n - 1); };
-      auto tile_dst = [&](int p) { return s_ring + (p % NS) * SB + (wave < 2 ? wave * TB : 2 * TB); };
-      const uint8_t* kvb = wave < 2 ? kbase : vbase;
-      // Lane l copies the 16 bytes the operand reads of lane l need: a K row
-      // holds them in lane order already; in a V row lane (c, j)'s chunk sits
-      // at (4 c + j) * 16 (read there in lane order, a 16-byte read at a 64-byte
-      // stride would hit each LDS bank four times).
-      const int src_off = (wave < 2 ? lane : 4 * c + j) * 16;
-      const int row0 = wave < 2 ? 0 : (wave & 1);   // K tiles: rows 0, 1, ..; V tiles interleaved
-      const int row_step = wave < 2 ? 1 : 2;
-#pragma unroll
-      for (int p = 0; p < NS - 1; ++p) {
-        const int phys = __builtin_amdgcn_readfirstlane(s_tab[tile_blk(p)]);
-        const uint8_t* src = kvb + ((size_t)(phys >= 0 && phys < a.num_blocks ? phys : 0) * hkv + kvh) * TB + src_off;
-        uint8_t* dst = tile_dst(p);
+      {
+        // Every wave computes over every block of the chunk: an entry outside
+        // the pool (its copies read block 0 instead) makes the result NaN.
+        bool ok = true;
+        for (int k = lane; k < n; k += kWave) {
+          const int e = s_tab[k];
+          ok = ok && e >= 0 && e < a.num_blocks;
+        }
+        bad = bad || __builtin_amdgcn_ballot_w64(!ok) != 0ull;
+      }
+      auto tile_blk = [&](int q) { return min(2 * min(q, npairs - 1) + (wave & 1), n - 1); };
+      auto tile_src = [&](int phys) {
+        return kvb + ((size_t)(phys >= 0 && phys < a.num_blocks ? phys : 0) * hkv + kvh) * TB + src_off;
+      };
+      auto tile_dst = [&](int q) { return s_ring + (q % NS) * SB + (wave < 2 ? wave * TB : 2 * TB); };
+      for (int q = 0; q < lead; ++q) {
+        const uint8_t* src = tile_src(__builtin_amdgcn_readfirstlane(s_tab[tile_blk(q)]));
+        uint8_t* dst = tile_dst(q);
 #pragma unroll
         for (int k = 0; k < LPS; ++k)
           __builtin_amdgcn_global_load_lds(src + k * 1024,
                                            (__attribute__((address_space(3))) void*)(dst + (row0 + row_step * k) * 1024),
                                            16, 0, 0);
       }
-      // The first copies are waited for here, in the compiler's view too:
-      // left in flight into the loop, they would make it wait for all copies
-      // at every step.
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      // One pair: wait for its copies, take the operands from its slot, send
-      // the copy of pair p + NS - 1 into the slot of pair p - 1, compute.
-      // Every wave runs npairs steps (one barrier each), first the pairs all
-      // its columns see whole, then the rest: two loops rather than a branch
-      // per step, which would hold both bodies' registers at once.
-      auto step = [&](int p, auto mode) {
-        // this wave's copies of pair p have landed; after the barrier so have
-        // everyone's, and every wave has finished pair p - 1, whose slot the
-        // next copy overwrites (s_waitcnt through the builtin, so that the
-        // compiler's own wait counting knows what is still in flight)
+      // The table entry of the tile this wave copies in the next iteration.
+      int ent = s_tab[tile_blk(lead)];
+
+      u32x4 kn_a[KW / 4], kn_b[KW / 4];   // K operands of the next pair
+      f32x4 sacc[NB][CS];                 // S = K q^T of the current pair
+      float lmx[CS];                      // this lane's largest raw product of the current pair, per set
+      auto lane_max = [&](const f32x4 (&sx)[NB][CS], float (&m)[CS]) {
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            mx = vmax(mx, vmax(vmax(sx[b][cs][0], sx[b][cs][1]), vmax(sx[b][cs][2], sx[b][cs][3])));
+          m[cs] = mx;
+        }
+      };
+
+      // Iteration head: wait for this wave's copies of the pair needed now,
+      // barrier (everyone's have landed, everyone is done with the previous
+      // iteration), then the LDS reads and the next copy.
+      auto ring_head = [&](int p, u32x4* va, u32x4* vb, auto read_v) {
+        constexpr bool RV = decltype(read_v)::value;
         static_assert(LPS * (NS - 2) < 16, "vmcnt field");
         __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 2)));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        const int i = 2 * p;
-        const bool has_b = i + 1 < n;
+        const uint8_t* src = tile_src(__builtin_amdgcn_readfirstlane(ent));
+        const int e = ring_io<TB, LPS, KW / 4, VQ, RV>(s_ring + ((p + 1) % NS) * SB, s_ring + (p % NS) * SB + 2 * TB,
+                                                       tile_dst(p + lead), s_tab, tile_blk(p + 1 + lead), src, row0,
+                                                       row_step, c, j, lane, kn_a, kn_b, va, vb);
+        if constexpr (RV) ent = e;
+      };
+      // QK of pair 0, its K operands loaded from the pool here (an LDS read
+      // of the ring outside the loops makes the compiler wait for every copy
+      // in flight before each read of the ring inside them).
+      {
+        const int e0 = __builtin_amdgcn_readfirstlane(s_tab[0]);
+        const int e1 = __builtin_amdgcn_readfirstlane(s_tab[min(1, n - 1)]);
+        const uint8_t* k0 = kbase + ((size_t)(e0 >= 0 && e0 < a.num_blocks ? e0 : 0) * hkv + kvh) * TB;
+        const uint8_t* k1 = kbase + ((size_t)(e1 >= 0 && e1 < a.num_blocks ? e1 : 0) * hkv + kvh) * TB;
+#pragma unroll
+        for (int w = 0; w < KW / 4; ++w) {
+          kn_a[w] = *reinterpret_cast<const u32x4*>(k0 + ((4 * w + j) * kBlockSize + c) * 16);
+          kn_b[w] = *reinterpret_cast<const u32x4*>(k1 + ((4 * w + j) * kBlockSize + c) * 16);
+        }
+        qk(kn_a, sacc[0]);
+        qk(kn_b, sacc[1]);
+        lane_max(sacc, lmx);
+      }
+      // The first copies are waited for here, in the compiler's view too:
+      // left in flight into the loop, they would make it wait for all copies
+      // at every step.
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      // Pairs every column sees whole, software-pipelined: the running max of
+      // pair p is checked first (this lane's largest product against the
+      // rescale threshold; a rescale, rare, takes the column's max), then one
+      // basic block interleaves the probabilities of each column set with the
+      // QK MFMAs of pair p + 1 and the PV MFMAs of the previous set.
+      auto pipe_step = [&](int p) {
+        bool any = false;
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) any = any || lmx[cs] * sl2 > m_run[cs] + kPfRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(any) != 0ull) {
+#pragma unroll
+          for (int cs = 0; cs < CS; ++cs) {
+            const float mb = (row_vmax4(lmx[cs]) - qbias[cs]) * sl2;
+            const bool need = mb > m_run[cs] + kPfRescaleSlack;
+            const float m_new = need ? mb : m_run[cs];
+            const float alpha = m_new == m_run[cs] ? 1.f : fast_exp2(m_run[cs] - m_new);
+            l_run[cs] *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[cs][t] *= alpha;
+            m_run[cs] = m_new;
+          }
+        }
+        // From here on one basic block: the LDS reads, the copy, then the
+        // MFMAs interleaved with the VALU work.
+        u32x4 va[VQ], vb[VQ];
+        ring_head(p, va, vb, std::true_type{});
+        __builtin_amdgcn_sched_barrier(0);   // the reads and the copy go out first, in their order
+        uint32_t ph[CS][2 * NB], pl[CS][2 * NB];
+        auto probs = [&](int cs) {
+          const float mref = m_run[cs] == -INFINITY ? 0.f : m_run[cs];
+          const float off = -(qbias[cs] * sl2) - mref;   // exponent = raw * |f| + off
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            float pr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(__builtin_fmaf(sacc[b][cs][e], sl2, off));
+            l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+            for (int w = 0; w < 2; ++w) pack_p(pr[2 * w], pr[2 * w + 1], ph[cs][2 * b + w], pl[cs][2 * b + w]);
+          }
+        };
+        // PV of one column set, two tiles at a time (high parts, then low
+        // parts): an MFMA never waits on the one just before it.
+        auto pv = [&](int cs) {
+#pragma unroll
+          for (int t = 0; t < NT; t += 2) {
+            u32x4 av[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              av[u] = u32x4{va[(2 * (t + u)) / 4][(2 * (t + u)) % 4], va[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4],
+                            vb[(2 * (t + u)) / 4][(2 * (t + u)) % 4], vb[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4]};
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              acc[cs][t + u] = mfma_k32v<F16>(av[u], u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, acc[cs][t + u]);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              acc[cs][t + u] = mfma_k32v<F16>(av[u], u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t + u]);
+          }
+        };
+        // QK of the next pair, both blocks' chains interleaved.
+        f32x4 snew[NB][CS];
+        auto qk_next = [&]() {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) snew[b][cs] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int st = 0; st < DPL / 8; ++st) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const u32x4 kq = b ? kn_b[st] : kn_a[st];
+              const uint32_t av[4] = {kq[0], kq[1], kq[2], kq[3]};
+#pragma unroll
+              for (int cs = 0; cs < CS; ++cs) {
+                snew[b][cs] = mfma_k32<F16>(av, &qhi[cs][4 * st], snew[b][cs]);
+                if constexpr (QSPLIT) snew[b][cs] = mfma_k32<F16>(av, &qlo[cs][4 * st], snew[b][cs]);
+              }
+            }
+          }
+        };
+        probs(0);
+        qk_next();
+#pragma unroll
+        for (int cs = 1; cs < CS; ++cs) {
+          probs(cs);
+          pv(cs - 1);
+        }
+        lane_max(snew, lmx);
+        pv(CS - 1);
+        constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
+        constexpr int kPvMfma = 2 * NT;
+        __builtin_amdgcn_sched_group_barrier(0x002, PKV_PREFILL_ILV_LEAD, 0);
+        interleave_mfma<kQkMfma, PKV_PREFILL_ILV_QK>();
+        if constexpr (CS > 1) interleave_mfma<kPvMfma * (CS - 1), PKV_PREFILL_ILV_PV>();
+        interleave_mfma<kPvMfma, 1>();
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int cs = 0; cs < CS; ++cs) sacc[b][cs] = snew[b][cs];
+      };
+      // The rest (pairs across some column's causal limit, and the chunk's
+      // last pair): masked softmax and PV of pair p, then QK of pair p + 1
+      // (after the last pair, of the reloaded last pair: discarded).
+      auto any_step = [&](int p) {
         Pair P;
-        ring_io<TB, LPS, KW / 4, VQ>(s_tab, s_ring + (p % NS) * SB, tile_dst(p + NS - 1), i, has_b,
-                                     tile_blk(p + NS - 1), kvb, hkv, kvh, a.num_blocks, row0, row_step, c, j, lane, src_off,
-                                     P.ka, P.kb, P.va, P.vb, P.oka, P.okb);
-        if (!has_b) clear_b(P);
-        f32x4 sacc[NB][CS];
+        ring_head(p, P.va, P.vb, std::true_type{});
         f32x4 kscale[NB] = {};
-        qk_step(P, sacc, kscale, i, has_b, false);
-        softmax_pv(P, sacc, kscale, i, has_b, mode);
+        softmax_pv(P, sacc, kscale, 2 * p, 2 * p + 1 < n, kAny);
+        mfma_phase(true);
+        qk(kn_a, sacc[0]);
+        qk(kn_b, sacc[1]);
+        mfma_phase(false);
       };
       // pairs p with both blocks below the wave's causal limits: (c0 + 2p + 2) * 16 <= all_visible
       const int p_full = min(npairs, max(0, (all_visible / kBlockSize - c0) / 2));
+      const int p_pipe = min(p_full, npairs - 1);   // the pipelined step needs a next pair
       int p = 0;
 #pragma unroll 1
-      for (; p < p_full; ++p) step(p, kFull);
+      for (; p < p_pipe; ++p) pipe_step(p);
 #pragma unroll 1
-      for (; p < npairs; ++p) step(p, kAny);
+      for (; p < npairs; ++p) any_step(p);
       __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies too
       __syncthreads();                 // s_tab and the ring are rewritten by the next chunk
     }
