@@ -64,6 +64,19 @@ __device__ __forceinline__ float row_vmax4(float x) {
   return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// Two floats as one word of f16 MFMA operands, each rounded to nearest even
+// (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2_t));
+}
+// A word of two bf16 values as two f16 values: exact over f16's normal range
+// (bf16 carries 8 significant bits, f16 11), rounded to nearest below 2^-14,
+// and +-inf above 65504 (round-to-nearest overflow).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
 namespace {
 
 constexpr int kPfWaves = 4;
@@ -90,12 +103,9 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #ifndef PKV_PREFILL_ILV_PV
 #define PKV_PREFILL_ILV_PV 4              // ... after each PV MFMA of a column set but the last
 #endif
-
-
-
-namespace {
-
-}  // namespace
+#ifndef PKV_PREFILL_PV16
+#define PKV_PREFILL_PV16 1                // 16-bit pools: PV as f16 x f16 with one probability operand
+#endif
 
 // One iteration of the LDS ring: this lane's K operand chunks of the next
 // pair (slot at rk), its V operand chunks of the current pair (V rows at rv),
@@ -105,11 +115,30 @@ namespace {
 // through the restrict parameters, so once inlined the compiler knows the copy
 // writes none of what the reads return; otherwise each read waits for every
 // copy in flight (vmcnt(0)) and the ring holds a single pair.
-template <int TB, int LPS, int KW4, int VQ, bool READ_V = true>
+//
+// With CONV, this wave's share of a later pair's V rows (at cv: rows wave,
+// wave + 4, ..) is rewritten from bf16 to f16 in place.
+template <int VQ>
+__device__ __forceinline__ void convert_v_rows(uint8_t* __restrict__ cv, int wave, int lane) {
+  constexpr int CR = 2 * VQ / 4;   // 2 * VQ rows of 1 KiB, shared by the 4 waves
+  u32x4 x[CR];
+#pragma unroll
+  for (int k = 0; k < CR; ++k) x[k] = *reinterpret_cast<const u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16);
+#pragma unroll
+  for (int k = 0; k < CR; ++k) {
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = bf16x2_to_f16x2(x[k][e]);
+    *reinterpret_cast<u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16) = y;
+  }
+}
+
+template <int TB, int LPS, int KW4, int VQ, bool READ_V, bool CONV, class Body>
 __device__ __forceinline__ int ring_io(const uint8_t* __restrict__ rk, const uint8_t* __restrict__ rv,
                                        uint8_t* __restrict__ wr, const int* __restrict__ tab, int next,
                                        const uint8_t* __restrict__ src, int row0, int row_step, int c, int j, int lane,
-                                       u32x4* ka, u32x4* kb, u32x4* va, u32x4* vb) {
+                                       u32x4* ka, u32x4* kb, u32x4* va, u32x4* vb, uint8_t* __restrict__ cv,
+                                       int wave, Body&& body) {
 #pragma unroll
   for (int w = 0; w < KW4; ++w) {
     ka[w] = *reinterpret_cast<const u32x4*>(rk + ((4 * w + j) * kBlockSize + c) * 16);
@@ -126,10 +155,35 @@ __device__ __forceinline__ int ring_io(const uint8_t* __restrict__ rk, const uin
     }
   }
   const int e = READ_V ? tab[next] : 0;
+  // The rewrite's reads go out last (the operand reads are waited for first)
+  // and before the copy (a ring read after a copy in the same iteration gets
+  // a wait for every copy in flight); its arithmetic and stores come after
+  // the step's work (body), beside its last MFMAs.
+  constexpr int CR = 2 * VQ / 4;                 // 2 * VQ V rows of 1 KiB, shared by the 4 waves
+  u32x4 x[CONV ? CR : 1];
+  if constexpr (CONV) {
 #pragma unroll
-  for (int k = 0; k < LPS; ++k)
-    __builtin_amdgcn_global_load_lds(src + k * 1024, (__attribute__((address_space(3))) void*)(wr + (row0 + row_step * k) * 1024),
-                                     16, 0, 0);
+    for (int k = 0; k < CR; ++k) x[k] = *reinterpret_cast<const u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16);
+  }
+  auto copy = [&]() {
+#pragma unroll
+    for (int k = 0; k < LPS; ++k)
+      __builtin_amdgcn_global_load_lds(src + k * 1024,
+                                       (__attribute__((address_space(3))) void*)(wr + (row0 + row_step * k) * 1024), 16, 0, 0);
+  };
+  if constexpr (!CONV) copy();
+  body();
+  if constexpr (CONV) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < CR; ++k) {
+      u32x4 y;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) y[e2] = bf16x2_to_f16x2(x[k][e2]);
+      *reinterpret_cast<u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16) = y;
+    }
+    copy();
+  }
   return e;
 }
 
@@ -173,6 +227,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   constexpr int LPS = TB / 1024;                 // direct-to-LDS loads per wave and slot
   __shared__ int s_tab_all[STAGE ? 1 : kPfWaves][kPfTab];
   __shared__ __attribute__((aligned(16))) uint8_t s_ring[STAGE ? NS * SB : 16];
+  __shared__ int s_redo;                         // f16 PV: some accumulator came out non-finite
 
   const int hq = a.num_q_heads;
   const int hkv = a.num_kv_heads;
@@ -478,8 +533,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   //  kAny    also keys past the context: their V values are zeroed.
   // Only kAny changes P, so the branch between kFull and kCausal in the loop
   // joins with the same operand registers.
-  auto softmax_pv = [&](Pair& P, f32x4 (&sacc)[NB][CS], const f32x4 (&kscale)[NB], int i, bool has_b, auto mode) {
+  // pvf (16-bit pools read from the LDS ring only): the V operands hold f16
+  // values, and each probability is one f16 operand (PV error within 2^-12 of
+  // the output's scale), so one MFMA per tile instead of the high/low pair.
+  auto softmax_pv = [&](Pair& P, f32x4 (&sacc)[NB][CS], const f32x4 (&kscale)[NB], int i, bool has_b, auto mode,
+                        auto pvf) {
     constexpr int MODE = decltype(mode)::value;
+    constexpr bool PVF = decltype(pvf)::value;
     constexpr bool FULL = MODE == 0;
     constexpr bool TAIL = MODE == 2;
     constexpr bool RAWMAX = FULL && !is_quantised(KVT);
@@ -555,9 +615,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
           for (int w = 0; w < 2; ++w) {
             const float f0 = pv[2 * w], f1 = pv[2 * w + 1];
-            uint32_t hw, lw;
-            pack_p(f0, f1, hw, lw);
-            if constexpr (!F16) {
+            uint32_t hw, lw = 0;
+            if constexpr (PVF) hw = pack_f16x2(f0, f1);
+            else pack_p(f0, f1, hw, lw);
+            if constexpr (!F16 && !PVF) {
               if constexpr (BIAS)
                 p_run[cs] += (bf16_to_f32(hw & 0xffffu) + bf16_to_f32(lw & 0xffffu)) +
                              (bf16_to_f32(hw >> 16) + bf16_to_f32(lw >> 16));
@@ -594,8 +655,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         }
 #pragma unroll
         for (int cs = 0; cs < CS; ++cs) {
-          acc[cs][t] = mfma_k32v<F16>(av, u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, acc[cs][t]);
-          acc[cs][t] = mfma_k32v<F16>(av, u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t]);
+          if constexpr (PVF) {
+            acc[cs][t] = mfma_k32v<true>(av, u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, acc[cs][t]);
+          } else {
+            acc[cs][t] = mfma_k32v<F16>(av, u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, acc[cs][t]);
+            acc[cs][t] = mfma_k32v<F16>(av, u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t]);
+          }
         }
       }
       mfma_phase(false);
@@ -614,7 +679,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   constexpr std::integral_constant<int, 1> kCausal{};
   constexpr std::integral_constant<int, 2> kAny{};
 
+  // 16-bit pools: PV in f16 first (bf16 V rewritten to f16 in the ring); a V
+  // value beyond f16's range turns into inf there and leaves an accumulator
+  // non-finite, and then the workgroup computes again with the high/low
+  // probability split, which is also what a non-finite q, K or V gives.
+  constexpr bool PV16 = STAGE && PKV_PREFILL_PV16;
+  if constexpr (PV16) {
+    if (threadIdx.x == 0) s_redo = 0;   // ordered before its stores by the first barrier of the pass
+  }
   if constexpr (STAGE) {
+  auto stage_pass = [&](auto pvf) {
+    constexpr bool PVF = decltype(pvf)::value;
+    constexpr bool CONV = PVF && !F16;   // the V copies are bf16: rewritten to f16 in the ring
     // Pair q (blocks 2q, 2q + 1 of the chunk) has slot q % NS: K of its first
     // block, K of its second, then both V tiles by interleaved 1 KiB rows.  K
     // runs one pair ahead of V: iteration p reads V(p) and K(p + 1), so that
@@ -637,7 +713,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     const int src_off = (wave < 2 ? lane : 4 * c + j) * 16;
     const int row0 = wave < 2 ? 0 : (wave & 1);   // K tiles: rows 0, 1, ..; V tiles interleaved
     const int row_step = wave < 2 ? 1 : 2;
-    for (; c0 < n_blocks; c0 += kPfTab) {
+    for (c0 = 0; c0 < n_blocks; c0 += kPfTab) {
       const int n = min(kPfTab, n_blocks - c0);
       for (int k = threadIdx.x; k < n; k += 256) s_tab[k] = trow[c0 + k];
       __syncthreads();                 // the ring is drained here: no copy in flight
@@ -686,16 +762,22 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       // Iteration head: wait for this wave's copies of the pair needed now,
       // barrier (everyone's have landed, everyone is done with the previous
       // iteration), then the LDS reads and the next copy.
-      auto ring_head = [&](int p, u32x4* va, u32x4* vb, auto read_v) {
+      auto ring_head = [&](int p, u32x4* va, u32x4* vb, auto read_v, auto&& body) {
         constexpr bool RV = decltype(read_v)::value;
-        static_assert(LPS * (NS - 2) < 16, "vmcnt field");
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (LPS * (NS - 2)));
+        // With CONV, iteration p also rewrites V(p + 1), so the copies of
+        // V(p + 1) must have landed here: one iteration's copies in flight
+        // instead of two, and this wave's rewrite of the previous iteration
+        // is finished before the barrier (lgkmcnt(0)).
+        constexpr int kVm = LPS * (NS - (CONV ? 3 : 2));
+        static_assert(kVm < 16 && NS >= 3, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt((CONV ? 0x0070 : 0x0F70) | kVm);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const uint8_t* src = tile_src(__builtin_amdgcn_readfirstlane(ent));
-        const int e = ring_io<TB, LPS, KW / 4, VQ, RV>(s_ring + ((p + 1) % NS) * SB, s_ring + (p % NS) * SB + 2 * TB,
-                                                       tile_dst(p + lead), s_tab, tile_blk(p + 1 + lead), src, row0,
-                                                       row_step, c, j, lane, kn_a, kn_b, va, vb);
+        const int e = ring_io<TB, LPS, KW / 4, VQ, RV, CONV>(
+            s_ring + ((p + 1) % NS) * SB, s_ring + (p % NS) * SB + 2 * TB, tile_dst(p + lead), s_tab,
+            tile_blk(p + 1 + lead), src, row0, row_step, c, j, lane, kn_a, kn_b, va, vb,
+            s_ring + ((p + 1) % NS) * SB + 2 * TB, wave, body);
         if constexpr (RV) ent = e;
       };
       // QK of pair 0, its K operands loaded from the pool here (an LDS read
@@ -721,6 +803,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      if constexpr (CONV) convert_v_rows<VQ>(s_ring + 2 * TB, wave, lane);   // V(0); published by the first iteration's barrier
       // Pairs every column sees whole, software-pipelined: the running max of
       // pair p is checked first (this lane's largest product against the
       // rescale threshold; a rescale, rare, takes the column's max), then one
@@ -744,10 +827,8 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           }
         }
         // From here on one basic block: the LDS reads, the copy, then the
-        // MFMAs interleaved with the VALU work.
+        // MFMAs interleaved with the VALU work (the body below).
         u32x4 va[VQ], vb[VQ];
-        ring_head(p, va, vb, std::true_type{});
-        __builtin_amdgcn_sched_barrier(0);   // the reads and the copy go out first, in their order
         uint32_t ph[CS][2 * NB], pl[CS][2 * NB];
         auto probs = [&](int cs) {
           const float mref = m_run[cs] == -INFINITY ? 0.f : m_run[cs];
@@ -759,7 +840,10 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
             for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(__builtin_fmaf(sacc[b][cs][e], sl2, off));
             l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
-            for (int w = 0; w < 2; ++w) pack_p(pr[2 * w], pr[2 * w + 1], ph[cs][2 * b + w], pl[cs][2 * b + w]);
+            for (int w = 0; w < 2; ++w) {
+              if constexpr (PVF) ph[cs][2 * b + w] = pack_f16x2(pr[2 * w], pr[2 * w + 1]);
+              else pack_p(pr[2 * w], pr[2 * w + 1], ph[cs][2 * b + w], pl[cs][2 * b + w]);
+            }
           }
         };
         // PV of one column set, two tiles at a time (high parts, then low
@@ -774,10 +858,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
                             vb[(2 * (t + u)) / 4][(2 * (t + u)) % 4], vb[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4]};
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-              acc[cs][t + u] = mfma_k32v<F16>(av[u], u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, acc[cs][t + u]);
+              acc[cs][t + u] = mfma_k32v<F16 || PVF>(av[u], u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]},
+                                                    acc[cs][t + u]);
+            if constexpr (!PVF) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-              acc[cs][t + u] = mfma_k32v<F16>(av[u], u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t + u]);
+              for (int u = 0; u < 2; ++u)
+                acc[cs][t + u] = mfma_k32v<F16>(av[u], u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t + u]);
+            }
           }
         };
         // QK of the next pair, both blocks' chains interleaved.
@@ -801,21 +888,24 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
             }
           }
         };
-        probs(0);
-        qk_next();
+        ring_head(p, va, vb, std::true_type{}, [&]() {
+          __builtin_amdgcn_sched_barrier(0);   // the reads and the copy go out first, in their order
+          probs(0);
+          qk_next();
 #pragma unroll
-        for (int cs = 1; cs < CS; ++cs) {
-          probs(cs);
-          pv(cs - 1);
-        }
-        lane_max(snew, lmx);
-        pv(CS - 1);
-        constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
-        constexpr int kPvMfma = 2 * NT;
-        __builtin_amdgcn_sched_group_barrier(0x002, PKV_PREFILL_ILV_LEAD, 0);
-        interleave_mfma<kQkMfma, PKV_PREFILL_ILV_QK>();
-        if constexpr (CS > 1) interleave_mfma<kPvMfma * (CS - 1), PKV_PREFILL_ILV_PV>();
-        interleave_mfma<kPvMfma, 1>();
+          for (int cs = 1; cs < CS; ++cs) {
+            probs(cs);
+            pv(cs - 1);
+          }
+          lane_max(snew, lmx);
+          pv(CS - 1);
+          constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
+          constexpr int kPvMfma = PVF ? NT : 2 * NT;
+          __builtin_amdgcn_sched_group_barrier(0x002, PKV_PREFILL_ILV_LEAD, 0);
+          interleave_mfma<kQkMfma, PKV_PREFILL_ILV_QK>();
+          if constexpr (CS > 1) interleave_mfma<kPvMfma * (CS - 1), PKV_PREFILL_ILV_PV>();
+          interleave_mfma<kPvMfma, 1>();
+        });
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -826,13 +916,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       // (after the last pair, of the reloaded last pair: discarded).
       auto any_step = [&](int p) {
         Pair P;
-        ring_head(p, P.va, P.vb, std::true_type{});
         f32x4 kscale[NB] = {};
-        softmax_pv(P, sacc, kscale, 2 * p, 2 * p + 1 < n, kAny);
-        mfma_phase(true);
-        qk(kn_a, sacc[0]);
-        qk(kn_b, sacc[1]);
-        mfma_phase(false);
+        ring_head(p, P.va, P.vb, std::true_type{}, [&]() {
+          softmax_pv(P, sacc, kscale, 2 * p, 2 * p + 1 < n, kAny, pvf);
+          mfma_phase(true);
+          qk(kn_a, sacc[0]);
+          qk(kn_b, sacc[1]);
+          mfma_phase(false);
+        });
       };
       // pairs p with both blocks below the wave's causal limits: (c0 + 2p + 2) * 16 <= all_visible
       const int p_full = min(npairs, max(0, (all_visible / kBlockSize - c0) / 2));
@@ -845,6 +936,34 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);   // the padding copies too
       __syncthreads();                 // s_tab and the ring are rewritten by the next chunk
     }
+  };
+  if constexpr (PV16) {
+    stage_pass(std::true_type{});
+    bool fin = true;
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      fin &= __builtin_isfinite(l_run[cs]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fin &= __builtin_isfinite(acc[cs][t][e]);
+    }
+    if (__builtin_amdgcn_ballot_w64(!fin) != 0ull) s_redo = 1;
+    __syncthreads();
+    if (s_redo) {
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) {
+        m_run[cs] = -INFINITY;
+        l_run[cs] = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[cs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      bad = !seq_ok;
+      stage_pass(std::false_type{});
+    }
+  } else {
+    stage_pass(std::false_type{});
+  }
   } else {
   for (; c0 < n_blocks; c0 += kPfTab) {
     const int n = min(kPfTab, n_blocks - c0);
@@ -891,7 +1010,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         f32x4 s_next[NB][CS];
         f32x4 k_next[NB] = {};
         qk_step(P, s_next, k_next, i + 2, true, true);    // QK of pair i + 2; K of pair i + 4 requested
-        softmax_pv(P, sacc, kscale, i, true, kFull);      // pair i with its V
+        softmax_pv(P, sacc, kscale, i, true, kFull, std::false_type{});      // pair i with its V
         load_v(P, kA, i + 2);
         load_v(P, kB, i + 3);
 #pragma unroll
@@ -901,7 +1020,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           for (int cs = 0; cs < CS; ++cs) sacc[b][cs] = s_next[b][cs];
         }
       }
-      softmax_pv(P, sacc, kscale, i, true, kFull);
+      softmax_pv(P, sacc, kscale, i, true, kFull, std::false_type{});
       load_v(P, kA, i + 2);
       load_v(P, kB, i + 3);
       i += 2;
@@ -909,14 +1028,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll 1
     for (; i + 3 < n; i += 2) {
       qk_step(P, sacc, kscale, i, true, true);
-      softmax_pv(P, sacc, kscale, i, true, kCausal);
+      softmax_pv(P, sacc, kscale, i, true, kCausal, std::false_type{});
       load_v(P, kA, i + 2);
       load_v(P, kB, i + 3);
     }
     const int rem = n - i;        // 0..3 blocks left; P holds blocks i, i + 1 where they exist
     if (rem >= 2) {
       qk_step(P, sacc, kscale, i, true, false);
-      softmax_pv(P, sacc, kscale, i, true, kAny);
+      softmax_pv(P, sacc, kscale, i, true, kAny, std::false_type{});
     }
     if (rem % 2) {                // one block left over: paired with an absent one
       if (rem == 3) {
@@ -926,7 +1045,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       clear_b(P);
       const int il = rem == 3 ? i + 2 : i;
       qk_step(P, sacc, kscale, il, false, false);
-      softmax_pv(P, sacc, kscale, il, false, kAny);
+      softmax_pv(P, sacc, kscale, il, false, kAny, std::false_type{});
     }
     __builtin_amdgcn_wave_barrier();   // the next chunk rewrites this wave's s_tab
   }
