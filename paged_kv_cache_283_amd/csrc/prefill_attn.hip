@@ -116,27 +116,49 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 // writes none of what the reads return; otherwise each read waits for every
 // copy in flight (vmcnt(0)) and the ring holds a single pair.
 //
-// With CONV, this wave's share of a later pair's V rows (at cv: rows wave,
-// wave + 4, ..) is rewritten from bf16 to f16 in place.
+// With CONV, a later pair's V rows are rewritten in place from bf16 to f16
+// and regrouped: rows 2g and 2g + 1 hold, per lane, chunk g of the first
+// block's V tile (words 0-1: tile 2g, 2-3: tile 2g + 1) and of the second's;
+// afterwards row t holds tile t's whole PV operand (first block's two words,
+// then the second's), so the operand is one 16-byte read.  Wave w regroups
+// chunk w (chunks past VQ: none).
+__device__ __forceinline__ void regroup_v_f16(const u32x4& xa, const u32x4& xb, u32x4& t0, u32x4& t1) {
+  t0 = u32x4{bf16x2_to_f16x2(xa[0]), bf16x2_to_f16x2(xa[1]), bf16x2_to_f16x2(xb[0]), bf16x2_to_f16x2(xb[1])};
+  t1 = u32x4{bf16x2_to_f16x2(xa[2]), bf16x2_to_f16x2(xa[3]), bf16x2_to_f16x2(xb[2]), bf16x2_to_f16x2(xb[3])};
+}
 template <int VQ>
 __device__ __forceinline__ void convert_v_rows(uint8_t* __restrict__ cv, int wave, int lane) {
-  constexpr int CR = 2 * VQ / 4;   // 2 * VQ rows of 1 KiB, shared by the 4 waves
-  u32x4 x[CR];
-#pragma unroll
-  for (int k = 0; k < CR; ++k) x[k] = *reinterpret_cast<const u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16);
-#pragma unroll
-  for (int k = 0; k < CR; ++k) {
-    u32x4 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = bf16x2_to_f16x2(x[k][e]);
-    *reinterpret_cast<u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16) = y;
+  if (VQ >= 4 || wave < VQ) {
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(cv + (2 * wave) * 1024 + lane * 16);
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(cv + (2 * wave + 1) * 1024 + lane * 16);
+    u32x4 t0, t1;
+    regroup_v_f16(xa, xb, t0, t1);
+    *reinterpret_cast<u32x4*>(cv + (2 * wave) * 1024 + lane * 16) = t0;
+    *reinterpret_cast<u32x4*>(cv + (2 * wave + 1) * 1024 + lane * 16) = t1;
   }
+}
+
+// Direct-to-LDS copy of one K or V tile (LPS rows of 1 KiB; row k of the tile
+// at base + k * 1024, lane l's 16 bytes from off + k * 1024, to LDS row
+// row0 + row_step * k at dst).  A buffer load with the tile as its range: the
+// compiler treats the global (flat-encoded) form as a possible LDS access that
+// returns out of order, and then waits for every LDS read at the first use of
+// one while a copy is in flight (always, in the ring).
+template <int TB, int LPS>
+__device__ __forceinline__ void copy_tile(const uint8_t* base, int off, uint8_t* __restrict__ dst, int row0,
+                                          int row_step) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, TB, 0x00020000);
+#pragma unroll
+  for (int k = 0; k < LPS; ++k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (row0 + row_step * k) * 1024),
+                                             16, off + k * 1024, 0, 0, 0);
 }
 
 template <int TB, int LPS, int KW4, int VQ, bool READ_V, bool CONV, class Body>
 __device__ __forceinline__ int ring_io(const uint8_t* __restrict__ rk, const uint8_t* __restrict__ rv,
                                        uint8_t* __restrict__ wr, const int* __restrict__ tab, int next,
-                                       const uint8_t* __restrict__ src, int row0, int row_step, int c, int j, int lane,
+                                       const uint8_t* __restrict__ src, int src_off, int row0, int row_step, int c,
+                                       int j, int lane,
                                        u32x4* ka, u32x4* kb, u32x4* va, u32x4* vb, uint8_t* __restrict__ cv,
                                        int wave, Body&& body) {
 #pragma unroll
@@ -147,40 +169,47 @@ __device__ __forceinline__ int ring_io(const uint8_t* __restrict__ rk, const uin
   // Both are in lane order: lane l's 16 bytes of row r at r * 1024 + l * 16
   // (the copy of a V tile gathers each lane's chunk from where the pool keeps
   // it, so that these reads are conflict-free).
-  if constexpr (READ_V) {
+  auto read_v = [&](u32x4* dst, int parity) {
 #pragma unroll
-    for (int g = 0; g < VQ; ++g) {
-      va[g] = *reinterpret_cast<const u32x4*>(rv + (2 * g) * 1024 + lane * 16);
-      vb[g] = *reinterpret_cast<const u32x4*>(rv + (2 * g + 1) * 1024 + lane * 16);
-    }
-  }
-  const int e = READ_V ? tab[next] : 0;
-  // The rewrite's reads go out last (the operand reads are waited for first)
-  // and before the copy (a ring read after a copy in the same iteration gets
-  // a wait for every copy in flight); its arithmetic and stores come after
-  // the step's work (body), beside its last MFMAs.
-  constexpr int CR = 2 * VQ / 4;                 // 2 * VQ V rows of 1 KiB, shared by the 4 waves
-  u32x4 x[CONV ? CR : 1];
-  if constexpr (CONV) {
-#pragma unroll
-    for (int k = 0; k < CR; ++k) x[k] = *reinterpret_cast<const u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16);
-  }
-  auto copy = [&]() {
-#pragma unroll
-    for (int k = 0; k < LPS; ++k)
-      __builtin_amdgcn_global_load_lds(src + k * 1024,
-                                       (__attribute__((address_space(3))) void*)(wr + (row0 + row_step * k) * 1024), 16, 0, 0);
+    for (int g = 0; g < VQ; ++g) dst[g] = *reinterpret_cast<const u32x4*>(rv + (2 * g + parity) * 1024 + lane * 16);
   };
-  if constexpr (!CONV) copy();
-  body();
-  if constexpr (CONV) {
+  auto copy = [&]() { copy_tile<TB, LPS>(src, src_off, wr, row0, row_step); };
+  int e = 0;
+  if constexpr (!CONV) {
+    if constexpr (READ_V) {
+      read_v(va, 0);
+      read_v(vb, 1);
+      e = tab[next];
+    }
+    copy();
+    __builtin_amdgcn_sched_barrier(0);   // the reads and the copy go out first, in their order
+    body();
+  } else {
+    // Half the V reads go out with the K reads; the other half, the table
+    // entry and the rewrite's reads go out inside the step's work (body,
+    // whose scheduling hints place them after most of the QK MFMAs), so that
+    // no more than 15 LDS reads are ever in flight (past that count the
+    // first operand cannot be waited for alone: the wait is for all).  Every
+    // ring access precedes the copy, issued last (a ring access after a copy
+    // in the same iteration gets a wait for every copy in flight), and the
+    // rewrite's arithmetic and stores follow the step's work.
+    const bool conv_wave = VQ >= 4 || wave < VQ;
+    u32x4 xa, xb;
+    read_v(va, 0);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < CR; ++k) {
-      u32x4 y;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) y[e2] = bf16x2_to_f16x2(x[k][e2]);
-      *reinterpret_cast<u32x4*>(cv + (wave + 4 * k) * 1024 + lane * 16) = y;
+    read_v(vb, 1);
+    e = tab[next];
+    if (conv_wave) {
+      xa = *reinterpret_cast<const u32x4*>(cv + (2 * wave) * 1024 + lane * 16);
+      xb = *reinterpret_cast<const u32x4*>(cv + (2 * wave + 1) * 1024 + lane * 16);
+    }
+    body();
+    __builtin_amdgcn_sched_barrier(0);
+    if (conv_wave) {
+      u32x4 t0, t1;
+      regroup_v_f16(xa, xb, t0, t1);
+      *reinterpret_cast<u32x4*>(cv + (2 * wave) * 1024 + lane * 16) = t0;
+      *reinterpret_cast<u32x4*>(cv + (2 * wave + 1) * 1024 + lane * 16) = t1;
     }
     copy();
   }
@@ -540,6 +569,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
                         auto pvf) {
     constexpr int MODE = decltype(mode)::value;
     constexpr bool PVF = decltype(pvf)::value;
+    constexpr bool RL = PVF && !F16;   // V rows regrouped in the ring: tile t's operand is row t
     constexpr bool FULL = MODE == 0;
     constexpr bool TAIL = MODE == 2;
     constexpr bool RAWMAX = FULL && !is_quantised(KVT);
@@ -561,7 +591,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       full[0] = blk0[0] + kBlockSize <= all_visible;
       full[1] = blk0[1] + kBlockSize <= all_visible && has_b;
     }
-    if constexpr (TAIL) {
+    if constexpr (TAIL && RL) {   // the operands are masked where they are built, below
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!full[0]) in_ctx[0][e] = blk0[0] + 4 * j + e < L;
+        if (!full[1]) in_ctx[1][e] = has_b && blk0[1] + 4 * j + e < L;
+      }
+    } else if constexpr (TAIL) {
       if (!full[0]) mask_tail(P, kA, blk0[0], in_ctx[0]);
       if (!full[1]) mask_tail(P, kB, has_b ? blk0[1] : L, in_ctx[1]);   // an absent block lies wholly past L
     }
@@ -645,7 +681,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         u32x4 av;
-        if constexpr (EB == 2) {
+        if constexpr (RL) {
+          av = (t & 1) ? P.vb[t / 2] : P.va[t / 2];
+          if constexpr (TAIL) {   // keys past the context: V zeroed (words 0-1 first block, 2-3 second)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              av[w] &= (in_ctx[w / 2][2 * (w % 2)] ? 0xffffu : 0u) | (in_ctx[w / 2][2 * (w % 2) + 1] ? 0xffff0000u : 0u);
+          }
+        } else if constexpr (EB == 2) {
           av = u32x4{vword(P, kA, t, 0), vword(P, kA, t, 1), vword(P, kB, t, 0), vword(P, kB, t, 1)};
         } else {
           uint32_t v0, v1, v2, v3;
@@ -730,17 +773,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       }
       auto tile_blk = [&](int q) { return min(2 * min(q, npairs - 1) + (wave & 1), n - 1); };
       auto tile_src = [&](int phys) {
-        return kvb + ((size_t)(phys >= 0 && phys < a.num_blocks ? phys : 0) * hkv + kvh) * TB + src_off;
+        return kvb + ((size_t)(phys >= 0 && phys < a.num_blocks ? phys : 0) * hkv + kvh) * TB;
       };
       auto tile_dst = [&](int q) { return s_ring + (q % NS) * SB + (wave < 2 ? wave * TB : 2 * TB); };
       for (int q = 0; q < lead; ++q) {
-        const uint8_t* src = tile_src(__builtin_amdgcn_readfirstlane(s_tab[tile_blk(q)]));
-        uint8_t* dst = tile_dst(q);
-#pragma unroll
-        for (int k = 0; k < LPS; ++k)
-          __builtin_amdgcn_global_load_lds(src + k * 1024,
-                                           (__attribute__((address_space(3))) void*)(dst + (row0 + row_step * k) * 1024),
-                                           16, 0, 0);
+        copy_tile<TB, LPS>(tile_src(__builtin_amdgcn_readfirstlane(s_tab[tile_blk(q)])), src_off, tile_dst(q), row0,
+                           row_step);
       }
       // The table entry of the tile this wave copies in the next iteration.
       int ent = s_tab[tile_blk(lead)];
@@ -776,7 +814,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         const uint8_t* src = tile_src(__builtin_amdgcn_readfirstlane(ent));
         const int e = ring_io<TB, LPS, KW / 4, VQ, RV, CONV>(
             s_ring + ((p + 1) % NS) * SB, s_ring + (p % NS) * SB + 2 * TB, tile_dst(p + lead), s_tab,
-            tile_blk(p + 1 + lead), src, row0, row_step, c, j, lane, kn_a, kn_b, va, vb,
+            tile_blk(p + 1 + lead), src, src_off, row0, row_step, c, j, lane, kn_a, kn_b, va, vb,
             s_ring + ((p + 1) % NS) * SB + 2 * TB, wave, body);
         if constexpr (RV) ent = e;
       };
@@ -799,8 +837,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       }
       // The first copies are waited for here, in the compiler's view too:
       // left in flight into the loop, they would make it wait for all copies
-      // at every step.
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+      // at every step.  So are all LDS and scalar loads: a scalar load still
+      // pending at the loop's entry (a kernel argument used after it) makes
+      // every first LDS wait of a step a wait for all of them (scalar loads
+      // return out of order, so no partial count is safe).
+      __builtin_amdgcn_s_waitcnt(0x0070);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if constexpr (CONV) convert_v_rows<VQ>(s_ring + 2 * TB, wave, lane);   // V(0); published by the first iteration's barrier
@@ -853,9 +894,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           for (int t = 0; t < NT; t += 2) {
             u32x4 av[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-              av[u] = u32x4{va[(2 * (t + u)) / 4][(2 * (t + u)) % 4], va[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4],
-                            vb[(2 * (t + u)) / 4][(2 * (t + u)) % 4], vb[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4]};
+            for (int u = 0; u < 2; ++u) {
+              if constexpr (CONV)   // regrouped rows: tile t's operand is row t
+                av[u] = ((t + u) & 1) ? vb[(t + u) / 2] : va[(t + u) / 2];
+              else
+                av[u] = u32x4{va[(2 * (t + u)) / 4][(2 * (t + u)) % 4], va[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4],
+                              vb[(2 * (t + u)) / 4][(2 * (t + u)) % 4], vb[(2 * (t + u) + 1) / 4][(2 * (t + u) + 1) % 4]};
+            }
 #pragma unroll
             for (int u = 0; u < 2; ++u)
               acc[cs][t + u] = mfma_k32v<F16 || PVF>(av[u], u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]},
@@ -889,7 +934,6 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           }
         };
         ring_head(p, va, vb, std::true_type{}, [&]() {
-          __builtin_amdgcn_sched_barrier(0);   // the reads and the copy go out first, in their order
           probs(0);
           qk_next();
 #pragma unroll
@@ -902,7 +946,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
           constexpr int kPvMfma = PVF ? NT : 2 * NT;
           __builtin_amdgcn_sched_group_barrier(0x002, PKV_PREFILL_ILV_LEAD, 0);
-          interleave_mfma<kQkMfma, PKV_PREFILL_ILV_QK>();
+          if constexpr (CONV) {   // the late LDS reads (second V half, table entry, rewrite) before the last 4 QK MFMAs
+            interleave_mfma<kQkMfma - 4, PKV_PREFILL_ILV_QK>();
+            __builtin_amdgcn_sched_group_barrier(0x100, VQ + 3, 0);
+            interleave_mfma<4, PKV_PREFILL_ILV_QK>();
+          } else {
+            interleave_mfma<kQkMfma, PKV_PREFILL_ILV_QK>();
+          }
           if constexpr (CS > 1) interleave_mfma<kPvMfma * (CS - 1), PKV_PREFILL_ILV_PV>();
           interleave_mfma<kPvMfma, 1>();
         });
