@@ -98,7 +98,7 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #define PKV_PREFILL_ILV_LEAD 8            // VALU instructions scheduled between the LDS reads and the first MFMA
 #endif
 #ifndef PKV_PREFILL_ILV_QK
-#define PKV_PREFILL_ILV_QK 4              // VALU instructions scheduled after each QK MFMA of the next pair
+#define PKV_PREFILL_ILV_QK 1              // VALU instructions scheduled after each QK MFMA of the next pair
 #endif
 #ifndef PKV_PREFILL_ILV_PV
 #define PKV_PREFILL_ILV_PV 4              // ... after each PV MFMA of a column set but the last
