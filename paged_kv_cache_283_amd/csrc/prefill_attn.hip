@@ -103,6 +103,12 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #ifndef PKV_PREFILL_ILV_PV
 #define PKV_PREFILL_ILV_PV 4              // ... after each PV MFMA of a column set but the last
 #endif
+#ifndef PKV_PREFILL_ILV_PVL
+#define PKV_PREFILL_ILV_PVL 1             // ... after each PV MFMA of the last column set
+#endif
+#ifndef PKV_PREFILL_LATE_QK
+#define PKV_PREFILL_LATE_QK 4             // QK MFMAs after the late LDS reads of a step (f16 rewrite)
+#endif
 #ifndef PKV_PREFILL_PV16
 #define PKV_PREFILL_PV16 1                // 16-bit pools: PV as f16 x f16 with one probability operand
 #endif
@@ -371,11 +377,15 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   float m_run[CS], l_run[CS];
   float p_run[CS];   // biased V operands: this lane's share of the sum of P operand values
   f32x4 acc[CS][NT];
+  // f16 PV steps: the column's normaliser, summed by one more MFMA from the
+  // probability operands (every row of the result holds the column's sum).
+  f32x4 lacc[CS];
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) {
     p_run[cs] = 0.f;
     m_run[cs] = -INFINITY;
     l_run[cs] = 0.f;
+    lacc[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[cs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -629,6 +639,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
         const float m_new = need ? mb : m_run[cs];
         const float alpha = m_new == m_run[cs] ? 1.f : fast_exp2(m_run[cs] - m_new);
         l_run[cs] *= alpha;
+        lacc[cs] *= alpha;
         if constexpr (BIAS) p_run[cs] *= alpha;
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[cs][t] *= alpha;
@@ -850,6 +861,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       // rescale threshold; a rescale, rare, takes the column's max), then one
       // basic block interleaves the probabilities of each column set with the
       // QK MFMAs of pair p + 1 and the PV MFMAs of the previous set.
+      // The exponent's offset per set, -m_run (0 while m_run is -inf), changed
+      // only by a rescale.
+      float offp[CS];
+      auto set_off = [&]() {
+#pragma unroll
+        for (int cs = 0; cs < CS; ++cs) offp[cs] = -(qbias[cs] * sl2) - (m_run[cs] == -INFINITY ? 0.f : m_run[cs]);
+      };
+      set_off();
       auto pipe_step = [&](int p) {
         bool any = false;
 #pragma unroll
@@ -862,24 +881,25 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
             const float m_new = need ? mb : m_run[cs];
             const float alpha = m_new == m_run[cs] ? 1.f : fast_exp2(m_run[cs] - m_new);
             l_run[cs] *= alpha;
+            lacc[cs] *= alpha;
 #pragma unroll
             for (int t = 0; t < NT; ++t) acc[cs][t] *= alpha;
             m_run[cs] = m_new;
           }
+          set_off();
         }
         // From here on one basic block: the LDS reads, the copy, then the
         // MFMAs interleaved with the VALU work (the body below).
         u32x4 va[VQ], vb[VQ];
         uint32_t ph[CS][2 * NB], pl[CS][2 * NB];
         auto probs = [&](int cs) {
-          const float mref = m_run[cs] == -INFINITY ? 0.f : m_run[cs];
-          const float off = -(qbias[cs] * sl2) - mref;   // exponent = raw * |f| + off
+          const float off = offp[cs];   // exponent = raw * |f| + off
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             float pr[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) pr[e] = fast_exp2(__builtin_fmaf(sacc[b][cs][e], sl2, off));
-            l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            if constexpr (!PVF) l_run[cs] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
               if constexpr (PVF) ph[cs][2 * b + w] = pack_f16x2(pr[2 * w], pr[2 * w + 1]);
@@ -910,6 +930,11 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
               for (int u = 0; u < 2; ++u)
                 acc[cs][t + u] = mfma_k32v<F16>(av[u], u32x4{pl[cs][0], pl[cs][1], pl[cs][2], pl[cs][3]}, acc[cs][t + u]);
             }
+          }
+          if constexpr (PVF) {   // the normaliser: all-ones rows times the probabilities
+            constexpr uint32_t kOnes = 0x3C003C00u;   // f16 1.0, twice
+            lacc[cs] = mfma_k32v<true>(u32x4{kOnes, kOnes, kOnes, kOnes},
+                                       u32x4{ph[cs][0], ph[cs][1], ph[cs][2], ph[cs][3]}, lacc[cs]);
           }
         };
         // QK of the next pair, both blocks' chains interleaved.
@@ -944,17 +969,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
           lane_max(snew, lmx);
           pv(CS - 1);
           constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
-          constexpr int kPvMfma = PVF ? NT : 2 * NT;
+          constexpr int kPvMfma = PVF ? NT + 1 : 2 * NT;
           __builtin_amdgcn_sched_group_barrier(0x002, PKV_PREFILL_ILV_LEAD, 0);
           if constexpr (CONV) {   // the late LDS reads (second V half, table entry, rewrite) before the last 4 QK MFMAs
-            interleave_mfma<kQkMfma - 4, PKV_PREFILL_ILV_QK>();
+            interleave_mfma<kQkMfma - PKV_PREFILL_LATE_QK, PKV_PREFILL_ILV_QK>();
             __builtin_amdgcn_sched_group_barrier(0x100, VQ + 3, 0);
-            interleave_mfma<4, PKV_PREFILL_ILV_QK>();
+            interleave_mfma<PKV_PREFILL_LATE_QK, PKV_PREFILL_ILV_QK>();
           } else {
             interleave_mfma<kQkMfma, PKV_PREFILL_ILV_QK>();
           }
           if constexpr (CS > 1) interleave_mfma<kPvMfma * (CS - 1), PKV_PREFILL_ILV_PV>();
-          interleave_mfma<kPvMfma, 1>();
+          interleave_mfma<kPvMfma, PKV_PREFILL_ILV_PVL>();
         });
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -992,7 +1017,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
     bool fin = true;
 #pragma unroll
     for (int cs = 0; cs < CS; ++cs) {
-      fin &= __builtin_isfinite(l_run[cs]);
+      fin &= __builtin_isfinite(l_run[cs]) & __builtin_isfinite(lacc[cs][0]);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -1005,6 +1030,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       for (int cs = 0; cs < CS; ++cs) {
         m_run[cs] = -INFINITY;
         l_run[cs] = 0.f;
+        lacc[cs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[cs][t] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -1103,7 +1129,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) {
-    float l = row_sum4(l_run[cs]);
+    float l = row_sum4(l_run[cs]) + lacc[cs][0];
     if (bad) l = __builtin_nanf("");
     const float vbias = BIAS ? kInt8Bias * row_sum4(p_run[cs]) : 0.f;   // biased V operands
     if (!wave_live || !col_ok[cs]) continue;
