@@ -109,6 +109,9 @@ constexpr float kPfRescaleSlack = 8.f;    // base-2 slack before accumulators ar
 #ifndef PKV_PREFILL_LATE_QK
 #define PKV_PREFILL_LATE_QK 4             // QK MFMAs after the late LDS reads of a step (f16 rewrite)
 #endif
+#ifndef PKV_PREFILL_F16_ONE_MAX
+#define PKV_PREFILL_F16_ONE_MAX 1         // f16 PV steps: the running max only from a chunk's first pair
+#endif
 #ifndef PKV_PREFILL_PV16
 #define PKV_PREFILL_PV16 1                // 16-bit pools: PV as f16 x f16 with one probability operand
 #endif
@@ -870,9 +873,18 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       };
       set_off();
       auto pipe_step = [&](int p) {
+        // f16 PV steps (with PKV_PREFILL_F16_ONE_MAX) take the running max
+        // from a chunk's first pair only: a later logit up to 16 (base 2)
+        // above it gives a probability up to 2^16, still an f16 value; past
+        // that the probability is inf, the accumulators turn non-finite and
+        // the workgroup computes again with the split path, which checks
+        // every pair.  This saves the max over every later pair's products.
+        constexpr bool kOneMax = PVF && PKV_PREFILL_F16_ONE_MAX;
         bool any = false;
+        if (!kOneMax || p == 0) {
 #pragma unroll
-        for (int cs = 0; cs < CS; ++cs) any = any || lmx[cs] * sl2 > m_run[cs] + kPfRescaleSlack;
+          for (int cs = 0; cs < CS; ++cs) any = any || lmx[cs] * sl2 > m_run[cs] + kPfRescaleSlack;
+        }
         if (__builtin_amdgcn_ballot_w64(any) != 0ull) {
 #pragma unroll
           for (int cs = 0; cs < CS; ++cs) {
@@ -966,7 +978,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
             probs(cs);
             pv(cs - 1);
           }
-          lane_max(snew, lmx);
+          if constexpr (!kOneMax) lane_max(snew, lmx);
           pv(CS - 1);
           constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
           constexpr int kPvMfma = PVF ? NT + 1 : 2 * NT;

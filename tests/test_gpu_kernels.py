@@ -1184,6 +1184,35 @@ def test_prefill_v_beyond_f16_range():
         assert err <= tol, (s, err, tol)
 
 
+@pytest.mark.parametrize("jump", [0.6, 30.0])
+def test_prefill_late_logit_jump(jump):
+    """A key past a chunk's first block pair whose logit exceeds every earlier one: by about 10
+    (base 2, jump 0.6), the f16 path keeps the first pair's max and the probabilities reach ~2^10;
+    by several hundred (jump 30) they pass f16's range, and the workgroup computes again with the
+    split path.  Both match the oracle."""
+    lens, n_qs = (300, 1000), (37, 120)
+    w, case, qt, qs = _prefill_case("bf16", "bf16", 128, 32, 8, 106, lens, n_qs)
+    g = torch.Generator().manual_seed(7)
+    u = torch.randn(128, generator=g)
+    qt[:] = u.to(qt.dtype).to(qt.device)                        # every query row and head: u
+    ks = case.ksrc
+    r = torch.from_numpy(H.logical_rows(case.lay, 0, np.array([200]))).to(ks.device).long()
+    r1 = torch.from_numpy(H.logical_rows(case.lay, 1, np.array([700, 950]))).to(ks.device).long()
+    ks[r] = (jump * u).to(ks.dtype).to(ks.device)               # all KV heads
+    ks[r1] = (jump * u).to(ks.dtype).to(ks.device)
+    H.fill(w, case.lay, case.pools, ks, case.vsrc, case.tables)
+    out = torch.full(qt.shape, float("nan"), dtype=torch.float32, device="cuda")
+    k, v, _, _ = case.pools
+    ops.paged_prefill_attn(out, qt, k, v, case.tables, case.lens, qs, case.lay.max_len, max(n_qs))
+    worst = 0.0
+    for s in range(len(lens)):
+        ref = _prefill_oracle(w, case, qt, qs, s)
+        a, b = int(qs[s]), int(qs[s + 1])
+        worst = max(worst, H.max_err(H.to_f64(out[a:b]), ref))
+    print(f"prefill with a late logit jump x{jump}: max abs err {worst:.3e}")
+    assert worst <= TOL["bf16"]
+
+
 def test_prefill_invalid_sequences():
     lens = (40, 40, 40)
     n_qs = (8, 8, 8)
