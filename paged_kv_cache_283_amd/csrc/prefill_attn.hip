@@ -979,7 +979,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
             pv(cs - 1);
           }
           if constexpr (!kOneMax) lane_max(snew, lmx);
+          mfma_phase(true);   // the last set's PV MFMAs run back to back: ahead of the other wave's VALU
           pv(CS - 1);
+          mfma_phase(false);
           constexpr int kQkMfma = NB * (DPL / 8) * CS * (QSPLIT ? 2 : 1);
           constexpr int kPvMfma = PVF ? NT + 1 : 2 * NT;
           __builtin_amdgcn_sched_group_barrier(0x002, PKV_PREFILL_ILV_LEAD, 0);
