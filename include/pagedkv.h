@@ -374,6 +374,12 @@ int paged_decode_attn_compact(void* out, int out_dtype,
  * [0, num_tokens) is skipped; one with L < n, L > max_context_len or L >
  * 16 * stride, or that needs a table entry outside [0, num_blocks), gets NaN
  * in its rows.  Rows not owned by any sequence are left untouched.
+ * Precision: over BF16/F16 pools the probabilities enter the P.V product as
+ * f16 values (relative rounding <= 2^-11) against V in f16 (BF16 V converted
+ * exactly over f16's normal range); a workgroup whose inputs leave f16's range
+ * (|V| > 65504, a logit far above its chunk's first block pair) computes again
+ * with ~16-bit probabilities and bf16 V, so any finite input is covered.  The
+ * other pools use ~16-bit probabilities throughout.
  */
 int paged_prefill_attn(void* out, int out_dtype, const void* q, int q_dtype,
                        const void* k_pool, const void* v_pool,

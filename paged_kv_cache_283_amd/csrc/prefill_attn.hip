@@ -27,6 +27,10 @@
 // the last one or two of a wave) take a path with no mask at all, where the
 // logit factor enters the exponent's fma; the factor's sign is folded into the
 // query operands so that the running max is taken on the raw products.
+// 16-bit pools stage each block pair once per workgroup in an LDS ring and run
+// PV in f16 (bf16 V rewritten to f16 in the ring, one probability operand per
+// tile); a workgroup whose values leave f16's range computes again with the
+// bf16 high/low probability split.
 #include <type_traits>
 
 #include "device_common.hpp"
