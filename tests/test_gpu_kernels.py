@@ -1184,14 +1184,14 @@ def test_prefill_v_beyond_f16_range():
         assert err <= tol, (s, err, tol)
 
 
-@pytest.mark.parametrize("jump", [0.6, 30.0])
-def test_prefill_late_logit_jump(jump):
+@pytest.mark.parametrize("kv,jump", [("bf16", 0.6), ("bf16", 30.0), ("f16", 30.0)])
+def test_prefill_late_logit_jump(kv, jump):
     """A key past a chunk's first block pair whose logit exceeds every earlier one: by about 10
     (base 2, jump 0.6), the f16 path keeps the first pair's max and the probabilities reach ~2^10;
     by several hundred (jump 30) they pass f16's range, and the workgroup computes again with the
     split path.  Both match the oracle."""
     lens, n_qs = (300, 1000), (37, 120)
-    w, case, qt, qs = _prefill_case("bf16", "bf16", 128, 32, 8, 106, lens, n_qs)
+    w, case, qt, qs = _prefill_case(kv, kv, 128, 32, 8, 106, lens, n_qs)
     g = torch.Generator().manual_seed(7)
     u = torch.randn(128, generator=g)
     qt[:] = u.to(qt.dtype).to(qt.device)                        # every query row and head: u
@@ -1209,8 +1209,8 @@ def test_prefill_late_logit_jump(jump):
         ref = _prefill_oracle(w, case, qt, qs, s)
         a, b = int(qs[s]), int(qs[s + 1])
         worst = max(worst, H.max_err(H.to_f64(out[a:b]), ref))
-    print(f"prefill with a late logit jump x{jump}: max abs err {worst:.3e}")
-    assert worst <= TOL["bf16"]
+    print(f"prefill {kv} with a late logit jump x{jump}: max abs err {worst:.3e}")
+    assert worst <= TOL[kv]
 
 
 def test_prefill_invalid_sequences():
