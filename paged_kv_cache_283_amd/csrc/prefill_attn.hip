@@ -284,16 +284,19 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   // Workgroup -> (sequence, KV head, tile).  With a pair count divisible by 8,
   // all tiles of a (sequence, KV head) go to one XCD (ids are dealt to the 8
   // XCDs in turn), so the waves re-reading its blocks share that XCD's L2.
+  // Tiles are dealt last first: a later tile's tokens attend more keys, so
+  // the longest workgroups start first and the short ones fill in at the end
+  // (measured 1.07-1.10 -> 1.03 ms on 4 x 2048 after 6144).
   const int tiles = a.tiles_per_pair;
   const int pairs = a.num_seqs * hkv;
   int pair, tile;
   if ((pairs & 7) == 0) {
     const int xcd = blockIdx.x & 7, k = blockIdx.x >> 3;
     pair = (k / tiles) * 8 + xcd;
-    tile = k % tiles;
+    tile = tiles - 1 - k % tiles;
   } else {
     pair = blockIdx.x / tiles;
-    tile = blockIdx.x % tiles;
+    tile = tiles - 1 - blockIdx.x % tiles;
   }
   const int s = pair / hkv, kvh = pair % hkv;
   const int q0 = a.query_start[s];
