@@ -1213,6 +1213,26 @@ def test_prefill_late_logit_jump(kv, jump):
     assert worst <= TOL[kv]
 
 
+@pytest.mark.parametrize("kv", ["bf16", "f16"])
+def test_prefill_context_beyond_one_table_chunk(kv):
+    """A context of 20000 tokens is 1250 blocks: the kernel stages its block table 1024 entries at
+    a time, so the ring restarts (prologue, V rewrite of the first pair, running-max check) inside
+    the sequence.  A 64-row chunk at the end and a 40-row chunk after 16384 + 8 tokens, against the
+    oracle."""
+    lens, n_qs = (20000, 16432), (64, 40)
+    w, case, qt, qs = _prefill_case(kv, kv, 128, 8, 2, 107, lens, n_qs)
+    out = torch.full(qt.shape, float("nan"), dtype=torch.float32, device="cuda")
+    k, v, _, _ = case.pools
+    ops.paged_prefill_attn(out, qt, k, v, case.tables, case.lens, qs, case.lay.max_len, max(n_qs))
+    worst = 0.0
+    for s in range(len(lens)):
+        ref = _prefill_oracle(w, case, qt, qs, s)
+        a, b = int(qs[s]), int(qs[s + 1])
+        worst = max(worst, H.max_err(H.to_f64(out[a:b]), ref))
+    print(f"prefill {kv} over 20000 / 16432 tokens: max abs err {worst:.3e}")
+    assert worst <= TOL[kv]
+
+
 def test_prefill_invalid_sequences():
     lens = (40, 40, 40)
     n_qs = (8, 8, 8)
