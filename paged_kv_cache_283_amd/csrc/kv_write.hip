@@ -131,9 +131,18 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   constexpr float kMaxCode = code_set(KVT) == DT_INT8 ? 127.f : 448.f;
   // Raw source bits of K and V, one word per element; rows padded by one word
   // so that threads reading the same dim of consecutive rows hit different
-  // LDS banks.
+  // LDS banks.  16-bit pools (fed from their own dtype, bits copied as they
+  // are) stage the rows packed instead, padded by 16 bytes; a workgroup whose
+  // 16 tokens fill one tile in slot order (bulk fills, prefills) then builds
+  // each K chunk from one 16-byte LDS read and each V chunk from eight 2-byte
+  // ones, with no per-element packing.
+  constexpr bool PACK16 = KVT == DT_BF16 || KVT == DT_F16;
+  static_assert(!PACK16 || SRC == KVT, "16-bit pools take their own dtype");
   constexpr int kRow = D + 1;
-  __shared__ uint32_t s_src[2][kWriteGroup][kRow];   // [K, V][token][dim]
+  constexpr int kRowH = D + 8;
+  __shared__ uint32_t s_src[PACK16 ? 1 : 2][PACK16 ? 1 : kWriteGroup][PACK16 ? 1 : kRow];   // [K, V][token][dim]
+  __shared__ __attribute__((aligned(16))) uint16_t s_h[PACK16 ? 2 : 1][PACK16 ? kWriteGroup : 1][PACK16 ? kRowH : 8];
+  __shared__ int s_full;                       // PACK16: the 16 tokens are rows 0..15 of one tile
   __shared__ int64_t s_slot[kWriteGroup];      // -1: token skipped
   __shared__ float s_scale[2][kWriteGroup];
   __shared__ int s_lead[kWriteGroup];          // V: 1 leads a complete quad, 2 is covered by one, 0 neither
@@ -143,6 +152,26 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   // of the source and write side-by-side tiles of the pool.
   const int h = (int)(blockIdx.x % (unsigned)num_kv_heads);
   const int t_base = (int)(blockIdx.x / (unsigned)num_kv_heads) * kWriteGroup;
+  // Both rows of every token, with 16-byte loads: K and V, row o, elements
+  // [8 p, 8 p + 8) (16-bit source) or [4 p, 4 p + 4) (f32).  All of a
+  // thread's loads and the slot lookup go out before any of them is waited
+  // for (one memory round trip per workgroup); rows of skipped tokens are
+  // simply not stored.
+  constexpr int kPer = 16 / (SRC == DT_F32 ? 4 : 2);
+  constexpr int kUnits = 2 * kWriteGroup * D / kPer;   // 16-byte pieces of the group's K and V rows
+  static_assert(kUnits % kThreads == 0, "whole loads per thread");
+  constexpr int kLoads = kUnits / kThreads;
+  u32x4 wv[kLoads];
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = tid + it * kThreads;
+    const int kv = e / (kWriteGroup * D / kPer), r = e % (kWriteGroup * D / kPer);
+    const int o = r / (D / kPer), d0 = (r % (D / kPer)) * kPer;
+    wv[it] = u32x4{0u, 0u, 0u, 0u};
+    if (t_base + o < num_tokens)
+      wv[it] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(kv == 0 ? k_new : v_new) +
+                                               (((size_t)(t_base + o) * num_kv_heads + h) * D + d0) * (16 / kPer));
+  }
   long long my_slot = -1;                      // lanes 0..15: token t_base + lane
   if (tid < kWriteGroup) {
     const int t = t_base + tid;
@@ -151,21 +180,20 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     my_slot = sl < 0 ? -1 : sl;
     s_slot[tid] = my_slot;
   }
-  // Both rows of every token, with 16-byte loads: K and V, row o, elements
-  // [8 p, 8 p + 8) (16-bit source) or [4 p, 4 p + 4) (f32).  They do not wait
-  // for the slot lookup above; rows of skipped tokens are simply not stored.
-  constexpr int kPer = 16 / (SRC == DT_F32 ? 4 : 2);
-  for (int e = tid; e < 2 * kWriteGroup * D / kPer; e += kThreads) {
+#pragma unroll
+  for (int it = 0; it < kLoads; ++it) {
+    const int e = tid + it * kThreads;
     const int kv = e / (kWriteGroup * D / kPer), r = e % (kWriteGroup * D / kPer);
     const int o = r / (D / kPer), d0 = (r % (D / kPer)) * kPer;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (t_base + o < num_tokens)
-      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(kv == 0 ? k_new : v_new) +
-                                          (((size_t)(t_base + o) * num_kv_heads + h) * D + d0) * (16 / kPer));
+    const u32x4 w = wv[it];
+    if constexpr (PACK16) {
+      *reinterpret_cast<u32x4*>(&s_h[kv][o][d0]) = w;
+    } else {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      if constexpr (SRC == DT_F32) s_src[kv][o][d0 + i] = w[i];
-      else s_src[kv][o][d0 + i] = (w[i / 2] >> (16 * (i % 2))) & 0xffffu;
+      for (int i = 0; i < kPer; ++i) {
+        if constexpr (SRC == DT_F32) s_src[kv][o][d0 + i] = w[i];
+        else s_src[kv][o][d0 + i] = (w[i / 2] >> (16 * (i % 2))) & 0xffffu;
+      }
     }
   }
   __syncthreads();
@@ -182,6 +210,12 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
               l3 = __shfl_up((int)lead, 3, kWave);
     const bool covered = (tid >= 1 && l1) || (tid >= 2 && l2) || (tid >= 3 && l3);
     if (tid < kWriteGroup) s_lead[tid] = lead ? 1 : (covered ? 2 : 0);
+    if constexpr (PACK16) {
+      const long long s0 = __shfl(my_slot, 0, kWave);
+      const bool ok = tid >= kWriteGroup || (s0 >= 0 && s0 % kBlockSize == 0 && my_slot == s0 + tid);
+      const bool full = __builtin_amdgcn_ballot_w64(!ok) == 0ull;
+      if (tid == 0) s_full = full ? 1 : 0;
+    }
   }
   if constexpr (is_quantised(KVT)) {
     // 8 threads per (K or V, row): absmax, then the row's scale
@@ -202,10 +236,14 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
 
   // Stored bits of element (token o, dim d) of K (kv 0) or V (kv 1).
   auto code_of = [&](int kv, int o, int d) -> uint32_t {
-    float sc = 0.f;
-    if constexpr (is_quantised(KVT)) sc = s_scale[kv][o];
-    if constexpr (is_channel_scaled(KVT)) sc = (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d];
-    return stored_code<SRC, KVT>(s_src[kv][o][d], sc);
+    if constexpr (PACK16) {
+      return s_h[kv][o][d];
+    } else {
+      float sc = 0.f;
+      if constexpr (is_quantised(KVT)) sc = s_scale[kv][o];
+      if constexpr (is_channel_scaled(KVT)) sc = (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d];
+      return stored_code<SRC, KVT>(s_src[kv][o][d], sc);
+    }
   };
   // 16 bytes from 16 / EB element codes.
   auto pack = [&](const uint32_t* el) {
@@ -219,6 +257,34 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   };
   uint8_t* kp = reinterpret_cast<uint8_t*>(k_pool);
   uint8_t* vp = reinterpret_cast<uint8_t*>(v_pool);
+
+  if constexpr (PACK16) {
+    if (s_full) {   // one whole tile, rows in slot order
+      const size_t tile = (size_t)(s_slot[0] / kBlockSize) * num_kv_heads + h;
+      uint8_t* kt = kp + tile * kBlockSize * D * EB;
+      uint8_t* vt = vp + tile * kBlockSize * D * EB;
+      // K chunk (c, o): dims 8c .. 8c + 7 of row o, at (c * 16 + o) * 16
+      for (int q = tid; q < kWriteGroup * (D / X); q += kThreads) {
+        const int o = q % kWriteGroup, c = q / kWriteGroup;
+        *reinterpret_cast<u32x4*>(kt + (size_t)(c * kBlockSize + o) * 16) =
+            *reinterpret_cast<const u32x4*>(&s_h[0][o][X * c]);
+      }
+      // V chunk q = (g * 16 + c) * 4 + jq: dims 16 (2g + u) + c, u < 2, of rows
+      // 4 jq .. 4 jq + 3, element order [u][row]
+      for (int q = tid; q < kWriteGroup * D / 8; q += kThreads) {
+        const int jq = q % 4, c = (q / 4) % kBlockSize, g = q / (4 * kBlockSize);
+        uint32_t w4[4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int d = 16 * (2 * g + u) + c;
+          w4[2 * u] = (uint32_t)s_h[1][4 * jq][d] | ((uint32_t)s_h[1][4 * jq + 1][d] << 16);
+          w4[2 * u + 1] = (uint32_t)s_h[1][4 * jq + 2][d] | ((uint32_t)s_h[1][4 * jq + 3][d] << 16);
+        }
+        *reinterpret_cast<u32x4*>(vt + (size_t)q * 16) = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+      return;
+    }
+  }
 
   // K: chunk c of token o = dims c X .. c X + X - 1 at [c][row][*] of its tile
   for (int q = tid; q < kWriteGroup * (D / X); q += kThreads) {
