@@ -983,7 +983,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
 #pragma unroll
           for (int cs = 1; cs < CS; ++cs) {
             probs(cs);
+            mfma_phase(true);   // (the previous set's PV MFMAs, interleaved with this set's softmax)
             pv(cs - 1);
+            mfma_phase(false);
           }
           if constexpr (!kOneMax) lane_max(snew, lmx);
           mfma_phase(true);   // the last set's PV MFMAs run back to back: ahead of the other wave's VALU
