@@ -1205,16 +1205,18 @@ __global__ void __launch_bounds__(256) attn_reduce_kernel(const AttnArgs a, int 
 }
 
 // H2O mass of 256 attended positions of sequence s (workgroup-uniform s):
-// scores[s][p] += mean over query heads of exp2(x - M_h) / l_h, kept p only.
-// The heads' global (M_h, l_h) are staged in LDS, 256 heads at a time, so the
-// loop over heads issues only the (coalesced) logit loads.  A head of a
+// scores[s][p] += mean over query heads of exp2(x - M_h) / l_h, kept p only,
+// taken as exp2(x - (M_h + log2 l_h)): one exponential per head and no
+// division (the folded offset's rounding moves the result by ~1e-6
+// relative).  The heads' offsets are staged in LDS, 256 heads at a time, so
+// the loop over heads issues only the (coalesced) logit loads.  A head of a
 // sequence that was one segment has them from its wave; otherwise the thread
 // of head h merges the segments' (max, exp-sum) pairs itself, 16 loads in
 // flight at a time (as many round trips as the output merge's 16 segments per
 // wave), so that the mass does not wait for the output merge.
 __device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
   constexpr int kPairs = 16;
-  __shared__ float s_m[256], s_l[256];
+  __shared__ float s_m[256];
   const int v = bx * 256 + threadIdx.x;                  // attended (virtual) position
   const int L = a.context_lens[s];
   const int len_cap = min(a.max_context_len, a.table_stride * kBlockSize);
@@ -1255,14 +1257,13 @@ __device__ __forceinline__ void mass_block(const AttnArgs& a, int s, int bx) {
           M = Mn;
         }
       }
-      s_m[threadIdx.x] = M;
-      s_l[threadIdx.x] = l;
+      s_m[threadIdx.x] = M + __builtin_amdgcn_logf(l);   // v_log_f32: log2
     }
     __syncthreads();
     if (active) {
       const float* x = a.stash + ((size_t)s * hq + h0) * a.nv_pad + v;
 #pragma unroll 8
-      for (int h = 0; h < hn; ++h) sum += fast_exp2(x[(size_t)h * a.nv_pad] - s_m[h]) / s_l[h];
+      for (int h = 0; h < hn; ++h) sum += fast_exp2(x[(size_t)h * a.nv_pad] - s_m[h]);
     }
   }
   if (!active) return;
