@@ -1150,6 +1150,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
   }
   }
 
+  const bool out_vec = (reinterpret_cast<uintptr_t>(a.out) & (a.out_dtype == DT_F32 ? 15 : 7)) == 0;
 #pragma unroll
   for (int cs = 0; cs < CS; ++cs) {
     float l = row_sum4(l_run[cs]) + lacc[cs][0];
@@ -1163,8 +1164,22 @@ __global__ void __launch_bounds__(256) prefill_kernel(const PrefillArgs a) {
       f32x4 o = acc[cs][t];
       if constexpr (BIAS) o -= vbias;
       if constexpr (CH) o *= *reinterpret_cast<const f32x4*>(a.v_scale + (size_t)kvh * D + 16 * t + 4 * j);
+      o *= inv;
+      const size_t oi = orow + 16 * t + 4 * j;   // 4 consecutive dims: one 8- or 16-byte store when aligned
+      if (out_vec) {
+        if (a.out_dtype == DT_F32) {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + oi) = o;
+        } else {
+          const bool bf = a.out_dtype == DT_BF16;
+          uint32_t w[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(a.out, orow + 16 * t + 4 * j + e, a.out_dtype, o[e] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = bf ? f32_to_bf16_rne(o[e]) : f32_to_f16_bits(o[e]);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + oi) = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_out(a.out, oi + e, a.out_dtype, o[e]);
+      }
     }
   }
 }

@@ -1233,6 +1233,21 @@ def test_prefill_context_beyond_one_table_chunk(kv):
     assert worst <= TOL[kv]
 
 
+def test_prefill_16bit_outputs_are_the_rounded_f32_output():
+    """bf16 and f16 outputs (written four dims per store) are the f32 output of the same call rounded
+    to nearest even, element for element."""
+    lens, n_qs = (300, 1000), (37, 150)
+    w, case, qt, qs = _prefill_case("bf16", "bf16", 128, 32, 8, 108, lens, n_qs)
+    k, v, _, _ = case.pools
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16, torch.float16):
+        outs[dt] = torch.empty(qt.shape, dtype=dt, device="cuda")
+        ops.paged_prefill_attn(outs[dt], qt, k, v, case.tables, case.lens, qs, case.lay.max_len, max(n_qs))
+    ref = outs[torch.float32]
+    for dt in (torch.bfloat16, torch.float16):
+        assert torch.equal(outs[dt], ref.to(dt)), dt
+
+
 def test_prefill_invalid_sequences():
     lens = (40, 40, 40)
     n_qs = (8, 8, 8)
