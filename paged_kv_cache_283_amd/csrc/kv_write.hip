@@ -129,19 +129,23 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   constexpr int Y = 4 / EB;                                        // dims per V chunk
   constexpr int kThreads = kWriteThreads;
   constexpr float kMaxCode = code_set(KVT) == DT_INT8 ? 127.f : 448.f;
-  // Raw source bits of K and V, one word per element; rows padded by one word
-  // so that threads reading the same dim of consecutive rows hit different
-  // LDS banks.  16-bit pools (fed from their own dtype, bits copied as they
-  // are) stage the rows packed instead, padded by 16 bytes; a workgroup whose
-  // 16 tokens fill one tile in slot order (bulk fills, prefills) then builds
-  // each K chunk from one 16-byte LDS read and each V chunk from eight 2-byte
-  // ones, with no per-element packing.
+  // Raw source bits of K and V.  f32 sources: one word per element, rows
+  // padded by one word so that threads reading the same dim of consecutive
+  // rows hit different LDS banks.  16-bit sources: packed as loaded, rows
+  // padded by 16 bytes, so a 16-byte LDS read yields 8 consecutive dims (the
+  // scale pass and the K chunks read them that way).  16-bit pools (fed from
+  // their own dtype, bits copied as they are): a workgroup whose 16 tokens
+  // fill one tile in slot order (bulk fills, prefills) builds each K chunk
+  // from one 16-byte LDS read and each V chunk from eight 2-byte ones, with
+  // no per-element packing.
   constexpr bool PACK16 = KVT == DT_BF16 || KVT == DT_F16;
+  constexpr bool H16 = SRC != DT_F32;
   static_assert(!PACK16 || SRC == KVT, "16-bit pools take their own dtype");
+  static_assert(!H16 || KVT != DT_F32, "f32 pools take f32");
   constexpr int kRow = D + 1;
   constexpr int kRowH = D + 8;
-  __shared__ uint32_t s_src[PACK16 ? 1 : 2][PACK16 ? 1 : kWriteGroup][PACK16 ? 1 : kRow];   // [K, V][token][dim]
-  __shared__ __attribute__((aligned(16))) uint16_t s_h[PACK16 ? 2 : 1][PACK16 ? kWriteGroup : 1][PACK16 ? kRowH : 8];
+  __shared__ uint32_t s_src[H16 ? 1 : 2][H16 ? 1 : kWriteGroup][H16 ? 1 : kRow];   // [K, V][token][dim]
+  __shared__ __attribute__((aligned(16))) uint16_t s_h[H16 ? 2 : 1][H16 ? kWriteGroup : 1][H16 ? kRowH : 8];
   __shared__ int s_full;                       // PACK16: the 16 tokens are rows 0..15 of one tile
   __shared__ int64_t s_slot[kWriteGroup];      // -1: token skipped
   __shared__ float s_scale[2][kWriteGroup];
@@ -186,7 +190,7 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     const int kv = e / (kWriteGroup * D / kPer), r = e % (kWriteGroup * D / kPer);
     const int o = r / (D / kPer), d0 = (r % (D / kPer)) * kPer;
     const u32x4 w = wv[it];
-    if constexpr (PACK16) {
+    if constexpr (H16) {
       *reinterpret_cast<u32x4*>(&s_h[kv][o][d0]) = w;
     } else {
 #pragma unroll
@@ -221,7 +225,15 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     // 8 threads per (K or V, row): absmax, then the row's scale
     const int kv = tid / (8 * kWriteGroup), o = (tid / 8) % kWriteGroup, l = tid % 8;
     float m = 0.f;
-    for (int d = l; d < D; d += 8) m = fmaxf(m, fabsf(raw_to_f32<SRC>(s_src[kv][o][d])));
+    if constexpr (H16) {
+      for (int p = l; p < D / 8; p += 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&s_h[kv][o][8 * p]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(raw_to_f32<SRC>((w[i / 2] >> (16 * (i % 2))) & 0xffffu)));
+      }
+    } else {
+      for (int d = l; d < D; d += 8) m = fmaxf(m, fabsf(raw_to_f32<SRC>(s_src[kv][o][d])));
+    }
 #pragma unroll
     for (int off = 4; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
     const float sc = __fdiv_rn(m, kMaxCode);
@@ -234,16 +246,21 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   }
   __syncthreads();
 
-  // Stored bits of element (token o, dim d) of K (kv 0) or V (kv 1).
-  auto code_of = [&](int kv, int o, int d) -> uint32_t {
+  // Stored bits of element (token o, dim d) of K (kv 0) or V (kv 1), from its
+  // raw source bits.
+  auto code_from = [&](int kv, int o, int d, uint32_t raw) -> uint32_t {
     if constexpr (PACK16) {
-      return s_h[kv][o][d];
+      return raw;
     } else {
       float sc = 0.f;
       if constexpr (is_quantised(KVT)) sc = s_scale[kv][o];
       if constexpr (is_channel_scaled(KVT)) sc = (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d];
-      return stored_code<SRC, KVT>(s_src[kv][o][d], sc);
+      return stored_code<SRC, KVT>(raw, sc);
     }
+  };
+  auto code_of = [&](int kv, int o, int d) -> uint32_t {
+    if constexpr (H16) return code_from(kv, o, d, s_h[kv][o][d]);
+    else return code_from(kv, o, d, s_src[kv][o][d]);
   };
   // 16 bytes from 16 / EB element codes.
   auto pack = [&](const uint32_t* el) {
@@ -292,8 +309,18 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     const int64_t sl = s_slot[o];
     if (sl < 0) continue;
     uint32_t el[16 / EB];
+    if constexpr (H16) {
 #pragma unroll
-    for (int i = 0; i < X; ++i) el[i] = code_of(0, o, c * X + i);
+      for (int j = 0; j < X / 8; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(&s_h[0][o][c * X + 8 * j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          el[8 * j + i] = code_from(0, o, c * X + 8 * j + i, (w[i / 2] >> (16 * (i % 2))) & 0xffffu);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < X; ++i) el[i] = code_of(0, o, c * X + i);
+    }
     const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
     *reinterpret_cast<u32x4*>(kp + tile * kBlockSize * D * EB + ((size_t)c * kBlockSize + sl % kBlockSize) * 16) =
         pack(el);
