@@ -76,7 +76,7 @@ def test_decode_and_token_slots_match_oracle():
                                       ("fp8", "bf16", 128), ("fp8", "f32", 64), ("fp8", "f16", 128),
                                       ("int8", "bf16", 128), ("int8", "f32", 64), ("int8", "f16", 128),
                                       ("fp8_ch", "bf16", 128), ("fp8_ch", "f32", 64), ("int8_ch", "bf16", 128),
-                                      ("int8_ch", "f16", 64)])
+                                      ("int8_ch", "f16", 64), ("fp8", "bf16", 64), ("int8", "f16", 64)])
 def test_write_pool_bytes_bit_exact(kv, src, d):
     w = dataclasses.replace(_case_workload(kv, "bf16", d, 8, 2, 91, lens=(35, 70, 16, 1)), src_dtype=src)
     case = H.Case(w)
