@@ -150,6 +150,8 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   __shared__ int64_t s_slot[kWriteGroup];      // -1: token skipped
   __shared__ float s_scale[2][kWriteGroup];
   __shared__ int s_lead[kWriteGroup];          // V: 1 leads a complete quad, 2 is covered by one, 0 neither
+  __shared__ int s_quad[kWriteGroup / 4];      // the tokens that lead a quad, in order
+  __shared__ int s_nquad, s_single;            // how many; whether any token is stored element by element
 
   const int tid = threadIdx.x;
   // KV head fastest: the heads of one token group read one contiguous stretch
@@ -214,6 +216,13 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
               l3 = __shfl_up((int)lead, 3, kWave);
     const bool covered = (tid >= 1 && l1) || (tid >= 2 && l2) || (tid >= 3 && l3);
     if (tid < kWriteGroup) s_lead[tid] = lead ? 1 : (covered ? 2 : 0);
+    const unsigned long long lm = __builtin_amdgcn_ballot_w64(lead);
+    if (lead) s_quad[__popcll(lm & ((1ull << tid) - 1ull))] = tid;
+    const unsigned long long sm = __builtin_amdgcn_ballot_w64(tid < kWriteGroup && my_slot >= 0 && !lead && !covered);
+    if (tid == 0) {
+      s_nquad = __popcll(lm);
+      s_single = sm != 0ull;
+    }
     if constexpr (PACK16) {
       const long long s0 = __shfl(my_slot, 0, kWave);
       const bool ok = tid >= kWriteGroup || (s0 >= 0 && s0 % kBlockSize == 0 && my_slot == s0 + tid);
@@ -303,46 +312,52 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     }
   }
 
-  // K: chunk c of token o = dims c X .. c X + X - 1 at [c][row][*] of its tile
-  for (int q = tid; q < kWriteGroup * (D / X); q += kThreads) {
-    const int o = q % kWriteGroup, c = q / kWriteGroup;
-    const int64_t sl = s_slot[o];
-    if (sl < 0) continue;
+  // K chunks and the V chunks of complete quads in one loop, so that every
+  // thread takes a share of both (the K chunks alone occupy only half the
+  // threads of an 8-bit pool's workgroup, the quads' V chunks another half).
+  // K: chunk c of token o = dims c X .. c X + X - 1 at [c][row][*] of its tile.
+  // V: chunk (g, c) of the quad led by token o holds dims 16 (g Y + u) + c,
+  // u < Y, of its 4 rows, element order [u][row].
+  constexpr int nK = kWriteGroup * (D / X);
+  const int nKV = nK + s_nquad * (D / Y);
+  for (int q = tid; q < nKV; q += kThreads) {
     uint32_t el[16 / EB];
-    if constexpr (H16) {
+    if (q < nK) {
+      const int o = q % kWriteGroup, c = q / kWriteGroup;
+      const int64_t sl = s_slot[o];
+      if (sl < 0) continue;
+      if constexpr (H16) {
 #pragma unroll
-      for (int j = 0; j < X / 8; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(&s_h[0][o][c * X + 8 * j]);
+        for (int j = 0; j < X / 8; ++j) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(&s_h[0][o][c * X + 8 * j]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          el[8 * j + i] = code_from(0, o, c * X + 8 * j + i, (w[i / 2] >> (16 * (i % 2))) & 0xffffu);
+          for (int i = 0; i < 8; ++i)
+            el[8 * j + i] = code_from(0, o, c * X + 8 * j + i, (w[i / 2] >> (16 * (i % 2))) & 0xffffu);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < X; ++i) el[i] = code_of(0, o, c * X + i);
       }
+      const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
+      *reinterpret_cast<u32x4*>(kp + tile * kBlockSize * D * EB + ((size_t)c * kBlockSize + sl % kBlockSize) * 16) =
+          pack(el);
     } else {
+      const int v = q - nK;
+      const int o = s_quad[v / (D / Y)], gc = v % (D / Y);
+      const int64_t sl = s_slot[o];
+      const int g = gc / kBlockSize, c = gc % kBlockSize;
 #pragma unroll
-      for (int i = 0; i < X; ++i) el[i] = code_of(0, o, c * X + i);
+      for (int u = 0; u < Y; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) el[u * 4 + e] = code_of(1, o + e, kBlockSize * (g * Y + u) + c);
+      }
+      const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
+      const int jq = (int)(sl % kBlockSize) / 4;
+      *reinterpret_cast<u32x4*>(vp + tile * kBlockSize * D * EB + (((size_t)g * kBlockSize + c) * 4 + jq) * 16) =
+          pack(el);
     }
-    const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
-    *reinterpret_cast<u32x4*>(kp + tile * kBlockSize * D * EB + ((size_t)c * kBlockSize + sl % kBlockSize) * 16) =
-        pack(el);
   }
-  // V, complete quads: chunk (g, c) of the quad led by token o holds dims
-  // 16 (g Y + u) + c, u < Y, of its 4 rows, element order [u][row]
-  for (int q = tid; q < kWriteGroup * (D / Y); q += kThreads) {
-    const int o = q / (D / Y), gc = q % (D / Y);
-    if (s_lead[o] != 1) continue;
-    const int64_t sl = s_slot[o];
-    const int g = gc / kBlockSize, c = gc % kBlockSize;
-    uint32_t el[16 / EB];
-#pragma unroll
-    for (int u = 0; u < Y; ++u) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) el[u * 4 + e] = code_of(1, o + e, kBlockSize * (g * Y + u) + c);
-    }
-    const size_t tile = (size_t)(sl / kBlockSize) * num_kv_heads + h;
-    const int jq = (int)(sl % kBlockSize) / 4;
-    *reinterpret_cast<u32x4*>(vp + tile * kBlockSize * D * EB + (((size_t)g * kBlockSize + c) * 4 + jq) * 16) =
-        pack(el);
-  }
+  if (!s_single) return;
   // V, other tokens: element by element
   for (int q = tid; q < kWriteGroup * D; q += kThreads) {
     const int o = q / D, d = q % D;
