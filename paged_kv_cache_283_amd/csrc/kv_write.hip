@@ -149,6 +149,7 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
   __shared__ int s_full;                       // PACK16: the 16 tokens are rows 0..15 of one tile
   __shared__ int64_t s_slot[kWriteGroup];      // -1: token skipped
   __shared__ float s_scale[2][kWriteGroup];
+  __shared__ float s_cs[is_channel_scaled(KVT) ? 2 : 1][is_channel_scaled(KVT) ? D : 1];   // K, V channel scales of head h
   __shared__ int s_lead[kWriteGroup];          // V: 1 leads a complete quad, 2 is covered by one, 0 neither
   __shared__ int s_quad[kWriteGroup / 4];      // the tokens that lead a quad, in order
   __shared__ int s_nquad, s_single;            // how many; whether any token is stored element by element
@@ -178,6 +179,10 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
       wv[it] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(kv == 0 ? k_new : v_new) +
                                                (((size_t)(t_base + o) * num_kv_heads + h) * D + d0) * (16 / kPer));
   }
+  static_assert(2 * D <= kThreads, "one channel scale per thread");
+  float cs = 0.f;
+  if constexpr (is_channel_scaled(KVT))
+    if (tid < 2 * D) cs = (tid < D ? k_scale : v_scale)[(size_t)h * D + tid % D];
   long long my_slot = -1;                      // lanes 0..15: token t_base + lane
   if (tid < kWriteGroup) {
     const int t = t_base + tid;
@@ -202,6 +207,8 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
       }
     }
   }
+  if constexpr (is_channel_scaled(KVT))
+    if (tid < 2 * D) s_cs[tid / D][tid % D] = cs;
   __syncthreads();
   if (tid < kWave) {
     // V quads, in the first wave's registers: token o leads one when it and
@@ -263,7 +270,7 @@ __global__ void __launch_bounds__(kWriteThreads) kv_write_kernel(const void* k_n
     } else {
       float sc = 0.f;
       if constexpr (is_quantised(KVT)) sc = s_scale[kv][o];
-      if constexpr (is_channel_scaled(KVT)) sc = (kv == 0 ? k_scale : v_scale)[(size_t)h * D + d];
+      if constexpr (is_channel_scaled(KVT)) sc = s_cs[kv][d];
       return stored_code<SRC, KVT>(raw, sc);
     }
   };
