@@ -101,6 +101,41 @@ def test_write_pool_bytes_bit_exact(kv, src, d):
         assert np.array_equal(g, exp.view(np.uint8).reshape(-1))
 
 
+
+@pytest.mark.parametrize("kv,src", [("bf16", "bf16"), ("fp8", "bf16"), ("int8", "f16"), ("f32", "f32")])
+def test_write_scattered_slots_bit_exact(kv, src):
+    """An explicit slot list made of runs of consecutive slots in shuffled order (runs that start off a
+    multiple of 4, quads split between workgroups, lone tokens), with skipped (-1) and out-of-range
+    slots, stores exactly the bytes the oracle's write stores; every other byte stays untouched."""
+    nb, hkv, d, t = 12, 2, 128, 160
+    rng = np.random.default_rng(283)
+    total = nb * 16
+    runs = np.split(np.arange(total), np.sort(rng.choice(np.arange(1, total), 40, replace=False)))
+    slots = np.concatenate([runs[i] for i in rng.permutation(len(runs))])[:t].astype(np.int64)
+    skip = rng.choice(t, 10, replace=False)
+    slots[skip[:5]] = -1
+    slots[skip[5:]] = total + 3
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[src]
+    ks = torch.from_numpy(rng.standard_normal((t, hkv, d)).astype(np.float32) * 3).to(tdt)
+    vs = torch.from_numpy(rng.standard_normal((t, hkv, d)).astype(np.float32) * 3).to(tdt)
+    got = ops.allocate_pools(nb, hkv, d, W.storage_dtype(kv), "cuda", fill_byte=0xFF)
+    ops.paged_kv_write(ks.cuda(), vs.cuda(), got[0], got[1], torch.from_numpy(slots).cuda(), got[2], got[3])
+    ref = list(paging.new_pools(nb, hkv, d, kv))
+    for a in ref:
+        if a is not None:
+            a.view(np.uint8)[...] = 0xFF
+    ok = (slots >= 0) & (slots < total)
+    conv = {"f32": lambda x: x.numpy(), "f16": lambda x: x.numpy(),
+            "bf16": lambda x: x.view(torch.int16).numpy().view(np.uint16)}
+    table = np.arange(nb, dtype=np.int32)[None, :]
+    paging.write_tokens(ref, kv, conv[src](ks[torch.from_numpy(ok)]), conv[src](vs[torch.from_numpy(ok)]), src,
+                        table, np.zeros(int(ok.sum()), np.int32), slots[ok])
+    for g, e in zip(got, ref):
+        if e is None:
+            assert g is None
+            continue
+        assert np.array_equal(g.cpu().contiguous().view(torch.uint8).numpy().reshape(-1), e.view(np.uint8).reshape(-1))
+
 def test_fp8_encoder_on_crafted_values():
     """Rows whose absmax is 448 have scale exactly 1, so codes are the encoder applied to the values."""
     table = fp8.decode_table()
